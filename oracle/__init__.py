@@ -1,0 +1,213 @@
+"""CPU oracle for the QSA hot path (ctypes wrapper over ``qsa_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product library and its Python
+binding never import this package.
+
+Every function takes and returns numpy arrays.  bf16 tensors are passed as
+``uint16`` bit patterns, fp32 tensors as ``float32``.  The C source cites the
+page passage behind each step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libqsa_oracle.so")
+
+F32 = 0
+BF16 = 1
+FLAG_NO_ROPE = 1
+FLAG_POOL_RMSNORM = 2
+
+DIM = 128
+IDX_HEADS = 4
+BLOCK = 4
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C99 + OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+               "-D_DEFAULT_SOURCE", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64, u32, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_double
+    lib.qsa_oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.qsa_oracle_bf16_to_double.restype = f64
+    lib.qsa_oracle_bf16_from_double.argtypes = [f64]
+    lib.qsa_oracle_bf16_from_double.restype = ctypes.c_uint16
+    lib.qsa_oracle_rope.argtypes = [P, i64, f64]
+    lib.qsa_oracle_rope.restype = None
+    lib.qsa_oracle_pool.argtypes = [P, i64, P, i64, i32, i32, i32, f64, u32, i32]
+    lib.qsa_oracle_pool.restype = ctypes.c_int
+    lib.qsa_oracle_score_topk.argtypes = [P, P, P, i32, P, i64, i32, f64, u32, i32, P, P, P, P, i64]
+    lib.qsa_oracle_score_topk.restype = ctypes.c_int
+    lib.qsa_oracle_sparse_attn_prefill.argtypes = [P, P, P, i32, P, P, i64, P, P, i32, i32, i32,
+                                                   i32, f64, i32, P, P]
+    lib.qsa_oracle_sparse_attn_prefill.restype = ctypes.c_int
+    lib.qsa_oracle_sparse_attn_decode.argtypes = [P, P, i32, i32, P, P, P, i64, P, P, i32, i32,
+                                                  i32, i32, f64, i32, P, P]
+    lib.qsa_oracle_sparse_attn_decode.restype = ctypes.c_int
+    lib.qsa_oracle_threads.argtypes = []
+    lib.qsa_oracle_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"oracle {what} failed with code {rc}")
+
+
+def _dtype_code(arr) -> int:
+    if arr.dtype == np.uint16:
+        return BF16
+    if arr.dtype == np.float32:
+        return F32
+    raise TypeError(f"oracle takes uint16 (bf16 bits) or float32 arrays, got {arr.dtype}")
+
+
+def _c(a, dtype=None):
+    return np.ascontiguousarray(np.asarray(a) if dtype is None else np.asarray(a, dtype=dtype))
+
+
+def threads() -> int:
+    return int(_load().qsa_oracle_threads())
+
+
+def bf16_to_float(bits) -> np.ndarray:
+    lib = _load()
+    bits = np.asarray(bits, dtype=np.uint16)
+    out = np.array([lib.qsa_oracle_bf16_to_double(int(b)) for b in bits.reshape(-1)], dtype=np.float64)
+    return out.reshape(bits.shape)
+
+
+def bf16_from_float(x) -> np.ndarray:
+    lib = _load()
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array([lib.qsa_oracle_bf16_from_double(float(v)) for v in x.reshape(-1)], dtype=np.uint16)
+    return out.reshape(x.shape)
+
+
+def rope(vec, pos: int, theta: float) -> np.ndarray:
+    """Rotate one 128-d vector (float64) at `pos`; returns a new array."""
+    v = np.array(vec, dtype=np.float64, copy=True).reshape(DIM)
+    _load().qsa_oracle_rope(_ptr(v), int(pos), float(theta))
+    return v
+
+
+def pool(raw, block_begin: int, block_end: int, theta: float, flags: int = 0,
+         pooled=None) -> np.ndarray:
+    """a1-a3.  raw: [B][L][128] (uint16 bf16 bits or float32).  Returns (or
+    fills) pooled [B][NB][128], NB = pooled.shape[1] or block_end."""
+    raw = _c(raw)
+    dt = _dtype_code(raw)
+    B, L, d = raw.shape
+    assert d == DIM and 4 * block_end <= L
+    if pooled is None:
+        pooled = np.zeros((B, block_end, DIM), dtype=raw.dtype)
+    assert pooled.dtype == raw.dtype and pooled.flags.c_contiguous
+    rc = _load().qsa_oracle_pool(_ptr(raw), L * DIM, _ptr(pooled), pooled.shape[1] * DIM, B,
+                                 int(block_begin), int(block_end), float(theta), int(flags), dt)
+    _check(rc, "pool")
+    return pooled
+
+
+def score_topk(q_index, row_seq, row_pos, pooled, top_k: int, theta: float, flags: int = 0,
+               want_raw: bool = False):
+    """a4-a6.  q_index: [R][4][128]; pooled: [B][NB][128].
+    Returns (sel [R][top_k] int32, count [R] int32, scores [R][top_k] float32,
+    raw [R][NB] float64 or None)."""
+    q_index = _c(q_index)
+    pooled = _c(pooled)
+    dt = _dtype_code(q_index)
+    assert _dtype_code(pooled) == dt
+    row_seq = _c(row_seq, np.int32)
+    row_pos = _c(row_pos, np.int32)
+    R = q_index.shape[0]
+    NB = pooled.shape[1]
+    assert q_index.shape[1:] == (IDX_HEADS, DIM)
+    for r in range(R):  # contract: the visible blocks exist
+        assert (int(row_pos[r]) + 1) // BLOCK <= NB
+    sel = np.empty((R, top_k), np.int32)
+    cnt = np.empty((R,), np.int32)
+    sc = np.empty((R, top_k), np.float32)
+    raw = np.full((R, NB), np.nan, np.float64) if want_raw else None
+    rc = _load().qsa_oracle_score_topk(_ptr(q_index), _ptr(row_seq), _ptr(row_pos), R, _ptr(pooled),
+                                       NB * DIM, int(top_k), float(theta), int(flags), dt,
+                                       _ptr(sel), _ptr(cnt), _ptr(sc), _ptr(raw), NB)
+    _check(rc, "score_topk")
+    return sel, cnt, sc, raw
+
+
+def sparse_attn_prefill(q, row_seq, row_pos, k_cache, v_cache, sel, count, softmax_scale=None):
+    """a7+a8.  q: [R][Hq][D]; k/v: [B][L][Hkv][D]; sel: [R][top_k]; count: [R].
+    Returns (out [R][Hq][D] same dtype as q, lse [R][Hq] float32)."""
+    q = _c(q)
+    k_cache = _c(k_cache)
+    v_cache = _c(v_cache)
+    dt = _dtype_code(q)
+    R, Hq, D = q.shape
+    B, L, Hkv, D2 = k_cache.shape
+    assert D2 == D and v_cache.shape == k_cache.shape
+    sel = _c(sel, np.int32)
+    count = _c(count, np.int32)
+    top_k = sel.shape[1]
+    scale = float(softmax_scale) if softmax_scale is not None else 1.0 / np.sqrt(D)
+    out = np.empty_like(q)
+    lse = np.empty((R, Hq), np.float32)
+    rc = _load().qsa_oracle_sparse_attn_prefill(
+        _ptr(q), _ptr(_c(row_seq, np.int32)), _ptr(_c(row_pos, np.int32)), R, _ptr(k_cache),
+        _ptr(v_cache), L * Hkv * D, _ptr(sel), _ptr(count), top_k, Hq, Hkv, D, scale, dt, _ptr(out),
+        _ptr(lse))
+    _check(rc, "sparse_attn_prefill")
+    return out, lse
+
+
+def sparse_attn_decode(q, row_pos, k_cache, v_cache, sel, count, tail_start=None,
+                       softmax_scale=None):
+    """a7+a9.  q: [B][Qn][Hq][D]; row_pos: [B][Qn]; sel: [B][top_k]; count: [B];
+    tail_start: [B] or None.  Returns (out like q, lse [B][Qn][Hq] float32)."""
+    q = _c(q)
+    k_cache = _c(k_cache)
+    v_cache = _c(v_cache)
+    dt = _dtype_code(q)
+    B, Qn, Hq, D = q.shape
+    Bk, L, Hkv, D2 = k_cache.shape
+    assert D2 == D and Bk >= B and v_cache.shape == k_cache.shape
+    sel = _c(sel, np.int32)
+    count = _c(count, np.int32)
+    top_k = sel.shape[1]
+    scale = float(softmax_scale) if softmax_scale is not None else 1.0 / np.sqrt(D)
+    ts = None if tail_start is None else _c(tail_start, np.int32)
+    out = np.empty_like(q)
+    lse = np.empty((B, Qn, Hq), np.float32)
+    rc = _load().qsa_oracle_sparse_attn_decode(
+        _ptr(q), _ptr(_c(row_pos, np.int32)), B, Qn, _ptr(ts), _ptr(k_cache), _ptr(v_cache),
+        L * Hkv * D, _ptr(sel), _ptr(count), top_k, Hq, Hkv, D, scale, dt, _ptr(out), _ptr(lse))
+    _check(rc, "sparse_attn_decode")
+    return out, lse

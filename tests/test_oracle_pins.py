@@ -1,0 +1,513 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+No test here compares the oracle with itself.  Each pins one step against a
+closed form, an invariant, a textbook/library routine (numpy sort, einsum,
+torch SDPA), brute force on tiny inputs, or the constants the pages print
+(tests/golden/qsa_page_constants.json).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_long_amd import synth
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "qsa_page_constants.json")))
+K4 = GOLD["block_tokens"]["value"]
+DIM = GOLD["index_dim"]["value"]
+IH = GOLD["index_query_heads"]["value"]
+
+
+def f32(x):
+    return np.asarray(x, np.float32)
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding (storage format of the compressed key and bf16 operands)
+# --------------------------------------------------------------------------
+
+def test_bf16_known_values():
+    cases = [
+        (1.0, 0x3F80),
+        (-2.0, 0xC000),
+        (1.0 + 2.0 ** -8, 0x3F80),                 # tie -> even (down)
+        (1.0 + 3 * 2.0 ** -8, 0x3F82),             # tie -> even (up)
+        (1.0 + 2.0 ** -8 + 2.0 ** -30, 0x3F81),    # just above the tie
+        (2.0 ** -133, 0x0001),                     # smallest subnormal
+        (2.0 ** -134, 0x0000),                     # tie between 0 and 2^-133 -> even (0)
+        (1.5 * 2.0 ** -133, 0x0002),               # tie between 1 and 2 steps -> even
+        ((2 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F),    # largest finite
+        (2.0 ** 128, 0x7F80),                      # overflow -> inf
+        (0.0, 0x0000),
+        (-0.0, 0x8000),
+    ]
+    for x, bits in cases:
+        assert int(oracle.bf16_from_float([x])[0]) == bits, (x, hex(bits))
+
+
+def test_bf16_matches_torch_conversion():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(4000).astype(np.float32),
+                        (rng.standard_normal(1000) * 1e-39).astype(np.float32),  # subnormals
+                        (rng.standard_normal(1000) * 1e30).astype(np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_from_float(x.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+    back = oracle.bf16_to_float(got)
+    np.testing.assert_array_equal(back, torch.from_numpy(want.view(np.int16)).view(torch.bfloat16)
+                                  .to(torch.float64).numpy())
+
+
+# --------------------------------------------------------------------------
+# RoPE (post-pool key rotation, query rotation)
+# --------------------------------------------------------------------------
+
+def test_rope_position_zero_is_identity():
+    x = np.random.default_rng(1).standard_normal(DIM)
+    np.testing.assert_array_equal(oracle.rope(x, 0, 1e7), x)
+
+
+def test_rope_theta_one_turns_every_pair_by_pos_radians():
+    # theta = 1 -> every frequency is 1: pair (j, j+64) turns by exactly `pos`.
+    for j in (0, 17, 63):
+        for pos in (1, 5, 1000):
+            e = np.zeros(DIM)
+            e[j] = 1.0
+            out = oracle.rope(e, pos, 1.0)
+            want = np.zeros(DIM)
+            want[j], want[j + 64] = math.cos(pos), math.sin(pos)
+            np.testing.assert_allclose(out, want, atol=1e-12)
+            e = np.zeros(DIM)
+            e[j + 64] = 1.0
+            out = oracle.rope(e, pos, 1.0)
+            want = np.zeros(DIM)
+            want[j], want[j + 64] = -math.sin(pos), math.cos(pos)
+            np.testing.assert_allclose(out, want, atol=1e-12)
+
+
+def test_rope_frequency_schedule():
+    # theta = 2^64 -> theta^(-j/64) = 2^-j: at pos 1 pair j turns by 2^-j rad.
+    for j in range(0, 64, 7):
+        e = np.zeros(DIM)
+        e[j] = 1.0
+        out = oracle.rope(e, 1, 2.0 ** 64)
+        assert math.isclose(math.atan2(out[j + 64], out[j]), 2.0 ** -j, rel_tol=1e-12)
+    # theta = 1e8, pair 32 -> frequency theta^-1/2 = 1e-4: pos 10,000 turns by 1 rad.
+    e = np.zeros(DIM)
+    e[32] = 1.0
+    out = oracle.rope(e, 10_000, 1e8)
+    assert math.isclose(math.atan2(out[96], out[32]), 1.0, rel_tol=1e-12)
+
+
+def test_rope_norm_composition_relative_shift():
+    rng = np.random.default_rng(2)
+    x, y = rng.standard_normal(DIM), rng.standard_normal(DIM)
+    th = 1e7
+    for p in (3, 4096, 1_048_575):
+        assert math.isclose(np.linalg.norm(oracle.rope(x, p, th)), np.linalg.norm(x), rel_tol=1e-13)
+    np.testing.assert_allclose(oracle.rope(oracle.rope(x, 1234, th), 777, th),
+                               oracle.rope(x, 2011, th), atol=1e-11)
+    # <R(p)x, R(p')y> depends only on p - p'
+    a = oracle.rope(x, 1000, th) @ oracle.rope(y, 200, th)
+    b = oracle.rope(x, 1000 + 4 * 12345, th) @ oracle.rope(y, 200 + 4 * 12345, th)
+    assert math.isclose(a, b, rel_tol=1e-9, abs_tol=1e-9)
+
+
+# --------------------------------------------------------------------------
+# a1-a3: block mean in FP32, then RoPE at the block's first position
+# --------------------------------------------------------------------------
+
+def _raw(L, fill=None, B=1):
+    r = np.zeros((B, L, DIM), np.float32)
+    if fill is not None:
+        r[:] = fill
+    return r
+
+
+def test_pool_hand_example():
+    # Block 1 = tokens 4..7.  dim 0 holds 2,4,6,8 (mean 5), dim 1 holds 1 (mean 1).
+    raw = _raw(8)
+    raw[0, 4:8, 0] = [2, 4, 6, 8]
+    raw[0, 4:8, 1] = 1
+    th = 1e7
+    out = oracle.pool(raw, 0, 2, th)[0, 1].astype(np.float64)
+    want = np.zeros(DIM)
+    want[0], want[64] = 5 * math.cos(4.0), 5 * math.sin(4.0)      # pair 0: frequency 1
+    w1 = 4.0 * 10.0 ** (-7.0 / 64.0)                               # pair 1: 4 * theta^(-1/64)
+    want[1], want[65] = math.cos(w1), math.sin(w1)
+    np.testing.assert_allclose(out, want, rtol=1e-6, atol=1e-7)
+    # block 0 is all zero
+    np.testing.assert_array_equal(oracle.pool(raw, 0, 2, th)[0, 0], 0)
+
+
+def test_pool_mean_is_fp32_in_token_order():
+    # ((1 + 2^-24) + 2^-24) + 0 = 1 in FP32, so the mean is exactly 0.25;
+    # an exact (fp64) mean would be 0.25 + 2^-25, which FP32 can hold.
+    raw = _raw(4)
+    raw[0, :, 0] = [1.0, 2.0 ** -24, 2.0 ** -24, 0.0]
+    out = oracle.pool(raw, 0, 1, 1e7, flags=oracle.FLAG_NO_ROPE)
+    assert out[0, 0, 0] == np.float32(0.25)
+
+
+def test_pool_integer_means_exact_and_linear():
+    rng = np.random.default_rng(3)
+    x = rng.integers(-8, 9, size=(2, 64, DIM)).astype(np.float32)
+    y = rng.integers(-8, 9, size=(2, 64, DIM)).astype(np.float32)
+    flags = oracle.FLAG_NO_ROPE
+    px, py = oracle.pool(x, 0, 16, 1e7, flags), oracle.pool(y, 0, 16, 1e7, flags)
+    np.testing.assert_array_equal(px, x.reshape(2, 16, 4, DIM).sum(2) / 4)  # exact small integers
+    np.testing.assert_array_equal(oracle.pool(2 * x - 0.5 * y, 0, 16, 1e7, flags), 2 * px - 0.5 * py)
+    # with RoPE the map is still linear (a rotation), up to FP32 rounding
+    pr = oracle.pool(2 * x - 0.5 * y, 0, 16, 1e7)
+    lin = 2 * oracle.pool(x, 0, 16, 1e7) - 0.5 * oracle.pool(y, 0, 16, 1e7)
+    np.testing.assert_allclose(pr, lin, rtol=1e-5, atol=1e-4)
+
+
+def test_pool_constant_block_is_rotated_key():
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal(DIM).astype(np.float32)
+    raw = _raw(40)
+    raw[0, 4 * 7:4 * 8] = k
+    out = oracle.pool(raw, 7, 8, 1e7)[0, 7]
+    np.testing.assert_allclose(out, oracle.rope(k.astype(np.float64), 28, 1e7), rtol=1e-6, atol=1e-6)
+
+
+def test_pool_rotates_after_pooling_at_first_token():
+    # Four different keys with energy in the fast pairs: rotating each token at
+    # its own position before averaging, or rotating the mean at 4b+3, gives a
+    # clearly different compressed key ([ARCH] item 2 says after pooling).
+    rng = np.random.default_rng(5)
+    b = 11
+    keys = rng.standard_normal((4, DIM))
+    raw = _raw(4 * (b + 1))
+    raw[0, 4 * b:4 * b + 4] = keys.astype(np.float32)
+    got = oracle.pool(raw, b, b + 1, 1e7)[0, b].astype(np.float64)
+    mean = raw[0, 4 * b:4 * b + 4].astype(np.float64).mean(0)
+    post = oracle.rope(mean, 4 * b, 1e7)
+    pre = np.mean([oracle.rope(raw[0, 4 * b + i].astype(np.float64), 4 * b + i, 1e7)
+                   for i in range(4)], axis=0)
+    late = oracle.rope(mean, 4 * b + 3, 1e7)
+    np.testing.assert_allclose(got, post, rtol=1e-5, atol=1e-5)
+    assert np.abs(got - pre).max() > 1e-2
+    assert np.abs(got - late).max() > 1e-2
+
+
+def test_pool_bf16_storage_is_rounded_fp32_result():
+    rng = np.random.default_rng(6)
+    raw32 = synth.bf16_to_f32(synth.bf16_bits(rng.standard_normal((1, 256, DIM)).astype(np.float32)))
+    p32 = oracle.pool(raw32, 0, 64, 1e7)
+    pbf = oracle.pool(synth.bf16_bits(raw32), 0, 64, 1e7)
+    want = torch.from_numpy(p32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    diff = np.abs(pbf.astype(np.int32) - want.astype(np.int32))
+    assert diff.max() <= 1                      # double rounding via fp32 may move one ulp
+    assert (diff == 0).mean() > 0.999
+
+
+def test_pool_rmsnorm_flag_gives_unit_rms():
+    rng = np.random.default_rng(8)
+    raw = rng.standard_normal((1, 64, DIM)).astype(np.float32) * 3
+    out = oracle.pool(raw, 0, 16, 1e7, flags=oracle.FLAG_NO_ROPE | oracle.FLAG_POOL_RMSNORM)
+    rms = np.sqrt((out.astype(np.float64) ** 2).mean(-1))
+    np.testing.assert_allclose(rms, 1.0, rtol=1e-5)
+
+
+# --------------------------------------------------------------------------
+# a4-a6: block score and top-k selection
+# --------------------------------------------------------------------------
+
+def _rotated_queries(q, pos, theta, flags, dtype):
+    out = np.zeros(q.shape, np.float64)
+    for r in range(q.shape[0]):
+        for h in range(IH):
+            v = q[r, h].astype(np.float64) if dtype == "f32" else synth.bf16_to_f32(q[r, h]).astype(np.float64)
+            if not flags & oracle.FLAG_NO_ROPE:
+                v = oracle.rope(v, int(pos[r]), theta)
+            out[r, h] = v.astype(np.float32) if dtype == "f32" else oracle.bf16_to_float(oracle.bf16_from_float(v))
+    return out
+
+
+@pytest.mark.parametrize("dtype,flags", [("f32", 0), ("bf16", 0), ("bf16", oracle.FLAG_NO_ROPE)])
+def test_score_equals_einsum_brute_force(dtype, flags):
+    rng = np.random.default_rng(9)
+    B, NB, R, th = 2, 24, 7, 1e7
+    pooled = rng.standard_normal((B, NB, DIM)).astype(np.float32)
+    q = rng.standard_normal((R, IH, DIM)).astype(np.float32)
+    if dtype == "bf16":
+        pooled, q = synth.bf16_bits(pooled), synth.bf16_bits(q)
+    seq = rng.integers(0, B, R).astype(np.int32)
+    pos = rng.integers(0, 4 * NB, R).astype(np.int32)
+    sel, cnt, sc, raw = oracle.score_topk(q, seq, pos, pooled, 64, th, flags, want_raw=True)
+    qr = _rotated_queries(q, pos, th, flags, dtype)
+    kv = pooled.astype(np.float64) if dtype == "f32" else synth.bf16_to_f32(pooled).astype(np.float64)
+    dots = np.einsum("rhd,rbd->rhb", qr, kv[seq])
+    want = np.maximum(dots, 0).sum(1)
+    for r in range(R):
+        nc = (int(pos[r]) + 1) // 4
+        np.testing.assert_allclose(raw[r, :nc], want[r, :nc], rtol=1e-12, atol=1e-12)
+        assert np.isnan(raw[r, nc:]).all()  # invisible blocks are never scored
+        assert cnt[r] == nc and list(sel[r, :nc]) == list(range(nc))
+        np.testing.assert_allclose(sc[r, :nc], want[r, :nc] / math.sqrt(128), rtol=1e-6)
+
+
+def test_score_relu_per_head():
+    # integer vectors, no rotation: head 0 points against the key, heads 1..3 along it
+    k = np.zeros(DIM, np.float32)
+    k[:5] = [1, 2, 3, 0, -1]
+    pooled = np.stack([k, 2 * k])[None]          # [1][2][128]
+    q = np.stack([-k, k, k, k])[None]            # [1][4][128]
+    sel, cnt, sc, raw = oracle.score_topk(q, [0], [7], pooled, 4, 1e7, oracle.FLAG_NO_ROPE, want_raw=True)
+    assert list(raw[0]) == [3 * 15.0, 6 * 15.0]    # |k|^2 = 15; the negative head adds 0
+    assert sc[0, 1] == np.float32(90 / math.sqrt(128))
+
+
+def test_visibility_only_complete_blocks():
+    # block b is visible to the row at t iff 4b+3 <= t; a huge invisible block is ignored
+    pooled = np.ones((1, 8, DIM), np.float32)
+    pooled[0, 2] = 100.0
+    q = np.ones((1, IH, DIM), np.float32)
+    for t, want in [(0, 0), (2, 0), (3, 1), (6, 1), (7, 2), (10, 2), (11, 3)]:
+        sel, cnt, _, _ = oracle.score_topk(q, [0], [t], pooled, 1 if want else 4, 1e7, oracle.FLAG_NO_ROPE)
+        assert cnt[0] == min(want, sel.shape[1])
+        if t < 11:
+            assert 2 not in sel[0]
+
+
+def _lexsort_topk(raw_row, k):
+    order = np.lexsort((np.arange(raw_row.size), -raw_row))  # score desc, then index asc
+    return np.sort(order[:k])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_selection_equals_full_sort(seed):
+    rng = np.random.default_rng(seed)
+    NB, R, k = 80, 9, 13
+    pooled = rng.standard_normal((1, NB, DIM)).astype(np.float32)
+    q = rng.standard_normal((R, IH, DIM)).astype(np.float32)
+    pos = rng.integers(4 * k, 4 * NB, R).astype(np.int32)
+    sel, cnt, _, raw = oracle.score_topk(q, np.zeros(R, np.int32), pos, pooled, k, 1e7, 0, want_raw=True)
+    qr = _rotated_queries(q, pos, 1e7, 0, "f32")
+    want_raw = np.maximum(np.einsum("rhd,bd->rhb", qr, pooled[0].astype(np.float64)), 0).sum(1)
+    for r in range(R):
+        nc = (int(pos[r]) + 1) // 4
+        assert cnt[r] == k
+        np.testing.assert_array_equal(sel[r], _lexsort_topk(want_raw[r, :nc], k))
+
+
+def test_selection_ties_go_to_lower_block_index():
+    # integer keys with many exact repeats; no rotation -> exact integer scores
+    rng = np.random.default_rng(11)
+    NB, k = 60, 10
+    base = rng.integers(-2, 3, size=(6, DIM)).astype(np.float32)
+    pooled = base[rng.integers(0, 6, NB)][None]          # only 6 distinct keys
+    q = rng.integers(-2, 3, size=(3, IH, DIM)).astype(np.float32)
+    pos = np.array([4 * NB - 1, 4 * 40 + 2, 4 * 25], np.int32)
+    sel, cnt, _, raw = oracle.score_topk(q, np.zeros(3, np.int32), pos, pooled, k, 1e7,
+                                         oracle.FLAG_NO_ROPE, want_raw=True)
+    for r in range(3):
+        nc = (int(pos[r]) + 1) // 4
+        exact = np.array([sum(max(0, int(np.dot(q[r, h].astype(np.int64), pooled[0, b].astype(np.int64))))
+                              for h in range(IH)) for b in range(nc)])
+        np.testing.assert_array_equal(raw[r, :nc], exact)
+        np.testing.assert_array_equal(sel[r], _lexsort_topk(exact.astype(np.float64), k))
+        chosen = set(sel[r].tolist())
+        worst = min((exact[b], -b) for b in chosen)
+        best_out = max(((exact[b], -b) for b in range(nc) if b not in chosen), default=None)
+        assert best_out is None or worst > best_out
+
+
+def test_fewer_visible_than_k_keeps_all_and_pads():
+    pooled = np.random.default_rng(12).standard_normal((1, 50, DIM)).astype(np.float32)
+    q = np.random.default_rng(13).standard_normal((2, IH, DIM)).astype(np.float32)
+    sel, cnt, sc, _ = oracle.score_topk(q, [0, 0], [4 * 7 + 1, 4 * 50 - 1], pooled, 64, 1e7)
+    assert cnt.tolist() == [7, 50]
+    assert sel[0, :7].tolist() == list(range(7)) and (sel[0, 7:] == -1).all()
+    assert sel[1, :50].tolist() == list(range(50)) and (sel[1, 50:] == -1).all()
+
+
+def test_planted_needles_recovered_decode():
+    spec = synth.scaled("decode-128k", batch=2, ctx=16384)
+    w = synth.make(spec)
+    pooled = oracle.pool(w["raw_keys"], 0, spec.n_blocks, spec.theta)
+    sel, cnt, _, _ = oracle.score_topk(w["idx_q"], w["row_seq"], w["row_pos"], pooled, spec.top_k,
+                                       spec.theta)
+    for s in range(spec.batch):
+        assert cnt[s] == spec.top_k
+        assert set(w["planted"][s].tolist()) <= set(sel[s].tolist())
+
+
+def test_planted_set_is_the_selection_draft():
+    spec = synth.scaled("decode-1m-draft", batch=2, ctx=16384)
+    w = synth.make(spec)
+    pooled = oracle.pool(w["raw_keys"], 0, spec.n_blocks, spec.theta)
+    sel, cnt, _, raw = oracle.score_topk(w["idx_q"], w["row_seq"], w["row_pos"], pooled, spec.top_k,
+                                         spec.theta, want_raw=True)
+    for s in range(spec.batch):
+        np.testing.assert_array_equal(sel[s], w["planted"][s])
+        others = np.setdiff1d(np.arange(spec.n_blocks), w["planted"][s])
+        assert raw[s, w["planted"][s]].min() > 1.25 * raw[s, others].max()
+
+
+def test_planted_runs_fill_the_selection_chunk():
+    spec = synth.scaled("chunk-256k", ctx=8192, chunk=64)
+    w = synth.make(spec)
+    pooled = oracle.pool(w["raw_keys"], 0, spec.n_blocks, spec.theta)
+    rows = np.arange(0, 64, 9)
+    sel, cnt, _, _ = oracle.score_topk(w["idx_q"][rows], w["row_seq"][rows], w["row_pos"][rows], pooled,
+                                       spec.top_k, spec.theta)
+    planted = set(w["planted"][0].tolist())
+    for r in range(len(rows)):
+        assert cnt[r] == 512 and set(sel[r].tolist()) <= planted
+
+
+# --------------------------------------------------------------------------
+# a7-a9: expansion, tail, sparse GQA attention
+# --------------------------------------------------------------------------
+
+def _sdpa_dense_causal(q, k, v, scale):
+    """torch SDPA (is_causal) in fp64 on the CPU; q [L][Hq][D], k/v [L][Hkv][D]."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    qt = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)
+    kt = torch.from_numpy(k.astype(np.float64)).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+    vt = torch.from_numpy(v.astype(np.float64)).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+    o = torch.nn.functional.scaled_dot_product_attention(qt[None], kt[None], vt[None], is_causal=True,
+                                                         scale=scale)[0]
+    logits = (qt @ kt.transpose(1, 2)) * scale
+    mask = torch.triu(torch.ones(q.shape[0], q.shape[0], dtype=torch.bool), 1)
+    lse = torch.logsumexp(logits.masked_fill(mask, -math.inf), -1)
+    return o.permute(1, 0, 2).numpy(), lse.permute(1, 0).numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (4, 2), (6, 3)])
+def test_topk_at_least_visible_equals_dense_causal(Hq, Hkv):
+    # every row keeps all its visible blocks (top_k >= nc) -> QSA == dense causal attention
+    rng = np.random.default_rng(20 + Hq + Hkv)
+    L, D, k = 70, 32, 32
+    pooled = rng.standard_normal((1, L // 4, DIM)).astype(np.float32)
+    iq = rng.standard_normal((L, IH, DIM)).astype(np.float32)
+    pos = np.arange(L, dtype=np.int32)
+    seq = np.zeros(L, np.int32)
+    sel, cnt, _, _ = oracle.score_topk(iq, seq, pos, pooled, k, 1e7)
+    q = rng.standard_normal((L, Hq, D)).astype(np.float32)
+    kc = rng.standard_normal((1, L, Hkv, D)).astype(np.float32)
+    vc = rng.standard_normal((1, L, Hkv, D)).astype(np.float32)
+    out, lse = oracle.sparse_attn_prefill(q, seq, pos, kc, vc, sel, cnt, 1 / math.sqrt(D))
+    want, want_lse = _sdpa_dense_causal(q, kc[0], vc[0], 1 / math.sqrt(D))
+    np.testing.assert_allclose(out, want, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(lse, want_lse, rtol=1e-6, atol=1e-6)
+
+
+def test_attention_constant_v_single_position_permutation():
+    rng = np.random.default_rng(30)
+    L, D, Hq, Hkv = 64, 16, 2, 1
+    q = rng.standard_normal((3, Hq, D)).astype(np.float32)
+    kc = rng.standard_normal((1, L, Hkv, D)).astype(np.float32)
+    vc = np.broadcast_to(rng.standard_normal(D).astype(np.float32), (1, L, Hkv, D)).copy()
+    sel = np.array([[1, 4, 9, 2], [3, 0, -1, -1], [-1, -1, -1, -1]], np.int32)
+    cnt = np.array([4, 2, 0], np.int32)
+    pos = np.array([63, 13, 0], np.int32)
+    out, _ = oracle.sparse_attn_prefill(q, np.zeros(3, np.int32), pos, kc, vc, sel, cnt)
+    np.testing.assert_allclose(out, np.broadcast_to(vc[0, 0, 0], out.shape), rtol=1e-6)
+    # a row at t = 0 with no complete block attends only position 0
+    vc2 = rng.standard_normal((1, L, Hkv, D)).astype(np.float32)
+    out2, lse2 = oracle.sparse_attn_prefill(q, np.zeros(3, np.int32), pos, kc, vc2, sel, cnt)
+    np.testing.assert_array_equal(out2[2], np.broadcast_to(vc2[0, 0, 0], (Hq, D)))
+    np.testing.assert_allclose(lse2[2], (q[2] @ kc[0, 0, 0]) / math.sqrt(D), rtol=1e-6)
+    # the order of the kept blocks does not matter
+    perm = sel.copy()
+    perm[0, :4] = [9, 2, 1, 4]
+    out3, _ = oracle.sparse_attn_prefill(q, np.zeros(3, np.int32), pos, kc, vc2, perm, cnt)
+    np.testing.assert_allclose(out3, out2, rtol=1e-6, atol=1e-7)
+
+
+def _indicator_counts(n_blocks_ctx, t, top_k, sel=None, cnt=None, tail_start=None, decode=False):
+    """Uniform attention (q = 0) over V = [1, is_tail, is_selected_block_token]:
+    out = [1, n_tail/n, n_sel/n] reveals how many positions were attended."""
+    L = max(t + 1, 4 * n_blocks_ctx)
+    D = 8
+    kc = np.zeros((1, L, 1, D), np.float32)
+    vc = np.zeros((1, L, 1, D), np.float32)
+    vc[0, :, 0, 0] = 1
+    ts = tail_start if tail_start is not None else 4 * ((t + 1) // 4)
+    vc[0, ts:t + 1, 0, 1] = 1
+    if sel is None:
+        sel = np.arange(top_k, dtype=np.int32)[None]
+        cnt = np.array([top_k], np.int32)
+    for b in sel[0, :cnt[0]]:
+        vc[0, 4 * b:4 * b + 4, 0, 2] = 1
+    if decode:
+        q = np.zeros((1, 1, 1, D), np.float32)
+        out, _ = oracle.sparse_attn_decode(q, np.array([[t]], np.int32), kc, vc, sel, cnt,
+                                           None if tail_start is None else np.array([tail_start], np.int32))
+        out = out[0, 0, 0]
+    else:
+        q = np.zeros((1, 1, D), np.float32)
+        out, _ = oracle.sparse_attn_prefill(q, [0], [t], kc, vc, sel, cnt)
+        out = out[0, 0]
+    n = 1.0 / out[1] * (t + 1 - ts) if t + 1 > ts else None
+    return out, n
+
+
+def test_position_budget_from_the_pages():
+    top = GOLD["top_blocks"]["value"]
+    sel_tok = GOLD["selected_tokens"]["value"]
+    mx = GOLD["max_positions"]["value"]
+    assert top * K4 == sel_tok
+    for tail in range(GOLD["tail_tokens_min"]["value"], GOLD["tail_tokens_max"]["value"] + 1):
+        t = 4 * 600 + tail - 1                       # nc = 600 > 512 complete blocks; tail tokens
+        out, _ = _indicator_counts(600, t, top)
+        assert out[0] == pytest.approx(1.0, rel=1e-6)
+        n_total = sel_tok + tail
+        assert out[1] == pytest.approx(tail / n_total, rel=1e-6, abs=1e-9)   # tail always attended
+        assert out[2] == pytest.approx(sel_tok / n_total, rel=1e-6)          # 512 blocks -> 2048 tokens
+        assert n_total <= mx
+    assert sel_tok + GOLD["tail_tokens_max"]["value"] == mx
+
+
+def test_decode_shared_selection_with_drafted_positions():
+    # IndexShare: rows after the anchor reuse its selection and add [tail_start, t]
+    rng = np.random.default_rng(40)
+    L, D, Hq, Hkv, k = 4 * 40, 16, 4, 2, 8
+    Qn = 3
+    kc = rng.standard_normal((2, L + Qn, Hkv, D)).astype(np.float32)
+    vc = rng.standard_normal((2, L + Qn, Hkv, D)).astype(np.float32)
+    q = rng.standard_normal((2, Qn, Hq, D)).astype(np.float32)
+    sel = np.sort(rng.choice(40, size=(2, k), replace=True), axis=1).astype(np.int32)
+    sel = np.stack([np.sort(rng.choice(40, k, replace=False)) for _ in range(2)]).astype(np.int32)
+    cnt = np.array([k, k - 2], np.int32)
+    sel[1, k - 2:] = -1
+    rp = (L + np.tile(np.arange(Qn), (2, 1))).astype(np.int32)
+    ts = np.array([L, L], np.int32)
+    out, lse = oracle.sparse_attn_decode(q, rp, kc, vc, sel, cnt, ts)
+    for s in range(2):
+        for j in range(Qn):
+            P = [4 * b + i for b in sel[s, :cnt[s]] for i in range(4)] + list(range(L, L + j + 1))
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                qt = torch.from_numpy(q[s, j, h].astype(np.float64))[None, None, None]
+                kt = torch.from_numpy(kc[s, P, g].astype(np.float64))[None, None]
+                vt = torch.from_numpy(vc[s, P, g].astype(np.float64))[None, None]
+                o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=1 / math.sqrt(D))
+                np.testing.assert_allclose(out[s, j, h], o[0, 0, 0].numpy(), rtol=1e-5, atol=1e-6)
+                want_lse = torch.logsumexp((kt[0, 0] @ qt[0, 0, 0]) / math.sqrt(D), 0).item()
+                assert lse[s, j, h] == pytest.approx(want_lse, rel=1e-6)
+
+
+def test_attention_bf16_output_is_rounded():
+    rng = np.random.default_rng(50)
+    L, D = 32, 16
+    q = rng.standard_normal((4, 2, D)).astype(np.float32)
+    kc = rng.standard_normal((1, L, 1, D)).astype(np.float32)
+    vc = rng.standard_normal((1, L, 1, D)).astype(np.float32)
+    qb, kb, vb = synth.bf16_bits(q), synth.bf16_bits(kc), synth.bf16_bits(vc)
+    sel = np.tile(np.arange(4, dtype=np.int32), (4, 1))
+    cnt = np.array([0, 1, 2, 4], np.int32)
+    pos = np.array([2, 5, 10, 19], np.int32)
+    out32, _ = oracle.sparse_attn_prefill(synth.bf16_to_f32(qb), [0] * 4, pos, synth.bf16_to_f32(kb),
+                                          synth.bf16_to_f32(vb), sel, cnt)
+    outb, _ = oracle.sparse_attn_prefill(qb, [0] * 4, pos, kb, vb, sel, cnt)
+    want = torch.from_numpy(out32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.abs(outb.astype(np.int32) - want.astype(np.int32)).max() <= 1
