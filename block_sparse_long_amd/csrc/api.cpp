@@ -1,0 +1,330 @@
+// api.cpp -- the C-ABI of libqsa: argument validation (on the host, before
+// any HIP call), workspace layout, kernel launches on the caller's stream,
+// status strings and optional per-kernel timing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "qsa.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+
+// ---------------------------------------------------------------------------
+// launch bookkeeping
+// ---------------------------------------------------------------------------
+static thread_local hipError_t g_launch_err = hipSuccess;
+
+void note_launch(hipError_t err)
+{
+    if (err != hipSuccess && g_launch_err == hipSuccess) g_launch_err = err;
+}
+
+static void clear_launch_err() { g_launch_err = hipSuccess; }
+static qsa_status_t launch_status() { return g_launch_err == hipSuccess ? QSA_OK : QSA_ERR_DEVICE; }
+
+struct ProfRecord {
+    std::string name;
+    hipEvent_t start, stop;
+};
+static bool g_prof = false;
+static std::vector<ProfRecord> g_records;
+static std::vector<hipEvent_t> g_free_events;
+static std::string g_pending_name;
+static hipEvent_t g_pending_start = nullptr;
+
+static hipEvent_t take_event()
+{
+    if (!g_free_events.empty()) {
+        hipEvent_t e = g_free_events.back();
+        g_free_events.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+bool profiling_enabled() { return g_prof; }
+
+void prof_begin(const char *name, hipStream_t stream)
+{
+    g_pending_name = name;
+    g_pending_start = take_event();
+    if (g_pending_start) (void)hipEventRecord(g_pending_start, stream);
+}
+
+void prof_end(hipStream_t stream)
+{
+    hipEvent_t stop = take_event();
+    if (!g_pending_start || !stop) return;
+    (void)hipEventRecord(stop, stream);
+    g_records.push_back({g_pending_name, g_pending_start, stop});
+    g_pending_start = nullptr;
+}
+
+// ---------------------------------------------------------------------------
+// validation helpers
+// ---------------------------------------------------------------------------
+static bool aligned16(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static bool dtype_ok(qsa_dtype_t d) { return d == QSA_F32 || d == QSA_BF16; }
+static size_t elem_bytes(qsa_dtype_t d) { return d == QSA_BF16 ? 2 : 4; }
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Rows up to this count use the per-row streaming scorer; more rows use the
+// MFMA GEMM scorer, which shares each key tile among 16 rows.
+constexpr int32_t kRowsPathMax = 64;
+
+struct ScoreLayout {
+    int64_t sc_stride;
+    size_t qrot_off, scores_off, total;
+};
+
+static ScoreLayout score_layout(int32_t rows, int32_t max_nb, qsa_dtype_t dtype)
+{
+    ScoreLayout L;
+    L.sc_stride = ((int64_t)max_nb + 63) / 64 * 64;
+    L.qrot_off = 0;
+    L.scores_off = align256((size_t)rows * kIdxHeads * kDim * elem_bytes(dtype));
+    L.total = L.scores_off + align256((size_t)rows * (size_t)L.sc_stride * sizeof(float));
+    return L;
+}
+
+}  // namespace qsa
+
+using namespace qsa;
+
+extern "C" {
+
+const char *qsa_status_string(qsa_status_t s)
+{
+    switch (s) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_INVALID_ARG: return "invalid argument";
+    case QSA_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+    case QSA_ERR_WORKSPACE: return "workspace too small";
+    case QSA_ERR_DEVICE: return "HIP launch or runtime error";
+    }
+    return "unknown status";
+}
+
+qsa_status_t qsa_pool_index_keys(const void *raw_keys, int64_t raw_seq_stride, void *pooled,
+                                 int64_t pooled_seq_stride, int32_t batch, int32_t block_begin,
+                                 int32_t block_end, double rope_theta, uint32_t flags, qsa_dtype_t dtype,
+                                 void *stream)
+{
+    if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
+    if (batch < 0 || block_begin < 0 || block_end < block_begin) return QSA_ERR_INVALID_ARG;
+    if (flags & ~(uint32_t)(QSA_FLAG_NO_ROPE | QSA_FLAG_POOL_RMSNORM)) return QSA_ERR_INVALID_ARG;
+    if (!(flags & QSA_FLAG_NO_ROPE) && !(rope_theta > 1.0 && std::isfinite(rope_theta))) return QSA_ERR_INVALID_ARG;
+    if (batch == 0 || block_end == block_begin) return QSA_OK;
+    if (!aligned16(raw_keys) || !aligned16(pooled)) return QSA_ERR_INVALID_ARG;
+    if (raw_seq_stride % 8 || pooled_seq_stride % 8) return QSA_ERR_INVALID_ARG;
+    if (batch > 1 && (raw_seq_stride < (int64_t)kBlock * block_end * kDim || pooled_seq_stride < (int64_t)block_end * kDim))
+        return QSA_ERR_INVALID_ARG;
+    clear_launch_err();
+    launch_pool(raw_keys, raw_seq_stride, pooled, pooled_seq_stride, batch, block_begin, block_end, rope_theta, flags,
+                dtype == QSA_BF16, (hipStream_t)stream);
+    return launch_status();
+}
+
+size_t qsa_score_topk_workspace_size(int32_t rows, int32_t max_visible_blocks, int32_t top_k, qsa_dtype_t dtype)
+{
+    (void)top_k;
+    if (rows <= 0 || max_visible_blocks < 0 || !dtype_ok(dtype)) return 0;
+    return score_layout(rows, max_visible_blocks, dtype).total;
+}
+
+qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+                            const void *pooled, int64_t pooled_seq_stride, int32_t max_visible_blocks, int32_t top_k,
+                            double rope_theta, uint32_t flags, qsa_dtype_t dtype, int32_t *sel_blocks,
+                            int32_t *sel_count, float *sel_scores, void *workspace, size_t workspace_bytes,
+                            void *stream)
+{
+    if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
+    if (rows < 0 || max_visible_blocks < 0 || top_k < 1 || top_k > QSA_MAX_TOP_K) return QSA_ERR_INVALID_ARG;
+    const uint32_t known = QSA_FLAG_NO_ROPE | QSA_FLAG_SCORE_ROWS | QSA_FLAG_SCORE_GEMM;
+    if (flags & ~known) return QSA_ERR_INVALID_ARG;
+    if ((flags & QSA_FLAG_SCORE_ROWS) && (flags & QSA_FLAG_SCORE_GEMM)) return QSA_ERR_INVALID_ARG;
+    if ((flags & QSA_FLAG_SCORE_GEMM) && dtype != QSA_BF16) return QSA_ERR_UNSUPPORTED;
+    if (!(flags & QSA_FLAG_NO_ROPE) && !(rope_theta > 1.0 && std::isfinite(rope_theta))) return QSA_ERR_INVALID_ARG;
+    if (rows == 0) return QSA_OK;
+    if (!aligned16(q_index) || !aligned16(pooled) || !row_seq || !row_pos || !sel_blocks || !sel_count)
+        return QSA_ERR_INVALID_ARG;
+    if (pooled_seq_stride % 8 || pooled_seq_stride < 0) return QSA_ERR_INVALID_ARG;
+    const ScoreLayout L = score_layout(rows, max_visible_blocks, dtype);
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return QSA_ERR_INVALID_ARG;
+    if (workspace_bytes < L.total) return QSA_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const bool bf16 = dtype == QSA_BF16;
+    char *ws = (char *)workspace;
+    void *qrot = ws + L.qrot_off;
+    float *scores = (float *)(ws + L.scores_off);
+    clear_launch_err();
+    launch_rope_query(q_index, row_pos, rows, qrot, rope_theta, flags & QSA_FLAG_NO_ROPE, bf16, st);
+    if (max_visible_blocks > 0) {
+        bool gemm = bf16 && rows > kRowsPathMax;
+        if (flags & QSA_FLAG_SCORE_ROWS) gemm = false;
+        if (flags & QSA_FLAG_SCORE_GEMM) gemm = true;
+        if (gemm)
+            launch_score_gemm(qrot, row_seq, row_pos, rows, pooled, pooled_seq_stride, max_visible_blocks, scores,
+                              L.sc_stride, st);
+        else
+            launch_score_rows(qrot, row_seq, row_pos, rows, pooled, pooled_seq_stride, max_visible_blocks, scores,
+                              L.sc_stride, bf16, st);
+    }
+    launch_select_rows(scores, L.sc_stride, row_pos, rows, max_visible_blocks, top_k, sel_blocks, sel_count, sel_scores, st);
+    return launch_status();
+}
+
+static qsa_status_t check_attn_common(const void *q, const void *k_cache, const void *v_cache, int64_t kv_seq_stride,
+                                      const int32_t *sel_blocks, const int32_t *sel_count, int32_t top_k, int32_t Hq,
+                                      int32_t Hkv, int32_t D, float softmax_scale, qsa_dtype_t dtype, const void *out)
+{
+    if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
+    if (D != kDim) return QSA_ERR_UNSUPPORTED;
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return QSA_ERR_INVALID_ARG;
+    if (top_k < 1 || top_k > QSA_MAX_TOP_K) return QSA_ERR_INVALID_ARG;
+    if (!std::isfinite(softmax_scale)) return QSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !sel_blocks || !sel_count || !out)
+        return QSA_ERR_INVALID_ARG;
+    if (kv_seq_stride < 0 || kv_seq_stride % 8) return QSA_ERR_INVALID_ARG;
+    return QSA_OK;
+}
+
+qsa_status_t qsa_sparse_attn_prefill(const void *q, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+                                     const void *k_cache, const void *v_cache, int64_t kv_seq_stride,
+                                     const int32_t *sel_blocks, const int32_t *sel_count, int32_t top_k, int32_t Hq,
+                                     int32_t Hkv, int32_t D, float softmax_scale, qsa_dtype_t dtype, void *out,
+                                     float *lse, void *stream)
+{
+    if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
+    if (rows < 0) return QSA_ERR_INVALID_ARG;
+    if (D != kDim) return QSA_ERR_UNSUPPORTED;
+    if (Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && Hq / Hkv > QSA_MAX_QUERY_GROUP) return QSA_ERR_UNSUPPORTED;
+    if (rows == 0) {
+        if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || top_k < 1 || top_k > QSA_MAX_TOP_K) return QSA_ERR_INVALID_ARG;
+        return QSA_OK;
+    }
+    qsa_status_t st = check_attn_common(q, k_cache, v_cache, kv_seq_stride, sel_blocks, sel_count, top_k, Hq, Hkv, D,
+                                        softmax_scale, dtype, out);
+    if (st != QSA_OK) return st;
+    if (!row_seq || !row_pos) return QSA_ERR_INVALID_ARG;
+    AttnArgs a{};
+    a.q = q;
+    a.row_seq = row_seq;
+    a.row_pos = row_pos;
+    a.tail_start = nullptr;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.kv_seq_stride = kv_seq_stride;
+    a.sel_blocks = sel_blocks;
+    a.sel_count = sel_count;
+    a.top_k = top_k;
+    a.n_sel = rows;
+    a.q_per_sel = 1;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.scale = softmax_scale;
+    a.out = out;
+    a.lse = lse;
+    a.partial = nullptr;
+    a.nsplit = 1;
+    clear_launch_err();
+    launch_attn_prefill(a, dtype == QSA_BF16, (hipStream_t)stream);
+    return launch_status();
+}
+
+size_t qsa_sparse_attn_decode_workspace_size(int32_t batch, int32_t q_per_seq, int32_t Hq, int32_t D, int32_t top_k)
+{
+    if (batch <= 0 || q_per_seq <= 0 || Hq <= 0 || D != kDim || top_k < 1 || top_k > QSA_MAX_TOP_K) return 0;
+    const size_t nsplit = (size_t)attn_decode_splits(top_k);
+    return align256((size_t)batch * q_per_seq * Hq * nsplit * (kDim + 2) * sizeof(float));
+}
+
+qsa_status_t qsa_sparse_attn_decode(const void *q, const int32_t *row_pos, int32_t batch, int32_t q_per_seq,
+                                    const int32_t *tail_start, const void *k_cache, const void *v_cache,
+                                    int64_t kv_seq_stride, const int32_t *sel_blocks, const int32_t *sel_count,
+                                    int32_t top_k, int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                                    qsa_dtype_t dtype, void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                    void *stream)
+{
+    if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
+    if (batch < 0 || q_per_seq < 1) return QSA_ERR_INVALID_ARG;
+    if (D != kDim) return QSA_ERR_UNSUPPORTED;
+    if (Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && (int64_t)q_per_seq * (Hq / Hkv) > QSA_MAX_QUERY_GROUP)
+        return QSA_ERR_UNSUPPORTED;
+    if (batch == 0) {
+        if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || top_k < 1 || top_k > QSA_MAX_TOP_K) return QSA_ERR_INVALID_ARG;
+        return QSA_OK;
+    }
+    qsa_status_t st = check_attn_common(q, k_cache, v_cache, kv_seq_stride, sel_blocks, sel_count, top_k, Hq, Hkv, D,
+                                        softmax_scale, dtype, out);
+    if (st != QSA_OK) return st;
+    if (!row_pos) return QSA_ERR_INVALID_ARG;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return QSA_ERR_INVALID_ARG;
+    if (workspace_bytes < qsa_sparse_attn_decode_workspace_size(batch, q_per_seq, Hq, D, top_k))
+        return QSA_ERR_WORKSPACE;
+    AttnArgs a{};
+    a.q = q;
+    a.row_seq = nullptr;
+    a.row_pos = row_pos;
+    a.tail_start = tail_start;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.kv_seq_stride = kv_seq_stride;
+    a.sel_blocks = sel_blocks;
+    a.sel_count = sel_count;
+    a.top_k = top_k;
+    a.n_sel = batch;
+    a.q_per_sel = q_per_seq;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.scale = softmax_scale;
+    a.out = out;
+    a.lse = lse;
+    a.partial = (float *)workspace;
+    a.nsplit = attn_decode_splits(top_k);
+    clear_launch_err();
+    launch_attn_decode(a, dtype == QSA_BF16, (hipStream_t)stream);
+    return launch_status();
+}
+
+qsa_status_t qsa_profile_enable(int enable)
+{
+    g_prof = enable != 0;
+    return QSA_OK;
+}
+
+qsa_status_t qsa_profile_reset(void)
+{
+    for (auto &r : g_records) {
+        g_free_events.push_back(r.start);
+        g_free_events.push_back(r.stop);
+    }
+    g_records.clear();
+    return QSA_OK;
+}
+
+int32_t qsa_profile_kernel_ms(const char *name, double *total_ms)
+{
+    double total = 0.0;
+    int32_t n = 0;
+    if (name) {
+        for (auto &r : g_records) {
+            if (r.name != name) continue;
+            if (hipEventSynchronize(r.stop) != hipSuccess) continue;
+            float ms = 0.0f;
+            if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) continue;
+            total += ms;
+            ++n;
+        }
+    }
+    if (total_ms) *total_ms = total;
+    return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// pool.hip -- steps a1-a4: block mean pooling with post-pool RoPE, and the
+// rotation of the index queries.
+//
+// "Qwen3.8-Flash-Next: Day-0 Support in SGLang", section "Qwen Sparse
+// Attention": four raw index keys are averaged in FP32 and rotated with the
+// first token's position; the compressed key is stored in BF16.  Architecture
+// guide, "How a token moves through the model", item 2: the rotation comes
+// after pooling, so keys of different positions are not averaged with
+// different phases.  The index queries are rotated at their own positions
+// (reading: the pages use RoPE in the indexer but do not spell out the query
+// side; without it a score would not depend on the query's position).
+#include "qsa_device.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+
+// One wave per pooled block: lane j owns the rotary pair (j, j + 64).  The
+// wave reads the block's 4 tokens x 128 dims (contiguous in memory) with 8
+// coalesced loads.
+template <typename T>
+__global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ raw, int64_t raw_stride,
+                                                        T *__restrict__ pooled, int64_t pooled_stride,
+                                                        int64_t total, int32_t nblk, int32_t block_begin,
+                                                        double theta, uint32_t flags)
+{
+    __shared__ double inv_freq[kHalf];
+    if (threadIdx.x < kHalf) inv_freq[threadIdx.x] = pow(theta, -(double)threadIdx.x / (double)kHalf);
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (w >= total) return;
+    const int64_t s = w / nblk;
+    const int64_t b = block_begin + w % nblk;
+    const T *src = raw + s * raw_stride + b * (kBlock * kDim);
+    float x = 0.0f, y = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) {  // FP32 sum in token order, then times 1/4
+        x += load_f32(src + i * kDim + lane);
+        y += load_f32(src + i * kDim + kHalf + lane);
+    }
+    x *= 0.25f;
+    y *= 0.25f;
+    double dx = x, dy = y;
+    if (flags & kFlagRmsNorm) {
+        const double ss = wave_sum_f64(dx * dx + dy * dy);
+        const double inv = 1.0 / sqrt(ss / (double)kDim + 1e-6);
+        dx *= inv;
+        dy *= inv;
+    }
+    if (!(flags & kFlagNoRope)) rope_pair(dx, dy, kBlock * b, inv_freq[lane]);
+    T *dst = pooled + s * pooled_stride + b * kDim;
+    store_f64(dst + lane, dx);
+    store_f64(dst + kHalf + lane, dy);
+}
+
+// One wave per (row, index head): q~ = round_dtype(RoPE(q, row_pos)).
+template <typename T>
+__global__ __launch_bounds__(256) void rope_query_kernel(const T *__restrict__ q, const int32_t *__restrict__ row_pos,
+                                                         int32_t rows, T *__restrict__ qrot, double theta,
+                                                         uint32_t flags)
+{
+    __shared__ double inv_freq[kHalf];
+    if (threadIdx.x < kHalf) inv_freq[threadIdx.x] = pow(theta, -(double)threadIdx.x / (double)kHalf);
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (w >= (int64_t)rows * kIdxHeads) return;
+    const int64_t r = w / kIdxHeads;
+    const T *src = q + w * kDim;
+    double dx = load_f32(src + lane), dy = load_f32(src + kHalf + lane);
+    if (!(flags & kFlagNoRope)) rope_pair(dx, dy, row_pos[r], inv_freq[lane]);
+    store_f64(qrot + w * kDim + lane, dx);
+    store_f64(qrot + w * kDim + kHalf + lane, dy);
+}
+
+void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pooled_stride, int32_t batch,
+                 int32_t block_begin, int32_t block_end, double theta, uint32_t flags, bool bf16,
+                 hipStream_t stream)
+{
+    const int32_t nblk = block_end - block_begin;
+    const int64_t total = (int64_t)batch * nblk;
+    const dim3 grid((unsigned)((total + 3) / 4)), block(256);
+    if (bf16)
+        QSA_LAUNCH("pool_rope", (pool_rope_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)raw,
+                   raw_stride, (bf16_t *)pooled, pooled_stride, total, nblk, block_begin, theta, flags);
+    else
+        QSA_LAUNCH("pool_rope", (pool_rope_kernel<float>), grid, block, 0, stream, (const float *)raw, raw_stride,
+                   (float *)pooled, pooled_stride, total, nblk, block_begin, theta, flags);
+}
+
+void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,
+                       uint32_t flags, bool bf16, hipStream_t stream)
+{
+    const int64_t waves = (int64_t)rows * kIdxHeads;
+    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    if (bf16)
+        QSA_LAUNCH("rope_query", (rope_query_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)q, row_pos,
+                   rows, (bf16_t *)qrot, theta, flags);
+    else
+        QSA_LAUNCH("rope_query", (rope_query_kernel<float>), grid, block, 0, stream, (const float *)q, row_pos,
+                   rows, (float *)qrot, theta, flags);
+}
+
+}  // namespace qsa

@@ -1,0 +1,118 @@
+// qsa_device.h -- device helpers shared by the libqsa kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qsa_internal.h"
+
+namespace qsa {
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));   // MFMA operand (8 x bf16)
+typedef float f32x4_t __attribute__((ext_vector_type(4)));      // 16x16 MFMA accumulator
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ bf16x8_t zero_bf16x8() { return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0)); }
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float -> bf16, round to nearest, ties to even.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+// double -> bf16 with a single rounding (nearest-even): narrow to float with
+// round-to-odd (truncate toward zero, then set the last bit if anything was
+// dropped); float keeps 16 more bits than bf16, so the final nearest-even
+// step then rounds exactly as a direct double -> bf16 rounding would.
+__device__ __forceinline__ bf16_t f64_to_bf16(double x)
+{
+    float r = (float)x;
+    if (!isfinite(r) || (double)r == x) return f32_to_bf16(r);
+    if (fabs((double)r) > fabs(x)) r = __uint_as_float(__float_as_uint(r) - 1u);  // toward zero
+    return f32_to_bf16(__uint_as_float(__float_as_uint(r) | 1u));
+}
+
+template <typename T> __device__ __forceinline__ float load_f32(const T *p);
+template <> __device__ __forceinline__ float load_f32<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float load_f32<bf16_t>(const bf16_t *p) { return bf16_to_f32(*p); }
+
+template <typename T> __device__ __forceinline__ void store_f64(T *p, double v);
+template <> __device__ __forceinline__ void store_f64<float>(float *p, double v) { *p = (float)v; }
+template <> __device__ __forceinline__ void store_f64<bf16_t>(bf16_t *p, double v) { *p = f64_to_bf16(v); }
+
+template <typename T> __device__ __forceinline__ void store_f32(T *p, float v);
+template <> __device__ __forceinline__ void store_f32<float>(float *p, float v) { *p = v; }
+template <> __device__ __forceinline__ void store_f32<bf16_t>(bf16_t *p, float v) { *p = f32_to_bf16(v); }
+
+// Eight consecutive elements as floats (16-byte aligned for bf16, 32 for fp32).
+__device__ __forceinline__ void load8(const bf16_t *p, float *o)
+{
+    const uint4 v = *(const uint4 *)p;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(w[i] << 16);
+        o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8(const float *p, float *o)
+{
+    const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+// Order-preserving unsigned key of a float score (bigger score -> bigger
+// key); -0 and +0 map to one key.
+__device__ __forceinline__ uint32_t score_key(float s)
+{
+    uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k)
+{
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+// Complete micro-blocks visible to a query at position t: 4b + 3 <= t.
+__device__ __forceinline__ int64_t visible_blocks(int64_t t) { return (t + 1) / kBlock; }
+
+// Rotate the pair (x, y) = (v[j], v[j+64]) at integer position `pos` with
+// frequency inv_freq = theta^(-j/64); the angle and the rotation are formed
+// in double precision.
+__device__ __forceinline__ void rope_pair(double &x, double &y, int64_t pos, double inv_freq)
+{
+#pragma clang fp contract(off)
+    const double ang = (double)pos * inv_freq;
+    double s, c;
+    sincos(ang, &s, &c);
+    const double nx = x * c - y * s;
+    const double ny = x * s + y * c;
+    x = nx;
+    y = ny;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v)
+{
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+}  // namespace qsa

@@ -1,0 +1,85 @@
+// qsa_internal.h -- what the C-ABI layer (api.cpp) and the kernel files share:
+// the launch wrapper and the host-side launchers of every kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+constexpr int kDim = 128;       // indexer key / query dim, attention head dim
+constexpr int kHalf = 64;       // rotate-half pairs (j, j + 64)
+constexpr int kIdxHeads = 4;    // indexer query heads
+constexpr int kBlock = 4;       // tokens per micro-block
+constexpr int kWave = 64;       // CDNA wavefront
+constexpr uint32_t kFlagNoRope = 1u;
+constexpr uint32_t kFlagRmsNorm = 2u;
+
+// ---- launch bookkeeping (api.cpp) -----------------------------------------
+bool profiling_enabled();
+void prof_begin(const char *name, hipStream_t stream);
+void prof_end(hipStream_t stream);
+void note_launch(hipError_t err);
+
+// ---- pool.hip ---------------------------------------------------------------
+void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pooled_stride, int32_t batch,
+                 int32_t block_begin, int32_t block_end, double theta, uint32_t flags, bool bf16,
+                 hipStream_t stream);
+void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,
+                       uint32_t flags, bool bf16, hipStream_t stream);
+
+// ---- score.hip --------------------------------------------------------------
+void launch_score_rows(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+                       const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores,
+                       int64_t sc_stride, bool bf16, hipStream_t stream);
+void launch_score_gemm(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+                       const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores,
+                       int64_t sc_stride, hipStream_t stream);
+
+// ---- select.hip -------------------------------------------------------------
+void launch_select_rows(const float *scores, int64_t sc_stride, const int32_t *row_pos, int32_t rows,
+                        int32_t max_nb, int32_t top_k, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
+                        hipStream_t stream);
+
+// ---- attn.hip ---------------------------------------------------------------
+// Position chunk of the attention kernels and the largest query group one
+// workgroup holds (query rows sharing a selection x query heads per KV head).
+constexpr int kAttnChunk = 64;
+constexpr int kAttnMaxQ = 64;
+
+struct AttnArgs {
+    const void *q;            // prefill [rows][Hq][D]; decode [B][Qn][Hq][D]
+    const int32_t *row_seq;   // prefill: sequence of each row; decode: unused
+    const int32_t *row_pos;   // prefill [rows]; decode [B][Qn]
+    const int32_t *tail_start;  // decode [B] or null
+    const void *k_cache;
+    const void *v_cache;
+    int64_t kv_seq_stride;
+    const int32_t *sel_blocks;  // [groups-of-rows][top_k]
+    const int32_t *sel_count;
+    int32_t top_k;
+    int32_t n_sel;            // prefill: rows; decode: batch
+    int32_t q_per_sel;        // prefill 1; decode Qn
+    int32_t Hq, Hkv;
+    float scale;
+    void *out;
+    float *lse;
+    float *partial;           // decode split partials, or null (prefill: no split)
+    int32_t nsplit;
+};
+int32_t attn_decode_splits(int32_t top_k);
+void launch_attn_prefill(const AttnArgs &a, bool bf16, hipStream_t stream);
+void launch_attn_decode(const AttnArgs &a, bool bf16, hipStream_t stream);
+
+}  // namespace qsa
+
+// Launch `kernel` on `stream`; record a failed launch for the calling entry
+// point; bracket the launch with timing events while profiling is on.
+#define QSA_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                  \
+    do {                                                                           \
+        const bool qsa_prof_ = qsa::profiling_enabled();                           \
+        if (qsa_prof_) qsa::prof_begin(name, stream);                              \
+        hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);        \
+        qsa::note_launch(hipGetLastError());                                       \
+        if (qsa_prof_) qsa::prof_end(stream);                                      \
+    } while (0)

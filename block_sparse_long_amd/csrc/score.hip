@@ -1,0 +1,222 @@
+// score.hip -- step a5: block scores raw(t,b), materialized as fp32.
+//
+// "Qwen3.8-Flash-Next: Day-0 Support in SGLang", section "Qwen Sparse
+// Attention", score equation: s_{t,b} = 1/sqrt(128) * sum over the 4 index
+// heads of ReLU(<q_{t,h}, kbar_b>), over the blocks visible to t.  The kernels
+// store the un-scaled sum raw(t,b); the selection ranks raw (the scale is a
+// positive constant) and only reported scores are scaled.
+//
+// bf16 uses the gfx950 MFMA v_mfma_f32_16x16x32_bf16.  Lane l of a wave
+// supplies A[m = l%16][8 k-slots] and B[8 k-slots][n = l%16] and receives
+// C[4*(l/16) + j][l%16], j = 0..3.  A and B take the same 8 k-slots for one
+// lane group l/16, so any one-to-one assignment of head dims to (group, slot)
+// pairs gives the same dot product: lane group g supplies the dims
+// 32g + 8s .. 32g + 8s + 7 at MFMA step s (s = 0..3), i.e. 64 contiguous bytes
+// of a key per lane.
+#include "qsa_device.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+
+constexpr int kChunk = 1024;  // blocks per workgroup in the row-split kernels
+
+__device__ __forceinline__ float relu_sum4(f32x4_t a)
+{
+    return ((fmaxf(a[0], 0.0f) + fmaxf(a[1], 0.0f)) + fmaxf(a[2], 0.0f)) + fmaxf(a[3], 0.0f);
+}
+
+// ---------------------------------------------------------------------------
+// Few rows, many blocks (decode): grid (chunks of 1024 blocks, rows).  The 4
+// index heads sit in MFMA rows 0..3 (rows 4..15 are zero), 16 blocks per MFMA
+// column tile.  HBM-bound: each block's 256 bytes are read once per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void score_rows_bf16_kernel(
+    const bf16_t *__restrict__ qrot, const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_pos,
+    const bf16_t *__restrict__ pooled, int64_t pooled_stride, int32_t max_nb, float *__restrict__ scores,
+    int64_t sc_stride)
+{
+    const int r = blockIdx.y;
+    const int64_t nc = min(visible_blocks(row_pos[r]), (int64_t)max_nb);
+    const int64_t b_begin = (int64_t)blockIdx.x * kChunk;
+    if (b_begin >= nc) return;
+    const int64_t b_end = min(nc, b_begin + (int64_t)kChunk);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    bf16x8_t a[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        a[s] = m < kIdxHeads
+                   ? as_bf16x8(*(const uint4 *)(qrot + ((int64_t)r * kIdxHeads + m) * kDim + 32 * g + 8 * s))
+                   : zero_bf16x8();
+    const bf16_t *kb = pooled + (int64_t)row_seq[r] * pooled_stride;
+    float *srow = scores + (int64_t)r * sc_stride;
+    // each wave handles 64 consecutive blocks per iteration (4 column tiles)
+    for (int64_t base = b_begin + wave * 64; base < b_end; base += 256) {
+        uint4 v[4][4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int64_t b = min(base + nt * 16 + m, b_end - 1);  // clamp: stays inside the visible range
+            const uint4 *src = (const uint4 *)(kb + b * kDim + 32 * g);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) v[nt][s] = src[s];
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], as_bf16x8(v[nt][s]), acc, 0, 0, 0);
+            const int64_t b = base + nt * 16 + m;
+            if (g == 0 && b < b_end) srow[b] = relu_sum4(acc);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32, any number of rows: one thread per block, q~ of the row in LDS.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void score_rows_f32_kernel(
+    const float *__restrict__ qrot, const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_pos,
+    const float *__restrict__ pooled, int64_t pooled_stride, int32_t max_nb, float *__restrict__ scores,
+    int64_t sc_stride)
+{
+    __shared__ float4 qs[kIdxHeads * kDim / 4];
+    const int r = blockIdx.y;
+    const int64_t nc = min(visible_blocks(row_pos[r]), (int64_t)max_nb);
+    const int64_t b_begin = (int64_t)blockIdx.x * kChunk;
+    if (b_begin >= nc) return;
+    const int64_t b_end = min(nc, b_begin + (int64_t)kChunk);
+    for (int i = threadIdx.x; i < kIdxHeads * kDim / 4; i += blockDim.x)
+        qs[i] = ((const float4 *)(qrot + (int64_t)r * kIdxHeads * kDim))[i];
+    __syncthreads();
+    const float *kb = pooled + (int64_t)row_seq[r] * pooled_stride;
+    for (int64_t b = b_begin + threadIdx.x; b < b_end; b += blockDim.x) {
+        const float4 *kr = (const float4 *)(kb + b * kDim);
+        float d[kIdxHeads] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = 0; i < kDim / 4; ++i) {
+            const float4 kv = kr[i];
+#pragma unroll
+            for (int h = 0; h < kIdxHeads; ++h) {
+                const float4 qv = qs[h * (kDim / 4) + i];
+                d[h] = fmaf(qv.x, kv.x, d[h]);
+                d[h] = fmaf(qv.y, kv.y, d[h]);
+                d[h] = fmaf(qv.z, kv.z, d[h]);
+                d[h] = fmaf(qv.w, kv.w, d[h]);
+            }
+        }
+        scores[(int64_t)r * sc_stride + b] =
+            ((fmaxf(d[0], 0.0f) + fmaxf(d[1], 0.0f)) + fmaxf(d[2], 0.0f)) + fmaxf(d[3], 0.0f);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Many rows (prefill), bf16: a GEMM of the rotated queries (rows x 4 heads)
+// against the pooled keys.  One wave owns 16 query rows = 4 MFMA row tiles of
+// (4 rows x 4 heads): MFMA row m of tile mt is query row 4*mt + m/4, head m%4,
+// so the 4 accumulators a lane receives are the 4 heads of one (row, block)
+// pair and the ReLU-sum stays inside the lane.  The 16 x 4 x 128 query tile
+// stays in registers while the wave streams 64 blocks per step; grid.y splits
+// the block range so that the chip has enough waves.  Rows of one wave that
+// belong to different sequences are handled one sequence at a time.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void score_gemm_bf16_kernel(
+    const bf16_t *__restrict__ qrot, const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_pos,
+    int32_t rows, const bf16_t *__restrict__ pooled, int64_t pooled_stride, int32_t max_nb, float *__restrict__ scores,
+    int64_t sc_stride)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * 16;
+    if (row0 >= rows) return;
+    bf16x8_t a[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int64_t qr = row0 + 4 * mt + (m >> 2);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            a[mt][s] = qr < rows ? as_bf16x8(*(const uint4 *)(qrot + (qr * kIdxHeads + (m & 3)) * kDim + 32 * g + 8 * s))
+                                 : zero_bf16x8();
+    }
+    // the output rows this lane writes: row0 + 4*mt + g
+    int64_t my_nc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int64_t qr = row0 + 4 * mt + g;
+        my_nc[mt] = qr < rows ? min(visible_blocks(row_pos[qr]), (int64_t)max_nb) : 0;
+    }
+    const int64_t split_len = ((int64_t)max_nb + gridDim.y - 1) / gridDim.y;
+    const int64_t split_lo = (int64_t)blockIdx.y * split_len;
+    const int64_t split_hi = min((int64_t)max_nb, split_lo + split_len);
+    uint32_t todo = 0;  // bit i: row row0 + i still to do
+    for (int i = 0; i < 16; ++i)
+        if (row0 + i < rows) todo |= 1u << i;
+    while (todo) {  // wave-uniform: one sequence of this wave's rows at a time
+        const int first = __builtin_ctz(todo);
+        const int seq = row_seq[row0 + first];
+        int64_t nb_hi = 0;
+        uint32_t mine = 0;
+        for (int i = 0; i < 16; ++i) {
+            if (((todo >> i) & 1u) && row_seq[row0 + i] == seq) {
+                mine |= 1u << i;
+                nb_hi = max(nb_hi, visible_blocks(row_pos[row0 + i]));
+            }
+        }
+        todo &= ~mine;
+        const int64_t lo = split_lo, hi = min(split_hi, nb_hi);
+        const bf16_t *kb = pooled + (int64_t)seq * pooled_stride;
+        for (int64_t base = lo; base < hi; base += 64) {
+            uint4 v[4][4];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int64_t b = min(base + nt * 16 + m, hi - 1);
+                const uint4 *src = (const uint4 *)(kb + b * kDim + 32 * g);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) v[nt][s] = src[s];
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][s], as_bf16x8(v[nt][s]), acc, 0, 0, 0);
+                    const int64_t b = base + nt * 16 + m;
+                    const int ri = 4 * mt + g;
+                    if (((mine >> ri) & 1u) && b < my_nc[mt] && b < hi)
+                        scores[(row0 + ri) * sc_stride + b] = relu_sum4(acc);
+                }
+            }
+        }
+    }
+}
+
+int64_t score_chunks(int32_t max_nb) { return ((int64_t)max_nb + kChunk - 1) / kChunk; }
+
+void launch_score_rows(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+                       const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores, int64_t sc_stride,
+                       bool bf16, hipStream_t stream)
+{
+    const dim3 grid((unsigned)score_chunks(max_nb), (unsigned)rows), block(256);
+    if (bf16)
+        QSA_LAUNCH("score_rows_bf16", score_rows_bf16_kernel, grid, block, 0, stream, (const bf16_t *)qrot, row_seq,
+                   row_pos, (const bf16_t *)pooled, pooled_stride, max_nb, scores, sc_stride);
+    else
+        QSA_LAUNCH("score_rows_f32", score_rows_f32_kernel, grid, block, 0, stream, (const float *)qrot, row_seq,
+                   row_pos, (const float *)pooled, pooled_stride, max_nb, scores, sc_stride);
+}
+
+void launch_score_gemm(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+                       const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores, int64_t sc_stride,
+                       hipStream_t stream)
+{
+    const int64_t waves = ((int64_t)rows + 15) / 16;
+    const int64_t wgs = (waves + 3) / 4;
+    int64_t split = (2048 + waves - 1) / waves;  // aim at >= 2048 waves on the chip
+    split = max((int64_t)1, min(split, ((int64_t)max_nb + 1023) / 1024));
+    const dim3 grid((unsigned)wgs, (unsigned)split), block(256);
+    QSA_LAUNCH("score_gemm_bf16", score_gemm_bf16_kernel, grid, block, 0, stream, (const bf16_t *)qrot, row_seq,
+               row_pos, rows, (const bf16_t *)pooled, pooled_stride, max_nb, scores, sc_stride);
+}
+
+}  // namespace qsa

@@ -1,0 +1,208 @@
+/*
+ * qsa.h -- C-ABI of libqsa, the MI355X (gfx950) hot path of Qwen Sparse
+ * Attention (QSA).
+ *
+ * Sources (web pages, by title and section):
+ *   [SGL]  "Qwen3.8-Flash-Next: Day-0 Support in SGLang", section "Qwen Sparse
+ *          Attention: Retrieve Coarsely, Attend Precisely" (indexer pooling
+ *          c4, post-pool rotation, score equation s_{t,b}, best 512 blocks,
+ *          2048 token positions plus the zero-to-three tail tokens, attention
+ *          on the original K/V) and section "IndexShare MTP" (draft rows
+ *          reuse one selection plus the positions drafted since).
+ *   [ARCH] "Qwen3.8-Flash-Next architecture" guide, "How a token moves through
+ *          the model", item 2 (RoPE after key pooling; 512 blocks = 2,048
+ *          tokens plus the incomplete tail block).
+ *   [LBL]  "Qwen3.8-Flash-Next, Layer by Layer", section "Token mixing" (4 query
+ *          heads and 1 key head of 128 dims, mean of every 4 keys, best 512).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a device pointer (hipMalloc'd or equivalent).
+ *     The caller owns every buffer; the library allocates no device memory,
+ *     keeps no pointer after returning, and holds no state besides the
+ *     optional timing records below.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *     asynchronous on that stream; the library never synchronizes.  Inputs
+ *     must stay alive until the stream has passed the call.
+ *   - Strides and sizes count elements, not bytes.  Tensors are read with
+ *     16-byte vector loads: their base pointers must be 16-byte aligned and
+ *     their strides multiples of 8 elements.
+ *   - Arguments are validated on the host before any HIP call.  A rejected
+ *     call returns its status and launches nothing.  Calls with nothing to do
+ *     (zero rows, an empty block range) return QSA_OK and launch nothing.
+ *   - Data-dependent contracts (positions inside the caches, pooled blocks
+ *     present for every visible block, kept block ids below the row's visible
+ *     count) are the caller's; they are not checked.
+ *   - Index-key dim 128, 4 indexer heads, 4 tokens per block ([SGL], [LBL]);
+ *     the attention head dim must be 128.
+ *   - A block b is visible to a query at position t when it is complete:
+ *     4b + 3 <= t, i.e. b < nc(t) = floor((t+1)/4) ([SGL]: the visible
+ *     compressed blocks plus the zero-to-three tail tokens).
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QSA_OK = 0,
+    QSA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, stride or flag */
+    QSA_ERR_UNSUPPORTED = 2, /* dtype or head shape the library does not implement */
+    QSA_ERR_WORKSPACE = 3,   /* workspace smaller than the matching *_workspace_size() */
+    QSA_ERR_DEVICE = 4       /* a HIP call or kernel launch failed */
+} qsa_status_t;
+
+typedef enum {
+    QSA_F32 = 0,  /* IEEE binary32 everywhere */
+    QSA_BF16 = 1  /* bfloat16 storage; FP32 accumulation inside the kernels */
+} qsa_dtype_t;
+
+enum {
+    QSA_FLAG_NO_ROPE = 1u << 0,       /* skip both rotations (keys and index queries) */
+    QSA_FLAG_POOL_RMSNORM = 1u << 1,  /* pooled key -> x / sqrt(mean(x^2) + 1e-6) before RoPE */
+    /* qsa_score_topk only: pick the scoring kernel instead of the library's
+     * choice (per-row streaming for few rows, the MFMA GEMM for many rows).
+     * The result does not depend on it; tests and tuning use it. */
+    QSA_FLAG_SCORE_ROWS = 1u << 8,
+    QSA_FLAG_SCORE_GEMM = 1u << 9
+};
+
+#define QSA_INDEX_DIM 128
+#define QSA_INDEX_HEADS 4
+#define QSA_BLOCK_TOKENS 4
+#define QSA_MAX_TOP_K 4096
+#define QSA_MAX_QUERY_GROUP 64 /* query rows sharing a selection x (Hq / Hkv) */
+
+/*
+ * Steps a1-a3 ([SGL] pooling; [ARCH] item 2 rotation order): for every
+ * sequence s < batch and block b in [block_begin, block_end), average the
+ * four raw index keys of tokens 4b..4b+3 in FP32 (sum in token order, times
+ * 1/4), optionally RMS-normalize (QSA_FLAG_POOL_RMSNORM), rotate with RoPE at
+ * position 4b (pairs (j, j+64), angle 4b * rope_theta^(-j/64), formed in
+ * double precision), and store the result rounded to `dtype` (nearest-even).
+ *
+ *   raw_keys  [batch][raw_seq_stride]: token i of sequence s at
+ *             raw_keys + s*raw_seq_stride + i*128.  Read only.
+ *   pooled    [batch][pooled_seq_stride]: block b at pooled + s*stride + b*128.
+ *             Blocks outside [block_begin, block_end) are not touched.
+ *   Requirements: raw_seq_stride >= 4*block_end*128 and pooled_seq_stride >=
+ *   block_end*128 when batch > 1, both multiples of 8; rope_theta > 1 unless
+ *   QSA_FLAG_NO_ROPE.
+ */
+qsa_status_t qsa_pool_index_keys(const void *raw_keys, int64_t raw_seq_stride, void *pooled,
+                                 int64_t pooled_seq_stride, int32_t batch, int32_t block_begin,
+                                 int32_t block_end, double rope_theta, uint32_t flags,
+                                 qsa_dtype_t dtype, void *stream);
+
+/*
+ * Bytes of device workspace qsa_score_topk needs for `rows` rows whose visible
+ * block counts are at most `max_visible_blocks`.  0 when rows == 0.
+ */
+size_t qsa_score_topk_workspace_size(int32_t rows, int32_t max_visible_blocks, int32_t top_k,
+                                     qsa_dtype_t dtype);
+
+/*
+ * Steps a4-a6 ([SGL] score equation and top-512; [LBL]).  For every row r with
+ * sequence s = row_seq[r] and position t = row_pos[r]:
+ *   - q~_h = round_dtype(RoPE(q_index[r][h], t)) for the 4 index heads;
+ *   - raw(t,b) = sum_h max(0, <q~_h, pooled[s][b]>) for the visible blocks
+ *     b < nc(t);
+ *   - keep all visible blocks if nc(t) <= top_k, else the top_k best under
+ *     (raw descending, block ascending).
+ *   sel_blocks [rows][top_k] (out): kept blocks ascending, padded with -1.
+ *   sel_count  [rows] (out): number kept = min(top_k, nc(t)).
+ *   sel_scores [rows][top_k] (out, may be NULL): s_{t,b} = raw / sqrt(128) of
+ *              each kept block, in the order of sel_blocks (0 for padding).
+ *   q_index    [rows][4][128], un-rotated.  row_seq, row_pos: device int32.
+ *   pooled     as written by qsa_pool_index_keys.
+ *   max_visible_blocks: an upper bound of nc(row_pos[r]) over all rows; it
+ *              sizes the grid and the workspace (positions live on the device,
+ *              so the host cannot read them without a synchronization).
+ *   workspace: device memory of at least qsa_score_topk_workspace_size()
+ *              bytes, 256-byte aligned; its contents on entry do not matter.
+ *   1 <= top_k <= QSA_MAX_TOP_K.  flags: QSA_FLAG_NO_ROPE, QSA_FLAG_SCORE_*.
+ */
+qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const int32_t *row_pos,
+                            int32_t rows, const void *pooled, int64_t pooled_seq_stride,
+                            int32_t max_visible_blocks, int32_t top_k, double rope_theta,
+                            uint32_t flags, qsa_dtype_t dtype, int32_t *sel_blocks,
+                            int32_t *sel_count, float *sel_scores, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * Steps a7+a8 ([SGL]: expansion of the kept blocks to token positions, the
+ * zero-to-three tail tokens, attention on the original K/V).  Row r (sequence
+ * row_seq[r], position t = row_pos[r]) attends P = {4b+i : b in
+ * sel_blocks[r][0..sel_count[r]), i < 4} U [4*nc(t), t]; query head h uses KV
+ * head floor(h / (Hq/Hkv)); out = softmax(softmax_scale * q K_P^T) V_P.
+ *   q        [rows][Hq][D]; k_cache, v_cache [B][kv_seq_stride]: token p of
+ *            sequence s, KV head g at s*kv_seq_stride + (p*Hkv + g)*D.
+ *   sel_blocks [rows][top_k], sel_count [rows] as written by qsa_score_topk.
+ *   out      [rows][Hq][D], dtype.  lse [rows][Hq] fp32 natural-log
+ *            log-sum-exp of the scaled logits, or NULL.
+ *   D == 128; Hq % Hkv == 0; Hq/Hkv <= QSA_MAX_QUERY_GROUP;
+ *   1 <= top_k <= QSA_MAX_TOP_K.
+ */
+qsa_status_t qsa_sparse_attn_prefill(const void *q, const int32_t *row_seq, const int32_t *row_pos,
+                                     int32_t rows, const void *k_cache, const void *v_cache,
+                                     int64_t kv_seq_stride, const int32_t *sel_blocks,
+                                     const int32_t *sel_count, int32_t top_k, int32_t Hq,
+                                     int32_t Hkv, int32_t D, float softmax_scale,
+                                     qsa_dtype_t dtype, void *out, float *lse, void *stream);
+
+/*
+ * Bytes of device workspace qsa_sparse_attn_decode needs (fp32 partial
+ * softmax states, one per row, head and split of the positions).
+ */
+size_t qsa_sparse_attn_decode_workspace_size(int32_t batch, int32_t q_per_seq, int32_t Hq,
+                                             int32_t D, int32_t top_k);
+
+/*
+ * Steps a7+a9 ([SGL] attention on the original K/V; [SGL] "IndexShare MTP":
+ * rows of one sequence share that sequence's selection plus the positions
+ * since it was taken).  Row j of sequence s sits at t = row_pos[s][j] and
+ * attends P = {4b+i : b in sel_blocks[s][0..sel_count[s]), i < 4} U
+ * [tail_start[s], t].  tail_start == NULL means 4*nc(t) for every row (plain
+ * decode).  Contract: every position in P is < the cache length, and
+ * tail_start[s] >= 4*(largest kept block + 1).
+ *   q, out   [batch][q_per_seq][Hq][D]; lse [batch][q_per_seq][Hq] or NULL.
+ *   row_pos  [batch][q_per_seq]; tail_start [batch] or NULL.
+ *   sel_blocks [batch][top_k], sel_count [batch].
+ *   workspace: at least qsa_sparse_attn_decode_workspace_size() bytes,
+ *   256-byte aligned.  q_per_seq * (Hq/Hkv) <= QSA_MAX_QUERY_GROUP.
+ *   Other arguments as in qsa_sparse_attn_prefill.
+ */
+qsa_status_t qsa_sparse_attn_decode(const void *q, const int32_t *row_pos, int32_t batch,
+                                    int32_t q_per_seq, const int32_t *tail_start,
+                                    const void *k_cache, const void *v_cache,
+                                    int64_t kv_seq_stride, const int32_t *sel_blocks,
+                                    const int32_t *sel_count, int32_t top_k, int32_t Hq,
+                                    int32_t Hkv, int32_t D, float softmax_scale,
+                                    qsa_dtype_t dtype, void *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *qsa_status_string(qsa_status_t status);
+
+/*
+ * Kernel timing, for benchmarks.  While enabled, every kernel the library
+ * launches is bracketed by a pair of hipEvents recorded on its stream.
+ * qsa_profile_kernel_ms() waits for the recorded events, then returns how many
+ * launches of kernel `name` were recorded and their total duration in
+ * milliseconds (*total_ms).  qsa_profile_reset() drops the records.  A kernel
+ * name not launched returns 0.  Timing is off by default and costs nothing
+ * then.  Not thread-safe: enable it from one host thread at a time.
+ */
+qsa_status_t qsa_profile_enable(int enable);
+qsa_status_t qsa_profile_reset(void);
+int32_t qsa_profile_kernel_ms(const char *name, double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -1,0 +1,142 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every symbol
+include/qsa.h declares, and rejects bad arguments on the host before any HIP
+call (so none of these calls touches a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_long_amd import qsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "qsa.h")
+
+# fake, 256-byte aligned "device" addresses: validation never dereferences them
+A = 0x10000
+B_ = 0x20000
+C = 0x30000
+MIS = 0x10008  # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HDR).read()
+    return sorted(set(re.findall(r"\b(qsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_exports(libqsa):
+    decl = declared_functions()
+    assert set(decl) == set(qsa.EXPORTS)
+    for name in decl:
+        assert hasattr(libqsa, name), name
+
+
+def test_exports_are_c_symbols(libqsa):
+    raw = ctypes.CDLL(qsa.LIB_PATH)
+    for name in declared_functions():
+        assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value
+
+
+def test_status_strings(libqsa):
+    assert qsa.status_string(qsa.OK) == "ok"
+    assert "workspace" in qsa.status_string(qsa.ERR_WORKSPACE)
+    assert qsa.status_string(99) == "unknown status"
+
+
+def test_pool_validation(libqsa):
+    f = libqsa.qsa_pool_index_keys
+    # empty work -> OK, no launch
+    assert f(A, 1024, B_, 256, 0, 0, 2, 1e7, 0, qsa.BF16, None) == qsa.OK
+    assert f(A, 1024, B_, 256, 2, 3, 3, 1e7, 0, qsa.BF16, None) == qsa.OK
+    assert f(A, 1024, B_, 256, 2, 0, 2, 1e7, 0, 7, None) == qsa.ERR_UNSUPPORTED
+    assert f(None, 1024, B_, 256, 2, 0, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG
+    assert f(MIS, 1024, B_, 256, 2, 0, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG
+    assert f(A, 1024, B_, 256, 2, 2, 1, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG  # end < begin
+    assert f(A, 1024, B_, 256, -1, 0, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG
+    assert f(A, 1020, B_, 256, 2, 0, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG  # stride % 8
+    assert f(A, 512, B_, 256, 2, 0, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG   # raw stride short
+    assert f(A, 1024, B_, 128, 2, 0, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG  # pooled short
+    assert f(A, 1024, B_, 256, 2, 0, 2, 0.5, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG  # theta
+    assert f(A, 1024, B_, 256, 2, 0, 2, 1e7, 1 << 5, qsa.BF16, None) == qsa.ERR_INVALID_ARG  # flag
+
+
+def test_score_topk_validation(libqsa):
+    f = libqsa.qsa_score_topk
+    ws = qsa.score_topk_workspace_size(4, 100, 16, qsa.BF16)
+    assert ws > 0 and qsa.score_topk_workspace_size(0, 100, 16, qsa.BF16) == 0
+    good = dict(q=A, seq=B_, pos=C, rows=4, pooled=A, stride=128 * 100, nb=100, k=16, theta=1e7,
+                flags=0, dt=qsa.BF16, sel=B_, cnt=C, sc=None, ws=0x100000, wsb=ws)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["q"], a["seq"], a["pos"], a["rows"], a["pooled"], a["stride"], a["nb"], a["k"],
+                 a["theta"], a["flags"], a["dt"], a["sel"], a["cnt"], a["sc"], a["ws"], a["wsb"], None)
+
+    assert call(rows=0) == qsa.OK
+    assert call(wsb=ws - 1) == qsa.ERR_WORKSPACE
+    assert call(ws=0x100010) == qsa.ERR_INVALID_ARG      # workspace not 256-aligned
+    assert call(k=0) == qsa.ERR_INVALID_ARG
+    assert call(k=qsa.MAX_TOP_K + 1) == qsa.ERR_INVALID_ARG
+    assert call(q=None) == qsa.ERR_INVALID_ARG
+    assert call(q=MIS) == qsa.ERR_INVALID_ARG
+    assert call(sel=None) == qsa.ERR_INVALID_ARG
+    assert call(nb=-1) == qsa.ERR_INVALID_ARG
+    assert call(dt=5) == qsa.ERR_UNSUPPORTED
+    assert call(flags=qsa.FLAG_SCORE_ROWS | qsa.FLAG_SCORE_GEMM) == qsa.ERR_INVALID_ARG
+    assert call(flags=qsa.FLAG_SCORE_GEMM, dt=qsa.F32,
+                wsb=qsa.score_topk_workspace_size(4, 100, 16, qsa.F32)) == qsa.ERR_UNSUPPORTED
+    assert call(flags=qsa.FLAG_POOL_RMSNORM) == qsa.ERR_INVALID_ARG  # pooling flag, not a score flag
+    assert call(theta=float("nan")) == qsa.ERR_INVALID_ARG
+
+
+def test_attn_validation(libqsa):
+    fp = libqsa.qsa_sparse_attn_prefill
+    # rows == 0 -> OK without touching anything
+    assert fp(None, None, None, 0, None, None, 0, None, None, 512, 8, 1, 128, 0.1, qsa.BF16, None, None,
+              None) == qsa.OK
+    args = [A, B_, C, 4, A, B_, 1024, C, A, 512, 8, 1, 128, 0.1, qsa.BF16, B_, None, None]
+
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return fp(*a)
+
+    assert fp(*args[:12], 64, *args[13:]) == qsa.ERR_UNSUPPORTED       # D != 128
+    assert call(11, 3) == qsa.ERR_INVALID_ARG                          # Hq % Hkv
+    assert call(10, 128) == qsa.ERR_UNSUPPORTED                        # group of 128 heads
+    assert call(9, 0) == qsa.ERR_INVALID_ARG                           # top_k
+    assert call(0, MIS) == qsa.ERR_INVALID_ARG
+    assert call(6, 1001) == qsa.ERR_INVALID_ARG                        # kv stride % 8
+    assert call(14, 9) == qsa.ERR_UNSUPPORTED
+    assert call(13, float("inf")) == qsa.ERR_INVALID_ARG
+
+    fd = libqsa.qsa_sparse_attn_decode
+    ws = qsa.sparse_attn_decode_workspace_size(4, 4, 8, 128, 512)
+    assert ws == 4 * 4 * 8 * (4 * 512 // 64 + 1) * 130 * 4
+    d = [A, B_, 4, 4, None, A, B_, 1024, C, A, 512, 8, 1, 128, 0.1, qsa.BF16, B_, None, 0x100000, ws, None]
+
+    def dcall(i, v):
+        a = list(d)
+        a[i] = v
+        return fd(*a)
+
+    assert dcall(19, ws - 1) == qsa.ERR_WORKSPACE
+    assert dcall(3, 9) == qsa.ERR_UNSUPPORTED                          # 9 rows x 8 heads > 64
+    assert dcall(3, 0) == qsa.ERR_INVALID_ARG
+    assert dcall(2, 0) == qsa.OK
+    assert dcall(18, 0x100004) == qsa.ERR_INVALID_ARG
+    assert dcall(1, None) == qsa.ERR_INVALID_ARG
+
+
+def test_profile_api_without_launches(libqsa):
+    qsa.profile_enable(True)
+    qsa.profile_reset()
+    assert qsa.profile_kernel_ms("score_rows_bf16") == (0, 0.0)
+    qsa.profile_enable(False)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(qsa, "LIB_PATH", str(tmp_path / "libqsa.so"))
+    monkeypatch.setattr(qsa, "_lib", None)
+    with pytest.raises(qsa.QsaLibraryMissing):
+        qsa.load()

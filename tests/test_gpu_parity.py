@@ -1,0 +1,277 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU oracle, element by
+element, on seeded inputs that span several tiles and end in ragged tails.
+
+Tolerances: pooled keys within 1 bf16 ulp (bit-exact on integer inputs with
+RoPE off); selections identical except near-ties within 1e-3 relative of the
+k-th score, and identical with no exception on integer inputs; attention
+output within 2e-2 abs + 1e-2 rel in bf16 and 1e-4 in fp32.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from block_sparse_long_amd import qsa, synth
+from helpers import as_float, assert_close_out, check_selection, dev, host
+
+pytestmark = pytest.mark.gpu
+
+DIM = 128
+THETA = 1.0e7
+
+
+def _store(x, dtype):
+    return synth.bf16_bits(x.astype(np.float32)) if dtype == "bf16" else x.astype(np.float32)
+
+
+def _code(dtype):
+    return qsa.BF16 if dtype == "bf16" else qsa.F32
+
+
+def _random_selection(rng, pos, k):
+    """A valid selection per row: min(k, nc) distinct blocks < nc, ascending."""
+    R = len(pos)
+    sel = np.full((R, k), -1, np.int32)
+    cnt = np.zeros(R, np.int32)
+    for r, t in enumerate(pos):
+        nc = (int(t) + 1) // 4
+        n = min(k, nc)
+        if n:
+            sel[r, :n] = np.sort(rng.choice(nc, size=n, replace=False))
+        cnt[r] = n
+    return sel, cnt
+
+
+# ---------------------------------------------------------------------------
+# a1-a3 pooling
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("flags", [0, qsa.FLAG_NO_ROPE, qsa.FLAG_POOL_RMSNORM])
+def test_pool_matches_oracle(gpu, dtype, flags):
+    rng = np.random.default_rng(100 + flags)
+    B, NB = 2, 517
+    L = 4 * NB + 3                                  # a ragged, incomplete last block
+    raw = _store(rng.standard_normal((B, L, DIM)) * 2.0, dtype)
+    want = oracle.pool(raw, 0, NB, THETA, flags)
+    pooled = dev(np.zeros((B, NB, DIM), raw.dtype), dtype)
+    qsa.pool_index_keys(dev(raw, dtype), pooled, 0, NB, THETA, flags)
+    got = host(pooled)
+    if dtype == "bf16":
+        diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
+        assert diff.max() <= 1 and (diff == 0).mean() > 0.999
+    else:
+        np.testing.assert_allclose(got, want, rtol=2e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_pool_block_range_only(gpu, dtype):
+    rng = np.random.default_rng(7)
+    B, NB = 3, 300
+    raw = _store(rng.standard_normal((B, 4 * NB, DIM)), dtype)
+    sentinel = _store(np.full((B, NB, DIM), 3.25), dtype)
+    pooled = dev(sentinel, dtype)
+    qsa.pool_index_keys(dev(raw, dtype), pooled, 97, 211, THETA)
+    got = host(pooled)
+    want = oracle.pool(raw, 97, 211, THETA, pooled=sentinel.copy())
+    np.testing.assert_array_equal(got[:, :97], sentinel[:, :97])
+    np.testing.assert_array_equal(got[:, 211:], sentinel[:, 211:])
+    if dtype == "bf16":
+        assert np.abs(got.astype(np.int32) - want.astype(np.int32)).max() <= 1
+    else:
+        np.testing.assert_allclose(got, want, rtol=2e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_pool_integer_inputs_bit_exact(gpu, dtype):
+    rng = np.random.default_rng(8)
+    raw = _store(rng.integers(-8, 9, size=(2, 4 * 333, DIM)).astype(np.float32), dtype)
+    want = oracle.pool(raw, 0, 333, THETA, qsa.FLAG_NO_ROPE)
+    pooled = dev(np.zeros((2, 333, DIM), raw.dtype), dtype)
+    qsa.pool_index_keys(dev(raw, dtype), pooled, 0, 333, THETA, qsa.FLAG_NO_ROPE)
+    np.testing.assert_array_equal(host(pooled), want)
+
+
+# ---------------------------------------------------------------------------
+# a4-a6 scoring and selection
+# ---------------------------------------------------------------------------
+
+PATHS = {"rows": qsa.FLAG_SCORE_ROWS, "gemm": qsa.FLAG_SCORE_GEMM}
+
+
+def _score_case(seed, dtype, B, NB, R, k, integer=False):
+    rng = np.random.default_rng(seed)
+    if integer:
+        base = rng.integers(-4, 5, size=(7, DIM)).astype(np.float32)
+        pooled = base[rng.integers(0, 7, size=(B, NB))]          # few distinct keys -> exact ties
+        iq = rng.integers(-3, 4, size=(R, 4, DIM)).astype(np.float32)
+    else:
+        pooled = rng.standard_normal((B, NB, DIM)).astype(np.float32)
+        iq = rng.standard_normal((R, 4, DIM)).astype(np.float32)
+    pooled, iq = _store(pooled, dtype), _store(iq, dtype)
+    seq = rng.integers(0, B, R).astype(np.int32)
+    pos = rng.integers(0, 4 * NB, R).astype(np.int32)
+    pos[:3] = [0, 4 * k - 2, 4 * NB - 1]          # no block, just below k blocks, every block
+    return pooled, iq, seq, pos
+
+
+@pytest.mark.parametrize("dtype,path", [("bf16", "rows"), ("bf16", "gemm"), ("f32", "rows")])
+@pytest.mark.parametrize("k", [512, 37])
+def test_score_topk_matches_oracle(gpu, dtype, path, k):
+    B, NB, R = 2, 2600, 90
+    pooled, iq, seq, pos = _score_case(11 + k, dtype, B, NB, R, k)
+    o_sel, o_cnt, o_sc, o_raw = oracle.score_topk(iq, seq, pos, pooled, k, THETA, want_raw=True)
+    sel, cnt, sc = qsa.score_topk(dev(iq, dtype), dev(seq, "i"), dev(pos, "i"), dev(pooled, dtype), NB, k,
+                                  THETA, flags=PATHS[path])
+    g_sel, g_cnt, g_sc = host(sel), host(cnt), host(sc)
+    check_selection(g_sel, g_cnt, o_sel, o_cnt, o_raw, exact=False)
+    for r in range(R):
+        n = g_cnt[r]
+        want = o_raw[r, g_sel[r, :n]] / math.sqrt(128)
+        np.testing.assert_allclose(g_sc[r, :n], want, rtol=1e-3, atol=1e-3)
+        assert np.all(g_sc[r, n:] == 0)
+
+
+@pytest.mark.parametrize("dtype,path", [("bf16", "rows"), ("bf16", "gemm"), ("f32", "rows")])
+def test_score_topk_integer_inputs_bit_exact(gpu, dtype, path):
+    B, NB, R, k = 2, 1500, 80, 64
+    pooled, iq, seq, pos = _score_case(5, dtype, B, NB, R, k, integer=True)
+    o_sel, o_cnt, o_sc, o_raw = oracle.score_topk(iq, seq, pos, pooled, k, THETA, qsa.FLAG_NO_ROPE,
+                                                  want_raw=True)
+    sel, cnt, sc = qsa.score_topk(dev(iq, dtype), dev(seq, "i"), dev(pos, "i"), dev(pooled, dtype), NB, k,
+                                  THETA, flags=qsa.FLAG_NO_ROPE | PATHS[path])
+    np.testing.assert_array_equal(host(cnt), o_cnt)
+    np.testing.assert_array_equal(host(sel), o_sel)       # ties resolved to the lower block, exactly
+    np.testing.assert_array_equal(host(sc), o_sc)
+
+
+def test_score_topk_default_paths_agree(gpu):
+    # few rows take the streaming scorer, many rows the GEMM: same answer
+    B, NB, R, k = 1, 3000, 130, 100
+    pooled, iq, seq, pos = _score_case(21, "bf16", B, NB, R, k)
+    args = (dev(iq, "bf16"), dev(seq, "i"), dev(pos, "i"), dev(pooled, "bf16"), NB, k, THETA)
+    a = [host(x) for x in qsa.score_topk(*args)]
+    b = [host(x) for x in qsa.score_topk(*args, flags=qsa.FLAG_SCORE_ROWS)]
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# a7-a9 attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (16, 2), (4, 4)])
+def test_attn_prefill_matches_oracle(gpu, dtype, Hq, Hkv):
+    rng = np.random.default_rng(30 + Hq + Hkv)
+    L, R, k = 4 * 700 + 2, 70, 64
+    pos = np.sort(rng.choice(L, R, replace=False)).astype(np.int32)
+    pos[:4] = [0, 1, 2, 3]                        # tails of 1..3 tokens, one complete block
+    seq = np.zeros(R, np.int32)
+    sel, cnt = _random_selection(rng, pos, k)
+    q = _store(rng.standard_normal((R, Hq, DIM)), dtype)
+    kc = _store(rng.standard_normal((1, L, Hkv, DIM)), dtype)
+    vc = _store(rng.standard_normal((1, L, Hkv, DIM)), dtype)
+    want, want_lse = oracle.sparse_attn_prefill(q, seq, pos, kc, vc, sel, cnt)
+    out, lse = qsa.sparse_attn_prefill(dev(q, dtype), dev(seq, "i"), dev(pos, "i"), dev(kc, dtype),
+                                       dev(vc, dtype), dev(sel, "i"), dev(cnt, "i"))
+    assert_close_out(host(out), want, dtype)
+    np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Qn,Hq,Hkv,draft", [(1, 8, 1, False), (4, 8, 1, True), (2, 16, 2, True),
+                                             (3, 4, 2, False)])
+def test_attn_decode_matches_oracle(gpu, dtype, Qn, Hq, Hkv, draft):
+    rng = np.random.default_rng(40 + Qn * Hq)
+    B, ctx, k = 3, 4 * 900 + 1, 128
+    L = ctx + (Qn if draft else 0)
+    if draft:  # IndexShare rows after the anchor at ctx - 1
+        rp = (ctx + np.tile(np.arange(Qn), (B, 1))).astype(np.int32)
+        ts = np.full(B, 4 * (ctx // 4), np.int32)
+        anchor = np.full(B, ctx - 1, np.int32)
+    else:      # independent rows at (possibly) different positions, own tails
+        rp = rng.integers(4 * k, ctx, size=(B, Qn)).astype(np.int32)
+        ts = None
+        anchor = rp.min(1)
+    sel, cnt = _random_selection(rng, anchor, k)
+    cnt[1] = 5                                     # a short selection
+    sel[1, 5:] = -1
+    q = _store(rng.standard_normal((B, Qn, Hq, DIM)), dtype)
+    kc = _store(rng.standard_normal((B, L, Hkv, DIM)), dtype)
+    vc = _store(rng.standard_normal((B, L, Hkv, DIM)), dtype)
+    want, want_lse = oracle.sparse_attn_decode(q, rp, kc, vc, sel, cnt, ts)
+    out, lse = qsa.sparse_attn_decode(dev(q, dtype), dev(rp, "i"), dev(kc, dtype), dev(vc, dtype),
+                                      dev(sel, "i"), dev(cnt, "i"),
+                                      None if ts is None else dev(ts, "i"))
+    assert_close_out(host(out), want, dtype)
+    np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
+
+
+# ---------------------------------------------------------------------------
+# the whole path on scaled-down copies of the five workloads
+# ---------------------------------------------------------------------------
+
+SCALED = {
+    "decode-8k-f32": dict(ctx=4 * 1200 + 2),
+    "prefill-32k": dict(ctx=4 * 700, chunk=4 * 700),
+    "decode-128k": dict(batch=5, ctx=4 * 2500 + 3),
+    "chunk-256k": dict(ctx=4 * 3000, chunk=150, n_plant=60),
+    "decode-1m-draft": dict(ctx=4 * 3000),
+}
+
+
+@pytest.mark.parametrize("name", synth.CONFIG_ORDER)
+def test_whole_path_scaled(gpu, name):
+    spec = synth.scaled(name, **SCALED[name])
+    w = synth.make(spec)
+    dt = spec.dtype
+    B, nb, k = spec.batch, spec.n_blocks, spec.top_k
+    # a1-a3
+    pooled_d = dev(np.zeros((B, nb, DIM), w["raw_keys"].dtype), dt)
+    qsa.pool_index_keys(dev(w["raw_keys"], dt), pooled_d, 0, nb, spec.theta)
+    pooled = host(pooled_d)
+    o_pooled = oracle.pool(w["raw_keys"], 0, nb, spec.theta)
+    if dt == "bf16":
+        assert np.abs(pooled.astype(np.int32) - o_pooled.astype(np.int32)).max() <= 1
+    else:
+        np.testing.assert_allclose(pooled, o_pooled, rtol=2e-6, atol=1e-6)
+    # a4-a6 (the oracle scores the GPU's pooled keys, so pooling rounding does not cascade)
+    max_nb = int((w["row_pos"].max() + 1) // 4)
+    sel, cnt, _ = qsa.score_topk(dev(w["idx_q"], dt), dev(w["row_seq"], "i"), dev(w["row_pos"], "i"),
+                                 pooled_d, max_nb, k, spec.theta)
+    o_sel, o_cnt, _, o_raw = oracle.score_topk(w["idx_q"], w["row_seq"], w["row_pos"], pooled, k,
+                                               spec.theta, want_raw=True)
+    g_sel, g_cnt = host(sel), host(cnt)
+    check_selection(g_sel, g_cnt, o_sel, o_cnt, o_raw, exact=False)
+    # planted blocks are found
+    if spec.kind == "decode":
+        for s in range(B):
+            planted = set(w["planted"][s].tolist())
+            got = set(g_sel[s, :g_cnt[s]].tolist())
+            assert planted <= got if len(planted) <= k else got <= planted
+    # a7-a9 on the GPU's own selection
+    if spec.kind == "decode":
+        ts = None if w["tail_start"] is None else dev(w["tail_start"], "i")
+        out, lse = qsa.sparse_attn_decode(dev(w["q"], dt), dev(w["attn_pos"], "i"), dev(w["k_cache"], dt),
+                                          dev(w["v_cache"], dt), sel, cnt, ts)
+        want, want_lse = oracle.sparse_attn_decode(w["q"], w["attn_pos"], w["k_cache"], w["v_cache"], g_sel,
+                                                   g_cnt, w["tail_start"])
+    else:
+        out, lse = qsa.sparse_attn_prefill(dev(w["q"], dt), dev(w["row_seq"], "i"), dev(w["row_pos"], "i"),
+                                           dev(w["k_cache"], dt), dev(w["v_cache"], dt), sel, cnt)
+        want, want_lse = oracle.sparse_attn_prefill(w["q"], w["row_seq"], w["row_pos"], w["k_cache"],
+                                                    w["v_cache"], g_sel, g_cnt)
+    assert_close_out(host(out), want, dt)
+    np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
+
+
+def test_empty_calls_launch_nothing(gpu):
+    import torch
+    e = torch.empty((0, 4, DIM), dtype=torch.bfloat16, device="cuda")
+    i = torch.empty((0,), dtype=torch.int32, device="cuda")
+    pooled = torch.zeros((1, 8, DIM), dtype=torch.bfloat16, device="cuda")
+    sel, cnt, sc = qsa.score_topk(e, i, i, pooled, 8, 16, THETA)
+    assert sel.shape == (0, 16)
+    torch.cuda.synchronize()
