@@ -1,0 +1,365 @@
+"""Throughput of the QSA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--decode-workload NAME|none] [--no-cpu-baseline]
+
+Prints ONE JSON line.  The headline is prefill: one step is a whole pass of
+the prefill path (pool the chunk's new blocks -> rotate index queries, score,
+top-512 -> sparse attention) over the 8,192-token chunk at the end of a
+262,144-token context; `value` is chunk tokens per second.  The decode
+workload (4 sequences x 4 draft rows sharing one selection at 1,048,576
+tokens) is timed in the same run and reported under "decode" in query rows
+per second.  Inputs are seeded synthetic tensors resident in HBM before the
+timed region; decode rotates three copies of its pooled keys and K/V so the
+256 MiB Infinity Cache cannot serve a step from the previous one.
+
+"roofline" is the dominant kernel's achieved rate (algorithmic flops or bytes
+per launch / its average duration, from hipEvents the library records around
+each launch on the launch stream) against MI355X's datasheet peak.
+"cpu_baseline" is the CPU oracle, untuned, timed on a bounded sample of the
+same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QSA prefill tokens/s @256K + decode queries/s @1M; % of HBM/MFMA peak"
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, datasheet
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA, datasheet
+PEAK_F32_VALU_TFLOPS = 157.3
+DIM = 128
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)
+    return t.cuda()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work per launch (what the method must compute / move)
+# ---------------------------------------------------------------------------
+
+def visible(t):
+    return (np.asarray(t, np.int64) + 1) // 4
+
+
+def positions_per_row(nc, t, k, tail_start=None):
+    nc = np.asarray(nc, np.int64)
+    t = np.asarray(t, np.int64)
+    ts = 4 * nc if tail_start is None else np.asarray(tail_start, np.int64)
+    return 4 * np.minimum(nc, k) + np.maximum(t - ts + 1, 0)
+
+
+def prefill_work(spec, row_pos):
+    eb = 2 if spec.dtype == "bf16" else 4
+    nc = visible(row_pos)
+    pairs = int(nc.sum())
+    npos = positions_per_row(nc, row_pos, spec.top_k)
+    new_blocks = spec.chunk // 4
+    return {
+        "pool_rope": ("hbm", new_blocks * (4 + 1) * DIM * eb, "B"),
+        "score_gemm_bf16": ("mfma", 2.0 * 4 * DIM * pairs, "flop"),
+        "score_rows_bf16": ("hbm", float(pairs) * DIM * eb, "B"),
+        "select_rows": ("hbm", 4.0 * pairs, "B"),   # scans the fp32 scores once
+        "attn_prefill": ("alu", 4.0 * spec.Hq * DIM * float(npos.sum()), "flop"),
+    }, pairs, float(npos.sum())
+
+
+def decode_work(spec, anchor_pos, attn_pos, tail_start):
+    eb = 2 if spec.dtype == "bf16" else 4
+    nc = visible(anchor_pos)
+    pairs = int(nc.sum())
+    # K and V rows of each sequence's positions, read once per sequence
+    kv_bytes = 0.0
+    for s in range(spec.batch):
+        P = 4 * min(int(nc[s]), spec.top_k)
+        ts = int(tail_start[s]) if tail_start is not None else 4 * int(visible(attn_pos[s]).min())
+        P += max(int(np.max(attn_pos[s])) - ts + 1, 0)
+        kv_bytes += 2.0 * P * spec.Hkv * DIM * eb
+    q_bytes = 2.0 * spec.batch * spec.q_per_seq * spec.Hq * DIM * eb
+    kind = "score_rows_bf16" if spec.dtype == "bf16" else "score_rows_f32"
+    return {
+        kind: ("hbm", float(pairs) * DIM * eb, "B"),
+        "select_rows": ("hbm", 4.0 * pairs, "B"),
+        "attn_decode": ("hbm", kv_bytes + q_bytes, "B"),
+    }, pairs
+
+
+def roofline_for(name, work, avg_ms):
+    bound, amount, unit = work
+    if unit == "flop":
+        achieved = amount / (avg_ms * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_F32_VALU_TFLOPS
+        u = "TFLOP/s"
+    else:
+        achieved = amount / (avg_ms * 1e-3) / 1e9
+        peak = PEAK_HBM_GBS
+        u = "GB/s"
+    return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": u,
+            "frac": round(achieved / peak, 4), "per_launch": amount, "avg_us": round(avg_ms * 1e3, 2),
+            "traffic": None}
+
+
+def kernel_times(run_step, nsteps, names):
+    """Average per-launch ms of each kernel over `nsteps` steps (hipEvents)."""
+    import torch
+    from block_sparse_long_amd import qsa
+    torch.cuda.synchronize()
+    qsa.profile_reset()
+    qsa.profile_enable(True)
+    for i in range(nsteps):
+        run_step(i)
+    torch.cuda.synchronize()
+    qsa.profile_enable(False)
+    out = {}
+    for n in names:
+        cnt, tot = qsa.profile_kernel_ms(n)
+        if cnt:
+            out[n] = (cnt, tot / cnt, tot / nsteps)
+    qsa.profile_reset()
+    return out
+
+
+def timed(run_step, steps, warmup):
+    import torch
+    for i in range(warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run_step(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+ALL_KERNELS = ["pool_rope", "rope_query", "score_rows_bf16", "score_rows_f32", "score_gemm_bf16", "select_rows",
+               "attn_prefill", "attn_decode", "attn_combine"]
+
+
+# ---------------------------------------------------------------------------
+# prefill workload
+# ---------------------------------------------------------------------------
+
+def bench_prefill(spec, steps, warmup, cpu_baseline):
+    import torch
+    from block_sparse_long_amd import qsa, synth
+    t0 = time.perf_counter()
+    w = synth.make(spec)
+    log(f"{spec.name}: inputs drawn in {time.perf_counter() - t0:.1f}s")
+    L, nb, k = spec.ctx, spec.n_blocks, spec.top_k
+    first_new = (L - spec.chunk) // 4
+    raw = to_dev(w["raw_keys"])
+    pooled = torch.zeros((1, nb, DIM), dtype=raw.dtype, device="cuda")
+    if first_new > 0:  # the context before the chunk is already pooled
+        qsa.pool_index_keys(raw, pooled, 0, first_new, spec.theta)
+    iq, seq, pos = to_dev(w["idx_q"]), to_dev(w["row_seq"]), to_dev(w["row_pos"])
+    q, kc, vc = to_dev(w["q"]), to_dev(w["k_cache"]), to_dev(w["v_cache"])
+    R = spec.chunk
+    max_nb = L // 4
+    sel = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((R,), dtype=torch.int32, device="cuda")
+    ws = torch.empty((max(qsa.score_topk_workspace_size(R, max_nb, k, qsa.BF16), 256),), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((R, spec.Hq), dtype=torch.float32, device="cuda")
+
+    def step(_i):
+        qsa.pool_index_keys(raw, pooled, first_new, nb, spec.theta)
+        qsa.score_topk(iq, seq, pos, pooled, max_nb, k, spec.theta, sel_blocks=sel, sel_count=cnt,
+                       workspace=ws, want_scores=False)
+        qsa.sparse_attn_prefill(q, seq, pos, kc, vc, sel, cnt, out=out, lse=lse)
+
+    ms = timed(step, steps, warmup)
+    log(f"{spec.name}: {ms:.3f} ms/step")
+    kt = kernel_times(step, max(3, min(steps, 10)), ALL_KERNELS)
+    work, pairs, npos = prefill_work(spec, w["row_pos"])
+    kernels = {n: {"launches_per_step": c / max(3, min(steps, 10)), "avg_us": round(a * 1e3, 2)}
+               for n, (c, a, _) in kt.items()}
+    dom = max((n for n in kt if n in work), key=lambda n: kt[n][2])
+    res = {"ms_per_step": ms, "value": R / (ms * 1e-3), "kernels": kernels,
+           "roofline": roofline_for(dom, work[dom], kt[dom][1]),
+           "rooflines": {n: roofline_for(n, work[n], kt[n][1]) for n in kt if n in work},
+           "pairs": pairs, "positions": npos}
+    if cpu_baseline:
+        res["cpu_baseline"] = cpu_prefill(spec, w)
+    return res
+
+
+def cpu_prefill(spec, w, target_s=12.0):
+    import oracle
+    L, nb, k = spec.ctx, spec.n_blocks, spec.top_k
+    first_new = (L - spec.chunk) // 4
+    pooled = np.zeros((1, nb, DIM), w["raw_keys"].dtype)
+    if first_new:  # the context before the chunk (not part of a step)
+        oracle.pool(w["raw_keys"], 0, first_new, spec.theta, pooled=pooled)
+    t0 = time.perf_counter()
+    oracle.pool(w["raw_keys"], first_new, nb, spec.theta, pooled=pooled)
+    t_pool = time.perf_counter() - t0
+
+    def rows_time(rows):
+        t = time.perf_counter()
+        s, c, _, _ = oracle.score_topk(w["idx_q"][rows], w["row_seq"][rows], w["row_pos"][rows], pooled, k,
+                                       spec.theta)
+        oracle.sparse_attn_prefill(w["q"][rows], w["row_seq"][rows], w["row_pos"][rows], w["k_cache"],
+                                   w["v_cache"], s, c)
+        return time.perf_counter() - t
+
+    R = spec.chunk
+    n0 = max(oracle.threads(), 8)
+    probe = np.linspace(R - 1, R // 2, n0).astype(np.int64)   # the heaviest (latest) rows
+    tp = rows_time(probe)
+    n = int(min(R, max(n0, n0 * target_s / max(tp, 1e-3))))
+    rows = np.unique(np.linspace(0, R - 1, n).astype(np.int64))
+    t = rows_time(rows)
+    per_step = t_pool + t * R / len(rows)
+    return {"value": R / per_step, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"pool of the chunk's {spec.chunk // 4} new blocks, then score/top-{k} and attention for "
+                      f"{len(rows)} of {R} rows spread over the chunk ({t_pool + t:.1f}s); per-step time "
+                      f"extrapolated to all rows"}
+
+
+# ---------------------------------------------------------------------------
+# decode workload
+# ---------------------------------------------------------------------------
+
+def bench_decode(spec, steps, warmup, cpu_baseline, copies=3):
+    import torch
+    from block_sparse_long_amd import qsa, synth
+    t0 = time.perf_counter()
+    w = synth.make(spec)
+    log(f"{spec.name}: inputs drawn in {time.perf_counter() - t0:.1f}s")
+    B, nb, k = spec.batch, spec.n_blocks, spec.top_k
+    raw = to_dev(w["raw_keys"])
+    pooled0 = torch.zeros((B, nb, DIM), dtype=raw.dtype, device="cuda")
+    qsa.pool_index_keys(raw, pooled0, 0, nb, spec.theta)   # built before timing
+    del raw
+    pooled_h = None
+    if cpu_baseline:
+        pooled_h = pooled0[:1].cpu()
+    kc0, vc0 = to_dev(w["k_cache"]), to_dev(w["v_cache"])
+    pooled = [pooled0] + [pooled0.clone() for _ in range(copies - 1)]
+    kcs = [kc0] + [kc0.clone() for _ in range(copies - 1)]
+    vcs = [vc0] + [vc0.clone() for _ in range(copies - 1)]
+    iq, seq, apos = to_dev(w["idx_q"]), to_dev(w["row_seq"]), to_dev(w["row_pos"])
+    q, rpos = to_dev(w["q"]), to_dev(w["attn_pos"])
+    ts = None if w["tail_start"] is None else to_dev(w["tail_start"])
+    max_nb = int(visible(w["row_pos"]).max())
+    dcode = qsa.BF16 if spec.dtype == "bf16" else qsa.F32
+    sel = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B,), dtype=torch.int32, device="cuda")
+    ws = torch.empty((max(qsa.score_topk_workspace_size(B, max_nb, k, dcode), 256),), dtype=torch.uint8,
+                     device="cuda")
+    wsa = torch.empty((max(qsa.sparse_attn_decode_workspace_size(B, spec.q_per_seq, spec.Hq, DIM, k), 256),),
+                      dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, spec.q_per_seq, spec.Hq), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        c = i % copies
+        qsa.score_topk(iq, seq, apos, pooled[c], max_nb, k, spec.theta, sel_blocks=sel, sel_count=cnt,
+                       workspace=ws, want_scores=False)
+        qsa.sparse_attn_decode(q, rpos, kcs[c], vcs[c], sel, cnt, ts, out=out, lse=lse, workspace=wsa)
+
+    ms = timed(step, steps, warmup)
+    log(f"{spec.name}: {ms:.3f} ms/step")
+    nprof = max(3, min(steps, 30))
+    kt = kernel_times(step, nprof, ALL_KERNELS)
+    work, pairs = decode_work(spec, w["row_pos"], w["attn_pos"], w["tail_start"])
+    kernels = {n: {"launches_per_step": c / nprof, "avg_us": round(a * 1e3, 2)} for n, (c, a, _) in kt.items()}
+    dom = max((n for n in kt if n in work), key=lambda n: kt[n][2])
+    rows = spec.batch * spec.q_per_seq
+    res = {"workload": spec.name, "value": rows / (ms * 1e-3), "unit": "query rows/s", "ms_per_step": ms,
+           "kernels": kernels, "roofline": roofline_for(dom, work[dom], kt[dom][1]),
+           "rooflines": {n: roofline_for(n, work[n], kt[n][1]) for n in kt if n in work}}
+    if cpu_baseline:
+        res["cpu_baseline"] = cpu_decode(spec, w, pooled_h)
+    return res
+
+
+def cpu_decode(spec, w, pooled_h):
+    import torch
+    import oracle
+    k = spec.top_k
+    p = pooled_h
+    pooled = (p.view(torch.int16).numpy().view(np.uint16) if p.dtype == torch.bfloat16 else p.numpy())
+    t0 = time.perf_counter()
+    s, c, _, _ = oracle.score_topk(w["idx_q"][:1], w["row_seq"][:1], w["row_pos"][:1], pooled, k, spec.theta)
+    ts = None if w["tail_start"] is None else w["tail_start"][:1]
+    oracle.sparse_attn_decode(w["q"][:1], w["attn_pos"][:1], w["k_cache"][:1], w["v_cache"][:1], s, c, ts)
+    t = time.perf_counter() - t0
+    return {"value": spec.q_per_seq / t, "unit": "query rows/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"one of {spec.batch} sequences: score/top-{k} of its anchor over "
+                      f"{int(visible(w['row_pos'][0]))} blocks and attention of its {spec.q_per_seq} rows "
+                      f"({t:.1f}s)"}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="chunk-256k")
+    ap.add_argument("--decode-workload", default="decode-1m-draft")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs the QSA hot path on one GPU only (asked for {args.gpus}); "
+              "sharding across GPUs is a design note, not implemented", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from block_sparse_long_amd import qsa, synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    qsa.load()
+    cpu = not args.no_cpu_baseline
+    spec = synth.SPECS[args.workload]
+    if spec.kind == "prefill":
+        pre = bench_prefill(spec, args.steps, args.warmup, cpu)
+        value, unit, ms = pre["value"], "tokens/s", pre["ms_per_step"]
+        main_res = pre
+    else:
+        pre = bench_decode(spec, args.steps * 10, args.warmup, cpu)
+        value, unit, ms = pre["value"], pre["unit"], pre["ms_per_step"]
+        main_res = pre
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic (seeded N(0,1) with planted blocks)",
+        "config": {"workload": spec.name, "context": spec.ctx, "rows": spec.attn_rows, "batch": spec.batch,
+                   "Hq": spec.Hq, "Hkv": spec.Hkv, "head_dim": spec.D, "index_heads": 4, "index_dim": 128,
+                   "block": 4, "top_k": spec.top_k, "rope_theta": spec.theta},
+        "roofline": main_res["roofline"],
+        "cpu_baseline": main_res.get("cpu_baseline"),
+        "kernels": main_res["kernels"],
+        "rooflines": main_res["rooflines"],
+    }
+    if args.decode_workload != "none" and spec.kind == "prefill":
+        dspec = synth.SPECS[args.decode_workload]
+        dec = bench_decode(dspec, args.steps * 10, args.warmup, cpu)
+        line["decode"] = {k: v for k, v in dec.items()}
+        line["decode"]["config"] = {"context": dspec.ctx, "batch": dspec.batch, "q_per_seq": dspec.q_per_seq,
+                                    "Hq": dspec.Hq, "Hkv": dspec.Hkv, "top_k": dspec.top_k,
+                                    "steps": args.steps * 10}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
