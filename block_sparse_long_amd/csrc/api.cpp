@@ -234,7 +234,10 @@ qsa_status_t qsa_sparse_attn_prefill(const void *q, const int32_t *row_seq, cons
     a.partial = nullptr;
     a.nsplit = 1;
     clear_launch_err();
-    launch_attn_prefill(a, dtype == QSA_BF16, (hipStream_t)stream);
+    if (attn_mfma_supported(Hq, Hkv, 1, dtype == QSA_BF16))
+        launch_attn_prefill_mfma(a, (hipStream_t)stream);
+    else
+        launch_attn_prefill(a, dtype == QSA_BF16, (hipStream_t)stream);
     return launch_status();
 }
 
@@ -289,7 +292,12 @@ qsa_status_t qsa_sparse_attn_decode(const void *q, const int32_t *row_pos, int32
     a.partial = (float *)workspace;
     a.nsplit = attn_decode_splits(top_k);
     clear_launch_err();
-    launch_attn_decode(a, dtype == QSA_BF16, (hipStream_t)stream);
+    if (attn_mfma_supported(Hq, Hkv, q_per_seq, dtype == QSA_BF16)) {
+        launch_attn_decode_mfma(a, (hipStream_t)stream);
+        launch_attn_combine(a, true, (hipStream_t)stream);
+    } else {
+        launch_attn_decode(a, dtype == QSA_BF16, (hipStream_t)stream);
+    }
     return launch_status();
 }
 

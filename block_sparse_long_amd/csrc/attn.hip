@@ -263,6 +263,11 @@ void launch_attn_decode(const AttnArgs &a, bool bf16, hipStream_t stream)
         if (bf16) QSA_LAUNCH("attn_decode", (attn_kernel<bf16_t, kAttnMaxQ, true>), grid, block, 0, stream, a);
         else QSA_LAUNCH("attn_decode", (attn_kernel<float, kAttnMaxQ, true>), grid, block, 0, stream, a);
     }
+    launch_attn_combine(a, bf16, stream);
+}
+
+void launch_attn_combine(const AttnArgs &a, bool bf16, hipStream_t stream)
+{
     const int64_t qrows = (int64_t)a.n_sel * a.q_per_sel * a.Hq;
     if (bf16)
         QSA_LAUNCH("attn_combine", attn_combine_kernel<bf16_t>, dim3((unsigned)qrows), dim3(128), 0, stream,

@@ -1,0 +1,523 @@
+// attn_mfma.hip -- steps a7-a9 on bf16 MFMA: gather attention over the kept
+// blocks plus the tail, shared by the query rows of a workgroup.
+//
+// "Qwen3.8-Flash-Next: Day-0 Support in SGLang", section "Qwen Sparse
+// Attention": each kept block stands for its 4 token positions, the
+// zero-to-three tail tokens of the query's incomplete block are appended, and
+// attention reads the original K/V at those positions.  Section "IndexShare
+// MTP": draft rows share one selection plus the positions drafted since.
+// Readings: query head h uses KV head floor(h / (Hq/Hkv)); logits are
+// softmax_scale * <q, k>; P is rounded to bf16 as an MFMA operand.
+//
+// Layout of the work.  A workgroup owns up to 64 queries that share one KV
+// head: (rows of the tile) x (Hq/Hkv heads), as 4 MFMA tiles of 16 queries,
+// one per wave.  It walks a list of positions in chunks of 64: the chunk's K
+// rows (row-major) and V rows (transposed) are gathered into LDS once and
+// every wave computes S^T = K Q^T for its 16 queries (v_mfma_f32_16x16x32_bf16,
+// positions on M, queries on N), an online softmax, then O += P V (queries on
+// M, head dims on N).  Each position of a chunk carries a mask of the query
+// rows that attend it, so one gathered chunk serves every row of the tile:
+//   - prefill: the tile is up to 64/(Hq/Hkv) consecutive rows; the position
+//     list is the union of their kept blocks (built in LDS with a bitmap per
+//     window of 65,536 blocks) followed by each row's tail tokens;
+//   - decode: the rows of one sequence share its selection; a workgroup takes
+//     one chunk of 16 kept blocks (split) or the tail, and a combine kernel
+//     merges the splits' partial softmaxes.
+// A wave skips the MFMAs of a 16-position sub-tile that none of its rows
+// attends, so disjoint selections cost gathers but not matrix work.
+//
+// MFMA operand layout (16x16x32): lane l supplies A[m = l%16][8 k-slots of
+// group l/16] and B[8 k-slots of group l/16][n = l%16] and receives
+// C[4*(l/16) + j][l%16].  For S^T = K Q^T the k-slots of group g at step s
+// are head dims 32g + 8s .. +7.  For O = P V, a 32-position step covers
+// sub-tiles 2i and 2i+1; group g's slots 0-3 are positions 4g..4g+3 of
+// sub-tile 2i and slots 4-7 those of sub-tile 2i+1 -- exactly the S^T values
+// the lane already holds, so P needs no shuffle.
+#include "qsa_device.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+
+namespace {
+
+constexpr int kCh = 64;             // positions per chunk
+constexpr int kKRow = kDim + 8;     // LDS row stride of K (bf16), 272 B: conflict-free b128 reads
+constexpr int kVRow = kCh + 8;      // LDS row stride of V^T (bf16), 144 B
+constexpr int kWin = 1 << 16;       // union bitmap window, in blocks
+constexpr int kWinWords = kWin / 32;
+constexpr int kMaxUnionBlocks = 4096;  // rows per tile x top_k is kept at or below this
+constexpr int kMaxTileRows = 16;       // row masks are 16 bits
+
+struct ChunkSmem {
+    bf16_t k[kCh][kKRow];
+    bf16_t vt[kDim][kVRow];
+    int32_t pos[kCh];
+    uint32_t pmask[kCh];
+};
+
+struct UnionSmem {
+    uint32_t bitmap[kWinWords];
+    uint16_t wprefix[kWinWords];     // < kMaxUnionBlocks
+    int32_t blk[kMaxUnionBlocks];
+    uint32_t mask[kMaxUnionBlocks];  // bit r: tile row r keeps the block
+    uint32_t count;
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// Per-wave attention state: 16 queries, lane l <-> query l%16 for m / l,
+// O[q = 4*(l/16) + j][dim 16*nt + l%16] in o[nt][j].
+struct WaveState {
+    f32x4_t o[8];
+    float m, l;
+};
+
+// Gather K and V^T of positions pos[0..n) into LDS (zeros beyond n).
+__device__ __forceinline__ void gather_chunk(ChunkSmem &cs, const bf16_t *__restrict__ kbase,
+                                             const bf16_t *__restrict__ vbase, int64_t row_stride, int n)
+{
+    const int t = threadIdx.x;
+    {   // K: thread -> row t/4, 64 bytes at dim 32*(t%4)
+        const int p = t >> 2, d0 = (t & 3) * 32;
+        uint4 v[4];
+        if (p < n) {
+            const uint4 *src = (const uint4 *)(kbase + (int64_t)cs.pos[p] * row_stride + d0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = src[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(uint4 *)&cs.k[p][d0 + 8 * i] = v[i];
+    }
+    {   // V^T: thread -> positions 4*(t/16) .. +3, dims 8*(t%16) .. +7
+        const int p0 = (t >> 4) * 4, d0 = (t & 15) * 8;
+        uint4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = (p0 + i < n) ? *(const uint4 *)(vbase + (int64_t)cs.pos[p0 + i] * row_stride + d0)
+                                : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+            const int w = d >> 1, hi = d & 1;
+            uint32_t e[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t word = w == 0 ? v[i].x : w == 1 ? v[i].y : w == 2 ? v[i].z : v[i].w;
+                e[i] = hi ? (word >> 16) : (word & 0xffffu);
+            }
+            *(uint2 *)&cs.vt[d0 + d][p0] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+        }
+    }
+}
+
+// One chunk for one wave: S^T, online softmax, O += P V.  `qbit` is the mask
+// bit of this lane's query row (0 when the query slot is unused).
+__device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, int n, const bf16x8_t (&qb)[4], uint32_t qbit,
+                                           float scale, WaveState &st)
+{
+    const int lane = threadIdx.x & 63;
+    const int m16 = lane & 15, g = lane >> 4;
+    float s[4][4];
+    bool any[4];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+        bool ok[4];
+        bool lane_any = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int pi = sub * 16 + 4 * g + j;
+            ok[j] = pi < n && (cs.pmask[pi] & qbit) != 0u;
+            lane_any |= ok[j];
+        }
+        any[sub] = __ballot(lane_any) != 0ull;
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (any[sub]) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const uint4 kv = *(const uint4 *)&cs.k[sub * 16 + m16][32 * g + 8 * ks];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), qb[ks], acc, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[sub][j] = ok[j] ? acc[j] * scale : -INFINITY;
+    }
+    // online softmax, per query (lane l%16), over the 4 lane groups
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, s[sub][j]);
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float m_new = fmaxf(st.m, cmax);
+    float alpha = 1.0f;
+    float psum = 0.0f;
+    float p[4][4];
+    if (m_new == -INFINITY) {
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[sub][j] = 0.0f;
+    } else {
+        alpha = st.m == -INFINITY ? 0.0f : __expf(st.m - m_new);
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                p[sub][j] = s[sub][j] == -INFINITY ? 0.0f : __expf(s[sub][j] - m_new);
+                psum += p[sub][j];
+            }
+    }
+    st.m = m_new;
+    st.l = st.l * alpha + psum;  // per-lane partial; the 4 groups are summed at the end
+    // rescale O rows (queries 4g + j) by their alpha
+    float a4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a4[j] = __shfl(alpha, 4 * g + j);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st.o[nt][j] *= a4[j];
+    // O += P V over two 32-position steps
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        if (!(any[2 * i] || any[2 * i + 1])) continue;
+        const uint4 pa = make_uint4(pack_bf16x2(p[2 * i][0], p[2 * i][1]), pack_bf16x2(p[2 * i][2], p[2 * i][3]),
+                                    pack_bf16x2(p[2 * i + 1][0], p[2 * i + 1][1]),
+                                    pack_bf16x2(p[2 * i + 1][2], p[2 * i + 1][3]));
+        const bf16x8_t A = as_bf16x8(pa);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const bf16_t *row = &cs.vt[16 * nt + m16][0];
+            const uint2 lo = *(const uint2 *)(row + 32 * i + 4 * g);
+            const uint2 hi = *(const uint2 *)(row + 32 * i + 16 + 4 * g);
+            const bf16x8_t Bv = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+            st.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv, st.o[nt], 0, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ void load_query(const bf16_t *__restrict__ qrow, bool valid, bf16x8_t (&qb)[4])
+{
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        qb[ks] = valid ? as_bf16x8(*(const uint4 *)(qrow + 32 * g + 8 * ks)) : zero_bf16x8();
+}
+
+__device__ __forceinline__ void init_state(WaveState &st)
+{
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) st.o[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    st.m = -INFINITY;
+    st.l = 0.0f;
+}
+
+// Final per-query sums; returns l_total of the lane's query (l%16).
+__device__ __forceinline__ float total_l(const WaveState &st)
+{
+    float l = st.l;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    return l;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Prefill: grid (row tiles, Hkv).  rows_per_tile * hg <= 64.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnArgs a, int32_t rows_per_tile)
+{
+    __shared__ ChunkSmem cs;
+    __shared__ UnionSmem us;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int m16 = lane & 15, g = lane >> 4;
+    const int hg = a.Hq / a.Hkv;
+    const int kvh = blockIdx.y;
+    const int64_t row0 = (int64_t)blockIdx.x * rows_per_tile;
+    const int nrows = (int)min((int64_t)rows_per_tile, (int64_t)a.n_sel - row0);
+    // this lane's query (as an S^T column): tile query qi = 16*wave + m16
+    const int qi = 16 * wave + m16;
+    const int r_local = qi / hg;
+    const bool q_valid = r_local < nrows;
+    const int head = kvh * hg + qi % hg;
+    bf16x8_t qb[4];
+    load_query((const bf16_t *)a.q + ((row0 + (q_valid ? r_local : 0)) * a.Hq + head) * kDim, q_valid, qb);
+    WaveState st;
+    init_state(st);
+    const int64_t row_stride = (int64_t)a.Hkv * kDim;
+    uint32_t todo = nrows >= 32 ? 0xffffffffu : ((1u << nrows) - 1u);
+    while (todo) {  // rows of one sequence at a time (uniform across the workgroup)
+        const int first = __builtin_ctz(todo);
+        const int32_t seq = a.row_seq[row0 + first];
+        uint32_t active = 0;
+        for (int r = first; r < nrows; ++r)
+            if (((todo >> r) & 1u) && a.row_seq[row0 + r] == seq) active |= 1u << r;
+        todo &= ~active;
+        const uint32_t qbit = q_valid ? (active & (1u << r_local)) : 0u;
+        const bf16_t *kbase = (const bf16_t *)a.k_cache + (int64_t)seq * a.kv_seq_stride + (int64_t)kvh * kDim;
+        const bf16_t *vbase = (const bf16_t *)a.v_cache + (int64_t)seq * a.kv_seq_stride + (int64_t)kvh * kDim;
+        // block range of the active rows' selections
+        int32_t hi_blk = 0;
+        for (int r = 0; r < nrows; ++r) {
+            if (!((active >> r) & 1u)) continue;
+            const int32_t c = min(a.sel_count[row0 + r], a.top_k);
+            if (c > 0) hi_blk = max(hi_blk, a.sel_blocks[(row0 + r) * a.top_k + c - 1] + 1);
+        }
+        for (int32_t w0 = 0; w0 < hi_blk; w0 += kWin) {
+            // ---- union of the active rows' kept blocks in [w0, w0 + kWin) ----
+            for (int i = t; i < kWinWords; i += blockDim.x) us.bitmap[i] = 0u;
+            __syncthreads();
+            for (int r = 0; r < nrows; ++r) {
+                if (!((active >> r) & 1u)) continue;
+                const int32_t c = min(a.sel_count[row0 + r], a.top_k);
+                const int32_t *sl = a.sel_blocks + (row0 + r) * a.top_k;
+                for (int i = t; i < c; i += blockDim.x) {
+                    const int32_t b = sl[i] - w0;
+                    if (b >= 0 && b < kWin) atomicOr(&us.bitmap[b >> 5], 1u << (b & 31));
+                }
+            }
+            __syncthreads();
+            {   // exclusive prefix of popcounts over the words (8 words per thread)
+                constexpr int per = kWinWords / 256;
+                uint32_t cnt = 0;
+#pragma unroll
+                for (int i = 0; i < per; ++i) cnt += __popc(us.bitmap[t * per + i]);
+                uint32_t x = cnt;
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t y = __shfl_up(x, o);
+                    if (lane >= o) x += y;
+                }
+                __shared__ uint32_t wsum[4];
+                if (lane == 63) wsum[wave] = x;
+                __syncthreads();
+                uint32_t before = 0;
+                for (int w = 0; w < wave; ++w) before += wsum[w];
+                if (t == 255) us.count = before + x;
+                uint32_t run = before + x - cnt;
+#pragma unroll
+                for (int i = 0; i < per; ++i) {
+                    const uint32_t word = us.bitmap[t * per + i];
+                    us.wprefix[t * per + i] = (uint16_t)run;
+                    uint32_t bits = word, k = run;
+                    while (bits) {
+                        const int b = __builtin_ctz(bits);
+                        bits &= bits - 1u;
+                        us.blk[k] = w0 + (t * per + i) * 32 + b;
+                        us.mask[k] = 0u;
+                        ++k;
+                    }
+                    run += __popc(word);
+                }
+            }
+            __syncthreads();
+            for (int r = 0; r < nrows; ++r) {
+                if (!((active >> r) & 1u)) continue;
+                const int32_t c = min(a.sel_count[row0 + r], a.top_k);
+                const int32_t *sl = a.sel_blocks + (row0 + r) * a.top_k;
+                for (int i = t; i < c; i += blockDim.x) {
+                    const int32_t b = sl[i] - w0;
+                    if (b >= 0 && b < kWin) {
+                        const uint32_t word = us.bitmap[b >> 5];
+                        const uint32_t idx = us.wprefix[b >> 5] + __popc(word & ((1u << (b & 31)) - 1u));
+                        atomicOr(&us.mask[idx], 1u << r);
+                    }
+                }
+            }
+            __syncthreads();
+            const int32_t nu = (int32_t)us.count;
+            // ---- the union's blocks, 16 per chunk ----
+            for (int32_t c0 = 0; c0 < nu; c0 += kCh / kBlock) {
+                const int nb = min(kCh / kBlock, nu - c0);
+                if (t < kCh) {
+                    const int bi = t / kBlock;
+                    cs.pos[t] = bi < nb ? us.blk[c0 + bi] * kBlock + (t % kBlock) : 0;
+                    cs.pmask[t] = bi < nb ? us.mask[c0 + bi] : 0u;
+                }
+                __syncthreads();
+                gather_chunk(cs, kbase, vbase, row_stride, nb * kBlock);
+                __syncthreads();
+                wave_chunk(cs, nb * kBlock, qb, qbit, a.scale, st);
+                __syncthreads();
+            }
+        }
+        // ---- tails: positions [4*nc(t), t] of every active row ----
+        if (t < kCh) {
+            int n = 0;
+            int32_t pos = 0;
+            uint32_t msk = 0;
+            for (int r = 0; r < nrows && n <= t; ++r) {
+                if (!((active >> r) & 1u)) continue;
+                const int32_t tr = a.row_pos[row0 + r];
+                const int32_t ts = (int32_t)(kBlock * visible_blocks(tr));
+                const int len = tr - ts + 1;  // 0..3
+                if (t < n + len) {
+                    pos = ts + (t - n);
+                    msk = 1u << r;
+                }
+                n += len;
+            }
+            cs.pos[t] = pos;
+            cs.pmask[t] = msk;
+        }
+        __syncthreads();
+        int ntail = 0;
+        for (int r = 0; r < nrows; ++r) {
+            if (!((active >> r) & 1u)) continue;
+            const int32_t tr = a.row_pos[row0 + r];
+            ntail += tr - (int32_t)(kBlock * visible_blocks(tr)) + 1;
+        }
+        ntail = min(ntail, kCh);  // at most 16 rows x 3 tokens
+        if (ntail > 0) {
+            gather_chunk(cs, kbase, vbase, row_stride, ntail);
+            __syncthreads();
+            // positions beyond n carry no mask bit, so they stay out
+            wave_chunk(cs, kCh, qb, qbit, a.scale, st);
+        }
+        __syncthreads();
+    }
+    // ---- output ----
+    const float ltot = total_l(st);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int qo = 16 * wave + 4 * g + j;   // query of o[.][j]
+        const int ro = qo / hg;
+        const float lq = __shfl(ltot, 4 * g + j);
+        if (ro >= nrows) continue;
+        const int ho = kvh * hg + qo % hg;
+        bf16_t *orow = (bf16_t *)a.out + ((row0 + ro) * a.Hq + ho) * kDim;
+        const float inv = lq > 0.0f ? 1.0f / lq : 0.0f;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) orow[16 * nt + m16] = f32_to_bf16(st.o[nt][j] * inv);
+    }
+    if (a.lse && g == 0 && q_valid) a.lse[(row0 + r_local) * a.Hq + head] = ltot > 0.0f ? st.m + __logf(ltot) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Decode: grid (splits, batch * Hkv).  q_per_sel * hg <= 64.  Split i < nsplit-1
+// takes kept blocks [16i, 16i + 16); the last split takes the tails.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void attn_decode_mfma_kernel(AttnArgs a)
+{
+    __shared__ ChunkSmem cs;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int m16 = lane & 15, g = lane >> 4;
+    const int hg = a.Hq / a.Hkv;
+    const int64_t s = blockIdx.y / a.Hkv;
+    const int kvh = blockIdx.y % a.Hkv;
+    const int split = blockIdx.x;
+    const int nq = a.q_per_sel * hg;
+    const int qi = 16 * wave + m16;
+    const int jrow = qi / hg;
+    const bool q_valid = qi < nq;
+    const int head = kvh * hg + qi % hg;
+    const int64_t qrow = (s * a.q_per_sel + (q_valid ? jrow : 0)) * a.Hq + head;
+    bf16x8_t qb[4];
+    load_query((const bf16_t *)a.q + qrow * kDim, q_valid, qb);
+    WaveState st;
+    init_state(st);
+    const uint32_t qbit = q_valid ? (1u << jrow) : 0u;
+    const int64_t row_stride = (int64_t)a.Hkv * kDim;
+    const bf16_t *kbase = (const bf16_t *)a.k_cache + s * a.kv_seq_stride + (int64_t)kvh * kDim;
+    const bf16_t *vbase = (const bf16_t *)a.v_cache + s * a.kv_seq_stride + (int64_t)kvh * kDim;
+    const int32_t count = min(a.sel_count[s], a.top_k);
+    const uint32_t all_rows = a.q_per_sel >= 32 ? 0xffffffffu : ((1u << a.q_per_sel) - 1u);
+    if (split < a.nsplit - 1) {
+        const int32_t b0 = split * (kCh / kBlock);
+        const int nb = max(0, min(kCh / kBlock, count - b0));
+        if (nb > 0) {
+            if (t < kCh) {
+                const int bi = t / kBlock;
+                cs.pos[t] = bi < nb ? a.sel_blocks[s * a.top_k + b0 + bi] * kBlock + (t % kBlock) : 0;
+                cs.pmask[t] = bi < nb ? all_rows : 0u;
+            }
+            __syncthreads();
+            gather_chunk(cs, kbase, vbase, row_stride, nb * kBlock);
+            __syncthreads();
+            wave_chunk(cs, nb * kBlock, qb, qbit, a.scale, st);
+        }
+    } else {
+        // tails: row j attends [ts_j, t_j]; walk [min ts, max t] in chunks
+        int32_t lo = INT32_MAX, hi = -1;
+        for (int j = 0; j < a.q_per_sel; ++j) {
+            const int32_t tj = a.row_pos[s * a.q_per_sel + j];
+            const int32_t ts = a.tail_start ? a.tail_start[s] : (int32_t)(kBlock * visible_blocks(tj));
+            lo = min(lo, ts);
+            hi = max(hi, tj);
+        }
+        for (int64_t p0 = lo; p0 <= hi; p0 += kCh) {
+            const int n = (int)min((int64_t)kCh, (int64_t)hi - p0 + 1);
+            if (t < kCh) {
+                const int64_t p = p0 + t;
+                uint32_t msk = 0;
+                if (t < n) {
+                    for (int j = 0; j < a.q_per_sel; ++j) {
+                        const int32_t tj = a.row_pos[s * a.q_per_sel + j];
+                        const int32_t ts = a.tail_start ? a.tail_start[s] : (int32_t)(kBlock * visible_blocks(tj));
+                        if (p >= ts && p <= tj) msk |= 1u << j;
+                    }
+                }
+                cs.pos[t] = t < n ? (int32_t)p : 0;
+                cs.pmask[t] = msk;
+            }
+            __syncthreads();
+            gather_chunk(cs, kbase, vbase, row_stride, n);
+            __syncthreads();
+            wave_chunk(cs, n, qb, qbit, a.scale, st);
+            __syncthreads();
+        }
+    }
+    // ---- partial softmax state of this split ----
+    const float ltot = total_l(st);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int qo = 16 * wave + 4 * g + j;
+        if (qo >= nq) continue;
+        const int jo = qo / hg, ho = kvh * hg + qo % hg;
+        float *pp = a.partial + (((s * a.q_per_sel + jo) * a.Hq + ho) * a.nsplit + split) * (kDim + 2);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) pp[16 * nt + m16] = st.o[nt][j];
+    }
+    if (q_valid && g == 0) {
+        float *pp = a.partial + (qrow * a.nsplit + split) * (kDim + 2);
+        pp[kDim] = st.m;
+        pp[kDim + 1] = ltot;
+    }
+}
+
+int32_t attn_prefill_rows_per_tile(int32_t hg, int32_t top_k)
+{
+    int32_t r = max(1, 64 / hg);
+    r = min(r, kMaxTileRows);                  // also: every row's 0..3 tail tokens fit one chunk
+    r = min(r, kMaxUnionBlocks / top_k);       // the union of the rows' selections fits LDS
+    return max(r, 1);
+}
+
+bool attn_mfma_supported(int32_t Hq, int32_t Hkv, int32_t q_per_sel, bool bf16)
+{
+    const int32_t hg = Hq / Hkv;
+    return bf16 && (hg == 1 || hg == 2 || hg == 4 || hg == 8 || hg == 16 || hg == 32 || hg == 64) &&
+           (int64_t)q_per_sel * hg <= 64;
+}
+
+void launch_attn_prefill_mfma(const AttnArgs &a, hipStream_t stream)
+{
+    const int32_t hg = a.Hq / a.Hkv;
+    const int32_t rpt = attn_prefill_rows_per_tile(hg, a.top_k);
+    const dim3 grid((unsigned)((a.n_sel + rpt - 1) / rpt), (unsigned)a.Hkv), block(256);
+    QSA_LAUNCH("attn_prefill_mfma", attn_prefill_mfma_kernel, grid, block, 0, stream, a, rpt);
+}
+
+void launch_attn_decode_mfma(const AttnArgs &a, hipStream_t stream)
+{
+    const dim3 grid((unsigned)a.nsplit, (unsigned)((int64_t)a.n_sel * a.Hkv)), block(256);
+    QSA_LAUNCH("attn_decode_mfma", attn_decode_mfma_kernel, grid, block, 0, stream, a);
+}
+
+}  // namespace qsa

@@ -70,6 +70,13 @@ struct AttnArgs {
 int32_t attn_decode_splits(int32_t top_k);
 void launch_attn_prefill(const AttnArgs &a, bool bf16, hipStream_t stream);
 void launch_attn_decode(const AttnArgs &a, bool bf16, hipStream_t stream);
+void launch_attn_combine(const AttnArgs &a, bool bf16, hipStream_t stream);
+
+// ---- attn_mfma.hip (bf16, Hq/Hkv a power of two up to 64) ---------------------
+bool attn_mfma_supported(int32_t Hq, int32_t Hkv, int32_t q_per_sel, bool bf16);
+int32_t attn_prefill_rows_per_tile(int32_t hg, int32_t top_k);
+void launch_attn_prefill_mfma(const AttnArgs &a, hipStream_t stream);
+void launch_attn_decode_mfma(const AttnArgs &a, hipStream_t stream);
 
 }  // namespace qsa
 

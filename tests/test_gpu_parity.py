@@ -162,7 +162,7 @@ def test_score_topk_default_paths_agree(gpu):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (16, 2), (4, 4)])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (16, 2), (4, 4), (6, 2), (32, 1)])
 def test_attn_prefill_matches_oracle(gpu, dtype, Hq, Hkv):
     rng = np.random.default_rng(30 + Hq + Hkv)
     L, R, k = 4 * 700 + 2, 70, 64
@@ -180,9 +180,38 @@ def test_attn_prefill_matches_oracle(gpu, dtype, Hq, Hkv):
     np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
 
 
+def test_attn_prefill_overlapping_and_mixed_sequences(gpu):
+    # consecutive rows whose selections overlap (a shared core plus own blocks),
+    # rows of two sequences interleaved, and runs of identical rows
+    rng = np.random.default_rng(33)
+    B, L, R, k, Hq, Hkv = 2, 4 * 900 + 3, 77, 96, 8, 1
+    seq = rng.integers(0, 2, R).astype(np.int32)
+    seq[20:40] = 1
+    pos = rng.integers(4 * k, L, R).astype(np.int32)
+    pos[50:60] = pos[50]
+    core = np.sort(rng.choice(4 * k // 4, 60, replace=False))
+    sel = np.full((R, k), -1, np.int32)
+    cnt = np.zeros(R, np.int32)
+    for r, t in enumerate(pos):
+        nc = (int(t) + 1) // 4
+        own = rng.choice(np.setdiff1d(np.arange(nc), core), k - len(core), replace=False)
+        s_ = np.sort(np.concatenate([core, own]))
+        sel[r] = s_
+        cnt[r] = k
+    sel[55] = sel[50]
+    q = synth.bf16_bits(rng.standard_normal((R, Hq, DIM)).astype(np.float32))
+    kc = synth.bf16_bits(rng.standard_normal((B, L, Hkv, DIM)).astype(np.float32))
+    vc = synth.bf16_bits(rng.standard_normal((B, L, Hkv, DIM)).astype(np.float32))
+    want, want_lse = oracle.sparse_attn_prefill(q, seq, pos, kc, vc, sel, cnt)
+    out, lse = qsa.sparse_attn_prefill(dev(q, "bf16"), dev(seq, "i"), dev(pos, "i"), dev(kc, "bf16"),
+                                       dev(vc, "bf16"), dev(sel, "i"), dev(cnt, "i"))
+    assert_close_out(host(out), want, "bf16")
+    np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("Qn,Hq,Hkv,draft", [(1, 8, 1, False), (4, 8, 1, True), (2, 16, 2, True),
-                                             (3, 4, 2, False)])
+                                             (3, 4, 2, False), (2, 6, 2, True), (8, 8, 1, True)])
 def test_attn_decode_matches_oracle(gpu, dtype, Qn, Hq, Hkv, draft):
     rng = np.random.default_rng(40 + Qn * Hq)
     B, ctx, k = 3, 4 * 900 + 1, 128
