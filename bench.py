@@ -79,6 +79,7 @@ def prefill_work(spec, row_pos):
         "score_rows_bf16": ("hbm", float(pairs) * DIM * eb, "B"),
         "select_rows": ("hbm", 4.0 * pairs, "B"),   # scans the fp32 scores once
         "attn_prefill": ("alu", 4.0 * spec.Hq * DIM * float(npos.sum()), "flop"),
+        "attn_prefill_mfma": ("mfma", 4.0 * spec.Hq * DIM * float(npos.sum()), "flop"),
     }, pairs, float(npos.sum())
 
 
@@ -98,7 +99,9 @@ def decode_work(spec, anchor_pos, attn_pos, tail_start):
     return {
         kind: ("hbm", float(pairs) * DIM * eb, "B"),
         "select_rows": ("hbm", 4.0 * pairs, "B"),
+        "select_collect": ("hbm", 4.0 * pairs, "B"),
         "attn_decode": ("hbm", kv_bytes + q_bytes, "B"),
+        "attn_decode_mfma": ("hbm", kv_bytes + q_bytes, "B"),
     }, pairs
 
 
@@ -150,6 +153,7 @@ def timed(run_step, steps, warmup):
 
 
 ALL_KERNELS = ["pool_rope", "rope_query", "score_rows_bf16", "score_rows_f32", "score_gemm_bf16", "select_rows",
+               "select_collect", "attn_prefill_mfma", "attn_decode_mfma",
                "attn_prefill", "attn_decode", "attn_combine"]
 
 

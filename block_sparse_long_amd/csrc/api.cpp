@@ -78,18 +78,30 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // MFMA GEMM scorer, which shares each key tile among 16 rows.
 constexpr int32_t kRowsPathMax = 64;
 
+// Workspace of qsa_score_topk: rotated index queries and fp32 scores; for
+// few rows also the split selection's per-row scratch, kept-for-sure and
+// candidate lists.
 struct ScoreLayout {
     int64_t sc_stride;
-    size_t qrot_off, scores_off, total;
+    bool split;
+    size_t qrot_off, scores_off, scratch_off, sure_off, cand_off, total;
 };
 
-static ScoreLayout score_layout(int32_t rows, int32_t max_nb, qsa_dtype_t dtype)
+static ScoreLayout score_layout(int32_t rows, int32_t max_nb, int32_t top_k, qsa_dtype_t dtype)
 {
     ScoreLayout L;
     L.sc_stride = ((int64_t)max_nb + 63) / 64 * 64;
+    L.split = rows <= kRowsPathMax;
     L.qrot_off = 0;
     L.scores_off = align256((size_t)rows * kIdxHeads * kDim * elem_bytes(dtype));
-    L.total = L.scores_off + align256((size_t)rows * (size_t)L.sc_stride * sizeof(float));
+    L.scratch_off = L.scores_off + align256((size_t)rows * (size_t)L.sc_stride * sizeof(float));
+    if (!L.split) {
+        L.sure_off = L.cand_off = L.total = L.scratch_off;
+        return L;
+    }
+    L.sure_off = L.scratch_off + align256((size_t)rows * kRowScratch * sizeof(uint32_t));
+    L.cand_off = L.sure_off + align256((size_t)rows * (size_t)top_k * sizeof(uint2));
+    L.total = L.cand_off + align256((size_t)rows * (size_t)L.sc_stride * sizeof(uint2));
     return L;
 }
 
@@ -133,9 +145,8 @@ qsa_status_t qsa_pool_index_keys(const void *raw_keys, int64_t raw_seq_stride, v
 
 size_t qsa_score_topk_workspace_size(int32_t rows, int32_t max_visible_blocks, int32_t top_k, qsa_dtype_t dtype)
 {
-    (void)top_k;
-    if (rows <= 0 || max_visible_blocks < 0 || !dtype_ok(dtype)) return 0;
-    return score_layout(rows, max_visible_blocks, dtype).total;
+    if (rows <= 0 || max_visible_blocks < 0 || top_k < 1 || top_k > QSA_MAX_TOP_K || !dtype_ok(dtype)) return 0;
+    return score_layout(rows, max_visible_blocks, top_k, dtype).total;
 }
 
 qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
@@ -155,7 +166,7 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
     if (!aligned16(q_index) || !aligned16(pooled) || !row_seq || !row_pos || !sel_blocks || !sel_count)
         return QSA_ERR_INVALID_ARG;
     if (pooled_seq_stride % 8 || pooled_seq_stride < 0) return QSA_ERR_INVALID_ARG;
-    const ScoreLayout L = score_layout(rows, max_visible_blocks, dtype);
+    const ScoreLayout L = score_layout(rows, max_visible_blocks, top_k, dtype);
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return QSA_ERR_INVALID_ARG;
     if (workspace_bytes < L.total) return QSA_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
@@ -163,20 +174,34 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
     char *ws = (char *)workspace;
     void *qrot = ws + L.qrot_off;
     float *scores = (float *)(ws + L.scores_off);
+    bool gemm = bf16 && rows > kRowsPathMax;
+    if (flags & QSA_FLAG_SCORE_ROWS) gemm = false;
+    if (flags & QSA_FLAG_SCORE_GEMM) gemm = true;
+    const bool split = L.split && !gemm;
+    SplitSelect ss{};
+    if (split) {
+        ss.scratch = (uint32_t *)(ws + L.scratch_off);
+        ss.sure = (uint2 *)(ws + L.sure_off);
+        ss.cand = (uint2 *)(ws + L.cand_off);
+        ss.cand_stride = L.sc_stride;
+    }
     clear_launch_err();
-    launch_rope_query(q_index, row_pos, rows, qrot, rope_theta, flags & QSA_FLAG_NO_ROPE, bf16, st);
+    launch_rope_query(q_index, row_pos, rows, qrot, rope_theta, flags & QSA_FLAG_NO_ROPE, bf16,
+                      split ? ss.scratch : nullptr, kRowScratch, st);
     if (max_visible_blocks > 0) {
-        bool gemm = bf16 && rows > kRowsPathMax;
-        if (flags & QSA_FLAG_SCORE_ROWS) gemm = false;
-        if (flags & QSA_FLAG_SCORE_GEMM) gemm = true;
         if (gemm)
             launch_score_gemm(qrot, row_seq, row_pos, rows, pooled, pooled_seq_stride, max_visible_blocks, scores,
                               L.sc_stride, st);
         else
             launch_score_rows(qrot, row_seq, row_pos, rows, pooled, pooled_seq_stride, max_visible_blocks, scores,
-                              L.sc_stride, bf16, st);
+                              L.sc_stride, split ? ss.scratch : nullptr, bf16, st);
     }
-    launch_select_rows(scores, L.sc_stride, row_pos, rows, max_visible_blocks, top_k, sel_blocks, sel_count, sel_scores, st);
+    if (split)
+        launch_select_split(scores, L.sc_stride, row_pos, rows, max_visible_blocks, top_k, ss, sel_blocks, sel_count,
+                            sel_scores, st);
+    else
+        launch_select_rows(scores, L.sc_stride, row_pos, rows, max_visible_blocks, top_k, sel_blocks, sel_count,
+                           sel_scores, st);
     return launch_status();
 }
 

@@ -54,10 +54,13 @@ __global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ ra
 }
 
 // One wave per (row, index head): q~ = round_dtype(RoPE(q, row_pos)).
+// It also clears `zero_per_row` words of per-row select scratch (each of the
+// row's 4 waves a quarter), so the selection needs no separate fill.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_query_kernel(const T *__restrict__ q, const int32_t *__restrict__ row_pos,
                                                          int32_t rows, T *__restrict__ qrot, double theta,
-                                                         uint32_t flags)
+                                                         uint32_t flags, uint32_t *__restrict__ zero,
+                                                         int64_t zero_per_row)
 {
     __shared__ double inv_freq[kHalf];
     if (threadIdx.x < kHalf) inv_freq[threadIdx.x] = pow(theta, -(double)threadIdx.x / (double)kHalf);
@@ -66,6 +69,11 @@ __global__ __launch_bounds__(256) void rope_query_kernel(const T *__restrict__ q
     const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (w >= (int64_t)rows * kIdxHeads) return;
     const int64_t r = w / kIdxHeads;
+    if (zero) {
+        const int64_t quarter = (zero_per_row + kIdxHeads - 1) / kIdxHeads;
+        const int64_t lo = (w % kIdxHeads) * quarter, hi = min(zero_per_row, lo + quarter);
+        for (int64_t i = lo + lane; i < hi; i += kWave) zero[r * zero_per_row + i] = 0u;
+    }
     const T *src = q + w * kDim;
     double dx = load_f32(src + lane), dy = load_f32(src + kHalf + lane);
     if (!(flags & kFlagNoRope)) rope_pair(dx, dy, row_pos[r], inv_freq[lane]);
@@ -89,16 +97,16 @@ void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pool
 }
 
 void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,
-                       uint32_t flags, bool bf16, hipStream_t stream)
+                       uint32_t flags, bool bf16, uint32_t *zero, int64_t zero_per_row, hipStream_t stream)
 {
     const int64_t waves = (int64_t)rows * kIdxHeads;
     const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
     if (bf16)
         QSA_LAUNCH("rope_query", (rope_query_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)q, row_pos,
-                   rows, (bf16_t *)qrot, theta, flags);
+                   rows, (bf16_t *)qrot, theta, flags, zero, zero_per_row);
     else
         QSA_LAUNCH("rope_query", (rope_query_kernel<float>), grid, block, 0, stream, (const float *)q, row_pos,
-                   rows, (float *)qrot, theta, flags);
+                   rows, (float *)qrot, theta, flags, zero, zero_per_row);
 }
 
 }  // namespace qsa

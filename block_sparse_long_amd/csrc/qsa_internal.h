@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qsa.h"
+
 namespace qsa {
 
 constexpr int kDim = 128;       // indexer key / query dim, attention head dim
@@ -26,12 +28,15 @@ void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pool
                  int32_t block_begin, int32_t block_end, double theta, uint32_t flags, bool bf16,
                  hipStream_t stream);
 void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,
-                       uint32_t flags, bool bf16, hipStream_t stream);
+                       uint32_t flags, bool bf16, uint32_t *zero, int64_t zero_per_row, hipStream_t stream);
 
 // ---- score.hip --------------------------------------------------------------
+// Select histogram: 4096 bins of the top 12 bits of a score's order key.
+constexpr int kHistBins = 4096;
+constexpr int kHistShift = 20;
 void launch_score_rows(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
                        const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores,
-                       int64_t sc_stride, bool bf16, hipStream_t stream);
+                       int64_t sc_stride, uint32_t *hist, bool bf16, hipStream_t stream);
 void launch_score_gemm(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
                        const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores,
                        int64_t sc_stride, hipStream_t stream);
@@ -40,6 +45,21 @@ void launch_score_gemm(const void *qrot, const int32_t *row_seq, const int32_t *
 void launch_select_rows(const float *scores, int64_t sc_stride, const int32_t *row_pos, int32_t rows,
                         int32_t max_nb, int32_t top_k, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
                         hipStream_t stream);
+// Few rows: per-row scratch of the split selection (zeroed by rope_query):
+// row r owns kRowScratch words at scratch + r * kRowScratch, the histogram
+// first, then the counters (kept-for-sure count, candidate count, finished
+// chunks, unused).
+constexpr int kSelCounters = 4;
+constexpr int kRowScratch = kHistBins + kSelCounters;
+struct SplitSelect {
+    uint32_t *scratch;    // [rows][kRowScratch]
+    uint2 *sure;          // [rows][top_k] (key, block)
+    uint2 *cand;          // [rows][cand_stride] (key, block)
+    int64_t cand_stride;  // >= max_nb
+};
+void launch_select_split(const float *scores, int64_t sc_stride, const int32_t *row_pos, int32_t rows, int32_t max_nb,
+                         int32_t top_k, const SplitSelect &ss, int32_t *sel_blocks, int32_t *sel_count,
+                         float *sel_scores, hipStream_t stream);
 
 // ---- attn.hip ---------------------------------------------------------------
 // Position chunk of the attention kernels and the largest query group one

@@ -25,6 +25,22 @@ __device__ __forceinline__ float relu_sum4(f32x4_t a)
     return ((fmaxf(a[0], 0.0f) + fmaxf(a[1], 0.0f)) + fmaxf(a[2], 0.0f)) + fmaxf(a[3], 0.0f);
 }
 
+// Per-row histogram of the score keys' top 12 bits: counted in LDS, then
+// added to the row's global histogram (only the non-empty bins).
+__device__ __forceinline__ void hist_clear(uint32_t *lhist)
+{
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lhist[i] = 0u;
+    __syncthreads();
+}
+__device__ __forceinline__ void hist_flush(const uint32_t *lhist, uint32_t *ghist)
+{
+    __syncthreads();
+    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) {
+        const uint32_t c = lhist[i];
+        if (c) atomicAdd(&ghist[i], c);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Few rows, many blocks (decode): grid (chunks of 1024 blocks, rows).  The 4
 // index heads sit in MFMA rows 0..3 (rows 4..15 are zero), 16 blocks per MFMA
@@ -33,13 +49,15 @@ __device__ __forceinline__ float relu_sum4(f32x4_t a)
 __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
     const bf16_t *__restrict__ qrot, const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_pos,
     const bf16_t *__restrict__ pooled, int64_t pooled_stride, int32_t max_nb, float *__restrict__ scores,
-    int64_t sc_stride)
+    int64_t sc_stride, uint32_t *__restrict__ hist)
 {
+    __shared__ uint32_t lhist[kHistBins];
     const int r = blockIdx.y;
     const int64_t nc = min(visible_blocks(row_pos[r]), (int64_t)max_nb);
     const int64_t b_begin = (int64_t)blockIdx.x * kChunk;
     if (b_begin >= nc) return;
     const int64_t b_end = min(nc, b_begin + (int64_t)kChunk);
+    if (hist) hist_clear(lhist);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
     bf16x8_t a[4];
@@ -67,9 +85,14 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
             for (int s = 0; s < 4; ++s)
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], as_bf16x8(v[nt][s]), acc, 0, 0, 0);
             const int64_t b = base + nt * 16 + m;
-            if (g == 0 && b < b_end) srow[b] = relu_sum4(acc);
+            if (g == 0 && b < b_end) {
+                const float sc = relu_sum4(acc);
+                srow[b] = sc;
+                if (hist) atomicAdd(&lhist[score_key(sc) >> kHistShift], 1u);
+            }
         }
     }
+    if (hist) hist_flush(lhist, hist + (int64_t)r * kRowScratch);
 }
 
 // ---------------------------------------------------------------------------
@@ -78,14 +101,16 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
 __global__ __launch_bounds__(256) void score_rows_f32_kernel(
     const float *__restrict__ qrot, const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_pos,
     const float *__restrict__ pooled, int64_t pooled_stride, int32_t max_nb, float *__restrict__ scores,
-    int64_t sc_stride)
+    int64_t sc_stride, uint32_t *__restrict__ hist)
 {
     __shared__ float4 qs[kIdxHeads * kDim / 4];
+    __shared__ uint32_t lhist[kHistBins];
     const int r = blockIdx.y;
     const int64_t nc = min(visible_blocks(row_pos[r]), (int64_t)max_nb);
     const int64_t b_begin = (int64_t)blockIdx.x * kChunk;
     if (b_begin >= nc) return;
     const int64_t b_end = min(nc, b_begin + (int64_t)kChunk);
+    if (hist) hist_clear(lhist);
     for (int i = threadIdx.x; i < kIdxHeads * kDim / 4; i += blockDim.x)
         qs[i] = ((const float4 *)(qrot + (int64_t)r * kIdxHeads * kDim))[i];
     __syncthreads();
@@ -104,9 +129,11 @@ __global__ __launch_bounds__(256) void score_rows_f32_kernel(
                 d[h] = fmaf(qv.w, kv.w, d[h]);
             }
         }
-        scores[(int64_t)r * sc_stride + b] =
-            ((fmaxf(d[0], 0.0f) + fmaxf(d[1], 0.0f)) + fmaxf(d[2], 0.0f)) + fmaxf(d[3], 0.0f);
+        const float sc = ((fmaxf(d[0], 0.0f) + fmaxf(d[1], 0.0f)) + fmaxf(d[2], 0.0f)) + fmaxf(d[3], 0.0f);
+        scores[(int64_t)r * sc_stride + b] = sc;
+        if (hist) atomicAdd(&lhist[score_key(sc) >> kHistShift], 1u);
     }
+    if (hist) hist_flush(lhist, hist + (int64_t)r * kRowScratch);
 }
 
 // ---------------------------------------------------------------------------
@@ -195,15 +222,15 @@ int64_t score_chunks(int32_t max_nb) { return ((int64_t)max_nb + kChunk - 1) / k
 
 void launch_score_rows(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
                        const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores, int64_t sc_stride,
-                       bool bf16, hipStream_t stream)
+                       uint32_t *hist, bool bf16, hipStream_t stream)
 {
     const dim3 grid((unsigned)score_chunks(max_nb), (unsigned)rows), block(256);
     if (bf16)
         QSA_LAUNCH("score_rows_bf16", score_rows_bf16_kernel, grid, block, 0, stream, (const bf16_t *)qrot, row_seq,
-                   row_pos, (const bf16_t *)pooled, pooled_stride, max_nb, scores, sc_stride);
+                   row_pos, (const bf16_t *)pooled, pooled_stride, max_nb, scores, sc_stride, hist);
     else
         QSA_LAUNCH("score_rows_f32", score_rows_f32_kernel, grid, block, 0, stream, (const float *)qrot, row_seq,
-                   row_pos, (const float *)pooled, pooled_stride, max_nb, scores, sc_stride);
+                   row_pos, (const float *)pooled, pooled_stride, max_nb, scores, sc_stride, hist);
 }
 
 void launch_score_gemm(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,

@@ -21,7 +21,8 @@
 namespace qsa {
 
 constexpr int kSelThreads = 512;
-constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSplitThreads = 256;
+constexpr int kCollectChunk = 4096;  // blocks per collect workgroup
 
 // Reported score s = raw / sqrt(128) (the score equation's scale), divided in
 // double and rounded once to float.
@@ -29,8 +30,10 @@ __device__ __forceinline__ float scaled_score(float raw) { return (float)((doubl
 
 // Exclusive rank of `pred` among the workgroup's threads (thread order) and
 // the workgroup-wide count.  Every thread must call it.
+template <int NT>
 __device__ __forceinline__ uint32_t wg_rank(bool pred, uint32_t *wtot, uint32_t &total)
 {
+    constexpr int kSelWaves = NT / kWave;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint64_t m = __ballot(pred);
     const uint32_t in_wave = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
@@ -49,8 +52,10 @@ __device__ __forceinline__ uint32_t wg_rank(bool pred, uint32_t *wtot, uint32_t 
 }
 
 // Inclusive scan of a per-thread count over the workgroup (thread order).
+template <int NT>
 __device__ __forceinline__ uint32_t wg_inclusive_scan(uint32_t v, uint32_t *wtot)
 {
+    constexpr int kSelWaves = NT / kWave;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t x = v;
 #pragma unroll
@@ -69,15 +74,16 @@ __device__ __forceinline__ uint32_t wg_inclusive_scan(uint32_t v, uint32_t *wtot
 
 // Bin b* of `hist` (nbins = 4096 or 256, scanned from the top) such that
 // above(b*) < need <= above(b*) + hist[b*]; writes b* and above(b*) to LDS.
+template <int NT>
 __device__ __forceinline__ void find_bin(const uint32_t *hist, int nbins, uint32_t need, uint32_t *wtot,
                                          uint32_t *out_bin, uint32_t *out_above)
 {
-    const int per = nbins / kSelThreads > 0 ? nbins / kSelThreads : 1;
+    const int per = nbins / NT > 0 ? nbins / NT : 1;
     const int owned = (int)threadIdx.x * per < nbins ? per : 0;
     const int hi = nbins - (int)threadIdx.x * per;  // this thread owns [hi - owned, hi)
     uint32_t sum = 0;
     for (int i = 0; i < owned; ++i) sum += hist[hi - 1 - i];
-    const uint32_t incl = wg_inclusive_scan(sum, wtot);
+    const uint32_t incl = wg_inclusive_scan<NT>(sum, wtot);
     const uint32_t before = incl - sum;
     if (owned && before < need && incl >= need) {
         uint32_t acc = before;
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(const float *_
                                                                   float *__restrict__ sel_scores)
 {
     __shared__ uint32_t hist[4096];
-    __shared__ uint32_t wtot[kSelWaves];
+    __shared__ uint32_t wtot[kSelThreads / kWave];
     __shared__ uint32_t s_bin, s_above;
     const int64_t r = blockIdx.x;
     const int32_t nc = (int32_t)min(visible_blocks(row_pos[r]), (int64_t)max_nb);  // max_nb: caller's bound
@@ -138,7 +144,7 @@ __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(const float *_
             if (sh == 32 || (key >> sh) == prefix) atomicAdd(&hist[(key >> nsh) & (uint32_t)(nbins - 1)], 1u);
         }
         __syncthreads();
-        find_bin(hist, nbins, need, wtot, &s_bin, &s_above);
+        find_bin<kSelThreads>(hist, nbins, need, wtot, &s_bin, &s_above);
         const uint32_t bin = s_bin, above = s_above;
         const uint32_t cnt = hist[bin];
         __syncthreads();
@@ -157,9 +163,9 @@ __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(const float *_
         const bool gt = valid && top > prefix;
         const bool eq = valid && top == prefix;
         uint32_t eq_total, take_total;
-        const uint32_t eq_rank = eq_before + wg_rank(eq, wtot, eq_total);
+        const uint32_t eq_rank = eq_before + wg_rank<kSelThreads>(eq, wtot, eq_total);
         const bool take = gt || (eq && eq_rank < need);
-        const uint32_t pos = out_before + wg_rank(take, wtot, take_total);
+        const uint32_t pos = out_before + wg_rank<kSelThreads>(take, wtot, take_total);
         if (take && pos < (uint32_t)kk) {
             out[pos] = b;
             if (osc) osc[pos] = scaled_score(sc);
@@ -174,6 +180,169 @@ void launch_select_rows(const float *scores, int64_t sc_stride, const int32_t *r
 {
     QSA_LAUNCH("select_rows", select_rows_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, stream, scores,
                sc_stride, row_pos, max_nb, top_k, sel_blocks, sel_count, sel_scores);
+}
+
+// ---------------------------------------------------------------------------
+// Few rows, many blocks: the selection split over many workgroups.
+//   - the scorer has filled the row's 12-bit key histogram;
+//   - collect (grid: chunks of 4096 blocks x rows): every workgroup finds the
+//     bin b* holding the k-th best key, then appends the blocks of its chunk
+//     above b* to the row's "sure" list and those inside b* to its candidate
+//     list;
+//   - the workgroup that finishes a row's last chunk picks the missing
+//     `need` entries among the candidates with a radix select on the unique
+//     composite (low 20 key bits, ~block) -- a higher score first, then the
+//     lower block -- and writes the kept set sorted by block id.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void wave_append(bool pred, uint2 item, uint32_t *counter, uint2 *list)
+{
+    const uint64_t mask = __ballot(pred);
+    if (!mask) return;
+    const int lane = threadIdx.x & 63;
+    const uint32_t n = (uint32_t)__popcll(mask);
+    const int leader = __ffsll((unsigned long long)mask) - 1;
+    uint32_t base = 0;
+    if (lane == leader) base = atomicAdd(counter, n);
+    base = __shfl(base, leader);
+    if (pred) list[base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull))] = item;
+}
+
+__device__ __forceinline__ uint64_t composite20(uint2 e)
+{
+    return ((uint64_t)(e.x & 0x000fffffu) << 32) | (uint64_t)(~e.y);
+}
+
+__global__ __launch_bounds__(kSplitThreads) void select_collect_kernel(
+    const float *__restrict__ scores, int64_t sc_stride, const int32_t *__restrict__ row_pos, int32_t max_nb,
+    int32_t top_k, SplitSelect ss, int32_t *__restrict__ sel_blocks, int32_t *__restrict__ sel_count,
+    float *__restrict__ sel_scores)
+{
+    __shared__ uint64_t buf[QSA_MAX_TOP_K];
+    __shared__ uint32_t dhist[256];
+    __shared__ uint32_t wtot[kSplitThreads / kWave];
+    __shared__ uint32_t s_bin, s_above, s_ticket, s_digit, s_dabove, s_dcnt, s_fill;
+    const int t = threadIdx.x;
+    const int64_t r = blockIdx.y;
+    const int32_t nc = (int32_t)min(visible_blocks(row_pos[r]), (int64_t)max_nb);
+    const int32_t kk = min(top_k, nc);
+    const float *srow = scores + r * sc_stride;
+    int32_t *out = sel_blocks + r * top_k;
+    float *osc = sel_scores ? sel_scores + r * top_k : nullptr;
+    uint32_t *hist = ss.scratch + r * kRowScratch;
+    uint32_t *cnt = hist + kHistBins;
+    uint2 *sure = ss.sure + r * top_k;
+    uint2 *cand = ss.cand + r * ss.cand_stride;
+    const int64_t b_begin = (int64_t)blockIdx.x * kCollectChunk;
+    if (nc <= top_k) {  // every visible block is kept: one workgroup writes the row
+        if (blockIdx.x != 0) return;
+        if (t == 0) sel_count[r] = kk;
+        for (int32_t i = t; i < top_k; i += kSplitThreads) {
+            out[i] = i < nc ? i : -1;
+            if (osc) osc[i] = i < nc ? scaled_score(srow[i]) : 0.0f;
+        }
+        return;
+    }
+    if (b_begin >= nc) return;
+    // ---- collect ----
+    find_bin<kSplitThreads>(hist, kHistBins, (uint32_t)kk, wtot, &s_bin, &s_above);
+    const uint32_t beta = s_bin;
+    const int64_t b_end = min((int64_t)nc, b_begin + kCollectChunk);
+    for (int64_t b0 = b_begin; b0 < b_end; b0 += kSplitThreads) {
+        const int64_t b = b0 + t;
+        const bool valid = b < b_end;
+        const uint32_t key = valid ? score_key(srow[b]) : 0u;
+        const uint32_t bin = key >> kHistShift;
+        const uint2 item = make_uint2(key, (uint32_t)b);
+        wave_append(valid && bin > beta, item, &cnt[0], sure);
+        wave_append(valid && bin == beta, item, &cnt[1], cand);
+    }
+    // ---- the last workgroup of the row finishes it ----
+    __threadfence();
+    __syncthreads();
+    if (t == 0) s_ticket = atomicAdd(&cnt[2], 1u);
+    __syncthreads();
+    const uint32_t nchunks = (uint32_t)((nc + kCollectChunk - 1) / kCollectChunk);
+    if (s_ticket != nchunks - 1) return;
+    __threadfence();
+    const uint32_t n_sure = __atomic_load_n(&cnt[0], __ATOMIC_RELAXED);
+    const uint32_t n_cand = __atomic_load_n(&cnt[1], __ATOMIC_RELAXED);
+    uint32_t need = (uint32_t)kk - n_sure;  // 1 <= need <= n_cand
+    uint64_t prefix = 0, pmask = 0;
+    if (need < n_cand) {
+        for (int sh = 44;; sh -= 8) {  // 8-bit digits of the 52-bit composite, from the top
+            const int s2 = sh < 0 ? 0 : sh;
+            const uint32_t dmask = sh < 0 ? (1u << (8 + sh)) - 1u : 0xffu;
+            dhist[t] = 0u;
+            __syncthreads();
+            for (uint32_t i = t; i < n_cand; i += kSplitThreads) {
+                const uint64_t c = composite20(cand[i]);
+                if ((c & pmask) == prefix) atomicAdd(&dhist[(uint32_t)(c >> s2) & dmask], 1u);
+            }
+            __syncthreads();
+            const uint32_t hv = dhist[255 - t];
+            const uint32_t incl = wg_inclusive_scan<kSplitThreads>(hv, wtot);
+            if (hv && incl - hv < need && incl >= need) {
+                s_digit = 255u - (uint32_t)t;
+                s_dabove = incl - hv;
+                s_dcnt = hv;
+            }
+            __syncthreads();
+            prefix |= (uint64_t)s_digit << s2;
+            pmask |= (uint64_t)dmask << s2;
+            need -= s_dabove;
+            const bool done = s_dcnt == need || s2 == 0;
+            __syncthreads();
+            if (done) break;
+        }
+    }
+    // ---- kept set: the sure entries and the picked candidates ----
+    if (t == 0) s_fill = 0;
+    __syncthreads();
+    for (uint32_t i = t; i < n_sure; i += kSplitThreads) {
+        const uint2 e = sure[i];
+        buf[atomicAdd(&s_fill, 1u)] = ((uint64_t)e.y << 32) | e.x;
+    }
+    for (uint32_t i = t; i < n_cand; i += kSplitThreads) {
+        const uint2 e = cand[i];
+        if ((composite20(e) & pmask) >= prefix) buf[atomicAdd(&s_fill, 1u)] = ((uint64_t)e.y << 32) | e.x;
+    }
+    __syncthreads();
+    const uint32_t n = min(s_fill, (uint32_t)kk);
+    uint32_t n2 = 1;
+    while (n2 < n) n2 <<= 1;
+    for (uint32_t i = n + t; i < n2; i += kSplitThreads) buf[i] = ~0ull;
+    __syncthreads();
+    for (uint32_t size = 2; size <= n2; size <<= 1) {  // bitonic sort by block id
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            for (uint32_t i = t; i < n2 / 2; i += kSplitThreads) {
+                const uint32_t lo = 2 * i - (i & (stride - 1));
+                const uint32_t hi = lo + stride;
+                const bool up = (lo & size) == 0;
+                const uint64_t x = buf[lo], y = buf[hi];
+                if ((x > y) == up) {
+                    buf[lo] = y;
+                    buf[hi] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (t == 0) sel_count[r] = (int32_t)n;
+    for (int32_t i = t; i < top_k; i += kSplitThreads) {
+        const bool kept = (uint32_t)i < n;
+        const uint64_t e = kept ? buf[i] : 0ull;
+        out[i] = kept ? (int32_t)(e >> 32) : -1;
+        if (osc) osc[i] = kept ? scaled_score(key_score((uint32_t)e)) : 0.0f;
+    }
+}
+
+void launch_select_split(const float *scores, int64_t sc_stride, const int32_t *row_pos, int32_t rows, int32_t max_nb,
+                         int32_t top_k, const SplitSelect &ss, int32_t *sel_blocks, int32_t *sel_count,
+                         float *sel_scores, hipStream_t stream)
+{
+    const int64_t chunks = max((int64_t)1, ((int64_t)max_nb + kCollectChunk - 1) / kCollectChunk);
+    QSA_LAUNCH("select_collect", select_collect_kernel, dim3((unsigned)chunks, (unsigned)rows), dim3(kSplitThreads),
+               0, stream, scores, sc_stride, row_pos, max_nb, top_k, ss, sel_blocks, sel_count, sel_scores);
 }
 
 }  // namespace qsa

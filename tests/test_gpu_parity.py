@@ -116,10 +116,13 @@ def _score_case(seed, dtype, B, NB, R, k, integer=False):
     return pooled, iq, seq, pos
 
 
-@pytest.mark.parametrize("dtype,path", [("bf16", "rows"), ("bf16", "gemm"), ("f32", "rows")])
+@pytest.mark.parametrize("dtype,path,R,NB", [("bf16", "rows", 90, 2600), ("bf16", "gemm", 90, 2600),
+                                             ("f32", "rows", 90, 2600), ("bf16", "rows", 40, 9001),
+                                             ("f32", "rows", 13, 9001), ("bf16", "gemm", 40, 9001)])
 @pytest.mark.parametrize("k", [512, 37])
-def test_score_topk_matches_oracle(gpu, dtype, path, k):
-    B, NB, R = 2, 2600, 90
+def test_score_topk_matches_oracle(gpu, dtype, path, R, NB, k):
+    # 90 rows: per-row select; <= 64 rows: the split select (several chunks at 9001 blocks)
+    B = 2
     pooled, iq, seq, pos = _score_case(11 + k, dtype, B, NB, R, k)
     o_sel, o_cnt, o_sc, o_raw = oracle.score_topk(iq, seq, pos, pooled, k, THETA, want_raw=True)
     sel, cnt, sc = qsa.score_topk(dev(iq, dtype), dev(seq, "i"), dev(pos, "i"), dev(pooled, dtype), NB, k,
@@ -133,9 +136,11 @@ def test_score_topk_matches_oracle(gpu, dtype, path, k):
         assert np.all(g_sc[r, n:] == 0)
 
 
-@pytest.mark.parametrize("dtype,path", [("bf16", "rows"), ("bf16", "gemm"), ("f32", "rows")])
-def test_score_topk_integer_inputs_bit_exact(gpu, dtype, path):
-    B, NB, R, k = 2, 1500, 80, 64
+@pytest.mark.parametrize("dtype,path,R,NB", [("bf16", "rows", 80, 1500), ("bf16", "gemm", 80, 1500),
+                                             ("f32", "rows", 80, 1500), ("bf16", "rows", 30, 9001),
+                                             ("f32", "rows", 30, 9001)])
+def test_score_topk_integer_inputs_bit_exact(gpu, dtype, path, R, NB):
+    B, k = 2, 64
     pooled, iq, seq, pos = _score_case(5, dtype, B, NB, R, k, integer=True)
     o_sel, o_cnt, o_sc, o_raw = oracle.score_topk(iq, seq, pos, pooled, k, THETA, qsa.FLAG_NO_ROPE,
                                                   want_raw=True)
