@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libqsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "pool.hip", "score.hip", "select.hip", "attn.hip", "attn_mfma.hip"]
+SOURCES = ["api.cpp", "pool.hip", "score.hip", "select.hip", "attn.hip", "attn_mfma.hip", "score_fused.hip"]
 
 
 def hipcc() -> str:

@@ -78,30 +78,46 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // MFMA GEMM scorer, which shares each key tile among 16 rows.
 constexpr int32_t kRowsPathMax = 64;
 
-// Workspace of qsa_score_topk: rotated index queries and fp32 scores; for
-// few rows also the split selection's per-row scratch, kept-for-sure and
-// candidate lists.
+// Workspace of qsa_score_topk.  Few rows: rotated index queries, fp32
+// scores, the split selection's per-row scratch, kept-for-sure and candidate
+// lists.  Many rows (bf16): rotated index queries and the fused scorer's
+// per-(row, split) pair buffers, counts and thresholds.
 struct ScoreLayout {
+    bool few;
     int64_t sc_stride;
-    bool split;
-    size_t qrot_off, scores_off, scratch_off, sure_off, cand_off, total;
+    size_t qrot_off, scores_off, scratch_off, sure_off, cand_off;
+    int32_t nsplit, split_len, cap;
+    size_t buf_off, cnt_off, tau_off;
+    size_t total;
 };
 
 static ScoreLayout score_layout(int32_t rows, int32_t max_nb, int32_t top_k, qsa_dtype_t dtype)
 {
-    ScoreLayout L;
+    ScoreLayout L{};
+    L.few = rows <= kRowsPathMax || dtype != QSA_BF16;
     L.sc_stride = ((int64_t)max_nb + 63) / 64 * 64;
-    L.split = rows <= kRowsPathMax;
     L.qrot_off = 0;
-    L.scores_off = align256((size_t)rows * kIdxHeads * kDim * elem_bytes(dtype));
-    L.scratch_off = L.scores_off + align256((size_t)rows * (size_t)L.sc_stride * sizeof(float));
-    if (!L.split) {
-        L.sure_off = L.cand_off = L.total = L.scratch_off;
-        return L;
+    const size_t after_q = align256((size_t)rows * kIdxHeads * kDim * elem_bytes(dtype));
+    // scores (every layout keeps them: the per-row scorer is selectable by flag)
+    L.scores_off = after_q;
+    size_t off = L.scores_off + align256((size_t)rows * (size_t)L.sc_stride * sizeof(float));
+    size_t few_total = 0, fused_total = 0;
+    if (L.few) {  // split selection scratch
+        L.scratch_off = off;
+        L.sure_off = L.scratch_off + align256((size_t)rows * kRowScratch * sizeof(uint32_t));
+        L.cand_off = L.sure_off + align256((size_t)rows * (size_t)top_k * sizeof(uint2));
+        few_total = L.cand_off + align256((size_t)rows * (size_t)L.sc_stride * sizeof(uint2));
     }
-    L.sure_off = L.scratch_off + align256((size_t)rows * kRowScratch * sizeof(uint32_t));
-    L.cand_off = L.sure_off + align256((size_t)rows * (size_t)top_k * sizeof(uint2));
-    L.total = L.cand_off + align256((size_t)rows * (size_t)L.sc_stride * sizeof(uint2));
+    if (dtype == QSA_BF16) {  // fused scorer buffers (alternative use of the same bytes)
+        L.nsplit = fused_score_splits(rows, max_nb);
+        L.split_len = fused_score_split_len(max_nb, L.nsplit);
+        L.cap = fused_score_cap(top_k);
+        L.buf_off = off;
+        L.cnt_off = L.buf_off + align256((size_t)rows * L.nsplit * (size_t)L.cap * sizeof(uint2));
+        L.tau_off = L.cnt_off + align256((size_t)rows * L.nsplit * sizeof(uint32_t));
+        fused_total = L.tau_off + align256((size_t)rows * L.nsplit * sizeof(uint32_t));
+    }
+    L.total = few_total > fused_total ? few_total : fused_total;
     return L;
 }
 
@@ -160,7 +176,6 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
     const uint32_t known = QSA_FLAG_NO_ROPE | QSA_FLAG_SCORE_ROWS | QSA_FLAG_SCORE_GEMM;
     if (flags & ~known) return QSA_ERR_INVALID_ARG;
     if ((flags & QSA_FLAG_SCORE_ROWS) && (flags & QSA_FLAG_SCORE_GEMM)) return QSA_ERR_INVALID_ARG;
-    if ((flags & QSA_FLAG_SCORE_GEMM) && dtype != QSA_BF16) return QSA_ERR_UNSUPPORTED;
     if (!(flags & QSA_FLAG_NO_ROPE) && !(rope_theta > 1.0 && std::isfinite(rope_theta))) return QSA_ERR_INVALID_ARG;
     if (rows == 0) return QSA_OK;
     if (!aligned16(q_index) || !aligned16(pooled) || !row_seq || !row_pos || !sel_blocks || !sel_count)
@@ -174,10 +189,15 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
     char *ws = (char *)workspace;
     void *qrot = ws + L.qrot_off;
     float *scores = (float *)(ws + L.scores_off);
-    bool gemm = bf16 && rows > kRowsPathMax;
-    if (flags & QSA_FLAG_SCORE_ROWS) gemm = false;
-    if (flags & QSA_FLAG_SCORE_GEMM) gemm = true;
-    const bool split = L.split && !gemm;
+    // many bf16 rows: the fused MFMA scorer + merge; few rows (or the per-row
+    // flag): per-row streaming scorer with a split (few) or per-row select
+    bool fused = !L.few;
+    if (flags & QSA_FLAG_SCORE_ROWS) fused = false;
+    if (flags & QSA_FLAG_SCORE_GEMM) {
+        if (!bf16) return QSA_ERR_UNSUPPORTED;
+        fused = true;
+    }
+    const bool split = L.few && !fused;
     SplitSelect ss{};
     if (split) {
         ss.scratch = (uint32_t *)(ws + L.scratch_off);
@@ -188,14 +208,28 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
     clear_launch_err();
     launch_rope_query(q_index, row_pos, rows, qrot, rope_theta, flags & QSA_FLAG_NO_ROPE, bf16,
                       split ? ss.scratch : nullptr, kRowScratch, st);
-    if (max_visible_blocks > 0) {
-        if (gemm)
-            launch_score_gemm(qrot, row_seq, row_pos, rows, pooled, pooled_seq_stride, max_visible_blocks, scores,
-                              L.sc_stride, st);
-        else
-            launch_score_rows(qrot, row_seq, row_pos, rows, pooled, pooled_seq_stride, max_visible_blocks, scores,
-                              L.sc_stride, split ? ss.scratch : nullptr, bf16, st);
+    if (fused) {
+        FusedScoreArgs fa{};
+        fa.qrot = (const uint16_t *)qrot;
+        fa.row_seq = row_seq;
+        fa.row_pos = row_pos;
+        fa.rows = rows;
+        fa.pooled = (const uint16_t *)pooled;
+        fa.pooled_stride = pooled_seq_stride;
+        fa.max_nb = max_visible_blocks;
+        fa.top_k = top_k;
+        fa.nsplit = L.nsplit;
+        fa.split_len = L.split_len;
+        fa.cap = L.cap;
+        fa.buf = (uint2 *)(ws + L.buf_off);
+        fa.cnt = (uint32_t *)(ws + L.cnt_off);
+        fa.tau = (uint32_t *)(ws + L.tau_off);
+        launch_score_fused(fa, sel_blocks, sel_count, sel_scores, st);
+        return launch_status();
     }
+    if (max_visible_blocks > 0)
+        launch_score_rows(qrot, row_seq, row_pos, rows, pooled, pooled_seq_stride, max_visible_blocks, scores,
+                          L.sc_stride, split ? ss.scratch : nullptr, bf16, st);
     if (split)
         launch_select_split(scores, L.sc_stride, row_pos, rows, max_visible_blocks, top_k, ss, sel_blocks, sel_count,
                             sel_scores, st);

@@ -41,6 +41,29 @@ void launch_score_gemm(const void *qrot, const int32_t *row_seq, const int32_t *
                        const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores,
                        int64_t sc_stride, hipStream_t stream);
 
+// ---- score_fused.hip (many rows, bf16) ----------------------------------------
+struct FusedScoreArgs {
+    const uint16_t *qrot;     // [rows][4][128] rotated index queries (bf16)
+    const int32_t *row_seq;
+    const int32_t *row_pos;
+    int32_t rows;
+    const uint16_t *pooled;   // [B][pooled_stride] (bf16)
+    int64_t pooled_stride;
+    int32_t max_nb;
+    int32_t top_k;
+    int32_t nsplit;           // block-range splits
+    int32_t split_len;        // blocks per split (multiple of 64)
+    int32_t cap;              // pair-buffer capacity per (row, split)
+    uint2 *buf;               // [rows][nsplit][cap] (key, block)
+    uint32_t *cnt;            // [rows][nsplit] pairs written (may exceed cap: overflow)
+    uint32_t *tau;            // [rows][nsplit] final threshold key
+};
+int32_t fused_score_splits(int32_t rows, int32_t max_nb);
+int32_t fused_score_split_len(int32_t max_nb, int32_t nsplit);
+int32_t fused_score_cap(int32_t top_k);
+void launch_score_fused(const FusedScoreArgs &a, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
+                        hipStream_t stream);
+
 // ---- select.hip -------------------------------------------------------------
 void launch_select_rows(const float *scores, int64_t sc_stride, const int32_t *row_pos, int32_t rows,
                         int32_t max_nb, int32_t top_k, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,

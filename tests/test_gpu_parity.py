@@ -151,6 +151,30 @@ def test_score_topk_integer_inputs_bit_exact(gpu, dtype, path, R, NB):
     np.testing.assert_array_equal(host(sc), o_sc)
 
 
+def test_score_topk_all_ties_lowest_blocks_win(gpu):
+    # every pooled key identical: every visible block scores the same, so the
+    # kept set is blocks 0..k-1 (ties go to the lower block).  With 4,100 rows
+    # the fused scorer's per-split pair buffers overflow and the merge redoes
+    # the rows from recomputed scores.
+    rng = np.random.default_rng(17)
+    NB, R, k = 40000, 4100, 512
+    key = rng.integers(-4, 5, size=DIM).astype(np.float32)
+    pooled = synth.bf16_bits(np.broadcast_to(key, (1, NB, DIM)).copy())
+    iq = rng.integers(-3, 4, size=(R, 4, DIM)).astype(np.float32)
+    pos = rng.integers(0, 4 * NB, R).astype(np.int32)
+    pos[:2] = [4 * NB - 1, 4 * k + 1]
+    sel, cnt, sc = qsa.score_topk(dev(synth.bf16_bits(iq), "bf16"), dev(np.zeros(R, np.int32), "i"),
+                                  dev(pos, "i"), dev(pooled, "bf16"), NB, k, THETA, flags=qsa.FLAG_NO_ROPE)
+    sel, cnt, sc = host(sel), host(cnt), host(sc)
+    raw = np.maximum(iq.astype(np.float64) @ key.astype(np.float64), 0).sum(1)
+    for r in range(R):
+        n = min(k, (int(pos[r]) + 1) // 4)
+        assert cnt[r] == n
+        np.testing.assert_array_equal(sel[r, :n], np.arange(n))
+        assert np.all(sel[r, n:] == -1)
+        np.testing.assert_array_equal(sc[r, :n], np.float32(raw[r] / math.sqrt(128)))
+
+
 def test_score_topk_default_paths_agree(gpu):
     # few rows take the streaming scorer, many rows the GEMM: same answer
     B, NB, R, k = 1, 3000, 130, 100
