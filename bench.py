@@ -153,7 +153,7 @@ def timed(run_step, steps, warmup):
 
 
 ALL_KERNELS = ["pool_rope", "rope_query", "score_rows_bf16", "score_rows_f32", "score_gemm_bf16", "select_rows",
-               "select_collect", "attn_prefill_mfma", "attn_decode_mfma",
+               "select_collect", "score_filter", "select_merge", "attn_prefill_mfma", "attn_decode_mfma",
                "attn_prefill", "attn_decode", "attn_combine"]
 
 

@@ -78,12 +78,30 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // MFMA GEMM scorer, which shares each key tile among 16 rows.
 constexpr int32_t kRowsPathMax = 64;
 
-// Workspace of qsa_score_topk.  Few rows: rotated index queries, fp32
-// scores, the split selection's per-row scratch, kept-for-sure and candidate
-// lists.  Many rows (bf16): rotated index queries and the fused scorer's
-// per-(row, split) pair buffers, counts and thresholds.
+// Which kernels qsa_score_topk runs: many bf16 rows take the fused MFMA
+// scorer + merge; few rows (or QSA_FLAG_SCORE_ROWS) the per-row streaming
+// scorer, followed by the split selection (few rows) or the per-row select.
+struct ScorePlan {
+    bool fused, split;
+};
+
+static ScorePlan score_plan(int32_t rows, qsa_dtype_t dtype, uint32_t flags)
+{
+    const bool few = rows <= kRowsPathMax || dtype != QSA_BF16;
+    ScorePlan p;
+    p.fused = !few;
+    if (flags & QSA_FLAG_SCORE_ROWS) p.fused = false;
+    if (flags & QSA_FLAG_SCORE_GEMM) p.fused = true;
+    p.split = few && !p.fused;
+    return p;
+}
+
+// Workspace of qsa_score_topk: rotated index queries, then either the fp32
+// scores (+ the split selection's per-row scratch, kept-for-sure and
+// candidate lists) or the fused scorer's per-(row, split) pair buffers,
+// counts and thresholds.
 struct ScoreLayout {
-    bool few;
+    ScorePlan plan;
     int64_t sc_stride;
     size_t qrot_off, scores_off, scratch_off, sure_off, cand_off;
     int32_t nsplit, split_len, cap;
@@ -91,34 +109,40 @@ struct ScoreLayout {
     size_t total;
 };
 
-static ScoreLayout score_layout(int32_t rows, int32_t max_nb, int32_t top_k, qsa_dtype_t dtype)
+static ScoreLayout score_layout(int32_t rows, int32_t max_nb, int32_t top_k, qsa_dtype_t dtype, uint32_t flags)
 {
     ScoreLayout L{};
-    L.few = rows <= kRowsPathMax || dtype != QSA_BF16;
+    L.plan = score_plan(rows, dtype, flags);
     L.sc_stride = ((int64_t)max_nb + 63) / 64 * 64;
     L.qrot_off = 0;
-    const size_t after_q = align256((size_t)rows * kIdxHeads * kDim * elem_bytes(dtype));
-    // scores (every layout keeps them: the per-row scorer is selectable by flag)
-    L.scores_off = after_q;
-    size_t off = L.scores_off + align256((size_t)rows * (size_t)L.sc_stride * sizeof(float));
-    size_t few_total = 0, fused_total = 0;
-    if (L.few) {  // split selection scratch
-        L.scratch_off = off;
-        L.sure_off = L.scratch_off + align256((size_t)rows * kRowScratch * sizeof(uint32_t));
-        L.cand_off = L.sure_off + align256((size_t)rows * (size_t)top_k * sizeof(uint2));
-        few_total = L.cand_off + align256((size_t)rows * (size_t)L.sc_stride * sizeof(uint2));
-    }
-    if (dtype == QSA_BF16) {  // fused scorer buffers (alternative use of the same bytes)
+    const size_t off = align256((size_t)rows * kIdxHeads * kDim * elem_bytes(dtype));
+    if (L.plan.fused) {
         L.nsplit = fused_score_splits(rows, max_nb);
         L.split_len = fused_score_split_len(max_nb, L.nsplit);
         L.cap = fused_score_cap(top_k);
         L.buf_off = off;
         L.cnt_off = L.buf_off + align256((size_t)rows * L.nsplit * (size_t)L.cap * sizeof(uint2));
         L.tau_off = L.cnt_off + align256((size_t)rows * L.nsplit * sizeof(uint32_t));
-        fused_total = L.tau_off + align256((size_t)rows * L.nsplit * sizeof(uint32_t));
+        L.total = L.tau_off + align256((size_t)rows * L.nsplit * sizeof(uint32_t));
+        return L;
     }
-    L.total = few_total > fused_total ? few_total : fused_total;
+    L.scores_off = off;
+    L.total = L.scores_off + align256((size_t)rows * (size_t)L.sc_stride * sizeof(float));
+    if (L.plan.split) {
+        L.scratch_off = L.total;
+        L.sure_off = L.scratch_off + align256((size_t)rows * kRowScratch * sizeof(uint32_t));
+        L.cand_off = L.sure_off + align256((size_t)rows * (size_t)top_k * sizeof(uint2));
+        L.total = L.cand_off + align256((size_t)rows * (size_t)L.sc_stride * sizeof(uint2));
+    }
     return L;
+}
+
+static bool score_flags_ok(uint32_t flags, qsa_dtype_t dtype)
+{
+    const uint32_t known = QSA_FLAG_NO_ROPE | QSA_FLAG_SCORE_ROWS | QSA_FLAG_SCORE_GEMM;
+    if (flags & ~known) return false;
+    if ((flags & QSA_FLAG_SCORE_ROWS) && (flags & QSA_FLAG_SCORE_GEMM)) return false;
+    return true;
 }
 
 }  // namespace qsa
@@ -159,10 +183,12 @@ qsa_status_t qsa_pool_index_keys(const void *raw_keys, int64_t raw_seq_stride, v
     return launch_status();
 }
 
-size_t qsa_score_topk_workspace_size(int32_t rows, int32_t max_visible_blocks, int32_t top_k, qsa_dtype_t dtype)
+size_t qsa_score_topk_workspace_size(int32_t rows, int32_t max_visible_blocks, int32_t top_k, qsa_dtype_t dtype,
+                                     uint32_t flags)
 {
     if (rows <= 0 || max_visible_blocks < 0 || top_k < 1 || top_k > QSA_MAX_TOP_K || !dtype_ok(dtype)) return 0;
-    return score_layout(rows, max_visible_blocks, top_k, dtype).total;
+    if (!score_flags_ok(flags, dtype)) return 0;
+    return score_layout(rows, max_visible_blocks, top_k, dtype, flags).total;
 }
 
 qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
@@ -173,33 +199,22 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
 {
     if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
     if (rows < 0 || max_visible_blocks < 0 || top_k < 1 || top_k > QSA_MAX_TOP_K) return QSA_ERR_INVALID_ARG;
-    const uint32_t known = QSA_FLAG_NO_ROPE | QSA_FLAG_SCORE_ROWS | QSA_FLAG_SCORE_GEMM;
-    if (flags & ~known) return QSA_ERR_INVALID_ARG;
-    if ((flags & QSA_FLAG_SCORE_ROWS) && (flags & QSA_FLAG_SCORE_GEMM)) return QSA_ERR_INVALID_ARG;
+    if (!score_flags_ok(flags, dtype)) return QSA_ERR_INVALID_ARG;
+    if ((flags & QSA_FLAG_SCORE_GEMM) && dtype != QSA_BF16) return QSA_ERR_UNSUPPORTED;
     if (!(flags & QSA_FLAG_NO_ROPE) && !(rope_theta > 1.0 && std::isfinite(rope_theta))) return QSA_ERR_INVALID_ARG;
     if (rows == 0) return QSA_OK;
     if (!aligned16(q_index) || !aligned16(pooled) || !row_seq || !row_pos || !sel_blocks || !sel_count)
         return QSA_ERR_INVALID_ARG;
     if (pooled_seq_stride % 8 || pooled_seq_stride < 0) return QSA_ERR_INVALID_ARG;
-    const ScoreLayout L = score_layout(rows, max_visible_blocks, top_k, dtype);
+    const ScoreLayout L = score_layout(rows, max_visible_blocks, top_k, dtype, flags);
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return QSA_ERR_INVALID_ARG;
     if (workspace_bytes < L.total) return QSA_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     const bool bf16 = dtype == QSA_BF16;
     char *ws = (char *)workspace;
     void *qrot = ws + L.qrot_off;
-    float *scores = (float *)(ws + L.scores_off);
-    // many bf16 rows: the fused MFMA scorer + merge; few rows (or the per-row
-    // flag): per-row streaming scorer with a split (few) or per-row select
-    bool fused = !L.few;
-    if (flags & QSA_FLAG_SCORE_ROWS) fused = false;
-    if (flags & QSA_FLAG_SCORE_GEMM) {
-        if (!bf16) return QSA_ERR_UNSUPPORTED;
-        fused = true;
-    }
-    const bool split = L.few && !fused;
     SplitSelect ss{};
-    if (split) {
+    if (L.plan.split) {
         ss.scratch = (uint32_t *)(ws + L.scratch_off);
         ss.sure = (uint2 *)(ws + L.sure_off);
         ss.cand = (uint2 *)(ws + L.cand_off);
@@ -207,8 +222,8 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
     }
     clear_launch_err();
     launch_rope_query(q_index, row_pos, rows, qrot, rope_theta, flags & QSA_FLAG_NO_ROPE, bf16,
-                      split ? ss.scratch : nullptr, kRowScratch, st);
-    if (fused) {
+                      L.plan.split ? ss.scratch : nullptr, kRowScratch, st);
+    if (L.plan.fused) {
         FusedScoreArgs fa{};
         fa.qrot = (const uint16_t *)qrot;
         fa.row_seq = row_seq;
@@ -227,10 +242,11 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
         launch_score_fused(fa, sel_blocks, sel_count, sel_scores, st);
         return launch_status();
     }
+    float *scores = (float *)(ws + L.scores_off);
     if (max_visible_blocks > 0)
         launch_score_rows(qrot, row_seq, row_pos, rows, pooled, pooled_seq_stride, max_visible_blocks, scores,
-                          L.sc_stride, split ? ss.scratch : nullptr, bf16, st);
-    if (split)
+                          L.sc_stride, L.plan.split ? ss.scratch : nullptr, bf16, st);
+    if (L.plan.split)
         launch_select_split(scores, L.sc_stride, row_pos, rows, max_visible_blocks, top_k, ss, sel_blocks, sel_count,
                             sel_scores, st);
     else

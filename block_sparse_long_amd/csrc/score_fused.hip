@@ -15,21 +15,26 @@
 // >= tau, and a pair below it cannot be kept).  Each row counts its written
 // pairs in a 256-bin histogram over key space -- 1/32 octave per bin, 4
 // octaves either side of an anchor (the row's best score in its first 64
-// blocks), everything above or below lumped into the end bins -- and after
-// every 64-block step a row that received pairs raises tau to the lowest key
-// of the highest bin at which k pairs are reached.
+// blocks), everything above or below lumped into the end bins.  tau is the
+// lowest key of bin b*, the highest bin at which k written pairs are reached;
+// every written pair lies in a bin <= b*, so after each 64-block step b*
+// only moves up while the bins above it still hold k pairs (a few LDS reads
+// per row).  A step's pairs get their slots with one LDS atomic per row,
+// ordered by block, so each split's list is ascending.
 //
 // Workgroup: 4 waves x 16 query rows (MFMA row m of tile mt = query row
 // 4*mt + m/4, index head m%4, so a lane's 4 accumulators are the 4 heads of
 // one (row, block) pair), one split of the block range.  The 64-block key
 // tile is staged through LDS (double buffered) and shared by the 4 waves.
 // The merge kernel takes, per row, the pairs of every split at or above the
-// best split's tau, picks the exact top k with a radix select on the unique
-// composite (key, ~block), and emits them sorted by block.  A row whose pair
-// buffer overflowed (e.g. massive exact ties) is redone by the merge kernel
-// from recomputed scores.
+// best split's tau -- in block order, since the splits are ordered and each
+// list is ascending -- finds the exact k-th key with a radix select (12, 12,
+// 8 bits), and emits, in block order, every pair above it and the first
+// `need` pairs equal to it (lower blocks win ties).  A row whose pair buffer
+// overflowed (e.g. massive exact ties) is redone from recomputed scores.
 #include "qsa_device.h"
 #include "qsa_internal.h"
+#include "qsa_wg.h"
 
 namespace qsa {
 
@@ -42,7 +47,7 @@ constexpr int kTauBins = 256;
 constexpr int kTauShift = 18;         // 2^18 key units = 1/32 octave
 constexpr int64_t kTauHalf = 1ll << 25;  // 4 octaves
 constexpr int kMergeThreads = 256;
-constexpr int kMergeLds = 4096;       // pairs a merge workgroup stages in LDS
+constexpr int kMergeLds = 7936;       // pairs a merge workgroup stages in LDS (2 workgroups per CU)
 
 __device__ __forceinline__ float relu_sum4f(f32x4_t a)
 {
@@ -70,13 +75,16 @@ __device__ __forceinline__ uint32_t tau_bin_floor(int b, uint32_t anchor)
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void score_filter_kernel(FusedScoreArgs a)
+__device__ __forceinline__ uint32_t hist_get(const uint32_t *h, int b) { return (h[b >> 1] >> (16 * (b & 1))) & 0xffffu; }
+
+__global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
 {
     const bf16_t *__restrict__ qrot = (const bf16_t *)a.qrot;
     const bf16_t *__restrict__ pooled = (const bf16_t *)a.pooled;
     __shared__ bf16_t keys[2][kFStep][kFKRow];
     __shared__ uint32_t hist[kFRows][kTauBins / 2];  // two 16-bit bins per word
-    __shared__ uint32_t cnt[kFRows], tau[kFRows], anchor[kFRows], dirty[kFRows];
+    __shared__ uint32_t cnt[kFRows], tau[kFRows], anchor[kFRows], removed[kFRows];
+    __shared__ int32_t bstar[kFRows];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m = lane & 15, g = lane >> 4;
     const int64_t row0 = (int64_t)blockIdx.x * kFRows;
@@ -89,7 +97,8 @@ __global__ __launch_bounds__(256) void score_filter_kernel(FusedScoreArgs a)
         cnt[t] = 0u;
         tau[t] = 0u;
         anchor[t] = 0x80000000u;
-        dirty[t] = 0u;
+        removed[t] = 0u;
+        bstar[t] = kTauBins - 1;
     }
     // A operands: this wave's 16 rows x 4 heads
     bf16x8_t qa[4][4];
@@ -196,58 +205,55 @@ __global__ __launch_bounds__(256) void score_filter_kernel(FusedScoreArgs a)
             if (__ballot(any)) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
+                    // slots of row 16*wave + 4*mt + g, ordered by block (nt, then m)
                     const int rw = 16 * wave + 4 * mt + g;
+                    uint32_t mine[4], total = 0;
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt) {
-                        if (!pass[mt][nt]) continue;
-                        const uint32_t key = score_key(sc[mt][nt]);
-                        const uint32_t slot = atomicAdd(&cnt[rw], 1u);
-                        if (slot < (uint32_t)a.cap) {
+                        const uint32_t grp = (uint32_t)(__ballot(pass[mt][nt]) >> (16 * g)) & 0xffffu;
+                        mine[nt] = total + (uint32_t)__popc(grp & ((1u << m) - 1u));
+                        total += (uint32_t)__popc(grp);
+                    }
+                    uint32_t slot0 = 0;
+                    if (m == 0 && total) slot0 = atomicAdd(&cnt[rw], total);
+                    slot0 = __shfl(slot0, 16 * g);
+                    const uint32_t anc = anchor[rw];
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) {
+                        const uint32_t slot = slot0 + mine[nt];
+                        if (pass[mt][nt] && slot < (uint32_t)a.cap) {
+                            const uint32_t key = score_key(sc[mt][nt]);
                             a.buf[((row0 + rw) * a.nsplit + split) * (int64_t)a.cap + slot] =
                                 make_uint2(key, (uint32_t)(base + nt * 16 + m));
-                            const int bin = tau_bin(key, anchor[rw]);
+                            const int bin = tau_bin(key, anc);
                             atomicAdd(&hist[rw][bin >> 1], (bin & 1) ? 0x10000u : 1u);
-                            dirty[rw] = 1u;
                         }
                     }
                 }
-                // ---- raise tau of the wave's rows that received pairs ----
+                // ---- raise tau: lane i < 16 moves row 16*wave + i's b* up ----
                 bool changed = false;
-                for (int i = 0; i < 16; ++i) {
-                    const int rw = 16 * wave + i;
-                    if (!dirty[rw]) continue;  // wave-uniform (LDS broadcast)
-                    const uint32_t c = cnt[rw];
-                    if (lane == 0) dirty[rw] = 0u;
-                    if (c < (uint32_t)a.top_k || c > (uint32_t)a.cap) continue;
-                    const uint32_t w0 = hist[rw][2 * lane], w1 = hist[rw][2 * lane + 1];
-                    const uint32_t h4[4] = {w0 & 0xffffu, w0 >> 16, w1 & 0xffffu, w1 >> 16};
-                    const uint32_t sum = h4[0] + h4[1] + h4[2] + h4[3];
-                    uint32_t incl = sum;
-                    for (int o = 1; o < 64; o <<= 1) {
-                        const uint32_t y = __shfl_up(incl, o);
-                        if (lane >= o) incl += y;
-                    }
-                    const uint64_t reach = __ballot(incl >= (uint32_t)a.top_k);
-                    const int l_star = __ffsll((unsigned long long)reach) - 1;  // exists: total >= top_k
-                    int b_star = kTauBins - 1;
-                    if (lane == l_star) {
-                        uint32_t acc = incl - sum;
-                        for (int j = 0; j < 4; ++j) {
-                            acc += h4[j];
-                            if (acc >= (uint32_t)a.top_k) {
-                                b_star = 4 * lane + j;
-                                break;
-                            }
+                if (lane < 16) {
+                    const int rw = 16 * wave + lane;
+                    const uint32_t c_all = cnt[rw];
+                    if (c_all <= (uint32_t)a.cap) {
+                        uint32_t c = c_all - removed[rw];
+                        int bs = bstar[rw];
+                        const uint32_t *h = hist[rw];
+                        while (bs > 0) {
+                            const uint32_t hb = hist_get(h, bs);
+                            if (c - hb < (uint32_t)a.top_k) break;
+                            c -= hb;
+                            --bs;
+                        }
+                        if (bs != bstar[rw]) {
+                            removed[rw] = c_all - c;
+                            bstar[rw] = bs;
+                            tau[rw] = tau_bin_floor(bs, anchor[rw]);
+                            changed = true;
                         }
                     }
-                    b_star = __shfl(b_star, l_star);
-                    const uint32_t nt_key = tau_bin_floor(b_star, anchor[rw]);
-                    if (nt_key > tau[rw]) {
-                        if (lane == 0) tau[rw] = nt_key;
-                        changed = true;
-                    }
                 }
-                if (changed) {
+                if (__ballot(changed)) {
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt) tauf[mt] = tau_float(tau[16 * wave + 4 * mt + g]);
                 }
@@ -268,43 +274,6 @@ __global__ __launch_bounds__(256) void score_filter_kernel(FusedScoreArgs a)
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int NT>
-__device__ __forceinline__ uint32_t incl_scan(uint32_t v, uint32_t *wtot)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) wtot[wave] = x;
-    __syncthreads();
-    uint32_t before = 0;
-    for (int w = 0; w < wave; ++w) before += wtot[w];
-    __syncthreads();
-    return before + x;
-}
-
-template <int NT>
-__device__ __forceinline__ uint32_t rank_of(bool pred, uint32_t *wtot, uint32_t &total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint64_t msk = __ballot(pred);
-    const uint32_t in_wave = (uint32_t)__popcll(msk & ((1ull << lane) - 1ull));
-    if (lane == 0) wtot[wave] = (uint32_t)__popcll(msk);
-    __syncthreads();
-    uint32_t before = 0, tot = 0;
-    for (int w = 0; w < NT / kWave; ++w) {
-        before += w < wave ? wtot[w] : 0u;
-        tot += wtot[w];
-    }
-    __syncthreads();
-    total = tot;
-    return before + in_wave;
-}
-
-__device__ __forceinline__ uint64_t composite32(uint2 e) { return ((uint64_t)e.x << 32) | (uint64_t)(~e.y); }
-
 // Raw score of (row, block) recomputed on the VALU (bf16 operands, fp32 sums).
 __device__ __forceinline__ float recompute_score(const bf16_t *__restrict__ q4, const bf16_t *__restrict__ key)
 {
@@ -323,6 +292,8 @@ __device__ __forceinline__ float recompute_score(const bf16_t *__restrict__ q4, 
     return ((fmaxf(d[0], 0.0f) + fmaxf(d[1], 0.0f)) + fmaxf(d[2], 0.0f)) + fmaxf(d[3], 0.0f);
 }
 
+__device__ __forceinline__ float scaled(float raw) { return (float)((double)raw / sqrt((double)kDim)); }
+
 }  // namespace
 
 __global__ __launch_bounds__(kMergeThreads) void select_merge_kernel(FusedScoreArgs a, int32_t *__restrict__ sel_blocks,
@@ -330,177 +301,144 @@ __global__ __launch_bounds__(kMergeThreads) void select_merge_kernel(FusedScoreA
                                                                    float *__restrict__ sel_scores)
 {
     __shared__ uint2 stage[kMergeLds];
-    __shared__ uint64_t kept[QSA_MAX_TOP_K];
-    __shared__ uint32_t dh[256];
+    __shared__ uint32_t hbins[4096];
     __shared__ uint32_t wtot[kMergeThreads / kWave];
-    __shared__ uint32_t s_n, s_digit, s_above, s_cnt, s_fill;
+    __shared__ uint32_t s_n, s_bin, s_above;
     const int t = threadIdx.x;
     const int64_t r = blockIdx.x;
     const int32_t nc = (int32_t)min(visible_blocks(a.row_pos[r]), (int64_t)a.max_nb);
     const int32_t kk = min(a.top_k, nc);
     int32_t *out = sel_blocks + r * a.top_k;
     float *osc = sel_scores ? sel_scores + r * a.top_k : nullptr;
-    if (nc <= 0) {  // no visible block (the scorer may not have run at all)
-        if (t == 0) sel_count[r] = 0;
-        for (int32_t i = t; i < a.top_k; i += kMergeThreads) {
-            out[i] = -1;
-            if (osc) osc[i] = 0.0f;
-        }
-        return;
+    if (t == 0) sel_count[r] = max(kk, 0);
+    for (int32_t i = max(kk, 0) + t; i < a.top_k; i += kMergeThreads) {
+        out[i] = -1;
+        if (osc) osc[i] = 0.0f;
     }
-    // pairs of every split; the best split's tau bounds the row's k-th best
+    if (nc <= 0) return;  // no visible block (the scorer may not have run at all)
+    // the splits' pairs; the best split's tau bounds the row's k-th best
     bool overflow = false;
-    uint32_t tau_max = 0, total = 0;
+    uint32_t tau_max = 0;
     for (int s = 0; s < a.nsplit; ++s) {
-        const uint32_t c = a.cnt[r * a.nsplit + s];
-        overflow |= c > (uint32_t)a.cap;
-        total += min(c, (uint32_t)a.cap);
+        overflow |= a.cnt[r * a.nsplit + s] > (uint32_t)a.cap;
         tau_max = max(tau_max, a.tau[r * a.nsplit + s]);
     }
-    if (t == 0) sel_count[r] = kk;
+    uint32_t n = 0;
     if (!overflow) {
-        // stage the pairs >= tau_max (LDS when they fit, else they are re-read)
+        // stage the pairs >= tau_max in block order (stable compaction)
         if (t == 0) s_n = 0;
         __syncthreads();
         for (int s = 0; s < a.nsplit; ++s) {
-            const uint32_t c = min(a.cnt[r * a.nsplit + s], (uint32_t)a.cap);
+            const uint32_t c = a.cnt[r * a.nsplit + s];
             const uint2 *src = a.buf + (r * a.nsplit + s) * (int64_t)a.cap;
             for (uint32_t i0 = 0; i0 < c; i0 += kMergeThreads) {
                 const uint32_t i = i0 + t;
                 const uint2 e = i < c ? src[i] : make_uint2(0u, 0u);
                 const bool keep = i < c && e.x >= tau_max;
                 uint32_t tot;
-                const uint32_t rk = rank_of<kMergeThreads>(keep, wtot, tot);
-                if (keep && s_n + rk < (uint32_t)kMergeLds) stage[s_n + rk] = e;
-                __syncthreads();
+                const uint32_t at = s_n + wg_rank<kMergeThreads>(keep, wtot, tot);
+                if (keep && at < (uint32_t)kMergeLds) stage[at] = e;
                 if (t == 0) s_n += tot;
                 __syncthreads();
             }
         }
-        const uint32_t n = s_n;
-        if (n <= (uint32_t)kMergeLds) {
-            // radix select of the kk-th largest composite among stage[0..n)
-            uint32_t need = (uint32_t)kk;
-            uint64_t prefix = 0, pmask = 0;
-            if (need < n) {
-                for (int sh = 56; sh >= 0; sh -= 8) {
-                    dh[t] = 0u;
-                    __syncthreads();
-                    for (uint32_t i = t; i < n; i += kMergeThreads) {
-                        const uint64_t c = composite32(stage[i]);
-                        if ((c & pmask) == prefix) atomicAdd(&dh[(uint32_t)(c >> sh) & 0xffu], 1u);
-                    }
-                    __syncthreads();
-                    const uint32_t hv = dh[255 - t];
-                    const uint32_t incl = incl_scan<kMergeThreads>(hv, wtot);
-                    if (hv && incl - hv < need && incl >= need) {
-                        s_digit = 255u - (uint32_t)t;
-                        s_above = incl - hv;
-                        s_cnt = hv;
-                    }
-                    __syncthreads();
-                    prefix |= (uint64_t)s_digit << sh;
-                    pmask |= 0xffull << sh;
-                    need -= s_above;
-                    const bool done = s_cnt == need;
-                    __syncthreads();
-                    if (done) break;
-                }
-            }
-            if (t == 0) s_fill = 0;
-            __syncthreads();
-            for (uint32_t i = t; i < n; i += kMergeThreads) {
-                const uint2 e = stage[i];
-                if ((composite32(e) & pmask) >= prefix) {
-                    const uint32_t at = atomicAdd(&s_fill, 1u);
-                    if (at < (uint32_t)QSA_MAX_TOP_K) kept[at] = ((uint64_t)e.y << 32) | e.x;
-                }
-            }
-            __syncthreads();
-            const uint32_t nk = min(s_fill, (uint32_t)kk);
-            uint32_t n2 = 1;
-            while (n2 < nk) n2 <<= 1;
-            for (uint32_t i = nk + t; i < n2; i += kMergeThreads) kept[i] = ~0ull;
-            __syncthreads();
-            for (uint32_t size = 2; size <= n2; size <<= 1) {
-                for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-                    for (uint32_t i = t; i < n2 / 2; i += kMergeThreads) {
-                        const uint32_t lo = 2 * i - (i & (stride - 1));
-                        const uint32_t hi = lo + stride;
-                        const bool up = (lo & size) == 0;
-                        const uint64_t x = kept[lo], y = kept[hi];
-                        if ((x > y) == up) {
-                            kept[lo] = y;
-                            kept[hi] = x;
-                        }
-                    }
-                    __syncthreads();
-                }
-            }
-            for (int32_t i = t; i < a.top_k; i += kMergeThreads) {
-                const bool k_ = (uint32_t)i < nk;
-                const uint64_t e = k_ ? kept[i] : 0ull;
-                out[i] = k_ ? (int32_t)(e >> 32) : -1;
-                if (osc) osc[i] = k_ ? (float)((double)key_score((uint32_t)e) / sqrt((double)kDim)) : 0.0f;
-            }
-            return;
-        }
+        n = s_n;
     }
-    // ---- fallback: radix select over recomputed scores of every visible block,
-    // in block order (too many pairs for the staged merge) ----
+    if (!overflow && n <= (uint32_t)kMergeLds) {
+        // radix select of the kk-th key among stage[0..n): bits 31-20, 19-8, 7-0
+        uint32_t need = (uint32_t)kk, prefix = 0;
+        int sh = 32;
+        if ((uint32_t)kk < n) {
+            const int widths[3] = {12, 12, 8};
+            for (int pass = 0; pass < 3; ++pass) {
+                const int w = widths[pass], nsh = sh - w, nbins = 1 << w;
+                for (int i = t; i < nbins; i += kMergeThreads) hbins[i] = 0u;
+                __syncthreads();
+                for (uint32_t i = t; i < n; i += kMergeThreads) {
+                    const uint32_t key = stage[i].x;
+                    if (sh == 32 || (key >> sh) == prefix) atomicAdd(&hbins[(key >> nsh) & (uint32_t)(nbins - 1)], 1u);
+                }
+                __syncthreads();
+                find_bin<kMergeThreads>(hbins, nbins, need, wtot, &s_bin, &s_above);
+                const uint32_t bin = s_bin, above = s_above, cntb = hbins[bin];
+                __syncthreads();
+                need -= above;
+                prefix = (sh == 32 ? 0u : (prefix << w)) | bin;
+                sh = nsh;
+                if (cntb == need) break;
+            }
+        } else {
+            prefix = 0;  // keep everything: every key >> 32... handled by sh == 32
+        }
+        // emit in block order: keys above the bin, and the first `need` inside it
+        uint32_t eq_before = 0, out_before = 0;
+        for (uint32_t i0 = 0; i0 < n; i0 += kMergeThreads) {
+            const uint32_t i = i0 + t;
+            const bool valid = i < n;
+            const uint2 e = valid ? stage[i] : make_uint2(0u, 0u);
+            const bool all = sh == 32;
+            const uint32_t top = all ? 0u : (e.x >> sh);
+            const bool gt = valid && (all || top > prefix);
+            const bool eq = valid && !all && top == prefix;
+            uint32_t eq_total, take_total;
+            const uint32_t eq_rank = eq_before + wg_rank<kMergeThreads>(eq, wtot, eq_total);
+            const bool take = gt || (eq && eq_rank < need);
+            const uint32_t pos = out_before + wg_rank<kMergeThreads>(take, wtot, take_total);
+            if (take && pos < (uint32_t)kk) {
+                out[pos] = (int32_t)e.y;
+                if (osc) osc[pos] = scaled(key_score(e.x));
+            }
+            eq_before += eq_total;
+            out_before += take_total;
+        }
+        return;
+    }
+    // ---- fallback: radix select over recomputed scores of every visible
+    // block, in block order ----
     const int32_t seq = a.row_seq[r];
     const bf16_t *q4 = (const bf16_t *)a.qrot + r * kIdxHeads * kDim;
     const bf16_t *kb = (const bf16_t *)a.pooled + (int64_t)seq * a.pooled_stride;
-    uint32_t need = (uint32_t)kk;
-    uint32_t prefix = 0;
+    uint32_t need = (uint32_t)kk, prefix = 0;
     int sh = 32;
-    const int widths[4] = {8, 8, 8, 8};
-    for (int pass = 0; pass < 4 && need > 0; ++pass) {
-        const int nsh = sh - widths[pass];
-        dh[t] = 0u;
-        __syncthreads();
-        for (int32_t b = t; b < nc; b += kMergeThreads) {
-            const uint32_t key = score_key(recompute_score(q4, kb + (int64_t)b * kDim));
-            if (sh == 32 || (key >> sh) == prefix) atomicAdd(&dh[(key >> nsh) & 0xffu], 1u);
+    if (kk < nc) {
+        const int widths[3] = {12, 12, 8};
+        for (int pass = 0; pass < 3; ++pass) {
+            const int w = widths[pass], nsh = sh - w, nbins = 1 << w;
+            for (int i = t; i < nbins; i += kMergeThreads) hbins[i] = 0u;
+            __syncthreads();
+            for (int32_t b = t; b < nc; b += kMergeThreads) {
+                const uint32_t key = score_key(recompute_score(q4, kb + (int64_t)b * kDim));
+                if (sh == 32 || (key >> sh) == prefix) atomicAdd(&hbins[(key >> nsh) & (uint32_t)(nbins - 1)], 1u);
+            }
+            __syncthreads();
+            find_bin<kMergeThreads>(hbins, nbins, need, wtot, &s_bin, &s_above);
+            const uint32_t bin = s_bin, above = s_above, cntb = hbins[bin];
+            __syncthreads();
+            need -= above;
+            prefix = (sh == 32 ? 0u : (prefix << w)) | bin;
+            sh = nsh;
+            if (cntb == need) break;
         }
-        __syncthreads();
-        const uint32_t hv = dh[255 - t];
-        const uint32_t incl = incl_scan<kMergeThreads>(hv, wtot);
-        if (hv && incl - hv < need && incl >= need) {
-            s_digit = 255u - (uint32_t)t;
-            s_above = incl - hv;
-            s_cnt = hv;
-        }
-        __syncthreads();
-        need -= s_above;
-        prefix = (sh == 32 ? 0u : (prefix << 8)) | s_digit;
-        sh = nsh;
-        const bool done = s_cnt == need;
-        __syncthreads();
-        if (done) break;
     }
     uint32_t eq_before = 0, out_before = 0;
     for (int32_t b0 = 0; b0 < nc; b0 += kMergeThreads) {
         const int32_t b = b0 + t;
         const bool valid = b < nc;
         const float sc = valid ? recompute_score(q4, kb + (int64_t)b * kDim) : 0.0f;
-        const uint32_t top = valid ? (score_key(sc) >> sh) : 0u;
-        const bool gt = valid && top > prefix;
-        const bool eq = valid && top == prefix;
+        const bool all = sh == 32;
+        const uint32_t top = all ? 0u : (score_key(sc) >> sh);
+        const bool gt = valid && (all || top > prefix);
+        const bool eq = valid && !all && top == prefix;
         uint32_t eq_total, take_total;
-        const uint32_t eq_rank = eq_before + rank_of<kMergeThreads>(eq, wtot, eq_total);
+        const uint32_t eq_rank = eq_before + wg_rank<kMergeThreads>(eq, wtot, eq_total);
         const bool take = gt || (eq && eq_rank < need);
-        const uint32_t pos = out_before + rank_of<kMergeThreads>(take, wtot, take_total);
+        const uint32_t pos = out_before + wg_rank<kMergeThreads>(take, wtot, take_total);
         if (take && pos < (uint32_t)kk) {
             out[pos] = b;
-            if (osc) osc[pos] = (float)((double)sc / sqrt((double)kDim));
+            if (osc) osc[pos] = scaled(sc);
         }
         eq_before += eq_total;
         out_before += take_total;
-    }
-    for (int32_t i = kk + t; i < a.top_k; i += kMergeThreads) {
-        out[i] = -1;
-        if (osc) osc[i] = 0.0f;
     }
 }
 

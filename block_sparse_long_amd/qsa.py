@@ -57,7 +57,7 @@ def load():
     st = ctypes.c_int
     lib.qsa_pool_index_keys.argtypes = [P, i64, P, i64, i32, i32, i32, f64, u32, st, P]
     lib.qsa_pool_index_keys.restype = st
-    lib.qsa_score_topk_workspace_size.argtypes = [i32, i32, i32, st]
+    lib.qsa_score_topk_workspace_size.argtypes = [i32, i32, i32, st, u32]
     lib.qsa_score_topk_workspace_size.restype = sz
     lib.qsa_score_topk.argtypes = [P, P, P, i32, P, i64, i32, i32, f64, u32, st, P, P, P, P, sz, P]
     lib.qsa_score_topk.restype = st
@@ -130,9 +130,10 @@ def pool_index_keys(raw_keys, pooled, block_begin: int, block_end: int, rope_the
     _check("qsa_pool_index_keys", rc)
 
 
-def score_topk_workspace_size(rows: int, max_visible_blocks: int, top_k: int, dtype_code: int) -> int:
+def score_topk_workspace_size(rows: int, max_visible_blocks: int, top_k: int, dtype_code: int,
+                              flags: int = 0) -> int:
     return int(load().qsa_score_topk_workspace_size(int(rows), int(max_visible_blocks), int(top_k),
-                                                    int(dtype_code)))
+                                                    int(dtype_code), int(flags)))
 
 
 def score_topk(q_index, row_seq, row_pos, pooled, max_visible_blocks: int, top_k: int,
@@ -152,7 +153,7 @@ def score_topk(q_index, row_seq, row_pos, pooled, max_visible_blocks: int, top_k
         sel_count = torch.empty((R,), dtype=torch.int32, device=dev)
     if sel_scores is None and want_scores:
         sel_scores = torch.empty((R, top_k), dtype=torch.float32, device=dev)
-    need = score_topk_workspace_size(R, max_visible_blocks, top_k, dt)
+    need = score_topk_workspace_size(R, max_visible_blocks, top_k, dt, flags)
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
     rc = load().qsa_score_topk(_ptr(q_index), _ptr(row_seq), _ptr(row_pos), R, _ptr(pooled),

@@ -100,10 +100,12 @@ qsa_status_t qsa_pool_index_keys(const void *raw_keys, int64_t raw_seq_stride, v
 
 /*
  * Bytes of device workspace qsa_score_topk needs for `rows` rows whose visible
- * block counts are at most `max_visible_blocks`.  0 when rows == 0.
+ * block counts are at most `max_visible_blocks`, with the same `flags` the
+ * call will get (the scoring kernel decides the layout).  0 when rows == 0 or
+ * an argument is out of range.
  */
 size_t qsa_score_topk_workspace_size(int32_t rows, int32_t max_visible_blocks, int32_t top_k,
-                                     qsa_dtype_t dtype);
+                                     qsa_dtype_t dtype, uint32_t flags);
 
 /*
  * Steps a4-a6 ([SGL] score equation and top-512; [LBL]).  For every row r with

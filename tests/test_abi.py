@@ -64,6 +64,12 @@ def test_score_topk_validation(libqsa):
     f = libqsa.qsa_score_topk
     ws = qsa.score_topk_workspace_size(4, 100, 16, qsa.BF16)
     assert ws > 0 and qsa.score_topk_workspace_size(0, 100, 16, qsa.BF16) == 0
+    assert qsa.score_topk_workspace_size(4, 100, 0, qsa.BF16) == 0
+    assert qsa.score_topk_workspace_size(4, 100, 16, qsa.BF16, 1 << 12) == 0
+    # many rows: the fused scorer keeps no score matrix; the per-row scorer does
+    big = qsa.score_topk_workspace_size(8192, 65536, 512, qsa.BF16, qsa.FLAG_SCORE_ROWS)
+    fused = qsa.score_topk_workspace_size(8192, 65536, 512, qsa.BF16)
+    assert big >= 8192 * 65536 * 4 and fused < big
     good = dict(q=A, seq=B_, pos=C, rows=4, pooled=A, stride=128 * 100, nb=100, k=16, theta=1e7,
                 flags=0, dt=qsa.BF16, sel=B_, cnt=C, sc=None, ws=0x100000, wsb=ws)
 
@@ -85,6 +91,9 @@ def test_score_topk_validation(libqsa):
     assert call(flags=qsa.FLAG_SCORE_ROWS | qsa.FLAG_SCORE_GEMM) == qsa.ERR_INVALID_ARG
     assert call(flags=qsa.FLAG_SCORE_GEMM, dt=qsa.F32,
                 wsb=qsa.score_topk_workspace_size(4, 100, 16, qsa.F32)) == qsa.ERR_UNSUPPORTED
+    assert call(flags=qsa.FLAG_SCORE_GEMM, wsb=ws) == qsa.ERR_WORKSPACE   # the fused layout is larger
+    assert call(flags=qsa.FLAG_SCORE_GEMM,
+                wsb=qsa.score_topk_workspace_size(4, 100, 16, qsa.BF16, qsa.FLAG_SCORE_GEMM)) != qsa.ERR_WORKSPACE
     assert call(flags=qsa.FLAG_POOL_RMSNORM) == qsa.ERR_INVALID_ARG  # pooling flag, not a score flag
     assert call(theta=float("nan")) == qsa.ERR_INVALID_ARG
 
