@@ -45,37 +45,45 @@ constexpr int kFStep = 64;            // blocks per step
 constexpr int kFKRow = kDim + 8;      // LDS key row stride (bf16): conflict-free b128 reads
 constexpr int kTauBins = 256;
 constexpr int kTauShift = 18;         // 2^18 key units = 1/32 octave
-constexpr int64_t kTauHalf = 1ll << 25;  // 4 octaves
-constexpr int kMergeThreads = 256;
-constexpr int kMergeLds = 7936;       // pairs a merge workgroup stages in LDS (2 workgroups per CU)
+constexpr int kMergeWaves = 4;        // merge: rows per workgroup, one wave each
+constexpr int kStage = 2048;          // merge: pairs a wave stages in LDS
 
 __device__ __forceinline__ float relu_sum4f(f32x4_t a)
 {
     return ((fmaxf(a[0], 0.0f) + fmaxf(a[1], 0.0f)) + fmaxf(a[2], 0.0f)) + fmaxf(a[3], 0.0f);
 }
 
-__device__ __forceinline__ int tau_bin(uint32_t key, uint32_t anchor)
+// Top of a row's bin window: its anchor key + 4 octaves (2^25 key units).
+__device__ __forceinline__ uint32_t window_top(uint32_t anchor)
 {
-    const int64_t d = (int64_t)anchor + kTauHalf - (int64_t)key;
-    if (d < 0) return 0;
-    const int64_t b = d >> kTauShift;
-    return b >= kTauBins - 1 ? kTauBins - 1 : (int)b;
+    const uint64_t t = (uint64_t)anchor + (1ull << 25);
+    return t > 0xffffffffull ? 0xffffffffu : (uint32_t)t;
+}
+
+// Bin of a key: 0 at and above the window top, 255 for everything 8 octaves down.
+__device__ __forceinline__ int tau_bin(uint32_t key, uint32_t top)
+{
+    if (key >= top) return 0;
+    const uint32_t b = (top - key) >> kTauShift;
+    return b >= (uint32_t)(kTauBins - 1) ? kTauBins - 1 : (int)b;
 }
 
 // Threshold key -> float for `score >= tau` (key 0: no threshold yet).
 __device__ __forceinline__ float tau_float(uint32_t key) { return key == 0u ? -INFINITY : key_score(key); }
 
 // Lowest key of bin b (the last bin reaches down to every key).
-__device__ __forceinline__ uint32_t tau_bin_floor(int b, uint32_t anchor)
+__device__ __forceinline__ uint32_t tau_bin_floor(int b, uint32_t top)
 {
     if (b >= kTauBins - 1) return 0u;
-    const int64_t k = (int64_t)anchor + kTauHalf - ((int64_t)(b + 1) << kTauShift) + 1;
-    return k <= 0 ? 0u : (k >= 0xffffffffll ? 0xffffffffu : (uint32_t)k);
+    const int64_t k = (int64_t)top - ((int64_t)(b + 1) << kTauShift) + 1;
+    return k <= 0 ? 0u : (uint32_t)k;
 }
 
-}  // namespace
-
 __device__ __forceinline__ uint32_t hist_get(const uint32_t *h, int b) { return (h[b >> 1] >> (16 * (b & 1))) & 0xffffu; }
+
+__device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+}  // namespace
 
 __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
 {
@@ -83,7 +91,7 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
     const bf16_t *__restrict__ pooled = (const bf16_t *)a.pooled;
     __shared__ bf16_t keys[2][kFStep][kFKRow];
     __shared__ uint32_t hist[kFRows][kTauBins / 2];  // two 16-bit bins per word
-    __shared__ uint32_t cnt[kFRows], tau[kFRows], anchor[kFRows], removed[kFRows];
+    __shared__ uint32_t cnt[kFRows], tau[kFRows], wtop[kFRows], removed[kFRows];
     __shared__ int32_t bstar[kFRows];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m = lane & 15, g = lane >> 4;
@@ -96,7 +104,7 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
     if (t < kFRows) {
         cnt[t] = 0u;
         tau[t] = 0u;
-        anchor[t] = 0x80000000u;
+        wtop[t] = window_top(0x80000000u);
         removed[t] = 0u;
         bstar[t] = kTauBins - 1;
     }
@@ -114,11 +122,13 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
     // the 4 rows whose scores this lane receives: 16*wave + 4*mt + g
     int64_t my_nc[4];
     int32_t my_seq[4];
+    uint2 *my_buf[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const int rw = 16 * wave + 4 * mt + g;
         my_nc[mt] = rw < nrows ? min(visible_blocks(a.row_pos[row0 + rw]), (int64_t)a.max_nb) : 0;
         my_seq[mt] = rw < nrows ? a.row_seq[row0 + rw] : -1;
+        my_buf[mt] = a.buf + ((row0 + min(rw, nrows - 1)) * a.nsplit + split) * (int64_t)a.cap;
     }
     __syncthreads();
     uint64_t todo = nrows >= 64 ? ~0ull : ((1ull << nrows) - 1ull);
@@ -163,22 +173,29 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
         for (int64_t base = lo; base < hi; base += kFStep) {
             const bool more = base + kFStep < hi;
             if (more) load_tile(base + kFStep);
-            // ---- scores of the step: 4 row tiles x 4 block tiles ----
+            // ---- scores of the step: 4 block tiles x (4 independent row-tile chains) ----
             float sc[4][4];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 bf16x8_t bk[4];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) bk[s] = as_bf16x8(*(const uint4 *)&keys[cur][nt * 16 + m][32 * g + 8 * s]);
+                f32x4_t acc[4];
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], bk[s], acc, 0, 0, 0);
-                    sc[mt][nt] = relu_sum4f(acc);
-                }
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], bk[s], acc[mt], 0, 0, 0);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) sc[mt][nt] = relu_sum4f(acc[mt]);
             }
             if (more) store_tile(cur ^ 1);
+            // valid iff 16*nt < lr[mt] (block base + 16*nt + m below the row's bound)
+            int32_t lr[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) lr[mt] = (int32_t)max(min(lim[mt] - base - m, (int64_t)kFStep), (int64_t)-1);
             // ---- anchors: each row's best score in its first step ----
             if (first_step) {
 #pragma unroll
@@ -186,50 +203,52 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
                     float mx = 0.0f;
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
-                        if (base + nt * 16 + m < lim[mt]) mx = fmaxf(mx, sc[mt][nt]);
+                        if (16 * nt < lr[mt]) mx = fmaxf(mx, sc[mt][nt]);
                     for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-                    if (m == 0 && lim[mt] > 0) anchor[16 * wave + 4 * mt + g] = score_key(mx);
+                    if (m == 0 && lim[mt] > 0) wtop[16 * wave + 4 * mt + g] = window_top(score_key(mx));
                 }
+                wave_fence();
                 first_step = false;
             }
             // ---- filter: pairs at or above the row's tau are written out ----
-            bool pass[4][4];
-            bool any = false;
+            bool appended = false;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt) {
+                bool pass[4];
+                bool any = false;
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
-                    pass[mt][nt] = sc[mt][nt] >= tauf[mt] && base + nt * 16 + m < lim[mt];
-                    any |= pass[mt][nt];
+                    pass[nt] = sc[mt][nt] >= tauf[mt] && 16 * nt < lr[mt];
+                    any |= pass[nt];
                 }
-            if (__ballot(any)) {
+                if (!__ballot(any)) continue;  // wave-uniform
+                appended = true;
+                // slots of row 16*wave + 4*mt + g, ordered by block (nt, then m)
+                const int rw = 16 * wave + 4 * mt + g;
+                uint32_t mine[4], total = 0;
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    // slots of row 16*wave + 4*mt + g, ordered by block (nt, then m)
-                    const int rw = 16 * wave + 4 * mt + g;
-                    uint32_t mine[4], total = 0;
+                for (int nt = 0; nt < 4; ++nt) {
+                    const uint32_t grp = (uint32_t)(__ballot(pass[nt]) >> (16 * g)) & 0xffffu;
+                    mine[nt] = total + (uint32_t)__popc(grp & ((1u << m) - 1u));
+                    total += (uint32_t)__popc(grp);
+                }
+                uint32_t slot0 = 0;
+                if (m == 0 && total) slot0 = atomicAdd(&cnt[rw], total);
+                slot0 = __shfl(slot0, 16 * g);
+                const uint32_t top = wtop[rw];
 #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt) {
-                        const uint32_t grp = (uint32_t)(__ballot(pass[mt][nt]) >> (16 * g)) & 0xffffu;
-                        mine[nt] = total + (uint32_t)__popc(grp & ((1u << m) - 1u));
-                        total += (uint32_t)__popc(grp);
-                    }
-                    uint32_t slot0 = 0;
-                    if (m == 0 && total) slot0 = atomicAdd(&cnt[rw], total);
-                    slot0 = __shfl(slot0, 16 * g);
-                    const uint32_t anc = anchor[rw];
-#pragma unroll
-                    for (int nt = 0; nt < 4; ++nt) {
-                        const uint32_t slot = slot0 + mine[nt];
-                        if (pass[mt][nt] && slot < (uint32_t)a.cap) {
-                            const uint32_t key = score_key(sc[mt][nt]);
-                            a.buf[((row0 + rw) * a.nsplit + split) * (int64_t)a.cap + slot] =
-                                make_uint2(key, (uint32_t)(base + nt * 16 + m));
-                            const int bin = tau_bin(key, anc);
-                            atomicAdd(&hist[rw][bin >> 1], (bin & 1) ? 0x10000u : 1u);
-                        }
+                for (int nt = 0; nt < 4; ++nt) {
+                    const uint32_t slot = slot0 + mine[nt];
+                    if (pass[nt] && slot < (uint32_t)a.cap) {
+                        const uint32_t key = score_key(sc[mt][nt]);
+                        my_buf[mt][slot] = make_uint2(key, (uint32_t)(base + nt * 16 + m));
+                        const int bin = tau_bin(key, top);
+                        atomicAdd(&hist[rw][bin >> 1], (bin & 1) ? 0x10000u : 1u);
                     }
                 }
+            }
+            if (appended) {
+                wave_fence();
                 // ---- raise tau: lane i < 16 moves row 16*wave + i's b* up ----
                 bool changed = false;
                 if (lane < 16) {
@@ -248,12 +267,13 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
                         if (bs != bstar[rw]) {
                             removed[rw] = c_all - c;
                             bstar[rw] = bs;
-                            tau[rw] = tau_bin_floor(bs, anchor[rw]);
+                            tau[rw] = tau_bin_floor(bs, wtop[rw]);
                             changed = true;
                         }
                     }
                 }
                 if (__ballot(changed)) {
+                    wave_fence();
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt) tauf[mt] = tau_float(tau[16 * wave + 4 * mt + g]);
                 }
@@ -296,150 +316,152 @@ __device__ __forceinline__ float scaled(float raw) { return (float)((double)raw 
 
 }  // namespace
 
-__global__ __launch_bounds__(kMergeThreads) void select_merge_kernel(FusedScoreArgs a, int32_t *__restrict__ sel_blocks,
-                                                                   int32_t *__restrict__ sel_count,
-                                                                   float *__restrict__ sel_scores)
+// One wave per row, four rows per workgroup; no workgroup barriers.  The
+// row's pairs >= the best split's tau are visited in block order -- from LDS
+// when they fit, else straight from the pair buffers -- or, for a row whose
+// buffer overflowed, as recomputed scores of every visible block.
+__global__ __launch_bounds__(256) void select_merge_kernel(FusedScoreArgs a, int32_t *__restrict__ sel_blocks,
+                                                         int32_t *__restrict__ sel_count, float *__restrict__ sel_scores)
 {
-    __shared__ uint2 stage[kMergeLds];
-    __shared__ uint32_t hbins[4096];
-    __shared__ uint32_t wtot[kMergeThreads / kWave];
-    __shared__ uint32_t s_n, s_bin, s_above;
-    const int t = threadIdx.x;
-    const int64_t r = blockIdx.x;
+    __shared__ uint2 stage[kMergeWaves][kStage];
+    __shared__ uint32_t hb[kMergeWaves][256];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t r = (int64_t)blockIdx.x * kMergeWaves + w;
+    if (r >= a.rows) return;
+    const uint64_t lt = (1ull << lane) - 1ull;  // lanes below this one
     const int32_t nc = (int32_t)min(visible_blocks(a.row_pos[r]), (int64_t)a.max_nb);
-    const int32_t kk = min(a.top_k, nc);
+    const int32_t kk = max(0, min(a.top_k, nc));
     int32_t *out = sel_blocks + r * a.top_k;
     float *osc = sel_scores ? sel_scores + r * a.top_k : nullptr;
-    if (t == 0) sel_count[r] = max(kk, 0);
-    for (int32_t i = max(kk, 0) + t; i < a.top_k; i += kMergeThreads) {
+    if (lane == 0) sel_count[r] = kk;
+    for (int32_t i = kk + lane; i < a.top_k; i += kWave) {
         out[i] = -1;
         if (osc) osc[i] = 0.0f;
     }
     if (nc <= 0) return;  // no visible block (the scorer may not have run at all)
-    // the splits' pairs; the best split's tau bounds the row's k-th best
     bool overflow = false;
     uint32_t tau_max = 0;
     for (int s = 0; s < a.nsplit; ++s) {
         overflow |= a.cnt[r * a.nsplit + s] > (uint32_t)a.cap;
         tau_max = max(tau_max, a.tau[r * a.nsplit + s]);
     }
+    uint2 *st = stage[w];
+    uint32_t *h = hb[w];
+    // ---- the pairs to rank: mode 0 staged in LDS, 1 in the buffers, 2 recomputed ----
     uint32_t n = 0;
+    int mode = 2;
     if (!overflow) {
-        // stage the pairs >= tau_max in block order (stable compaction)
-        if (t == 0) s_n = 0;
-        __syncthreads();
         for (int s = 0; s < a.nsplit; ++s) {
             const uint32_t c = a.cnt[r * a.nsplit + s];
             const uint2 *src = a.buf + (r * a.nsplit + s) * (int64_t)a.cap;
-            for (uint32_t i0 = 0; i0 < c; i0 += kMergeThreads) {
-                const uint32_t i = i0 + t;
+            for (uint32_t i0 = 0; i0 < c; i0 += kWave) {
+                const uint32_t i = i0 + lane;
                 const uint2 e = i < c ? src[i] : make_uint2(0u, 0u);
                 const bool keep = i < c && e.x >= tau_max;
-                uint32_t tot;
-                const uint32_t at = s_n + wg_rank<kMergeThreads>(keep, wtot, tot);
-                if (keep && at < (uint32_t)kMergeLds) stage[at] = e;
-                if (t == 0) s_n += tot;
-                __syncthreads();
+                const uint64_t bal = __ballot(keep);
+                const uint32_t pos = n + (uint32_t)__popcll(bal & lt);
+                if (keep && pos < (uint32_t)kStage) st[pos] = e;
+                n += (uint32_t)__popcll(bal);
             }
         }
-        n = s_n;
+        mode = n <= (uint32_t)kStage ? 0 : 1;
     }
-    if (!overflow && n <= (uint32_t)kMergeLds) {
-        // radix select of the kk-th key among stage[0..n): bits 31-20, 19-8, 7-0
-        uint32_t need = (uint32_t)kk, prefix = 0;
-        int sh = 32;
-        if ((uint32_t)kk < n) {
-            const int widths[3] = {12, 12, 8};
-            for (int pass = 0; pass < 3; ++pass) {
-                const int w = widths[pass], nsh = sh - w, nbins = 1 << w;
-                for (int i = t; i < nbins; i += kMergeThreads) hbins[i] = 0u;
-                __syncthreads();
-                for (uint32_t i = t; i < n; i += kMergeThreads) {
-                    const uint32_t key = stage[i].x;
-                    if (sh == 32 || (key >> sh) == prefix) atomicAdd(&hbins[(key >> nsh) & (uint32_t)(nbins - 1)], 1u);
-                }
-                __syncthreads();
-                find_bin<kMergeThreads>(hbins, nbins, need, wtot, &s_bin, &s_above);
-                const uint32_t bin = s_bin, above = s_above, cntb = hbins[bin];
-                __syncthreads();
-                need -= above;
-                prefix = (sh == 32 ? 0u : (prefix << w)) | bin;
-                sh = nsh;
-                if (cntb == need) break;
-            }
-        } else {
-            prefix = 0;  // keep everything: every key >> 32... handled by sh == 32
-        }
-        // emit in block order: keys above the bin, and the first `need` inside it
-        uint32_t eq_before = 0, out_before = 0;
-        for (uint32_t i0 = 0; i0 < n; i0 += kMergeThreads) {
-            const uint32_t i = i0 + t;
-            const bool valid = i < n;
-            const uint2 e = valid ? stage[i] : make_uint2(0u, 0u);
-            const bool all = sh == 32;
-            const uint32_t top = all ? 0u : (e.x >> sh);
-            const bool gt = valid && (all || top > prefix);
-            const bool eq = valid && !all && top == prefix;
-            uint32_t eq_total, take_total;
-            const uint32_t eq_rank = eq_before + wg_rank<kMergeThreads>(eq, wtot, eq_total);
-            const bool take = gt || (eq && eq_rank < need);
-            const uint32_t pos = out_before + wg_rank<kMergeThreads>(take, wtot, take_total);
-            if (take && pos < (uint32_t)kk) {
-                out[pos] = (int32_t)e.y;
-                if (osc) osc[pos] = scaled(key_score(e.x));
-            }
-            eq_before += eq_total;
-            out_before += take_total;
-        }
-        return;
-    }
-    // ---- fallback: radix select over recomputed scores of every visible
-    // block, in block order ----
     const int32_t seq = a.row_seq[r];
     const bf16_t *q4 = (const bf16_t *)a.qrot + r * kIdxHeads * kDim;
     const bf16_t *kb = (const bf16_t *)a.pooled + (int64_t)seq * a.pooled_stride;
-    uint32_t need = (uint32_t)kk, prefix = 0;
-    int sh = 32;
-    if (kk < nc) {
-        const int widths[3] = {12, 12, 8};
-        for (int pass = 0; pass < 3; ++pass) {
-            const int w = widths[pass], nsh = sh - w, nbins = 1 << w;
-            for (int i = t; i < nbins; i += kMergeThreads) hbins[i] = 0u;
-            __syncthreads();
-            for (int32_t b = t; b < nc; b += kMergeThreads) {
-                const uint32_t key = score_key(recompute_score(q4, kb + (int64_t)b * kDim));
-                if (sh == 32 || (key >> sh) == prefix) atomicAdd(&hbins[(key >> nsh) & (uint32_t)(nbins - 1)], 1u);
+    if (mode == 2) n = (uint32_t)nc;
+    wave_fence();
+    // visit every pair in block order, 64 at a time: fn(pair, valid)
+    auto visit = [&](auto &&fn) {
+        if (mode == 0) {
+            for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
+                const uint32_t i = i0 + lane;
+                fn(i < n ? st[i] : make_uint2(0u, 0u), i < n);
             }
-            __syncthreads();
-            find_bin<kMergeThreads>(hbins, nbins, need, wtot, &s_bin, &s_above);
-            const uint32_t bin = s_bin, above = s_above, cntb = hbins[bin];
-            __syncthreads();
+        } else if (mode == 1) {
+            for (int s = 0; s < a.nsplit; ++s) {
+                const uint32_t c = a.cnt[r * a.nsplit + s];
+                const uint2 *src = a.buf + (r * a.nsplit + s) * (int64_t)a.cap;
+                for (uint32_t i0 = 0; i0 < c; i0 += kWave) {
+                    const uint32_t i = i0 + lane;
+                    const uint2 e = i < c ? src[i] : make_uint2(0u, 0u);
+                    fn(e, i < c && e.x >= tau_max);
+                }
+            }
+        } else {
+            for (int32_t b0 = 0; b0 < nc; b0 += kWave) {
+                const int32_t b = b0 + lane;
+                const bool v = b < nc;
+                const uint32_t key = v ? score_key(recompute_score(q4, kb + (int64_t)b * kDim)) : 0u;
+                fn(make_uint2(key, (uint32_t)b), v);
+            }
+        }
+    };
+    // ---- radix select of the kk-th key, 8 bits at a time ----
+    uint32_t need = (uint32_t)kk, prefix = 0;
+    int sh = 32;  // key >> sh == prefix marks the current bin (32: none yet)
+    if ((uint32_t)kk < n) {
+        for (int pass = 0; pass < 4; ++pass) {
+            const int nsh = sh - 8;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) h[4 * lane + j] = 0u;
+            wave_fence();
+            visit([&](uint2 e, bool v) {
+                if (v && (sh == 32 || (e.x >> sh) == prefix)) atomicAdd(&h[(e.x >> nsh) & 0xffu], 1u);
+            });
+            wave_fence();
+            uint32_t hv[4], sum = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hv[j] = h[255 - 4 * lane - j];
+                sum += hv[j];
+            }
+            uint32_t incl = sum;
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
+            }
+            const int ls = __ffsll((unsigned long long)__ballot(incl >= need)) - 1;
+            uint32_t digit = 0, above = 0, cntd = 0;
+            if (lane == ls) {
+                uint32_t acc = incl - sum;
+                for (int j = 0; j < 4; ++j) {
+                    if (acc + hv[j] >= need) {
+                        digit = 255u - 4u * (uint32_t)lane - (uint32_t)j;
+                        above = acc;
+                        cntd = hv[j];
+                        break;
+                    }
+                    acc += hv[j];
+                }
+            }
+            digit = __shfl(digit, ls);
+            above = __shfl(above, ls);
+            cntd = __shfl(cntd, ls);
             need -= above;
-            prefix = (sh == 32 ? 0u : (prefix << w)) | bin;
+            prefix = (sh == 32 ? 0u : (prefix << 8)) | digit;
             sh = nsh;
-            if (cntb == need) break;
+            if (cntd == need) break;
         }
     }
+    // ---- emit in block order: keys above the bin, and the first `need` in it ----
     uint32_t eq_before = 0, out_before = 0;
-    for (int32_t b0 = 0; b0 < nc; b0 += kMergeThreads) {
-        const int32_t b = b0 + t;
-        const bool valid = b < nc;
-        const float sc = valid ? recompute_score(q4, kb + (int64_t)b * kDim) : 0.0f;
+    visit([&](uint2 e, bool v) {
         const bool all = sh == 32;
-        const uint32_t top = all ? 0u : (score_key(sc) >> sh);
-        const bool gt = valid && (all || top > prefix);
-        const bool eq = valid && !all && top == prefix;
-        uint32_t eq_total, take_total;
-        const uint32_t eq_rank = eq_before + wg_rank<kMergeThreads>(eq, wtot, eq_total);
-        const bool take = gt || (eq && eq_rank < need);
-        const uint32_t pos = out_before + wg_rank<kMergeThreads>(take, wtot, take_total);
+        const uint32_t top = all ? 0u : (e.x >> sh);
+        const bool gt = v && (all || top > prefix);
+        const bool eq = v && !all && top == prefix;
+        const uint64_t eb = __ballot(eq);
+        const bool take = gt || (eq && eq_before + (uint32_t)__popcll(eb & lt) < need);
+        const uint64_t tb = __ballot(take);
+        const uint32_t pos = out_before + (uint32_t)__popcll(tb & lt);
         if (take && pos < (uint32_t)kk) {
-            out[pos] = b;
-            if (osc) osc[pos] = scaled(sc);
+            out[pos] = (int32_t)e.y;
+            if (osc) osc[pos] = scaled(key_score(e.x));
         }
-        eq_before += eq_total;
-        out_before += take_total;
-    }
+        eq_before += (uint32_t)__popcll(eb);
+        out_before += (uint32_t)__popcll(tb);
+    });
 }
 
 // Split of the block range: enough workgroups to fill the chip, each split a
@@ -467,8 +489,8 @@ void launch_score_fused(const FusedScoreArgs &a, int32_t *sel_blocks, int32_t *s
         const dim3 grid((unsigned)((a.rows + kFRows - 1) / kFRows), (unsigned)a.nsplit), block(256);
         QSA_LAUNCH("score_filter", score_filter_kernel, grid, block, 0, stream, a);
     }
-    QSA_LAUNCH("select_merge", select_merge_kernel, dim3((unsigned)a.rows), dim3(kMergeThreads), 0, stream, a,
-               sel_blocks, sel_count, sel_scores);
+    QSA_LAUNCH("select_merge", select_merge_kernel, dim3((unsigned)((a.rows + kMergeWaves - 1) / kMergeWaves)),
+               dim3(kMergeWaves * kWave), 0, stream, a, sel_blocks, sel_count, sel_scores);
 }
 
 }  // namespace qsa
