@@ -104,8 +104,8 @@ struct ScoreLayout {
     ScorePlan plan;
     int64_t sc_stride;
     size_t qrot_off, scores_off, scratch_off, sure_off, cand_off;
-    int32_t nsplit, split_len, cap;
-    size_t buf_off, cnt_off, tau_off;
+    int32_t nsplit, split_len, subcap, nsample;
+    size_t buf_off, cnt_off, sample_off, tau_off;
     size_t total;
 };
 
@@ -119,11 +119,13 @@ static ScoreLayout score_layout(int32_t rows, int32_t max_nb, int32_t top_k, qsa
     if (L.plan.fused) {
         L.nsplit = fused_score_splits(rows, max_nb);
         L.split_len = fused_score_split_len(max_nb, L.nsplit);
-        L.cap = fused_score_cap(top_k);
+        L.subcap = fused_score_subcap(top_k, L.nsplit);
+        L.nsample = fused_score_nsample(max_nb);
         L.buf_off = off;
-        L.cnt_off = L.buf_off + align256((size_t)rows * L.nsplit * (size_t)L.cap * sizeof(uint2));
-        L.tau_off = L.cnt_off + align256((size_t)rows * L.nsplit * sizeof(uint32_t));
-        L.total = L.tau_off + align256((size_t)rows * L.nsplit * sizeof(uint32_t));
+        L.cnt_off = L.buf_off + align256((size_t)rows * L.nsplit * 16 * (size_t)L.subcap * sizeof(uint2));
+        L.sample_off = L.cnt_off + align256((size_t)rows * L.nsplit * 16 * sizeof(uint32_t));
+        L.tau_off = L.sample_off + align256((size_t)rows * (size_t)L.nsample * sizeof(float));
+        L.total = L.tau_off + align256((size_t)rows * sizeof(uint32_t));
         return L;
     }
     L.scores_off = off;
@@ -235,9 +237,11 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
         fa.top_k = top_k;
         fa.nsplit = L.nsplit;
         fa.split_len = L.split_len;
-        fa.cap = L.cap;
+        fa.subcap = L.subcap;
         fa.buf = (uint2 *)(ws + L.buf_off);
         fa.cnt = (uint32_t *)(ws + L.cnt_off);
+        fa.nsample = L.nsample;
+        fa.sample = (float *)(ws + L.sample_off);
         fa.tau = (uint32_t *)(ws + L.tau_off);
         launch_score_fused(fa, sel_blocks, sel_count, sel_scores, st);
         return launch_status();

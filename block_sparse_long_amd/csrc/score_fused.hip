@@ -8,30 +8,25 @@
 // un-scaled sum.
 //
 // Materializing every score would cost 4 bytes per (row, block) pair of HBM
-// traffic, more than the GEMM's own time at MFMA rate, so the GEMM keeps per
-// row a lower bound tau on the row's k-th best score and writes out only the
-// pairs with score >= tau.  tau is valid whenever at least k already written
-// pairs of the row score >= tau (then the k-th best of all visible blocks is
-// >= tau, and a pair below it cannot be kept).  Each row counts its written
-// pairs in a 256-bin histogram over key space -- 1/32 octave per bin, 4
-// octaves either side of an anchor (the row's best score in its first 64
-// blocks), everything above or below lumped into the end bins.  tau is the
-// lowest key of bin b*, the highest bin at which k written pairs are reached;
-// every written pair lies in a bin <= b*, so after each 64-block step b*
-// only moves up while the bins above it still hold k pairs (a few LDS reads
-// per row).  A step's pairs get their slots with one LDS atomic per row,
-// ordered by block, so each split's list is ascending.
-//
-// Workgroup: 4 waves x 16 query rows (MFMA row m of tile mt = query row
-// 4*mt + m/4, index head m%4, so a lane's 4 accumulators are the 4 heads of
-// one (row, block) pair), one split of the block range.  The 64-block key
-// tile is staged through LDS (double buffered) and shared by the 4 waves.
-// The merge kernel takes, per row, the pairs of every split at or above the
-// best split's tau -- in block order, since the splits are ordered and each
-// list is ascending -- finds the exact k-th key with a radix select (12, 12,
-// 8 bits), and emits, in block order, every pair above it and the first
-// `need` pairs equal to it (lower blocks win ties).  A row whose pair buffer
-// overflowed (e.g. massive exact ties) is redone from recomputed scores.
+// traffic, more than the GEMM's own time at MFMA rate.  Instead:
+//   1. sample: every row is scored against one block in 32 (a fixed
+//      pseudo-random pick inside each group of 32), about 3% of the GEMM;
+//   2. threshold: tau = the row's j-th best sampled score, j = ceil(3k/32)
+//      (so about 3k of the row's blocks are expected to score >= tau);
+//   3. filter: the full GEMM writes out only the (key, block) pairs with
+//      score >= tau, each lane into its own list (no atomics, no cross-lane
+//      work in the MFMA loop);
+//   4. merge: a row is exact when at least min(k, nc) of its pairs reached
+//      tau -- then the k-th best of all visible blocks is >= tau and every
+//      block it keeps is among the pairs -- and the merge picks the top k
+//      among them with a radix select on the unique composite (key, ~block),
+//      then sorts them by block.  A row whose count fell short, or whose list
+//      overflowed, is redone from recomputed scores of every visible block.
+// Workgroup of the GEMMs: 4 waves x 16 query rows; MFMA row m of tile mt is
+// query row 4*mt + m/4, index head m%4, so a lane's 4 accumulators are the 4
+// heads of one (row, block) pair and the ReLU-sum stays in the lane.  The
+// 64-block key tile is staged through LDS (double buffered) and shared by the
+// 4 waves.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 #include "qsa_wg.h"
@@ -40,76 +35,39 @@ namespace qsa {
 
 namespace {
 
-constexpr int kFRows = 64;            // rows per workgroup
+constexpr int kFRows = 64;            // rows per GEMM workgroup
 constexpr int kFStep = 64;            // blocks per step
 constexpr int kFKRow = kDim + 8;      // LDS key row stride (bf16): conflict-free b128 reads
-constexpr int kTauBins = 256;
-constexpr int kTauShift = 18;         // 2^18 key units = 1/32 octave
+constexpr int kSampleStride = 32;     // one sampled block per 32
 constexpr int kMergeWaves = 4;        // merge: rows per workgroup, one wave each
 constexpr int kStage = 2048;          // merge: pairs a wave stages in LDS
+
+__device__ __forceinline__ int32_t sample_j(int32_t top_k) { return (3 * top_k + kSampleStride - 1) / kSampleStride; }
+
+// Block of sample i: group i of 32 blocks, a fixed pseudo-random offset in it.
+__device__ __forceinline__ int64_t sample_block(int64_t i)
+{
+    const uint32_t h = (uint32_t)i * 2654435761u;  // Knuth's multiplicative hash
+    return i * kSampleStride + (h >> 27);
+}
 
 __device__ __forceinline__ float relu_sum4f(f32x4_t a)
 {
     return ((fmaxf(a[0], 0.0f) + fmaxf(a[1], 0.0f)) + fmaxf(a[2], 0.0f)) + fmaxf(a[3], 0.0f);
 }
 
-// Top of a row's bin window: its anchor key + 4 octaves (2^25 key units).
-__device__ __forceinline__ uint32_t window_top(uint32_t anchor)
-{
-    const uint64_t t = (uint64_t)anchor + (1ull << 25);
-    return t > 0xffffffffull ? 0xffffffffu : (uint32_t)t;
-}
+// Order key of a non-negative score (a sum of ReLUs; -0 and +0 map to one key).
+__device__ __forceinline__ uint32_t pos_key(float s) { return __float_as_uint(s) | 0x80000000u; }
 
-// Bin of a key: 0 at and above the window top, 255 for everything 8 octaves down.
-__device__ __forceinline__ int tau_bin(uint32_t key, uint32_t top)
-{
-    if (key >= top) return 0;
-    const uint32_t b = (top - key) >> kTauShift;
-    return b >= (uint32_t)(kTauBins - 1) ? kTauBins - 1 : (int)b;
-}
-
-// Threshold key -> float for `score >= tau` (key 0: no threshold yet).
 __device__ __forceinline__ float tau_float(uint32_t key) { return key == 0u ? -INFINITY : key_score(key); }
-
-// Lowest key of bin b (the last bin reaches down to every key).
-__device__ __forceinline__ uint32_t tau_bin_floor(int b, uint32_t top)
-{
-    if (b >= kTauBins - 1) return 0u;
-    const int64_t k = (int64_t)top - ((int64_t)(b + 1) << kTauShift) + 1;
-    return k <= 0 ? 0u : (uint32_t)k;
-}
-
-__device__ __forceinline__ uint32_t hist_get(const uint32_t *h, int b) { return (h[b >> 1] >> (16 * (b & 1))) & 0xffffu; }
 
 __device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
-}  // namespace
-
-__global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
+// The 16 x 4 x 128 query tile of a wave as MFMA A operands (zeros past nrows).
+__device__ __forceinline__ void load_query_tile(const bf16_t *__restrict__ qrot, int64_t row0, int nrows, int wave,
+                                                bf16x8_t (&qa)[4][4])
 {
-    const bf16_t *__restrict__ qrot = (const bf16_t *)a.qrot;
-    const bf16_t *__restrict__ pooled = (const bf16_t *)a.pooled;
-    __shared__ bf16_t keys[2][kFStep][kFKRow];
-    __shared__ uint32_t hist[kFRows][kTauBins / 2];  // two 16-bit bins per word
-    __shared__ uint32_t cnt[kFRows], tau[kFRows], wtop[kFRows], removed[kFRows];
-    __shared__ int32_t bstar[kFRows];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int m = lane & 15, g = lane >> 4;
-    const int64_t row0 = (int64_t)blockIdx.x * kFRows;
-    const int nrows = (int)min((int64_t)kFRows, (int64_t)a.rows - row0);
-    const int split = blockIdx.y;
-    const int64_t split_lo = (int64_t)split * a.split_len;
-    const int64_t split_hi = min((int64_t)a.max_nb, split_lo + a.split_len);
-    for (int i = t; i < kFRows * kTauBins / 2; i += 256) (&hist[0][0])[i] = 0u;
-    if (t < kFRows) {
-        cnt[t] = 0u;
-        tau[t] = 0u;
-        wtop[t] = window_top(0x80000000u);
-        removed[t] = 0u;
-        bstar[t] = kTauBins - 1;
-    }
-    // A operands: this wave's 16 rows x 4 heads
-    bf16x8_t qa[4][4];
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const int rw = 16 * wave + 4 * mt + (m >> 2);
@@ -119,163 +77,263 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
             qa[mt][s] = ok ? as_bf16x8(*(const uint4 *)(qrot + ((row0 + rw) * kIdxHeads + (m & 3)) * kDim + 32 * g + 8 * s))
                            : zero_bf16x8();
     }
-    // the 4 rows whose scores this lane receives: 16*wave + 4*mt + g
+}
+
+// Scores of one 64-block tile in LDS: sc[mt][nt] = raw(row 16*wave + 4*mt + g,
+// block nt*16 + m of the tile).  Four independent accumulator chains.
+__device__ __forceinline__ void tile_scores(const bf16_t (*keys)[kFKRow], const bf16x8_t (&qa)[4][4],
+                                            float (&sc)[4][4])
+{
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        bf16x8_t bk[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bk[s] = as_bf16x8(*(const uint4 *)&keys[nt * 16 + m][32 * g + 8 * s]);
+        f32x4_t acc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], bk[s], acc[mt], 0, 0, 0);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) sc[mt][nt] = relu_sum4f(acc[mt]);
+    }
+}
+
+// Rows of one sequence at a time: the next group of the workgroup's rows
+// (uniform across the workgroup).  Returns the sequence and the largest
+// visible-block count of the group; clears the group's bits from `todo`.
+__device__ __forceinline__ int32_t next_seq_group(const FusedScoreArgs &a, int64_t row0, int nrows, uint64_t &todo,
+                                                  int64_t &nb_hi)
+{
+    const int first = __builtin_ctzll(todo);
+    const int32_t seq = a.row_seq[row0 + first];
+    nb_hi = 0;
+    for (int r = first; r < nrows; ++r)
+        if (((todo >> r) & 1ull) && a.row_seq[row0 + r] == seq) {
+            todo &= ~(1ull << r);
+            nb_hi = max(nb_hi, min(visible_blocks(a.row_pos[row0 + r]), (int64_t)a.max_nb));
+        }
+    return seq;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// 1. sample: grid = row tiles.  sample[row][i] = raw(row, sample_block(i)), or
+//    -1 when that block is not visible to the row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void score_sample_kernel(FusedScoreArgs a)
+{
+    __shared__ bf16_t keys[kFStep][kFKRow];
+    const bf16_t *__restrict__ qrot = (const bf16_t *)a.qrot;
+    const bf16_t *__restrict__ pooled = (const bf16_t *)a.pooled;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t row0 = (int64_t)blockIdx.x * kFRows;
+    const int nrows = (int)min((int64_t)kFRows, (int64_t)a.rows - row0);
+    bf16x8_t qa[4][4];
+    load_query_tile(qrot, row0, nrows, wave, qa);
     int64_t my_nc[4];
     int32_t my_seq[4];
-    uint2 *my_buf[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const int rw = 16 * wave + 4 * mt + g;
         my_nc[mt] = rw < nrows ? min(visible_blocks(a.row_pos[row0 + rw]), (int64_t)a.max_nb) : 0;
         my_seq[mt] = rw < nrows ? a.row_seq[row0 + rw] : -1;
-        my_buf[mt] = a.buf + ((row0 + min(rw, nrows - 1)) * a.nsplit + split) * (int64_t)a.cap;
     }
+    // every row's sample list starts as "not visible"
+    for (int i = t; i < nrows * a.nsample; i += 256) a.sample[row0 * a.nsample + i] = -1.0f;
     __syncthreads();
     uint64_t todo = nrows >= 64 ? ~0ull : ((1ull << nrows) - 1ull);
-    while (todo) {  // rows of one sequence at a time (uniform across the workgroup)
-        const int first = __builtin_ctzll(todo);
-        const int32_t seq = a.row_seq[row0 + first];
-        int64_t nb_hi = 0;
-        uint64_t active = 0;
-        for (int r = first; r < nrows; ++r)
-            if (((todo >> r) & 1ull) && a.row_seq[row0 + r] == seq) {
-                active |= 1ull << r;
-                nb_hi = max(nb_hi, min(visible_blocks(a.row_pos[row0 + r]), (int64_t)a.max_nb));
+    while (todo) {
+        int64_t nb_hi;
+        const int32_t seq = next_seq_group(a, row0, nrows, todo, nb_hi);
+        const bf16_t *kb = pooled + (int64_t)seq * a.pooled_stride;
+        const int64_t ns = (nb_hi + kSampleStride - 1) / kSampleStride;  // samples that can be visible
+        const int lrow = t >> 2, ldim = (t & 3) * 32;
+        for (int64_t i0 = 0; i0 < ns; i0 += kFStep) {
+            {   // gather the step's sampled keys
+                const int64_t b = min(sample_block(min(i0 + lrow, ns - 1)), nb_hi - 1);
+                const uint4 *src = (const uint4 *)(kb + b * kDim + ldim);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) *(uint4 *)&keys[lrow][ldim + 8 * i] = src[i];
             }
-        todo &= ~active;
-        int64_t lim[4];  // visible bound of the lane's rows in this pass (0: not in it)
+            __syncthreads();
+            float sc[4][4];
+            tile_scores(keys, qa, sc);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int rw = 16 * wave + 4 * mt + g;
+                if (my_seq[mt] != seq) continue;
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const int64_t i = i0 + nt * 16 + m;
+                    if (i < ns && sample_block(i) < my_nc[mt]) a.sample[(row0 + rw) * a.nsample + i] = sc[mt][nt];
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 2. threshold: one wave per row.  tau[row] = key of the j-th best sampled
+//    score, or 0 (no threshold) when fewer than j samples are visible.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void sample_threshold_kernel(FusedScoreArgs a)
+{
+    __shared__ uint32_t hb[4][256];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t r = (int64_t)blockIdx.x * 4 + w;
+    if (r >= a.rows) return;
+    const float *srow = a.sample + r * a.nsample;
+    uint32_t *h = hb[w];
+    const uint32_t j = (uint32_t)sample_j(a.top_k);
+    uint32_t valid = 0;
+    for (int32_t i = lane; i < a.nsample; i += kWave) valid += srow[i] >= 0.0f ? 1u : 0u;
+    for (int o = 32; o > 0; o >>= 1) valid += __shfl_xor(valid, o);
+    if (valid < j) {
+        if (lane == 0) a.tau[r] = 0u;
+        return;
+    }
+    uint32_t need = j, prefix = 0;
+    int sh = 32;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int nsh = sh - 8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h[4 * lane + q] = 0u;
+        wave_fence();
+        for (int32_t i = lane; i < a.nsample; i += kWave) {
+            const float v = srow[i];
+            const uint32_t key = pos_key(v);
+            if (v >= 0.0f && (sh == 32 || (key >> sh) == prefix)) atomicAdd(&h[(key >> nsh) & 0xffu], 1u);
+        }
+        wave_fence();
+        uint32_t hv[4], sum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            hv[q] = h[255 - 4 * lane - q];
+            sum += hv[q];
+        }
+        uint32_t incl = sum;
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        const int ls = __ffsll((unsigned long long)__ballot(incl >= need)) - 1;
+        uint32_t digit = 0, above = 0;
+        if (lane == ls) {
+            uint32_t acc = incl - sum;
+            for (int q = 0; q < 4; ++q) {
+                if (acc + hv[q] >= need) {
+                    digit = 255u - 4u * (uint32_t)lane - (uint32_t)q;
+                    above = acc;
+                    break;
+                }
+                acc += hv[q];
+            }
+        }
+        digit = __shfl(digit, ls);
+        above = __shfl(above, ls);
+        need -= above;
+        prefix = (sh == 32 ? 0u : (prefix << 8)) | digit;
+        sh = nsh;
+    }
+    if (lane == 0) a.tau[r] = prefix;  // all 32 bits resolved: the j-th best key
+}
+
+// ---------------------------------------------------------------------------
+// 3. filter: grid (row tiles, splits).  Lane (mt, g, m) owns list m of row
+//    16*wave + 4*mt + g in this split and appends its pairs >= tau there.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
+{
+    __shared__ bf16_t keys[2][kFStep][kFKRow];
+    const bf16_t *__restrict__ qrot = (const bf16_t *)a.qrot;
+    const bf16_t *__restrict__ pooled = (const bf16_t *)a.pooled;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t row0 = (int64_t)blockIdx.x * kFRows;
+    const int nrows = (int)min((int64_t)kFRows, (int64_t)a.rows - row0);
+    const int split = blockIdx.y;
+    const int64_t split_lo = (int64_t)split * a.split_len;
+    const int64_t split_hi = min((int64_t)a.max_nb, split_lo + a.split_len);
+    bf16x8_t qa[4][4];
+    load_query_tile(qrot, row0, nrows, wave, qa);
+    int64_t my_nc[4];
+    int32_t my_seq[4];
+    uint2 *my_list[4];
+    uint32_t my_cnt[4];
+    float tauf[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int rw = 16 * wave + 4 * mt + g;
+        const bool ok = rw < nrows;
+        my_nc[mt] = ok ? min(visible_blocks(a.row_pos[row0 + rw]), (int64_t)a.max_nb) : 0;
+        my_seq[mt] = ok ? a.row_seq[row0 + rw] : -1;
+        my_list[mt] = a.buf + (((row0 + (ok ? rw : 0)) * a.nsplit + split) * 16 + m) * (int64_t)a.subcap;
+        my_cnt[mt] = 0;
+        tauf[mt] = ok ? tau_float(a.tau[row0 + rw]) : INFINITY;
+    }
+    uint64_t todo = nrows >= 64 ? ~0ull : ((1ull << nrows) - 1ull);
+    while (todo) {
+        int64_t nb_hi;
+        const int32_t seq = next_seq_group(a, row0, nrows, todo, nb_hi);
+        int64_t lim[4];  // visible bound of the lane's rows in this group (0: not in it)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) lim[mt] = my_seq[mt] == seq ? my_nc[mt] : 0;
         const int64_t lo = split_lo, hi = min(split_hi, nb_hi);
         if (lo >= hi) continue;
         const bf16_t *kb = pooled + (int64_t)seq * a.pooled_stride;
-        // key tile loader: thread -> block t/4 of the step, 64 bytes at dim 32*(t%4)
         const int lrow = t >> 2, ldim = (t & 3) * 32;
-        uint4 pre[4];
-        auto load_tile = [&](int64_t base) {
-            const int64_t b = min(base + lrow, hi - 1);
-            const uint4 *src = (const uint4 *)(kb + b * kDim + ldim);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pre[i] = src[i];
-        };
-        auto store_tile = [&](int buf) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) *(uint4 *)&keys[buf][lrow][ldim + 8 * i] = pre[i];
-        };
-        load_tile(lo);
-        store_tile(0);
+        uint4 p0, p1, p2, p3;  // the next tile's 64 bytes for this thread
+        {
+            const uint4 *src = (const uint4 *)(kb + min(lo + lrow, hi - 1) * kDim + ldim);
+            p0 = src[0];
+            p1 = src[1];
+            p2 = src[2];
+            p3 = src[3];
+            uint4 *dst = (uint4 *)&keys[0][lrow][ldim];
+            dst[0] = p0;
+            dst[1] = p1;
+            dst[2] = p2;
+            dst[3] = p3;
+        }
         __syncthreads();
-        float tauf[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) tauf[mt] = tau_float(tau[16 * wave + 4 * mt + g]);
         int cur = 0;
-        bool first_step = true;
         for (int64_t base = lo; base < hi; base += kFStep) {
             const bool more = base + kFStep < hi;
-            if (more) load_tile(base + kFStep);
-            // ---- scores of the step: 4 block tiles x (4 independent row-tile chains) ----
+            if (more) {
+                const uint4 *src = (const uint4 *)(kb + min(base + kFStep + lrow, hi - 1) * kDim + ldim);
+                p0 = src[0];
+                p1 = src[1];
+                p2 = src[2];
+                p3 = src[3];
+            }
             float sc[4][4];
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                bf16x8_t bk[4];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) bk[s] = as_bf16x8(*(const uint4 *)&keys[cur][nt * 16 + m][32 * g + 8 * s]);
-                f32x4_t acc[4];
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], bk[s], acc[mt], 0, 0, 0);
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) sc[mt][nt] = relu_sum4f(acc[mt]);
+            tile_scores(keys[cur], qa, sc);
+            if (more) {
+                uint4 *dst = (uint4 *)&keys[cur ^ 1][lrow][ldim];
+                dst[0] = p0;
+                dst[1] = p1;
+                dst[2] = p2;
+                dst[3] = p3;
             }
-            if (more) store_tile(cur ^ 1);
-            // valid iff 16*nt < lr[mt] (block base + 16*nt + m below the row's bound)
-            int32_t lr[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) lr[mt] = (int32_t)max(min(lim[mt] - base - m, (int64_t)kFStep), (int64_t)-1);
-            // ---- anchors: each row's best score in its first step ----
-            if (first_step) {
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    float mx = 0.0f;
-#pragma unroll
-                    for (int nt = 0; nt < 4; ++nt)
-                        if (16 * nt < lr[mt]) mx = fmaxf(mx, sc[mt][nt]);
-                    for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-                    if (m == 0 && lim[mt] > 0) wtop[16 * wave + 4 * mt + g] = window_top(score_key(mx));
-                }
-                wave_fence();
-                first_step = false;
-            }
-            // ---- filter: pairs at or above the row's tau are written out ----
-            bool appended = false;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                bool pass[4];
-                bool any = false;
+                // block base + 16*nt + m is visible iff 16*nt < lr
+                const int32_t lr = (int32_t)max(min(lim[mt] - base - m, (int64_t)kFStep), (int64_t)-1);
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
-                    pass[nt] = sc[mt][nt] >= tauf[mt] && 16 * nt < lr[mt];
-                    any |= pass[nt];
-                }
-                if (!__ballot(any)) continue;  // wave-uniform
-                appended = true;
-                // slots of row 16*wave + 4*mt + g, ordered by block (nt, then m)
-                const int rw = 16 * wave + 4 * mt + g;
-                uint32_t mine[4], total = 0;
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    const uint32_t grp = (uint32_t)(__ballot(pass[nt]) >> (16 * g)) & 0xffffu;
-                    mine[nt] = total + (uint32_t)__popc(grp & ((1u << m) - 1u));
-                    total += (uint32_t)__popc(grp);
-                }
-                uint32_t slot0 = 0;
-                if (m == 0 && total) slot0 = atomicAdd(&cnt[rw], total);
-                slot0 = __shfl(slot0, 16 * g);
-                const uint32_t top = wtop[rw];
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    const uint32_t slot = slot0 + mine[nt];
-                    if (pass[nt] && slot < (uint32_t)a.cap) {
-                        const uint32_t key = score_key(sc[mt][nt]);
-                        my_buf[mt][slot] = make_uint2(key, (uint32_t)(base + nt * 16 + m));
-                        const int bin = tau_bin(key, top);
-                        atomicAdd(&hist[rw][bin >> 1], (bin & 1) ? 0x10000u : 1u);
+                    if (sc[mt][nt] >= tauf[mt] && 16 * nt < lr) {
+                        if (my_cnt[mt] < (uint32_t)a.subcap)
+                            my_list[mt][my_cnt[mt]] = make_uint2(pos_key(sc[mt][nt]), (uint32_t)(base + nt * 16 + m));
+                        ++my_cnt[mt];
                     }
-                }
-            }
-            if (appended) {
-                wave_fence();
-                // ---- raise tau: lane i < 16 moves row 16*wave + i's b* up ----
-                bool changed = false;
-                if (lane < 16) {
-                    const int rw = 16 * wave + lane;
-                    const uint32_t c_all = cnt[rw];
-                    if (c_all <= (uint32_t)a.cap) {
-                        uint32_t c = c_all - removed[rw];
-                        int bs = bstar[rw];
-                        const uint32_t *h = hist[rw];
-                        while (bs > 0) {
-                            const uint32_t hb = hist_get(h, bs);
-                            if (c - hb < (uint32_t)a.top_k) break;
-                            c -= hb;
-                            --bs;
-                        }
-                        if (bs != bstar[rw]) {
-                            removed[rw] = c_all - c;
-                            bstar[rw] = bs;
-                            tau[rw] = tau_bin_floor(bs, wtop[rw]);
-                            changed = true;
-                        }
-                    }
-                }
-                if (__ballot(changed)) {
-                    wave_fence();
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) tauf[mt] = tau_float(tau[16 * wave + 4 * mt + g]);
                 }
             }
             __syncthreads();
@@ -283,14 +341,15 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
         }
         __syncthreads();
     }
-    if (t < nrows) {
-        a.cnt[(row0 + t) * a.nsplit + split] = cnt[t];
-        a.tau[(row0 + t) * a.nsplit + split] = tau[t];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int rw = 16 * wave + 4 * mt + g;
+        if (rw < nrows) a.cnt[((row0 + rw) * a.nsplit + split) * 16 + m] = my_cnt[mt];
     }
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one workgroup per row.
+// 4. merge: one wave per row, four rows per workgroup; no workgroup barriers.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -313,13 +372,10 @@ __device__ __forceinline__ float recompute_score(const bf16_t *__restrict__ q4, 
 }
 
 __device__ __forceinline__ float scaled(float raw) { return (float)((double)raw / sqrt((double)kDim)); }
+__device__ __forceinline__ uint64_t composite(uint2 e) { return ((uint64_t)e.x << 32) | (uint64_t)(~e.y); }
 
 }  // namespace
 
-// One wave per row, four rows per workgroup; no workgroup barriers.  The
-// row's pairs >= the best split's tau are visited in block order -- from LDS
-// when they fit, else straight from the pair buffers -- or, for a row whose
-// buffer overflowed, as recomputed scores of every visible block.
 __global__ __launch_bounds__(256) void select_merge_kernel(FusedScoreArgs a, int32_t *__restrict__ sel_blocks,
                                                          int32_t *__restrict__ sel_count, float *__restrict__ sel_scores)
 {
@@ -338,40 +394,46 @@ __global__ __launch_bounds__(256) void select_merge_kernel(FusedScoreArgs a, int
         out[i] = -1;
         if (osc) osc[i] = 0.0f;
     }
-    if (nc <= 0) return;  // no visible block (the scorer may not have run at all)
-    bool overflow = false;
-    uint32_t tau_max = 0;
-    for (int s = 0; s < a.nsplit; ++s) {
-        overflow |= a.cnt[r * a.nsplit + s] > (uint32_t)a.cap;
-        tau_max = max(tau_max, a.tau[r * a.nsplit + s]);
-    }
+    if (nc <= 0) return;  // no visible block (the GEMMs may not have run at all)
     uint2 *st = stage[w];
     uint32_t *h = hb[w];
-    // ---- the pairs to rank: mode 0 staged in LDS, 1 in the buffers, 2 recomputed ----
+    // ---- the row's pairs (list i of 16 * nsplit) ----
+    const int nlists = a.nsplit * 16;
+    uint32_t total = 0;
+    bool overflow = false;
+    for (int i0 = 0; i0 < nlists; i0 += kWave) {
+        const uint32_t c = i0 + lane < nlists ? a.cnt[r * nlists + i0 + lane] : 0u;
+        overflow |= __ballot(c > (uint32_t)a.subcap) != 0ull;
+        uint32_t s = c;
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+        total += s;
+    }
+    // exact only if at least kk pairs reached tau (and none was dropped); a
+    // kept set too large to sort in LDS is ranked and emitted in block order
+    // from recomputed scores
+    int mode = (overflow || total < (uint32_t)kk || kk > kStage) ? 2 : (total <= (uint32_t)kStage ? 0 : 1);
+    const uint2 *lists = a.buf + (int64_t)r * nlists * a.subcap;
     uint32_t n = 0;
-    int mode = 2;
-    if (!overflow) {
-        for (int s = 0; s < a.nsplit; ++s) {
-            const uint32_t c = a.cnt[r * a.nsplit + s];
-            const uint2 *src = a.buf + (r * a.nsplit + s) * (int64_t)a.cap;
+    if (mode == 0) {  // stage the pairs in LDS
+        for (int li = 0; li < nlists; ++li) {
+            const uint32_t c = a.cnt[r * nlists + li];
             for (uint32_t i0 = 0; i0 < c; i0 += kWave) {
                 const uint32_t i = i0 + lane;
-                const uint2 e = i < c ? src[i] : make_uint2(0u, 0u);
-                const bool keep = i < c && e.x >= tau_max;
-                const uint64_t bal = __ballot(keep);
-                const uint32_t pos = n + (uint32_t)__popcll(bal & lt);
-                if (keep && pos < (uint32_t)kStage) st[pos] = e;
-                n += (uint32_t)__popcll(bal);
+                if (i < c) st[n + i] = lists[(int64_t)li * a.subcap + i];
             }
+            n += c;
         }
-        mode = n <= (uint32_t)kStage ? 0 : 1;
+    } else if (mode == 1) {
+        n = total;
+    } else {
+        n = (uint32_t)nc;
     }
     const int32_t seq = a.row_seq[r];
     const bf16_t *q4 = (const bf16_t *)a.qrot + r * kIdxHeads * kDim;
     const bf16_t *kb = (const bf16_t *)a.pooled + (int64_t)seq * a.pooled_stride;
-    if (mode == 2) n = (uint32_t)nc;
     wave_fence();
-    // visit every pair in block order, 64 at a time: fn(pair, valid)
+    // visit every candidate, 64 at a time: fn(pair, valid).  Staged and listed
+    // pairs come in no particular order; recomputed ones in block order.
     auto visit = [&](auto &&fn) {
         if (mode == 0) {
             for (uint32_t i0 = 0; i0 < n; i0 += kWave) {
@@ -379,42 +441,39 @@ __global__ __launch_bounds__(256) void select_merge_kernel(FusedScoreArgs a, int
                 fn(i < n ? st[i] : make_uint2(0u, 0u), i < n);
             }
         } else if (mode == 1) {
-            for (int s = 0; s < a.nsplit; ++s) {
-                const uint32_t c = a.cnt[r * a.nsplit + s];
-                const uint2 *src = a.buf + (r * a.nsplit + s) * (int64_t)a.cap;
+            for (int li = 0; li < nlists; ++li) {
+                const uint32_t c = a.cnt[r * nlists + li];
                 for (uint32_t i0 = 0; i0 < c; i0 += kWave) {
                     const uint32_t i = i0 + lane;
-                    const uint2 e = i < c ? src[i] : make_uint2(0u, 0u);
-                    fn(e, i < c && e.x >= tau_max);
+                    fn(i < c ? lists[(int64_t)li * a.subcap + i] : make_uint2(0u, 0u), i < c);
                 }
             }
         } else {
             for (int32_t b0 = 0; b0 < nc; b0 += kWave) {
                 const int32_t b = b0 + lane;
                 const bool v = b < nc;
-                const uint32_t key = v ? score_key(recompute_score(q4, kb + (int64_t)b * kDim)) : 0u;
-                fn(make_uint2(key, (uint32_t)b), v);
+                fn(make_uint2(v ? pos_key(recompute_score(q4, kb + (int64_t)b * kDim)) : 0u, (uint32_t)b), v);
             }
         }
     };
-    // ---- radix select of the kk-th key, 8 bits at a time ----
-    uint32_t need = (uint32_t)kk, prefix = 0;
-    int sh = 32;  // key >> sh == prefix marks the current bin (32: none yet)
+    // ---- radix select of the kk-th largest composite, 8 bits at a time ----
+    uint32_t need = (uint32_t)kk;
+    uint64_t prefix = 0, pmask = 0;
     if ((uint32_t)kk < n) {
-        for (int pass = 0; pass < 4; ++pass) {
-            const int nsh = sh - 8;
+        for (int sh = 56; sh >= 0; sh -= 8) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) h[4 * lane + j] = 0u;
+            for (int q = 0; q < 4; ++q) h[4 * lane + q] = 0u;
             wave_fence();
             visit([&](uint2 e, bool v) {
-                if (v && (sh == 32 || (e.x >> sh) == prefix)) atomicAdd(&h[(e.x >> nsh) & 0xffu], 1u);
+                const uint64_t c = composite(e);
+                if (v && (c & pmask) == prefix) atomicAdd(&h[(uint32_t)(c >> sh) & 0xffu], 1u);
             });
             wave_fence();
             uint32_t hv[4], sum = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                hv[j] = h[255 - 4 * lane - j];
-                sum += hv[j];
+            for (int q = 0; q < 4; ++q) {
+                hv[q] = h[255 - 4 * lane - q];
+                sum += hv[q];
             }
             uint32_t incl = sum;
             for (int o = 1; o < 64; o <<= 1) {
@@ -425,47 +484,80 @@ __global__ __launch_bounds__(256) void select_merge_kernel(FusedScoreArgs a, int
             uint32_t digit = 0, above = 0, cntd = 0;
             if (lane == ls) {
                 uint32_t acc = incl - sum;
-                for (int j = 0; j < 4; ++j) {
-                    if (acc + hv[j] >= need) {
-                        digit = 255u - 4u * (uint32_t)lane - (uint32_t)j;
+                for (int q = 0; q < 4; ++q) {
+                    if (acc + hv[q] >= need) {
+                        digit = 255u - 4u * (uint32_t)lane - (uint32_t)q;
                         above = acc;
-                        cntd = hv[j];
+                        cntd = hv[q];
                         break;
                     }
-                    acc += hv[j];
+                    acc += hv[q];
                 }
             }
             digit = __shfl(digit, ls);
             above = __shfl(above, ls);
             cntd = __shfl(cntd, ls);
             need -= above;
-            prefix = (sh == 32 ? 0u : (prefix << 8)) | digit;
-            sh = nsh;
-            if (cntd == need) break;
+            prefix |= (uint64_t)digit << sh;
+            pmask |= 0xffull << sh;
+            if (cntd == need) break;  // the whole digit bin is kept
         }
     }
-    // ---- emit in block order: keys above the bin, and the first `need` in it ----
-    uint32_t eq_before = 0, out_before = 0;
+    // ---- emit the kk kept pairs (composite >= prefix) in block order ----
+    if (mode == 2) {  // recomputed pairs come in block order
+        uint32_t out_before = 0;
+        visit([&](uint2 e, bool v) {
+            const bool take = v && (composite(e) & pmask) >= prefix;
+            const uint64_t tb = __ballot(take);
+            const uint32_t pos = out_before + (uint32_t)__popcll(tb & lt);
+            if (take && pos < (uint32_t)kk) {
+                out[pos] = (int32_t)e.y;
+                if (osc) osc[pos] = scaled(key_score(e.x));
+            }
+            out_before += (uint32_t)__popcll(tb);
+        });
+        return;
+    }
+    // gather the kept pairs into stage[0..kk) as (block << 32 | key); in place
+    // for staged pairs: each write lands at or below the slot it was read from
+    uint32_t filled = 0;
     visit([&](uint2 e, bool v) {
-        const bool all = sh == 32;
-        const uint32_t top = all ? 0u : (e.x >> sh);
-        const bool gt = v && (all || top > prefix);
-        const bool eq = v && !all && top == prefix;
-        const uint64_t eb = __ballot(eq);
-        const bool take = gt || (eq && eq_before + (uint32_t)__popcll(eb & lt) < need);
+        const bool take = v && (composite(e) & pmask) >= prefix;
         const uint64_t tb = __ballot(take);
-        const uint32_t pos = out_before + (uint32_t)__popcll(tb & lt);
-        if (take && pos < (uint32_t)kk) {
-            out[pos] = (int32_t)e.y;
-            if (osc) osc[pos] = scaled(key_score(e.x));
-        }
-        eq_before += (uint32_t)__popcll(eb);
-        out_before += (uint32_t)__popcll(tb);
+        const uint32_t pos = filled + (uint32_t)__popcll(tb & lt);
+        wave_fence();
+        if (take && pos < (uint32_t)kk) *(uint64_t *)&st[pos] = ((uint64_t)e.y << 32) | e.x;
+        wave_fence();
+        filled += (uint32_t)__popcll(tb);
     });
+    uint64_t *kept = (uint64_t *)st;
+    uint32_t n2 = 1;
+    while (n2 < (uint32_t)kk) n2 <<= 1;
+    for (uint32_t i = (uint32_t)kk + lane; i < n2; i += kWave) kept[i] = ~0ull;
+    wave_fence();
+    for (uint32_t size = 2; size <= n2; size <<= 1) {  // bitonic sort by block id
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            for (uint32_t i = lane; i < n2 / 2; i += kWave) {
+                const uint32_t lo = 2 * i - (i & (stride - 1));
+                const uint32_t hi = lo + stride;
+                const bool up = (lo & size) == 0;
+                const uint64_t x = kept[lo], y = kept[hi];
+                if ((x > y) == up) {
+                    kept[lo] = y;
+                    kept[hi] = x;
+                }
+            }
+            wave_fence();
+        }
+    }
+    for (int32_t i = lane; i < kk; i += kWave) {
+        const uint64_t e = kept[i];
+        out[i] = (int32_t)(e >> 32);
+        if (osc) osc[i] = scaled(key_score((uint32_t)e));
+    }
 }
 
-// Split of the block range: enough workgroups to fill the chip, each split a
-// multiple of the step.
+// Split of the main pass's block range: enough workgroups to fill the chip.
 int32_t fused_score_splits(int32_t rows, int32_t max_nb)
 {
     const int64_t tiles = ((int64_t)rows + kFRows - 1) / kFRows;
@@ -480,14 +572,28 @@ int32_t fused_score_split_len(int32_t max_nb, int32_t nsplit)
     return (int32_t)((len + kFStep - 1) / kFStep * kFStep);
 }
 
-int32_t fused_score_cap(int32_t top_k) { return max(4096, 8 * top_k); }
+// A lane list holds its expected share of ~3k pairs with a wide margin, and
+// every visible block of a row without a threshold (fewer than j samples,
+// i.e. fewer than about 32*j visible blocks).
+int32_t fused_score_subcap(int32_t top_k, int32_t nsplit)
+{
+    const int32_t j = (3 * top_k + kSampleStride - 1) / kSampleStride;
+    const int32_t no_tau = (j + 1) * kSampleStride / 16 + 8;
+    const int32_t share = (int32_t)(((int64_t)6 * top_k + 16 * nsplit - 1) / (16 * nsplit));
+    return (max(no_tau, share) + 7) / 8 * 8;
+}
+
+int32_t fused_score_nsample(int32_t max_nb) { return (max_nb + kSampleStride - 1) / kSampleStride; }
 
 void launch_score_fused(const FusedScoreArgs &a, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
                         hipStream_t stream)
 {
     if (a.max_nb > 0) {
-        const dim3 grid((unsigned)((a.rows + kFRows - 1) / kFRows), (unsigned)a.nsplit), block(256);
-        QSA_LAUNCH("score_filter", score_filter_kernel, grid, block, 0, stream, a);
+        const unsigned tiles = (unsigned)((a.rows + kFRows - 1) / kFRows);
+        QSA_LAUNCH("score_sample", score_sample_kernel, dim3(tiles), dim3(256), 0, stream, a);
+        QSA_LAUNCH("sample_threshold", sample_threshold_kernel, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0,
+                   stream, a);
+        QSA_LAUNCH("score_filter", score_filter_kernel, dim3(tiles, (unsigned)a.nsplit), dim3(256), 0, stream, a);
     }
     QSA_LAUNCH("select_merge", select_merge_kernel, dim3((unsigned)((a.rows + kMergeWaves - 1) / kMergeWaves)),
                dim3(kMergeWaves * kWave), 0, stream, a, sel_blocks, sel_count, sel_scores);
