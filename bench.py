@@ -80,6 +80,7 @@ def prefill_work(spec, row_pos):
         "select_rows": ("hbm", 4.0 * pairs, "B"),   # scans the fp32 scores once
         "attn_prefill": ("alu", 4.0 * spec.Hq * DIM * float(npos.sum()), "flop"),
         "attn_prefill_mfma": ("mfma", 4.0 * spec.Hq * DIM * float(npos.sum()), "flop"),
+        "score_filter": ("mfma", 2.0 * 4 * DIM * pairs, "flop"),
     }, pairs, float(npos.sum())
 
 
@@ -153,7 +154,7 @@ def timed(run_step, steps, warmup):
 
 
 ALL_KERNELS = ["pool_rope", "rope_query", "score_rows_bf16", "score_rows_f32", "score_gemm_bf16", "select_rows",
-               "select_collect", "score_filter", "select_merge", "attn_prefill_mfma", "attn_decode_mfma",
+               "select_collect", "score_sample", "sample_threshold", "score_filter", "select_merge", "attn_prefill_mfma", "attn_decode_mfma",
                "attn_prefill", "attn_decode", "attn_combine"]
 
 

@@ -75,44 +75,65 @@ struct WaveState {
     float m, l;
 };
 
-// Gather K and V^T of positions pos[0..n) into LDS (zeros beyond n).
+// A thread's share of one chunk's gather: K row t/4 (64 bytes at dim
+// 32*(t%4)) and V of positions 4*(t/16) .. +3 at dims 8*(t%16) .. +7.
+struct ChunkRegs {
+    uint4 k[4];
+    uint4 v[4];
+};
+
+// Load the chunk of positions pos(0..n) into registers (zeros beyond n).  The
+// loads are only consumed by chunk_store, so they can stay in flight while
+// the previous chunk is computed.
+template <class PosFn>
+__device__ __forceinline__ void chunk_load(ChunkRegs &cr, const bf16_t *__restrict__ kbase,
+                                           const bf16_t *__restrict__ vbase, int64_t row_stride, int n, PosFn pos)
+{
+    const int t = threadIdx.x;
+    const int p = t >> 2, dk = (t & 3) * 32;
+    if (p < n) {
+        const uint4 *src = (const uint4 *)(kbase + (int64_t)pos(p) * row_stride + dk);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cr.k[i] = src[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cr.k[i] = make_uint4(0, 0, 0, 0);
+    }
+    const int p0 = (t >> 4) * 4, dv = (t & 15) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        cr.v[i] = (p0 + i < n) ? *(const uint4 *)(vbase + (int64_t)pos(p0 + i) * row_stride + dv)
+                               : make_uint4(0, 0, 0, 0);
+}
+
+// Registers -> LDS: K row-major, V transposed.
+__device__ __forceinline__ void chunk_store(ChunkSmem &cs, const ChunkRegs &cr)
+{
+    const int t = threadIdx.x;
+    const int p = t >> 2, dk = (t & 3) * 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(uint4 *)&cs.k[p][dk + 8 * i] = cr.k[i];
+    const int p0 = (t >> 4) * 4, dv = (t & 15) * 8;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+        const int w = d >> 1, hi = d & 1;
+        uint32_t e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t word = w == 0 ? cr.v[i].x : w == 1 ? cr.v[i].y : w == 2 ? cr.v[i].z : cr.v[i].w;
+            e[i] = hi ? (word >> 16) : (word & 0xffffu);
+        }
+        *(uint2 *)&cs.vt[dv + d][p0] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+    }
+}
+
+// Gather K and V^T of positions cs.pos[0..n) into LDS (zeros beyond n).
 __device__ __forceinline__ void gather_chunk(ChunkSmem &cs, const bf16_t *__restrict__ kbase,
                                              const bf16_t *__restrict__ vbase, int64_t row_stride, int n)
 {
-    const int t = threadIdx.x;
-    {   // K: thread -> row t/4, 64 bytes at dim 32*(t%4)
-        const int p = t >> 2, d0 = (t & 3) * 32;
-        uint4 v[4];
-        if (p < n) {
-            const uint4 *src = (const uint4 *)(kbase + (int64_t)cs.pos[p] * row_stride + d0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = src[i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *(uint4 *)&cs.k[p][d0 + 8 * i] = v[i];
-    }
-    {   // V^T: thread -> positions 4*(t/16) .. +3, dims 8*(t%16) .. +7
-        const int p0 = (t >> 4) * 4, d0 = (t & 15) * 8;
-        uint4 v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            v[i] = (p0 + i < n) ? *(const uint4 *)(vbase + (int64_t)cs.pos[p0 + i] * row_stride + d0)
-                                : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            const int w = d >> 1, hi = d & 1;
-            uint32_t e[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t word = w == 0 ? v[i].x : w == 1 ? v[i].y : w == 2 ? v[i].z : v[i].w;
-                e[i] = hi ? (word >> 16) : (word & 0xffffu);
-            }
-            *(uint2 *)&cs.vt[d0 + d][p0] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
-        }
-    }
+    ChunkRegs cr;
+    chunk_load(cr, kbase, vbase, row_stride, n, [&](int i) { return (int64_t)cs.pos[i]; });
+    chunk_store(cs, cr);
 }
 
 // One chunk for one wave: S^T, online softmax, O += P V.  `qbit` is the mask
@@ -332,17 +353,25 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnArgs a, int3
             }
             __syncthreads();
             const int32_t nu = (int32_t)us.count;
-            // ---- the union's blocks, 16 per chunk ----
-            for (int32_t c0 = 0; c0 < nu; c0 += kCh / kBlock) {
-                const int nb = min(kCh / kBlock, nu - c0);
-                if (t < kCh) {
-                    const int bi = t / kBlock;
-                    cs.pos[t] = bi < nb ? us.blk[c0 + bi] * kBlock + (t % kBlock) : 0;
-                    cs.pmask[t] = bi < nb ? us.mask[c0 + bi] : 0u;
+            // ---- the union's blocks, 16 per chunk; chunk c+1's gather is in
+            // flight while chunk c is computed ----
+            constexpr int kChB = kCh / kBlock;
+            const int32_t nch = (nu + kChB - 1) / kChB;
+            ChunkRegs cr;
+            if (nch > 0)
+                chunk_load(cr, kbase, vbase, row_stride, min(kChB, nu) * kBlock,
+                           [&](int i) { return (int64_t)us.blk[i / kBlock] * kBlock + (i % kBlock); });
+            for (int32_t c = 0; c < nch; ++c) {
+                const int32_t c0 = c * kChB;
+                const int nb = min(kChB, nu - c0);
+                chunk_store(cs, cr);
+                if (t < kCh) cs.pmask[t] = t / kBlock < nb ? us.mask[c0 + t / kBlock] : 0u;
+                __syncthreads();
+                if (c + 1 < nch) {
+                    const int32_t c1 = c0 + kChB;
+                    chunk_load(cr, kbase, vbase, row_stride, min(kChB, nu - c1) * kBlock,
+                               [&](int i) { return (int64_t)us.blk[c1 + i / kBlock] * kBlock + (i % kBlock); });
                 }
-                __syncthreads();
-                gather_chunk(cs, kbase, vbase, row_stride, nb * kBlock);
-                __syncthreads();
                 wave_chunk(cs, nb * kBlock, qb, qbit, a.scale, st);
                 __syncthreads();
             }

@@ -414,14 +414,28 @@ __global__ __launch_bounds__(256) void select_merge_kernel(FusedScoreArgs a, int
     int mode = (overflow || total < (uint32_t)kk || kk > kStage) ? 2 : (total <= (uint32_t)kStage ? 0 : 1);
     const uint2 *lists = a.buf + (int64_t)r * nlists * a.subcap;
     uint32_t n = 0;
-    if (mode == 0) {  // stage the pairs in LDS
-        for (int li = 0; li < nlists; ++li) {
-            const uint32_t c = a.cnt[r * nlists + li];
-            for (uint32_t i0 = 0; i0 < c; i0 += kWave) {
-                const uint32_t i = i0 + lane;
-                if (i < c) st[n + i] = lists[(int64_t)li * a.subcap + i];
+    if (mode == 0) {  // stage the pairs in LDS: 64 lists at a time, lane i copies list i
+        for (int i0 = 0; i0 < nlists; i0 += kWave) {
+            const int li = i0 + lane;
+            const uint32_t c = li < nlists ? a.cnt[r * nlists + li] : 0u;
+            uint32_t off = c, cmax = c;
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(off, o);
+                if (lane >= o) off += y;
+                cmax = max(cmax, __shfl_xor(cmax, o));
             }
-            n += c;
+            const uint32_t chunk = __shfl(off, 63);
+            off = n + off - c;
+            const uint2 *src = lists + (int64_t)min(li, nlists - 1) * a.subcap;
+            for (uint32_t j = 0; j < cmax; j += 4) {
+                uint2 e[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) e[q] = j + q < c ? src[j + q] : make_uint2(0u, 0u);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (j + q < c) st[off + j + q] = e[q];
+            }
+            n += chunk;
         }
     } else if (mode == 1) {
         n = total;
