@@ -104,8 +104,8 @@ struct ScoreLayout {
     ScorePlan plan;
     int64_t sc_stride;
     size_t qrot_off, scores_off, scratch_off, sure_off, cand_off;
-    int32_t nsplit, split_len, subcap, nsample;
-    size_t buf_off, cnt_off, sample_off, tau_off;
+    int32_t nsplit, split_len, subcap, nsample, ssplit;
+    size_t buf_off, cnt_off, scand_off, tau_off;
     size_t total;
 };
 
@@ -121,10 +121,11 @@ static ScoreLayout score_layout(int32_t rows, int32_t max_nb, int32_t top_k, qsa
         L.split_len = fused_score_split_len(max_nb, L.nsplit);
         L.subcap = fused_score_subcap(top_k, L.nsplit);
         L.nsample = fused_score_nsample(max_nb);
+        L.ssplit = fused_score_ssplit(rows, L.nsample);
         L.buf_off = off;
         L.cnt_off = L.buf_off + align256((size_t)rows * L.nsplit * 16 * (size_t)L.subcap * sizeof(uint2));
-        L.sample_off = L.cnt_off + align256((size_t)rows * L.nsplit * 16 * sizeof(uint32_t));
-        L.tau_off = L.sample_off + align256((size_t)rows * (size_t)L.nsample * sizeof(float));
+        L.scand_off = L.cnt_off + align256((size_t)rows * L.nsplit * 16 * sizeof(uint32_t));
+        L.tau_off = L.scand_off + align256((size_t)rows * L.ssplit * 64 * sizeof(uint32_t));
         L.total = L.tau_off + align256((size_t)rows * sizeof(uint32_t));
         return L;
     }
@@ -241,7 +242,8 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
         fa.buf = (uint2 *)(ws + L.buf_off);
         fa.cnt = (uint32_t *)(ws + L.cnt_off);
         fa.nsample = L.nsample;
-        fa.sample = (float *)(ws + L.sample_off);
+        fa.ssplit = L.ssplit;
+        fa.cand = (uint32_t *)(ws + L.scand_off);
         fa.tau = (uint32_t *)(ws + L.tau_off);
         launch_score_fused(fa, sel_blocks, sel_count, sel_scores, st);
         return launch_status();

@@ -56,14 +56,16 @@ struct FusedScoreArgs {
     int32_t subcap;           // capacity of one lane's pair list (16 lists per row and split)
     uint2 *buf;               // [rows][nsplit][16][subcap] (key, block)
     uint32_t *cnt;            // [rows][nsplit][16] pairs per list (may exceed subcap: overflow)
-    int32_t nsample;          // sampled blocks per row
-    float *sample;            // [rows][nsample] sampled scores (-1: not visible)
+    int32_t nsample;          // sampled blocks per row (one per 32)
+    int32_t ssplit;           // sample-range splits
+    uint32_t *cand;           // [rows][ssplit][16][4] best sampled keys of each lane (0: none)
     uint32_t *tau;            // [rows] threshold key (0: no threshold)
 };
 int32_t fused_score_splits(int32_t rows, int32_t max_nb);
 int32_t fused_score_split_len(int32_t max_nb, int32_t nsplit);
 int32_t fused_score_subcap(int32_t top_k, int32_t nsplit);
 int32_t fused_score_nsample(int32_t max_nb);
+int32_t fused_score_ssplit(int32_t rows, int32_t nsample);
 void launch_score_fused(const FusedScoreArgs &a, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
                         hipStream_t stream);
 

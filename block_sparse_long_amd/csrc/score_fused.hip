@@ -11,17 +11,20 @@
 // traffic, more than the GEMM's own time at MFMA rate.  Instead:
 //   1. sample: every row is scored against one block in 32 (a fixed
 //      pseudo-random pick inside each group of 32), about 3% of the GEMM;
-//   2. threshold: tau = the row's j-th best sampled score, j = ceil(3k/32)
-//      (so about 3k of the row's blocks are expected to score >= tau);
+//      each lane keeps its 4 best sampled scores per row;
+//   2. threshold: tau = the j-th best of those candidates, j = ceil(3k/32),
+//      which is at most the row's j-th best sampled score (so about 3k of the
+//      row's blocks are expected to score >= tau);
 //   3. filter: the full GEMM writes out only the (key, block) pairs with
 //      score >= tau, each lane into its own list (no atomics, no cross-lane
 //      work in the MFMA loop);
 //   4. merge: a row is exact when at least min(k, nc) of its pairs reached
 //      tau -- then the k-th best of all visible blocks is >= tau and every
-//      block it keeps is among the pairs -- and the merge picks the top k
-//      among them with a radix select on the unique composite (key, ~block),
-//      then sorts them by block.  A row whose count fell short, or whose list
-//      overflowed, is redone from recomputed scores of every visible block.
+//      block it keeps is among the pairs -- and the merge finds the k-th
+//      best key T among them (radix select), sorts the pairs >= T by block,
+//      and keeps those above T and the lowest-block ones equal to it.  A row
+//      whose count fell short, or whose list overflowed, is redone from
+//      recomputed scores of every visible block.
 // Workgroup of the GEMMs: 4 waves x 16 query rows; MFMA row m of tile mt is
 // query row 4*mt + m/4, index head m%4, so a lane's 4 accumulators are the 4
 // heads of one (row, block) pair and the ReLU-sum stays in the lane.  The
@@ -123,8 +126,10 @@ __device__ __forceinline__ int32_t next_seq_group(const FusedScoreArgs &a, int64
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// 1. sample: grid = row tiles.  sample[row][i] = raw(row, sample_block(i)), or
-//    -1 when that block is not visible to the row.
+// 1. sample: grid (row tiles, sample-range splits).  Lane (mt, g, m) keeps the
+//    4 best scores of row 16*wave + 4*mt + g among the samples it computes
+//    (samples i with i % 16 == m of each 64-sample step) and writes their
+//    keys to cand[row][split][m][0..3] (0: fewer than 4).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 2) void score_sample_kernel(FusedScoreArgs a)
 {
@@ -135,54 +140,86 @@ __global__ __launch_bounds__(256, 2) void score_sample_kernel(FusedScoreArgs a)
     const int m = lane & 15, g = lane >> 4;
     const int64_t row0 = (int64_t)blockIdx.x * kFRows;
     const int nrows = (int)min((int64_t)kFRows, (int64_t)a.rows - row0);
+    const int split = blockIdx.y;
+    const int64_t slen = ((int64_t)a.nsample + a.ssplit - 1) / a.ssplit;
+    const int64_t s_lo = split * slen, s_hi = min((int64_t)a.nsample, s_lo + slen);
     bf16x8_t qa[4][4];
     load_query_tile(qrot, row0, nrows, wave, qa);
     int64_t my_nc[4];
     int32_t my_seq[4];
+    float top[4][4];  // per row: the lane's 4 best sampled scores, descending (-1: none)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const int rw = 16 * wave + 4 * mt + g;
         my_nc[mt] = rw < nrows ? min(visible_blocks(a.row_pos[row0 + rw]), (int64_t)a.max_nb) : 0;
         my_seq[mt] = rw < nrows ? a.row_seq[row0 + rw] : -1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) top[mt][q] = -1.0f;
     }
-    // every row's sample list starts as "not visible"
-    for (int i = t; i < nrows * a.nsample; i += 256) a.sample[row0 * a.nsample + i] = -1.0f;
-    __syncthreads();
     uint64_t todo = nrows >= 64 ? ~0ull : ((1ull << nrows) - 1ull);
     while (todo) {
         int64_t nb_hi;
         const int32_t seq = next_seq_group(a, row0, nrows, todo, nb_hi);
         const bf16_t *kb = pooled + (int64_t)seq * a.pooled_stride;
-        const int64_t ns = (nb_hi + kSampleStride - 1) / kSampleStride;  // samples that can be visible
+        const int64_t hi = min(s_hi, (nb_hi + kSampleStride - 1) / kSampleStride);  // samples that can be visible
         const int lrow = t >> 2, ldim = (t & 3) * 32;
-        for (int64_t i0 = 0; i0 < ns; i0 += kFStep) {
-            {   // gather the step's sampled keys
-                const int64_t b = min(sample_block(min(i0 + lrow, ns - 1)), nb_hi - 1);
-                const uint4 *src = (const uint4 *)(kb + b * kDim + ldim);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) *(uint4 *)&keys[lrow][ldim + 8 * i] = src[i];
+        uint4 p0, p1, p2, p3;
+        auto fetch = [&](int64_t i0) {
+            const int64_t b = min(sample_block(min(i0 + lrow, hi - 1)), nb_hi - 1);
+            const uint4 *src = (const uint4 *)(kb + b * kDim + ldim);
+            p0 = src[0];
+            p1 = src[1];
+            p2 = src[2];
+            p3 = src[3];
+        };
+        if (s_lo < hi) fetch(s_lo);
+        for (int64_t i0 = s_lo; i0 < hi; i0 += kFStep) {
+            {
+                uint4 *dst = (uint4 *)&keys[lrow][ldim];
+                dst[0] = p0;
+                dst[1] = p1;
+                dst[2] = p2;
+                dst[3] = p3;
             }
             __syncthreads();
+            if (i0 + kFStep < hi) fetch(i0 + kFStep);
             float sc[4][4];
             tile_scores(keys, qa, sc);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const int rw = 16 * wave + 4 * mt + g;
                 if (my_seq[mt] != seq) continue;
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
                     const int64_t i = i0 + nt * 16 + m;
-                    if (i < ns && sample_block(i) < my_nc[mt]) a.sample[(row0 + rw) * a.nsample + i] = sc[mt][nt];
+                    float v = (i < hi && sample_block(i) < my_nc[mt]) ? sc[mt][nt] : -1.0f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {  // insert into the descending top-4
+                        const float hi_v = fmaxf(top[mt][q], v);
+                        v = fminf(top[mt][q], v);
+                        top[mt][q] = hi_v;
+                    }
                 }
             }
             __syncthreads();
         }
     }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int rw = 16 * wave + 4 * mt + g;
+        if (rw >= nrows) continue;
+        uint4 k;
+        k.x = top[mt][0] >= 0.0f ? pos_key(top[mt][0]) : 0u;
+        k.y = top[mt][1] >= 0.0f ? pos_key(top[mt][1]) : 0u;
+        k.z = top[mt][2] >= 0.0f ? pos_key(top[mt][2]) : 0u;
+        k.w = top[mt][3] >= 0.0f ? pos_key(top[mt][3]) : 0u;
+        *(uint4 *)(a.cand + (((row0 + rw) * a.ssplit + split) * 16 + m) * 4) = k;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// 2. threshold: one wave per row.  tau[row] = key of the j-th best sampled
-//    score, or 0 (no threshold) when fewer than j samples are visible.
+// 2. threshold: one wave per row.  tau[row] = the j-th best key among the
+//    row's candidates (at most the j-th best sampled score), or 0 (no
+//    threshold) when fewer than j candidates exist.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedScoreArgs a)
 {
@@ -190,16 +227,23 @@ __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedScoreArgs a)
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t r = (int64_t)blockIdx.x * 4 + w;
     if (r >= a.rows) return;
-    const float *srow = a.sample + r * a.nsample;
-    uint32_t *h = hb[w];
-    const uint32_t j = (uint32_t)sample_j(a.top_k);
+    constexpr int kMaxPer = 8;  // ssplit <= 8: at most 8 candidates per lane
+    const int n = a.ssplit * 64;
+    const uint32_t *crow = a.cand + r * n;
+    uint32_t v[kMaxPer];
     uint32_t valid = 0;
-    for (int32_t i = lane; i < a.nsample; i += kWave) valid += srow[i] >= 0.0f ? 1u : 0u;
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) {
+        v[q] = q * 64 + lane < n ? crow[q * 64 + lane] : 0u;
+        valid += v[q] != 0u ? 1u : 0u;
+    }
     for (int o = 32; o > 0; o >>= 1) valid += __shfl_xor(valid, o);
+    const uint32_t j = (uint32_t)sample_j(a.top_k);
     if (valid < j) {
         if (lane == 0) a.tau[r] = 0u;
         return;
     }
+    uint32_t *h = hb[w];
     uint32_t need = j, prefix = 0;
     int sh = 32;
     for (int pass = 0; pass < 4; ++pass) {
@@ -207,11 +251,9 @@ __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedScoreArgs a)
 #pragma unroll
         for (int q = 0; q < 4; ++q) h[4 * lane + q] = 0u;
         wave_fence();
-        for (int32_t i = lane; i < a.nsample; i += kWave) {
-            const float v = srow[i];
-            const uint32_t key = pos_key(v);
-            if (v >= 0.0f && (sh == 32 || (key >> sh) == prefix)) atomicAdd(&h[(key >> nsh) & 0xffu], 1u);
-        }
+#pragma unroll
+        for (int q = 0; q < kMaxPer; ++q)
+            if (v[q] != 0u && (sh == 32 || (v[q] >> sh) == prefix)) atomicAdd(&h[(v[q] >> nsh) & 0xffu], 1u);
         wave_fence();
         uint32_t hv[4], sum = 0;
 #pragma unroll
@@ -242,6 +284,7 @@ __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedScoreArgs a)
         need -= above;
         prefix = (sh == 32 ? 0u : (prefix << 8)) | digit;
         sh = nsh;
+        wave_fence();
     }
     if (lane == 0) a.tau[r] = prefix;  // all 32 bits resolved: the j-th best key
 }
@@ -372,7 +415,6 @@ __device__ __forceinline__ float recompute_score(const bf16_t *__restrict__ q4, 
 }
 
 __device__ __forceinline__ float scaled(float raw) { return (float)((double)raw / sqrt((double)kDim)); }
-__device__ __forceinline__ uint64_t composite(uint2 e) { return ((uint64_t)e.x << 32) | (uint64_t)(~e.y); }
 
 }  // namespace
 
@@ -470,17 +512,23 @@ __global__ __launch_bounds__(256) void select_merge_kernel(FusedScoreArgs a, int
             }
         }
     };
-    // ---- radix select of the kk-th largest composite, 8 bits at a time ----
-    uint32_t need = (uint32_t)kk;
-    uint64_t prefix = 0, pmask = 0;
-    if ((uint32_t)kk < n) {
-        for (int sh = 56; sh >= 0; sh -= 8) {
+    // ---- radix select of the kk-th largest key T, 8 bits at a time: keys
+    // whose top bits beat `prefix` are kept, and of those equal to it the
+    // `need` lowest blocks ----
+    uint32_t need = (uint32_t)kk, prefix = 0;
+    int sh = 32;  // key >> sh is compared with prefix (32: every key is kept)
+    auto select_t = [&]() {
+        need = (uint32_t)kk;
+        prefix = 0;
+        sh = 32;
+        if ((uint32_t)kk >= n) return;
+        for (int pass = 0; pass < 4; ++pass) {
+            const int nsh = sh - 8;
 #pragma unroll
             for (int q = 0; q < 4; ++q) h[4 * lane + q] = 0u;
             wave_fence();
             visit([&](uint2 e, bool v) {
-                const uint64_t c = composite(e);
-                if (v && (c & pmask) == prefix) atomicAdd(&h[(uint32_t)(c >> sh) & 0xffu], 1u);
+                if (v && (sh == 32 || (e.x >> sh) == prefix)) atomicAdd(&h[(e.x >> nsh) & 0xffu], 1u);
             });
             wave_fence();
             uint32_t hv[4], sum = 0;
@@ -512,42 +560,57 @@ __global__ __launch_bounds__(256) void select_merge_kernel(FusedScoreArgs a, int
             above = __shfl(above, ls);
             cntd = __shfl(cntd, ls);
             need -= above;
-            prefix |= (uint64_t)digit << sh;
-            pmask |= 0xffull << sh;
-            if (cntd == need) break;  // the whole digit bin is kept
+            prefix = (sh == 32 ? 0u : (prefix << 8)) | digit;
+            sh = nsh;
+            wave_fence();
+            if (cntd == need) break;  // the whole bin is kept
+        }
+    };
+    select_t();
+    auto above_t = [&](uint32_t key) { return sh == 32 || (key >> sh) > prefix; };
+    auto at_t = [&](uint32_t key) { return sh != 32 && (key >> sh) == prefix; };
+    // ---- gather the keys >= T as (block << 32 | key), sort them by block ----
+    uint32_t g = 0;
+    if (mode != 2) {
+        visit([&](uint2 e, bool v) { g += (uint32_t)__popcll(__ballot(v && (above_t(e.x) || at_t(e.x)))); });
+        if (g > (uint32_t)kStage) {  // too many exact ties to sort: rank recomputed scores instead
+            mode = 2;
+            n = (uint32_t)nc;
+            select_t();
         }
     }
-    // ---- emit the kk kept pairs (composite >= prefix) in block order ----
-    if (mode == 2) {  // recomputed pairs come in block order
-        uint32_t out_before = 0;
+    if (mode == 2) {  // recomputed pairs come in block order: emit directly
+        uint32_t eq_before = 0, out_before = 0;
         visit([&](uint2 e, bool v) {
-            const bool take = v && (composite(e) & pmask) >= prefix;
+            const bool gt = v && above_t(e.x), eq = v && at_t(e.x);
+            const uint64_t eb = __ballot(eq);
+            const bool take = gt || (eq && eq_before + (uint32_t)__popcll(eb & lt) < need);
             const uint64_t tb = __ballot(take);
             const uint32_t pos = out_before + (uint32_t)__popcll(tb & lt);
             if (take && pos < (uint32_t)kk) {
                 out[pos] = (int32_t)e.y;
                 if (osc) osc[pos] = scaled(key_score(e.x));
             }
+            eq_before += (uint32_t)__popcll(eb);
             out_before += (uint32_t)__popcll(tb);
         });
         return;
     }
-    // gather the kept pairs into stage[0..kk) as (block << 32 | key); in place
-    // for staged pairs: each write lands at or below the slot it was read from
+    // in place for staged pairs: each write lands at or below its read
     uint32_t filled = 0;
     visit([&](uint2 e, bool v) {
-        const bool take = v && (composite(e) & pmask) >= prefix;
+        const bool take = v && (above_t(e.x) || at_t(e.x));
         const uint64_t tb = __ballot(take);
         const uint32_t pos = filled + (uint32_t)__popcll(tb & lt);
         wave_fence();
-        if (take && pos < (uint32_t)kk) *(uint64_t *)&st[pos] = ((uint64_t)e.y << 32) | e.x;
+        if (take) *(uint64_t *)&st[pos] = ((uint64_t)e.y << 32) | e.x;
         wave_fence();
         filled += (uint32_t)__popcll(tb);
     });
     uint64_t *kept = (uint64_t *)st;
     uint32_t n2 = 1;
-    while (n2 < (uint32_t)kk) n2 <<= 1;
-    for (uint32_t i = (uint32_t)kk + lane; i < n2; i += kWave) kept[i] = ~0ull;
+    while (n2 < g) n2 <<= 1;
+    for (uint32_t i = g + lane; i < n2; i += kWave) kept[i] = ~0ull;
     wave_fence();
     for (uint32_t size = 2; size <= n2; size <<= 1) {  // bitonic sort by block id
         for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
@@ -564,10 +627,24 @@ __global__ __launch_bounds__(256) void select_merge_kernel(FusedScoreArgs a, int
             wave_fence();
         }
     }
-    for (int32_t i = lane; i < kk; i += kWave) {
-        const uint64_t e = kept[i];
-        out[i] = (int32_t)(e >> 32);
-        if (osc) osc[i] = scaled(key_score((uint32_t)e));
+    // emit in block order: keys above T, and the first `need` equal to T
+    uint32_t eq_before = 0, out_before = 0;
+    for (uint32_t i0 = 0; i0 < g; i0 += kWave) {
+        const uint32_t i = i0 + lane;
+        const bool v = i < g;
+        const uint64_t e = v ? kept[i] : 0ull;
+        const uint32_t key = (uint32_t)e;
+        const bool gt = v && above_t(key), eq = v && at_t(key);
+        const uint64_t eb = __ballot(eq);
+        const bool take = gt || (eq && eq_before + (uint32_t)__popcll(eb & lt) < need);
+        const uint64_t tb = __ballot(take);
+        const uint32_t pos = out_before + (uint32_t)__popcll(tb & lt);
+        if (take && pos < (uint32_t)kk) {
+            out[pos] = (int32_t)(e >> 32);
+            if (osc) osc[pos] = scaled(key_score(key));
+        }
+        eq_before += (uint32_t)__popcll(eb);
+        out_before += (uint32_t)__popcll(tb);
     }
 }
 
@@ -599,12 +676,23 @@ int32_t fused_score_subcap(int32_t top_k, int32_t nsplit)
 
 int32_t fused_score_nsample(int32_t max_nb) { return (max_nb + kSampleStride - 1) / kSampleStride; }
 
+// Sample-range splits: enough sampling workgroups to fill the chip, at most 8
+// (the threshold kernel holds 8 candidates per lane), at least 64 samples each.
+int32_t fused_score_ssplit(int32_t rows, int32_t nsample)
+{
+    const int64_t tiles = ((int64_t)rows + kFRows - 1) / kFRows;
+    int64_t s = (512 + tiles - 1) / tiles;
+    s = min(s, (int64_t)8);
+    s = min(s, ((int64_t)nsample + kFStep - 1) / kFStep);
+    return (int32_t)max((int64_t)1, s);
+}
+
 void launch_score_fused(const FusedScoreArgs &a, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
                         hipStream_t stream)
 {
     if (a.max_nb > 0) {
         const unsigned tiles = (unsigned)((a.rows + kFRows - 1) / kFRows);
-        QSA_LAUNCH("score_sample", score_sample_kernel, dim3(tiles), dim3(256), 0, stream, a);
+        QSA_LAUNCH("score_sample", score_sample_kernel, dim3(tiles, (unsigned)a.ssplit), dim3(256), 0, stream, a);
         QSA_LAUNCH("sample_threshold", sample_threshold_kernel, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0,
                    stream, a);
         QSA_LAUNCH("score_filter", score_filter_kernel, dim3(tiles, (unsigned)a.nsplit), dim3(256), 0, stream, a);
