@@ -2,6 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--decode-workload NAME|none] [--no-cpu-baseline]
+                    [--copy-calibration]
+    python bench.py --rocprof-summary DIR [DIR ...]
+    python bench.py --traffic-summary FETCH_DIR WRITE_DIR --workload NAME
 
 Prints ONE JSON line.  The headline is prefill: one step is a whole pass of
 the prefill path (pool the chunk's new blocks -> rotate index queries, score,
@@ -18,10 +21,20 @@ per launch / its average duration, from hipEvents the library records around
 each launch on the launch stream) against MI355X's datasheet peak.
 "cpu_baseline" is the CPU oracle, untuned, timed on a bounded sample of the
 same workload on this host.
+
+"traffic" is the kernel's measured memory traffic per launch (bytes L2 fetched
+plus wrote, from rocprofv3's FETCH_SIZE and WRITE_SIZE counters scaled by what
+the same counters read for a copy of known size), taken from
+profiles/hbm_traffic_<workload>.txt, and null when the kernel's source has
+changed since those counters were taken.  The two summary modes reduce
+rocprofv3 CSV output (``--output-format csv -o run``) to those text files.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -106,7 +119,7 @@ def decode_work(spec, anchor_pos, attn_pos, tail_start):
     }, pairs
 
 
-def roofline_for(name, work, avg_ms):
+def roofline_for(name, work, avg_ms, traffic=None):
     bound, amount, unit = work
     if unit == "flop":
         achieved = amount / (avg_ms * 1e-3) / 1e12
@@ -118,7 +131,7 @@ def roofline_for(name, work, avg_ms):
         u = "GB/s"
     return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": u,
             "frac": round(achieved / peak, 4), "per_launch": amount, "avg_us": round(avg_ms * 1e3, 2),
-            "traffic": None}
+            "traffic": (traffic or {}).get(name)}
 
 
 def kernel_times(run_step, nsteps, names):
@@ -198,9 +211,10 @@ def bench_prefill(spec, steps, warmup, cpu_baseline):
     kernels = {n: {"launches_per_step": c / max(3, min(steps, 10)), "avg_us": round(a * 1e3, 2)}
                for n, (c, a, _) in kt.items()}
     dom = max((n for n in kt if n in work), key=lambda n: kt[n][2])
+    tr = load_traffic(spec.name)
     res = {"ms_per_step": ms, "value": R / (ms * 1e-3), "kernels": kernels,
-           "roofline": roofline_for(dom, work[dom], kt[dom][1]),
-           "rooflines": {n: roofline_for(n, work[n], kt[n][1]) for n in kt if n in work},
+           "roofline": roofline_for(dom, work[dom], kt[dom][1], tr),
+           "rooflines": {n: roofline_for(n, work[n], kt[n][1], tr) for n in kt if n in work},
            "pairs": pairs, "positions": npos}
     if cpu_baseline:
         res["cpu_baseline"] = cpu_prefill(spec, w)
@@ -290,9 +304,10 @@ def bench_decode(spec, steps, warmup, cpu_baseline, copies=3):
     kernels = {n: {"launches_per_step": c / nprof, "avg_us": round(a * 1e3, 2)} for n, (c, a, _) in kt.items()}
     dom = max((n for n in kt if n in work), key=lambda n: kt[n][2])
     rows = spec.batch * spec.q_per_seq
+    tr = load_traffic(spec.name)
     res = {"workload": spec.name, "value": rows / (ms * 1e-3), "unit": "query rows/s", "ms_per_step": ms,
-           "kernels": kernels, "roofline": roofline_for(dom, work[dom], kt[dom][1]),
-           "rooflines": {n: roofline_for(n, work[n], kt[n][1]) for n in kt if n in work}}
+           "kernels": kernels, "roofline": roofline_for(dom, work[dom], kt[dom][1], tr),
+           "rooflines": {n: roofline_for(n, work[n], kt[n][1], tr) for n in kt if n in work}}
     if cpu_baseline:
         res["cpu_baseline"] = cpu_decode(spec, w, pooled_h)
     return res
@@ -315,6 +330,143 @@ def cpu_decode(spec, w, pooled_h):
                       f"({t:.1f}s)"}
 
 
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries and measured traffic
+# ---------------------------------------------------------------------------
+
+CSRC = os.path.join(ROOT, "block_sparse_long_amd", "csrc")
+HEADERS = ["qsa_internal.h", "qsa_device.h", "qsa_wg.h"]
+KERNEL_SOURCE = {"pool_rope": "pool.hip", "rope_query": "pool.hip", "score_rows_bf16": "score.hip",
+                 "score_rows_f32": "score.hip", "score_gemm_bf16": "score.hip", "select_rows": "select.hip",
+                 "select_collect": "select.hip", "score_sample": "score_fused.hip",
+                 "sample_threshold": "score_fused.hip", "score_filter": "score_fused.hip",
+                 "select_merge": "score_fused.hip", "attn_prefill_mfma": "attn_mfma.hip",
+                 "attn_decode_mfma": "attn_mfma.hip", "attn_prefill": "attn.hip", "attn_decode": "attn.hip",
+                 "attn_combine": "attn.hip"}
+COPY_BYTES = 1 << 30
+
+
+def source_digest(kernel):
+    """Digest of the source a kernel is built from (its file and the shared headers)."""
+    h = hashlib.sha256()
+    for f in [KERNEL_SOURCE[kernel]] + HEADERS:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_kernel_name(full):
+    """libqsa's launch name of a kernel from its demangled rocprofv3 name, else None."""
+    base = full.split("(")[0].replace("void ", "").strip()
+    if not base.startswith("qsa::"):
+        return "copy" if "neg_kernel" in full else None
+    base = base[5:]
+    tmpl = base[base.find("<"):] if "<" in base else ""
+    base = base.split("<")[0]
+    if base == "attn_kernel":
+        return "attn_decode" if tmpl.rstrip(">").strip().endswith("true") else "attn_prefill"
+    if base.startswith("attn_combine"):
+        return "attn_combine"
+    return base[:-7] if base.endswith("_kernel") else base
+
+
+def copy_calibration():
+    """A copy of known size for scaling memory counters: one elementwise pass
+    (negation) that reads COPY_BYTES and writes COPY_BYTES, three times."""
+    import torch
+    src = torch.ones((COPY_BYTES // 2,), dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _csvs(d, suffix):
+    return sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+
+
+def kernel_trace_stats(d):
+    """{kernel: (launches, avg_us, min_us, max_us)} from a --kernel-trace run."""
+    per = {}
+    for f in _csvs(d, "kernel_trace.csv"):
+        for r in csv.DictReader(open(f)):
+            n = short_kernel_name(r["Kernel_Name"])
+            if n is None:
+                continue
+            per.setdefault(n, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return {n: (len(v), sum(v) / len(v), min(v), max(v)) for n, v in per.items()}
+
+
+def counter_means(d):
+    """{kernel: {counter: mean value per dispatch}} from a --pmc run."""
+    acc = {}
+    for f in _csvs(d, "counter_collection.csv"):
+        for r in csv.DictReader(open(f)):
+            n = short_kernel_name(r["Kernel_Name"])
+            if n is None:
+                continue
+            key = (n, r["Counter_Name"])
+            acc.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+            acc[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    out = {}
+    for (n, c), per in acc.items():
+        out.setdefault(n, {})[c] = sum(per.values()) / len(per)
+    return out
+
+
+def rocprof_summary(dirs):
+    for d in dirs:
+        print(f"# rocprofv3 output: {d}")
+        st = kernel_trace_stats(d)
+        if st:
+            print(f"{'kernel':<20} {'launches':>9} {'avg_us':>10} {'min_us':>10} {'max_us':>10}")
+            for n, (c, a, lo, hi) in sorted(st.items(), key=lambda x: -x[1][0] * x[1][1]):
+                print(f"{n:<20} {c:>9} {a:>10.2f} {lo:>10.2f} {hi:>10.2f}")
+        for f in _csvs(d, "kernel_stats.csv"):  # rocprofv3's own --stats table
+            print(f"# {os.path.basename(f)}: kernel, calls, average ns, min ns, max ns")
+            for r in csv.DictReader(open(f)):
+                n = short_kernel_name(r["Name"]) or r["Name"][:40]
+                print(f"  {n:<20} {r['Calls']:>6} {float(r['AverageNs']):>12.0f} {r['MinNs']:>10} {r['MaxNs']:>10}")
+        cm = counter_means(d)
+        for n in sorted(cm):
+            print(f"{n:<20} " + "  ".join(f"{c}={v:.6g}" for c, v in sorted(cm[n].items())))
+
+
+def traffic_summary(fetch_dir, write_dir, workload):
+    """Measured bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+    scaled so that the calibration copy reads and writes COPY_BYTES."""
+    fm, wm = counter_means(fetch_dir), counter_means(write_dir)
+    fcopy, wcopy = fm["copy"]["FETCH_SIZE"], wm["copy"]["WRITE_SIZE"]
+    ff, fw = COPY_BYTES / (fcopy * 1024.0), COPY_BYTES / (wcopy * 1024.0)
+    print(f"# workload {workload}: memory traffic per launch (bytes), from rocprofv3 --pmc FETCH_SIZE "
+          f"({fetch_dir}) and --pmc WRITE_SIZE ({write_dir})")
+    print(f"# calibration copy of {COPY_BYTES} B: FETCH_SIZE {fcopy:.1f} KiB -> factor {ff:.4f}; "
+          f"WRITE_SIZE {wcopy:.1f} KiB -> factor {fw:.4f}")
+    print("# kernel  source_digest  fetch_bytes  write_bytes  traffic_bytes")
+    for n in sorted(set(fm) & set(wm)):
+        if n == "copy" or n not in KERNEL_SOURCE:
+            continue
+        fb = fm[n]["FETCH_SIZE"] * 1024.0 * ff
+        wb = wm[n]["WRITE_SIZE"] * 1024.0 * fw
+        print(f"kernel {n} {source_digest(n)} {fb:.0f} {wb:.0f} {fb + wb:.0f}")
+
+
+def load_traffic(workload):
+    """{kernel: bytes per launch} from profiles/hbm_traffic_<workload>.txt, for
+    kernels whose source still matches the digest recorded with the counters."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    out = {}
+    if not os.path.exists(path):
+        return out
+    for line in open(path):
+        p = line.split()
+        if len(p) == 6 and p[0] == "kernel" and p[1] in KERNEL_SOURCE and p[2] == source_digest(p[1]):
+            out[p[1]] = float(p[5])
+    return out
+
+
 # ---------------------------------------------------------------------------
 
 def main():
@@ -325,15 +477,27 @@ def main():
     ap.add_argument("--workload", default="chunk-256k")
     ap.add_argument("--decode-workload", default="decode-1m-draft")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a copy of known size first (for scaling memory counters)")
+    ap.add_argument("--rocprof-summary", nargs="+", metavar="DIR")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary)
+        return
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, args.workload)
+        return
     if args.gpus != 1:
-        print(f"bench.py: this build runs the QSA hot path on one GPU only (asked for {args.gpus}); "
-              "sharding across GPUs is a design note, not implemented", file=sys.stderr)
+        print(f"bench.py: libqsa runs the QSA hot path on one GPU only (asked for {args.gpus}); "
+              "sharding across GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
     import torch
     from block_sparse_long_amd import qsa, synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     qsa.load()
+    if args.copy_calibration:
+        copy_calibration()
     cpu = not args.no_cpu_baseline
     spec = synth.SPECS[args.workload]
     if spec.kind == "prefill":

@@ -33,7 +33,8 @@ def hipcc() -> str:
 
 def _flags() -> list:
     return ["-x", "hip", "-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",
-            # packed fp32 VALU ops stay off (see the build notes in the design doc)
+            # packed fp32 VALU instructions stay off: ordinary float code is
+            # compiled to plain VALU ops only
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
 

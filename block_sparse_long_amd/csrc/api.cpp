@@ -17,13 +17,20 @@ namespace qsa {
 // launch bookkeeping
 // ---------------------------------------------------------------------------
 static thread_local hipError_t g_launch_err = hipSuccess;
+static thread_local hipError_t g_last_failure = hipSuccess;  // kept until the next failure
 
 void note_launch(hipError_t err)
 {
-    if (err != hipSuccess && g_launch_err == hipSuccess) g_launch_err = err;
+    if (err != hipSuccess && g_launch_err == hipSuccess) g_launch_err = g_last_failure = err;
 }
 
-static void clear_launch_err() { g_launch_err = hipSuccess; }
+// Drops an error another caller left pending in this thread (hipGetLastError
+// reports the last error of any HIP call), so a launch reports only its own.
+static void clear_launch_err()
+{
+    (void)hipGetLastError();
+    g_launch_err = hipSuccess;
+}
 static qsa_status_t launch_status() { return g_launch_err == hipSuccess ? QSA_OK : QSA_ERR_DEVICE; }
 
 struct ProfRecord {
@@ -164,6 +171,11 @@ const char *qsa_status_string(qsa_status_t s)
     case QSA_ERR_DEVICE: return "HIP launch or runtime error";
     }
     return "unknown status";
+}
+
+const char *qsa_last_device_error(void)
+{
+    return g_last_failure == hipSuccess ? "none" : hipGetErrorString(g_last_failure);
 }
 
 qsa_status_t qsa_pool_index_keys(const void *raw_keys, int64_t raw_seq_stride, void *pooled,

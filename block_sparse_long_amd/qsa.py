@@ -27,7 +27,7 @@ INDEX_DIM, INDEX_HEADS, BLOCK_TOKENS, MAX_TOP_K, MAX_QUERY_GROUP = 128, 4, 4, 40
 # every symbol include/qsa.h declares
 EXPORTS = ("qsa_pool_index_keys", "qsa_score_topk_workspace_size", "qsa_score_topk",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode_workspace_size",
-           "qsa_sparse_attn_decode", "qsa_status_string", "qsa_profile_enable",
+           "qsa_sparse_attn_decode", "qsa_status_string", "qsa_last_device_error", "qsa_profile_enable",
            "qsa_profile_reset", "qsa_profile_kernel_ms")
 
 
@@ -51,6 +51,12 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise QsaLibraryMissing(f"{LIB_PATH} is not built; run `python -m block_sparse_long_amd.build`")
+    # torch ships its own HIP runtime under the same soname as ROCm's.  Loaded
+    # first, it is the one libqsa binds to, so the process has one runtime and
+    # torch's device memory and stream handles are valid in libqsa's calls.
+    # Opened in the other order, two runtimes coexist and the second finds
+    # no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P, i32, i64, u32, f32, f64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
                                       ctypes.c_float, ctypes.c_double, ctypes.c_size_t)
@@ -71,6 +77,8 @@ def load():
     lib.qsa_sparse_attn_decode.restype = st
     lib.qsa_status_string.argtypes = [st]
     lib.qsa_status_string.restype = ctypes.c_char_p
+    lib.qsa_last_device_error.argtypes = []
+    lib.qsa_last_device_error.restype = ctypes.c_char_p
     lib.qsa_profile_enable.argtypes = [ctypes.c_int]
     lib.qsa_profile_enable.restype = st
     lib.qsa_profile_reset.argtypes = []
@@ -87,7 +95,10 @@ def status_string(code: int) -> str:
 
 def _check(fn: str, rc: int):
     if rc != OK:
-        raise QsaError(fn, rc, status_string(rc))
+        msg = status_string(rc)
+        if rc == ERR_DEVICE:
+            msg += ": " + load().qsa_last_device_error().decode()
+        raise QsaError(fn, rc, msg)
 
 
 def _ptr(t) -> Optional[int]:

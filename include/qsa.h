@@ -191,6 +191,13 @@ qsa_status_t qsa_sparse_attn_decode(const void *q, const int32_t *row_pos, int32
 const char *qsa_status_string(qsa_status_t status);
 
 /*
+ * HIP's description of the error behind the last QSA_ERR_DEVICE returned on
+ * the calling thread ("none" if there was none).  Static string; the record
+ * is per thread and kept until the next failure.
+ */
+const char *qsa_last_device_error(void);
+
+/*
  * Kernel timing, for benchmarks.  While enabled, every kernel the library
  * launches is bracketed by a pair of hipEvents recorded on its stream.
  * qsa_profile_kernel_ms() waits for the recorded events, then returns how many
