@@ -114,6 +114,7 @@ def decode_work(spec, anchor_pos, attn_pos, tail_start):
         kind: ("hbm", float(pairs) * DIM * eb, "B"),
         "select_rows": ("hbm", 4.0 * pairs, "B"),
         "select_collect": ("hbm", 4.0 * pairs, "B"),
+        "select_final": ("hbm", 8.0 * spec.batch * spec.top_k, "B"),
         "attn_decode": ("hbm", kv_bytes + q_bytes, "B"),
         "attn_decode_mfma": ("hbm", kv_bytes + q_bytes, "B"),
     }, pairs
@@ -167,7 +168,7 @@ def timed(run_step, steps, warmup):
 
 
 ALL_KERNELS = ["pool_rope", "rope_query", "score_rows_bf16", "score_rows_f32", "score_gemm_bf16", "select_rows",
-               "select_collect", "score_sample", "sample_threshold", "score_filter", "select_merge", "attn_prefill_mfma", "attn_decode_mfma",
+               "select_collect", "select_final", "score_sample", "sample_threshold", "score_filter", "select_merge", "attn_prefill_mfma", "attn_decode_mfma",
                "attn_prefill", "attn_decode", "attn_combine"]
 
 
@@ -339,7 +340,7 @@ CSRC = os.path.join(ROOT, "block_sparse_long_amd", "csrc")
 HEADERS = ["qsa_internal.h", "qsa_device.h", "qsa_wg.h"]
 KERNEL_SOURCE = {"pool_rope": "pool.hip", "rope_query": "pool.hip", "score_rows_bf16": "score.hip",
                  "score_rows_f32": "score.hip", "score_gemm_bf16": "score.hip", "select_rows": "select.hip",
-                 "select_collect": "select.hip", "score_sample": "score_fused.hip",
+                 "select_collect": "select.hip", "select_final": "select.hip", "score_sample": "score_fused.hip",
                  "sample_threshold": "score_fused.hip", "score_filter": "score_fused.hip",
                  "select_merge": "score_fused.hip", "attn_prefill_mfma": "attn_mfma.hip",
                  "attn_decode_mfma": "attn_mfma.hip", "attn_prefill": "attn.hip", "attn_decode": "attn.hip",

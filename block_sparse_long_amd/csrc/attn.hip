@@ -214,26 +214,50 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
 }
 
 // Merge the decode splits of one (row, head): grid = rows*Hq, 128 threads.
+// Wave 0 reduces the splits' (m, l) with one split per lane; then every thread
+// owns one output dim and sums the splits' weighted partial outputs, several
+// loads in flight at once.
+constexpr int kMaxDecodeSplits = (kBlock * QSA_MAX_TOP_K + kAC - 1) / kAC + 1;
+
 template <typename T>
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float *__restrict__ partial, int32_t nsplit,
                                                            void *out, float *lse)
 {
+    __shared__ float wsplit[kMaxDecodeSplits];
+    __shared__ float s_m, s_l;
     const int64_t qrow = blockIdx.x;
     const int d = threadIdx.x;
     const float *pp = partial + qrow * nsplit * (kDim + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[s * (kDim + 2) + kDim]);
-    float L = 0.0f, acc = 0.0f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < nsplit; ++s) {
+    if (d < kWave) {
+        float m = -INFINITY;
+        for (int s = d; s < nsplit; s += kWave) m = fmaxf(m, pp[s * (kDim + 2) + kDim]);
+        m = wave_max(m);
+        float l = 0.0f;
+        for (int s = d; s < nsplit; s += kWave) {
             const float ms = pp[s * (kDim + 2) + kDim];
-            if (ms == -INFINITY) continue;
-            const float e = __expf(ms - M);
-            L += pp[s * (kDim + 2) + kDim + 1] * e;
-            acc += pp[s * (kDim + 2) + d] * e;
+            const float e = ms == -INFINITY ? 0.0f : __expf(ms - m);
+            wsplit[s] = e;
+            l += pp[s * (kDim + 2) + kDim + 1] * e;
+        }
+        l = wave_sum(l);
+        if (d == 0) {
+            s_m = m;
+            s_l = l;
         }
     }
-    store_f32((T *)out + qrow * kDim + d, L > 0.0f ? acc / L : 0.0f);
+    __syncthreads();
+    const float M = s_m, L = s_l;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (L > 0.0f) {
+        int s = 0;
+        for (; s + 4 <= nsplit; s += 4) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] += wsplit[s + j] * pp[(s + j) * (kDim + 2) + d];
+        }
+        for (; s < nsplit; ++s) acc[0] += wsplit[s] * pp[s * (kDim + 2) + d];
+    }
+    const float o = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    store_f32((T *)out + qrow * kDim + d, L > 0.0f ? o / L : 0.0f);
     if (lse && d == 0) lse[qrow] = L > 0.0f ? M + __logf(L) : -INFINITY;
 }
 

@@ -18,7 +18,7 @@
 
 namespace qsa {
 
-constexpr int kChunk = 1024;  // blocks per workgroup in the row-split kernels
+constexpr int kChunk = 2048;  // blocks per workgroup in the row-split kernels
 
 __device__ __forceinline__ float relu_sum4(f32x4_t a)
 {
@@ -42,7 +42,7 @@ __device__ __forceinline__ void hist_flush(const uint32_t *lhist, uint32_t *ghis
 }
 
 // ---------------------------------------------------------------------------
-// Few rows, many blocks (decode): grid (chunks of 1024 blocks, rows).  The 4
+// Few rows, many blocks (decode): grid (chunks of 2048 blocks, rows).  The 4
 // index heads sit in MFMA rows 0..3 (rows 4..15 are zero), 16 blocks per MFMA
 // column tile.  HBM-bound: each block's 256 bytes are read once per row.
 // ---------------------------------------------------------------------------
@@ -68,9 +68,9 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
                    : zero_bf16x8();
     const bf16_t *kb = pooled + (int64_t)row_seq[r] * pooled_stride;
     float *srow = scores + (int64_t)r * sc_stride;
-    // each wave handles 64 consecutive blocks per iteration (4 column tiles)
-    for (int64_t base = b_begin + wave * 64; base < b_end; base += 256) {
-        uint4 v[4][4];
+    // each wave handles 64 consecutive blocks per iteration (4 column tiles);
+    // the next iteration's keys are in flight during this one's MFMAs
+    auto load = [&](int64_t base, uint4 (&v)[4][4]) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const int64_t b = min(base + nt * 16 + m, b_end - 1);  // clamp: stays inside the visible range
@@ -78,6 +78,12 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
 #pragma unroll
             for (int s = 0; s < 4; ++s) v[nt][s] = src[s];
         }
+    };
+    uint4 v[4][4], vn[4][4];
+    int64_t base = b_begin + wave * 64;
+    if (base < b_end) load(base, v);
+    for (; base < b_end; base += 256) {
+        if (base + 256 < b_end) load(base + 256, vn);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -91,6 +97,10 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
                 if (hist) atomicAdd(&lhist[score_key(sc) >> kHistShift], 1u);
             }
         }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) v[nt][s] = vn[nt][s];
     }
     if (hist) hist_flush(lhist, hist + (int64_t)r * kRowScratch);
 }

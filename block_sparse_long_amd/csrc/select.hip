@@ -24,6 +24,8 @@ namespace qsa {
 constexpr int kSelThreads = 512;
 constexpr int kSplitThreads = 256;
 constexpr int kCollectChunk = 4096;  // blocks per collect workgroup
+constexpr int kCandStage = 3072;     // candidates the final pass keeps in LDS
+constexpr int kEmitWords = 8192;     // bitmap window of the final pass: 262,144 blocks
 
 // Reported score s = raw / sqrt(128) (the score equation's scale), divided in
 // double and rounded once to float.
@@ -118,7 +120,7 @@ void launch_select_rows(const float *scores, int64_t sc_stride, const int32_t *r
 //     bin b* holding the k-th best key, then appends the blocks of its chunk
 //     above b* to the row's "sure" list and those inside b* to its candidate
 //     list;
-//   - the workgroup that finishes a row's last chunk picks the missing
+//   - final (one workgroup per row, a second launch): picks the missing
 //     `need` entries among the candidates with a radix select on the unique
 //     composite (low 20 key bits, ~block) -- a higher score first, then the
 //     lower block -- and writes the kept set sorted by block id.
@@ -141,15 +143,45 @@ __device__ __forceinline__ uint64_t composite20(uint2 e)
     return ((uint64_t)(e.x & 0x000fffffu) << 32) | (uint64_t)(~e.y);
 }
 
+// find_bin over a row's 4096-bin histogram in global memory: thread t owns
+// bins [4080 - 16t, 4096 - 16t), read with four 16-byte loads issued together
+// and kept in registers for the search inside the owning thread.
+__device__ __forceinline__ void find_bin_global(const uint32_t *__restrict__ hist, uint32_t need, uint32_t *wtot,
+                                                uint32_t *out_bin, uint32_t *out_above)
+{
+    static_assert(kHistBins == 16 * kSplitThreads, "16 bins per thread");
+    const int lo = kHistBins - 16 * ((int)threadIdx.x + 1);
+    uint4 q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = ((const uint4 *)(hist + lo))[j];
+    const uint32_t c[16] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w,
+                            q[2].x, q[2].y, q[2].z, q[2].w, q[3].x, q[3].y, q[3].z, q[3].w};
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += c[i];
+    const uint32_t incl = wg_inclusive_scan<kSplitThreads>(sum, wtot);
+    const uint32_t before = incl - sum;
+    if (before < need && incl >= need) {
+        uint32_t acc = before;
+        for (int i = 15; i >= 0; --i) {
+            if (acc + c[i] >= need) {
+                *out_bin = (uint32_t)(lo + i);
+                *out_above = acc;
+                break;
+            }
+            acc += c[i];
+        }
+    }
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(kSplitThreads) void select_collect_kernel(
     const float *__restrict__ scores, int64_t sc_stride, const int32_t *__restrict__ row_pos, int32_t max_nb,
     int32_t top_k, SplitSelect ss, int32_t *__restrict__ sel_blocks, int32_t *__restrict__ sel_count,
     float *__restrict__ sel_scores)
 {
-    __shared__ uint64_t buf[QSA_MAX_TOP_K];
-    __shared__ uint32_t dhist[256];
     __shared__ uint32_t wtot[kSplitThreads / kWave];
-    __shared__ uint32_t s_bin, s_above, s_ticket, s_digit, s_dabove, s_dcnt, s_fill;
+    __shared__ uint32_t s_bin, s_above;
     const int t = threadIdx.x;
     const int64_t r = blockIdx.y;
     const int32_t nc = (int32_t)min(visible_blocks(row_pos[r]), (int64_t)max_nb);
@@ -173,29 +205,66 @@ __global__ __launch_bounds__(kSplitThreads) void select_collect_kernel(
     }
     if (b_begin >= nc) return;
     // ---- collect ----
-    find_bin<kSplitThreads>(hist, kHistBins, (uint32_t)kk, wtot, &s_bin, &s_above);
+    find_bin_global(hist, (uint32_t)kk, wtot, &s_bin, &s_above);
     const uint32_t beta = s_bin;
     const int64_t b_end = min((int64_t)nc, b_begin + kCollectChunk);
-    for (int64_t b0 = b_begin; b0 < b_end; b0 += kSplitThreads) {
-        const int64_t b = b0 + t;
-        const bool valid = b < b_end;
-        const uint32_t key = valid ? score_key(srow[b]) : 0u;
-        const uint32_t bin = key >> kHistShift;
-        const uint2 item = make_uint2(key, (uint32_t)b);
-        wave_append(valid && bin > beta, item, &cnt[0], sure);
-        wave_append(valid && bin == beta, item, &cnt[1], cand);
+    // the whole chunk in flight at once: thread t holds blocks b_begin +
+    // 1024*j + 4*t + i (rows are padded to 64 floats, so a 4-block group that
+    // starts inside the row ends inside it)
+    float4 v[kCollectChunk / (4 * kSplitThreads)];
+#pragma unroll
+    for (int j = 0; j < kCollectChunk / (4 * kSplitThreads); ++j) {
+        const int64_t b4 = b_begin + (int64_t)j * 4 * kSplitThreads + 4 * t;
+        v[j] = b4 < b_end ? *(const float4 *)(srow + b4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    // ---- the last workgroup of the row finishes it ----
-    __threadfence();
-    __syncthreads();
-    if (t == 0) s_ticket = atomicAdd(&cnt[2], 1u);
-    __syncthreads();
-    const uint32_t nchunks = (uint32_t)((nc + kCollectChunk - 1) / kCollectChunk);
-    if (s_ticket != nchunks - 1) return;
-    __threadfence();
-    const uint32_t n_sure = __atomic_load_n(&cnt[0], __ATOMIC_RELAXED);
-    const uint32_t n_cand = __atomic_load_n(&cnt[1], __ATOMIC_RELAXED);
+#pragma unroll
+    for (int j = 0; j < kCollectChunk / (4 * kSplitThreads); ++j) {
+        const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t b = b_begin + (int64_t)j * 4 * kSplitThreads + 4 * t + i;
+            const bool valid = b < b_end;
+            const uint32_t key = valid ? score_key(e[i]) : 0u;
+            const uint32_t bin = key >> kHistShift;
+            const uint2 item = make_uint2(key, (uint32_t)b);
+            wave_append(valid && bin > beta, item, &cnt[0], sure);
+            wave_append(valid && bin == beta, item, &cnt[1], cand);
+        }
+    }
+}
+
+// One workgroup per row: picks the missing `need` entries among the row's
+// candidates and writes the kept set sorted by block id.
+__global__ __launch_bounds__(kSplitThreads) void select_final_kernel(
+    const float *__restrict__ scores, int64_t sc_stride, const int32_t *__restrict__ row_pos, int32_t max_nb,
+    int32_t top_k, SplitSelect ss, int32_t *__restrict__ sel_blocks, int32_t *__restrict__ sel_count,
+    float *__restrict__ sel_scores)
+{
+    __shared__ uint64_t buf[QSA_MAX_TOP_K];
+    __shared__ uint2 cst[kCandStage];
+    __shared__ uint32_t bm[kEmitWords];
+    __shared__ uint32_t dhist[256];
+    __shared__ uint32_t wtot[kSplitThreads / kWave];
+    __shared__ uint32_t s_digit, s_dabove, s_dcnt, s_fill, s_total;
+    const int t = threadIdx.x;
+    const int64_t r = blockIdx.x;
+    const int32_t nc = (int32_t)min(visible_blocks(row_pos[r]), (int64_t)max_nb);
+    const int32_t kk = min(top_k, nc);
+    if (nc <= top_k) return;  // written by the collect kernel
+    int32_t *out = sel_blocks + r * top_k;
+    float *osc = sel_scores ? sel_scores + r * top_k : nullptr;
+    const uint32_t *cnt = ss.scratch + r * kRowScratch + kHistBins;
+    const uint2 *sure = ss.sure + r * top_k;
+    const uint2 *cand = ss.cand + r * ss.cand_stride;
+    const uint32_t n_sure = cnt[0];
+    const uint32_t n_cand = cnt[1];
     uint32_t need = (uint32_t)kk - n_sure;  // 1 <= need <= n_cand
+    // candidates staged in LDS once when they fit (read by every radix pass)
+    const bool staged = n_cand <= (uint32_t)kCandStage;
+    if (staged)
+        for (uint32_t i = t; i < n_cand; i += kSplitThreads) cst[i] = cand[i];
+    __syncthreads();
+    const uint2 *cl = staged ? cst : cand;
     uint64_t prefix = 0, pmask = 0;
     if (need < n_cand) {
         for (int sh = 44;; sh -= 8) {  // 8-bit digits of the 52-bit composite, from the top
@@ -204,7 +273,7 @@ __global__ __launch_bounds__(kSplitThreads) void select_collect_kernel(
             dhist[t] = 0u;
             __syncthreads();
             for (uint32_t i = t; i < n_cand; i += kSplitThreads) {
-                const uint64_t c = composite20(cand[i]);
+                const uint64_t c = composite20(cl[i]);
                 if ((c & pmask) == prefix) atomicAdd(&dhist[(uint32_t)(c >> s2) & dmask], 1u);
             }
             __syncthreads();
@@ -232,36 +301,52 @@ __global__ __launch_bounds__(kSplitThreads) void select_collect_kernel(
         buf[atomicAdd(&s_fill, 1u)] = ((uint64_t)e.y << 32) | e.x;
     }
     for (uint32_t i = t; i < n_cand; i += kSplitThreads) {
-        const uint2 e = cand[i];
+        const uint2 e = cl[i];
         if ((composite20(e) & pmask) >= prefix) buf[atomicAdd(&s_fill, 1u)] = ((uint64_t)e.y << 32) | e.x;
     }
     __syncthreads();
     const uint32_t n = min(s_fill, (uint32_t)kk);
-    uint32_t n2 = 1;
-    while (n2 < n) n2 <<= 1;
-    for (uint32_t i = n + t; i < n2; i += kSplitThreads) buf[i] = ~0ull;
-    __syncthreads();
-    for (uint32_t size = 2; size <= n2; size <<= 1) {  // bitonic sort by block id
-        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-            for (uint32_t i = t; i < n2 / 2; i += kSplitThreads) {
-                const uint32_t lo = 2 * i - (i & (stride - 1));
-                const uint32_t hi = lo + stride;
-                const bool up = (lo & size) == 0;
-                const uint64_t x = buf[lo], y = buf[hi];
-                if ((x > y) == up) {
-                    buf[lo] = y;
-                    buf[hi] = x;
-                }
-            }
-            __syncthreads();
-        }
-    }
     if (t == 0) sel_count[r] = (int32_t)n;
-    for (int32_t i = t; i < top_k; i += kSplitThreads) {
-        const bool kept = (uint32_t)i < n;
-        const uint64_t e = kept ? buf[i] : 0ull;
-        out[i] = kept ? (int32_t)(e >> 32) : -1;
-        if (osc) osc[i] = kept ? scaled_score(key_score((uint32_t)e)) : 0.0f;
+    // ---- emit in block order: mark the kept blocks in an LDS bitmap (one
+    // window of the visible range at a time), then each thread writes the set
+    // bits of its run of words at its prefix-sum offset ----
+    const float *srow = scores + r * sc_stride;
+    uint32_t out_base = 0;
+    for (int64_t w0 = 0; w0 < nc; w0 += 32 * kEmitWords) {
+        const int nwords = (int)min((int64_t)kEmitWords, (nc - w0 + 31) / 32);
+        for (int i = t; i < nwords; i += kSplitThreads) bm[i] = 0u;
+        __syncthreads();
+        for (uint32_t i = t; i < n; i += kSplitThreads) {
+            const int64_t b = (int64_t)(buf[i] >> 32) - w0;
+            if (b >= 0 && b < 32 * (int64_t)nwords) atomicOr(&bm[b >> 5], 1u << (b & 31));
+        }
+        __syncthreads();
+        const int per = (nwords + kSplitThreads - 1) / kSplitThreads;
+        const int i0 = min(nwords, t * per), i1 = min(nwords, i0 + per);
+        uint32_t c = 0;
+        for (int i = i0; i < i1; ++i) c += (uint32_t)__popc(bm[i]);
+        const uint32_t incl = wg_inclusive_scan<kSplitThreads>(c, wtot);
+        if (t == kSplitThreads - 1) s_total = incl;
+        uint32_t pos = out_base + incl - c;
+        for (int i = i0; i < i1; ++i) {
+            uint32_t word = bm[i];
+            while (word) {
+                const int bit = __ffs(word) - 1;
+                word &= word - 1u;
+                const int64_t b = w0 + 32 * (int64_t)i + bit;
+                if (pos < (uint32_t)kk) {
+                    out[pos] = (int32_t)b;
+                    if (osc) osc[pos] = scaled_score(srow[b]);
+                }
+                ++pos;
+            }
+        }
+        __syncthreads();
+        out_base += s_total;
+    }
+    for (int32_t i = (int32_t)n + t; i < top_k; i += kSplitThreads) {
+        out[i] = -1;
+        if (osc) osc[i] = 0.0f;
     }
 }
 
@@ -272,6 +357,8 @@ void launch_select_split(const float *scores, int64_t sc_stride, const int32_t *
     const int64_t chunks = max((int64_t)1, ((int64_t)max_nb + kCollectChunk - 1) / kCollectChunk);
     QSA_LAUNCH("select_collect", select_collect_kernel, dim3((unsigned)chunks, (unsigned)rows), dim3(kSplitThreads),
                0, stream, scores, sc_stride, row_pos, max_nb, top_k, ss, sel_blocks, sel_count, sel_scores);
+    QSA_LAUNCH("select_final", select_final_kernel, dim3((unsigned)rows), dim3(kSplitThreads), 0, stream, scores,
+               sc_stride, row_pos, max_nb, top_k, ss, sel_blocks, sel_count, sel_scores);
 }
 
 }  // namespace qsa
