@@ -99,6 +99,49 @@ __device__ __forceinline__ void rope_pair(double &x, double &y, int64_t pos, dou
     y = ny;
 }
 
+// max(x, 0) of a finite float as one integer max on its bits: a negative
+// float (or -0) has the sign bit set and so compares below 0 as an int; the
+// float form would first quiet a possible signalling NaN.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Inclusive scan of `op` over the 64 lanes of a wave through DPP lane moves
+// (no LDS round trip): shifts by 1, 2, 4 and 8 inside each 16-lane row, then
+// the last lane of a row is broadcast into the rows after it.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_incl_scan_op(uint32_t v, Op op)
+{
+    const int lane = threadIdx.x & 63, rl = lane & 15;
+    uint32_t t;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v = rl >= 1 ? op(v, t) : v;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v = rl >= 2 ? op(v, t) : v;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v = rl >= 4 ? op(v, t) : v;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v = rl >= 8 ? op(v, t) : v;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x142, 0xf, 0xf, false);  // row_bcast:15
+    v = (lane & 31) >= 16 ? op(v, t) : v;
+    t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x143, 0xf, 0xf, false);  // row_bcast:31
+    v = lane >= 32 ? op(v, t) : v;
+    return v;
+}
+
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v)
+{
+    return wave_incl_scan_op(v, [](uint32_t x, uint32_t y) { return x + y; });
+}
+
+// Value of a wave-uniform lane's register.
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int lane) { return (uint32_t)__builtin_amdgcn_readlane((int)v, lane); }
+
+// Bitwise OR of a value over the wave's lanes.
+__device__ __forceinline__ uint32_t wave_or(uint32_t v)
+{
+    return lane_value(wave_incl_scan_op(v, [](uint32_t x, uint32_t y) { return x | y; }), 63);
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

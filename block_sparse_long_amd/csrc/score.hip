@@ -22,7 +22,7 @@ constexpr int kChunk = 2048;  // blocks per workgroup in the row-split kernels
 
 __device__ __forceinline__ float relu_sum4(f32x4_t a)
 {
-    return ((fmaxf(a[0], 0.0f) + fmaxf(a[1], 0.0f)) + fmaxf(a[2], 0.0f)) + fmaxf(a[3], 0.0f);
+    return ((relu(a[0]) + relu(a[1])) + relu(a[2])) + relu(a[3]);
 }
 
 // Per-row histogram of the score keys' top 12 bits: counted in LDS, then

@@ -56,7 +56,7 @@ __device__ __forceinline__ int64_t sample_block(int64_t i)
 
 __device__ __forceinline__ float relu_sum4f(f32x4_t a)
 {
-    return ((fmaxf(a[0], 0.0f) + fmaxf(a[1], 0.0f)) + fmaxf(a[2], 0.0f)) + fmaxf(a[3], 0.0f);
+    return ((relu(a[0]) + relu(a[1])) + relu(a[2])) + relu(a[3]);
 }
 
 // Order key of a non-negative score (a sum of ReLUs; -0 and +0 map to one key).
@@ -416,13 +416,192 @@ __device__ __forceinline__ float recompute_score(const bf16_t *__restrict__ q4, 
 
 __device__ __forceinline__ float scaled(float raw) { return (float)((double)raw / sqrt((double)kDim)); }
 
+// The merge of one row whose n <= kStage pairs sit in the wave's LDS stage.
+// The pairs move to registers (kStage / 64 per lane; an empty slot holds key
+// 0, which no pair has: pair keys always carry the top bit).  A radix select
+// over the keys finds the kk-th largest key T; when T is shared by more pairs
+// than still needed, a second radix select over the blocks of those pairs
+// keeps the lowest ones.  The kept blocks are then written in block order:
+// marked in a bitmap of the visible range (one 65,536-block window at a time,
+// in the stage's LDS), whose per-word prefix counts give each one its slot.
+constexpr int kRegPairs = kStage / kWave;
+constexpr int kWinWords = 2048;  // bitmap window: 65,536 blocks
+// Lane l owns bitmap words [32l, 32l + 32).  Word w is stored at w + w/32 and
+// its u16 prefix count at w + 2(w/32), so the 64 lanes walking their own
+// words hit distinct LDS banks.
+__device__ __forceinline__ uint32_t bm_slot(uint32_t w) { return w + (w >> 5); }
+__device__ __forceinline__ uint32_t pre_slot(uint32_t w) { return w + 2u * (w >> 5); }
+constexpr int kBmSlots = kWinWords + kWinWords / 32;
+constexpr int kPreSlots = kWinWords + 2 * (kWinWords / 32);
+static_assert(kBmSlots * 4 + kPreSlots * 2 <= kStage * 8, "bitmap + prefix fit the stage");
+
+// The pick step of one radix pass (of `width` <= 8 bits) of a descending
+// select in the wave: `h` holds the counts of the digits of the values whose
+// higher bits match `prefix`; narrows (prefix, need) to the bin holding the
+// need-th largest (prefix restarts on the first pass) and returns that bin's
+// count.
+__device__ __forceinline__ uint32_t radix_pass_pick(uint32_t *h, uint32_t &need, uint32_t &prefix, bool first,
+                                                    int width)
+{
+    const int lane = threadIdx.x & 63;
+    wave_fence();
+    uint32_t hv[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        hv[q] = h[255 - 4 * lane - q];
+        sum += hv[q];
+    }
+    const uint32_t incl = wave_incl_scan(sum);
+    const int ls = __ffsll((unsigned long long)__ballot(incl >= need)) - 1;
+    uint32_t digit = 0, above = 0, cntd = 0;
+    {  // every lane computes; lane ls's values are the ones used
+        uint32_t acc = incl - sum;
+        bool found = false;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool hit = !found && acc + hv[q] >= need;
+            digit = hit ? 255u - 4u * (uint32_t)lane - (uint32_t)q : digit;
+            above = hit ? acc : above;
+            cntd = hit ? hv[q] : cntd;
+            found = found || hit;
+            acc += hv[q];
+        }
+    }
+    digit = lane_value(digit, ls);
+    above = lane_value(above, ls);
+    cntd = lane_value(cntd, ls);
+    need -= above;
+    prefix = first ? digit : (prefix << width) | digit;
+    wave_fence();
+    return cntd;
+}
+
+__device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n, int32_t nc, int32_t kk,
+                                             int32_t *__restrict__ out, float *__restrict__ osc)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t key[kRegPairs], nblk[kRegPairs];  // key and ~block; an empty slot is (0, 0)
+#pragma unroll
+    for (int i = 0; i < kRegPairs; ++i) {
+        const uint32_t idx = (uint32_t)(i * kWave + lane);
+        const uint2 e = idx < n ? st[idx] : make_uint2(0u, 0xffffffffu);
+        key[i] = e.x;
+        nblk[i] = ~e.y;
+    }
+    // ---- kk-th largest key.  Bits that every pair shares are skipped (the
+    // first pass starts below them, so its digits spread over the bins); a
+    // pass counts the next digit of every key whose resolved top bits match,
+    // and a non-matching key (or an empty slot) counts in the lane's spare
+    // slot.  (key >> sh) > tp is kept, == tp is the current bin. ----
+    uint32_t need = (uint32_t)kk, tp = 0, cnt = 0;
+    int sh = 32;
+    if ((uint32_t)kk < n) {
+        const uint32_t k0 = lane_value(key[0], 0);  // the first staged pair
+        uint32_t x = 0;
+#pragma unroll
+        for (int i = 0; i < kRegPairs; ++i) x |= key[i] != 0u ? key[i] ^ k0 : 0u;
+        x = wave_or(x);
+        sh = x ? 32 - __clz(x) : 0;  // pair keys share bit 31, so sh <= 31
+        tp = k0 >> sh;
+        cnt = n;
+        while (sh > 0 && cnt != need) {
+            const int nsh = max(sh - 8, 0), width = sh - nsh;
+            const uint32_t himask = 0xffffffffu << sh, hv = tp << sh;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) h[4 * lane + q] = 0u;
+            wave_fence();
+#pragma unroll
+            for (int i = 0; i < kRegPairs; ++i) {
+                const bool m = (key[i] & himask) == hv;
+                atomicAdd(&h[m ? (key[i] >> nsh) & ((1u << width) - 1u) : 256u + (uint32_t)lane], 1u);
+            }
+            cnt = radix_pass_pick(h, need, tp, false, width);
+            sh = nsh;
+        }
+    }
+    // ---- ties at T cut: keep the `need` lowest blocks among key == T, the
+    // largest values of ~block ----
+    const bool cut = sh == 0 && cnt != need;
+    uint32_t bp = 0;
+    int bsh = 32;
+    if (cut) {
+        for (; bsh > 0;) {
+            const int nsh = bsh - 8;
+            const uint32_t himask = bsh == 32 ? 0u : 0xffffffffu << bsh;
+            const uint32_t hv = bsh == 32 ? 0u : bp << bsh;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) h[4 * lane + q] = 0u;
+            wave_fence();
+#pragma unroll
+            for (int i = 0; i < kRegPairs; ++i) {
+                const bool m = (key[i] == tp) & ((nblk[i] & himask) == hv);
+                atomicAdd(&h[m ? (nblk[i] >> nsh) & 0xffu : 256u + (uint32_t)lane], 1u);
+            }
+            cnt = radix_pass_pick(h, need, bp, bsh == 32, 8);
+            bsh = nsh;
+            if (cnt == need) break;
+        }
+    }
+    // kept <=> (key << 32 | ~block) >= C: every composite above the resolved
+    // bin, and all of the final bin (kept whole, or cut by the block passes)
+    uint64_t C;
+    if (sh == 32) C = 1ull;  // keep every pair (empty slots are 0)
+    else if (!cut) C = (uint64_t)(tp << sh) << 32;
+    else C = ((uint64_t)tp << 32) | (uint64_t)(bsh == 32 ? 0u : bp << bsh);
+    // ---- emission through the bitmap, window by window ----
+    uint32_t *bm = (uint32_t *)st;
+    uint16_t *pre = (uint16_t *)(bm + kBmSlots);
+    uint32_t base = 0;
+    for (int32_t w0 = 0; w0 < nc; w0 += 32 * kWinWords) {
+        const int nwords = min(kWinWords, (nc - w0 + 31) / 32);
+        const uint32_t wbits = 32u * (uint32_t)nwords;
+        for (int i = lane; i < kBmSlots; i += kWave) bm[i] = 0u;
+        wave_fence();
+#pragma unroll
+        for (int i = 0; i < kRegPairs; ++i) {  // a pair not kept ORs 0 into its lane's word
+            const uint32_t b = ~nblk[i] - (uint32_t)w0;
+            const bool k = ((((uint64_t)key[i] << 32) | nblk[i]) >= C) & (b < wbits);
+            atomicOr(&bm[k ? bm_slot(b >> 5) : (uint32_t)lane], k ? 1u << (b & 31u) : 0u);
+        }
+        wave_fence();
+        // exclusive prefix count of each word, in word order
+        constexpr int kPer = kWinWords / kWave;
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) c += (uint32_t)__popc(bm[bm_slot((uint32_t)(lane * kPer + j))]);
+        const uint32_t incl = wave_incl_scan(c);
+        uint32_t run = incl - c;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const uint32_t wi = (uint32_t)(lane * kPer + j);
+            pre[pre_slot(wi)] = (uint16_t)run;
+            run += (uint32_t)__popc(bm[bm_slot(wi)]);
+        }
+        wave_fence();
+#pragma unroll
+        for (int i = 0; i < kRegPairs; ++i) {
+            const uint32_t b = ~nblk[i] - (uint32_t)w0;
+            const bool k = ((((uint64_t)key[i] << 32) | nblk[i]) >= C) & (b < wbits);
+            const uint32_t wd = k ? b >> 5 : 0u;
+            const uint32_t pos =
+                base + (uint32_t)pre[pre_slot(wd)] + (uint32_t)__popc(bm[bm_slot(wd)] & ((1u << (b & 31u)) - 1u));
+            if (k && pos < (uint32_t)kk) {
+                out[pos] = (int32_t)(w0 + b);
+                if (osc) osc[pos] = scaled(key_score(key[i]));
+            }
+        }
+        base += lane_value(incl, kWave - 1);
+        if (w0 + 32 * kWinWords < nc) wave_fence();  // the next window reuses the bitmap
+    }
+}
+
 }  // namespace
 
-__global__ __launch_bounds__(256) void select_merge_kernel(FusedScoreArgs a, int32_t *__restrict__ sel_blocks,
+__global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, int32_t *__restrict__ sel_blocks,
                                                          int32_t *__restrict__ sel_count, float *__restrict__ sel_scores)
 {
     __shared__ uint2 stage[kMergeWaves][kStage];
-    __shared__ uint32_t hb[kMergeWaves][256];
+    __shared__ uint32_t hb[kMergeWaves][256 + kWave];  // 256 bins + a spare slot per lane
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t r = (int64_t)blockIdx.x * kMergeWaves + w;
     if (r >= a.rows) return;
@@ -469,12 +648,12 @@ __global__ __launch_bounds__(256) void select_merge_kernel(FusedScoreArgs a, int
             const uint32_t chunk = __shfl(off, 63);
             off = n + off - c;
             const uint2 *src = lists + (int64_t)min(li, nlists - 1) * a.subcap;
-            for (uint32_t j = 0; j < cmax; j += 4) {
-                uint2 e[4];
+            for (uint32_t j = 0; j < cmax; j += 16) {  // 16 loads in flight per lane
+                uint2 e[16];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) e[q] = j + q < c ? src[j + q] : make_uint2(0u, 0u);
+                for (int q = 0; q < 16; ++q) e[q] = j + q < c ? src[j + q] : make_uint2(0u, 0u);
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < 16; ++q)
                     if (j + q < c) st[off + j + q] = e[q];
             }
             n += chunk;
@@ -484,10 +663,14 @@ __global__ __launch_bounds__(256) void select_merge_kernel(FusedScoreArgs a, int
     } else {
         n = (uint32_t)nc;
     }
+    wave_fence();
+    if (mode == 0) {
+        merge_staged(st, h, n, nc, kk, out, osc);
+        return;
+    }
     const int32_t seq = a.row_seq[r];
     const bf16_t *q4 = (const bf16_t *)a.qrot + r * kIdxHeads * kDim;
     const bf16_t *kb = (const bf16_t *)a.pooled + (int64_t)seq * a.pooled_stride;
-    wave_fence();
     // visit every candidate, 64 at a time: fn(pair, valid).  Staged and listed
     // pairs come in no particular order; recomputed ones in block order.
     auto visit = [&](auto &&fn) {
