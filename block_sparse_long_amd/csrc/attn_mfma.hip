@@ -48,14 +48,14 @@ constexpr int kWinWords = kWin / 32;
 constexpr int kMaxUnionBlocks = 4096;  // rows per tile x top_k is kept at or below this
 constexpr int kMaxTileRows = 16;       // row masks are 16 bits
 
-struct ChunkSmem {
+struct alignas(16) ChunkSmem {
     bf16_t k[kCh][kKRow];
     bf16_t vt[kDim][kVRow];
     int32_t pos[kCh];
     uint32_t pmask[kCh];
 };
 
-struct UnionSmem {
+struct alignas(16) UnionSmem {
     uint32_t bitmap[kWinWords];
     uint16_t wprefix[kWinWords];     // < kMaxUnionBlocks
     int32_t blk[kMaxUnionBlocks];
@@ -63,10 +63,21 @@ struct UnionSmem {
     uint32_t count;
 };
 
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, b16x2_t));
 }
+
+// Logits are kept in base-2 units (softmax_scale * log2(e) * <q, k>).  The
+// softmax reference max of a query moves only when a logit exceeds it by more
+// than kLazy: until then P = 2^(s - m) <= 2^kLazy, and O and l keep their
+// scale (the final O / l and lse = m + log2(l) are the same either way).
+constexpr float kLazy = 8.0f;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 
 // Per-wave attention state: 16 queries, lane l <-> query l%16 for m / l,
 // O[q = 4*(l/16) + j][dim 16*nt + l%16] in o[nt][j].
@@ -99,7 +110,7 @@ __device__ __forceinline__ void chunk_load(ChunkRegs &cr, const bf16_t *__restri
 #pragma unroll
         for (int i = 0; i < 4; ++i) cr.k[i] = make_uint4(0, 0, 0, 0);
     }
-    const int p0 = (t >> 4) * 4, dv = (t & 15) * 8;
+    const int p0 = (t & 15) * 4, dv = (t >> 4) * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         cr.v[i] = (p0 + i < n) ? *(const uint4 *)(vbase + (int64_t)pos(p0 + i) * row_stride + dv)
@@ -113,17 +124,17 @@ __device__ __forceinline__ void chunk_store(ChunkSmem &cs, const ChunkRegs &cr)
     const int p = t >> 2, dk = (t & 3) * 32;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *(uint4 *)&cs.k[p][dk + 8 * i] = cr.k[i];
-    const int p0 = (t >> 4) * 4, dv = (t & 15) * 8;
+    // the 16 lanes sharing dv write 16 consecutive 8-byte pieces of a V^T row
+    const int p0 = (t & 15) * 4, dv = (t >> 4) * 8;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-        const int w = d >> 1, hi = d & 1;
-        uint32_t e[4];
+    for (int w = 0; w < 4; ++w) {  // dims dv + 2w (low halves) and dv + 2w + 1 (high halves)
+        uint32_t x[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t word = w == 0 ? cr.v[i].x : w == 1 ? cr.v[i].y : w == 2 ? cr.v[i].z : cr.v[i].w;
-            e[i] = hi ? (word >> 16) : (word & 0xffffu);
-        }
-        *(uint2 *)&cs.vt[dv + d][p0] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+        for (int i = 0; i < 4; ++i) x[i] = w == 0 ? cr.v[i].x : w == 1 ? cr.v[i].y : w == 2 ? cr.v[i].z : cr.v[i].w;
+        *(uint2 *)&cs.vt[dv + 2 * w][p0] = make_uint2(__builtin_amdgcn_perm(x[1], x[0], 0x05040100u),
+                                                      __builtin_amdgcn_perm(x[3], x[2], 0x05040100u));
+        *(uint2 *)&cs.vt[dv + 2 * w + 1][p0] = make_uint2(__builtin_amdgcn_perm(x[1], x[0], 0x07060302u),
+                                                          __builtin_amdgcn_perm(x[3], x[2], 0x07060302u));
     }
 }
 
@@ -137,9 +148,10 @@ __device__ __forceinline__ void gather_chunk(ChunkSmem &cs, const bf16_t *__rest
 }
 
 // One chunk for one wave: S^T, online softmax, O += P V.  `qbit` is the mask
-// bit of this lane's query row (0 when the query slot is unused).
-__device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, int n, const bf16x8_t (&qb)[4], uint32_t qbit,
-                                           float scale, WaveState &st)
+// bit of this lane's query row (0 when the query slot is unused); positions
+// past the chunk's end carry no mask bit.  `scale2` = softmax_scale * log2(e).
+__device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, const bf16x8_t (&qb)[4], uint32_t qbit,
+                                           float scale2, WaveState &st)
 {
     const int lane = threadIdx.x & 63;
     const int m16 = lane & 15, g = lane >> 4;
@@ -147,15 +159,9 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, int n, const bf1
     bool any[4];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-        bool ok[4];
-        bool lane_any = false;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int pi = sub * 16 + 4 * g + j;
-            ok[j] = pi < n && (cs.pmask[pi] & qbit) != 0u;
-            lane_any |= ok[j];
-        }
-        any[sub] = __ballot(lane_any) != 0ull;
+        const uint4 pm = *(const uint4 *)&cs.pmask[sub * 16 + 4 * g];  // positions 4g .. 4g+3 of the sub-tile
+        const bool ok[4] = {(pm.x & qbit) != 0u, (pm.y & qbit) != 0u, (pm.z & qbit) != 0u, (pm.w & qbit) != 0u};
+        any[sub] = __ballot(ok[0] | ok[1] | ok[2] | ok[3]) != 0ull;
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
         if (any[sub]) {
 #pragma unroll
@@ -165,9 +171,9 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, int n, const bf1
             }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s[sub][j] = ok[j] ? acc[j] * scale : -INFINITY;
+        for (int j = 0; j < 4; ++j) s[sub][j] = ok[j] ? acc[j] * scale2 : -INFINITY;
     }
-    // online softmax, per query (lane l%16), over the 4 lane groups
+    // online softmax per query (lane l%16; the 4 lane groups hold its positions)
     float cmax = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub)
@@ -175,35 +181,30 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, int n, const bf1
         for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, s[sub][j]);
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(st.m, cmax);
-    float alpha = 1.0f;
-    float psum = 0.0f;
-    float p[4][4];
-    if (m_new == -INFINITY) {
+    const bool raise = cmax > st.m + kLazy;  // also the first logit of a query (st.m = -inf)
+    const float m_ref = raise ? cmax : st.m;
+    if (__ballot(raise && st.m != -INFINITY)) {  // some query's O and l change scale
+        const float alpha = raise ? __builtin_amdgcn_exp2f(st.m - m_ref) : 1.0f;
+        st.l *= alpha;
+        float a4[4];
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub)
+        for (int j = 0; j < 4; ++j) a4[j] = __shfl(alpha, 4 * g + j);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) p[sub][j] = 0.0f;
-    } else {
-        alpha = st.m == -INFINITY ? 0.0f : __expf(st.m - m_new);
+        for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                p[sub][j] = s[sub][j] == -INFINITY ? 0.0f : __expf(s[sub][j] - m_new);
-                psum += p[sub][j];
-            }
+            for (int j = 0; j < 4; ++j) st.o[nt][j] *= a4[j];
     }
-    st.m = m_new;
-    st.l = st.l * alpha + psum;  // per-lane partial; the 4 groups are summed at the end
-    // rescale O rows (queries 4g + j) by their alpha
-    float a4[4];
+    st.m = m_ref;
+    float p[4][4];
+    float psum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a4[j] = __shfl(alpha, 4 * g + j);
+    for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) st.o[nt][j] *= a4[j];
+        for (int j = 0; j < 4; ++j) {
+            p[sub][j] = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s[sub][j] - m_ref);
+            psum += p[sub][j];
+        }
+    st.l += psum;  // per-lane partial; the 4 groups are summed at the end
     // O += P V over two 32-position steps
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -253,7 +254,7 @@ __device__ __forceinline__ float total_l(const WaveState &st)
 // ---------------------------------------------------------------------------
 // Prefill: grid (row tiles, Hkv).  rows_per_tile * hg <= 64.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnArgs a, int32_t rows_per_tile)
+__global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, int32_t rows_per_tile)
 {
     __shared__ ChunkSmem cs;
     __shared__ UnionSmem us;
@@ -272,6 +273,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnArgs a, int3
     load_query((const bf16_t *)a.q + ((row0 + (q_valid ? r_local : 0)) * a.Hq + head) * kDim, q_valid, qb);
     WaveState st;
     init_state(st);
+    const float scale2 = a.scale * kLog2e;
     const int64_t row_stride = (int64_t)a.Hkv * kDim;
     uint32_t todo = nrows >= 32 ? 0xffffffffu : ((1u << nrows) - 1u);
     while (todo) {  // rows of one sequence at a time (uniform across the workgroup)
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnArgs a, int3
                     chunk_load(cr, kbase, vbase, row_stride, min(kChB, nu - c1) * kBlock,
                                [&](int i) { return (int64_t)us.blk[c1 + i / kBlock] * kBlock + (i % kBlock); });
                 }
-                wave_chunk(cs, nb * kBlock, qb, qbit, a.scale, st);
+                wave_chunk(cs, qb, qbit, scale2, st);
                 __syncthreads();
             }
         }
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnArgs a, int3
             gather_chunk(cs, kbase, vbase, row_stride, ntail);
             __syncthreads();
             // positions beyond n carry no mask bit, so they stay out
-            wave_chunk(cs, kCh, qb, qbit, a.scale, st);
+            wave_chunk(cs, qb, qbit, scale2, st);
         }
         __syncthreads();
     }
@@ -425,7 +427,8 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnArgs a, int3
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) orow[16 * nt + m16] = f32_to_bf16(st.o[nt][j] * inv);
     }
-    if (a.lse && g == 0 && q_valid) a.lse[(row0 + r_local) * a.Hq + head] = ltot > 0.0f ? st.m + __logf(ltot) : -INFINITY;
+    if (a.lse && g == 0 && q_valid)
+        a.lse[(row0 + r_local) * a.Hq + head] = ltot > 0.0f ? (st.m + __log2f(ltot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -451,6 +454,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(AttnArgs a)
     load_query((const bf16_t *)a.q + qrow * kDim, q_valid, qb);
     WaveState st;
     init_state(st);
+    const float scale2 = a.scale * kLog2e;
     const uint32_t qbit = q_valid ? (1u << jrow) : 0u;
     const int64_t row_stride = (int64_t)a.Hkv * kDim;
     const bf16_t *kbase = (const bf16_t *)a.k_cache + s * a.kv_seq_stride + (int64_t)kvh * kDim;
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(AttnArgs a)
             __syncthreads();
             gather_chunk(cs, kbase, vbase, row_stride, nb * kBlock);
             __syncthreads();
-            wave_chunk(cs, nb * kBlock, qb, qbit, a.scale, st);
+            wave_chunk(cs, qb, qbit, scale2, st);
         }
     } else {
         // tails: row j attends [ts_j, t_j]; walk [min ts, max t] in chunks
@@ -498,7 +502,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(AttnArgs a)
             __syncthreads();
             gather_chunk(cs, kbase, vbase, row_stride, n);
             __syncthreads();
-            wave_chunk(cs, n, qb, qbit, a.scale, st);
+            wave_chunk(cs, qb, qbit, scale2, st);
             __syncthreads();
         }
     }
@@ -515,7 +519,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(AttnArgs a)
     }
     if (q_valid && g == 0) {
         float *pp = a.partial + (qrow * a.nsplit + split) * (kDim + 2);
-        pp[kDim] = st.m;
+        pp[kDim] = st.m * kLn2;  // natural-log units for the combine
         pp[kDim + 1] = ltot;
     }
 }
