@@ -322,6 +322,7 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
         my_cnt[mt] = 0;
         tauf[mt] = ok ? tau_float(a.tau[row0 + rw]) : INFINITY;
     }
+    const uint32_t cap_last = (uint32_t)a.subcap - 1u;
     uint64_t todo = nrows >= 64 ? ~0ull : ((1ull << nrows) - 1ull);
     while (todo) {
         int64_t nb_hi;
@@ -329,6 +330,15 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
         int64_t lim[4];  // visible bound of the lane's rows in this group (0: not in it)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) lim[mt] = my_seq[mt] == seq ? my_nc[mt] : 0;
+        // smallest bound over the wave's 16 rows (an empty row slot has tau = +inf, so it never appends)
+        int64_t lim_min = INT64_MAX;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int rw = 16 * wave + 4 * mt + g;
+            if (rw < nrows) lim_min = min(lim_min, lim[mt]);
+        }
+        lim_min = min(lim_min, (int64_t)__shfl_xor((long long)lim_min, 16));
+        lim_min = min(lim_min, (int64_t)__shfl_xor((long long)lim_min, 32));
         const int64_t lo = split_lo, hi = min(split_hi, nb_hi);
         if (lo >= hi) continue;
         const bf16_t *kb = pooled + (int64_t)seq * a.pooled_stride;
@@ -366,17 +376,31 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
                 dst[2] = p2;
                 dst[3] = p3;
             }
+            // a pair >= tau goes to the lane's list; past the list's capacity
+            // the last slot is overwritten but the count goes on, so the
+            // merge sees the overflow (and recomputes the row)
+            if (base + kFStep <= lim_min) {  // every block of the step is visible to every row of the wave
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                // block base + 16*nt + m is visible iff 16*nt < lr
-                const int32_t lr = (int32_t)max(min(lim[mt] - base - m, (int64_t)kFStep), (int64_t)-1);
+                for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    if (sc[mt][nt] >= tauf[mt] && 16 * nt < lr) {
-                        if (my_cnt[mt] < (uint32_t)a.subcap)
-                            my_list[mt][my_cnt[mt]] = make_uint2(pos_key(sc[mt][nt]), (uint32_t)(base + nt * 16 + m));
-                        ++my_cnt[mt];
-                    }
+                    for (int nt = 0; nt < 4; ++nt)
+                        if (sc[mt][nt] >= tauf[mt]) {
+                            my_list[mt][min(my_cnt[mt], cap_last)] =
+                                make_uint2(pos_key(sc[mt][nt]), (uint32_t)(base + nt * 16 + m));
+                            ++my_cnt[mt];
+                        }
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    // block base + 16*nt + m is visible iff 16*nt < lr
+                    const int32_t lr = (int32_t)max(min(lim[mt] - base - m, (int64_t)kFStep), (int64_t)-1);
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+                        if (sc[mt][nt] >= tauf[mt] && 16 * nt < lr) {
+                            my_list[mt][min(my_cnt[mt], cap_last)] =
+                                make_uint2(pos_key(sc[mt][nt]), (uint32_t)(base + nt * 16 + m));
+                            ++my_cnt[mt];
+                        }
                 }
             }
             __syncthreads();
