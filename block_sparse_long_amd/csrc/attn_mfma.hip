@@ -275,36 +275,54 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
     init_state(st);
     const float scale2 = a.scale * kLog2e;
     const int64_t row_stride = (int64_t)a.Hkv * kDim;
+    // ---- the tile's rows, read once: position, sequence, kept count, last
+    // kept block; and all their kept blocks (at most kMaxUnionBlocks, 16 per
+    // thread), loaded together and kept in registers for the union passes ----
+    __shared__ int32_t s_pos[kMaxTileRows], s_seq[kMaxTileRows], s_cnt[kMaxTileRows], s_last[kMaxTileRows];
+    if (t < nrows) {
+        const int64_t r = row0 + t;
+        const int32_t c = max(0, min(a.sel_count[r], a.top_k));
+        s_pos[t] = a.row_pos[r];
+        s_seq[t] = a.row_seq[r];
+        s_cnt[t] = c;
+        s_last[t] = c > 0 ? a.sel_blocks[r * a.top_k + c - 1] : -1;
+    }
+    __syncthreads();
+    constexpr int kSelPerThread = kMaxUnionBlocks / 256;
+    int32_t eblk[kSelPerThread];  // kept block, or -1
+    int32_t erow[kSelPerThread];  // its tile row
+#pragma unroll
+    for (int j = 0; j < kSelPerThread; ++j) {
+        const int32_t idx = t + 256 * j;
+        const int32_t r = idx / a.top_k, i = idx - r * a.top_k;
+        const bool ok = r < nrows && i < s_cnt[min(r, nrows - 1)];
+        erow[j] = ok ? r : 0;
+        eblk[j] = ok ? a.sel_blocks[(row0 + r) * a.top_k + i] : -1;
+    }
     uint32_t todo = nrows >= 32 ? 0xffffffffu : ((1u << nrows) - 1u);
     while (todo) {  // rows of one sequence at a time (uniform across the workgroup)
         const int first = __builtin_ctz(todo);
-        const int32_t seq = a.row_seq[row0 + first];
+        const int32_t seq = s_seq[first];
         uint32_t active = 0;
         for (int r = first; r < nrows; ++r)
-            if (((todo >> r) & 1u) && a.row_seq[row0 + r] == seq) active |= 1u << r;
+            if (((todo >> r) & 1u) && s_seq[r] == seq) active |= 1u << r;
         todo &= ~active;
         const uint32_t qbit = q_valid ? (active & (1u << r_local)) : 0u;
         const bf16_t *kbase = (const bf16_t *)a.k_cache + (int64_t)seq * a.kv_seq_stride + (int64_t)kvh * kDim;
         const bf16_t *vbase = (const bf16_t *)a.v_cache + (int64_t)seq * a.kv_seq_stride + (int64_t)kvh * kDim;
         // block range of the active rows' selections
         int32_t hi_blk = 0;
-        for (int r = 0; r < nrows; ++r) {
-            if (!((active >> r) & 1u)) continue;
-            const int32_t c = min(a.sel_count[row0 + r], a.top_k);
-            if (c > 0) hi_blk = max(hi_blk, a.sel_blocks[(row0 + r) * a.top_k + c - 1] + 1);
-        }
+        for (int r = 0; r < nrows; ++r)
+            if ((active >> r) & 1u) hi_blk = max(hi_blk, s_last[r] + 1);
         for (int32_t w0 = 0; w0 < hi_blk; w0 += kWin) {
             // ---- union of the active rows' kept blocks in [w0, w0 + kWin) ----
             for (int i = t; i < kWinWords; i += blockDim.x) us.bitmap[i] = 0u;
             __syncthreads();
-            for (int r = 0; r < nrows; ++r) {
-                if (!((active >> r) & 1u)) continue;
-                const int32_t c = min(a.sel_count[row0 + r], a.top_k);
-                const int32_t *sl = a.sel_blocks + (row0 + r) * a.top_k;
-                for (int i = t; i < c; i += blockDim.x) {
-                    const int32_t b = sl[i] - w0;
-                    if (b >= 0 && b < kWin) atomicOr(&us.bitmap[b >> 5], 1u << (b & 31));
-                }
+#pragma unroll
+            for (int j = 0; j < kSelPerThread; ++j) {
+                const int32_t b = eblk[j] - w0;
+                if (eblk[j] >= 0 && ((active >> erow[j]) & 1u) && b >= 0 && b < kWin)
+                    atomicOr(&us.bitmap[b >> 5], 1u << (b & 31));
             }
             __syncthreads();
             {   // exclusive prefix of popcounts over the words (8 words per thread)
@@ -312,11 +330,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
                 uint32_t cnt = 0;
 #pragma unroll
                 for (int i = 0; i < per; ++i) cnt += __popc(us.bitmap[t * per + i]);
-                uint32_t x = cnt;
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint32_t y = __shfl_up(x, o);
-                    if (lane >= o) x += y;
-                }
+                const uint32_t x = wave_incl_scan(cnt);
                 __shared__ uint32_t wsum[4];
                 if (lane == 63) wsum[wave] = x;
                 __syncthreads();
@@ -340,17 +354,13 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
                 }
             }
             __syncthreads();
-            for (int r = 0; r < nrows; ++r) {
-                if (!((active >> r) & 1u)) continue;
-                const int32_t c = min(a.sel_count[row0 + r], a.top_k);
-                const int32_t *sl = a.sel_blocks + (row0 + r) * a.top_k;
-                for (int i = t; i < c; i += blockDim.x) {
-                    const int32_t b = sl[i] - w0;
-                    if (b >= 0 && b < kWin) {
-                        const uint32_t word = us.bitmap[b >> 5];
-                        const uint32_t idx = us.wprefix[b >> 5] + __popc(word & ((1u << (b & 31)) - 1u));
-                        atomicOr(&us.mask[idx], 1u << r);
-                    }
+#pragma unroll
+            for (int j = 0; j < kSelPerThread; ++j) {
+                const int32_t b = eblk[j] - w0;
+                if (eblk[j] >= 0 && ((active >> erow[j]) & 1u) && b >= 0 && b < kWin) {
+                    const uint32_t word = us.bitmap[b >> 5];
+                    const uint32_t idx = us.wprefix[b >> 5] + __popc(word & ((1u << (b & 31)) - 1u));
+                    atomicOr(&us.mask[idx], 1u << erow[j]);
                 }
             }
             __syncthreads();
@@ -385,7 +395,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
             uint32_t msk = 0;
             for (int r = 0; r < nrows && n <= t; ++r) {
                 if (!((active >> r) & 1u)) continue;
-                const int32_t tr = a.row_pos[row0 + r];
+                const int32_t tr = s_pos[r];
                 const int32_t ts = (int32_t)(kBlock * visible_blocks(tr));
                 const int len = tr - ts + 1;  // 0..3
                 if (t < n + len) {
@@ -401,7 +411,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
         int ntail = 0;
         for (int r = 0; r < nrows; ++r) {
             if (!((active >> r) & 1u)) continue;
-            const int32_t tr = a.row_pos[row0 + r];
+            const int32_t tr = s_pos[r];
             ntail += tr - (int32_t)(kBlock * visible_blocks(tr)) + 1;
         }
         ntail = min(ntail, kCh);  // at most 16 rows x 3 tokens
