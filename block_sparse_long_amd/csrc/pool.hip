@@ -9,10 +9,25 @@
 // different phases.  The index queries are rotated at their own positions
 // (reading: the pages use RoPE in the indexer but do not spell out the query
 // side; without it a score would not depend on the query's position).
+#include <cmath>
+
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
 namespace qsa {
+
+// RoPE frequencies theta^(-j/64) of the 64 rotary pairs, formed once on the
+// host in double precision and passed by value.
+struct RopeFreq {
+    double f[kHalf];
+};
+
+static RopeFreq rope_freq(double theta)
+{
+    RopeFreq r;
+    for (int j = 0; j < kHalf; ++j) r.f[j] = std::pow(theta, -(double)j / (double)kHalf);
+    return r;
+}
 
 // One wave per pooled block: lane j owns the rotary pair (j, j + 64).  The
 // wave reads the block's 4 tokens x 128 dims (contiguous in memory) with 8
@@ -21,11 +36,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ raw, int64_t raw_stride,
                                                         T *__restrict__ pooled, int64_t pooled_stride,
                                                         int64_t total, int32_t nblk, int32_t block_begin,
-                                                        double theta, uint32_t flags)
+                                                        RopeFreq rf, uint32_t flags)
 {
-    __shared__ double inv_freq[kHalf];
-    if (threadIdx.x < kHalf) inv_freq[threadIdx.x] = pow(theta, -(double)threadIdx.x / (double)kHalf);
-    __syncthreads();
     const int lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (w >= total) return;
@@ -47,7 +59,7 @@ __global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ ra
         dx *= inv;
         dy *= inv;
     }
-    if (!(flags & kFlagNoRope)) rope_pair(dx, dy, kBlock * b, inv_freq[lane]);
+    if (!(flags & kFlagNoRope)) rope_pair(dx, dy, kBlock * b, rf.f[lane]);
     T *dst = pooled + s * pooled_stride + b * kDim;
     store_f64(dst + lane, dx);
     store_f64(dst + kHalf + lane, dy);
@@ -58,13 +70,10 @@ __global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ ra
 // row's 4 waves a quarter), so the selection needs no separate fill.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_query_kernel(const T *__restrict__ q, const int32_t *__restrict__ row_pos,
-                                                         int32_t rows, T *__restrict__ qrot, double theta,
+                                                         int32_t rows, T *__restrict__ qrot, RopeFreq rf,
                                                          uint32_t flags, uint32_t *__restrict__ zero,
                                                          int64_t zero_per_row)
 {
-    __shared__ double inv_freq[kHalf];
-    if (threadIdx.x < kHalf) inv_freq[threadIdx.x] = pow(theta, -(double)threadIdx.x / (double)kHalf);
-    __syncthreads();
     const int lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (w >= (int64_t)rows * kIdxHeads) return;
@@ -76,7 +85,7 @@ __global__ __launch_bounds__(256) void rope_query_kernel(const T *__restrict__ q
     }
     const T *src = q + w * kDim;
     double dx = load_f32(src + lane), dy = load_f32(src + kHalf + lane);
-    if (!(flags & kFlagNoRope)) rope_pair(dx, dy, row_pos[r], inv_freq[lane]);
+    if (!(flags & kFlagNoRope)) rope_pair(dx, dy, row_pos[r], rf.f[lane]);
     store_f64(qrot + w * kDim + lane, dx);
     store_f64(qrot + w * kDim + kHalf + lane, dy);
 }
@@ -88,12 +97,13 @@ void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pool
     const int32_t nblk = block_end - block_begin;
     const int64_t total = (int64_t)batch * nblk;
     const dim3 grid((unsigned)((total + 3) / 4)), block(256);
+    const RopeFreq rf = rope_freq(theta);
     if (bf16)
         QSA_LAUNCH("pool_rope", (pool_rope_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)raw,
-                   raw_stride, (bf16_t *)pooled, pooled_stride, total, nblk, block_begin, theta, flags);
+                   raw_stride, (bf16_t *)pooled, pooled_stride, total, nblk, block_begin, rf, flags);
     else
         QSA_LAUNCH("pool_rope", (pool_rope_kernel<float>), grid, block, 0, stream, (const float *)raw, raw_stride,
-                   (float *)pooled, pooled_stride, total, nblk, block_begin, theta, flags);
+                   (float *)pooled, pooled_stride, total, nblk, block_begin, rf, flags);
 }
 
 void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,
@@ -101,12 +111,13 @@ void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void
 {
     const int64_t waves = (int64_t)rows * kIdxHeads;
     const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    const RopeFreq rf = rope_freq(theta);
     if (bf16)
         QSA_LAUNCH("rope_query", (rope_query_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)q, row_pos,
-                   rows, (bf16_t *)qrot, theta, flags, zero, zero_per_row);
+                   rows, (bf16_t *)qrot, rf, flags, zero, zero_per_row);
     else
         QSA_LAUNCH("rope_query", (rope_query_kernel<float>), grid, block, 0, stream, (const float *)q, row_pos,
-                   rows, (float *)qrot, theta, flags, zero, zero_per_row);
+                   rows, (float *)qrot, rf, flags, zero, zero_per_row);
 }
 
 }  // namespace qsa

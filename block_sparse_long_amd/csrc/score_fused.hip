@@ -672,13 +672,18 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
             const uint32_t chunk = __shfl(off, 63);
             off = n + off - c;
             const uint2 *src = lists + (int64_t)min(li, nlists - 1) * a.subcap;
-            for (uint32_t j = 0; j < cmax; j += 16) {  // 16 loads in flight per lane
-                uint2 e[16];
+            // 16-byte loads, two pairs each, 8 in flight per lane (a list's
+            // capacity is a multiple of 8 pairs, so a load never leaves it)
+            for (uint32_t j = 0; j < cmax; j += 16) {
+                uint4 e[8];
 #pragma unroll
-                for (int q = 0; q < 16; ++q) e[q] = j + q < c ? src[j + q] : make_uint2(0u, 0u);
+                for (int q = 0; q < 8; ++q)
+                    e[q] = j + 2 * q < c ? ((const uint4 *)src)[(j >> 1) + q] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    if (j + q < c) st[off + j + q] = e[q];
+                for (int q = 0; q < 8; ++q) {
+                    if (j + 2 * q < c) st[off + j + 2 * q] = make_uint2(e[q].x, e[q].y);
+                    if (j + 2 * q + 1 < c) st[off + j + 2 * q + 1] = make_uint2(e[q].z, e[q].w);
+                }
             }
             n += chunk;
         }

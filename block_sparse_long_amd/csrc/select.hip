@@ -26,6 +26,10 @@ constexpr int kSplitThreads = 256;
 constexpr int kCollectChunk = 4096;  // blocks per collect workgroup
 constexpr int kCandStage = 3072;     // candidates the final pass keeps in LDS
 constexpr int kEmitWords = 8192;     // bitmap window of the final pass: 262,144 blocks
+// Word w of the final pass's bitmap sits at w + w/32, so the 64 lanes of a
+// wave walking their own runs of 32 words hit distinct LDS banks.
+constexpr int kEmitSlots = kEmitWords + kEmitWords / 32;
+__device__ __forceinline__ int emit_slot(int w) { return w + (w >> 5); }
 
 // Reported score s = raw / sqrt(128) (the score equation's scale), divided in
 // double and rounded once to float.
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(kSplitThreads) void select_final_kernel(
 {
     __shared__ uint64_t buf[QSA_MAX_TOP_K];
     __shared__ uint2 cst[kCandStage];
-    __shared__ uint32_t bm[kEmitWords];
+    __shared__ uint32_t bm[kEmitSlots];
     __shared__ uint32_t dhist[256];
     __shared__ uint32_t wtot[kSplitThreads / kWave];
     __shared__ uint32_t s_digit, s_dabove, s_dcnt, s_fill, s_total;
@@ -314,22 +318,22 @@ __global__ __launch_bounds__(kSplitThreads) void select_final_kernel(
     uint32_t out_base = 0;
     for (int64_t w0 = 0; w0 < nc; w0 += 32 * kEmitWords) {
         const int nwords = (int)min((int64_t)kEmitWords, (nc - w0 + 31) / 32);
-        for (int i = t; i < nwords; i += kSplitThreads) bm[i] = 0u;
+        for (int i = t; i < emit_slot(nwords); i += kSplitThreads) bm[i] = 0u;
         __syncthreads();
         for (uint32_t i = t; i < n; i += kSplitThreads) {
             const int64_t b = (int64_t)(buf[i] >> 32) - w0;
-            if (b >= 0 && b < 32 * (int64_t)nwords) atomicOr(&bm[b >> 5], 1u << (b & 31));
+            if (b >= 0 && b < 32 * (int64_t)nwords) atomicOr(&bm[emit_slot((int)(b >> 5))], 1u << (b & 31));
         }
         __syncthreads();
         const int per = (nwords + kSplitThreads - 1) / kSplitThreads;
         const int i0 = min(nwords, t * per), i1 = min(nwords, i0 + per);
         uint32_t c = 0;
-        for (int i = i0; i < i1; ++i) c += (uint32_t)__popc(bm[i]);
+        for (int i = i0; i < i1; ++i) c += (uint32_t)__popc(bm[emit_slot(i)]);
         const uint32_t incl = wg_inclusive_scan<kSplitThreads>(c, wtot);
         if (t == kSplitThreads - 1) s_total = incl;
         uint32_t pos = out_base + incl - c;
         for (int i = i0; i < i1; ++i) {
-            uint32_t word = bm[i];
+            uint32_t word = bm[emit_slot(i)];
             while (word) {
                 const int bit = __ffs(word) - 1;
                 word &= word - 1u;
