@@ -48,6 +48,16 @@ constexpr int kWinWords = kWin / 32;
 constexpr int kMaxUnionBlocks = 4096;  // rows per tile x top_k is kept at or below this
 constexpr int kMaxTileRows = 16;       // row masks are 16 bits
 
+// Column of chunk position p in a V^T row.  The P V MFMA of 32-position step
+// i takes, in lane group g, positions 32i + 4g .. +3 and 32i + 16 + 4g .. +3;
+// they are stored side by side at 32i + 8g .. +7, so one 16-byte read fetches
+// the lane's B operand.
+__device__ __forceinline__ int vt_col(int p)
+{
+    const int i = p >> 5, h = (p >> 4) & 1, g = (p >> 2) & 3, j = p & 3;
+    return 32 * i + 8 * g + 4 * h + j;
+}
+
 struct alignas(16) ChunkSmem {
     bf16_t k[kCh][kKRow];
     bf16_t vt[kDim][kVRow];
@@ -76,6 +86,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 // than kLazy: until then P = 2^(s - m) <= 2^kLazy, and O and l keep their
 // scale (the final O / l and lse = m + log2(l) are the same either way).
 constexpr float kLazy = 8.0f;
+constexpr float kNoMax = -1.0e30f;  // reference max before a query's first logit: finite, so 2^(-inf - m) = 0
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -124,16 +135,18 @@ __device__ __forceinline__ void chunk_store(ChunkSmem &cs, const ChunkRegs &cr)
     const int p = t >> 2, dk = (t & 3) * 32;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *(uint4 *)&cs.k[p][dk + 8 * i] = cr.k[i];
-    // the 16 lanes sharing dv write 16 consecutive 8-byte pieces of a V^T row
-    const int p0 = (t & 15) * 4, dv = (t >> 4) * 8;
+    // the 16 lanes sharing dv write 16 distinct 8-byte pieces of a V^T row;
+    // position p0 + j is stored at vt_col(p0) + j
+    const int q = t & 15, dv = (t >> 4) * 8;
+    const int c0 = vt_col(4 * q);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {  // dims dv + 2w (low halves) and dv + 2w + 1 (high halves)
         uint32_t x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = w == 0 ? cr.v[i].x : w == 1 ? cr.v[i].y : w == 2 ? cr.v[i].z : cr.v[i].w;
-        *(uint2 *)&cs.vt[dv + 2 * w][p0] = make_uint2(__builtin_amdgcn_perm(x[1], x[0], 0x05040100u),
+        *(uint2 *)&cs.vt[dv + 2 * w][c0] = make_uint2(__builtin_amdgcn_perm(x[1], x[0], 0x05040100u),
                                                       __builtin_amdgcn_perm(x[3], x[2], 0x05040100u));
-        *(uint2 *)&cs.vt[dv + 2 * w + 1][p0] = make_uint2(__builtin_amdgcn_perm(x[1], x[0], 0x07060302u),
+        *(uint2 *)&cs.vt[dv + 2 * w + 1][c0] = make_uint2(__builtin_amdgcn_perm(x[1], x[0], 0x07060302u),
                                                           __builtin_amdgcn_perm(x[3], x[2], 0x07060302u));
     }
 }
@@ -181,9 +194,9 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, const bf16x8_t (
         for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, s[sub][j]);
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const bool raise = cmax > st.m + kLazy;  // also the first logit of a query (st.m = -inf)
+    const bool raise = cmax > st.m + kLazy;  // also the first logit of a query (st.m = kNoMax)
     const float m_ref = raise ? cmax : st.m;
-    if (__ballot(raise && st.m != -INFINITY)) {  // some query's O and l change scale
+    if (__ballot(raise && st.m != kNoMax)) {  // some query's O and l change scale
         const float alpha = raise ? __builtin_amdgcn_exp2f(st.m - m_ref) : 1.0f;
         st.l *= alpha;
         float a4[4];
@@ -200,8 +213,8 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, const bf16x8_t (
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            p[sub][j] = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s[sub][j] - m_ref);
+        for (int j = 0; j < 4; ++j) {  // a masked logit (-inf) gives 0; m_ref is finite
+            p[sub][j] = __builtin_amdgcn_exp2f(s[sub][j] - m_ref);
             psum += p[sub][j];
         }
     st.l += psum;  // per-lane partial; the 4 groups are summed at the end
@@ -215,10 +228,7 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, const bf16x8_t (
         const bf16x8_t A = as_bf16x8(pa);
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
-            const bf16_t *row = &cs.vt[16 * nt + m16][0];
-            const uint2 lo = *(const uint2 *)(row + 32 * i + 4 * g);
-            const uint2 hi = *(const uint2 *)(row + 32 * i + 16 + 4 * g);
-            const bf16x8_t Bv = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+            const bf16x8_t Bv = as_bf16x8(*(const uint4 *)&cs.vt[16 * nt + m16][32 * i + 8 * g]);
             st.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv, st.o[nt], 0, 0, 0);
         }
     }
@@ -236,7 +246,7 @@ __device__ __forceinline__ void init_state(WaveState &st)
 {
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) st.o[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    st.m = -INFINITY;
+    st.m = kNoMax;
     st.l = 0.0f;
 }
 
