@@ -83,27 +83,31 @@ __device__ __forceinline__ void load_query_tile(const bf16_t *__restrict__ qrot,
 }
 
 // Scores of one 64-block tile in LDS: sc[mt][nt] = raw(row 16*wave + 4*mt + g,
-// block nt*16 + m of the tile).  Four independent accumulator chains.
+// block nt*16 + m of the tile).  Four independent accumulator chains per
+// 16-block slice; a slice's ReLU-sums are interleaved with the next slice's
+// MFMAs.
 __device__ __forceinline__ void tile_scores(const bf16_t (*keys)[kFKRow], const bf16x8_t (&qa)[4][4],
                                             float (&sc)[4][4])
 {
     const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    f32x4_t acc[2][4];  // slice nt's accumulators; slice nt-1's ReLU-sums run between its MFMAs
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
         bf16x8_t bk[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) bk[s] = as_bf16x8(*(const uint4 *)&keys[nt * 16 + m][32 * g + 8 * s]);
-        f32x4_t acc[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int mt = 0; mt < 4; ++mt) acc[nt & 1][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], bk[s], acc[mt], 0, 0, 0);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) sc[mt][nt] = relu_sum4f(acc[mt]);
+                acc[nt & 1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], bk[s], acc[nt & 1][mt], 0, 0, 0);
+            if (nt > 0) sc[s][nt - 1] = relu_sum4f(acc[(nt - 1) & 1][s]);  // row tile s of the previous slice
+        }
     }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) sc[mt][3] = relu_sum4f(acc[1][mt]);
 }
 
 // Rows of one sequence at a time: the next group of the workgroup's rows
