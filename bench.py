@@ -167,7 +167,7 @@ def timed(run_step, steps, warmup):
     return (time.perf_counter() - t0) / steps * 1e3
 
 
-ALL_KERNELS = ["pool_rope", "rope_query", "score_rows_bf16", "score_rows_f32", "score_gemm_bf16", "select_rows",
+ALL_KERNELS = ["pool_rope", "pool_append", "rope_query", "score_rows_bf16", "score_rows_f32", "score_gemm_bf16", "select_rows",
                "select_collect", "select_final", "score_sample", "sample_threshold", "score_filter", "select_merge", "attn_prefill_mfma", "attn_decode_mfma",
                "attn_prefill", "attn_decode", "attn_combine"]
 
@@ -309,9 +309,43 @@ def bench_decode(spec, steps, warmup, cpu_baseline, copies=3):
     res = {"workload": spec.name, "value": rows / (ms * 1e-3), "unit": "query rows/s", "ms_per_step": ms,
            "kernels": kernels, "roofline": roofline_for(dom, work[dom], kt[dom][1], tr),
            "rooflines": {n: roofline_for(n, work[n], kt[n][1], tr) for n in kt if n in work}}
+    res["pool_append"] = bench_pool_append(spec)
     if cpu_baseline:
         res["cpu_baseline"] = cpu_decode(spec, w, pooled_h)
     return res
+
+
+def bench_pool_append(spec, launches=50):
+    """Incremental decode pooling for the workload's batch: every launch
+    completes a block for every request (the costlier case), with the
+    compressed keys in a paged layout.  Per-launch time from the library's
+    hipEvents; bytes are what the step must move (new key in, 3 ring keys
+    in, ring slot and compressed key out)."""
+    import torch
+    from block_sparse_long_amd import qsa, synth
+    B = spec.batch
+    dt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    rng = np.random.default_rng(7)
+    slots = torch.from_numpy(synth.paged_slots(rng, B, 4 * launches, 16)).cuda()
+    keys = torch.randn((launches, B, DIM), device="cuda").to(dt)
+    ring = torch.zeros((B, 4, DIM), dtype=dt, device="cuda")
+    comp = torch.zeros((int(slots.max().item()) // 4 + 1, DIM), dtype=dt, device="cuda")
+    pos = torch.full((B,), spec.ctx + 3, dtype=torch.int32, device="cuda")
+    fs = [slots[:, 4 * j + 3].contiguous() for j in range(launches)]
+    for j in range(3):
+        qsa.pool_append(keys[j], pos, fs[j], ring, comp, spec.theta)
+    torch.cuda.synchronize()
+    qsa.profile_reset()
+    qsa.profile_enable(True)
+    for j in range(launches):
+        qsa.pool_append(keys[j], pos, fs[j], ring, comp, spec.theta)
+    torch.cuda.synchronize()
+    qsa.profile_enable(False)
+    n, tot = qsa.profile_kernel_ms("pool_append")
+    qsa.profile_reset()
+    eb = 2 if spec.dtype == "bf16" else 4
+    return {"batch": B, "avg_us": round(tot / max(n, 1) * 1e3, 2), "bytes_per_launch": B * 6 * DIM * eb,
+            "bound": "latency"}
 
 
 def cpu_decode(spec, w, pooled_h):
@@ -338,7 +372,7 @@ def cpu_decode(spec, w, pooled_h):
 
 CSRC = os.path.join(ROOT, "block_sparse_long_amd", "csrc")
 HEADERS = ["qsa_internal.h", "qsa_device.h", "qsa_wg.h"]
-KERNEL_SOURCE = {"pool_rope": "pool.hip", "rope_query": "pool.hip", "score_rows_bf16": "score.hip",
+KERNEL_SOURCE = {"pool_rope": "pool.hip", "pool_append": "pool.hip", "rope_query": "pool.hip", "score_rows_bf16": "score.hip",
                  "score_rows_f32": "score.hip", "score_gemm_bf16": "score.hip", "select_rows": "select.hip",
                  "select_collect": "select.hip", "select_final": "select.hip", "score_sample": "score_fused.hip",
                  "sample_threshold": "score_fused.hip", "score_filter": "score_fused.hip",

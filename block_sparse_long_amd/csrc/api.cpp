@@ -198,6 +198,23 @@ qsa_status_t qsa_pool_index_keys(const void *raw_keys, int64_t raw_seq_stride, v
     return launch_status();
 }
 
+qsa_status_t qsa_pool_append(const void *new_keys, const int32_t *positions, const int64_t *full_slots, void *ring,
+                             void *compressed, int32_t batch, double rope_theta, uint32_t flags, qsa_dtype_t dtype,
+                             void *stream)
+{
+    if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
+    if (batch < 0) return QSA_ERR_INVALID_ARG;
+    if (flags & ~(uint32_t)(QSA_FLAG_NO_ROPE | QSA_FLAG_POOL_RMSNORM)) return QSA_ERR_INVALID_ARG;
+    if (!(flags & QSA_FLAG_NO_ROPE) && !(rope_theta > 1.0 && std::isfinite(rope_theta))) return QSA_ERR_INVALID_ARG;
+    if (batch == 0) return QSA_OK;
+    if (!aligned16(new_keys) || !aligned16(ring) || !aligned16(compressed) || !positions || !full_slots)
+        return QSA_ERR_INVALID_ARG;
+    clear_launch_err();
+    launch_pool_append(new_keys, positions, full_slots, ring, compressed, batch, rope_theta, flags, dtype == QSA_BF16,
+                       (hipStream_t)stream);
+    return launch_status();
+}
+
 size_t qsa_score_topk_workspace_size(int32_t rows, int32_t max_visible_blocks, int32_t top_k, qsa_dtype_t dtype,
                                      uint32_t flags)
 {

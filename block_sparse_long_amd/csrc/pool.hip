@@ -90,6 +90,68 @@ __global__ __launch_bounds__(256) void rope_query_kernel(const T *__restrict__ q
     store_f64(qrot + w * kDim + kHalf + lane, dy);
 }
 
+// Incremental pooling for decode: one wave per request.  The new raw key goes
+// to ring slot t mod 4; when it completes block b = t / 4, the four ring keys
+// (slots 0..3 are tokens 4b..4b+3; slot 3 is the new key, taken from
+// registers) are pooled in FP32 token order, rotated at 4b and stored at
+// compressed slot full_slot / 4.  "Qwen3.8-Flash-Next: Day-0 Support in
+// SGLang", section "Qwen Sparse Attention": the raw keys of the unfinished
+// block live in a four-slot per-request ring, and page-aligned full_slot / 4
+// addressing places the compressed key.
+template <typename T>
+__global__ __launch_bounds__(256) void pool_append_kernel(const T *__restrict__ new_keys,
+                                                          const int32_t *__restrict__ positions,
+                                                          const int64_t *__restrict__ full_slots, T *__restrict__ ring,
+                                                          T *__restrict__ compressed, int32_t batch, RopeFreq rf,
+                                                          uint32_t flags)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (r >= batch) return;
+    const int64_t t = positions[r];
+    const int slot = (int)(t & (kBlock - 1));
+    const T *src = new_keys + r * kDim;
+    const T kx = src[lane], ky = src[kHalf + lane];
+    T *rr = ring + r * kBlock * kDim;
+    rr[slot * kDim + lane] = kx;
+    rr[slot * kDim + kHalf + lane] = ky;
+    if (slot != kBlock - 1) return;
+    float x = 0.0f, y = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kBlock - 1; ++i) {  // FP32 sum in token order, then times 1/4
+        x += load_f32(rr + i * kDim + lane);
+        y += load_f32(rr + i * kDim + kHalf + lane);
+    }
+    x += load_f32(&kx);
+    y += load_f32(&ky);
+    x *= 0.25f;
+    y *= 0.25f;
+    double dx = x, dy = y;
+    if (flags & kFlagRmsNorm) {
+        const double ss = wave_sum_f64(dx * dx + dy * dy);
+        const double inv = 1.0 / sqrt(ss / (double)kDim + 1e-6);
+        dx *= inv;
+        dy *= inv;
+    }
+    if (!(flags & kFlagNoRope)) rope_pair(dx, dy, t - slot, rf.f[lane]);
+    T *dst = compressed + (full_slots[r] / kBlock) * kDim;
+    store_f64(dst + lane, dx);
+    store_f64(dst + kHalf + lane, dy);
+}
+
+void launch_pool_append(const void *new_keys, const int32_t *positions, const int64_t *full_slots, void *ring,
+                        void *compressed, int32_t batch, double theta, uint32_t flags, bool bf16, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((batch + 3) / 4)), block(256);
+    const RopeFreq rf = rope_freq(theta);
+    if (bf16)
+        QSA_LAUNCH("pool_append", (pool_append_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)new_keys,
+                   positions, full_slots, (bf16_t *)ring, (bf16_t *)compressed, batch, rf, flags);
+    else
+        QSA_LAUNCH("pool_append", (pool_append_kernel<float>), grid, block, 0, stream, (const float *)new_keys,
+                   positions, full_slots, (float *)ring, (float *)compressed, batch, rf, flags);
+}
+
 void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pooled_stride, int32_t batch,
                  int32_t block_begin, int32_t block_end, double theta, uint32_t flags, bool bf16,
                  hipStream_t stream)

@@ -27,6 +27,8 @@ void note_launch(hipError_t err);
 void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pooled_stride, int32_t batch,
                  int32_t block_begin, int32_t block_end, double theta, uint32_t flags, bool bf16,
                  hipStream_t stream);
+void launch_pool_append(const void *new_keys, const int32_t *positions, const int64_t *full_slots, void *ring,
+                        void *compressed, int32_t batch, double theta, uint32_t flags, bool bf16, hipStream_t stream);
 void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,
                        uint32_t flags, bool bf16, uint32_t *zero, int64_t zero_per_row, hipStream_t stream);
 

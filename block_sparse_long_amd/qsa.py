@@ -25,7 +25,7 @@ FLAG_SCORE_GEMM = 1 << 9
 INDEX_DIM, INDEX_HEADS, BLOCK_TOKENS, MAX_TOP_K, MAX_QUERY_GROUP = 128, 4, 4, 4096, 64
 
 # every symbol include/qsa.h declares
-EXPORTS = ("qsa_pool_index_keys", "qsa_score_topk_workspace_size", "qsa_score_topk",
+EXPORTS = ("qsa_pool_index_keys", "qsa_pool_append", "qsa_score_topk_workspace_size", "qsa_score_topk",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode_workspace_size",
            "qsa_sparse_attn_decode", "qsa_status_string", "qsa_last_device_error", "qsa_profile_enable",
            "qsa_profile_reset", "qsa_profile_kernel_ms")
@@ -63,6 +63,8 @@ def load():
     st = ctypes.c_int
     lib.qsa_pool_index_keys.argtypes = [P, i64, P, i64, i32, i32, i32, f64, u32, st, P]
     lib.qsa_pool_index_keys.restype = st
+    lib.qsa_pool_append.argtypes = [P, P, P, P, P, i32, f64, u32, st, P]
+    lib.qsa_pool_append.restype = st
     lib.qsa_score_topk_workspace_size.argtypes = [i32, i32, i32, st, u32]
     lib.qsa_score_topk_workspace_size.restype = sz
     lib.qsa_score_topk.argtypes = [P, P, P, i32, P, i64, i32, i32, f64, u32, st, P, P, P, P, sz, P]
@@ -139,6 +141,18 @@ def pool_index_keys(raw_keys, pooled, block_begin: int, block_end: int, rope_the
                                     pooled.shape[1] * INDEX_DIM, B, int(block_begin), int(block_end),
                                     float(rope_theta), int(flags), _dtype_code(raw_keys), _stream(stream))
     _check("qsa_pool_index_keys", rc)
+
+
+def pool_append(new_keys, positions, full_slots, ring, compressed, rope_theta: float, flags: int = 0,
+                stream=None):
+    """One decode step of incremental pooling: new_keys [B][128] into the
+    4-slot rings [B][4][128]; a completed block's compressed key goes to
+    compressed [S][128] at full_slots // 4 (positions int32, full_slots int64)."""
+    _need_contig(new_keys, positions, full_slots, ring, compressed)
+    rc = load().qsa_pool_append(_ptr(new_keys), _ptr(positions), _ptr(full_slots), _ptr(ring), _ptr(compressed),
+                                new_keys.shape[0], float(rope_theta), int(flags), _dtype_code(new_keys),
+                                _stream(stream))
+    _check("qsa_pool_append", rc)
 
 
 def score_topk_workspace_size(rows: int, max_visible_blocks: int, top_k: int, dtype_code: int,

@@ -243,6 +243,19 @@ def make(spec: Spec, seed: Optional[int] = None) -> dict:
     return out
 
 
+def paged_slots(rng, batch: int, length: int, page_tokens: int = 16) -> np.ndarray:
+    """Physical KV slots [batch][length] of a paged pool: each request's
+    token t sits in page pages[r][t // page_tokens] at offset
+    t % page_tokens; the pages of all requests are a random permutation of
+    batch * ceil(length / page_tokens) pages.  page_tokens is a multiple of
+    4, so the 4 tokens of a block share a page (page-aligned slots)."""
+    assert page_tokens % BLOCK == 0
+    npg = (length + page_tokens - 1) // page_tokens
+    pages = rng.permutation(batch * npg).reshape(batch, npg).astype(np.int64)
+    t = np.arange(length, dtype=np.int64)
+    return pages[:, t // page_tokens] * page_tokens + (t % page_tokens)[None, :]
+
+
 def to_float(x: np.ndarray, spec: Spec) -> np.ndarray:
     """Storage format -> float32 values."""
     return _from_storage(x, spec.dtype)

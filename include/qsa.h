@@ -99,6 +99,31 @@ qsa_status_t qsa_pool_index_keys(const void *raw_keys, int64_t raw_seq_stride, v
                                  qsa_dtype_t dtype, void *stream);
 
 /*
+ * Incremental pooling for decode ([SGL] section "Qwen Sparse Attention": the
+ * raw index keys of a request's unfinished block live in a four-slot
+ * per-request ring, and the compressed cache is addressed by page-aligned
+ * full_slot / 4).  For each request r, with its new token at position
+ * t = positions[r] and physical KV slot full_slots[r]:
+ *   - ring[r][t mod 4] = new_keys[r];
+ *   - if t mod 4 == 3 (block b = t / 4 is complete): the four ring keys, which
+ *     are tokens 4b..4b+3, are pooled exactly as qsa_pool_index_keys pools a
+ *     block (FP32 sum in token order times 1/4, QSA_FLAG_POOL_RMSNORM, RoPE
+ *     at position 4b unless QSA_FLAG_NO_ROPE, rounding to dtype) and stored
+ *     at compressed[full_slots[r] / 4].
+ *   new_keys   [batch][128], read only.
+ *   positions  [batch] int32 (device), t >= 0.
+ *   full_slots [batch] int64 (device).  Contract: pages are aligned to 4
+ *              tokens, so full_slots[r] mod 4 == t mod 4 and the block's four
+ *              tokens share compressed slot full_slots[r] / 4.  Not checked.
+ *   ring       [batch][4][128], updated in place (slot t mod 4 written).
+ *   compressed [slots][128]: one compressed key per 4 physical KV slots.
+ *   Slots and positions are the caller's; the library keeps no state.
+ */
+qsa_status_t qsa_pool_append(const void *new_keys, const int32_t *positions, const int64_t *full_slots,
+                             void *ring, void *compressed, int32_t batch, double rope_theta, uint32_t flags,
+                             qsa_dtype_t dtype, void *stream);
+
+/*
  * Bytes of device workspace qsa_score_topk needs for `rows` rows whose visible
  * block counts are at most `max_visible_blocks`, with the same `flags` the
  * call will get (the scoring kernel decides the layout).  0 when rows == 0 or

@@ -60,6 +60,8 @@ def _load():
     lib.qsa_oracle_rope.restype = None
     lib.qsa_oracle_pool.argtypes = [P, i64, P, i64, i32, i32, i32, f64, u32, i32]
     lib.qsa_oracle_pool.restype = ctypes.c_int
+    lib.qsa_oracle_pool_append.argtypes = [P, P, P, P, P, i32, f64, u32, i32]
+    lib.qsa_oracle_pool_append.restype = ctypes.c_int
     lib.qsa_oracle_score_topk.argtypes = [P, P, P, i32, P, i64, i32, f64, u32, i32, P, P, P, P, i64]
     lib.qsa_oracle_score_topk.restype = ctypes.c_int
     lib.qsa_oracle_sparse_attn_prefill.argtypes = [P, P, P, i32, P, P, i64, P, P, i32, i32, i32,
@@ -135,6 +137,25 @@ def pool(raw, block_begin: int, block_end: int, theta: float, flags: int = 0,
                                  int(block_begin), int(block_end), float(theta), int(flags), dt)
     _check(rc, "pool")
     return pooled
+
+
+def pool_append(new_keys, positions, full_slots, ring, compressed, theta: float, flags: int = 0):
+    """One decode step of incremental pooling (see qsa_oracle_pool_append):
+    writes each request's new raw key into its 4-slot ring and, when that
+    completes a block, the block's compressed key at full_slot // 4.  `ring`
+    [B][4][128] and `compressed` [S][128] are updated in place (contiguous
+    numpy arrays of the keys' dtype)."""
+    new_keys = _c(new_keys)
+    dt = _dtype_code(new_keys)
+    for arr in (ring, compressed):
+        assert arr.flags["C_CONTIGUOUS"] and arr.dtype == new_keys.dtype
+    pos = _c(positions, np.int32)
+    slots = _c(full_slots, np.int64)
+    B = new_keys.shape[0]
+    assert ring.shape == (B, 4, DIM) and pos.shape == (B,) and slots.shape == (B,)
+    assert int(slots.max(initial=-1)) // 4 < compressed.shape[0]
+    _check(_load().qsa_oracle_pool_append(_ptr(new_keys), _ptr(pos), _ptr(slots), _ptr(ring), _ptr(compressed), B,
+                                          float(theta), int(flags), dt), "pool_append")
 
 
 def score_topk(q_index, row_seq, row_pos, pooled, top_k: int, theta: float, flags: int = 0,

@@ -199,6 +199,62 @@ int qsa_oracle_pool(const void *raw, int64_t raw_seq_stride, void *pooled,
     return OR_OK;
 }
 
+/*
+ * Incremental pooling for decode ([SGL]: the raw index keys of a request's
+ * unfinished block live in a four-slot per-request ring; one compressed key
+ * per four tokens is kept, addressed by page-aligned full_slot / 4).
+ *
+ * For each request r with its new token at position t = positions[r] and
+ * physical KV slot full_slots[r]:
+ *   ring[r][t mod 4] = new_keys[r];
+ *   if t mod 4 == 3 (the block b = t / 4 is now complete), the four ring
+ *   slots -- tokens 4b .. 4b+3, in that order -- are pooled exactly as
+ *   qsa_oracle_pool pools a block (FP32 sum in token order times 1/4,
+ *   optional RMS norm, rotation at 4b, rounding to dtype) and stored at
+ *   compressed[full_slots[r] / 4].
+ * Contract (pages aligned to 4 tokens): full_slots[r] mod 4 == t mod 4, so
+ * the block's four tokens share one compressed slot.
+ * new_keys [batch][128], ring [batch][4][128], compressed [slots / 4][128].
+ */
+int qsa_oracle_pool_append(const void *new_keys, const int32_t *positions, const int64_t *full_slots, void *ring,
+                           void *compressed, int32_t batch, double theta, uint32_t flags, int32_t dtype)
+{
+    if (!new_keys || !positions || !full_slots || !ring || !compressed || batch < 0)
+        return OR_ERR_ARG;
+    for (int32_t r = 0; r < batch; ++r) {
+        const int64_t t = positions[r];
+        if (t < 0)
+            return OR_ERR_ARG;
+        const int64_t slot = t % OR_BLOCK;
+        for (int d = 0; d < OR_DIM; ++d)
+            store_elem(ring, ((int64_t)r * OR_BLOCK + slot) * OR_DIM + d, dtype,
+                       load_elem(new_keys, (int64_t)r * OR_DIM + d, dtype));
+        if (slot != OR_BLOCK - 1)
+            continue;
+        double m[OR_DIM];
+        for (int d = 0; d < OR_DIM; ++d) {
+            float acc = 0.0f;
+            for (int i = 0; i < OR_BLOCK; ++i)
+                acc += (float)load_elem(ring, ((int64_t)r * OR_BLOCK + i) * OR_DIM + d, dtype);
+            m[d] = (double)(acc * 0.25f);
+        }
+        if (flags & OR_FLAG_POOL_RMSNORM) {
+            double ss = 0.0;
+            for (int d = 0; d < OR_DIM; ++d)
+                ss += m[d] * m[d];
+            double inv = 1.0 / sqrt(ss / OR_DIM + 1e-6);
+            for (int d = 0; d < OR_DIM; ++d)
+                m[d] *= inv;
+        }
+        if (!(flags & OR_FLAG_NO_ROPE))
+            qsa_oracle_rope(m, OR_BLOCK * (t / OR_BLOCK), theta);
+        const int64_t cslot = full_slots[r] / OR_BLOCK;
+        for (int d = 0; d < OR_DIM; ++d)
+            store_elem(compressed, cslot * OR_DIM + d, dtype, m[d]);
+    }
+    return OR_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* a4-a6: query rotation, block scores, top-k selection                      */
 /* ------------------------------------------------------------------------ */

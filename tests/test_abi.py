@@ -60,6 +60,20 @@ def test_pool_validation(libqsa):
     assert f(A, 1024, B_, 256, 2, 0, 2, 1e7, 1 << 5, qsa.BF16, None) == qsa.ERR_INVALID_ARG  # flag
 
 
+def test_pool_append_validation(libqsa):
+    f = libqsa.qsa_pool_append
+    assert f(A, B_, C, A, B_, 0, 1e7, 0, qsa.BF16, None) == qsa.OK            # empty batch
+    assert f(A, B_, C, A, B_, 2, 1e7, 0, 7, None) == qsa.ERR_UNSUPPORTED
+    assert f(None, B_, C, A, B_, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG
+    assert f(MIS, B_, C, A, B_, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG  # keys not 16-byte aligned
+    assert f(A, None, C, A, B_, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG
+    assert f(A, B_, None, A, B_, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG
+    assert f(A, B_, C, A, MIS, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG
+    assert f(A, B_, C, A, B_, -1, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG
+    assert f(A, B_, C, A, B_, 2, 0.5, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG     # theta
+    assert f(A, B_, C, A, B_, 2, 1e7, 1 << 8, qsa.BF16, None) == qsa.ERR_INVALID_ARG  # a score flag
+
+
 def test_score_topk_validation(libqsa):
     f = libqsa.qsa_score_topk
     ws = qsa.score_topk_workspace_size(4, 100, 16, qsa.BF16)

@@ -196,6 +196,62 @@ def test_pool_rotates_after_pooling_at_first_token():
     assert np.abs(got - late).max() > 1e-2
 
 
+def _stream_append(raw, slots, theta, flags=0, starts=None):
+    """Feed each request's tokens one decode step at a time through the ring."""
+    B, L, _ = raw.shape
+    ring = np.zeros((B, 4, DIM), raw.dtype)
+    sentinel = synth.bf16_bits(np.float32(-7.0)) if raw.dtype == np.uint16 else np.float32(-7.0)
+    comp = np.full((int(slots.max()) // 4 + 1, DIM), sentinel, raw.dtype)
+    starts = np.zeros(B, np.int64) if starts is None else starts
+    for step in range(L):
+        t = np.minimum(starts + step, L - 1)  # requests that finished repeat their last token harmlessly
+        live = starts + step < L
+        if not live.any():
+            break
+        r = np.nonzero(live)[0]
+        oracle.pool_append(raw[r, t[r]], t[r].astype(np.int32), slots[r, t[r]], ring_sub := ring[r].copy(), comp,
+                           theta, flags)
+        ring[r] = ring_sub
+    return ring, comp, sentinel
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("flags", [0, oracle.FLAG_POOL_RMSNORM])
+def test_pool_append_stream_equals_whole_sequence_pool(dtype, flags):
+    # [SGL]: raw keys of the unfinished block live in a 4-slot ring; the
+    # compressed key of a finished block sits at page-aligned full_slot / 4.
+    # Streaming the tokens through the ring must give, slot for slot, the
+    # (separately pinned) pooling of the whole sequence.
+    rng = np.random.default_rng(21)
+    B, L = 3, 47                                   # 11 complete blocks + 3 tokens
+    x = rng.standard_normal((B, L, DIM)).astype(np.float32)
+    raw = synth.bf16_bits(x) if dtype == "bf16" else x
+    slots = synth.paged_slots(rng, B, L, page_tokens=16)
+    ring, comp, sentinel = _stream_append(raw, slots, 1e7, flags)
+    whole = oracle.pool(raw, 0, L // 4, 1e7, flags=flags)
+    for r in range(B):
+        for b in range(L // 4):
+            np.testing.assert_array_equal(comp[slots[r, 4 * b] // 4], whole[r, b])
+        # the unfinished block has no compressed key yet; the ring holds its tokens
+        assert (comp[slots[r, 4 * (L // 4)] // 4] == sentinel).all()
+        for t in range(4 * (L // 4), L):
+            np.testing.assert_array_equal(ring[r, t % 4], raw[r, t])
+
+
+def test_pool_append_constant_keys_give_rotated_key():
+    # every token of a request carries the same key k: each finished block is
+    # R(4b) k (closed form), whichever page it landed in
+    rng = np.random.default_rng(22)
+    k = rng.standard_normal(DIM).astype(np.float32)
+    raw = np.broadcast_to(k, (2, 24, DIM)).copy()
+    slots = synth.paged_slots(rng, 2, 24, page_tokens=8)
+    _, comp, _ = _stream_append(raw, slots, 1e7, starts=np.array([0, 0]))
+    for r in range(2):
+        for b in range(6):
+            np.testing.assert_allclose(comp[slots[r, 4 * b] // 4], oracle.rope(k.astype(np.float64), 4 * b, 1e7),
+                                       rtol=1e-6, atol=1e-6)
+
+
 def test_pool_bf16_storage_is_rounded_fp32_result():
     rng = np.random.default_rng(6)
     raw32 = synth.bf16_to_f32(synth.bf16_bits(rng.standard_normal((1, 256, DIM)).astype(np.float32)))
