@@ -57,50 +57,71 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
     const int64_t b_begin = (int64_t)blockIdx.x * kChunk;
     if (b_begin >= nc) return;
     const int64_t b_end = min(nc, b_begin + (int64_t)kChunk);
-    if (hist) hist_clear(lhist);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: the step loop branches on scalars
     const int m = lane & 15, g = lane >> 4;
+    const bf16_t *kb = pooled + (int64_t)row_seq[r] * pooled_stride;
+    float *srow = scores + (int64_t)r * sc_stride;
+    // Each wave handles 64 consecutive blocks per step: MFMA column m of tile
+    // nt is block base + 4m + nt, so lane m of group 0 ends the step with the
+    // scores of 4 consecutive blocks and stores them at once.  Two register
+    // buffers take turns: the next step's keys are in flight during this
+    // step's MFMAs.  Every load is issued unconditionally (addresses are
+    // clamped to the last visible block), so the wait before each MFMA counts
+    // only the loads it needs and never drains the prefetch.
+    auto load = [&](int64_t base, uint4 (&v)[4][4]) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int64_t b = min(base + 4 * m + nt, b_end - 1);  // clamp: stays inside the visible range
+            const uint4 *src = (const uint4 *)(kb + b * kDim + 32 * g);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) v[nt][s] = src[s];
+        }
+    };
+    uint4 v0[4][4], v1[4][4];
+    int64_t base = b_begin + wave * 64;
+    load(base, v0);
+    if (hist) hist_clear(lhist);
     bf16x8_t a[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
         a[s] = m < kIdxHeads
                    ? as_bf16x8(*(const uint4 *)(qrot + ((int64_t)r * kIdxHeads + m) * kDim + 32 * g + 8 * s))
                    : zero_bf16x8();
-    const bf16_t *kb = pooled + (int64_t)row_seq[r] * pooled_stride;
-    float *srow = scores + (int64_t)r * sc_stride;
-    // each wave handles 64 consecutive blocks per iteration (4 column tiles);
-    // the next iteration's keys are in flight during this one's MFMAs
-    auto load = [&](int64_t base, uint4 (&v)[4][4]) {
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const int64_t b = min(base + nt * 16 + m, b_end - 1);  // clamp: stays inside the visible range
-            const uint4 *src = (const uint4 *)(kb + b * kDim + 32 * g);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) v[nt][s] = src[s];
-        }
-    };
-    uint4 v[4][4], vn[4][4];
-    int64_t base = b_begin + wave * 64;
-    if (base < b_end) load(base, v);
-    for (; base < b_end; base += 256) {
-        if (base + 256 < b_end) load(base + 256, vn);
+    auto score = [&](int64_t base, const uint4 (&v)[4][4]) {
+        float sc[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], as_bf16x8(v[nt][s]), acc, 0, 0, 0);
-            const int64_t b = base + nt * 16 + m;
-            if (g == 0 && b < b_end) {
-                const float sc = relu_sum4(acc);
-                srow[b] = sc;
-                if (hist) atomicAdd(&lhist[score_key(sc) >> kHistShift], 1u);
+            sc[nt] = relu_sum4(acc);
+        }
+        const int64_t b = base + 4 * m;
+        if (g == 0 && b < b_end) {
+            if (b + 3 < b_end) {
+                *(float4 *)(srow + b) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+            } else {
+                for (int j = 0; j < (int)(b_end - b); ++j) srow[b + j] = sc[j];
+            }
+            if (hist) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (b + j < b_end) atomicAdd(&lhist[score_key(sc[j]) >> kHistShift], 1u);
             }
         }
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) v[nt][s] = vn[nt][s];
+    };
+    // Two steps per trip and one exit test keep the loop a single uniform
+    // block; a second step past the end only re-reads the clamped last block
+    // and stores nothing.
+    for (; base < b_end; base += 512) {
+        load(base + 256, v1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the MFMAs
+        score(base, v0);
+        load(base + 512, v0);
+        __builtin_amdgcn_sched_barrier(0);
+        score(base + 256, v1);
     }
     if (hist) hist_flush(lhist, hist + (int64_t)r * kRowScratch);
 }

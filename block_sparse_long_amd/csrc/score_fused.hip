@@ -623,6 +623,41 @@ __device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n,
     }
 }
 
+// Every pair of a row's lists, read lane-parallel: lane i walks list i of
+// each group of 64 lists with 16-byte loads (two pairs each, eight in
+// flight); fn(pair, valid) sees 16 pair slots per lane and step, in the same
+// order on every lane, so it may use wave-wide ballots.
+template <typename F>
+__device__ __forceinline__ void for_each_listed(const uint2 *__restrict__ lists, const uint32_t *__restrict__ cnt,
+                                                int nlists, int32_t subcap, F &&fn)
+{
+    const int lane = threadIdx.x & 63;
+    for (int i0 = 0; i0 < nlists; i0 += kWave) {
+        const int li = i0 + lane;
+        const uint32_t c = li < nlists ? cnt[li] : 0u;
+        uint32_t cmax = c;
+        for (int o = 1; o < 64; o <<= 1) cmax = max(cmax, (uint32_t)__shfl_xor((int)cmax, o));
+        const uint4 *src = (const uint4 *)(lists + (int64_t)min(li, nlists - 1) * subcap);
+        for (uint32_t j = 0; j < cmax; j += 16) {
+            uint4 e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) e[q] = j + 2 * q < c ? src[(j >> 1) + q] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                fn(make_uint2(e[q].x, e[q].y), j + 2 * q < c);
+                fn(make_uint2(e[q].z, e[q].w), j + 2 * q + 1 < c);
+            }
+        }
+    }
+}
+
+// Histogram of a pair key's bits [30:19]: the float exponent and the top 4
+// mantissa bits of the score (every pair key carries bit 31), 1/16 octave per
+// bin; the table fills the wave's stage exactly.
+constexpr int kPreShift = 19;
+constexpr uint32_t kPreBins = 4096;
+static_assert(kPreBins * 4 == kStage * 8, "the prefilter histogram fills the stage");
+
 }  // namespace
 
 __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, int32_t *__restrict__ sel_blocks,
@@ -693,6 +728,52 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
         }
     } else if (mode == 1) {
         n = total;
+        // More pairs than the stage holds.  The histogram locates the bin of
+        // the kk-th largest key; only the pairs in or above that bin are
+        // staged.  They hold every pair the full ranking keeps (all keys above
+        // the kk-th and all keys equal to it), so merging them is exact.  A
+        // bin too crowded to stage falls through to the list-walking path.
+        uint32_t *hist = (uint32_t *)st;
+        for (uint32_t i = (uint32_t)lane; i < kPreBins; i += kWave) hist[i] = 0u;
+        wave_fence();
+        const uint32_t *lcnt = a.cnt + r * nlists;
+        for_each_listed(lists, lcnt, nlists, a.subcap, [&](uint2 e, bool v) {
+            if (v) atomicAdd(&hist[(e.x >> kPreShift) & (kPreBins - 1u)], 1u);
+        });
+        wave_fence();
+        // lane l sums bins [4032 - 64l, 4095 - 64l]: lanes in order walk the
+        // bins from the top
+        uint32_t sum = 0;
+        {
+            const uint4 *hv = (const uint4 *)(hist + kPreBins - 64u * (uint32_t)(lane + 1));
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const uint4 x = hv[q];
+                sum += (x.x + x.y) + (x.z + x.w);
+            }
+        }
+        const uint32_t incl = wave_incl_scan(sum);
+        const int ls = __ffsll((unsigned long long)__ballot(incl >= (uint32_t)kk)) - 1;  // total >= kk
+        const uint32_t above_ls = lane_value(incl - sum, ls);
+        // within lane ls's 64 bins: lane j takes bin 4095 - 64 ls - j
+        const uint32_t bj = kPreBins - 1u - 64u * (uint32_t)ls - (uint32_t)lane;
+        const uint32_t incl2 = above_ls + wave_incl_scan(hist[bj]);
+        const int lj = __ffsll((unsigned long long)__ballot(incl2 >= (uint32_t)kk)) - 1;
+        const uint32_t bin = lane_value(bj, lj), staged = lane_value(incl2, lj);
+        wave_fence();  // the histogram is read out before the stage reuses it
+        if (staged <= (uint32_t)kStage) {
+            const uint32_t kmin = 0x80000000u | (bin << kPreShift);
+            uint32_t nst = 0;
+            for_each_listed(lists, lcnt, nlists, a.subcap, [&](uint2 e, bool v) {
+                const bool take = v && e.x >= kmin;
+                const uint64_t tb = __ballot(take);
+                if (take) st[nst + (uint32_t)__popcll(tb & lt)] = e;
+                nst += (uint32_t)__popcll(tb);
+            });
+            wave_fence();
+            merge_staged(st, h, nst, nc, kk, out, osc);
+            return;
+        }
     } else {
         n = (uint32_t)nc;
     }

@@ -175,6 +175,39 @@ def test_score_topk_all_ties_lowest_blocks_win(gpu):
         np.testing.assert_array_equal(sc[r, :n], np.float32(raw[r] / math.sqrt(128)))
 
 
+@pytest.mark.parametrize("n_high,n_tied", [(600, 1600), (300, 1900)])
+def test_score_topk_long_pair_lists_exact(gpu, n_high, n_tied):
+    # Rows whose filter keeps more pairs than the merge stages at once.
+    # Block scores are exact integers: n_high distinct values >= 1024, n_tied
+    # blocks at 100, the rest at 1.  The sampled threshold lands on 100, so
+    # every row keeps n_high + n_tied = 2,200 pairs.  With 600 distinct high
+    # values the k-th best key's bin is narrow and only its pairs are staged;
+    # with 300 the k-th best is one of the ties and its bin alone exceeds the
+    # stage (the list-walking path).  Either way: exact, lowest tied blocks.
+    rng = np.random.default_rng(31 + n_high)
+    NB, R, k = 8192, 64, 512
+    exps = np.arange(10, 16)
+    mant = np.arange(128)
+    pool_vals = ((128 + mant[None, :]) * 2.0 ** (exps[:, None] - 7)).ravel().astype(np.float32)
+    vals = np.ones(NB, np.float32)
+    blocks = rng.permutation(NB)
+    vals[blocks[:n_high]] = rng.choice(pool_vals, size=n_high, replace=False)
+    vals[blocks[n_high:n_high + n_tied]] = 100.0
+    pooled = np.zeros((1, NB, DIM), np.float32)
+    pooled[0, :, 0] = vals
+    iq = np.zeros((R, 4, DIM), np.float32)
+    iq[:, 0, 0] = rng.integers(1, 5, R)            # head 0 reads dim 0; raw = q * value, exact
+    pooled, iq = synth.bf16_bits(pooled), synth.bf16_bits(iq)
+    seq = np.zeros(R, np.int32)
+    pos = np.full(R, 4 * NB - 1, np.int32)
+    o_sel, o_cnt, o_sc, _ = oracle.score_topk(iq, seq, pos, pooled, k, THETA, qsa.FLAG_NO_ROPE)
+    sel, cnt, sc = qsa.score_topk(dev(iq, "bf16"), dev(seq, "i"), dev(pos, "i"), dev(pooled, "bf16"), NB, k,
+                                  THETA, flags=qsa.FLAG_NO_ROPE | qsa.FLAG_SCORE_GEMM)
+    np.testing.assert_array_equal(host(cnt), o_cnt)
+    np.testing.assert_array_equal(host(sel), o_sel)
+    np.testing.assert_array_equal(host(sc), o_sc)
+
+
 def test_score_topk_default_paths_agree(gpu):
     # few rows take the streaming scorer, many rows the GEMM: same answer
     B, NB, R, k = 1, 3000, 130, 100
