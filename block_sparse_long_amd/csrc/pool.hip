@@ -65,9 +65,10 @@ __global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ ra
     store_f64(dst + kHalf + lane, dy);
 }
 
-// One wave per (row, index head): q~ = round_dtype(RoPE(q, row_pos)).
-// It also clears `zero_per_row` words of per-row select scratch (each of the
-// row's 4 waves a quarter), so the selection needs no separate fill.
+// One wave per row: q~ = round_dtype(RoPE(q, row_pos)) for the row's 4 index
+// heads.  Lane j forms the angle of rotary pair (j, j + 64) once and rotates
+// that pair of every head.  The wave also clears `zero_per_row` words of the
+// row's select scratch, so the selection needs no separate fill.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_query_kernel(const T *__restrict__ q, const int32_t *__restrict__ row_pos,
                                                          int32_t rows, T *__restrict__ qrot, RopeFreq rf,
@@ -75,19 +76,29 @@ __global__ __launch_bounds__(256) void rope_query_kernel(const T *__restrict__ q
                                                          int64_t zero_per_row)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (w >= (int64_t)rows * kIdxHeads) return;
-    const int64_t r = w / kIdxHeads;
-    if (zero) {
-        const int64_t quarter = (zero_per_row + kIdxHeads - 1) / kIdxHeads;
-        const int64_t lo = (w % kIdxHeads) * quarter, hi = min(zero_per_row, lo + quarter);
-        for (int64_t i = lo + lane; i < hi; i += kWave) zero[r * zero_per_row + i] = 0u;
+    const int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    if (zero)
+        for (int64_t i = lane; i < zero_per_row; i += kWave) zero[r * zero_per_row + i] = 0u;
+    const T *src = q + r * kIdxHeads * kDim;
+    double dx[kIdxHeads], dy[kIdxHeads];
+#pragma unroll
+    for (int h = 0; h < kIdxHeads; ++h) {
+        dx[h] = load_f32(src + h * kDim + lane);
+        dy[h] = load_f32(src + h * kDim + kHalf + lane);
     }
-    const T *src = q + w * kDim;
-    double dx = load_f32(src + lane), dy = load_f32(src + kHalf + lane);
-    if (!(flags & kFlagNoRope)) rope_pair(dx, dy, row_pos[r], rf.f[lane]);
-    store_f64(qrot + w * kDim + lane, dx);
-    store_f64(qrot + w * kDim + kHalf + lane, dy);
+    if (!(flags & kFlagNoRope)) {
+        double c, s;
+        rope_angle(row_pos[r], rf.f[lane], c, s);
+#pragma unroll
+        for (int h = 0; h < kIdxHeads; ++h) rope_apply(dx[h], dy[h], c, s);
+    }
+    T *dst = qrot + r * kIdxHeads * kDim;
+#pragma unroll
+    for (int h = 0; h < kIdxHeads; ++h) {
+        store_f64(dst + h * kDim + lane, dx[h]);
+        store_f64(dst + h * kDim + kHalf + lane, dy[h]);
+    }
 }
 
 // Incremental pooling for decode: one wave per request.  The new raw key goes
@@ -171,8 +182,7 @@ void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pool
 void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,
                        uint32_t flags, bool bf16, uint32_t *zero, int64_t zero_per_row, hipStream_t stream)
 {
-    const int64_t waves = (int64_t)rows * kIdxHeads;
-    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    const dim3 grid((unsigned)(((int64_t)rows + 3) / 4)), block(256);
     const RopeFreq rf = rope_freq(theta);
     if (bf16)
         QSA_LAUNCH("rope_query", (rope_query_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)q, row_pos,

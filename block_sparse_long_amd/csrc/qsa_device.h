@@ -87,16 +87,25 @@ __device__ __forceinline__ int64_t visible_blocks(int64_t t) { return (t + 1) / 
 // Rotate the pair (x, y) = (v[j], v[j+64]) at integer position `pos` with
 // frequency inv_freq = theta^(-j/64); the angle and the rotation are formed
 // in double precision.
-__device__ __forceinline__ void rope_pair(double &x, double &y, int64_t pos, double inv_freq)
+__device__ __forceinline__ void rope_angle(int64_t pos, double inv_freq, double &c, double &s)
 {
 #pragma clang fp contract(off)
     const double ang = (double)pos * inv_freq;
-    double s, c;
     sincos(ang, &s, &c);
+}
+__device__ __forceinline__ void rope_apply(double &x, double &y, double c, double s)
+{
+#pragma clang fp contract(off)
     const double nx = x * c - y * s;
     const double ny = x * s + y * c;
     x = nx;
     y = ny;
+}
+__device__ __forceinline__ void rope_pair(double &x, double &y, int64_t pos, double inv_freq)
+{
+    double c, s;
+    rope_angle(pos, inv_freq, c, s);
+    rope_apply(x, y, c, s);
 }
 
 // max(x, 0) of a finite float as one integer max on its bits: a negative
