@@ -176,12 +176,14 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, const bf16x8_t (
         const bool ok[4] = {(pm.x & qbit) != 0u, (pm.y & qbit) != 0u, (pm.z & qbit) != 0u, (pm.w & qbit) != 0u};
         any[sub] = __ballot(ok[0] | ok[1] | ok[2] | ok[3]) != 0ull;
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (any[sub]) {
+        if (any[sub]) {  // the sub-tile's 4 K operands are read together, then its MFMAs issue
+            uint4 kv[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const uint4 kv = *(const uint4 *)&cs.k[sub * 16 + m16][32 * g + 8 * ks];
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), qb[ks], acc, 0, 0, 0);
-            }
+            for (int ks = 0; ks < 4; ++ks) kv[ks] = *(const uint4 *)&cs.k[sub * 16 + m16][32 * g + 8 * ks];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks]), qb[ks], acc, 0, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) s[sub][j] = ok[j] ? acc[j] * scale2 : -INFINITY;
@@ -227,9 +229,15 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, const bf16x8_t (
                                     pack_bf16x2(p[2 * i + 1][2], p[2 * i + 1][3]));
         const bf16x8_t A = as_bf16x8(pa);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const bf16x8_t Bv = as_bf16x8(*(const uint4 *)&cs.vt[16 * nt + m16][32 * i + 8 * g]);
-            st.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv, st.o[nt], 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {  // V^T operands 4 at a time: one LDS wait per 4 MFMAs
+            bf16x8_t Bv[4];
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                Bv[n] = as_bf16x8(*(const uint4 *)&cs.vt[16 * (4 * h + n) + m16][32 * i + 8 * g]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                st.o[4 * h + n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv[n], st.o[4 * h + n], 0, 0, 0);
         }
     }
 }

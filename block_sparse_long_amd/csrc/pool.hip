@@ -78,8 +78,14 @@ __global__ __launch_bounds__(256) void rope_query_kernel(const T *__restrict__ q
     const int lane = threadIdx.x & 63;
     const int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (r >= rows) return;
-    if (zero)
-        for (int64_t i = lane; i < zero_per_row; i += kWave) zero[r * zero_per_row + i] = 0u;
+    if (zero) {
+        uint32_t *z = zero + r * zero_per_row;
+        if ((zero_per_row & 3) == 0 && ((uintptr_t)z & 15u) == 0) {  // 16-byte stores
+            for (int64_t i = lane; i < zero_per_row / 4; i += kWave) ((uint4 *)z)[i] = make_uint4(0u, 0u, 0u, 0u);
+        } else {
+            for (int64_t i = lane; i < zero_per_row; i += kWave) z[i] = 0u;
+        }
+    }
     const T *src = q + r * kIdxHeads * kDim;
     double dx[kIdxHeads], dy[kIdxHeads];
 #pragma unroll

@@ -93,9 +93,10 @@ __device__ __forceinline__ void tile_scores(const bf16_t (*keys)[kFKRow], const 
     f32x4_t acc[2][4];  // slice nt's accumulators; slice nt-1's ReLU-sums run between its MFMAs
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-        bf16x8_t bk[4];
+        bf16x8_t bk[4];  // the slice's 4 key operands are read together, before its MFMAs
 #pragma unroll
         for (int s = 0; s < 4; ++s) bk[s] = as_bf16x8(*(const uint4 *)&keys[nt * 16 + m][32 * g + 8 * s]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) acc[nt & 1][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll

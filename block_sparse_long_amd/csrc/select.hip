@@ -209,18 +209,18 @@ __global__ __launch_bounds__(kSplitThreads) void select_collect_kernel(
     }
     if (b_begin >= nc) return;
     // ---- collect ----
-    find_bin_global(hist, (uint32_t)kk, wtot, &s_bin, &s_above);
-    const uint32_t beta = s_bin;
+    // the whole chunk in flight at once, issued before the histogram search:
+    // thread t holds blocks b_begin + 1024*j + 4*t + i (rows are padded to 64
+    // floats, so a 4-block group that starts inside the row ends inside it)
     const int64_t b_end = min((int64_t)nc, b_begin + kCollectChunk);
-    // the whole chunk in flight at once: thread t holds blocks b_begin +
-    // 1024*j + 4*t + i (rows are padded to 64 floats, so a 4-block group that
-    // starts inside the row ends inside it)
     float4 v[kCollectChunk / (4 * kSplitThreads)];
 #pragma unroll
     for (int j = 0; j < kCollectChunk / (4 * kSplitThreads); ++j) {
         const int64_t b4 = b_begin + (int64_t)j * 4 * kSplitThreads + 4 * t;
         v[j] = b4 < b_end ? *(const float4 *)(srow + b4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
+    find_bin_global(hist, (uint32_t)kk, wtot, &s_bin, &s_above);
+    const uint32_t beta = s_bin;
 #pragma unroll
     for (int j = 0; j < kCollectChunk / (4 * kSplitThreads); ++j) {
         const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
@@ -263,6 +263,15 @@ __global__ __launch_bounds__(kSplitThreads) void select_final_kernel(
     const uint32_t n_sure = cnt[0];
     const uint32_t n_cand = cnt[1];
     uint32_t need = (uint32_t)kk - n_sure;  // 1 <= need <= n_cand
+    // the kept-for-sure entries (fewer than kk) are loaded now, alongside the
+    // candidates, and held in registers until the kept set is gathered
+    constexpr int kSurePer = QSA_MAX_TOP_K / kSplitThreads;
+    uint2 sure_r[kSurePer];
+#pragma unroll
+    for (int j = 0; j < kSurePer; ++j) {
+        const uint32_t i = (uint32_t)(t + j * kSplitThreads);
+        sure_r[j] = i < n_sure ? sure[i] : make_uint2(0u, 0u);
+    }
     // candidates staged in LDS once when they fit (read by every radix pass)
     const bool staged = n_cand <= (uint32_t)kCandStage;
     if (staged)
@@ -300,9 +309,10 @@ __global__ __launch_bounds__(kSplitThreads) void select_final_kernel(
     // ---- kept set: the sure entries and the picked candidates ----
     if (t == 0) s_fill = 0;
     __syncthreads();
-    for (uint32_t i = t; i < n_sure; i += kSplitThreads) {
-        const uint2 e = sure[i];
-        buf[atomicAdd(&s_fill, 1u)] = ((uint64_t)e.y << 32) | e.x;
+#pragma unroll
+    for (int j = 0; j < kSurePer; ++j) {
+        const uint32_t i = (uint32_t)(t + j * kSplitThreads);
+        if (i < n_sure) buf[atomicAdd(&s_fill, 1u)] = ((uint64_t)sure_r[j].y << 32) | sure_r[j].x;
     }
     for (uint32_t i = t; i < n_cand; i += kSplitThreads) {
         const uint2 e = cl[i];
