@@ -128,6 +128,31 @@ __device__ __forceinline__ void chunk_load(ChunkRegs &cr, const bf16_t *__restri
                                : make_uint4(0, 0, 0, 0);
 }
 
+// The same share of a chunk of whole blocks: ublk[0..nb) are the chunk's
+// blocks (16 at most, nb >= 1).  Thread t's K position is token (t/4)%4 of
+// block t/16 and its V positions are tokens 0..3 of block t%16, so one block
+// id serves each; a thread past the chunk's blocks reads the last one instead
+// (its positions carry no mask bit, so their P is exactly 0).  Every load is
+// unconditional.
+__device__ __forceinline__ void chunk_load_blocks(ChunkRegs &cr, const bf16_t *__restrict__ kbase,
+                                                  const bf16_t *__restrict__ vbase, uint32_t row_stride,
+                                                  const int32_t *ublk, int nb)
+{
+    const int t = threadIdx.x;
+    const uint32_t bstride = 4u * row_stride;  // elements per block
+    const int32_t bk = ublk[min(t >> 4, nb - 1)], bv = ublk[min(t & 15, nb - 1)];
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const u32x4_t *ks = (const u32x4_t *)(kbase + (uint64_t)(uint32_t)bk * bstride + ((t >> 2) & 3) * row_stride +
+                                          (t & 3) * 32);
+    const bf16_t *vs = vbase + (uint64_t)(uint32_t)bv * bstride + (t >> 4) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // element-wise vector loads (a block copy would go through memory)
+        const u32x4_t kx = ks[i], vx = *(const u32x4_t *)(vs + i * row_stride);
+        cr.k[i] = make_uint4(kx.x, kx.y, kx.z, kx.w);
+        cr.v[i] = make_uint4(vx.x, vx.y, vx.z, vx.w);
+    }
+}
+
 // Registers -> LDS: K row-major, V transposed.
 __device__ __forceinline__ void chunk_store(ChunkSmem &cs, const ChunkRegs &cr)
 {
@@ -388,9 +413,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
             constexpr int kChB = kCh / kBlock;
             const int32_t nch = (nu + kChB - 1) / kChB;
             ChunkRegs cr;
-            if (nch > 0)
-                chunk_load(cr, kbase, vbase, row_stride, min(kChB, nu) * kBlock,
-                           [&](int i) { return (int64_t)us.blk[i / kBlock] * kBlock + (i % kBlock); });
+            if (nch > 0) chunk_load_blocks(cr, kbase, vbase, (uint32_t)row_stride, us.blk, min(kChB, nu));
             for (int32_t c = 0; c < nch; ++c) {
                 const int32_t c0 = c * kChB;
                 const int nb = min(kChB, nu - c0);
@@ -399,8 +422,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
                 __syncthreads();
                 if (c + 1 < nch) {
                     const int32_t c1 = c0 + kChB;
-                    chunk_load(cr, kbase, vbase, row_stride, min(kChB, nu - c1) * kBlock,
-                               [&](int i) { return (int64_t)us.blk[c1 + i / kBlock] * kBlock + (i % kBlock); });
+                    chunk_load_blocks(cr, kbase, vbase, (uint32_t)row_stride, us.blk + c1, min(kChB, nu - c1));
                 }
                 wave_chunk(cs, qb, qbit, scale2, st);
                 __syncthreads();
@@ -564,7 +586,8 @@ bool attn_mfma_supported(int32_t Hq, int32_t Hkv, int32_t q_per_sel, bool bf16)
 {
     const int32_t hg = Hq / Hkv;
     return bf16 && (hg == 1 || hg == 2 || hg == 4 || hg == 8 || hg == 16 || hg == 32 || hg == 64) &&
-           (int64_t)q_per_sel * hg <= 64;
+           (int64_t)q_per_sel * hg <= 64 &&
+           (int64_t)Hkv * kDim * kBlock <= (int64_t)UINT32_MAX;  // a block's K/V span as a 32-bit element count
 }
 
 void launch_attn_prefill_mfma(const AttnArgs &a, hipStream_t stream)
