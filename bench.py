@@ -94,6 +94,8 @@ def prefill_work(spec, row_pos):
         "attn_prefill": ("alu", 4.0 * spec.Hq * DIM * float(npos.sum()), "flop"),
         "attn_prefill_mfma": ("mfma", 4.0 * spec.Hq * DIM * float(npos.sum()), "flop"),
         "score_filter": ("mfma", 2.0 * 4 * DIM * pairs, "flop"),
+        "score_filter_fp8": ("mfma", 2.0 * 4 * DIM * pairs, "flop"),
+        "pool_rope_fp8": ("hbm", new_blocks * (4 * DIM * eb + DIM + 4), "B"),
     }, pairs, float(npos.sum())
 
 
@@ -112,6 +114,7 @@ def decode_work(spec, anchor_pos, attn_pos, tail_start):
     kind = "score_rows_bf16" if spec.dtype == "bf16" else "score_rows_f32"
     return {
         kind: ("hbm", float(pairs) * DIM * eb, "B"),
+        "score_rows_fp8": ("hbm", float(pairs) * (DIM + 4), "B"),   # codes and the scale of each key
         "select_rows": ("hbm", 4.0 * pairs, "B"),
         "select_collect": ("hbm", 4.0 * pairs, "B"),
         "select_final": ("hbm", 8.0 * spec.batch * spec.top_k, "B"),
@@ -167,27 +170,39 @@ def timed(run_step, steps, warmup):
     return (time.perf_counter() - t0) / steps * 1e3
 
 
-ALL_KERNELS = ["pool_rope", "pool_append", "rope_query", "score_rows_bf16", "score_rows_f32", "score_gemm_bf16", "select_rows",
-               "select_collect", "select_final", "score_sample", "sample_threshold", "score_filter", "select_merge", "attn_prefill_mfma", "attn_decode_mfma",
-               "attn_prefill", "attn_decode", "attn_combine"]
+ALL_KERNELS = ["pool_rope", "pool_rope_fp8", "pool_append", "rope_query", "score_rows_bf16", "score_rows_f32",
+               "score_rows_fp8", "score_gemm_bf16", "select_rows", "select_collect", "select_final", "score_sample",
+               "score_sample_fp8", "sample_threshold", "score_filter", "score_filter_fp8", "select_merge",
+               "attn_prefill_mfma", "attn_decode_mfma", "attn_prefill", "attn_decode", "attn_combine"]
 
 
 # ---------------------------------------------------------------------------
 # prefill workload
 # ---------------------------------------------------------------------------
 
-def bench_prefill(spec, steps, warmup, cpu_baseline):
+def bench_prefill(spec, steps, warmup, cpu_baseline, keys="bf16", w=None):
+    """keys "fp8": the compressed keys stored as E4M3 codes plus one scale per
+    key (qsa_pool_index_keys_fp8 / qsa_score_topk_fp8); everything else as
+    with bf16 keys."""
     import torch
     from block_sparse_long_amd import qsa, synth
-    t0 = time.perf_counter()
-    w = synth.make(spec)
-    log(f"{spec.name}: inputs drawn in {time.perf_counter() - t0:.1f}s")
+    if w is None:
+        t0 = time.perf_counter()
+        w = synth.make(spec)
+        log(f"{spec.name}: inputs drawn in {time.perf_counter() - t0:.1f}s")
     L, nb, k = spec.ctx, spec.n_blocks, spec.top_k
     first_new = (L - spec.chunk) // 4
     raw = to_dev(w["raw_keys"])
-    pooled = torch.zeros((1, nb, DIM), dtype=raw.dtype, device="cuda")
-    if first_new > 0:  # the context before the chunk is already pooled
-        qsa.pool_index_keys(raw, pooled, 0, first_new, spec.theta)
+    fp8 = keys == "fp8"
+    if fp8:
+        codes = torch.zeros((1, nb, DIM), dtype=torch.uint8, device="cuda")
+        scales = torch.zeros((1, nb), dtype=torch.float32, device="cuda")
+        if first_new > 0:
+            qsa.pool_index_keys_fp8(raw, codes, scales, 0, first_new, spec.theta)
+    else:
+        pooled = torch.zeros((1, nb, DIM), dtype=raw.dtype, device="cuda")
+        if first_new > 0:  # the context before the chunk is already pooled
+            qsa.pool_index_keys(raw, pooled, 0, first_new, spec.theta)
     iq, seq, pos = to_dev(w["idx_q"]), to_dev(w["row_seq"]), to_dev(w["row_pos"])
     q, kc, vc = to_dev(w["q"]), to_dev(w["k_cache"]), to_dev(w["v_cache"])
     R = spec.chunk
@@ -200,13 +215,18 @@ def bench_prefill(spec, steps, warmup, cpu_baseline):
     lse = torch.empty((R, spec.Hq), dtype=torch.float32, device="cuda")
 
     def step(_i):
-        qsa.pool_index_keys(raw, pooled, first_new, nb, spec.theta)
-        qsa.score_topk(iq, seq, pos, pooled, max_nb, k, spec.theta, sel_blocks=sel, sel_count=cnt,
-                       workspace=ws, want_scores=False)
+        if fp8:
+            qsa.pool_index_keys_fp8(raw, codes, scales, first_new, nb, spec.theta)
+            qsa.score_topk_fp8(iq, seq, pos, codes, scales, max_nb, k, spec.theta, sel_blocks=sel, sel_count=cnt,
+                               workspace=ws, want_scores=False)
+        else:
+            qsa.pool_index_keys(raw, pooled, first_new, nb, spec.theta)
+            qsa.score_topk(iq, seq, pos, pooled, max_nb, k, spec.theta, sel_blocks=sel, sel_count=cnt,
+                           workspace=ws, want_scores=False)
         qsa.sparse_attn_prefill(q, seq, pos, kc, vc, sel, cnt, out=out, lse=lse)
 
     ms = timed(step, steps, warmup)
-    log(f"{spec.name}: {ms:.3f} ms/step")
+    log(f"{spec.name} ({keys} keys): {ms:.3f} ms/step")
     kt = kernel_times(step, max(3, min(steps, 10)), ALL_KERNELS)
     work, pairs, npos = prefill_work(spec, w["row_pos"])
     kernels = {n: {"launches_per_step": c / max(3, min(steps, 10)), "avg_us": round(a * 1e3, 2)}
@@ -219,6 +239,7 @@ def bench_prefill(spec, steps, warmup, cpu_baseline):
            "pairs": pairs, "positions": npos}
     if cpu_baseline:
         res["cpu_baseline"] = cpu_prefill(spec, w)
+    res["_inputs"] = w
     return res
 
 
@@ -259,22 +280,35 @@ def cpu_prefill(spec, w, target_s=12.0):
 # decode workload
 # ---------------------------------------------------------------------------
 
-def bench_decode(spec, steps, warmup, cpu_baseline, copies=3):
+def bench_decode(spec, steps, warmup, cpu_baseline, copies=3, keys="bf16", w=None):
+    """keys "fp8": E4M3 codes plus one scale per key, as in bench_prefill."""
     import torch
     from block_sparse_long_amd import qsa, synth
-    t0 = time.perf_counter()
-    w = synth.make(spec)
-    log(f"{spec.name}: inputs drawn in {time.perf_counter() - t0:.1f}s")
+    if w is None:
+        t0 = time.perf_counter()
+        w = synth.make(spec)
+        log(f"{spec.name}: inputs drawn in {time.perf_counter() - t0:.1f}s")
     B, nb, k = spec.batch, spec.n_blocks, spec.top_k
+    fp8 = keys == "fp8"
     raw = to_dev(w["raw_keys"])
-    pooled0 = torch.zeros((B, nb, DIM), dtype=raw.dtype, device="cuda")
-    qsa.pool_index_keys(raw, pooled0, 0, nb, spec.theta)   # built before timing
-    del raw
     pooled_h = None
-    if cpu_baseline:
-        pooled_h = pooled0[:1].cpu()
+    if fp8:   # built before timing
+        codes0 = torch.zeros((B, nb, DIM), dtype=torch.uint8, device="cuda")
+        scales0 = torch.zeros((B, nb), dtype=torch.float32, device="cuda")
+        qsa.pool_index_keys_fp8(raw, codes0, scales0, 0, nb, spec.theta)
+        pooled0 = None
+    else:
+        pooled0 = torch.zeros((B, nb, DIM), dtype=raw.dtype, device="cuda")
+        qsa.pool_index_keys(raw, pooled0, 0, nb, spec.theta)   # built before timing
+        if cpu_baseline:
+            pooled_h = pooled0[:1].cpu()
+    del raw
     kc0, vc0 = to_dev(w["k_cache"]), to_dev(w["v_cache"])
-    pooled = [pooled0] + [pooled0.clone() for _ in range(copies - 1)]
+    if fp8:
+        kcodes = [codes0] + [codes0.clone() for _ in range(copies - 1)]
+        kscales = [scales0] + [scales0.clone() for _ in range(copies - 1)]
+    else:
+        pooled = [pooled0] + [pooled0.clone() for _ in range(copies - 1)]
     kcs = [kc0] + [kc0.clone() for _ in range(copies - 1)]
     vcs = [vc0] + [vc0.clone() for _ in range(copies - 1)]
     iq, seq, apos = to_dev(w["idx_q"]), to_dev(w["row_seq"]), to_dev(w["row_pos"])
@@ -293,12 +327,16 @@ def bench_decode(spec, steps, warmup, cpu_baseline, copies=3):
 
     def step(i):
         c = i % copies
-        qsa.score_topk(iq, seq, apos, pooled[c], max_nb, k, spec.theta, sel_blocks=sel, sel_count=cnt,
-                       workspace=ws, want_scores=False)
+        if fp8:
+            qsa.score_topk_fp8(iq, seq, apos, kcodes[c], kscales[c], max_nb, k, spec.theta, sel_blocks=sel,
+                               sel_count=cnt, workspace=ws, want_scores=False)
+        else:
+            qsa.score_topk(iq, seq, apos, pooled[c], max_nb, k, spec.theta, sel_blocks=sel, sel_count=cnt,
+                           workspace=ws, want_scores=False)
         qsa.sparse_attn_decode(q, rpos, kcs[c], vcs[c], sel, cnt, ts, out=out, lse=lse, workspace=wsa)
 
     ms = timed(step, steps, warmup)
-    log(f"{spec.name}: {ms:.3f} ms/step")
+    log(f"{spec.name} ({keys} keys): {ms:.3f} ms/step")
     nprof = max(3, min(steps, 30))
     kt = kernel_times(step, nprof, ALL_KERNELS)
     work, pairs = decode_work(spec, w["row_pos"], w["attn_pos"], w["tail_start"])
@@ -309,9 +347,11 @@ def bench_decode(spec, steps, warmup, cpu_baseline, copies=3):
     res = {"workload": spec.name, "value": rows / (ms * 1e-3), "unit": "query rows/s", "ms_per_step": ms,
            "kernels": kernels, "roofline": roofline_for(dom, work[dom], kt[dom][1], tr),
            "rooflines": {n: roofline_for(n, work[n], kt[n][1], tr) for n in kt if n in work}}
-    res["pool_append"] = bench_pool_append(spec)
-    if cpu_baseline:
+    if not fp8:
+        res["pool_append"] = bench_pool_append(spec)
+    if cpu_baseline and not fp8:
         res["cpu_baseline"] = cpu_decode(spec, w, pooled_h)
+    res["_inputs"] = w
     return res
 
 
@@ -378,7 +418,8 @@ KERNEL_SOURCE = {"pool_rope": "pool.hip", "pool_append": "pool.hip", "rope_query
                  "sample_threshold": "score_fused.hip", "score_filter": "score_fused.hip",
                  "select_merge": "score_fused.hip", "attn_prefill_mfma": "attn_mfma.hip",
                  "attn_decode_mfma": "attn_mfma.hip", "attn_prefill": "attn.hip", "attn_decode": "attn.hip",
-                 "attn_combine": "attn.hip"}
+                 "attn_combine": "attn.hip", "pool_rope_fp8": "pool.hip", "score_rows_fp8": "score.hip",
+                 "score_sample_fp8": "score_fused.hip", "score_filter_fp8": "score_fused.hip"}
 COPY_BYTES = 1 << 30
 
 
@@ -403,6 +444,8 @@ def short_kernel_name(full):
         return "attn_decode" if tmpl.rstrip(">").strip().endswith("true") else "attn_prefill"
     if base.startswith("attn_combine"):
         return "attn_combine"
+    if base in ("score_sample_kernel", "score_filter_kernel") and tmpl.startswith("<true"):
+        return base[:-7] + "_fp8"   # the FP8-key instance
     return base[:-7] if base.endswith("_kernel") else base
 
 
@@ -512,6 +555,8 @@ def main():
     ap.add_argument("--workload", default="chunk-256k")
     ap.add_argument("--decode-workload", default="decode-1m-draft")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", dest="fp8", action="store_false",
+                    help="skip the extra runs with FP8 index keys")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a copy of known size first (for scaling memory counters)")
     ap.add_argument("--rocprof-summary", nargs="+", metavar="DIR")
@@ -543,6 +588,13 @@ def main():
         pre = bench_decode(spec, args.steps * 10, args.warmup, cpu)
         value, unit, ms = pre["value"], pre["unit"], pre["ms_per_step"]
         main_res = pre
+    fp8_res = {}
+    if args.fp8 and spec.dtype == "bf16":
+        if spec.kind == "prefill":
+            fp8_res[spec.name] = bench_prefill(spec, args.steps, args.warmup, False, keys="fp8", w=pre["_inputs"])
+        else:
+            fp8_res[spec.name] = bench_decode(spec, args.steps * 10, args.warmup, False, keys="fp8", w=pre["_inputs"])
+    pre.pop("_inputs", None)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -558,10 +610,24 @@ def main():
     if args.decode_workload != "none" and spec.kind == "prefill":
         dspec = synth.SPECS[args.decode_workload]
         dec = bench_decode(dspec, args.steps * 10, args.warmup, cpu)
+        if args.fp8 and dspec.dtype == "bf16":
+            fp8_res[dspec.name] = bench_decode(dspec, args.steps * 10, args.warmup, False, keys="fp8",
+                                               w=dec["_inputs"])
+        dec.pop("_inputs", None)
         line["decode"] = {k: v for k, v in dec.items()}
         line["decode"]["config"] = {"context": dspec.ctx, "batch": dspec.batch, "q_per_seq": dspec.q_per_seq,
                                     "Hq": dspec.Hq, "Hkv": dspec.Hkv, "top_k": dspec.top_k,
                                     "steps": args.steps * 10}
+    if fp8_res:
+        # the same workloads with the compressed index keys in FP8 E4M3 (one
+        # FP32 scale per key); not the headline: the headline keeps bf16 keys
+        line["fp8_keys"] = {}
+        for name, r in fp8_res.items():
+            r.pop("_inputs", None)
+            line["fp8_keys"][name] = {"value": round(r["value"], 1),
+                                      "unit": "tokens/s" if "workload" not in r else r["unit"],
+                                      "ms_per_step": round(r["ms_per_step"], 4), "kernels": r["kernels"],
+                                      "roofline": r["roofline"]}
     print(json.dumps(line), flush=True)
 
 

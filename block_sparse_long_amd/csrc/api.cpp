@@ -159,6 +159,19 @@ static bool score_flags_ok(uint32_t flags, qsa_dtype_t dtype)
 
 using namespace qsa;
 
+// Where qsa_score_topk's keys come from: `pooled` of the call's dtype, or FP8
+// codes with one scale per key.
+struct KeySource {
+    const void *pooled;
+    const uint8_t *codes;
+    const float *scales;
+};
+static qsa_status_t score_topk_run(const void *q_index, const int32_t *row_seq, const int32_t *row_pos,
+                                   int32_t rows, const KeySource &keys, int64_t pooled_seq_stride,
+                                   int32_t max_visible_blocks, int32_t top_k, double rope_theta, uint32_t flags,
+                                   qsa_dtype_t dtype, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
 extern "C" {
 
 const char *qsa_status_string(qsa_status_t s)
@@ -198,6 +211,26 @@ qsa_status_t qsa_pool_index_keys(const void *raw_keys, int64_t raw_seq_stride, v
     return launch_status();
 }
 
+qsa_status_t qsa_pool_index_keys_fp8(const void *raw_keys, int64_t raw_seq_stride, uint8_t *codes, float *scales,
+                                     int64_t pooled_seq_stride, int32_t batch, int32_t block_begin, int32_t block_end,
+                                     double rope_theta, uint32_t flags, qsa_dtype_t raw_dtype, void *stream)
+{
+    if (!dtype_ok(raw_dtype)) return QSA_ERR_UNSUPPORTED;
+    if (batch < 0 || block_begin < 0 || block_end < block_begin) return QSA_ERR_INVALID_ARG;
+    if (flags & ~(uint32_t)(QSA_FLAG_NO_ROPE | QSA_FLAG_POOL_RMSNORM)) return QSA_ERR_INVALID_ARG;
+    if (!(flags & QSA_FLAG_NO_ROPE) && !(rope_theta > 1.0 && std::isfinite(rope_theta))) return QSA_ERR_INVALID_ARG;
+    if (batch == 0 || block_end == block_begin) return QSA_OK;
+    if (!aligned16(raw_keys) || !aligned16(codes) || !scales || (reinterpret_cast<uintptr_t>(scales) & 3u))
+        return QSA_ERR_INVALID_ARG;
+    if (raw_seq_stride % 8 || pooled_seq_stride < 0) return QSA_ERR_INVALID_ARG;
+    if (batch > 1 && (raw_seq_stride < (int64_t)kBlock * block_end * kDim || pooled_seq_stride < (int64_t)block_end))
+        return QSA_ERR_INVALID_ARG;
+    clear_launch_err();
+    launch_pool_fp8(raw_keys, raw_seq_stride, codes, scales, pooled_seq_stride, batch, block_begin, block_end,
+                    rope_theta, flags, raw_dtype == QSA_BF16, (hipStream_t)stream);
+    return launch_status();
+}
+
 qsa_status_t qsa_pool_append(const void *new_keys, const int32_t *positions, const int64_t *full_slots, void *ring,
                              void *compressed, int32_t batch, double rope_theta, uint32_t flags, qsa_dtype_t dtype,
                              void *stream)
@@ -223,6 +256,11 @@ size_t qsa_score_topk_workspace_size(int32_t rows, int32_t max_visible_blocks, i
     return score_layout(rows, max_visible_blocks, top_k, dtype, flags).total;
 }
 
+size_t qsa_score_topk_fp8_workspace_size(int32_t rows, int32_t max_visible_blocks, int32_t top_k, uint32_t flags)
+{
+    return qsa_score_topk_workspace_size(rows, max_visible_blocks, top_k, QSA_BF16, flags);
+}
+
 qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
                             const void *pooled, int64_t pooled_seq_stride, int32_t max_visible_blocks, int32_t top_k,
                             double rope_theta, uint32_t flags, qsa_dtype_t dtype, int32_t *sel_blocks,
@@ -238,6 +276,43 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
     if (!aligned16(q_index) || !aligned16(pooled) || !row_seq || !row_pos || !sel_blocks || !sel_count)
         return QSA_ERR_INVALID_ARG;
     if (pooled_seq_stride % 8 || pooled_seq_stride < 0) return QSA_ERR_INVALID_ARG;
+    const KeySource keys{pooled, nullptr, nullptr};
+    return score_topk_run(q_index, row_seq, row_pos, rows, keys, pooled_seq_stride, max_visible_blocks, top_k,
+                          rope_theta, flags, dtype, sel_blocks, sel_count, sel_scores, workspace, workspace_bytes,
+                          stream);
+}
+
+qsa_status_t qsa_score_topk_fp8(const void *q_index, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+                                const uint8_t *codes, const float *scales, int64_t pooled_seq_stride,
+                                int32_t max_visible_blocks, int32_t top_k, double rope_theta, uint32_t flags,
+                                int32_t *sel_blocks, int32_t *sel_count, float *sel_scores, void *workspace,
+                                size_t workspace_bytes, void *stream)
+{
+    if (rows < 0 || max_visible_blocks < 0 || top_k < 1 || top_k > QSA_MAX_TOP_K) return QSA_ERR_INVALID_ARG;
+    if (!score_flags_ok(flags, QSA_BF16)) return QSA_ERR_INVALID_ARG;
+    if (!(flags & QSA_FLAG_NO_ROPE) && !(rope_theta > 1.0 && std::isfinite(rope_theta))) return QSA_ERR_INVALID_ARG;
+    if (rows == 0) return QSA_OK;
+    if (!aligned16(q_index) || !aligned16(codes) || !scales || (reinterpret_cast<uintptr_t>(scales) & 3u) || !row_seq ||
+        !row_pos || !sel_blocks || !sel_count)
+        return QSA_ERR_INVALID_ARG;
+    if (pooled_seq_stride < 0) return QSA_ERR_INVALID_ARG;
+    const KeySource keys{nullptr, codes, scales};
+    return score_topk_run(q_index, row_seq, row_pos, rows, keys, pooled_seq_stride, max_visible_blocks, top_k,
+                          rope_theta, flags, QSA_BF16, sel_blocks, sel_count, sel_scores, workspace, workspace_bytes,
+                          stream);
+}
+
+}  // extern "C"
+
+// The launches of qsa_score_topk / qsa_score_topk_fp8 after validation.
+// FP8 keys go with bf16 index queries (the same layout and kernels, with the
+// codes converted to bf16 on the way to the MFMA).
+static qsa_status_t score_topk_run(const void *q_index, const int32_t *row_seq, const int32_t *row_pos,
+                                   int32_t rows, const KeySource &keys, int64_t pooled_seq_stride,
+                                   int32_t max_visible_blocks, int32_t top_k, double rope_theta, uint32_t flags,
+                                   qsa_dtype_t dtype, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
+                                   void *workspace, size_t workspace_bytes, void *stream)
+{
     const ScoreLayout L = score_layout(rows, max_visible_blocks, top_k, dtype, flags);
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return QSA_ERR_INVALID_ARG;
     if (workspace_bytes < L.total) return QSA_ERR_WORKSPACE;
@@ -261,7 +336,9 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
         fa.row_seq = row_seq;
         fa.row_pos = row_pos;
         fa.rows = rows;
-        fa.pooled = (const uint16_t *)pooled;
+        fa.pooled = (const uint16_t *)keys.pooled;
+        fa.codes = keys.codes;
+        fa.scales = keys.scales;
         fa.pooled_stride = pooled_seq_stride;
         fa.max_nb = max_visible_blocks;
         fa.top_k = top_k;
@@ -278,9 +355,14 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
         return launch_status();
     }
     float *scores = (float *)(ws + L.scores_off);
-    if (max_visible_blocks > 0)
-        launch_score_rows(qrot, row_seq, row_pos, rows, pooled, pooled_seq_stride, max_visible_blocks, scores,
-                          L.sc_stride, L.plan.split ? ss.scratch : nullptr, bf16, st);
+    if (max_visible_blocks > 0) {
+        if (keys.codes)
+            launch_score_rows_fp8(qrot, row_seq, row_pos, rows, keys.codes, keys.scales, pooled_seq_stride,
+                                  max_visible_blocks, scores, L.sc_stride, L.plan.split ? ss.scratch : nullptr, st);
+        else
+            launch_score_rows(qrot, row_seq, row_pos, rows, keys.pooled, pooled_seq_stride, max_visible_blocks,
+                              scores, L.sc_stride, L.plan.split ? ss.scratch : nullptr, bf16, st);
+    }
     if (L.plan.split)
         launch_select_split(scores, L.sc_stride, row_pos, rows, max_visible_blocks, top_k, ss, sel_blocks, sel_count,
                             sel_scores, st);
@@ -289,6 +371,8 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
                            sel_scores, st);
     return launch_status();
 }
+
+extern "C" {
 
 static qsa_status_t check_attn_common(const void *q, const void *k_cache, const void *v_cache, int64_t kv_seq_stride,
                                       const int32_t *sel_blocks, const int32_t *sel_count, int32_t top_k, int32_t Hq,

@@ -73,14 +73,6 @@ struct alignas(16) UnionSmem {
     uint32_t count;
 };
 
-// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
-{
-    typedef float f32x2_t __attribute__((ext_vector_type(2)));
-    typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, b16x2_t));
-}
-
 // Logits are kept in base-2 units (softmax_scale * log2(e) * <q, k>).  The
 // softmax reference max of a query moves only when a logit exceeds it by more
 // than kLazy: until then P = 2^(s - m) <= 2^kLazy, and O and l keep their

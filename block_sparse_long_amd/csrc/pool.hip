@@ -65,6 +65,51 @@ __global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ ra
     store_f64(dst + kHalf + lane, dy);
 }
 
+// The same block pooling with the compressed key stored in FP8 E4M3 and one
+// FP32 scale ("Qwen3.8-Flash-Next, Layer by Layer", section "Serving it": the
+// indexer's keys are kept in FP8).  The rotated key is rounded to FP32; its
+// largest magnitude amax maps to 448, the largest E4M3 value: inv = 448/amax,
+// scale = amax/448 (IEEE FP32 quotients), code = E4M3(k * inv) rounded to
+// nearest even by v_cvt_pk_fp8_f32.  |k * inv| <= 448 (1 + 2^-23), so no code
+// overflows.  A zero key gets scale 0 and zero codes.
+template <typename T>
+__global__ __launch_bounds__(256) void pool_rope_fp8_kernel(const T *__restrict__ raw, int64_t raw_stride,
+                                                            uint8_t *__restrict__ codes, float *__restrict__ scales,
+                                                            int64_t pooled_stride, int64_t total, int32_t nblk,
+                                                            int32_t block_begin, RopeFreq rf, uint32_t flags)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (w >= total) return;
+    const int64_t s = w / nblk;
+    const int64_t b = block_begin + w % nblk;
+    const T *src = raw + s * raw_stride + b * (kBlock * kDim);
+    float x = 0.0f, y = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) {  // FP32 sum in token order, then times 1/4
+        x += load_f32(src + i * kDim + lane);
+        y += load_f32(src + i * kDim + kHalf + lane);
+    }
+    x *= 0.25f;
+    y *= 0.25f;
+    double dx = x, dy = y;
+    if (flags & kFlagRmsNorm) {
+        const double ss = wave_sum_f64(dx * dx + dy * dy);
+        const double inv = 1.0 / sqrt(ss / (double)kDim + 1e-6);
+        dx *= inv;
+        dy *= inv;
+    }
+    if (!(flags & kFlagNoRope)) rope_pair(dx, dy, kBlock * b, rf.f[lane]);
+    const float fx = (float)dx, fy = (float)dy;
+    const float amax = wave_max(fmaxf(fabsf(fx), fabsf(fy)));
+    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+    const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fx * inv, fy * inv, 0, false);
+    const int64_t slot = s * pooled_stride + b;
+    codes[slot * kDim + lane] = (uint8_t)(pk & 0xffu);
+    codes[slot * kDim + kHalf + lane] = (uint8_t)((pk >> 8) & 0xffu);
+    if (lane == 0) scales[slot] = amax / 448.0f;
+}
+
 // One wave per row: q~ = round_dtype(RoPE(q, row_pos)) for the row's 4 index
 // heads.  Lane j forms the angle of rotary pair (j, j + 64) once and rotates
 // that pair of every head.  The wave also clears `zero_per_row` words of the
@@ -183,6 +228,22 @@ void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pool
     else
         QSA_LAUNCH("pool_rope", (pool_rope_kernel<float>), grid, block, 0, stream, (const float *)raw, raw_stride,
                    (float *)pooled, pooled_stride, total, nblk, block_begin, rf, flags);
+}
+
+void launch_pool_fp8(const void *raw, int64_t raw_stride, uint8_t *codes, float *scales, int64_t pooled_stride,
+                     int32_t batch, int32_t block_begin, int32_t block_end, double theta, uint32_t flags,
+                     bool bf16_raw, hipStream_t stream)
+{
+    const int32_t nblk = block_end - block_begin;
+    const int64_t total = (int64_t)batch * nblk;
+    const dim3 grid((unsigned)((total + 3) / 4)), block(256);
+    const RopeFreq rf = rope_freq(theta);
+    if (bf16_raw)
+        QSA_LAUNCH("pool_rope_fp8", (pool_rope_fp8_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)raw,
+                   raw_stride, codes, scales, pooled_stride, total, nblk, block_begin, rf, flags);
+    else
+        QSA_LAUNCH("pool_rope_fp8", (pool_rope_fp8_kernel<float>), grid, block, 0, stream, (const float *)raw,
+                   raw_stride, codes, scales, pooled_stride, total, nblk, block_begin, rf, flags);
 }
 
 void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,

@@ -27,6 +27,9 @@ void note_launch(hipError_t err);
 void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pooled_stride, int32_t batch,
                  int32_t block_begin, int32_t block_end, double theta, uint32_t flags, bool bf16,
                  hipStream_t stream);
+void launch_pool_fp8(const void *raw, int64_t raw_stride, uint8_t *codes, float *scales, int64_t pooled_stride,
+                     int32_t batch, int32_t block_begin, int32_t block_end, double theta, uint32_t flags,
+                     bool bf16_raw, hipStream_t stream);
 void launch_pool_append(const void *new_keys, const int32_t *positions, const int64_t *full_slots, void *ring,
                         void *compressed, int32_t batch, double theta, uint32_t flags, bool bf16, hipStream_t stream);
 void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,
@@ -39,6 +42,9 @@ constexpr int kHistShift = 20;
 void launch_score_rows(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
                        const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores,
                        int64_t sc_stride, uint32_t *hist, bool bf16, hipStream_t stream);
+void launch_score_rows_fp8(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+                           const uint8_t *codes, const float *scales, int64_t pooled_stride, int32_t max_nb,
+                           float *scores, int64_t sc_stride, uint32_t *hist, hipStream_t stream);
 void launch_score_gemm(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
                        const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores,
                        int64_t sc_stride, hipStream_t stream);
@@ -49,8 +55,10 @@ struct FusedScoreArgs {
     const int32_t *row_seq;
     const int32_t *row_pos;
     int32_t rows;
-    const uint16_t *pooled;   // [B][pooled_stride] (bf16)
-    int64_t pooled_stride;
+    const uint16_t *pooled;   // [B][pooled_stride] (bf16), or NULL with FP8 keys
+    const uint8_t *codes;     // FP8 keys: [B][pooled_stride][128] E4M3 codes, else NULL
+    const float *scales;      // FP8 keys: [B][pooled_stride] one scale per key
+    int64_t pooled_stride;    // elements per sequence (bf16) or keys per sequence (FP8)
     int32_t max_nb;
     int32_t top_k;
     int32_t nsplit;           // block-range splits of the main pass

@@ -127,6 +127,96 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// The same on FP8 keys: a block is 128 E4M3 codes (128 bytes) and one FP32
+// scale.  A lane converts its 32 codes of a tile to bf16 (exact) for the MFMA,
+// and the ReLU-sum of a block is multiplied by the block's scale (a
+// non-negative factor commutes with the ReLUs).  Half the bytes of the bf16
+// keys, read once per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void score_rows_fp8_kernel(
+    const bf16_t *__restrict__ qrot, const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_pos,
+    const uint8_t *__restrict__ codes, const float *__restrict__ scales, int64_t pooled_stride, int32_t max_nb,
+    float *__restrict__ scores, int64_t sc_stride, uint32_t *__restrict__ hist)
+{
+    __shared__ uint32_t lhist[kHistBins];
+    const int r = blockIdx.y;
+    const int64_t nc = min(visible_blocks(row_pos[r]), (int64_t)max_nb);
+    const int64_t b_begin = (int64_t)blockIdx.x * kChunk;
+    if (b_begin >= nc) return;
+    const int64_t b_end = min(nc, b_begin + (int64_t)kChunk);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t seq = row_seq[r];
+    const uint8_t *kb = codes + seq * pooled_stride * kDim;
+    const float *sb = scales + seq * pooled_stride;
+    float *srow = scores + (int64_t)r * sc_stride;
+    // as the bf16 kernel: column m of tile nt is block base + 4m + nt; lane
+    // group g holds the codes of dims 32g .. 32g + 31 (32 bytes), and every
+    // lane also loads the scales of its 4 blocks (clamped, unconditional)
+    struct Step {
+        uint4 c[4][2];
+        float sc[4];
+    };
+    auto load = [&](int64_t base, Step &v) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int64_t b = min(base + 4 * m + nt, b_end - 1);
+            const uint4 *src = (const uint4 *)(kb + b * kDim + 32 * g);
+            v.c[nt][0] = src[0];
+            v.c[nt][1] = src[1];
+            v.sc[nt] = sb[b];
+        }
+    };
+    Step v0, v1;
+    int64_t base = b_begin + wave * 64;
+    load(base, v0);
+    if (hist) hist_clear(lhist);
+    bf16x8_t a[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        a[s] = m < kIdxHeads
+                   ? as_bf16x8(*(const uint4 *)(qrot + ((int64_t)r * kIdxHeads + m) * kDim + 32 * g + 8 * s))
+                   : zero_bf16x8();
+    auto score = [&](int64_t base, const Step &v) {
+        float sc[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const bf16x8_t bk[4] = {fp8x8_to_bf16x8(v.c[nt][0].x, v.c[nt][0].y),
+                                    fp8x8_to_bf16x8(v.c[nt][0].z, v.c[nt][0].w),
+                                    fp8x8_to_bf16x8(v.c[nt][1].x, v.c[nt][1].y),
+                                    fp8x8_to_bf16x8(v.c[nt][1].z, v.c[nt][1].w)};
+            f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bk[s], acc, 0, 0, 0);
+            sc[nt] = relu_sum4(acc) * v.sc[nt];
+        }
+        const int64_t b = base + 4 * m;
+        if (g == 0 && b < b_end) {
+            if (b + 3 < b_end) {
+                *(float4 *)(srow + b) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+            } else {
+                for (int j = 0; j < (int)(b_end - b); ++j) srow[b + j] = sc[j];
+            }
+            if (hist) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (b + j < b_end) atomicAdd(&lhist[score_key(sc[j]) >> kHistShift], 1u);
+            }
+        }
+    };
+    for (; base < b_end; base += 512) {
+        load(base + 256, v1);
+        __builtin_amdgcn_sched_barrier(0);
+        score(base, v0);
+        load(base + 512, v0);
+        __builtin_amdgcn_sched_barrier(0);
+        score(base + 256, v1);
+    }
+    if (hist) hist_flush(lhist, hist + (int64_t)r * kRowScratch);
+}
+
+// ---------------------------------------------------------------------------
 // fp32, any number of rows: one thread per block, q~ of the row in LDS.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void score_rows_f32_kernel(
@@ -262,6 +352,15 @@ void launch_score_rows(const void *qrot, const int32_t *row_seq, const int32_t *
     else
         QSA_LAUNCH("score_rows_f32", score_rows_f32_kernel, grid, block, 0, stream, (const float *)qrot, row_seq,
                    row_pos, (const float *)pooled, pooled_stride, max_nb, scores, sc_stride, hist);
+}
+
+void launch_score_rows_fp8(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+                           const uint8_t *codes, const float *scales, int64_t pooled_stride, int32_t max_nb,
+                           float *scores, int64_t sc_stride, uint32_t *hist, hipStream_t stream)
+{
+    const dim3 grid((unsigned)score_chunks(max_nb), (unsigned)rows), block(256);
+    QSA_LAUNCH("score_rows_fp8", score_rows_fp8_kernel, grid, block, 0, stream, (const bf16_t *)qrot, row_seq,
+               row_pos, codes, scales, pooled_stride, max_nb, scores, sc_stride, hist);
 }
 
 void launch_score_gemm(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,

@@ -128,6 +128,72 @@ __device__ __forceinline__ int32_t next_seq_group(const FusedScoreArgs &a, int64
     return seq;
 }
 
+// One thread's share of a 64-block key tile (block b of sequence seq, dims
+// ldim .. ldim + 31) on its way to LDS as bf16.  FP8 keys are read as 32
+// codes and converted when stored (exactly); their scale goes to the tile's
+// scale row, written by the first of the block's 4 threads.
+template <bool FP8> struct TileShare;
+template <> struct TileShare<false> {
+    uint4 p0, p1, p2, p3;
+    // element-wise vector loads: a plain 64-byte copy into the struct would be
+    // turned into a block copy and kept in scratch memory
+    __device__ __forceinline__ void load(const FusedScoreArgs &a, int32_t seq, int64_t b, int ldim)
+    {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t *src =
+            (const u32x4_t *)((const bf16_t *)a.pooled + (int64_t)seq * a.pooled_stride + b * kDim + ldim);
+        const u32x4_t x0 = src[0], x1 = src[1], x2 = src[2], x3 = src[3];
+        p0 = make_uint4(x0.x, x0.y, x0.z, x0.w);
+        p1 = make_uint4(x1.x, x1.y, x1.z, x1.w);
+        p2 = make_uint4(x2.x, x2.y, x2.z, x2.w);
+        p3 = make_uint4(x3.x, x3.y, x3.z, x3.w);
+    }
+    __device__ __forceinline__ void store(bf16_t *row, float *, bool) const
+    {
+        uint4 *dst = (uint4 *)row;
+        dst[0] = p0;
+        dst[1] = p1;
+        dst[2] = p2;
+        dst[3] = p3;
+    }
+};
+template <> struct TileShare<true> {
+    uint4 c[2];  // indexed with constants only
+    float s;
+    __device__ __forceinline__ void load(const FusedScoreArgs &a, int32_t seq, int64_t b, int ldim)
+    {
+        const int64_t key = (int64_t)seq * a.pooled_stride + b;
+        const uint4 *src = (const uint4 *)(a.codes + key * kDim + ldim);
+        c[0] = src[0];
+        c[1] = src[1];
+        s = a.scales[key];
+    }
+    __device__ __forceinline__ void store(bf16_t *row, float *scale, bool first) const
+    {
+        uint4 *dst = (uint4 *)row;
+        dst[0] = __builtin_bit_cast(uint4, fp8x8_to_bf16x8(c[0].x, c[0].y));
+        dst[1] = __builtin_bit_cast(uint4, fp8x8_to_bf16x8(c[0].z, c[0].w));
+        dst[2] = __builtin_bit_cast(uint4, fp8x8_to_bf16x8(c[1].x, c[1].y));
+        dst[3] = __builtin_bit_cast(uint4, fp8x8_to_bf16x8(c[1].z, c[1].w));
+        if (first) *scale = s;
+    }
+};
+
+// FP8 keys: a block's ReLU-sum times its scale (column m of slice nt is block
+// nt*16 + m of the tile).
+template <bool FP8>
+__device__ __forceinline__ void apply_scales(const float *tile_scale, float (&sc)[4][4])
+{
+    if (!FP8) return;
+    const int m = threadIdx.x & 15;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const float f = tile_scale[nt * 16 + m];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) sc[mt][nt] *= f;
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -136,11 +202,12 @@ __device__ __forceinline__ int32_t next_seq_group(const FusedScoreArgs &a, int64
 //    (samples i with i % 16 == m of each 64-sample step) and writes their
 //    keys to cand[row][split][m][0..3] (0: fewer than 4).
 // ---------------------------------------------------------------------------
+template <bool FP8>
 __global__ __launch_bounds__(256, 2) void score_sample_kernel(FusedScoreArgs a)
 {
     __shared__ bf16_t keys[kFStep][kFKRow];
+    __shared__ float tile_scale[kFStep];
     const bf16_t *__restrict__ qrot = (const bf16_t *)a.qrot;
-    const bf16_t *__restrict__ pooled = (const bf16_t *)a.pooled;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m = lane & 15, g = lane >> 4;
     const int64_t row0 = (int64_t)blockIdx.x * kFRows;
@@ -165,31 +232,18 @@ __global__ __launch_bounds__(256, 2) void score_sample_kernel(FusedScoreArgs a)
     while (todo) {
         int64_t nb_hi;
         const int32_t seq = next_seq_group(a, row0, nrows, todo, nb_hi);
-        const bf16_t *kb = pooled + (int64_t)seq * a.pooled_stride;
         const int64_t hi = min(s_hi, (nb_hi + kSampleStride - 1) / kSampleStride);  // samples that can be visible
         const int lrow = t >> 2, ldim = (t & 3) * 32;
-        uint4 p0, p1, p2, p3;
-        auto fetch = [&](int64_t i0) {
-            const int64_t b = min(sample_block(min(i0 + lrow, hi - 1)), nb_hi - 1);
-            const uint4 *src = (const uint4 *)(kb + b * kDim + ldim);
-            p0 = src[0];
-            p1 = src[1];
-            p2 = src[2];
-            p3 = src[3];
-        };
+        TileShare<FP8> ts;
+        auto fetch = [&](int64_t i0) { ts.load(a, seq, min(sample_block(min(i0 + lrow, hi - 1)), nb_hi - 1), ldim); };
         if (s_lo < hi) fetch(s_lo);
         for (int64_t i0 = s_lo; i0 < hi; i0 += kFStep) {
-            {
-                uint4 *dst = (uint4 *)&keys[lrow][ldim];
-                dst[0] = p0;
-                dst[1] = p1;
-                dst[2] = p2;
-                dst[3] = p3;
-            }
+            ts.store(&keys[lrow][ldim], &tile_scale[lrow], (t & 3) == 0);
             __syncthreads();
             if (i0 + kFStep < hi) fetch(i0 + kFStep);
             float sc[4][4];
             tile_scores(keys, qa, sc);
+            apply_scales<FP8>(tile_scale, sc);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 if (my_seq[mt] != seq) continue;
@@ -298,11 +352,12 @@ __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedScoreArgs a)
 // 3. filter: grid (row tiles, splits).  Lane (mt, g, m) owns list m of row
 //    16*wave + 4*mt + g in this split and appends its pairs >= tau there.
 // ---------------------------------------------------------------------------
+template <bool FP8>
 __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
 {
     __shared__ bf16_t keys[2][kFStep][kFKRow];
+    __shared__ float tile_scale[2][kFStep];
     const bf16_t *__restrict__ qrot = (const bf16_t *)a.qrot;
-    const bf16_t *__restrict__ pooled = (const bf16_t *)a.pooled;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m = lane & 15, g = lane >> 4;
     const int64_t row0 = (int64_t)blockIdx.x * kFRows;
@@ -346,41 +401,19 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
         lim_min = min(lim_min, (int64_t)__shfl_xor((long long)lim_min, 32));
         const int64_t lo = split_lo, hi = min(split_hi, nb_hi);
         if (lo >= hi) continue;
-        const bf16_t *kb = pooled + (int64_t)seq * a.pooled_stride;
         const int lrow = t >> 2, ldim = (t & 3) * 32;
-        uint4 p0, p1, p2, p3;  // the next tile's 64 bytes for this thread
-        {
-            const uint4 *src = (const uint4 *)(kb + min(lo + lrow, hi - 1) * kDim + ldim);
-            p0 = src[0];
-            p1 = src[1];
-            p2 = src[2];
-            p3 = src[3];
-            uint4 *dst = (uint4 *)&keys[0][lrow][ldim];
-            dst[0] = p0;
-            dst[1] = p1;
-            dst[2] = p2;
-            dst[3] = p3;
-        }
+        TileShare<FP8> ts;  // the next tile's share of this thread
+        ts.load(a, seq, min(lo + lrow, hi - 1), ldim);
+        ts.store(&keys[0][lrow][ldim], &tile_scale[0][lrow], (t & 3) == 0);
         __syncthreads();
         int cur = 0;
         for (int64_t base = lo; base < hi; base += kFStep) {
             const bool more = base + kFStep < hi;
-            if (more) {
-                const uint4 *src = (const uint4 *)(kb + min(base + kFStep + lrow, hi - 1) * kDim + ldim);
-                p0 = src[0];
-                p1 = src[1];
-                p2 = src[2];
-                p3 = src[3];
-            }
+            if (more) ts.load(a, seq, min(base + kFStep + lrow, hi - 1), ldim);
             float sc[4][4];
             tile_scores(keys[cur], qa, sc);
-            if (more) {
-                uint4 *dst = (uint4 *)&keys[cur ^ 1][lrow][ldim];
-                dst[0] = p0;
-                dst[1] = p1;
-                dst[2] = p2;
-                dst[3] = p3;
-            }
+            apply_scales<FP8>(tile_scale[cur], sc);
+            if (more) ts.store(&keys[cur ^ 1][lrow][ldim], &tile_scale[cur ^ 1][lrow], (t & 3) == 0);
             // a pair >= tau goes to the lane's list; past the list's capacity
             // the last slot is overwritten but the count goes on, so the
             // merge sees the overflow (and recomputes the row)
@@ -441,6 +474,37 @@ __device__ __forceinline__ float recompute_score(const bf16_t *__restrict__ q4, 
         }
     }
     return ((fmaxf(d[0], 0.0f) + fmaxf(d[1], 0.0f)) + fmaxf(d[2], 0.0f)) + fmaxf(d[3], 0.0f);
+}
+
+// The same for an FP8 key: codes converted exactly, the sum times the scale.
+__device__ __forceinline__ float recompute_score_fp8(const bf16_t *__restrict__ q4, const uint8_t *__restrict__ code,
+                                                     float scale)
+{
+    float d[kIdxHeads] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < kDim; i += 8) {
+        const uint2 w = *(const uint2 *)(code + i);
+        const auto k01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false), k23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+        const auto k45 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false), k67 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+        const float kv[8] = {k01[0], k01[1], k23[0], k23[1], k45[0], k45[1], k67[0], k67[1]};
+#pragma unroll
+        for (int h = 0; h < kIdxHeads; ++h) {
+            float qv[8];
+            load8(q4 + h * kDim + i, qv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d[h] = fmaf(qv[e], kv[e], d[h]);
+        }
+    }
+    return (((fmaxf(d[0], 0.0f) + fmaxf(d[1], 0.0f)) + fmaxf(d[2], 0.0f)) + fmaxf(d[3], 0.0f)) * scale;
+}
+
+template <bool FP8>
+__device__ __forceinline__ float recompute_block(const FusedScoreArgs &a, const bf16_t *q4, int32_t seq, int64_t b)
+{
+    if (FP8) {
+        const int64_t key = (int64_t)seq * a.pooled_stride + b;
+        return recompute_score_fp8(q4, a.codes + key * kDim, a.scales[key]);
+    }
+    return recompute_score(q4, (const bf16_t *)a.pooled + (int64_t)seq * a.pooled_stride + b * kDim);
 }
 
 __device__ __forceinline__ float scaled(float raw) { return (float)((double)raw / sqrt((double)kDim)); }
@@ -661,6 +725,7 @@ static_assert(kPreBins * 4 == kStage * 8, "the prefilter histogram fills the sta
 
 }  // namespace
 
+template <bool FP8>
 __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, int32_t *__restrict__ sel_blocks,
                                                          int32_t *__restrict__ sel_count, float *__restrict__ sel_scores)
 {
@@ -785,7 +850,6 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
     }
     const int32_t seq = a.row_seq[r];
     const bf16_t *q4 = (const bf16_t *)a.qrot + r * kIdxHeads * kDim;
-    const bf16_t *kb = (const bf16_t *)a.pooled + (int64_t)seq * a.pooled_stride;
     // visit every candidate, 64 at a time: fn(pair, valid).  Staged and listed
     // pairs come in no particular order; recomputed ones in block order.
     auto visit = [&](auto &&fn) {
@@ -806,7 +870,7 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
             for (int32_t b0 = 0; b0 < nc; b0 += kWave) {
                 const int32_t b = b0 + lane;
                 const bool v = b < nc;
-                fn(make_uint2(v ? pos_key(recompute_score(q4, kb + (int64_t)b * kDim)) : 0u, (uint32_t)b), v);
+                fn(make_uint2(v ? pos_key(recompute_block<FP8>(a, q4, seq, b)) : 0u, (uint32_t)b), v);
             }
         }
     };
@@ -988,15 +1052,31 @@ int32_t fused_score_ssplit(int32_t rows, int32_t nsample)
 void launch_score_fused(const FusedScoreArgs &a, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
                         hipStream_t stream)
 {
+    const bool fp8 = a.codes != nullptr;
     if (a.max_nb > 0) {
         const unsigned tiles = (unsigned)((a.rows + kFRows - 1) / kFRows);
-        QSA_LAUNCH("score_sample", score_sample_kernel, dim3(tiles, (unsigned)a.ssplit), dim3(256), 0, stream, a);
+        if (fp8)
+            QSA_LAUNCH("score_sample_fp8", score_sample_kernel<true>, dim3(tiles, (unsigned)a.ssplit), dim3(256), 0,
+                       stream, a);
+        else
+            QSA_LAUNCH("score_sample", score_sample_kernel<false>, dim3(tiles, (unsigned)a.ssplit), dim3(256), 0,
+                       stream, a);
         QSA_LAUNCH("sample_threshold", sample_threshold_kernel, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0,
                    stream, a);
-        QSA_LAUNCH("score_filter", score_filter_kernel, dim3(tiles, (unsigned)a.nsplit), dim3(256), 0, stream, a);
+        if (fp8)
+            QSA_LAUNCH("score_filter_fp8", score_filter_kernel<true>, dim3(tiles, (unsigned)a.nsplit), dim3(256), 0,
+                       stream, a);
+        else
+            QSA_LAUNCH("score_filter", score_filter_kernel<false>, dim3(tiles, (unsigned)a.nsplit), dim3(256), 0,
+                       stream, a);
     }
-    QSA_LAUNCH("select_merge", select_merge_kernel, dim3((unsigned)((a.rows + kMergeWaves - 1) / kMergeWaves)),
-               dim3(kMergeWaves * kWave), 0, stream, a, sel_blocks, sel_count, sel_scores);
+    const dim3 mgrid((unsigned)((a.rows + kMergeWaves - 1) / kMergeWaves)), mblock(kMergeWaves * kWave);
+    if (fp8)
+        QSA_LAUNCH("select_merge", select_merge_kernel<true>, mgrid, mblock, 0, stream, a, sel_blocks, sel_count,
+                   sel_scores);
+    else
+        QSA_LAUNCH("select_merge", select_merge_kernel<false>, mgrid, mblock, 0, stream, a, sel_blocks, sel_count,
+                   sel_scores);
 }
 
 }  // namespace qsa

@@ -25,7 +25,8 @@ FLAG_SCORE_GEMM = 1 << 9
 INDEX_DIM, INDEX_HEADS, BLOCK_TOKENS, MAX_TOP_K, MAX_QUERY_GROUP = 128, 4, 4, 4096, 64
 
 # every symbol include/qsa.h declares
-EXPORTS = ("qsa_pool_index_keys", "qsa_pool_append", "qsa_score_topk_workspace_size", "qsa_score_topk",
+EXPORTS = ("qsa_pool_index_keys", "qsa_pool_index_keys_fp8", "qsa_pool_append", "qsa_score_topk_workspace_size",
+           "qsa_score_topk", "qsa_score_topk_fp8_workspace_size", "qsa_score_topk_fp8",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode_workspace_size",
            "qsa_sparse_attn_decode", "qsa_status_string", "qsa_last_device_error", "qsa_profile_enable",
            "qsa_profile_reset", "qsa_profile_kernel_ms")
@@ -63,6 +64,12 @@ def load():
     st = ctypes.c_int
     lib.qsa_pool_index_keys.argtypes = [P, i64, P, i64, i32, i32, i32, f64, u32, st, P]
     lib.qsa_pool_index_keys.restype = st
+    lib.qsa_pool_index_keys_fp8.argtypes = [P, i64, P, P, i64, i32, i32, i32, f64, u32, st, P]
+    lib.qsa_pool_index_keys_fp8.restype = st
+    lib.qsa_score_topk_fp8_workspace_size.argtypes = [i32, i32, i32, u32]
+    lib.qsa_score_topk_fp8_workspace_size.restype = sz
+    lib.qsa_score_topk_fp8.argtypes = [P, P, P, i32, P, P, i64, i32, i32, f64, u32, P, P, P, P, sz, P]
+    lib.qsa_score_topk_fp8.restype = st
     lib.qsa_pool_append.argtypes = [P, P, P, P, P, i32, f64, u32, st, P]
     lib.qsa_pool_append.restype = st
     lib.qsa_score_topk_workspace_size.argtypes = [i32, i32, i32, st, u32]
@@ -143,6 +150,19 @@ def pool_index_keys(raw_keys, pooled, block_begin: int, block_end: int, rope_the
     _check("qsa_pool_index_keys", rc)
 
 
+def pool_index_keys_fp8(raw_keys, codes, scales, block_begin: int, block_end: int, rope_theta: float,
+                        flags: int = 0, stream=None):
+    """a1-a3 with FP8 storage: codes [B][NB][128] uint8 (E4M3) and scales
+    [B][NB] float32 from `raw_keys` [B][L][128] (bf16 or float32)."""
+    _need_contig(raw_keys, codes, scales)
+    B, L, _ = raw_keys.shape
+    assert codes.shape[:2] == scales.shape and codes.shape[2] == INDEX_DIM
+    rc = load().qsa_pool_index_keys_fp8(_ptr(raw_keys), L * INDEX_DIM, _ptr(codes), _ptr(scales), codes.shape[1], B,
+                                        int(block_begin), int(block_end), float(rope_theta), int(flags),
+                                        _dtype_code(raw_keys), _stream(stream))
+    _check("qsa_pool_index_keys_fp8", rc)
+
+
 def pool_append(new_keys, positions, full_slots, ring, compressed, rope_theta: float, flags: int = 0,
                 stream=None):
     """One decode step of incremental pooling: new_keys [B][128] into the
@@ -186,6 +206,36 @@ def score_topk(q_index, row_seq, row_pos, pooled, max_visible_blocks: int, top_k
                                float(rope_theta), int(flags), dt, _ptr(sel_blocks), _ptr(sel_count),
                                _ptr(sel_scores), _ptr(workspace), workspace.numel(), _stream(stream))
     _check("qsa_score_topk", rc)
+    return sel_blocks, sel_count, sel_scores
+
+
+def score_topk_fp8_workspace_size(rows: int, max_visible_blocks: int, top_k: int, flags: int = 0) -> int:
+    return int(load().qsa_score_topk_fp8_workspace_size(int(rows), int(max_visible_blocks), int(top_k), int(flags)))
+
+
+def score_topk_fp8(q_index, row_seq, row_pos, codes, scales, max_visible_blocks: int, top_k: int,
+                   rope_theta: float, flags: int = 0, sel_blocks=None, sel_count=None, sel_scores=None,
+                   workspace=None, want_scores: bool = True, stream=None):
+    """a4-a6 on FP8 keys (codes [B][NB][128] uint8, scales [B][NB] float32);
+    q_index bf16.  Returns as score_topk."""
+    import torch
+    _need_contig(q_index, row_seq, row_pos, codes, scales)
+    R = q_index.shape[0]
+    dev = q_index.device
+    if sel_blocks is None:
+        sel_blocks = torch.empty((R, top_k), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty((R,), dtype=torch.int32, device=dev)
+    if sel_scores is None and want_scores:
+        sel_scores = torch.empty((R, top_k), dtype=torch.float32, device=dev)
+    need = score_topk_fp8_workspace_size(R, max_visible_blocks, top_k, flags)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    rc = load().qsa_score_topk_fp8(_ptr(q_index), _ptr(row_seq), _ptr(row_pos), R, _ptr(codes), _ptr(scales),
+                                   codes.shape[1], int(max_visible_blocks), int(top_k), float(rope_theta), int(flags),
+                                   _ptr(sel_blocks), _ptr(sel_count), _ptr(sel_scores), _ptr(workspace),
+                                   workspace.numel(), _stream(stream))
+    _check("qsa_score_topk_fp8", rc)
     return sel_blocks, sel_count, sel_scores
 
 

@@ -99,6 +99,26 @@ qsa_status_t qsa_pool_index_keys(const void *raw_keys, int64_t raw_seq_stride, v
                                  qsa_dtype_t dtype, void *stream);
 
 /*
+ * Steps a1-a3 with the compressed keys stored in FP8 ([LBL] section "Serving
+ * it": the deployment keeps the indexer's keys in FP8).  Each block is pooled
+ * and rotated exactly as by qsa_pool_index_keys, then rounded to FP32; with
+ * amax its largest magnitude, inv = 448 / amax and scale = amax / 448 (IEEE
+ * FP32 quotients), and element d is stored as the OCP FP8 E4M3 code of
+ * k_d * inv (FP32 product, nearest-even).  The key stands for code * scale.
+ * A zero key gets scale 0 and zero codes.
+ *   raw_keys  [batch][raw_seq_stride] of raw_dtype (bf16 or fp32), as above.
+ *   codes     [batch][pooled_seq_stride][128] bytes; block b of sequence s at
+ *             codes + (s*pooled_seq_stride + b)*128.  16-byte aligned.
+ *   scales    [batch][pooled_seq_stride] fp32, one per key.  4-byte aligned.
+ *   pooled_seq_stride counts keys (blocks), not bytes.  Blocks outside
+ *   [block_begin, block_end) are not touched.
+ */
+qsa_status_t qsa_pool_index_keys_fp8(const void *raw_keys, int64_t raw_seq_stride, uint8_t *codes,
+                                     float *scales, int64_t pooled_seq_stride, int32_t batch,
+                                     int32_t block_begin, int32_t block_end, double rope_theta,
+                                     uint32_t flags, qsa_dtype_t raw_dtype, void *stream);
+
+/*
  * Incremental pooling for decode ([SGL] section "Qwen Sparse Attention": the
  * raw index keys of a request's unfinished block live in a four-slot
  * per-request ring, and the compressed cache is addressed by page-aligned
@@ -159,6 +179,22 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
                             uint32_t flags, qsa_dtype_t dtype, int32_t *sel_blocks,
                             int32_t *sel_count, float *sel_scores, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/*
+ * qsa_score_topk on FP8 keys (as written by qsa_pool_index_keys_fp8).  The
+ * index queries are bf16 and rotated as in qsa_score_topk; the key of block b
+ * is code_b * scale_b, so raw(t,b) = scale_b * sum_h max(0, <q~_h, code_b>)
+ * (a non-negative scale commutes with the ReLUs).  Selection, outputs and
+ * workspace rules are those of qsa_score_topk; pooled_seq_stride counts keys.
+ */
+size_t qsa_score_topk_fp8_workspace_size(int32_t rows, int32_t max_visible_blocks, int32_t top_k,
+                                         uint32_t flags);
+qsa_status_t qsa_score_topk_fp8(const void *q_index, const int32_t *row_seq, const int32_t *row_pos,
+                                int32_t rows, const uint8_t *codes, const float *scales,
+                                int64_t pooled_seq_stride, int32_t max_visible_blocks, int32_t top_k,
+                                double rope_theta, uint32_t flags, int32_t *sel_blocks,
+                                int32_t *sel_count, float *sel_scores, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /*
  * Steps a7+a8 ([SGL]: expansion of the kept blocks to token positions, the

@@ -60,6 +60,14 @@ def _load():
     lib.qsa_oracle_rope.restype = None
     lib.qsa_oracle_pool.argtypes = [P, i64, P, i64, i32, i32, i32, f64, u32, i32]
     lib.qsa_oracle_pool.restype = ctypes.c_int
+    lib.qsa_oracle_fp8_to_double.argtypes = [ctypes.c_uint8]
+    lib.qsa_oracle_fp8_to_double.restype = f64
+    lib.qsa_oracle_fp8_from_double.argtypes = [f64]
+    lib.qsa_oracle_fp8_from_double.restype = ctypes.c_uint8
+    lib.qsa_oracle_pool_fp8.argtypes = [P, i64, P, P, i64, i32, i32, i32, f64, u32, i32]
+    lib.qsa_oracle_pool_fp8.restype = ctypes.c_int
+    lib.qsa_oracle_score_topk_fp8.argtypes = [P, i32, P, P, i32, P, P, i64, i32, f64, u32, P, P, P, P, i64]
+    lib.qsa_oracle_score_topk_fp8.restype = ctypes.c_int
     lib.qsa_oracle_pool_append.argtypes = [P, P, P, P, P, i32, f64, u32, i32]
     lib.qsa_oracle_pool_append.restype = ctypes.c_int
     lib.qsa_oracle_score_topk.argtypes = [P, P, P, i32, P, i64, i32, f64, u32, i32, P, P, P, P, i64]
@@ -115,6 +123,22 @@ def bf16_from_float(x) -> np.ndarray:
     return out.reshape(x.shape)
 
 
+def fp8_to_float(codes) -> np.ndarray:
+    """E4M3 codes (uint8) -> values (float64, NaN for the NaN codes)."""
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8)
+    table = np.array([lib.qsa_oracle_fp8_to_double(c) for c in range(256)], dtype=np.float64)
+    return table[codes]
+
+
+def fp8_from_float(x) -> np.ndarray:
+    """values -> E4M3 codes (uint8), nearest with ties to the even code."""
+    lib = _load()
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array([lib.qsa_oracle_fp8_from_double(float(v)) for v in x.reshape(-1)], dtype=np.uint8)
+    return out.reshape(x.shape)
+
+
 def rope(vec, pos: int, theta: float) -> np.ndarray:
     """Rotate one 128-d vector (float64) at `pos`; returns a new array."""
     v = np.array(vec, dtype=np.float64, copy=True).reshape(DIM)
@@ -137,6 +161,25 @@ def pool(raw, block_begin: int, block_end: int, theta: float, flags: int = 0,
                                  int(block_begin), int(block_end), float(theta), int(flags), dt)
     _check(rc, "pool")
     return pooled
+
+
+def pool_fp8(raw, block_begin: int, block_end: int, theta: float, flags: int = 0, codes=None, scales=None):
+    """a1-a3 with FP8 storage (see qsa_oracle_pool_fp8).  raw: [B][L][128]
+    (uint16 bf16 bits or float32).  Returns (or fills) codes [B][NB][128]
+    uint8 and scales [B][NB] float32, NB = codes.shape[1] or block_end."""
+    raw = _c(raw)
+    dt = _dtype_code(raw)
+    B, L, d = raw.shape
+    assert d == DIM and 4 * block_end <= L
+    if codes is None:
+        codes = np.zeros((B, block_end, DIM), dtype=np.uint8)
+        scales = np.zeros((B, block_end), dtype=np.float32)
+    assert codes.dtype == np.uint8 and scales.dtype == np.float32 and codes.shape[:2] == scales.shape
+    assert codes.flags.c_contiguous and scales.flags.c_contiguous
+    rc = _load().qsa_oracle_pool_fp8(_ptr(raw), L * DIM, _ptr(codes), _ptr(scales), codes.shape[1], B,
+                                     int(block_begin), int(block_end), float(theta), int(flags), dt)
+    _check(rc, "pool_fp8")
+    return codes, scales
 
 
 def pool_append(new_keys, positions, full_slots, ring, compressed, theta: float, flags: int = 0):
@@ -182,6 +225,33 @@ def score_topk(q_index, row_seq, row_pos, pooled, top_k: int, theta: float, flag
                                        NB * DIM, int(top_k), float(theta), int(flags), dt,
                                        _ptr(sel), _ptr(cnt), _ptr(sc), _ptr(raw), NB)
     _check(rc, "score_topk")
+    return sel, cnt, sc, raw
+
+
+def score_topk_fp8(q_index, row_seq, row_pos, codes, scales, top_k: int, theta: float, flags: int = 0,
+                   want_raw: bool = False):
+    """a4-a6 on FP8 keys.  q_index: [R][4][128] (bf16 bits or float32);
+    codes: [B][NB][128] uint8; scales: [B][NB] float32.  Returns as
+    score_topk."""
+    q_index = _c(q_index)
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    dt = _dtype_code(q_index)
+    row_seq = _c(row_seq, np.int32)
+    row_pos = _c(row_pos, np.int32)
+    R = q_index.shape[0]
+    NB = codes.shape[1]
+    assert q_index.shape[1:] == (IDX_HEADS, DIM) and codes.shape[2] == DIM and scales.shape == codes.shape[:2]
+    for r in range(R):
+        assert (int(row_pos[r]) + 1) // BLOCK <= NB
+    sel = np.empty((R, top_k), np.int32)
+    cnt = np.empty((R,), np.int32)
+    sc = np.empty((R, top_k), np.float32)
+    raw = np.full((R, NB), np.nan, np.float64) if want_raw else None
+    rc = _load().qsa_oracle_score_topk_fp8(_ptr(q_index), dt, _ptr(row_seq), _ptr(row_pos), R, _ptr(codes),
+                                           _ptr(scales), NB, int(top_k), float(theta), int(flags), _ptr(sel),
+                                           _ptr(cnt), _ptr(sc), _ptr(raw), NB)
+    _check(rc, "score_topk_fp8")
     return sel, cnt, sc, raw
 
 

@@ -93,6 +93,56 @@ uint16_t qsa_oracle_bf16_from_double(double x)
     return x < 0 ? (uint16_t)(h | 0x8000u) : h;
 }
 
+/*
+ * FP8 E4M3 (the OCP 8-bit format: 1 sign bit, 4 exponent bits with bias 7, 3
+ * mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; exponent
+ * 15 with mantissa 7 is NaN; no infinities; largest finite value 448).
+ * Reading: "Qwen3.8-Flash-Next, Layer by Layer", section "Serving it", stores
+ * the indexer's keys in FP8 without naming the variant; E4M3 is the FP8 KV
+ * format of the engines it names.
+ */
+double qsa_oracle_fp8_to_double(uint8_t c)
+{
+    int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double v = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/*
+ * x -> E4M3 code: the nearest representable value, ties to the even code
+ * (mantissa lsb 0).  Magnitudes beyond 464 (halfway from 448 to the next
+ * binade step) have no finite neighbour and give NaN (0x7f / 0xff); the key
+ * scaling below never produces them.  The value is located on the grid of
+ * its binade: spacing 2^-9 below 2^-6, else 2^(e-3) for 2^e <= |x| < 2^(e+1).
+ */
+uint8_t qsa_oracle_fp8_from_double(double x)
+{
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double a = fabs(x);
+    if (isnan(a) || a > 464.0)
+        return sign | 0x7f;
+    double q;  /* grid spacing at a */
+    if (a < ldexp(1.0, -6)) {
+        q = ldexp(1.0, -9);
+    } else {
+        int e;
+        frexp(a, &e);          /* a = f * 2^e, 0.5 <= f < 1: binade [2^(e-1), 2^e) */
+        q = ldexp(1.0, e - 1 - 3);
+    }
+    double r = nearbyint(a / q) * q;  /* a / q is exact; nearbyint rounds ties to even */
+    if (r == 0.0)
+        return sign;
+    if (r < ldexp(1.0, -6))            /* subnormal: mantissa = r / 2^-9 */
+        return sign | (uint8_t)(r / ldexp(1.0, -9));
+    int e;
+    double f = frexp(r, &e);           /* r = f * 2^e, f in [0.5, 1) */
+    int ef = e - 1 + 7;                /* biased exponent of r = (2f) * 2^(e-1) */
+    int mant = (int)((2.0 * f - 1.0) * 8.0);
+    return sign | (uint8_t)(ef << 3) | (uint8_t)mant;
+}
+
 static double load_elem(const void *base, int64_t idx, int dtype)
 {
     if (dtype == OR_BF16)
@@ -255,6 +305,67 @@ int qsa_oracle_pool_append(const void *new_keys, const int32_t *positions, const
     return OR_OK;
 }
 
+/*
+ * a1-a3 with the compressed key stored in FP8 ("Qwen3.8-Flash-Next, Layer by
+ * Layer", section "Serving it": the indexer's keys kept in FP8).  The block
+ * is pooled and rotated exactly as qsa_oracle_pool does, the rotated key is
+ * rounded to FP32, and one FP32 scale per key carries its range.  Reading
+ * (the pages give no scaling): the largest magnitude amax maps to 448, the
+ * largest E4M3 value:
+ *     inv = 448 / amax, scale = amax / 448    (FP32 quotients)
+ *     code_d = E4M3(k_d * inv)                (FP32 product, then nearest-even)
+ * and a zero key gets scale 0 and zero codes.  Key element d stands for
+ * code_d * scale.
+ * raw:    [batch][raw_seq_stride] elements of raw_dtype (as qsa_oracle_pool).
+ * codes:  [batch][pooled_seq_stride * 128] bytes, block b at codes + (s*stride + b)*128.
+ * scales: [batch][pooled_seq_stride] FP32, block b at scales + s*stride + b.
+ */
+int qsa_oracle_pool_fp8(const void *raw, int64_t raw_seq_stride, uint8_t *codes, float *scales,
+                        int64_t pooled_seq_stride, int32_t batch, int32_t block_begin, int32_t block_end,
+                        double theta, uint32_t flags, int32_t raw_dtype)
+{
+    if (!raw || !codes || !scales || batch < 0 || block_begin < 0 || block_end < block_begin)
+        return OR_ERR_ARG;
+    int64_t nblk = (int64_t)block_end - block_begin;
+    int64_t total = (int64_t)batch * nblk;
+#pragma omp parallel for schedule(static)
+    for (int64_t w = 0; w < total; ++w) {
+        int64_t s = w / nblk;
+        int64_t b = block_begin + w % nblk;
+        double m[OR_DIM];
+        for (int d = 0; d < OR_DIM; ++d) {
+            float acc = 0.0f;
+            for (int i = 0; i < OR_BLOCK; ++i)
+                acc += (float)load_elem(raw, s * raw_seq_stride + (OR_BLOCK * b + i) * OR_DIM + d, raw_dtype);
+            m[d] = (double)(acc * 0.25f);
+        }
+        if (flags & OR_FLAG_POOL_RMSNORM) {
+            double ss = 0.0;
+            for (int d = 0; d < OR_DIM; ++d)
+                ss += m[d] * m[d];
+            double inv = 1.0 / sqrt(ss / OR_DIM + 1e-6);
+            for (int d = 0; d < OR_DIM; ++d)
+                m[d] *= inv;
+        }
+        if (!(flags & OR_FLAG_NO_ROPE))
+            qsa_oracle_rope(m, OR_BLOCK * b, theta);
+        float k[OR_DIM];
+        float amax = 0.0f;
+        for (int d = 0; d < OR_DIM; ++d) {
+            k[d] = (float)m[d];
+            amax = fabsf(k[d]) > amax ? fabsf(k[d]) : amax;
+        }
+        const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+        const int64_t slot = s * pooled_seq_stride + b;
+        scales[slot] = amax / 448.0f;
+        for (int d = 0; d < OR_DIM; ++d) {
+            const float v = k[d] * inv;
+            codes[slot * OR_DIM + d] = qsa_oracle_fp8_from_double((double)v);
+        }
+    }
+    return OR_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* a4-a6: query rotation, block scores, top-k selection                      */
 /* ------------------------------------------------------------------------ */
@@ -288,6 +399,36 @@ static int by_int_asc(const void *pa, const void *pb)
     return (a > b) - (a < b);
 }
 
+/* Where the compressed keys come from: `pooled` elements of `dtype`, or FP8
+ * codes with one scale per key (see qsa_oracle_pool_fp8). */
+typedef struct {
+    const void *pooled;
+    int dtype;
+    const uint8_t *codes;
+    const float *scales;
+} key_source;
+
+/*
+ * [SGL] score equation for one block (key slot `slot` = s*stride + b):
+ * sum_h ReLU(<q~_h, kbar_b>), in double precision.  For an FP8 key,
+ * kbar_b = code_b * scale_b, and the non-negative scale is taken out of the
+ * ReLU: scale_b * sum_h ReLU(<q~_h, code_b>).
+ */
+static double block_raw(const double q[OR_IDX_HEADS][OR_DIM], const key_source *ks, int64_t slot)
+{
+    double sum = 0.0;
+    for (int h = 0; h < OR_IDX_HEADS; ++h) {
+        double dot = 0.0;
+        for (int d = 0; d < OR_DIM; ++d) {
+            const double k = ks->codes ? qsa_oracle_fp8_to_double(ks->codes[slot * OR_DIM + d])
+                                       : load_elem(ks->pooled, slot * OR_DIM + d, ks->dtype);
+            dot += q[h][d] * k;
+        }
+        sum += dot > 0.0 ? dot : 0.0; /* ReLU */
+    }
+    return ks->codes ? (double)ks->scales[slot] * sum : sum;
+}
+
 /*
  * Scores and selection for `rows` query rows.
  *
@@ -302,20 +443,17 @@ static int by_int_asc(const void *pa, const void *pb)
  * ties go to the lower block index; the kept blocks are listed in ascending
  * order and padded with -1.
  *
- * q_index: [rows][4][128], un-rotated.  pooled: see qsa_oracle_pool.
- * sel_blocks: [rows][top_k]; sel_count: [rows]; sel_scores ([rows][top_k],
- * may be NULL) gets s_{t,b} of each kept block.  raw_out (may be NULL) gets
- * the un-scaled sum of every visible block: raw_out[r*raw_stride + b].
+ * q_index: [rows][4][128] of q_dtype, un-rotated.  `stride` counts keys per
+ * sequence.  sel_blocks: [rows][top_k]; sel_count: [rows]; sel_scores
+ * ([rows][top_k], may be NULL) gets s_{t,b} of each kept block.  raw_out (may
+ * be NULL) gets the un-scaled sum of every visible block:
+ * raw_out[r*raw_stride + b].
  */
-int qsa_oracle_score_topk(const void *q_index, const int32_t *row_seq, const int32_t *row_pos,
-                          int32_t rows, const void *pooled, int64_t pooled_seq_stride,
-                          int32_t top_k, double theta, uint32_t flags, int32_t dtype,
-                          int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
-                          double *raw_out, int64_t raw_stride)
+static int score_topk_core(const void *q_index, int q_dtype, const int32_t *row_seq, const int32_t *row_pos,
+                           int32_t rows, const key_source *ks, int64_t stride, int32_t top_k, double theta,
+                           uint32_t flags, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
+                           double *raw_out, int64_t raw_stride)
 {
-    if (rows < 0 || top_k < 1 || !q_index || !row_seq || !row_pos || !pooled || !sel_blocks ||
-        !sel_count)
-        return OR_ERR_ARG;
     int failed = 0;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int32_t r = 0; r < rows; ++r) {
@@ -325,11 +463,11 @@ int qsa_oracle_score_topk(const void *q_index, const int32_t *row_seq, const int
         double q[OR_IDX_HEADS][OR_DIM];
         for (int h = 0; h < OR_IDX_HEADS; ++h) {
             for (int d = 0; d < OR_DIM; ++d)
-                q[h][d] = load_elem(q_index, ((int64_t)r * OR_IDX_HEADS + h) * OR_DIM + d, dtype);
+                q[h][d] = load_elem(q_index, ((int64_t)r * OR_IDX_HEADS + h) * OR_DIM + d, q_dtype);
             if (!(flags & OR_FLAG_NO_ROPE))
                 qsa_oracle_rope(q[h], t, theta);
             for (int d = 0; d < OR_DIM; ++d)
-                q[h][d] = round_to_dtype(q[h][d], dtype);
+                q[h][d] = round_to_dtype(q[h][d], q_dtype);
         }
         scored_block *all = (scored_block *)malloc(sizeof(scored_block) * (size_t)(nc > 0 ? nc : 1));
         if (!all) {
@@ -337,14 +475,7 @@ int qsa_oracle_score_topk(const void *q_index, const int32_t *row_seq, const int
             continue;
         }
         for (int64_t b = 0; b < nc; ++b) {
-            const int64_t base = s * pooled_seq_stride + b * OR_DIM;
-            double sum = 0.0;
-            for (int h = 0; h < OR_IDX_HEADS; ++h) {
-                double dot = 0.0;
-                for (int d = 0; d < OR_DIM; ++d)
-                    dot += q[h][d] * load_elem(pooled, base + d, dtype);
-                sum += dot > 0.0 ? dot : 0.0; /* ReLU */
-            }
+            const double sum = block_raw(q, ks, s * stride + b);
             all[b].raw = sum;
             all[b].block = (int32_t)b;
             if (raw_out)
@@ -365,23 +496,46 @@ int qsa_oracle_score_topk(const void *q_index, const int32_t *row_seq, const int
         if (sel_scores) {
             /* scores of the kept blocks, listed in the same (ascending) order */
             float *so = sel_scores + (int64_t)r * top_k;
-            for (int64_t i = 0; i < keep; ++i) {
-                double raw = 0.0;
-                const int64_t base = s * pooled_seq_stride + (int64_t)out[i] * OR_DIM;
-                for (int h = 0; h < OR_IDX_HEADS; ++h) {
-                    double dot = 0.0;
-                    for (int d = 0; d < OR_DIM; ++d)
-                        dot += q[h][d] * load_elem(pooled, base + d, dtype);
-                    raw += dot > 0.0 ? dot : 0.0;
-                }
-                so[i] = (float)(raw / sqrt((double)OR_DIM));
-            }
+            for (int64_t i = 0; i < keep; ++i)
+                so[i] = (float)(block_raw(q, ks, s * stride + out[i]) / sqrt((double)OR_DIM));
             for (int64_t i = keep; i < top_k; ++i)
                 so[i] = 0.0f;
         }
         free(all);
     }
     return failed ? OR_ERR_ALLOC : OR_OK;
+}
+
+/* pooled: see qsa_oracle_pool; pooled_seq_stride counts elements. */
+int qsa_oracle_score_topk(const void *q_index, const int32_t *row_seq, const int32_t *row_pos,
+                          int32_t rows, const void *pooled, int64_t pooled_seq_stride,
+                          int32_t top_k, double theta, uint32_t flags, int32_t dtype,
+                          int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
+                          double *raw_out, int64_t raw_stride)
+{
+    if (rows < 0 || top_k < 1 || !q_index || !row_seq || !row_pos || !pooled || !sel_blocks ||
+        !sel_count || pooled_seq_stride % OR_DIM)
+        return OR_ERR_ARG;
+    const key_source ks = {pooled, dtype, NULL, NULL};
+    return score_topk_core(q_index, dtype, row_seq, row_pos, rows, &ks, pooled_seq_stride / OR_DIM, top_k, theta,
+                           flags, sel_blocks, sel_count, sel_scores, raw_out, raw_stride);
+}
+
+/* The same with FP8 keys (see qsa_oracle_pool_fp8); pooled_seq_stride counts
+ * keys.  The index query stays in q_dtype (the pages put only the stored keys
+ * in FP8). */
+int qsa_oracle_score_topk_fp8(const void *q_index, int32_t q_dtype, const int32_t *row_seq,
+                              const int32_t *row_pos, int32_t rows, const uint8_t *codes, const float *scales,
+                              int64_t pooled_seq_stride, int32_t top_k, double theta, uint32_t flags,
+                              int32_t *sel_blocks, int32_t *sel_count, float *sel_scores, double *raw_out,
+                              int64_t raw_stride)
+{
+    if (rows < 0 || top_k < 1 || !q_index || !row_seq || !row_pos || !codes || !scales || !sel_blocks ||
+        !sel_count)
+        return OR_ERR_ARG;
+    const key_source ks = {NULL, 0, codes, scales};
+    return score_topk_core(q_index, q_dtype, row_seq, row_pos, rows, &ks, pooled_seq_stride, top_k, theta, flags,
+                           sel_blocks, sel_count, sel_scores, raw_out, raw_stride);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -112,6 +112,26 @@ def test_score_topk_validation(libqsa):
     assert call(theta=float("nan")) == qsa.ERR_INVALID_ARG
 
 
+def test_fp8_validation(libqsa):
+    f = libqsa.qsa_pool_index_keys_fp8
+    assert f(A, 1024, B_, C, 8, 0, 0, 2, 1e7, 0, qsa.BF16, None) == qsa.OK          # empty batch
+    assert f(A, 1024, B_, C, 8, 2, 0, 2, 1e7, 0, 7, None) == qsa.ERR_UNSUPPORTED
+    assert f(A, 1024, MIS, C, 8, 2, 0, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG  # codes misaligned
+    assert f(A, 1024, B_, None, 8, 2, 0, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG
+    assert f(A, 1024, B_, C + 2, 8, 2, 0, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG  # scales misaligned
+    assert f(A, 1024, B_, C, 1, 2, 0, 2, 1e7, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG  # stride < blocks
+    assert f(A, 1024, B_, C, 8, 2, 0, 2, 0.5, 0, qsa.BF16, None) == qsa.ERR_INVALID_ARG  # theta
+    g = libqsa.qsa_score_topk_fp8
+    ws = qsa.score_topk_fp8_workspace_size(4, 100, 16)
+    assert ws == qsa.score_topk_workspace_size(4, 100, 16, qsa.BF16)
+    assert g(A, B_, C, 0, B_, C, 100, 100, 16, 1e7, 0, B_, C, None, 0x100000, ws, None) == qsa.OK
+    assert g(A, B_, C, 4, B_, C, 100, 100, 16, 1e7, 0, B_, C, None, 0x100000, ws - 1, None) == qsa.ERR_WORKSPACE
+    assert g(A, B_, C, 4, MIS, C, 100, 100, 16, 1e7, 0, B_, C, None, 0x100000, ws, None) == qsa.ERR_INVALID_ARG
+    assert g(A, B_, C, 4, B_, None, 100, 100, 16, 1e7, 0, B_, C, None, 0x100000, ws, None) == qsa.ERR_INVALID_ARG
+    assert g(A, B_, C, 4, B_, C, 100, 100, 0, 1e7, 0, B_, C, None, 0x100000, ws, None) == qsa.ERR_INVALID_ARG
+    assert g(A, B_, C, 4, B_, C, -1, 100, 16, 1e7, 0, B_, C, None, 0x100000, ws, None) == qsa.ERR_INVALID_ARG
+
+
 def test_attn_validation(libqsa):
     fp = libqsa.qsa_sparse_attn_prefill
     # rows == 0 -> OK without touching anything

@@ -567,3 +567,110 @@ def test_attention_bf16_output_is_rounded():
     outb, _ = oracle.sparse_attn_prefill(qb, [0] * 4, pos, kb, vb, sel, cnt)
     want = torch.from_numpy(out32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.abs(outb.astype(np.int32) - want.astype(np.int32)).max() <= 1
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3 index keys ("Qwen3.8-Flash-Next, Layer by Layer", "Serving it":
+# the indexer's keys stored in FP8)
+# --------------------------------------------------------------------------
+
+def _e4m3_table():
+    """Every finite E4M3 value, decoded from the bit fields of the OCP format
+    (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is
+    subnormal; 0x7f / 0xff are NaN) -- written from the format, not from the
+    oracle's rounding."""
+    vals = {}
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            continue
+        v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        vals[c] = -v if s else v
+    return vals
+
+
+def test_fp8_known_values():
+    t = oracle.fp8_to_float(np.array([0x7E, 0x01, 0x07, 0x08, 0x38, 0x40, 0xB8, 0x00, 0x80], np.uint8))
+    assert list(t) == [448.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 2.0, -1.0, 0.0, -0.0]
+    assert np.isnan(oracle.fp8_to_float(np.array([0x7F, 0xFF], np.uint8))).all()
+    table = _e4m3_table()
+    assert len(table) == 254 and max(table.values()) == 448.0
+
+
+def test_fp8_every_code_round_trips():
+    table = _e4m3_table()
+    codes = np.array(sorted(table), np.uint8)
+    np.testing.assert_array_equal(oracle.fp8_to_float(codes), np.array([table[c] for c in codes]))
+    np.testing.assert_array_equal(oracle.fp8_from_float(oracle.fp8_to_float(codes)), codes)
+
+
+def test_fp8_rounding_is_nearest_even_by_brute_force():
+    # against a scan of the whole value table: nearest value, ties to the
+    # code with an even mantissa (lsb 0)
+    table = _e4m3_table()
+    pos = sorted((v, c) for c, v in table.items() if c < 0x80)
+    rng = np.random.default_rng(41)
+    mags = 2.0 ** rng.uniform(-12, np.log2(464.0), 3000)
+    mids = [0.5 * (pos[i][0] + pos[i + 1][0]) for i in range(len(pos) - 1)]
+    xs = np.concatenate([mags, -mags[:500], np.array(mids), -np.array(mids[:40])])
+    want = []
+    for x in xs:
+        best = min(pos, key=lambda vc: (abs(abs(x) - vc[0]), vc[1] & 1))
+        want.append(best[1] | (0x80 if x < 0 and best[0] != 0.0 else 0) if best[0] != 0.0 else (0x80 if x < 0 else 0))
+    np.testing.assert_array_equal(oracle.fp8_from_float(xs), np.array(want, np.uint8))
+    # beyond 464 there is no finite neighbour: NaN
+    assert list(oracle.fp8_from_float([470.0, -1e6])) == [0x7F, 0xFF]
+
+
+def test_pool_fp8_max_maps_to_448_and_error_within_half_step():
+    rng = np.random.default_rng(43)
+    raw = synth.bf16_bits(rng.standard_normal((2, 64, DIM)).astype(np.float32) * 3)
+    codes, scales = oracle.pool_fp8(raw, 0, 16, 1e7)
+    ref = oracle.pool(synth.bf16_to_f32(raw).astype(np.float32), 0, 16, 1e7)   # the FP32-rounded rotated keys
+    table = _e4m3_table()
+    vals = oracle.fp8_to_float(codes)
+    amax = np.abs(ref).max(-1)
+    np.testing.assert_array_equal(scales, (amax / np.float32(448)).astype(np.float32))
+    # the largest magnitude of each key is the largest code
+    arg = np.abs(ref).argmax(-1)
+    got = np.take_along_axis(np.abs(vals), arg[..., None], -1)[..., 0]
+    assert (got == 448.0).all()
+    # every element within half an E4M3 step of the scaled value (step at the
+    # scaled magnitude: 2^-9 below 2^-6, else 2^(floor(log2 |x|) - 3))
+    x = ref.astype(np.float64) * (448.0 / amax[..., None].astype(np.float64))
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -6)))
+    step = np.where(np.abs(x) < 2.0 ** -6, 2.0 ** -9, 2.0 ** (e - 3))
+    assert (np.abs(vals - x) <= 0.5 * step * (1 + 1e-6)).all()
+    assert set(np.unique(codes)) <= set(table)
+
+
+def test_pool_fp8_power_of_two_scaling_moves_only_the_scale():
+    rng = np.random.default_rng(44)
+    raw = rng.standard_normal((1, 32, DIM)).astype(np.float32)
+    c1, s1 = oracle.pool_fp8(raw, 0, 8, 1e7, oracle.FLAG_NO_ROPE)
+    c2, s2 = oracle.pool_fp8(raw * np.float32(8), 0, 8, 1e7, oracle.FLAG_NO_ROPE)
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(s2, s1 * np.float32(8))
+
+
+def test_score_fp8_equals_exact_keys_of_the_other_path():
+    # keys whose values are exact E4M3 codes with scale 1 (and then 1/8): the
+    # FP8 score is the score of the same keys stored exactly (the bf16 path,
+    # pinned above against einsum), and the selection does not change
+    rng = np.random.default_rng(45)
+    B, NB, R, k = 2, 300, 9, 40
+    kv = rng.integers(-4, 5, size=(B, NB, DIM)).astype(np.float32)
+    kv[..., 0] = 448.0                                  # every key's amax: scale exactly 1
+    codes = oracle.fp8_from_float(kv)
+    scales = np.ones((B, NB), np.float32)
+    q = synth.bf16_bits(rng.integers(-3, 4, size=(R, IH, DIM)).astype(np.float32) / 64)
+    seq = rng.integers(0, B, R).astype(np.int32)
+    pos = rng.integers(0, 4 * NB, R).astype(np.int32)
+    a = oracle.score_topk_fp8(q, seq, pos, codes, scales, k, 1e7, oracle.FLAG_NO_ROPE, want_raw=True)
+    b = oracle.score_topk(q, seq, pos, synth.bf16_bits(kv), k, 1e7, oracle.FLAG_NO_ROPE, want_raw=True)
+    for x, y in zip(a[:3], b[:3]):
+        np.testing.assert_array_equal(x, y)
+    np.testing.assert_array_equal(a[3], b[3])
+    c = oracle.score_topk_fp8(q, seq, pos, codes, scales / np.float32(8), k, 1e7, oracle.FLAG_NO_ROPE, want_raw=True)
+    np.testing.assert_array_equal(c[0], a[0])
+    np.testing.assert_array_equal(c[3], a[3] / 8)
