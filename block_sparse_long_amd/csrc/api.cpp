@@ -165,6 +165,7 @@ struct KeySource {
     const void *pooled;
     const uint8_t *codes;
     const float *scales;
+    KeyPages kp;  // table null: contiguous
 };
 static qsa_status_t score_topk_run(const void *q_index, const int32_t *row_seq, const int32_t *row_pos,
                                    int32_t rows, const KeySource &keys, int64_t pooled_seq_stride,
@@ -276,7 +277,7 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
     if (!aligned16(q_index) || !aligned16(pooled) || !row_seq || !row_pos || !sel_blocks || !sel_count)
         return QSA_ERR_INVALID_ARG;
     if (pooled_seq_stride % 8 || pooled_seq_stride < 0) return QSA_ERR_INVALID_ARG;
-    const KeySource keys{pooled, nullptr, nullptr};
+    const KeySource keys{pooled, nullptr, nullptr, KeyPages{nullptr, 0, 1}};
     return score_topk_run(q_index, row_seq, row_pos, rows, keys, pooled_seq_stride, max_visible_blocks, top_k,
                           rope_theta, flags, dtype, sel_blocks, sel_count, sel_scores, workspace, workspace_bytes,
                           stream);
@@ -296,10 +297,37 @@ qsa_status_t qsa_score_topk_fp8(const void *q_index, const int32_t *row_seq, con
         !row_pos || !sel_blocks || !sel_count)
         return QSA_ERR_INVALID_ARG;
     if (pooled_seq_stride < 0) return QSA_ERR_INVALID_ARG;
-    const KeySource keys{nullptr, codes, scales};
+    const KeySource keys{nullptr, codes, scales, KeyPages{nullptr, 0, 1}};
     return score_topk_run(q_index, row_seq, row_pos, rows, keys, pooled_seq_stride, max_visible_blocks, top_k,
                           rope_theta, flags, QSA_BF16, sel_blocks, sel_count, sel_scores, workspace, workspace_bytes,
                           stream);
+}
+
+qsa_status_t qsa_score_topk_paged(const void *q_index, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+                                  const void *pooled, const uint8_t *codes, const float *scales,
+                                  const int32_t *page_table, int64_t page_table_stride, int32_t page_tokens,
+                                  int32_t max_visible_blocks, int32_t top_k, double rope_theta, uint32_t flags,
+                                  qsa_dtype_t dtype, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
+                                  void *workspace, size_t workspace_bytes, void *stream)
+{
+    const bool fp8 = codes != nullptr;
+    if (!fp8 && !dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
+    if (fp8 && dtype != QSA_BF16) return QSA_ERR_UNSUPPORTED;  // FP8 keys go with bf16 index queries
+    if (rows < 0 || max_visible_blocks < 0 || top_k < 1 || top_k > QSA_MAX_TOP_K) return QSA_ERR_INVALID_ARG;
+    if (!score_flags_ok(flags, dtype)) return QSA_ERR_INVALID_ARG;
+    if ((flags & QSA_FLAG_SCORE_GEMM) && dtype != QSA_BF16) return QSA_ERR_UNSUPPORTED;
+    if (!(flags & QSA_FLAG_NO_ROPE) && !(rope_theta > 1.0 && std::isfinite(rope_theta))) return QSA_ERR_INVALID_ARG;
+    if (page_tokens < kBlock || page_tokens % kBlock || page_table_stride < 0) return QSA_ERR_INVALID_ARG;
+    if (rows == 0) return QSA_OK;
+    if (!aligned16(q_index) || !row_seq || !row_pos || !sel_blocks || !sel_count || !page_table)
+        return QSA_ERR_INVALID_ARG;
+    if (fp8 ? (!aligned16(codes) || !scales || (reinterpret_cast<uintptr_t>(scales) & 3u) || pooled)
+            : (!aligned16(pooled) || scales))
+        return QSA_ERR_INVALID_ARG;
+    if ((int64_t)max_visible_blocks * kBlock > page_table_stride * (int64_t)page_tokens) return QSA_ERR_INVALID_ARG;
+    const KeySource keys{fp8 ? nullptr : pooled, codes, scales, KeyPages{page_table, page_table_stride, page_tokens / kBlock}};
+    return score_topk_run(q_index, row_seq, row_pos, rows, keys, 0, max_visible_blocks, top_k, rope_theta, flags, dtype,
+                          sel_blocks, sel_count, sel_scores, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -339,6 +367,7 @@ static qsa_status_t score_topk_run(const void *q_index, const int32_t *row_seq, 
         fa.pooled = (const uint16_t *)keys.pooled;
         fa.codes = keys.codes;
         fa.scales = keys.scales;
+        fa.kp = keys.kp;
         fa.pooled_stride = pooled_seq_stride;
         fa.max_nb = max_visible_blocks;
         fa.top_k = top_k;
@@ -357,11 +386,11 @@ static qsa_status_t score_topk_run(const void *q_index, const int32_t *row_seq, 
     float *scores = (float *)(ws + L.scores_off);
     if (max_visible_blocks > 0) {
         if (keys.codes)
-            launch_score_rows_fp8(qrot, row_seq, row_pos, rows, keys.codes, keys.scales, pooled_seq_stride,
+            launch_score_rows_fp8(qrot, row_seq, row_pos, rows, keys.codes, keys.scales, pooled_seq_stride, keys.kp,
                                   max_visible_blocks, scores, L.sc_stride, L.plan.split ? ss.scratch : nullptr, st);
         else
-            launch_score_rows(qrot, row_seq, row_pos, rows, keys.pooled, pooled_seq_stride, max_visible_blocks,
-                              scores, L.sc_stride, L.plan.split ? ss.scratch : nullptr, bf16, st);
+            launch_score_rows(qrot, row_seq, row_pos, rows, keys.pooled, pooled_seq_stride, keys.kp,
+                              max_visible_blocks, scores, L.sc_stride, L.plan.split ? ss.scratch : nullptr, bf16, st);
     }
     if (L.plan.split)
         launch_select_split(scores, L.sc_stride, row_pos, rows, max_visible_blocks, top_k, ss, sel_blocks, sel_count,
@@ -389,8 +418,9 @@ static qsa_status_t check_attn_common(const void *q, const void *k_cache, const 
     return QSA_OK;
 }
 
-qsa_status_t qsa_sparse_attn_prefill(const void *q, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+static qsa_status_t attn_prefill_impl(const void *q, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
                                      const void *k_cache, const void *v_cache, int64_t kv_seq_stride,
+                                     const int32_t *page_table, int64_t pt_stride, int32_t page_tokens,
                                      const int32_t *sel_blocks, const int32_t *sel_count, int32_t top_k, int32_t Hq,
                                      int32_t Hkv, int32_t D, float softmax_scale, qsa_dtype_t dtype, void *out,
                                      float *lse, void *stream)
@@ -427,12 +457,41 @@ qsa_status_t qsa_sparse_attn_prefill(const void *q, const int32_t *row_seq, cons
     a.lse = lse;
     a.partial = nullptr;
     a.nsplit = 1;
+    a.page_table = page_table;
+    a.pt_stride = pt_stride;
+    a.page_tokens = page_tokens;
+    const bool mfma = attn_mfma_supported(Hq, Hkv, 1, dtype == QSA_BF16);
+    if (page_table && !mfma) return QSA_ERR_UNSUPPORTED;  // the paged gather lives in the MFMA kernels
     clear_launch_err();
-    if (attn_mfma_supported(Hq, Hkv, 1, dtype == QSA_BF16))
+    if (mfma)
         launch_attn_prefill_mfma(a, (hipStream_t)stream);
     else
         launch_attn_prefill(a, dtype == QSA_BF16, (hipStream_t)stream);
     return launch_status();
+}
+
+qsa_status_t qsa_sparse_attn_prefill(const void *q, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+                                     const void *k_cache, const void *v_cache, int64_t kv_seq_stride,
+                                     const int32_t *sel_blocks, const int32_t *sel_count, int32_t top_k, int32_t Hq,
+                                     int32_t Hkv, int32_t D, float softmax_scale, qsa_dtype_t dtype, void *out,
+                                     float *lse, void *stream)
+{
+    return attn_prefill_impl(q, row_seq, row_pos, rows, k_cache, v_cache, kv_seq_stride, nullptr, 0, 0, sel_blocks,
+                             sel_count, top_k, Hq, Hkv, D, softmax_scale, dtype, out, lse, stream);
+}
+
+qsa_status_t qsa_sparse_attn_prefill_paged(const void *q, const int32_t *row_seq, const int32_t *row_pos,
+                                           int32_t rows, const void *k_cache, const void *v_cache,
+                                           const int32_t *page_table, int64_t page_table_stride, int32_t page_tokens,
+                                           const int32_t *sel_blocks, const int32_t *sel_count, int32_t top_k,
+                                           int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale, qsa_dtype_t dtype,
+                                           void *out, float *lse, void *stream)
+{
+    if (page_tokens < kBlock || page_tokens % kBlock || page_table_stride < 0) return QSA_ERR_INVALID_ARG;
+    if (rows > 0 && !page_table) return QSA_ERR_INVALID_ARG;
+    return attn_prefill_impl(q, row_seq, row_pos, rows, k_cache, v_cache, 0, page_table, page_table_stride,
+                             page_tokens, sel_blocks, sel_count, top_k, Hq, Hkv, D, softmax_scale, dtype, out, lse,
+                             stream);
 }
 
 size_t qsa_sparse_attn_decode_workspace_size(int32_t batch, int32_t q_per_seq, int32_t Hq, int32_t D, int32_t top_k)
@@ -442,9 +501,10 @@ size_t qsa_sparse_attn_decode_workspace_size(int32_t batch, int32_t q_per_seq, i
     return align256((size_t)batch * q_per_seq * Hq * nsplit * (kDim + 2) * sizeof(float));
 }
 
-qsa_status_t qsa_sparse_attn_decode(const void *q, const int32_t *row_pos, int32_t batch, int32_t q_per_seq,
+static qsa_status_t attn_decode_impl(const void *q, const int32_t *row_pos, int32_t batch, int32_t q_per_seq,
                                     const int32_t *tail_start, const void *k_cache, const void *v_cache,
-                                    int64_t kv_seq_stride, const int32_t *sel_blocks, const int32_t *sel_count,
+                                    int64_t kv_seq_stride, const int32_t *page_table, int64_t pt_stride,
+                                    int32_t page_tokens, const int32_t *sel_blocks, const int32_t *sel_count,
                                     int32_t top_k, int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
                                     qsa_dtype_t dtype, void *out, float *lse, void *workspace, size_t workspace_bytes,
                                     void *stream)
@@ -485,14 +545,46 @@ qsa_status_t qsa_sparse_attn_decode(const void *q, const int32_t *row_pos, int32
     a.lse = lse;
     a.partial = (float *)workspace;
     a.nsplit = attn_decode_splits(top_k);
+    a.page_table = page_table;
+    a.pt_stride = pt_stride;
+    a.page_tokens = page_tokens;
+    const bool mfma = attn_mfma_supported(Hq, Hkv, q_per_seq, dtype == QSA_BF16);
+    if (page_table && !mfma) return QSA_ERR_UNSUPPORTED;  // the paged gather lives in the MFMA kernels
     clear_launch_err();
-    if (attn_mfma_supported(Hq, Hkv, q_per_seq, dtype == QSA_BF16)) {
+    if (mfma) {
         launch_attn_decode_mfma(a, (hipStream_t)stream);
         launch_attn_combine(a, true, (hipStream_t)stream);
     } else {
         launch_attn_decode(a, dtype == QSA_BF16, (hipStream_t)stream);
     }
     return launch_status();
+}
+
+qsa_status_t qsa_sparse_attn_decode(const void *q, const int32_t *row_pos, int32_t batch, int32_t q_per_seq,
+                                    const int32_t *tail_start, const void *k_cache, const void *v_cache,
+                                    int64_t kv_seq_stride, const int32_t *sel_blocks, const int32_t *sel_count,
+                                    int32_t top_k, int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                                    qsa_dtype_t dtype, void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                    void *stream)
+{
+    return attn_decode_impl(q, row_pos, batch, q_per_seq, tail_start, k_cache, v_cache, kv_seq_stride, nullptr, 0, 0,
+                            sel_blocks, sel_count, top_k, Hq, Hkv, D, softmax_scale, dtype, out, lse, workspace,
+                            workspace_bytes, stream);
+}
+
+qsa_status_t qsa_sparse_attn_decode_paged(const void *q, const int32_t *row_pos, int32_t batch, int32_t q_per_seq,
+                                          const int32_t *tail_start, const void *k_cache, const void *v_cache,
+                                          const int32_t *page_table, int64_t page_table_stride, int32_t page_tokens,
+                                          const int32_t *sel_blocks, const int32_t *sel_count, int32_t top_k,
+                                          int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale, qsa_dtype_t dtype,
+                                          void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                          void *stream)
+{
+    if (page_tokens < kBlock || page_tokens % kBlock || page_table_stride < 0) return QSA_ERR_INVALID_ARG;
+    if (batch > 0 && !page_table) return QSA_ERR_INVALID_ARG;
+    return attn_decode_impl(q, row_pos, batch, q_per_seq, tail_start, k_cache, v_cache, 0, page_table,
+                            page_table_stride, page_tokens, sel_blocks, sel_count, top_k, Hq, Hkv, D, softmax_scale,
+                            dtype, out, lse, workspace, workspace_bytes, stream);
 }
 
 qsa_status_t qsa_profile_enable(int enable)

@@ -120,6 +120,15 @@ __device__ __forceinline__ void chunk_load(ChunkRegs &cr, const bf16_t *__restri
                                : make_uint4(0, 0, 0, 0);
 }
 
+// Slot of token p of sequence s in the K/V arrays: p itself when the caches
+// are contiguous (the sequence's base is then part of the pointers), else the
+// slot of p's page ([SGL]: the paged KV pool, addressed by physical slots).
+__device__ __forceinline__ int64_t kv_slot(const AttnArgs &a, int64_t s, int64_t p)
+{
+    if (!a.page_table) return p;
+    return (int64_t)a.page_table[s * a.pt_stride + p / a.page_tokens] * a.page_tokens + p % a.page_tokens;
+}
+
 // The same share of a chunk of whole blocks: ublk[0..nb) are the chunk's
 // blocks (16 at most, nb >= 1).  Thread t's K position is token (t/4)%4 of
 // block t/16 and its V positions are tokens 0..3 of block t%16, so one block
@@ -128,15 +137,16 @@ __device__ __forceinline__ void chunk_load(ChunkRegs &cr, const bf16_t *__restri
 // unconditional.
 __device__ __forceinline__ void chunk_load_blocks(ChunkRegs &cr, const bf16_t *__restrict__ kbase,
                                                   const bf16_t *__restrict__ vbase, uint32_t row_stride,
-                                                  const int32_t *ublk, int nb)
+                                                  const int32_t *ublk, int nb, const AttnArgs &a, int64_t seq)
 {
     const int t = threadIdx.x;
-    const uint32_t bstride = 4u * row_stride;  // elements per block
     const int32_t bk = ublk[min(t >> 4, nb - 1)], bv = ublk[min(t & 15, nb - 1)];
+    // first slot of each block: its 4 tokens are consecutive slots
+    const uint32_t sk = (uint32_t)kv_slot(a, seq, (int64_t)kBlock * bk), sv = (uint32_t)kv_slot(a, seq, (int64_t)kBlock * bv);
     typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    const u32x4_t *ks = (const u32x4_t *)(kbase + (uint64_t)(uint32_t)bk * bstride + ((t >> 2) & 3) * row_stride +
+    const u32x4_t *ks = (const u32x4_t *)(kbase + (uint64_t)sk * row_stride + ((t >> 2) & 3) * row_stride +
                                           (t & 3) * 32);
-    const bf16_t *vs = vbase + (uint64_t)(uint32_t)bv * bstride + (t >> 4) * 8;
+    const bf16_t *vs = vbase + (uint64_t)sv * row_stride + (t >> 4) * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // element-wise vector loads (a block copy would go through memory)
         const u32x4_t kx = ks[i], vx = *(const u32x4_t *)(vs + i * row_stride);
@@ -343,8 +353,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
             if (((todo >> r) & 1u) && s_seq[r] == seq) active |= 1u << r;
         todo &= ~active;
         const uint32_t qbit = q_valid ? (active & (1u << r_local)) : 0u;
-        const bf16_t *kbase = (const bf16_t *)a.k_cache + (int64_t)seq * a.kv_seq_stride + (int64_t)kvh * kDim;
-        const bf16_t *vbase = (const bf16_t *)a.v_cache + (int64_t)seq * a.kv_seq_stride + (int64_t)kvh * kDim;
+        const int64_t seq_off = a.page_table ? 0 : (int64_t)seq * a.kv_seq_stride;
+        const bf16_t *kbase = (const bf16_t *)a.k_cache + seq_off + (int64_t)kvh * kDim;
+        const bf16_t *vbase = (const bf16_t *)a.v_cache + seq_off + (int64_t)kvh * kDim;
         // block range of the active rows' selections
         int32_t hi_blk = 0;
         for (int r = 0; r < nrows; ++r)
@@ -405,7 +416,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
             constexpr int kChB = kCh / kBlock;
             const int32_t nch = (nu + kChB - 1) / kChB;
             ChunkRegs cr;
-            if (nch > 0) chunk_load_blocks(cr, kbase, vbase, (uint32_t)row_stride, us.blk, min(kChB, nu));
+            if (nch > 0) chunk_load_blocks(cr, kbase, vbase, (uint32_t)row_stride, us.blk, min(kChB, nu), a, seq);
             for (int32_t c = 0; c < nch; ++c) {
                 const int32_t c0 = c * kChB;
                 const int nb = min(kChB, nu - c0);
@@ -414,7 +425,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
                 __syncthreads();
                 if (c + 1 < nch) {
                     const int32_t c1 = c0 + kChB;
-                    chunk_load_blocks(cr, kbase, vbase, (uint32_t)row_stride, us.blk + c1, min(kChB, nu - c1));
+                    chunk_load_blocks(cr, kbase, vbase, (uint32_t)row_stride, us.blk + c1, min(kChB, nu - c1), a,
+                                      seq);
                 }
                 wave_chunk(cs, qb, qbit, scale2, st);
                 __syncthreads();
@@ -436,7 +448,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
                 }
                 n += len;
             }
-            cs.pos[t] = pos;
+            cs.pos[t] = (int32_t)kv_slot(a, seq, pos);
             cs.pmask[t] = msk;
         }
         __syncthreads();
@@ -499,8 +511,9 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(AttnArgs a)
     const float scale2 = a.scale * kLog2e;
     const uint32_t qbit = q_valid ? (1u << jrow) : 0u;
     const int64_t row_stride = (int64_t)a.Hkv * kDim;
-    const bf16_t *kbase = (const bf16_t *)a.k_cache + s * a.kv_seq_stride + (int64_t)kvh * kDim;
-    const bf16_t *vbase = (const bf16_t *)a.v_cache + s * a.kv_seq_stride + (int64_t)kvh * kDim;
+    const int64_t seq_off = a.page_table ? 0 : s * a.kv_seq_stride;
+    const bf16_t *kbase = (const bf16_t *)a.k_cache + seq_off + (int64_t)kvh * kDim;
+    const bf16_t *vbase = (const bf16_t *)a.v_cache + seq_off + (int64_t)kvh * kDim;
     const int32_t count = min(a.sel_count[s], a.top_k);
     const uint32_t all_rows = a.q_per_sel >= 32 ? 0xffffffffu : ((1u << a.q_per_sel) - 1u);
     if (split < a.nsplit - 1) {
@@ -509,7 +522,9 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(AttnArgs a)
         if (nb > 0) {
             if (t < kCh) {
                 const int bi = t / kBlock;
-                cs.pos[t] = bi < nb ? a.sel_blocks[s * a.top_k + b0 + bi] * kBlock + (t % kBlock) : 0;
+                cs.pos[t] = bi < nb ? (int32_t)kv_slot(a, s, (int64_t)a.sel_blocks[s * a.top_k + b0 + bi] * kBlock +
+                                                           (t % kBlock))
+                                    : 0;
                 cs.pmask[t] = bi < nb ? all_rows : 0u;
             }
             __syncthreads();
@@ -538,7 +553,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(AttnArgs a)
                         if (p >= ts && p <= tj) msk |= 1u << j;
                     }
                 }
-                cs.pos[t] = t < n ? (int32_t)p : 0;
+                cs.pos[t] = t < n ? (int32_t)kv_slot(a, s, p) : 0;
                 cs.pmask[t] = msk;
             }
             __syncthreads();

@@ -100,6 +100,21 @@ __device__ __forceinline__ float key_score(uint32_t k)
     return __uint_as_float(u);
 }
 
+// Key number of block b of sequence seq: seq*keys_per_seq + b, or through
+// the page table of the compressed-key pool.
+__device__ __forceinline__ int64_t key_index(const KeyPages &kp, int64_t keys_per_seq, int64_t seq, int64_t b)
+{
+    if (!kp.table) return seq * keys_per_seq + b;
+    return (int64_t)kp.table[seq * kp.stride + b / kp.bpp] * kp.bpp + b % kp.bpp;
+}
+// Element offset of that key's 128 values in a bf16 / fp32 key array whose
+// sequences are `seq_stride` elements apart when contiguous.
+__device__ __forceinline__ int64_t key_offset(const KeyPages &kp, int64_t seq_stride, int64_t seq, int64_t b)
+{
+    if (!kp.table) return seq * seq_stride + b * kDim;
+    return key_index(kp, 0, seq, b) * kDim;
+}
+
 // Complete micro-blocks visible to a query at position t: 4b + 3 <= t.
 __device__ __forceinline__ int64_t visible_blocks(int64_t t) { return (t + 1) / kBlock; }
 

@@ -39,12 +39,21 @@ void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void
 // Select histogram: 4096 bins of the top 12 bits of a score's order key.
 constexpr int kHistBins = 4096;
 constexpr int kHistShift = 20;
+// Paged compressed keys (table null: contiguous per sequence).  The KV pool
+// keeps one compressed key per 4 token slots, at full_slot / 4; with pages of
+// page_tokens slots (a multiple of 4), block b of sequence s is key
+// table[s*stride + b/bpp]*bpp + b%bpp, bpp = page_tokens / 4.
+struct KeyPages {
+    const int32_t *table;
+    int64_t stride;
+    int32_t bpp;
+};
 void launch_score_rows(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
-                       const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores,
+                       const void *pooled, int64_t pooled_stride, const KeyPages &kp, int32_t max_nb, float *scores,
                        int64_t sc_stride, uint32_t *hist, bool bf16, hipStream_t stream);
 void launch_score_rows_fp8(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
-                           const uint8_t *codes, const float *scales, int64_t pooled_stride, int32_t max_nb,
-                           float *scores, int64_t sc_stride, uint32_t *hist, hipStream_t stream);
+                           const uint8_t *codes, const float *scales, int64_t pooled_stride, const KeyPages &kp,
+                           int32_t max_nb, float *scores, int64_t sc_stride, uint32_t *hist, hipStream_t stream);
 void launch_score_gemm(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
                        const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores,
                        int64_t sc_stride, hipStream_t stream);
@@ -58,7 +67,8 @@ struct FusedScoreArgs {
     const uint16_t *pooled;   // [B][pooled_stride] (bf16), or NULL with FP8 keys
     const uint8_t *codes;     // FP8 keys: [B][pooled_stride][128] E4M3 codes, else NULL
     const float *scales;      // FP8 keys: [B][pooled_stride] one scale per key
-    int64_t pooled_stride;    // elements per sequence (bf16) or keys per sequence (FP8)
+    int64_t pooled_stride;    // elements per sequence (bf16) or keys per sequence (FP8); unused when paged
+    KeyPages kp;
     int32_t max_nb;
     int32_t top_k;
     int32_t nsplit;           // block-range splits of the main pass
@@ -124,6 +134,12 @@ struct AttnArgs {
     float *lse;
     float *partial;           // decode split partials, or null (prefill: no split)
     int32_t nsplit;
+    // paged K/V (null: contiguous per sequence): token p of sequence s sits
+    // at slot page_table[s*pt_stride + p/page_tokens]*page_tokens + p%page_tokens
+    // of k_cache / v_cache, which are then [slots][Hkv][D]
+    const int32_t *page_table;
+    int64_t pt_stride;
+    int32_t page_tokens;      // a multiple of 4: a block never straddles pages
 };
 int32_t attn_decode_splits(int32_t top_k);
 void launch_attn_prefill(const AttnArgs &a, bool bf16, hipStream_t stream);

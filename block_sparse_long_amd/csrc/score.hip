@@ -48,7 +48,7 @@ __device__ __forceinline__ void hist_flush(const uint32_t *lhist, uint32_t *ghis
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
     const bf16_t *__restrict__ qrot, const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_pos,
-    const bf16_t *__restrict__ pooled, int64_t pooled_stride, int32_t max_nb, float *__restrict__ scores,
+    const bf16_t *__restrict__ pooled, int64_t pooled_stride, KeyPages kp, int32_t max_nb, float *__restrict__ scores,
     int64_t sc_stride, uint32_t *__restrict__ hist)
 {
     __shared__ uint32_t lhist[kHistBins];
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: the step loop branches on scalars
     const int m = lane & 15, g = lane >> 4;
-    const bf16_t *kb = pooled + (int64_t)row_seq[r] * pooled_stride;
+    const int64_t seq = row_seq[r];
     float *srow = scores + (int64_t)r * sc_stride;
     // Each wave handles 64 consecutive blocks per step: MFMA column m of tile
     // nt is block base + 4m + nt, so lane m of group 0 ends the step with the
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const int64_t b = min(base + 4 * m + nt, b_end - 1);  // clamp: stays inside the visible range
-            const uint4 *src = (const uint4 *)(kb + b * kDim + 32 * g);
+            const uint4 *src = (const uint4 *)(pooled + key_offset(kp, pooled_stride, seq, b) + 32 * g);
 #pragma unroll
             for (int s = 0; s < 4; ++s) v[nt][s] = src[s];
         }
@@ -135,8 +135,8 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void score_rows_fp8_kernel(
     const bf16_t *__restrict__ qrot, const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_pos,
-    const uint8_t *__restrict__ codes, const float *__restrict__ scales, int64_t pooled_stride, int32_t max_nb,
-    float *__restrict__ scores, int64_t sc_stride, uint32_t *__restrict__ hist)
+    const uint8_t *__restrict__ codes, const float *__restrict__ scales, int64_t pooled_stride, KeyPages kp,
+    int32_t max_nb, float *__restrict__ scores, int64_t sc_stride, uint32_t *__restrict__ hist)
 {
     __shared__ uint32_t lhist[kHistBins];
     const int r = blockIdx.y;
@@ -148,8 +148,6 @@ __global__ __launch_bounds__(256) void score_rows_fp8_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int m = lane & 15, g = lane >> 4;
     const int64_t seq = row_seq[r];
-    const uint8_t *kb = codes + seq * pooled_stride * kDim;
-    const float *sb = scales + seq * pooled_stride;
     float *srow = scores + (int64_t)r * sc_stride;
     // as the bf16 kernel: column m of tile nt is block base + 4m + nt; lane
     // group g holds the codes of dims 32g .. 32g + 31 (32 bytes), and every
@@ -161,11 +159,11 @@ __global__ __launch_bounds__(256) void score_rows_fp8_kernel(
     auto load = [&](int64_t base, Step &v) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            const int64_t b = min(base + 4 * m + nt, b_end - 1);
-            const uint4 *src = (const uint4 *)(kb + b * kDim + 32 * g);
+            const int64_t key = key_index(kp, pooled_stride, seq, min(base + 4 * m + nt, b_end - 1));
+            const uint4 *src = (const uint4 *)(codes + key * kDim + 32 * g);
             v.c[nt][0] = src[0];
             v.c[nt][1] = src[1];
-            v.sc[nt] = sb[b];
+            v.sc[nt] = scales[key];
         }
     };
     Step v0, v1;
@@ -221,7 +219,7 @@ __global__ __launch_bounds__(256) void score_rows_fp8_kernel(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void score_rows_f32_kernel(
     const float *__restrict__ qrot, const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_pos,
-    const float *__restrict__ pooled, int64_t pooled_stride, int32_t max_nb, float *__restrict__ scores,
+    const float *__restrict__ pooled, int64_t pooled_stride, KeyPages kp, int32_t max_nb, float *__restrict__ scores,
     int64_t sc_stride, uint32_t *__restrict__ hist)
 {
     __shared__ float4 qs[kIdxHeads * kDim / 4];
@@ -235,9 +233,9 @@ __global__ __launch_bounds__(256) void score_rows_f32_kernel(
     for (int i = threadIdx.x; i < kIdxHeads * kDim / 4; i += blockDim.x)
         qs[i] = ((const float4 *)(qrot + (int64_t)r * kIdxHeads * kDim))[i];
     __syncthreads();
-    const float *kb = pooled + (int64_t)row_seq[r] * pooled_stride;
+    const int64_t seq = row_seq[r];
     for (int64_t b = b_begin + threadIdx.x; b < b_end; b += blockDim.x) {
-        const float4 *kr = (const float4 *)(kb + b * kDim);
+        const float4 *kr = (const float4 *)(pooled + key_offset(kp, pooled_stride, seq, b));
         float d[kIdxHeads] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int i = 0; i < kDim / 4; ++i) {
             const float4 kv = kr[i];
@@ -342,25 +340,25 @@ __global__ __launch_bounds__(256) void score_gemm_bf16_kernel(
 int64_t score_chunks(int32_t max_nb) { return ((int64_t)max_nb + kChunk - 1) / kChunk; }
 
 void launch_score_rows(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
-                       const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores, int64_t sc_stride,
-                       uint32_t *hist, bool bf16, hipStream_t stream)
+                       const void *pooled, int64_t pooled_stride, const KeyPages &kp, int32_t max_nb, float *scores,
+                       int64_t sc_stride, uint32_t *hist, bool bf16, hipStream_t stream)
 {
     const dim3 grid((unsigned)score_chunks(max_nb), (unsigned)rows), block(256);
     if (bf16)
         QSA_LAUNCH("score_rows_bf16", score_rows_bf16_kernel, grid, block, 0, stream, (const bf16_t *)qrot, row_seq,
-                   row_pos, (const bf16_t *)pooled, pooled_stride, max_nb, scores, sc_stride, hist);
+                   row_pos, (const bf16_t *)pooled, pooled_stride, kp, max_nb, scores, sc_stride, hist);
     else
         QSA_LAUNCH("score_rows_f32", score_rows_f32_kernel, grid, block, 0, stream, (const float *)qrot, row_seq,
-                   row_pos, (const float *)pooled, pooled_stride, max_nb, scores, sc_stride, hist);
+                   row_pos, (const float *)pooled, pooled_stride, kp, max_nb, scores, sc_stride, hist);
 }
 
 void launch_score_rows_fp8(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
-                           const uint8_t *codes, const float *scales, int64_t pooled_stride, int32_t max_nb,
-                           float *scores, int64_t sc_stride, uint32_t *hist, hipStream_t stream)
+                           const uint8_t *codes, const float *scales, int64_t pooled_stride, const KeyPages &kp,
+                           int32_t max_nb, float *scores, int64_t sc_stride, uint32_t *hist, hipStream_t stream)
 {
     const dim3 grid((unsigned)score_chunks(max_nb), (unsigned)rows), block(256);
     QSA_LAUNCH("score_rows_fp8", score_rows_fp8_kernel, grid, block, 0, stream, (const bf16_t *)qrot, row_seq,
-               row_pos, codes, scales, pooled_stride, max_nb, scores, sc_stride, hist);
+               row_pos, codes, scales, pooled_stride, kp, max_nb, scores, sc_stride, hist);
 }
 
 void launch_score_gemm(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,

@@ -140,8 +140,7 @@ template <> struct TileShare<false> {
     __device__ __forceinline__ void load(const FusedScoreArgs &a, int32_t seq, int64_t b, int ldim)
     {
         typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-        const u32x4_t *src =
-            (const u32x4_t *)((const bf16_t *)a.pooled + (int64_t)seq * a.pooled_stride + b * kDim + ldim);
+        const u32x4_t *src = (const u32x4_t *)((const bf16_t *)a.pooled + key_offset(a.kp, a.pooled_stride, seq, b) + ldim);
         const u32x4_t x0 = src[0], x1 = src[1], x2 = src[2], x3 = src[3];
         p0 = make_uint4(x0.x, x0.y, x0.z, x0.w);
         p1 = make_uint4(x1.x, x1.y, x1.z, x1.w);
@@ -162,7 +161,7 @@ template <> struct TileShare<true> {
     float s;
     __device__ __forceinline__ void load(const FusedScoreArgs &a, int32_t seq, int64_t b, int ldim)
     {
-        const int64_t key = (int64_t)seq * a.pooled_stride + b;
+        const int64_t key = key_index(a.kp, a.pooled_stride, seq, b);
         const uint4 *src = (const uint4 *)(a.codes + key * kDim + ldim);
         c[0] = src[0];
         c[1] = src[1];
@@ -501,10 +500,10 @@ template <bool FP8>
 __device__ __forceinline__ float recompute_block(const FusedScoreArgs &a, const bf16_t *q4, int32_t seq, int64_t b)
 {
     if (FP8) {
-        const int64_t key = (int64_t)seq * a.pooled_stride + b;
+        const int64_t key = key_index(a.kp, a.pooled_stride, seq, b);
         return recompute_score_fp8(q4, a.codes + key * kDim, a.scales[key]);
     }
-    return recompute_score(q4, (const bf16_t *)a.pooled + (int64_t)seq * a.pooled_stride + b * kDim);
+    return recompute_score(q4, (const bf16_t *)a.pooled + key_offset(a.kp, a.pooled_stride, seq, b));
 }
 
 __device__ __forceinline__ float scaled(float raw) { return (float)((double)raw / sqrt((double)kDim)); }

@@ -26,7 +26,8 @@ INDEX_DIM, INDEX_HEADS, BLOCK_TOKENS, MAX_TOP_K, MAX_QUERY_GROUP = 128, 4, 4, 40
 
 # every symbol include/qsa.h declares
 EXPORTS = ("qsa_pool_index_keys", "qsa_pool_index_keys_fp8", "qsa_pool_append", "qsa_score_topk_workspace_size",
-           "qsa_score_topk", "qsa_score_topk_fp8_workspace_size", "qsa_score_topk_fp8",
+           "qsa_score_topk", "qsa_score_topk_fp8_workspace_size", "qsa_score_topk_fp8", "qsa_score_topk_paged",
+           "qsa_sparse_attn_prefill_paged", "qsa_sparse_attn_decode_paged",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode_workspace_size",
            "qsa_sparse_attn_decode", "qsa_status_string", "qsa_last_device_error", "qsa_profile_enable",
            "qsa_profile_reset", "qsa_profile_kernel_ms")
@@ -70,6 +71,15 @@ def load():
     lib.qsa_score_topk_fp8_workspace_size.restype = sz
     lib.qsa_score_topk_fp8.argtypes = [P, P, P, i32, P, P, i64, i32, i32, f64, u32, P, P, P, P, sz, P]
     lib.qsa_score_topk_fp8.restype = st
+    lib.qsa_score_topk_paged.argtypes = [P, P, P, i32, P, P, P, P, i64, i32, i32, i32, f64, u32, st, P, P, P, P, sz,
+                                         P]
+    lib.qsa_score_topk_paged.restype = st
+    lib.qsa_sparse_attn_prefill_paged.argtypes = [P, P, P, i32, P, P, P, i64, i32, P, P, i32, i32, i32, i32, f32, st,
+                                                  P, P, P]
+    lib.qsa_sparse_attn_prefill_paged.restype = st
+    lib.qsa_sparse_attn_decode_paged.argtypes = [P, P, i32, i32, P, P, P, P, i64, i32, P, P, i32, i32, i32, i32, f32,
+                                                 st, P, P, P, sz, P]
+    lib.qsa_sparse_attn_decode_paged.restype = st
     lib.qsa_pool_append.argtypes = [P, P, P, P, P, i32, f64, u32, st, P]
     lib.qsa_pool_append.restype = st
     lib.qsa_score_topk_workspace_size.argtypes = [i32, i32, i32, st, u32]
@@ -287,6 +297,83 @@ def sparse_attn_decode(q, row_pos, k_cache, v_cache, sel_blocks, sel_count, tail
                                        Hq, Hkv, D, scale, _dtype_code(q), _ptr(out), _ptr(lse),
                                        _ptr(workspace), workspace.numel(), _stream(stream))
     _check("qsa_sparse_attn_decode", rc)
+    return out, lse
+
+
+def score_topk_paged(q_index, row_seq, row_pos, page_table, page_tokens: int, max_visible_blocks: int,
+                     top_k: int, rope_theta: float, pooled=None, codes=None, scales=None, flags: int = 0,
+                     sel_blocks=None, sel_count=None, sel_scores=None, workspace=None, want_scores: bool = True,
+                     stream=None):
+    """a4-a6 on paged compressed keys: `pooled` [slots/4][128] (dtype of
+    q_index), or FP8 `codes` [slots/4][128] uint8 + `scales` [slots/4];
+    page_table [n_seq][pages] int32.  Returns as score_topk."""
+    import torch
+    _need_contig(q_index, row_seq, row_pos, page_table, pooled, codes, scales)
+    R = q_index.shape[0]
+    dev = q_index.device
+    dt = _dtype_code(q_index)
+    if sel_blocks is None:
+        sel_blocks = torch.empty((R, top_k), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty((R,), dtype=torch.int32, device=dev)
+    if sel_scores is None and want_scores:
+        sel_scores = torch.empty((R, top_k), dtype=torch.float32, device=dev)
+    need = score_topk_workspace_size(R, max_visible_blocks, top_k, dt, flags)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    rc = load().qsa_score_topk_paged(_ptr(q_index), _ptr(row_seq), _ptr(row_pos), R, _ptr(pooled), _ptr(codes),
+                                     _ptr(scales), _ptr(page_table), page_table.shape[1], int(page_tokens),
+                                     int(max_visible_blocks), int(top_k), float(rope_theta), int(flags), dt,
+                                     _ptr(sel_blocks), _ptr(sel_count), _ptr(sel_scores), _ptr(workspace),
+                                     workspace.numel(), _stream(stream))
+    _check("qsa_score_topk_paged", rc)
+    return sel_blocks, sel_count, sel_scores
+
+
+def sparse_attn_prefill_paged(q, row_seq, row_pos, k_cache, v_cache, page_table, page_tokens: int, sel_blocks,
+                              sel_count, softmax_scale: Optional[float] = None, out=None, lse=None, want_lse=True,
+                              stream=None):
+    """a7+a8 on a paged K/V pool: k/v [slots][Hkv][D]; page_table [R_seq][pages]."""
+    import torch
+    _need_contig(q, row_seq, row_pos, k_cache, v_cache, page_table, sel_blocks, sel_count)
+    R, Hq, D = q.shape
+    _, Hkv, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((R, Hq), dtype=torch.float32, device=q.device)
+    rc = load().qsa_sparse_attn_prefill_paged(_ptr(q), _ptr(row_seq), _ptr(row_pos), R, _ptr(k_cache), _ptr(v_cache),
+                                              _ptr(page_table), page_table.shape[1], int(page_tokens),
+                                              _ptr(sel_blocks), _ptr(sel_count), sel_blocks.shape[1], Hq, Hkv, D,
+                                              scale, _dtype_code(q), _ptr(out), _ptr(lse), _stream(stream))
+    _check("qsa_sparse_attn_prefill_paged", rc)
+    return out, lse
+
+
+def sparse_attn_decode_paged(q, row_pos, k_cache, v_cache, page_table, page_tokens: int, sel_blocks, sel_count,
+                             tail_start=None, softmax_scale: Optional[float] = None, out=None, lse=None,
+                             want_lse=True, workspace=None, stream=None):
+    """a7+a9 on a paged K/V pool: k/v [slots][Hkv][D]; page_table [B][pages]."""
+    import torch
+    _need_contig(q, row_pos, k_cache, v_cache, page_table, sel_blocks, sel_count, tail_start)
+    B, Qn, Hq, D = q.shape
+    _, Hkv, _ = k_cache.shape
+    top_k = sel_blocks.shape[1]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Qn, Hq), dtype=torch.float32, device=q.device)
+    need = sparse_attn_decode_workspace_size(B, Qn, Hq, D, top_k)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+    rc = load().qsa_sparse_attn_decode_paged(_ptr(q), _ptr(row_pos), B, Qn, _ptr(tail_start), _ptr(k_cache),
+                                             _ptr(v_cache), _ptr(page_table), page_table.shape[1], int(page_tokens),
+                                             _ptr(sel_blocks), _ptr(sel_count), top_k, Hq, Hkv, D, scale,
+                                             _dtype_code(q), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                             _stream(stream))
+    _check("qsa_sparse_attn_decode_paged", rc)
     return out, lse
 
 

@@ -256,6 +256,18 @@ def paged_slots(rng, batch: int, length: int, page_tokens: int = 16) -> np.ndarr
     return pages[:, t // page_tokens] * page_tokens + (t % page_tokens)[None, :]
 
 
+def page_table(rng, batch: int, length: int, page_tokens: int = 16, spare_pages: int = 0) -> np.ndarray:
+    """Page table [batch][ceil(length / page_tokens)] int32 of a paged pool:
+    logical page j of request r is physical page table[r][j]; the pages are a
+    random choice of distinct pages among batch * npages + spare_pages (the
+    rest stay unused).  Token t of request r is slot table[r][t // P] * P +
+    t % P."""
+    assert page_tokens % BLOCK == 0
+    npg = (length + page_tokens - 1) // page_tokens
+    pages = rng.permutation(batch * npg + spare_pages)[: batch * npg]
+    return pages.reshape(batch, npg).astype(np.int32)
+
+
 def to_float(x: np.ndarray, spec: Spec) -> np.ndarray:
     """Storage format -> float32 values."""
     return _from_storage(x, spec.dtype)

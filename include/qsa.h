@@ -218,6 +218,41 @@ qsa_status_t qsa_sparse_attn_prefill(const void *q, const int32_t *row_seq, cons
                                      qsa_dtype_t dtype, void *out, float *lse, void *stream);
 
 /*
+ * Paged KV pool ([SGL] section "Qwen Sparse Attention": the compressed keys
+ * live in the paged KV pool, one per four token slots, addressed by
+ * page-aligned full_slot / 4).  A sequence's tokens sit in pages of
+ * page_tokens slots (a multiple of 4, so a block never straddles pages):
+ * token p of sequence s is slot page_table[s*page_table_stride + p/page_tokens]
+ * * page_tokens + p % page_tokens.  The paged variants below read
+ *   - compressed keys [slots / 4][128]: block b of s is key
+ *     slot(4b) / 4 (qsa_pool_append writes exactly there);
+ *   - K/V caches [slots][Hkv][D].
+ * page_table [n_seq][page_table_stride] int32 (device); its rows must cover
+ * every position the call reads.  Everything else is as in the contiguous
+ * entry points.
+ */
+/* qsa_score_topk on paged compressed keys: `pooled` (dtype) or, for FP8 keys,
+ * `codes` + `scales` (with dtype QSA_BF16 for the index queries; pass
+ * pooled = NULL).  Workspace: qsa_score_topk_workspace_size(..., dtype, flags). */
+qsa_status_t qsa_score_topk_paged(const void *q_index, const int32_t *row_seq, const int32_t *row_pos,
+                                  int32_t rows, const void *pooled, const uint8_t *codes,
+                                  const float *scales, const int32_t *page_table,
+                                  int64_t page_table_stride, int32_t page_tokens,
+                                  int32_t max_visible_blocks, int32_t top_k, double rope_theta,
+                                  uint32_t flags, qsa_dtype_t dtype, int32_t *sel_blocks,
+                                  int32_t *sel_count, float *sel_scores, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+/* qsa_sparse_attn_prefill on a paged K/V pool (bf16 with Hq/Hkv a power of
+ * two up to 64, else QSA_ERR_UNSUPPORTED). */
+qsa_status_t qsa_sparse_attn_prefill_paged(const void *q, const int32_t *row_seq, const int32_t *row_pos,
+                                           int32_t rows, const void *k_cache, const void *v_cache,
+                                           const int32_t *page_table, int64_t page_table_stride,
+                                           int32_t page_tokens, const int32_t *sel_blocks,
+                                           const int32_t *sel_count, int32_t top_k, int32_t Hq,
+                                           int32_t Hkv, int32_t D, float softmax_scale,
+                                           qsa_dtype_t dtype, void *out, float *lse, void *stream);
+
+/*
  * Bytes of device workspace qsa_sparse_attn_decode needs (fp32 partial
  * softmax states, one per row, head and split of the positions).
  */
@@ -247,6 +282,18 @@ qsa_status_t qsa_sparse_attn_decode(const void *q, const int32_t *row_pos, int32
                                     int32_t Hkv, int32_t D, float softmax_scale,
                                     qsa_dtype_t dtype, void *out, float *lse, void *workspace,
                                     size_t workspace_bytes, void *stream);
+
+/* qsa_sparse_attn_decode on a paged K/V pool (same restriction as the
+ * prefill variant). */
+qsa_status_t qsa_sparse_attn_decode_paged(const void *q, const int32_t *row_pos, int32_t batch,
+                                          int32_t q_per_seq, const int32_t *tail_start,
+                                          const void *k_cache, const void *v_cache,
+                                          const int32_t *page_table, int64_t page_table_stride,
+                                          int32_t page_tokens, const int32_t *sel_blocks,
+                                          const int32_t *sel_count, int32_t top_k, int32_t Hq,
+                                          int32_t Hkv, int32_t D, float softmax_scale,
+                                          qsa_dtype_t dtype, void *out, float *lse, void *workspace,
+                                          size_t workspace_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *qsa_status_string(qsa_status_t status);

@@ -132,6 +132,51 @@ def test_fp8_validation(libqsa):
     assert g(A, B_, C, 4, B_, C, -1, 100, 16, 1e7, 0, B_, C, None, 0x100000, ws, None) == qsa.ERR_INVALID_ARG
 
 
+def test_paged_validation(libqsa):
+    ws = qsa.score_topk_workspace_size(4, 100, 16, qsa.BF16)
+    g = libqsa.qsa_score_topk_paged
+
+    def score(**kw):
+        a = dict(q=A, seq=B_, pos=C, rows=4, pooled=A, codes=None, scales=None, table=C, pts=100, P=16, nb=100,
+                 k=16, th=1e7, flags=0, dt=qsa.BF16, sel=B_, cnt=C, sc=None, ws=0x100000, wsb=ws)
+        a.update(kw)
+        return g(a["q"], a["seq"], a["pos"], a["rows"], a["pooled"], a["codes"], a["scales"], a["table"], a["pts"],
+                 a["P"], a["nb"], a["k"], a["th"], a["flags"], a["dt"], a["sel"], a["cnt"], a["sc"], a["ws"],
+                 a["wsb"], None)
+
+    assert score(rows=0) == qsa.OK
+    assert score(P=6) == qsa.ERR_INVALID_ARG              # pages must hold whole blocks
+    assert score(P=0) == qsa.ERR_INVALID_ARG
+    assert score(table=None) == qsa.ERR_INVALID_ARG
+    assert score(pts=1) == qsa.ERR_INVALID_ARG            # the table cannot cover 100 blocks
+    assert score(pooled=MIS) == qsa.ERR_INVALID_ARG
+    assert score(pooled=A, codes=B_, scales=C) == qsa.ERR_INVALID_ARG  # both key formats
+    assert score(pooled=None, codes=B_, scales=C, dt=qsa.F32) == qsa.ERR_UNSUPPORTED
+    assert score(wsb=ws - 1) == qsa.ERR_WORKSPACE
+    f = libqsa.qsa_sparse_attn_prefill_paged
+    args = [A, B_, C, 4, A, B_, C, 100, 16, B_, C, 16, 8, 1, 128, 0.1, qsa.BF16, A, None, None]
+    assert f(*args[:3], 0, *args[4:]) == qsa.OK
+    bad = list(args)
+    bad[8] = 10
+    assert f(*bad) == qsa.ERR_INVALID_ARG                 # page_tokens % 4
+    bad = list(args)
+    bad[6] = None
+    assert f(*bad) == qsa.ERR_INVALID_ARG                 # no table
+    bad = list(args)
+    bad[16] = qsa.F32
+    assert f(*bad) == qsa.ERR_UNSUPPORTED                 # the paged gather is the bf16 MFMA path's
+    d = libqsa.qsa_sparse_attn_decode_paged
+    wsa = qsa.sparse_attn_decode_workspace_size(2, 1, 8, 128, 16)
+    dargs = [A, B_, 2, 1, None, A, B_, C, 100, 16, B_, C, 16, 8, 1, 128, 0.1, qsa.BF16, A, None, 0x100000, wsa, None]
+    assert d(*dargs[:2], 0, *dargs[3:]) == qsa.OK
+    bad = list(dargs)
+    bad[9] = 2
+    assert d(*bad) == qsa.ERR_INVALID_ARG
+    bad = list(dargs)
+    bad[7] = None
+    assert d(*bad) == qsa.ERR_INVALID_ARG
+
+
 def test_attn_validation(libqsa):
     fp = libqsa.qsa_sparse_attn_prefill
     # rows == 0 -> OK without touching anything
