@@ -446,6 +446,8 @@ def short_kernel_name(full):
         return "attn_combine"
     if base in ("score_sample_kernel", "score_filter_kernel") and tmpl.startswith("<true"):
         return base[:-7] + "_fp8"   # the FP8-key instance
+    if base in ("attn_prefill_mfma_kernel", "attn_decode_mfma_kernel") and tmpl.startswith("<256"):
+        return base[:-7] + "_d256"  # the head-dim-256 instance
     return base[:-7] if base.endswith("_kernel") else base
 
 

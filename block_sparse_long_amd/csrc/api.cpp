@@ -408,7 +408,6 @@ static qsa_status_t check_attn_common(const void *q, const void *k_cache, const 
                                       int32_t Hkv, int32_t D, float softmax_scale, qsa_dtype_t dtype, const void *out)
 {
     if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
-    if (D != kDim) return QSA_ERR_UNSUPPORTED;
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return QSA_ERR_INVALID_ARG;
     if (top_k < 1 || top_k > QSA_MAX_TOP_K) return QSA_ERR_INVALID_ARG;
     if (!std::isfinite(softmax_scale)) return QSA_ERR_INVALID_ARG;
@@ -427,8 +426,10 @@ static qsa_status_t attn_prefill_impl(const void *q, const int32_t *row_seq, con
 {
     if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
     if (rows < 0) return QSA_ERR_INVALID_ARG;
-    if (D != kDim) return QSA_ERR_UNSUPPORTED;
+    if (D != kDim && D != kDimWide) return QSA_ERR_UNSUPPORTED;
     if (Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && Hq / Hkv > QSA_MAX_QUERY_GROUP) return QSA_ERR_UNSUPPORTED;
+    const bool mfma = attn_mfma_supported(Hq, Hkv, 1, D, dtype == QSA_BF16);
+    if (D == kDimWide && !mfma) return QSA_ERR_UNSUPPORTED;  // D = 256 lives in the bf16 MFMA kernels
     if (rows == 0) {
         if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || top_k < 1 || top_k > QSA_MAX_TOP_K) return QSA_ERR_INVALID_ARG;
         return QSA_OK;
@@ -452,6 +453,7 @@ static qsa_status_t attn_prefill_impl(const void *q, const int32_t *row_seq, con
     a.q_per_sel = 1;
     a.Hq = Hq;
     a.Hkv = Hkv;
+    a.D = D;
     a.scale = softmax_scale;
     a.out = out;
     a.lse = lse;
@@ -460,7 +462,6 @@ static qsa_status_t attn_prefill_impl(const void *q, const int32_t *row_seq, con
     a.page_table = page_table;
     a.pt_stride = pt_stride;
     a.page_tokens = page_tokens;
-    const bool mfma = attn_mfma_supported(Hq, Hkv, 1, dtype == QSA_BF16);
     if (page_table && !mfma) return QSA_ERR_UNSUPPORTED;  // the paged gather lives in the MFMA kernels
     clear_launch_err();
     if (mfma)
@@ -496,9 +497,11 @@ qsa_status_t qsa_sparse_attn_prefill_paged(const void *q, const int32_t *row_seq
 
 size_t qsa_sparse_attn_decode_workspace_size(int32_t batch, int32_t q_per_seq, int32_t Hq, int32_t D, int32_t top_k)
 {
-    if (batch <= 0 || q_per_seq <= 0 || Hq <= 0 || D != kDim || top_k < 1 || top_k > QSA_MAX_TOP_K) return 0;
+    if (batch <= 0 || q_per_seq <= 0 || Hq <= 0 || (D != kDim && D != kDimWide) || top_k < 1 ||
+        top_k > QSA_MAX_TOP_K)
+        return 0;
     const size_t nsplit = (size_t)attn_decode_splits(top_k);
-    return align256((size_t)batch * q_per_seq * Hq * nsplit * (kDim + 2) * sizeof(float));
+    return align256((size_t)batch * q_per_seq * Hq * nsplit * (D + 2) * sizeof(float));
 }
 
 static qsa_status_t attn_decode_impl(const void *q, const int32_t *row_pos, int32_t batch, int32_t q_per_seq,
@@ -511,9 +514,11 @@ static qsa_status_t attn_decode_impl(const void *q, const int32_t *row_pos, int3
 {
     if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
     if (batch < 0 || q_per_seq < 1) return QSA_ERR_INVALID_ARG;
-    if (D != kDim) return QSA_ERR_UNSUPPORTED;
+    if (D != kDim && D != kDimWide) return QSA_ERR_UNSUPPORTED;
     if (Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && (int64_t)q_per_seq * (Hq / Hkv) > QSA_MAX_QUERY_GROUP)
         return QSA_ERR_UNSUPPORTED;
+    const bool mfma = attn_mfma_supported(Hq, Hkv, q_per_seq, D, dtype == QSA_BF16);
+    if (D == kDimWide && !mfma) return QSA_ERR_UNSUPPORTED;  // D = 256 lives in the bf16 MFMA kernels
     if (batch == 0) {
         if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || top_k < 1 || top_k > QSA_MAX_TOP_K) return QSA_ERR_INVALID_ARG;
         return QSA_OK;
@@ -540,6 +545,7 @@ static qsa_status_t attn_decode_impl(const void *q, const int32_t *row_pos, int3
     a.q_per_sel = q_per_seq;
     a.Hq = Hq;
     a.Hkv = Hkv;
+    a.D = D;
     a.scale = softmax_scale;
     a.out = out;
     a.lse = lse;
@@ -548,7 +554,6 @@ static qsa_status_t attn_decode_impl(const void *q, const int32_t *row_pos, int3
     a.page_table = page_table;
     a.pt_stride = pt_stride;
     a.page_tokens = page_tokens;
-    const bool mfma = attn_mfma_supported(Hq, Hkv, q_per_seq, dtype == QSA_BF16);
     if (page_table && !mfma) return QSA_ERR_UNSUPPORTED;  // the paged gather lives in the MFMA kernels
     clear_launch_err();
     if (mfma) {

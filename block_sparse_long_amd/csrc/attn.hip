@@ -213,31 +213,31 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a)
     }
 }
 
-// Merge the decode splits of one (row, head): grid = rows*Hq, 128 threads.
+// Merge the decode splits of one (row, head): grid = rows*Hq, DIM threads.
 // Wave 0 reduces the splits' (m, l) with one split per lane; then every thread
 // owns one output dim and sums the splits' weighted partial outputs, several
 // loads in flight at once.
 constexpr int kMaxDecodeSplits = (kBlock * QSA_MAX_TOP_K + kAC - 1) / kAC + 1;
 
-template <typename T>
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float *__restrict__ partial, int32_t nsplit,
+template <typename T, int DIM>
+__global__ __launch_bounds__(DIM) void attn_combine_kernel(const float *__restrict__ partial, int32_t nsplit,
                                                            void *out, float *lse)
 {
     __shared__ float wsplit[kMaxDecodeSplits];
     __shared__ float s_m, s_l;
     const int64_t qrow = blockIdx.x;
     const int d = threadIdx.x;
-    const float *pp = partial + qrow * nsplit * (kDim + 2);
+    const float *pp = partial + qrow * nsplit * (DIM + 2);
     if (d < kWave) {
         float m = -INFINITY;
-        for (int s = d; s < nsplit; s += kWave) m = fmaxf(m, pp[s * (kDim + 2) + kDim]);
+        for (int s = d; s < nsplit; s += kWave) m = fmaxf(m, pp[s * (DIM + 2) + DIM]);
         m = wave_max(m);
         float l = 0.0f;
         for (int s = d; s < nsplit; s += kWave) {
-            const float ms = pp[s * (kDim + 2) + kDim];
+            const float ms = pp[s * (DIM + 2) + DIM];
             const float e = ms == -INFINITY ? 0.0f : __expf(ms - m);
             wsplit[s] = e;
-            l += pp[s * (kDim + 2) + kDim + 1] * e;
+            l += pp[s * (DIM + 2) + DIM + 1] * e;
         }
         l = wave_sum(l);
         if (d == 0) {
@@ -252,12 +252,12 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float *__restri
         int s = 0;
         for (; s + 4 <= nsplit; s += 4) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] += wsplit[s + j] * pp[(s + j) * (kDim + 2) + d];
+            for (int j = 0; j < 4; ++j) acc[j] += wsplit[s + j] * pp[(s + j) * (DIM + 2) + d];
         }
-        for (; s < nsplit; ++s) acc[0] += wsplit[s] * pp[s * (kDim + 2) + d];
+        for (; s < nsplit; ++s) acc[0] += wsplit[s] * pp[s * (DIM + 2) + d];
     }
     const float o = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    store_f32((T *)out + qrow * kDim + d, L > 0.0f ? o / L : 0.0f);
+    store_f32((T *)out + qrow * DIM + d, L > 0.0f ? o / L : 0.0f);
     if (lse && d == 0) lse[qrow] = L > 0.0f ? M + __logf(L) : -INFINITY;
 }
 
@@ -293,12 +293,16 @@ void launch_attn_decode(const AttnArgs &a, bool bf16, hipStream_t stream)
 void launch_attn_combine(const AttnArgs &a, bool bf16, hipStream_t stream)
 {
     const int64_t qrows = (int64_t)a.n_sel * a.q_per_sel * a.Hq;
-    if (bf16)
-        QSA_LAUNCH("attn_combine", attn_combine_kernel<bf16_t>, dim3((unsigned)qrows), dim3(128), 0, stream,
-                   a.partial, a.nsplit, a.out, a.lse);
+    const dim3 grid((unsigned)qrows);
+    if (a.D == 256)  // the bf16 MFMA path's head dim
+        QSA_LAUNCH("attn_combine", (attn_combine_kernel<bf16_t, 256>), grid, dim3(256), 0, stream, a.partial,
+                   a.nsplit, a.out, a.lse);
+    else if (bf16)
+        QSA_LAUNCH("attn_combine", (attn_combine_kernel<bf16_t, kDim>), grid, dim3(kDim), 0, stream, a.partial,
+                   a.nsplit, a.out, a.lse);
     else
-        QSA_LAUNCH("attn_combine", attn_combine_kernel<float>, dim3((unsigned)qrows), dim3(128), 0, stream,
-                   a.partial, a.nsplit, a.out, a.lse);
+        QSA_LAUNCH("attn_combine", (attn_combine_kernel<float, kDim>), grid, dim3(kDim), 0, stream, a.partial,
+                   a.nsplit, a.out, a.lse);
 }
 
 }  // namespace qsa

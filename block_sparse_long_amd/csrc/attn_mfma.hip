@@ -11,25 +11,26 @@
 //
 // Layout of the work.  A workgroup owns up to 64 queries that share one KV
 // head: (rows of the tile) x (Hq/Hkv heads), as 4 MFMA tiles of 16 queries,
-// one per wave.  It walks a list of positions in chunks of 64: the chunk's K
-// rows (row-major) and V rows (transposed) are gathered into LDS once and
-// every wave computes S^T = K Q^T for its 16 queries (v_mfma_f32_16x16x32_bf16,
-// positions on M, queries on N), an online softmax, then O += P V (queries on
-// M, head dims on N).  Each position of a chunk carries a mask of the query
+// one per wave.  It walks a list of positions in chunks (64 positions at head
+// dim D = 128, 32 at D = 256, so a chunk is 16 KiB of K and of V either way):
+// the chunk's K rows (row-major) and V rows (transposed) are gathered into LDS
+// once and every wave computes S^T = K Q^T for its 16 queries
+// (v_mfma_f32_16x16x32_bf16, positions on M, queries on N), an online
+// softmax, then O += P V (queries on M, head dims on N).  Each position of a chunk carries a mask of the query
 // rows that attend it, so one gathered chunk serves every row of the tile:
 //   - prefill: the tile is up to 64/(Hq/Hkv) consecutive rows; the position
 //     list is the union of their kept blocks (built in LDS with a bitmap per
 //     window of 65,536 blocks) followed by each row's tail tokens;
 //   - decode: the rows of one sequence share its selection; a workgroup takes
-//     one chunk of 16 kept blocks (split) or the tail, and a combine kernel
-//     merges the splits' partial softmaxes.
+//     16 kept blocks (a split, one or two chunks) or the tail, and a combine
+//     kernel merges the splits' partial softmaxes.
 // A wave skips the MFMAs of a 16-position sub-tile that none of its rows
 // attends, so disjoint selections cost gathers but not matrix work.
 //
 // MFMA operand layout (16x16x32): lane l supplies A[m = l%16][8 k-slots of
 // group l/16] and B[8 k-slots of group l/16][n = l%16] and receives
 // C[4*(l/16) + j][l%16].  For S^T = K Q^T the k-slots of group g at step s
-// are head dims 32g + 8s .. +7.  For O = P V, a 32-position step covers
+// are head dims (D/4)g + 8s .. +7.  For O = P V, a 32-position step covers
 // sub-tiles 2i and 2i+1; group g's slots 0-3 are positions 4g..4g+3 of
 // sub-tile 2i and slots 4-7 those of sub-tile 2i+1 -- exactly the S^T values
 // the lane already holds, so P needs no shuffle.
@@ -40,13 +41,24 @@ namespace qsa {
 
 namespace {
 
-constexpr int kCh = 64;             // positions per chunk
-constexpr int kKRow = kDim + 8;     // LDS row stride of K (bf16), 272 B: conflict-free b128 reads
-constexpr int kVRow = kCh + 8;      // LDS row stride of V^T (bf16), 144 B
+// Shapes of one chunk at head dim DIM.
+template <int DIM>
+struct Geo {
+    static_assert(DIM == 128 || DIM == 256, "head dims 128 and 256");
+    static constexpr int kCh = 8192 / DIM;    // positions per chunk: 64 or 32
+    static constexpr int kKRow = DIM + 8;     // LDS row stride of K (bf16): 4 banks of skew per row
+    static constexpr int kVRow = kCh + 8;     // LDS row stride of V^T (bf16), a multiple of 16 bytes
+    static constexpr int kSub = kCh / 16;     // 16-position sub-tiles of S^T
+    static constexpr int kKs = DIM / 32;      // k-steps of S^T
+    static constexpr int kNt = DIM / 16;      // 16-column tiles of O
+    static constexpr int kTpp = 256 / kCh;    // gather threads per K row, 32 dims each
+    static constexpr int kChB = kCh / kBlock; // whole blocks per chunk
+};
+constexpr int kSplitBlocks = 16;    // kept blocks of one decode split (64 positions)
 constexpr int kWin = 1 << 16;       // union bitmap window, in blocks
 constexpr int kWinWords = kWin / 32;
 constexpr int kMaxUnionBlocks = 4096;  // rows per tile x top_k is kept at or below this
-constexpr int kMaxTileRows = 16;       // row masks are 16 bits
+constexpr int kMaxTileRows = 16;       // row masks are 16 bits, two per LDS word
 
 // Column of chunk position p in a V^T row.  The P V MFMA of 32-position step
 // i takes, in lane group g, positions 32i + 4g .. +3 and 32i + 16 + 4g .. +3;
@@ -58,20 +70,26 @@ __device__ __forceinline__ int vt_col(int p)
     return 32 * i + 8 * g + 4 * h + j;
 }
 
+template <int DIM>
 struct alignas(16) ChunkSmem {
-    bf16_t k[kCh][kKRow];
-    bf16_t vt[kDim][kVRow];
-    int32_t pos[kCh];
-    uint32_t pmask[kCh];
+    bf16_t k[Geo<DIM>::kCh][Geo<DIM>::kKRow];
+    bf16_t vt[DIM][Geo<DIM>::kVRow];
+    int32_t pos[Geo<DIM>::kCh];
+    uint32_t pmask[Geo<DIM>::kCh];
 };
 
 struct alignas(16) UnionSmem {
     uint32_t bitmap[kWinWords];
-    uint16_t wprefix[kWinWords];     // < kMaxUnionBlocks
+    uint16_t wprefix[kWinWords];         // < kMaxUnionBlocks
     int32_t blk[kMaxUnionBlocks];
-    uint32_t mask[kMaxUnionBlocks];  // bit r: tile row r keeps the block
+    uint32_t mask2[kMaxUnionBlocks / 2];  // union block i: bits 16(i%2) + r of word i/2, r = tile row keeping it
     uint32_t count;
 };
+
+__device__ __forceinline__ uint32_t union_mask(const UnionSmem &us, int i)
+{
+    return (us.mask2[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+}
 
 // Logits are kept in base-2 units (softmax_scale * log2(e) * <q, k>).  The
 // softmax reference max of a query moves only when a logit exceeds it by more
@@ -84,13 +102,15 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 // Per-wave attention state: 16 queries, lane l <-> query l%16 for m / l,
 // O[q = 4*(l/16) + j][dim 16*nt + l%16] in o[nt][j].
+template <int DIM>
 struct WaveState {
-    f32x4_t o[8];
+    f32x4_t o[Geo<DIM>::kNt];
     float m, l;
 };
 
-// A thread's share of one chunk's gather: K row t/4 (64 bytes at dim
-// 32*(t%4)) and V of positions 4*(t/16) .. +3 at dims 8*(t%16) .. +7.
+// A thread's share of one chunk's gather, 64 bytes of K and 64 of V: K row
+// t/kTpp at dims 32*(t%kTpp) .. +31, and V of positions 4q .. 4q+3 at dims
+// 8*(t/(kCh/4)) .. +7, q = t%(kCh/4).
 struct ChunkRegs {
     uint4 k[4];
     uint4 v[4];
@@ -99,12 +119,13 @@ struct ChunkRegs {
 // Load the chunk of positions pos(0..n) into registers (zeros beyond n).  The
 // loads are only consumed by chunk_store, so they can stay in flight while
 // the previous chunk is computed.
-template <class PosFn>
+template <int DIM, class PosFn>
 __device__ __forceinline__ void chunk_load(ChunkRegs &cr, const bf16_t *__restrict__ kbase,
                                            const bf16_t *__restrict__ vbase, int64_t row_stride, int n, PosFn pos)
 {
+    using G = Geo<DIM>;
     const int t = threadIdx.x;
-    const int p = t >> 2, dk = (t & 3) * 32;
+    const int p = t / G::kTpp, dk = (t % G::kTpp) * 32;
     if (p < n) {
         const uint4 *src = (const uint4 *)(kbase + (int64_t)pos(p) * row_stride + dk);
 #pragma unroll
@@ -113,7 +134,7 @@ __device__ __forceinline__ void chunk_load(ChunkRegs &cr, const bf16_t *__restri
 #pragma unroll
         for (int i = 0; i < 4; ++i) cr.k[i] = make_uint4(0, 0, 0, 0);
     }
-    const int p0 = (t & 15) * 4, dv = (t >> 4) * 8;
+    const int p0 = (t % (G::kCh / 4)) * 4, dv = (t / (G::kCh / 4)) * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         cr.v[i] = (p0 + i < n) ? *(const uint4 *)(vbase + (int64_t)pos(p0 + i) * row_stride + dv)
@@ -130,23 +151,25 @@ __device__ __forceinline__ int64_t kv_slot(const AttnArgs &a, int64_t s, int64_t
 }
 
 // The same share of a chunk of whole blocks: ublk[0..nb) are the chunk's
-// blocks (16 at most, nb >= 1).  Thread t's K position is token (t/4)%4 of
-// block t/16 and its V positions are tokens 0..3 of block t%16, so one block
-// id serves each; a thread past the chunk's blocks reads the last one instead
-// (its positions carry no mask bit, so their P is exactly 0).  Every load is
-// unconditional.
+// blocks (kChB at most, nb >= 1).  Thread t's K position is token (t/kTpp)%4
+// of block t/(4 kTpp) and its V positions are tokens 0..3 of block t%kChB, so
+// one block id serves each; a thread past the chunk's blocks reads the last
+// one instead (its positions carry no mask bit, so their P is exactly 0).
+// Every load is unconditional.
+template <int DIM>
 __device__ __forceinline__ void chunk_load_blocks(ChunkRegs &cr, const bf16_t *__restrict__ kbase,
                                                   const bf16_t *__restrict__ vbase, uint32_t row_stride,
                                                   const int32_t *ublk, int nb, const AttnArgs &a, int64_t seq)
 {
+    using G = Geo<DIM>;
     const int t = threadIdx.x;
-    const int32_t bk = ublk[min(t >> 4, nb - 1)], bv = ublk[min(t & 15, nb - 1)];
+    const int32_t bk = ublk[min(t / (4 * G::kTpp), nb - 1)], bv = ublk[min(t % G::kChB, nb - 1)];
     // first slot of each block: its 4 tokens are consecutive slots
     const uint32_t sk = (uint32_t)kv_slot(a, seq, (int64_t)kBlock * bk), sv = (uint32_t)kv_slot(a, seq, (int64_t)kBlock * bv);
     typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    const u32x4_t *ks = (const u32x4_t *)(kbase + (uint64_t)sk * row_stride + ((t >> 2) & 3) * row_stride +
-                                          (t & 3) * 32);
-    const bf16_t *vs = vbase + (uint64_t)sv * row_stride + (t >> 4) * 8;
+    const u32x4_t *ks = (const u32x4_t *)(kbase + (uint64_t)sk * row_stride +
+                                          ((t / G::kTpp) & 3) * row_stride + (t % G::kTpp) * 32);
+    const bf16_t *vs = vbase + (uint64_t)sv * row_stride + (t / G::kChB) * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // element-wise vector loads (a block copy would go through memory)
         const u32x4_t kx = ks[i], vx = *(const u32x4_t *)(vs + i * row_stride);
@@ -156,15 +179,17 @@ __device__ __forceinline__ void chunk_load_blocks(ChunkRegs &cr, const bf16_t *_
 }
 
 // Registers -> LDS: K row-major, V transposed.
-__device__ __forceinline__ void chunk_store(ChunkSmem &cs, const ChunkRegs &cr)
+template <int DIM>
+__device__ __forceinline__ void chunk_store(ChunkSmem<DIM> &cs, const ChunkRegs &cr)
 {
+    using G = Geo<DIM>;
     const int t = threadIdx.x;
-    const int p = t >> 2, dk = (t & 3) * 32;
+    const int p = t / G::kTpp, dk = (t % G::kTpp) * 32;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *(uint4 *)&cs.k[p][dk + 8 * i] = cr.k[i];
-    // the 16 lanes sharing dv write 16 distinct 8-byte pieces of a V^T row;
+    // the kCh/4 lanes sharing dv write distinct 8-byte pieces of a V^T row;
     // position p0 + j is stored at vt_col(p0) + j
-    const int q = t & 15, dv = (t >> 4) * 8;
+    const int q = t % (G::kCh / 4), dv = (t / (G::kCh / 4)) * 8;
     const int c0 = vt_col(4 * q);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {  // dims dv + 2w (low halves) and dv + 2w + 1 (high halves)
@@ -179,38 +204,45 @@ __device__ __forceinline__ void chunk_store(ChunkSmem &cs, const ChunkRegs &cr)
 }
 
 // Gather K and V^T of positions cs.pos[0..n) into LDS (zeros beyond n).
-__device__ __forceinline__ void gather_chunk(ChunkSmem &cs, const bf16_t *__restrict__ kbase,
+template <int DIM>
+__device__ __forceinline__ void gather_chunk(ChunkSmem<DIM> &cs, const bf16_t *__restrict__ kbase,
                                              const bf16_t *__restrict__ vbase, int64_t row_stride, int n)
 {
     ChunkRegs cr;
-    chunk_load(cr, kbase, vbase, row_stride, n, [&](int i) { return (int64_t)cs.pos[i]; });
-    chunk_store(cs, cr);
+    chunk_load<DIM>(cr, kbase, vbase, row_stride, n, [&](int i) { return (int64_t)cs.pos[i]; });
+    chunk_store<DIM>(cs, cr);
 }
 
 // One chunk for one wave: S^T, online softmax, O += P V.  `qbit` is the mask
 // bit of this lane's query row (0 when the query slot is unused); positions
 // past the chunk's end carry no mask bit.  `scale2` = softmax_scale * log2(e).
-__device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, const bf16x8_t (&qb)[4], uint32_t qbit,
-                                           float scale2, WaveState &st)
+template <int DIM>
+__device__ __forceinline__ void wave_chunk(const ChunkSmem<DIM> &cs, const bf16x8_t (&qb)[Geo<DIM>::kKs],
+                                           uint32_t qbit, float scale2, WaveState<DIM> &st)
 {
+    using G = Geo<DIM>;
     const int lane = threadIdx.x & 63;
     const int m16 = lane & 15, g = lane >> 4;
-    float s[4][4];
-    bool any[4];
+    float s[G::kSub][4];
+    bool any[G::kSub];
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
+    for (int sub = 0; sub < G::kSub; ++sub) {
         const uint4 pm = *(const uint4 *)&cs.pmask[sub * 16 + 4 * g];  // positions 4g .. 4g+3 of the sub-tile
         const bool ok[4] = {(pm.x & qbit) != 0u, (pm.y & qbit) != 0u, (pm.z & qbit) != 0u, (pm.w & qbit) != 0u};
         any[sub] = __ballot(ok[0] | ok[1] | ok[2] | ok[3]) != 0ull;
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (any[sub]) {  // the sub-tile's 4 K operands are read together, then its MFMAs issue
-            uint4 kv[4];
+        if (any[sub]) {  // the sub-tile's K operands are read 4 at a time, then their MFMAs issue
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) kv[ks] = *(const uint4 *)&cs.k[sub * 16 + m16][32 * g + 8 * ks];
-            __builtin_amdgcn_sched_barrier(0);
+            for (int k0 = 0; k0 < G::kKs; k0 += 4) {
+                uint4 kv[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks]), qb[ks], acc, 0, 0, 0);
+                for (int ks = 0; ks < 4; ++ks)
+                    kv[ks] = *(const uint4 *)&cs.k[sub * 16 + m16][(DIM / 4) * g + 8 * (k0 + ks)];
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks]), qb[k0 + ks], acc, 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) s[sub][j] = ok[j] ? acc[j] * scale2 : -INFINITY;
@@ -218,7 +250,7 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, const bf16x8_t (
     // online softmax per query (lane l%16; the 4 lane groups hold its positions)
     float cmax = -INFINITY;
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub)
+    for (int sub = 0; sub < G::kSub; ++sub)
 #pragma unroll
         for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, s[sub][j]);
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
@@ -232,31 +264,31 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, const bf16x8_t (
 #pragma unroll
         for (int j = 0; j < 4; ++j) a4[j] = __shfl(alpha, 4 * g + j);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
+        for (int nt = 0; nt < G::kNt; ++nt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) st.o[nt][j] *= a4[j];
     }
     st.m = m_ref;
-    float p[4][4];
+    float p[G::kSub][4];
     float psum = 0.0f;
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub)
+    for (int sub = 0; sub < G::kSub; ++sub)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {  // a masked logit (-inf) gives 0; m_ref is finite
             p[sub][j] = __builtin_amdgcn_exp2f(s[sub][j] - m_ref);
             psum += p[sub][j];
         }
     st.l += psum;  // per-lane partial; the 4 groups are summed at the end
-    // O += P V over two 32-position steps
+    // O += P V over the chunk's 32-position steps
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < G::kSub / 2; ++i) {
         if (!(any[2 * i] || any[2 * i + 1])) continue;
         const uint4 pa = make_uint4(pack_bf16x2(p[2 * i][0], p[2 * i][1]), pack_bf16x2(p[2 * i][2], p[2 * i][3]),
                                     pack_bf16x2(p[2 * i + 1][0], p[2 * i + 1][1]),
                                     pack_bf16x2(p[2 * i + 1][2], p[2 * i + 1][3]));
         const bf16x8_t A = as_bf16x8(pa);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {  // V^T operands 4 at a time: one LDS wait per 4 MFMAs
+        for (int h = 0; h < G::kNt / 4; ++h) {  // V^T operands 4 at a time: one LDS wait per 4 MFMAs
             bf16x8_t Bv[4];
 #pragma unroll
             for (int n = 0; n < 4; ++n)
@@ -269,24 +301,28 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem &cs, const bf16x8_t (
     }
 }
 
-__device__ __forceinline__ void load_query(const bf16_t *__restrict__ qrow, bool valid, bf16x8_t (&qb)[4])
+template <int DIM>
+__device__ __forceinline__ void load_query(const bf16_t *__restrict__ qrow, bool valid,
+                                           bf16x8_t (&qb)[Geo<DIM>::kKs])
 {
     const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        qb[ks] = valid ? as_bf16x8(*(const uint4 *)(qrow + 32 * g + 8 * ks)) : zero_bf16x8();
+    for (int ks = 0; ks < Geo<DIM>::kKs; ++ks)
+        qb[ks] = valid ? as_bf16x8(*(const uint4 *)(qrow + (DIM / 4) * g + 8 * ks)) : zero_bf16x8();
 }
 
-__device__ __forceinline__ void init_state(WaveState &st)
+template <int DIM>
+__device__ __forceinline__ void init_state(WaveState<DIM> &st)
 {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) st.o[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nt = 0; nt < Geo<DIM>::kNt; ++nt) st.o[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     st.m = kNoMax;
     st.l = 0.0f;
 }
 
 // Final per-query sums; returns l_total of the lane's query (l%16).
-__device__ __forceinline__ float total_l(const WaveState &st)
+template <int DIM>
+__device__ __forceinline__ float total_l(const WaveState<DIM> &st)
 {
     float l = st.l;
     l += __shfl_xor(l, 16);
@@ -296,12 +332,16 @@ __device__ __forceinline__ float total_l(const WaveState &st)
 
 }  // namespace
 
+static_assert(kSplitBlocks * kBlock == kAttnChunk, "a decode split covers one chunk of attn_decode_splits()");
+
 // ---------------------------------------------------------------------------
 // Prefill: grid (row tiles, Hkv).  rows_per_tile * hg <= 64.
 // ---------------------------------------------------------------------------
+template <int DIM>
 __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, int32_t rows_per_tile)
 {
-    __shared__ ChunkSmem cs;
+    using G = Geo<DIM>;
+    __shared__ ChunkSmem<DIM> cs;
     __shared__ UnionSmem us;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m16 = lane & 15, g = lane >> 4;
@@ -314,12 +354,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
     const int r_local = qi / hg;
     const bool q_valid = r_local < nrows;
     const int head = kvh * hg + qi % hg;
-    bf16x8_t qb[4];
-    load_query((const bf16_t *)a.q + ((row0 + (q_valid ? r_local : 0)) * a.Hq + head) * kDim, q_valid, qb);
-    WaveState st;
+    bf16x8_t qb[G::kKs];
+    load_query<DIM>((const bf16_t *)a.q + ((row0 + (q_valid ? r_local : 0)) * a.Hq + head) * DIM, q_valid, qb);
+    WaveState<DIM> st;
     init_state(st);
     const float scale2 = a.scale * kLog2e;
-    const int64_t row_stride = (int64_t)a.Hkv * kDim;
+    const int64_t row_stride = (int64_t)a.Hkv * DIM;
     // ---- the tile's rows, read once: position, sequence, kept count, last
     // kept block; and all their kept blocks (at most kMaxUnionBlocks, 16 per
     // thread), loaded together and kept in registers for the union passes ----
@@ -334,16 +374,19 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
     }
     __syncthreads();
     constexpr int kSelPerThread = kMaxUnionBlocks / 256;
-    int32_t eblk[kSelPerThread];  // kept block, or -1
-    int32_t erow[kSelPerThread];  // its tile row
+    int32_t eblk[kSelPerThread];           // kept block, or -1
+    uint32_t erow4[kSelPerThread / 8];     // its tile row, 4 bits per entry
+#pragma unroll
+    for (int j = 0; j < kSelPerThread / 8; ++j) erow4[j] = 0u;
 #pragma unroll
     for (int j = 0; j < kSelPerThread; ++j) {
         const int32_t idx = t + 256 * j;
         const int32_t r = idx / a.top_k, i = idx - r * a.top_k;
         const bool ok = r < nrows && i < s_cnt[min(r, nrows - 1)];
-        erow[j] = ok ? r : 0;
+        erow4[j / 8] |= (uint32_t)(ok ? r : 0) << (4 * (j % 8));
         eblk[j] = ok ? a.sel_blocks[(row0 + r) * a.top_k + i] : -1;
     }
+    auto erow = [&](int j) { return (int)((erow4[j / 8] >> (4 * (j % 8))) & 15u); };
     uint32_t todo = nrows >= 32 ? 0xffffffffu : ((1u << nrows) - 1u);
     while (todo) {  // rows of one sequence at a time (uniform across the workgroup)
         const int first = __builtin_ctz(todo);
@@ -354,8 +397,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
         todo &= ~active;
         const uint32_t qbit = q_valid ? (active & (1u << r_local)) : 0u;
         const int64_t seq_off = a.page_table ? 0 : (int64_t)seq * a.kv_seq_stride;
-        const bf16_t *kbase = (const bf16_t *)a.k_cache + seq_off + (int64_t)kvh * kDim;
-        const bf16_t *vbase = (const bf16_t *)a.v_cache + seq_off + (int64_t)kvh * kDim;
+        const bf16_t *kbase = (const bf16_t *)a.k_cache + seq_off + (int64_t)kvh * DIM;
+        const bf16_t *vbase = (const bf16_t *)a.v_cache + seq_off + (int64_t)kvh * DIM;
         // block range of the active rows' selections
         int32_t hi_blk = 0;
         for (int r = 0; r < nrows; ++r)
@@ -367,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
 #pragma unroll
             for (int j = 0; j < kSelPerThread; ++j) {
                 const int32_t b = eblk[j] - w0;
-                if (eblk[j] >= 0 && ((active >> erow[j]) & 1u) && b >= 0 && b < kWin)
+                if (eblk[j] >= 0 && ((active >> erow(j)) & 1u) && b >= 0 && b < kWin)
                     atomicOr(&us.bitmap[b >> 5], 1u << (b & 31));
             }
             __syncthreads();
@@ -393,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
                         const int b = __builtin_ctz(bits);
                         bits &= bits - 1u;
                         us.blk[k] = w0 + (t * per + i) * 32 + b;
-                        us.mask[k] = 0u;
+                        if (!(k & 1u)) us.mask2[k >> 1] = 0u;  // word k/2 has one even index, owned here
                         ++k;
                     }
                     run += __popc(word);
@@ -403,69 +446,71 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
 #pragma unroll
             for (int j = 0; j < kSelPerThread; ++j) {
                 const int32_t b = eblk[j] - w0;
-                if (eblk[j] >= 0 && ((active >> erow[j]) & 1u) && b >= 0 && b < kWin) {
+                if (eblk[j] >= 0 && ((active >> erow(j)) & 1u) && b >= 0 && b < kWin) {
                     const uint32_t word = us.bitmap[b >> 5];
                     const uint32_t idx = us.wprefix[b >> 5] + __popc(word & ((1u << (b & 31)) - 1u));
-                    atomicOr(&us.mask[idx], 1u << erow[j]);
+                    atomicOr(&us.mask2[idx >> 1], 1u << (erow(j) + 16 * (idx & 1u)));
                 }
             }
             __syncthreads();
             const int32_t nu = (int32_t)us.count;
-            // ---- the union's blocks, 16 per chunk; chunk c+1's gather is in
+            // ---- the union's blocks, kChB per chunk; chunk c+1's gather is in
             // flight while chunk c is computed ----
-            constexpr int kChB = kCh / kBlock;
+            constexpr int kChB = G::kChB;
             const int32_t nch = (nu + kChB - 1) / kChB;
             ChunkRegs cr;
-            if (nch > 0) chunk_load_blocks(cr, kbase, vbase, (uint32_t)row_stride, us.blk, min(kChB, nu), a, seq);
+            if (nch > 0)
+                chunk_load_blocks<DIM>(cr, kbase, vbase, (uint32_t)row_stride, us.blk, min(kChB, nu), a, seq);
             for (int32_t c = 0; c < nch; ++c) {
                 const int32_t c0 = c * kChB;
                 const int nb = min(kChB, nu - c0);
-                chunk_store(cs, cr);
-                if (t < kCh) cs.pmask[t] = t / kBlock < nb ? us.mask[c0 + t / kBlock] : 0u;
+                chunk_store<DIM>(cs, cr);
+                if (t < G::kCh) cs.pmask[t] = t / kBlock < nb ? union_mask(us, c0 + t / kBlock) : 0u;
                 __syncthreads();
                 if (c + 1 < nch) {
                     const int32_t c1 = c0 + kChB;
-                    chunk_load_blocks(cr, kbase, vbase, (uint32_t)row_stride, us.blk + c1, min(kChB, nu - c1), a,
-                                      seq);
+                    chunk_load_blocks<DIM>(cr, kbase, vbase, (uint32_t)row_stride, us.blk + c1, min(kChB, nu - c1),
+                                           a, seq);
                 }
-                wave_chunk(cs, qb, qbit, scale2, st);
+                wave_chunk<DIM>(cs, qb, qbit, scale2, st);
                 __syncthreads();
             }
         }
-        // ---- tails: positions [4*nc(t), t] of every active row ----
-        if (t < kCh) {
-            int n = 0;
-            int32_t pos = 0;
-            uint32_t msk = 0;
-            for (int r = 0; r < nrows && n <= t; ++r) {
-                if (!((active >> r) & 1u)) continue;
-                const int32_t tr = s_pos[r];
-                const int32_t ts = (int32_t)(kBlock * visible_blocks(tr));
-                const int len = tr - ts + 1;  // 0..3
-                if (t < n + len) {
-                    pos = ts + (t - n);
-                    msk = 1u << r;
-                }
-                n += len;
-            }
-            cs.pos[t] = (int32_t)kv_slot(a, seq, pos);
-            cs.pmask[t] = msk;
-        }
-        __syncthreads();
+        // ---- tails: positions [4*nc(t), t] of every active row (at most 16
+        // rows x 3 tokens), a chunk at a time ----
         int ntail = 0;
         for (int r = 0; r < nrows; ++r) {
             if (!((active >> r) & 1u)) continue;
             const int32_t tr = s_pos[r];
             ntail += tr - (int32_t)(kBlock * visible_blocks(tr)) + 1;
         }
-        ntail = min(ntail, kCh);  // at most 16 rows x 3 tokens
-        if (ntail > 0) {
-            gather_chunk(cs, kbase, vbase, row_stride, ntail);
+        for (int tc = 0; tc < ntail; tc += G::kCh) {
+            if (t < G::kCh) {
+                const int idx = tc + t;
+                int n = 0;
+                int32_t pos = 0;
+                uint32_t msk = 0;
+                for (int r = 0; r < nrows && n <= idx; ++r) {
+                    if (!((active >> r) & 1u)) continue;
+                    const int32_t tr = s_pos[r];
+                    const int32_t ts = (int32_t)(kBlock * visible_blocks(tr));
+                    const int len = tr - ts + 1;  // 0..3
+                    if (idx < n + len) {
+                        pos = ts + (idx - n);
+                        msk = 1u << r;
+                    }
+                    n += len;
+                }
+                cs.pos[t] = (int32_t)kv_slot(a, seq, pos);
+                cs.pmask[t] = msk;
+            }
             __syncthreads();
-            // positions beyond n carry no mask bit, so they stay out
-            wave_chunk(cs, qb, qbit, scale2, st);
+            // positions beyond the tails carry no mask bit, so they stay out
+            gather_chunk<DIM>(cs, kbase, vbase, row_stride, min(G::kCh, ntail - tc));
+            __syncthreads();
+            wave_chunk<DIM>(cs, qb, qbit, scale2, st);
+            __syncthreads();
         }
-        __syncthreads();
     }
     // ---- output ----
     const float ltot = total_l(st);
@@ -476,22 +521,25 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
         const float lq = __shfl(ltot, 4 * g + j);
         if (ro >= nrows) continue;
         const int ho = kvh * hg + qo % hg;
-        bf16_t *orow = (bf16_t *)a.out + ((row0 + ro) * a.Hq + ho) * kDim;
+        bf16_t *orow = (bf16_t *)a.out + ((row0 + ro) * a.Hq + ho) * DIM;
         const float inv = lq > 0.0f ? 1.0f / lq : 0.0f;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) orow[16 * nt + m16] = f32_to_bf16(st.o[nt][j] * inv);
+        for (int nt = 0; nt < G::kNt; ++nt) orow[16 * nt + m16] = f32_to_bf16(st.o[nt][j] * inv);
     }
     if (a.lse && g == 0 && q_valid)
         a.lse[(row0 + r_local) * a.Hq + head] = ltot > 0.0f ? (st.m + __log2f(ltot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
-// Decode: grid (splits, batch * Hkv).  q_per_sel * hg <= 64.  Split i < nsplit-1
-// takes kept blocks [16i, 16i + 16); the last split takes the tails.
+// Decode: grid (splits, batch * Hkv).  q_per_sel * hg <= 64, q_per_sel <= 32.
+// Split i < nsplit-1 takes kept blocks [16i, 16i + 16); the last split takes
+// the tails.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attn_decode_mfma_kernel(AttnArgs a)
+template <int DIM>
+__global__ __launch_bounds__(256, 2) void attn_decode_mfma_kernel(AttnArgs a)
 {
-    __shared__ ChunkSmem cs;
+    using G = Geo<DIM>;
+    __shared__ ChunkSmem<DIM> cs;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m16 = lane & 15, g = lane >> 4;
     const int hg = a.Hq / a.Hkv;
@@ -504,33 +552,35 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(AttnArgs a)
     const bool q_valid = qi < nq;
     const int head = kvh * hg + qi % hg;
     const int64_t qrow = (s * a.q_per_sel + (q_valid ? jrow : 0)) * a.Hq + head;
-    bf16x8_t qb[4];
-    load_query((const bf16_t *)a.q + qrow * kDim, q_valid, qb);
-    WaveState st;
+    bf16x8_t qb[G::kKs];
+    load_query<DIM>((const bf16_t *)a.q + qrow * DIM, q_valid, qb);
+    WaveState<DIM> st;
     init_state(st);
     const float scale2 = a.scale * kLog2e;
     const uint32_t qbit = q_valid ? (1u << jrow) : 0u;
-    const int64_t row_stride = (int64_t)a.Hkv * kDim;
+    const int64_t row_stride = (int64_t)a.Hkv * DIM;
     const int64_t seq_off = a.page_table ? 0 : s * a.kv_seq_stride;
-    const bf16_t *kbase = (const bf16_t *)a.k_cache + seq_off + (int64_t)kvh * kDim;
-    const bf16_t *vbase = (const bf16_t *)a.v_cache + seq_off + (int64_t)kvh * kDim;
+    const bf16_t *kbase = (const bf16_t *)a.k_cache + seq_off + (int64_t)kvh * DIM;
+    const bf16_t *vbase = (const bf16_t *)a.v_cache + seq_off + (int64_t)kvh * DIM;
     const int32_t count = min(a.sel_count[s], a.top_k);
     const uint32_t all_rows = a.q_per_sel >= 32 ? 0xffffffffu : ((1u << a.q_per_sel) - 1u);
     if (split < a.nsplit - 1) {
-        const int32_t b0 = split * (kCh / kBlock);
-        const int nb = max(0, min(kCh / kBlock, count - b0));
-        if (nb > 0) {
-            if (t < kCh) {
+        const int32_t b0 = split * kSplitBlocks;
+        const int nb = max(0, min(kSplitBlocks, count - b0));
+        for (int c0 = 0; c0 < nb; c0 += G::kChB) {
+            const int cb = min(G::kChB, nb - c0);
+            if (t < G::kCh) {
                 const int bi = t / kBlock;
-                cs.pos[t] = bi < nb ? (int32_t)kv_slot(a, s, (int64_t)a.sel_blocks[s * a.top_k + b0 + bi] * kBlock +
-                                                           (t % kBlock))
+                cs.pos[t] = bi < cb ? (int32_t)kv_slot(a, s, (int64_t)a.sel_blocks[s * a.top_k + b0 + c0 + bi] *
+                                                                 kBlock + (t % kBlock))
                                     : 0;
-                cs.pmask[t] = bi < nb ? all_rows : 0u;
+                cs.pmask[t] = bi < cb ? all_rows : 0u;
             }
             __syncthreads();
-            gather_chunk(cs, kbase, vbase, row_stride, nb * kBlock);
+            gather_chunk<DIM>(cs, kbase, vbase, row_stride, cb * kBlock);
             __syncthreads();
-            wave_chunk(cs, qb, qbit, scale2, st);
+            wave_chunk<DIM>(cs, qb, qbit, scale2, st);
+            __syncthreads();
         }
     } else {
         // tails: row j attends [ts_j, t_j]; walk [min ts, max t] in chunks
@@ -541,9 +591,9 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(AttnArgs a)
             lo = min(lo, ts);
             hi = max(hi, tj);
         }
-        for (int64_t p0 = lo; p0 <= hi; p0 += kCh) {
-            const int n = (int)min((int64_t)kCh, (int64_t)hi - p0 + 1);
-            if (t < kCh) {
+        for (int64_t p0 = lo; p0 <= hi; p0 += G::kCh) {
+            const int n = (int)min((int64_t)G::kCh, (int64_t)hi - p0 + 1);
+            if (t < G::kCh) {
                 const int64_t p = p0 + t;
                 uint32_t msk = 0;
                 if (t < n) {
@@ -557,9 +607,9 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(AttnArgs a)
                 cs.pmask[t] = msk;
             }
             __syncthreads();
-            gather_chunk(cs, kbase, vbase, row_stride, n);
+            gather_chunk<DIM>(cs, kbase, vbase, row_stride, n);
             __syncthreads();
-            wave_chunk(cs, qb, qbit, scale2, st);
+            wave_chunk<DIM>(cs, qb, qbit, scale2, st);
             __syncthreads();
         }
     }
@@ -570,31 +620,32 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(AttnArgs a)
         const int qo = 16 * wave + 4 * g + j;
         if (qo >= nq) continue;
         const int jo = qo / hg, ho = kvh * hg + qo % hg;
-        float *pp = a.partial + (((s * a.q_per_sel + jo) * a.Hq + ho) * a.nsplit + split) * (kDim + 2);
+        float *pp = a.partial + (((s * a.q_per_sel + jo) * a.Hq + ho) * a.nsplit + split) * (DIM + 2);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) pp[16 * nt + m16] = st.o[nt][j];
+        for (int nt = 0; nt < G::kNt; ++nt) pp[16 * nt + m16] = st.o[nt][j];
     }
     if (q_valid && g == 0) {
-        float *pp = a.partial + (qrow * a.nsplit + split) * (kDim + 2);
-        pp[kDim] = st.m * kLn2;  // natural-log units for the combine
-        pp[kDim + 1] = ltot;
+        float *pp = a.partial + (qrow * a.nsplit + split) * (DIM + 2);
+        pp[DIM] = st.m * kLn2;  // natural-log units for the combine
+        pp[DIM + 1] = ltot;
     }
 }
 
 int32_t attn_prefill_rows_per_tile(int32_t hg, int32_t top_k)
 {
     int32_t r = max(1, 64 / hg);
-    r = min(r, kMaxTileRows);                  // also: every row's 0..3 tail tokens fit one chunk
+    r = min(r, kMaxTileRows);                  // row masks are 16 bits
     r = min(r, kMaxUnionBlocks / top_k);       // the union of the rows' selections fits LDS
     return max(r, 1);
 }
 
-bool attn_mfma_supported(int32_t Hq, int32_t Hkv, int32_t q_per_sel, bool bf16)
+bool attn_mfma_supported(int32_t Hq, int32_t Hkv, int32_t q_per_sel, int32_t D, bool bf16)
 {
+    if (!bf16 || (D != 128 && D != 256) || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return false;
     const int32_t hg = Hq / Hkv;
-    return bf16 && (hg == 1 || hg == 2 || hg == 4 || hg == 8 || hg == 16 || hg == 32 || hg == 64) &&
-           (int64_t)q_per_sel * hg <= 64 &&
-           (int64_t)Hkv * kDim * kBlock <= (int64_t)UINT32_MAX;  // a block's K/V span as a 32-bit element count
+    return hg <= 64 && (int64_t)q_per_sel * hg <= 64 &&
+           q_per_sel <= 32 &&                            // decode row masks are 32 bits
+           (int64_t)Hkv * D * kBlock <= (int64_t)UINT32_MAX;  // a block's K/V span as a 32-bit element count
 }
 
 void launch_attn_prefill_mfma(const AttnArgs &a, hipStream_t stream)
@@ -602,13 +653,19 @@ void launch_attn_prefill_mfma(const AttnArgs &a, hipStream_t stream)
     const int32_t hg = a.Hq / a.Hkv;
     const int32_t rpt = attn_prefill_rows_per_tile(hg, a.top_k);
     const dim3 grid((unsigned)((a.n_sel + rpt - 1) / rpt), (unsigned)a.Hkv), block(256);
-    QSA_LAUNCH("attn_prefill_mfma", attn_prefill_mfma_kernel, grid, block, 0, stream, a, rpt);
+    if (a.D == 256)
+        QSA_LAUNCH("attn_prefill_mfma_d256", attn_prefill_mfma_kernel<256>, grid, block, 0, stream, a, rpt);
+    else
+        QSA_LAUNCH("attn_prefill_mfma", attn_prefill_mfma_kernel<128>, grid, block, 0, stream, a, rpt);
 }
 
 void launch_attn_decode_mfma(const AttnArgs &a, hipStream_t stream)
 {
     const dim3 grid((unsigned)a.nsplit, (unsigned)((int64_t)a.n_sel * a.Hkv)), block(256);
-    QSA_LAUNCH("attn_decode_mfma", attn_decode_mfma_kernel, grid, block, 0, stream, a);
+    if (a.D == 256)
+        QSA_LAUNCH("attn_decode_mfma_d256", attn_decode_mfma_kernel<256>, grid, block, 0, stream, a);
+    else
+        QSA_LAUNCH("attn_decode_mfma", attn_decode_mfma_kernel<128>, grid, block, 0, stream, a);
 }
 
 }  // namespace qsa

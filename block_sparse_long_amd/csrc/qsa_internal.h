@@ -10,6 +10,7 @@
 namespace qsa {
 
 constexpr int kDim = 128;       // indexer key / query dim, attention head dim
+constexpr int kDimWide = 256;   // the wider attention head dim (bf16 MFMA path)
 constexpr int kHalf = 64;       // rotate-half pairs (j, j + 64)
 constexpr int kIdxHeads = 4;    // indexer query heads
 constexpr int kBlock = 4;       // tokens per micro-block
@@ -129,6 +130,7 @@ struct AttnArgs {
     int32_t n_sel;            // prefill: rows; decode: batch
     int32_t q_per_sel;        // prefill 1; decode Qn
     int32_t Hq, Hkv;
+    int32_t D;                // head dim: 128 (every path) or 256 (bf16 MFMA path)
     float scale;
     void *out;
     float *lse;
@@ -146,8 +148,8 @@ void launch_attn_prefill(const AttnArgs &a, bool bf16, hipStream_t stream);
 void launch_attn_decode(const AttnArgs &a, bool bf16, hipStream_t stream);
 void launch_attn_combine(const AttnArgs &a, bool bf16, hipStream_t stream);
 
-// ---- attn_mfma.hip (bf16, Hq/Hkv a power of two up to 64) ---------------------
-bool attn_mfma_supported(int32_t Hq, int32_t Hkv, int32_t q_per_sel, bool bf16);
+// ---- attn_mfma.hip (bf16, D 128 or 256, Hq/Hkv up to 64) ----------------------
+bool attn_mfma_supported(int32_t Hq, int32_t Hkv, int32_t q_per_sel, int32_t D, bool bf16);
 int32_t attn_prefill_rows_per_tile(int32_t hg, int32_t top_k);
 void launch_attn_prefill_mfma(const AttnArgs &a, hipStream_t stream);
 void launch_attn_decode_mfma(const AttnArgs &a, hipStream_t stream);

@@ -189,7 +189,9 @@ def test_attn_validation(libqsa):
         a[i] = v
         return fp(*a)
 
-    assert fp(*args[:12], 64, *args[13:]) == qsa.ERR_UNSUPPORTED       # D != 128
+    assert fp(*args[:12], 64, *args[13:]) == qsa.ERR_UNSUPPORTED       # D is 128 or 256
+    assert fp(*args[:12], 192, *args[13:]) == qsa.ERR_UNSUPPORTED
+    assert fp(*args[:12], 256, *args[13:14], qsa.F32, *args[15:]) == qsa.ERR_UNSUPPORTED  # D = 256: bf16 only
     assert call(11, 3) == qsa.ERR_INVALID_ARG                          # Hq % Hkv
     assert call(10, 128) == qsa.ERR_UNSUPPORTED                        # group of 128 heads
     assert call(9, 0) == qsa.ERR_INVALID_ARG                           # top_k
@@ -212,6 +214,14 @@ def test_attn_validation(libqsa):
     assert dcall(3, 9) == qsa.ERR_UNSUPPORTED                          # 9 rows x 8 heads > 64
     assert dcall(3, 0) == qsa.ERR_INVALID_ARG
     assert dcall(2, 0) == qsa.OK
+    ws256 = qsa.sparse_attn_decode_workspace_size(4, 4, 24, 256, 512)
+    assert ws256 == 4 * 4 * 24 * (4 * 512 // 64 + 1) * 258 * 4
+    assert qsa.sparse_attn_decode_workspace_size(4, 4, 8, 192, 512) == 0
+    d256 = list(d)
+    d256[11], d256[12], d256[13], d256[19] = 24, 2, 256, ws256
+    assert fd(*d256[:15], qsa.F32, *d256[16:]) == qsa.ERR_UNSUPPORTED    # D = 256: bf16 only
+    assert fd(*d256[:3], 33, *d256[4:11], 2, 2, *d256[13:]) == qsa.ERR_UNSUPPORTED  # 33 rows > 32 masks
+    assert fd(*d256[:19], ws256 - 1, *d256[20:]) == qsa.ERR_WORKSPACE
     assert dcall(18, 0x100004) == qsa.ERR_INVALID_ARG
     assert dcall(1, None) == qsa.ERR_INVALID_ARG
 

@@ -437,11 +437,11 @@ def _sdpa_dense_causal(q, k, v, scale):
     return o.permute(1, 0, 2).numpy(), lse.permute(1, 0).numpy()
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (4, 2), (6, 3)])
-def test_topk_at_least_visible_equals_dense_causal(Hq, Hkv):
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 1, 32), (4, 2, 32), (6, 3, 32), (24, 2, 256)])
+def test_topk_at_least_visible_equals_dense_causal(Hq, Hkv, D):
     # every row keeps all its visible blocks (top_k >= nc) -> QSA == dense causal attention
     rng = np.random.default_rng(20 + Hq + Hkv)
-    L, D, k = 70, 32, 32
+    L, k = 70, 32
     pooled = rng.standard_normal((1, L // 4, DIM)).astype(np.float32)
     iq = rng.standard_normal((L, IH, DIM)).astype(np.float32)
     pos = np.arange(L, dtype=np.int32)
