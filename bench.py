@@ -60,6 +60,8 @@ def log(msg):
 
 def to_dev(a):
     import torch
+    if isinstance(a, torch.Tensor):   # drawn on the device already
+        return a
     a = np.ascontiguousarray(a)
     t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)
     return t.cuda()
@@ -91,8 +93,9 @@ def prefill_work(spec, row_pos):
         "score_gemm_bf16": ("mfma", 2.0 * 4 * DIM * pairs, "flop"),
         "score_rows_bf16": ("hbm", float(pairs) * DIM * eb, "B"),
         "select_rows": ("hbm", 4.0 * pairs, "B"),   # scans the fp32 scores once
-        "attn_prefill": ("alu", 4.0 * spec.Hq * DIM * float(npos.sum()), "flop"),
-        "attn_prefill_mfma": ("mfma", 4.0 * spec.Hq * DIM * float(npos.sum()), "flop"),
+        "attn_prefill": ("alu", 4.0 * spec.Hq * spec.D * float(npos.sum()), "flop"),
+        "attn_prefill_mfma": ("mfma", 4.0 * spec.Hq * spec.D * float(npos.sum()), "flop"),
+        "attn_prefill_mfma_d256": ("mfma", 4.0 * spec.Hq * spec.D * float(npos.sum()), "flop"),
         "score_filter": ("mfma", 2.0 * 4 * DIM * pairs, "flop"),
         "score_filter_fp8": ("mfma", 2.0 * 4 * DIM * pairs, "flop"),
         "pool_rope_fp8": ("hbm", new_blocks * (4 * DIM * eb + DIM + 4), "B"),
@@ -109,8 +112,8 @@ def decode_work(spec, anchor_pos, attn_pos, tail_start):
         P = 4 * min(int(nc[s]), spec.top_k)
         ts = int(tail_start[s]) if tail_start is not None else 4 * int(visible(attn_pos[s]).min())
         P += max(int(np.max(attn_pos[s])) - ts + 1, 0)
-        kv_bytes += 2.0 * P * spec.Hkv * DIM * eb
-    q_bytes = 2.0 * spec.batch * spec.q_per_seq * spec.Hq * DIM * eb
+        kv_bytes += 2.0 * P * spec.Hkv * spec.D * eb
+    q_bytes = 2.0 * spec.batch * spec.q_per_seq * spec.Hq * spec.D * eb
     kind = "score_rows_bf16" if spec.dtype == "bf16" else "score_rows_f32"
     return {
         kind: ("hbm", float(pairs) * DIM * eb, "B"),
@@ -120,6 +123,7 @@ def decode_work(spec, anchor_pos, attn_pos, tail_start):
         "select_final": ("hbm", 8.0 * spec.batch * spec.top_k, "B"),
         "attn_decode": ("hbm", kv_bytes + q_bytes, "B"),
         "attn_decode_mfma": ("hbm", kv_bytes + q_bytes, "B"),
+        "attn_decode_mfma_d256": ("hbm", kv_bytes + q_bytes, "B"),
     }, pairs
 
 
@@ -173,7 +177,8 @@ def timed(run_step, steps, warmup):
 ALL_KERNELS = ["pool_rope", "pool_rope_fp8", "pool_append", "rope_query", "score_rows_bf16", "score_rows_f32",
                "score_rows_fp8", "score_gemm_bf16", "select_rows", "select_collect", "select_final", "score_sample",
                "score_sample_fp8", "sample_threshold", "score_filter", "score_filter_fp8", "select_merge",
-               "attn_prefill_mfma", "attn_decode_mfma", "attn_prefill", "attn_decode", "attn_combine"]
+               "attn_prefill_mfma", "attn_decode_mfma", "attn_prefill_mfma_d256", "attn_decode_mfma_d256",
+               "attn_prefill", "attn_decode", "attn_combine"]
 
 
 # ---------------------------------------------------------------------------
@@ -320,7 +325,7 @@ def bench_decode(spec, steps, warmup, cpu_baseline, copies=3, keys="bf16", w=Non
     cnt = torch.empty((B,), dtype=torch.int32, device="cuda")
     ws = torch.empty((max(qsa.score_topk_workspace_size(B, max_nb, k, dcode), 256),), dtype=torch.uint8,
                      device="cuda")
-    wsa = torch.empty((max(qsa.sparse_attn_decode_workspace_size(B, spec.q_per_seq, spec.Hq, DIM, k), 256),),
+    wsa = torch.empty((max(qsa.sparse_attn_decode_workspace_size(B, spec.q_per_seq, spec.Hq, spec.D, k), 256),),
                       dtype=torch.uint8, device="cuda")
     out = torch.empty_like(q)
     lse = torch.empty((B, spec.q_per_seq, spec.Hq), dtype=torch.float32, device="cuda")
@@ -353,6 +358,25 @@ def bench_decode(spec, steps, warmup, cpu_baseline, copies=3, keys="bf16", w=Non
         res["cpu_baseline"] = cpu_decode(spec, w, pooled_h)
     res["_inputs"] = w
     return res
+
+
+def serving_shape_inputs(spec, w, Hq=24, Hkv=2, D=256, seed=2024):
+    """The workload's index inputs with attention at the serving head layout
+    (24 query heads over 2 KV heads, head dim 256): q, K and V are drawn
+    N(0,1) in bf16 on the device from a seeded generator (a host draw of the
+    1M-token caches would take minutes); the index side is unchanged."""
+    import dataclasses
+    import torch
+    s2 = dataclasses.replace(spec, Hq=Hq, Hkv=Hkv, D=D)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    w2 = dict(w)
+    B, L = spec.batch, spec.kv_len
+    qshape = (B, spec.q_per_seq, Hq, D) if spec.kind == "decode" else (spec.chunk, Hq, D)
+    w2["q"] = torch.randn(qshape, generator=g, device="cuda", dtype=torch.bfloat16)
+    w2["k_cache"] = torch.randn((B, L, Hkv, D), generator=g, device="cuda", dtype=torch.bfloat16)
+    w2["v_cache"] = torch.randn((B, L, Hkv, D), generator=g, device="cuda", dtype=torch.bfloat16)
+    return s2, w2
 
 
 def bench_pool_append(spec, launches=50):
@@ -417,7 +441,8 @@ KERNEL_SOURCE = {"pool_rope": "pool.hip", "pool_append": "pool.hip", "rope_query
                  "select_collect": "select.hip", "select_final": "select.hip", "score_sample": "score_fused.hip",
                  "sample_threshold": "score_fused.hip", "score_filter": "score_fused.hip",
                  "select_merge": "score_fused.hip", "attn_prefill_mfma": "attn_mfma.hip",
-                 "attn_decode_mfma": "attn_mfma.hip", "attn_prefill": "attn.hip", "attn_decode": "attn.hip",
+                 "attn_decode_mfma": "attn_mfma.hip", "attn_prefill_mfma_d256": "attn_mfma.hip",
+                 "attn_decode_mfma_d256": "attn_mfma.hip", "attn_prefill": "attn.hip", "attn_decode": "attn.hip",
                  "attn_combine": "attn.hip", "pool_rope_fp8": "pool.hip", "score_rows_fp8": "score.hip",
                  "score_sample_fp8": "score_fused.hip", "score_filter_fp8": "score_fused.hip"}
 COPY_BYTES = 1 << 30
@@ -559,6 +584,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", dest="fp8", action="store_false",
                     help="skip the extra runs with FP8 index keys")
+    ap.add_argument("--no-serving-shape", dest="serving", action="store_false",
+                    help="skip the extra runs with attention at 24 q / 2 KV heads, head dim 256")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a copy of known size first (for scaling memory counters)")
     ap.add_argument("--rocprof-summary", nargs="+", metavar="DIR")
@@ -590,7 +617,14 @@ def main():
         pre = bench_decode(spec, args.steps * 10, args.warmup, cpu)
         value, unit, ms = pre["value"], pre["unit"], pre["ms_per_step"]
         main_res = pre
-    fp8_res = {}
+    fp8_res, serve_res = {}, {}
+    if args.serving and spec.dtype == "bf16":
+        s2, w2 = serving_shape_inputs(spec, pre["_inputs"])
+        if spec.kind == "prefill":
+            serve_res[spec.name] = bench_prefill(s2, args.steps, args.warmup, False, w=w2)
+        else:
+            serve_res[spec.name] = bench_decode(s2, args.steps * 10, args.warmup, False, w=w2)
+        del w2
     if args.fp8 and spec.dtype == "bf16":
         if spec.kind == "prefill":
             fp8_res[spec.name] = bench_prefill(spec, args.steps, args.warmup, False, keys="fp8", w=pre["_inputs"])
@@ -615,6 +649,10 @@ def main():
         if args.fp8 and dspec.dtype == "bf16":
             fp8_res[dspec.name] = bench_decode(dspec, args.steps * 10, args.warmup, False, keys="fp8",
                                                w=dec["_inputs"])
+        if args.serving and dspec.dtype == "bf16":
+            s2, w2 = serving_shape_inputs(dspec, dec["_inputs"])
+            serve_res[dspec.name] = bench_decode(s2, args.steps * 10, args.warmup, False, w=w2)
+            del w2
         dec.pop("_inputs", None)
         line["decode"] = {k: v for k, v in dec.items()}
         line["decode"]["config"] = {"context": dspec.ctx, "batch": dspec.batch, "q_per_seq": dspec.q_per_seq,
@@ -630,6 +668,17 @@ def main():
                                       "unit": "tokens/s" if "workload" not in r else r["unit"],
                                       "ms_per_step": round(r["ms_per_step"], 4), "kernels": r["kernels"],
                                       "roofline": r["roofline"]}
+    if serve_res:
+        # the same workloads with attention at the serving head layout (24
+        # query heads, 2 KV heads, head dim 256); index side unchanged
+        line["serving_shape"] = {}
+        for name, r in serve_res.items():
+            r.pop("_inputs", None)
+            line["serving_shape"][name] = {"Hq": 24, "Hkv": 2, "head_dim": 256, "value": round(r["value"], 1),
+                                           "unit": "tokens/s" if "workload" not in r else r["unit"],
+                                           "ms_per_step": round(r["ms_per_step"], 4), "kernels": r["kernels"],
+                                           "rooflines": {n: v for n, v in r["rooflines"].items()
+                                                         if n.startswith("attn")}}
     print(json.dumps(line), flush=True)
 
 

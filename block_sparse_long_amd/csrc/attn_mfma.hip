@@ -535,8 +535,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
 // Split i < nsplit-1 takes kept blocks [16i, 16i + 16); the last split takes
 // the tails.
 // ---------------------------------------------------------------------------
-template <int DIM>
-__global__ __launch_bounds__(256, 2) void attn_decode_mfma_kernel(AttnArgs a)
+template <int DIM>  // D = 256 needs the two-wave register budget to avoid spilling
+__global__ __launch_bounds__(256, DIM == 256 ? 2 : 1) void attn_decode_mfma_kernel(AttnArgs a)
 {
     using G = Geo<DIM>;
     __shared__ ChunkSmem<DIM> cs;
