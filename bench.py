@@ -354,6 +354,9 @@ def bench_decode(spec, steps, warmup, cpu_baseline, copies=3, keys="bf16", w=Non
            "rooflines": {n: roofline_for(n, work[n], kt[n][1], tr) for n in kt if n in work}}
     if not fp8:
         res["pool_append"] = bench_pool_append(spec)
+    if not fp8 and spec.draft:
+        res["draft_loop"] = bench_draft_loop(spec, iq, seq, apos, pooled, kcs, vcs, q, ts, max_nb, ws,
+                                             max(steps, 10), warmup)
     if cpu_baseline and not fp8:
         res["cpu_baseline"] = cpu_decode(spec, w, pooled_h)
     res["_inputs"] = w
@@ -377,6 +380,51 @@ def serving_shape_inputs(spec, w, Hq=24, Hkv=2, D=256, seed=2024):
     w2["k_cache"] = torch.randn((B, L, Hkv, D), generator=g, device="cuda", dtype=torch.bfloat16)
     w2["v_cache"] = torch.randn((B, L, Hkv, D), generator=g, device="cuda", dtype=torch.bfloat16)
     return s2, w2
+
+
+def bench_draft_loop(spec, iq, seq, apos, pooled, kcs, vcs, q, ts, max_nb, ws, steps, warmup):
+    """The IndexShare draft loop: the anchor selects once, then each of the N
+    draft steps attends with one row per sequence (position ctx + i) over the
+    shared selection plus the positions drafted since, and appends the
+    drafted token's raw index key to the ring (completing a block at the last
+    step).  One loop = 1 selection + N one-row attention calls + N appends;
+    rows/s counts the N x batch draft rows."""
+    import torch
+    from block_sparse_long_amd import qsa
+    B, N, L, k = spec.batch, spec.q_per_seq, spec.ctx, spec.top_k
+    copies = len(pooled)
+    qs = [q[:, i:i + 1].contiguous() for i in range(N)]
+    ps = [torch.full((B, 1), L + i, dtype=torch.int32, device="cuda") for i in range(N)]
+    outs = [torch.empty_like(x) for x in qs]
+    lses = [torch.empty((B, 1, spec.Hq), dtype=torch.float32, device="cuda") for _ in range(N)]
+    wsa = torch.empty((max(qsa.sparse_attn_decode_workspace_size(B, 1, spec.Hq, spec.D, k), 256),),
+                      dtype=torch.uint8, device="cuda")
+    sel = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B,), dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    keys = torch.randn((N, B, DIM), generator=g, device="cuda").to(pooled[0].dtype)
+    ring = torch.zeros((B, 4, DIM), dtype=pooled[0].dtype, device="cuda")
+    comp = torch.zeros((B * (N // 4 + 2), DIM), dtype=pooled[0].dtype, device="cuda")
+    tpos = [torch.full((B,), L + i, dtype=torch.int32, device="cuda") for i in range(N)]
+    slots = [torch.tensor([b * 4 * (N // 4 + 2) + L % 4 + i for b in range(B)], dtype=torch.int64, device="cuda")
+             for i in range(N)]
+
+    def loop(j):
+        c = j % copies
+        qsa.score_topk(iq, seq, apos, pooled[c], max_nb, k, spec.theta, sel_blocks=sel, sel_count=cnt,
+                       workspace=ws, want_scores=False)
+        for i in range(N):
+            qsa.sparse_attn_decode(qs[i], ps[i], kcs[c], vcs[c], sel, cnt, ts, out=outs[i], lse=lses[i],
+                                   workspace=wsa)
+            qsa.pool_append(keys[i], tpos[i], slots[i], ring, comp, spec.theta)
+
+    ms = timed(loop, steps, warmup)
+    kt = kernel_times(loop, 5, ALL_KERNELS)
+    log(f"{spec.name} draft loop ({N} steps): {ms:.3f} ms/loop")
+    return {"draft_steps": N, "ms_per_loop": round(ms, 4), "value": round(B * N / (ms * 1e-3), 1),
+            "unit": "draft rows/s",
+            "kernels": {n: {"launches_per_loop": c / 5, "avg_us": round(a * 1e3, 2)} for n, (c, a, _) in kt.items()}}
 
 
 def bench_pool_append(spec, launches=50):
@@ -679,6 +727,8 @@ def main():
                                            "ms_per_step": round(r["ms_per_step"], 4), "kernels": r["kernels"],
                                            "rooflines": {n: v for n, v in r["rooflines"].items()
                                                          if n.startswith("attn")}}
+            if "draft_loop" in r:
+                line["serving_shape"][name]["draft_loop"] = r["draft_loop"]
     print(json.dumps(line), flush=True)
 
 
