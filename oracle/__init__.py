@@ -78,6 +78,12 @@ def _load():
     lib.qsa_oracle_sparse_attn_decode.argtypes = [P, P, i32, i32, P, P, P, i64, P, P, i32, i32,
                                                   i32, i32, f64, i32, P, P]
     lib.qsa_oracle_sparse_attn_decode.restype = ctypes.c_int
+    lib.qsa_oracle_sparse_attn_prefill_fp8kv.argtypes = [P, P, P, i32, P, P, i64, f64, f64, P, P, i32, i32,
+                                                         i32, i32, f64, i32, P, P]
+    lib.qsa_oracle_sparse_attn_prefill_fp8kv.restype = ctypes.c_int
+    lib.qsa_oracle_sparse_attn_decode_fp8kv.argtypes = [P, P, i32, i32, P, P, P, i64, f64, f64, P, P, i32,
+                                                        i32, i32, i32, f64, i32, P, P]
+    lib.qsa_oracle_sparse_attn_decode_fp8kv.restype = ctypes.c_int
     lib.qsa_oracle_threads.argtypes = []
     lib.qsa_oracle_threads.restype = ctypes.c_int
     _lib = lib
@@ -301,4 +307,55 @@ def sparse_attn_decode(q, row_pos, k_cache, v_cache, sel, count, tail_start=None
         _ptr(q), _ptr(_c(row_pos, np.int32)), B, Qn, _ptr(ts), _ptr(k_cache), _ptr(v_cache),
         L * Hkv * D, _ptr(sel), _ptr(count), top_k, Hq, Hkv, D, scale, dt, _ptr(out), _ptr(lse))
     _check(rc, "sparse_attn_decode")
+    return out, lse
+
+
+def sparse_attn_prefill_fp8kv(q, row_seq, row_pos, k_codes, v_codes, k_scale, v_scale, sel, count,
+                              softmax_scale=None):
+    """a7+a8 on an FP8 K/V cache: k_codes / v_codes [B][L][Hkv][D] uint8 E4M3
+    codes whose values are k_scale * E4M3(code) and v_scale * E4M3(code).
+    q: [R][Hq][D] (bf16 bits or float32).  Returns (out like q, lse)."""
+    q = _c(q)
+    k_codes = _c(k_codes, np.uint8)
+    v_codes = _c(v_codes, np.uint8)
+    dt = _dtype_code(q)
+    R, Hq, D = q.shape
+    B, L, Hkv, D2 = k_codes.shape
+    assert D2 == D and v_codes.shape == k_codes.shape
+    sel = _c(sel, np.int32)
+    count = _c(count, np.int32)
+    top_k = sel.shape[1]
+    scale = float(softmax_scale) if softmax_scale is not None else 1.0 / np.sqrt(D)
+    out = np.empty_like(q)
+    lse = np.empty((R, Hq), np.float32)
+    rc = _load().qsa_oracle_sparse_attn_prefill_fp8kv(
+        _ptr(q), _ptr(_c(row_seq, np.int32)), _ptr(_c(row_pos, np.int32)), R, _ptr(k_codes), _ptr(v_codes),
+        L * Hkv * D, float(k_scale), float(v_scale), _ptr(sel), _ptr(count), top_k, Hq, Hkv, D, scale, dt,
+        _ptr(out), _ptr(lse))
+    _check(rc, "sparse_attn_prefill_fp8kv")
+    return out, lse
+
+
+def sparse_attn_decode_fp8kv(q, row_pos, k_codes, v_codes, k_scale, v_scale, sel, count, tail_start=None,
+                             softmax_scale=None):
+    """a7+a9 on an FP8 K/V cache (as sparse_attn_prefill_fp8kv)."""
+    q = _c(q)
+    k_codes = _c(k_codes, np.uint8)
+    v_codes = _c(v_codes, np.uint8)
+    dt = _dtype_code(q)
+    B, Qn, Hq, D = q.shape
+    Bk, L, Hkv, D2 = k_codes.shape
+    assert D2 == D and Bk >= B and v_codes.shape == k_codes.shape
+    sel = _c(sel, np.int32)
+    count = _c(count, np.int32)
+    top_k = sel.shape[1]
+    scale = float(softmax_scale) if softmax_scale is not None else 1.0 / np.sqrt(D)
+    ts = None if tail_start is None else _c(tail_start, np.int32)
+    out = np.empty_like(q)
+    lse = np.empty((B, Qn, Hq), np.float32)
+    rc = _load().qsa_oracle_sparse_attn_decode_fp8kv(
+        _ptr(q), _ptr(_c(row_pos, np.int32)), B, Qn, _ptr(ts), _ptr(k_codes), _ptr(v_codes), L * Hkv * D,
+        float(k_scale), float(v_scale), _ptr(sel), _ptr(count), top_k, Hq, Hkv, D, scale, dt, _ptr(out),
+        _ptr(lse))
+    _check(rc, "sparse_attn_decode_fp8kv")
     return out, lse

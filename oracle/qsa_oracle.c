@@ -16,7 +16,8 @@
  *          the model", item 2 (RoPE after pooling, 512 blocks = 2,048 tokens
  *          plus the incomplete tail block).
  *   [LBL]  "Qwen3.8-Flash-Next, Layer by Layer", section "Token mixing"
- *          (4 query heads, 1 key head, 128 dims, mean of 4 keys, best 512).
+ *          (4 query heads, 1 key head, 128 dims, mean of 4 keys, best 512)
+ *          and section "Serving it" (indexer keys and the KV cache in FP8).
  *
  * Every floating-point step runs in double precision, except where the pages
  * fix the precision: the block mean is taken in FP32 ([SGL]) and the
@@ -563,13 +564,33 @@ static int64_t expand_positions(const int32_t *sel, int32_t count, int64_t tail_
 }
 
 /*
+ * A K or V cache: elements of the query's dtype, or FP8 codes.  Reading for
+ * the FP8 KV cache of [LBL] "Serving it" (the page names neither the variant
+ * nor the scaling): OCP E4M3 codes with one FP32 scale per cache tensor (one
+ * for K, one for V); an element's value is scale * E4M3(code), in double.
+ */
+enum { OR_KV_FP8 = 2 };
+typedef struct {
+    const void *ptr;
+    int dtype;       /* OR_F32, OR_BF16 or OR_KV_FP8 */
+    double scale;    /* OR_KV_FP8 only */
+} kv_src;
+
+static double load_kv(const kv_src *c, int64_t idx)
+{
+    if (c->dtype == OR_KV_FP8)
+        return c->scale * qsa_oracle_fp8_to_double(((const uint8_t *)c->ptr)[idx]);
+    return load_elem(c->ptr, idx, c->dtype);
+}
+
+/*
  * Softmax attention of one query head over the listed positions, on the
  * original K/V ([SGL]: "the compressed keys are only an index").  GQA reading:
  * query head h uses KV head floor(h / (Hq/Hkv)).  Max-subtracted softmax in
  * double; lse = max + log(sum exp).
  */
-static void attend_one_head(const void *qrow, int64_t qoff, const void *k_cache,
-                            const void *v_cache, int64_t kv_base, int32_t Hkv, int32_t g, int32_t D,
+static void attend_one_head(const void *qrow, int64_t qoff, const kv_src *k_cache,
+                            const kv_src *v_cache, int64_t kv_base, int32_t Hkv, int32_t g, int32_t D,
                             const int64_t *pos, int64_t n, double scale, int32_t dtype, void *out,
                             int64_t ooff, float *lse_out, double *logit)
 {
@@ -578,7 +599,7 @@ static void attend_one_head(const void *qrow, int64_t qoff, const void *k_cache,
         int64_t koff = kv_base + (pos[i] * Hkv + g) * D;
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
-            dot += load_elem(qrow, qoff + d, dtype) * load_elem(k_cache, koff + d, dtype);
+            dot += load_elem(qrow, qoff + d, dtype) * load_kv(k_cache, koff + d);
         logit[i] = scale * dot;
         if (logit[i] > mx)
             mx = logit[i];
@@ -592,7 +613,7 @@ static void attend_one_head(const void *qrow, int64_t qoff, const void *k_cache,
         double acc = 0.0;
         for (int64_t i = 0; i < n; ++i) {
             int64_t voff = kv_base + (pos[i] * Hkv + g) * D;
-            acc += logit[i] * load_elem(v_cache, voff + d, dtype);
+            acc += logit[i] * load_kv(v_cache, voff + d);
         }
         store_elem(out, ooff + d, dtype, acc / denom);
     }
@@ -608,15 +629,13 @@ static void attend_one_head(const void *qrow, int64_t qoff, const void *k_cache,
  * s, KV head g at s*kv_seq_stride + (p*Hkv + g)*D; out: [rows][Hq][D];
  * lse: [rows][Hq] or NULL.
  */
-int qsa_oracle_sparse_attn_prefill(const void *q, const int32_t *row_seq, const int32_t *row_pos,
-                                   int32_t rows, const void *k_cache, const void *v_cache,
-                                   int64_t kv_seq_stride, const int32_t *sel_blocks,
-                                   const int32_t *sel_count, int32_t top_k, int32_t Hq, int32_t Hkv,
-                                   int32_t D, double softmax_scale, int32_t dtype, void *out,
-                                   float *lse)
+static int attn_prefill(const void *q, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+                        const kv_src *k_cache, const kv_src *v_cache, int64_t kv_seq_stride,
+                        const int32_t *sel_blocks, const int32_t *sel_count, int32_t top_k, int32_t Hq,
+                        int32_t Hkv, int32_t D, double softmax_scale, int32_t dtype, void *out, float *lse)
 {
     if (rows < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || top_k < 1 || !q || !row_seq ||
-        !row_pos || !k_cache || !v_cache || !sel_blocks || !sel_count || !out)
+        !row_pos || !k_cache->ptr || !v_cache->ptr || !sel_blocks || !sel_count || !out)
         return OR_ERR_ARG;
     int failed = 0;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -646,6 +665,34 @@ int qsa_oracle_sparse_attn_prefill(const void *q, const int32_t *row_seq, const 
     return failed ? OR_ERR_ALLOC : OR_OK;
 }
 
+int qsa_oracle_sparse_attn_prefill(const void *q, const int32_t *row_seq, const int32_t *row_pos,
+                                   int32_t rows, const void *k_cache, const void *v_cache,
+                                   int64_t kv_seq_stride, const int32_t *sel_blocks,
+                                   const int32_t *sel_count, int32_t top_k, int32_t Hq, int32_t Hkv,
+                                   int32_t D, double softmax_scale, int32_t dtype, void *out,
+                                   float *lse)
+{
+    kv_src k = {k_cache, dtype, 1.0}, v = {v_cache, dtype, 1.0};
+    return attn_prefill(q, row_seq, row_pos, rows, &k, &v, kv_seq_stride, sel_blocks, sel_count, top_k, Hq,
+                        Hkv, D, softmax_scale, dtype, out, lse);
+}
+
+/*
+ * The same with an FP8 K/V cache: E4M3 codes, k_scale and v_scale (see
+ * kv_src); q, out in q_dtype.
+ */
+int qsa_oracle_sparse_attn_prefill_fp8kv(const void *q, const int32_t *row_seq, const int32_t *row_pos,
+                                         int32_t rows, const uint8_t *k_codes, const uint8_t *v_codes,
+                                         int64_t kv_seq_stride, double k_scale, double v_scale,
+                                         const int32_t *sel_blocks, const int32_t *sel_count, int32_t top_k,
+                                         int32_t Hq, int32_t Hkv, int32_t D, double softmax_scale,
+                                         int32_t q_dtype, void *out, float *lse)
+{
+    kv_src k = {k_codes, OR_KV_FP8, k_scale}, v = {v_codes, OR_KV_FP8, v_scale};
+    return attn_prefill(q, row_seq, row_pos, rows, &k, &v, kv_seq_stride, sel_blocks, sel_count, top_k, Hq,
+                        Hkv, D, softmax_scale, q_dtype, out, lse);
+}
+
 /*
  * a7+a9, decode: q_per_seq rows per sequence share that sequence's selection
  * sel_blocks[s] ([SGL] "IndexShare MTP").  Row j of sequence s sits at
@@ -654,15 +701,14 @@ int qsa_oracle_sparse_attn_prefill(const void *q, const int32_t *row_seq, const 
  * each row (a plain decode row).
  * q, out: [batch][q_per_seq][Hq][D]; lse: [batch][q_per_seq][Hq] or NULL.
  */
-int qsa_oracle_sparse_attn_decode(const void *q, const int32_t *row_pos, int32_t batch,
-                                  int32_t q_per_seq, const int32_t *tail_start,
-                                  const void *k_cache, const void *v_cache, int64_t kv_seq_stride,
-                                  const int32_t *sel_blocks, const int32_t *sel_count,
-                                  int32_t top_k, int32_t Hq, int32_t Hkv, int32_t D,
-                                  double softmax_scale, int32_t dtype, void *out, float *lse)
+static int attn_decode(const void *q, const int32_t *row_pos, int32_t batch, int32_t q_per_seq,
+                       const int32_t *tail_start, const kv_src *k_cache, const kv_src *v_cache,
+                       int64_t kv_seq_stride, const int32_t *sel_blocks, const int32_t *sel_count,
+                       int32_t top_k, int32_t Hq, int32_t Hkv, int32_t D, double softmax_scale, int32_t dtype,
+                       void *out, float *lse)
 {
     if (batch < 0 || q_per_seq < 1 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || top_k < 1 ||
-        !q || !row_pos || !k_cache || !v_cache || !sel_blocks || !sel_count || !out)
+        !q || !row_pos || !k_cache->ptr || !v_cache->ptr || !sel_blocks || !sel_count || !out)
         return OR_ERR_ARG;
     int64_t rows = (int64_t)batch * q_per_seq;
     int failed = 0;
@@ -693,6 +739,31 @@ int qsa_oracle_sparse_attn_decode(const void *q, const int32_t *row_pos, int32_t
         free(logit);
     }
     return failed ? OR_ERR_ALLOC : OR_OK;
+}
+
+int qsa_oracle_sparse_attn_decode(const void *q, const int32_t *row_pos, int32_t batch,
+                                  int32_t q_per_seq, const int32_t *tail_start,
+                                  const void *k_cache, const void *v_cache, int64_t kv_seq_stride,
+                                  const int32_t *sel_blocks, const int32_t *sel_count,
+                                  int32_t top_k, int32_t Hq, int32_t Hkv, int32_t D,
+                                  double softmax_scale, int32_t dtype, void *out, float *lse)
+{
+    kv_src k = {k_cache, dtype, 1.0}, v = {v_cache, dtype, 1.0};
+    return attn_decode(q, row_pos, batch, q_per_seq, tail_start, &k, &v, kv_seq_stride, sel_blocks, sel_count,
+                       top_k, Hq, Hkv, D, softmax_scale, dtype, out, lse);
+}
+
+/* The same with an FP8 K/V cache (see kv_src). */
+int qsa_oracle_sparse_attn_decode_fp8kv(const void *q, const int32_t *row_pos, int32_t batch,
+                                        int32_t q_per_seq, const int32_t *tail_start, const uint8_t *k_codes,
+                                        const uint8_t *v_codes, int64_t kv_seq_stride, double k_scale,
+                                        double v_scale, const int32_t *sel_blocks, const int32_t *sel_count,
+                                        int32_t top_k, int32_t Hq, int32_t Hkv, int32_t D,
+                                        double softmax_scale, int32_t q_dtype, void *out, float *lse)
+{
+    kv_src k = {k_codes, OR_KV_FP8, k_scale}, v = {v_codes, OR_KV_FP8, v_scale};
+    return attn_decode(q, row_pos, batch, q_per_seq, tail_start, &k, &v, kv_seq_stride, sel_blocks, sel_count,
+                       top_k, Hq, Hkv, D, softmax_scale, q_dtype, out, lse);
 }
 
 /* Threads the OpenMP loops above will use (reported by the CPU baseline). */

@@ -674,3 +674,84 @@ def test_score_fp8_equals_exact_keys_of_the_other_path():
     c = oracle.score_topk_fp8(q, seq, pos, codes, scales / np.float32(8), k, 1e7, oracle.FLAG_NO_ROPE, want_raw=True)
     np.testing.assert_array_equal(c[0], a[0])
     np.testing.assert_array_equal(c[3], a[3] / 8)
+
+
+# ---------------------------------------------------------------------------
+# FP8 K/V cache ("Qwen3.8-Flash-Next, Layer by Layer", "Serving it"): E4M3
+# codes with one scale for K and one for V; value = scale * E4M3(code)
+# ---------------------------------------------------------------------------
+
+def _fp8kv_case(seed, L=4 * 60 + 2, R=9, Hq=6, Hkv=2, D=32, k=16):
+    rng = np.random.default_rng(seed)
+    pos = np.sort(rng.choice(np.arange(4 * k, L), R, replace=False)).astype(np.int32)
+    pos[0] = 2                                                   # no complete block: the tail alone
+    sel = np.full((R, k), -1, np.int32)
+    cnt = np.zeros(R, np.int32)
+    for r, t in enumerate(pos):
+        n = min(k, (int(t) + 1) // 4)
+        sel[r, :n] = np.sort(rng.choice((int(t) + 1) // 4, n, replace=False))
+        cnt[r] = n
+    q = rng.standard_normal((R, Hq, D)).astype(np.float32)
+    kint = rng.integers(-8, 9, size=(1, L, Hkv, D)).astype(np.float32)   # exact E4M3 values
+    vint = rng.integers(-8, 9, size=(1, L, Hkv, D)).astype(np.float32)
+    return q, np.zeros(R, np.int32), pos, kint, vint, sel, cnt
+
+
+def test_fp8kv_attention_equals_plain_attention_on_exact_values():
+    # integer codes times a power-of-two scale are exact fp32 values: the FP8
+    # cache and the fp32 cache of the same values give the same result
+    q, seq, pos, kint, vint, sel, cnt = _fp8kv_case(90)
+    kc, vc = oracle.fp8_from_float(kint), oracle.fp8_from_float(vint)
+    np.testing.assert_array_equal(oracle.fp8_to_float(kc), kint)
+    out, lse = oracle.sparse_attn_prefill_fp8kv(q, seq, pos, kc, vc, 0.25, 0.5, sel, cnt)
+    want, want_lse = oracle.sparse_attn_prefill(q, seq, pos, kint * 0.25, vint * 0.5, sel, cnt)
+    np.testing.assert_array_equal(out, want)
+    np.testing.assert_array_equal(lse, want_lse)
+    qd = q.reshape(3, 3, 6, 32)
+    rp = np.array([[200, 201, 202]] * 3, np.int32)
+    ts = np.array([200, 200, 200], np.int32)
+    out, lse = oracle.sparse_attn_decode_fp8kv(qd, rp, np.repeat(kc, 3, 0), np.repeat(vc, 3, 0), 0.25, 0.5,
+                                               sel[:3], cnt[:3], ts)
+    want, want_lse = oracle.sparse_attn_decode(qd, rp, np.repeat(kint, 3, 0) * 0.25, np.repeat(vint, 3, 0) * 0.5,
+                                               sel[:3], cnt[:3], ts)
+    np.testing.assert_array_equal(out, want)
+    np.testing.assert_array_equal(lse, want_lse)
+
+
+def test_fp8kv_scales_act_as_logit_and_output_factors():
+    rng = np.random.default_rng(91)
+    q, seq, pos, _, _, sel, cnt = _fp8kv_case(91)
+    L, Hkv, D = 4 * 60 + 2, 2, 32
+    kc = rng.integers(0, 256, size=(1, L, Hkv, D)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(1, L, Hkv, D)).astype(np.uint8)
+    kc[(kc & 0x7f) == 0x7f] = 0x38                               # no NaN codes
+    vc[(vc & 0x7f) == 0x7f] = 0x38
+    ks, vs, sm = 0.0137, 0.0211, 1 / math.sqrt(D)
+    out, lse = oracle.sparse_attn_prefill_fp8kv(q, seq, pos, kc, vc, ks, vs, sel, cnt, sm)
+    # k_scale multiplies every logit: the same as scaling the softmax scale
+    out2, lse2 = oracle.sparse_attn_prefill_fp8kv(q, seq, pos, kc, vc, ks * 3.0, vs, sel, cnt, sm / 3.0)
+    np.testing.assert_allclose(out2, out, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-6, atol=1e-7)
+    # v_scale multiplies the output and leaves lse alone
+    out3, lse3 = oracle.sparse_attn_prefill_fp8kv(q, seq, pos, kc, vc, ks, vs * 5.0, sel, cnt, sm)
+    np.testing.assert_allclose(out3, out * 5.0, rtol=1e-6, atol=1e-7)
+    np.testing.assert_array_equal(lse3, lse)
+
+
+def test_fp8kv_zero_query_averages_the_decoded_values():
+    # q = 0: uniform weights over the attended positions, whose values are
+    # v_scale * E4M3(code); lse = log(number of positions)
+    q, seq, pos, kint, vint, sel, cnt = _fp8kv_case(92)
+    rng = np.random.default_rng(93)
+    vc = rng.integers(0, 256, size=vint.shape).astype(np.uint8)
+    vc[(vc & 0x7f) == 0x7f] = 0x40
+    vs = 0.037
+    out, lse = oracle.sparse_attn_prefill_fp8kv(np.zeros_like(q), seq, pos, oracle.fp8_from_float(kint), vc, 0.5,
+                                                vs, sel, cnt)
+    vals = oracle.fp8_to_float(vc).astype(np.float64) * vs
+    for r, t in enumerate(pos):
+        P = [4 * b + i for b in sel[r, :cnt[r]] for i in range(4)] + list(range(4 * ((t + 1) // 4), t + 1))
+        for h in range(q.shape[1]):
+            g = h // (q.shape[1] // vint.shape[2])
+            np.testing.assert_allclose(out[r, h], vals[0, P, g].mean(0), rtol=1e-6, atol=1e-7)
+            assert lse[r, h] == pytest.approx(math.log(len(P)), rel=1e-6)
