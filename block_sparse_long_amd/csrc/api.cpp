@@ -405,7 +405,8 @@ extern "C" {
 
 static qsa_status_t check_attn_common(const void *q, const void *k_cache, const void *v_cache, int64_t kv_seq_stride,
                                       const int32_t *sel_blocks, const int32_t *sel_count, int32_t top_k, int32_t Hq,
-                                      int32_t Hkv, int32_t D, float softmax_scale, qsa_dtype_t dtype, const void *out)
+                                      int32_t Hkv, int32_t D, float softmax_scale, qsa_dtype_t dtype, const void *out,
+                                      bool kv_fp8 = false)
 {
     if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return QSA_ERR_INVALID_ARG;
@@ -413,8 +414,14 @@ static qsa_status_t check_attn_common(const void *q, const void *k_cache, const 
     if (!std::isfinite(softmax_scale)) return QSA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !sel_blocks || !sel_count || !out)
         return QSA_ERR_INVALID_ARG;
-    if (kv_seq_stride < 0 || kv_seq_stride % 8) return QSA_ERR_INVALID_ARG;
+    if (kv_seq_stride < 0 || kv_seq_stride % (kv_fp8 ? 16 : 8)) return QSA_ERR_INVALID_ARG;  // 16-byte rows
     return QSA_OK;
+}
+
+// FP8 K/V: the two per-tensor scales must be positive and finite.
+static bool kv_scales_ok(float k_scale, float v_scale)
+{
+    return std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.0f && v_scale > 0.0f;
 }
 
 static qsa_status_t attn_prefill_impl(const void *q, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
@@ -422,7 +429,8 @@ static qsa_status_t attn_prefill_impl(const void *q, const int32_t *row_seq, con
                                      const int32_t *page_table, int64_t pt_stride, int32_t page_tokens,
                                      const int32_t *sel_blocks, const int32_t *sel_count, int32_t top_k, int32_t Hq,
                                      int32_t Hkv, int32_t D, float softmax_scale, qsa_dtype_t dtype, void *out,
-                                     float *lse, void *stream)
+                                     float *lse, void *stream, bool kv_fp8 = false, float k_scale = 1.0f,
+                                     float v_scale = 1.0f)
 {
     if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
     if (rows < 0) return QSA_ERR_INVALID_ARG;
@@ -430,12 +438,14 @@ static qsa_status_t attn_prefill_impl(const void *q, const int32_t *row_seq, con
     if (Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && Hq / Hkv > QSA_MAX_QUERY_GROUP) return QSA_ERR_UNSUPPORTED;
     const bool mfma = attn_mfma_supported(Hq, Hkv, 1, D, dtype == QSA_BF16);
     if (D == kDimWide && !mfma) return QSA_ERR_UNSUPPORTED;  // D = 256 lives in the bf16 MFMA kernels
+    if (kv_fp8 && !mfma) return QSA_ERR_UNSUPPORTED;         // and so do FP8 K/V
+    if (kv_fp8 && !kv_scales_ok(k_scale, v_scale)) return QSA_ERR_INVALID_ARG;
     if (rows == 0) {
         if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || top_k < 1 || top_k > QSA_MAX_TOP_K) return QSA_ERR_INVALID_ARG;
         return QSA_OK;
     }
     qsa_status_t st = check_attn_common(q, k_cache, v_cache, kv_seq_stride, sel_blocks, sel_count, top_k, Hq, Hkv, D,
-                                        softmax_scale, dtype, out);
+                                        softmax_scale, dtype, out, kv_fp8);
     if (st != QSA_OK) return st;
     if (!row_seq || !row_pos) return QSA_ERR_INVALID_ARG;
     AttnArgs a{};
@@ -462,6 +472,9 @@ static qsa_status_t attn_prefill_impl(const void *q, const int32_t *row_seq, con
     a.page_table = page_table;
     a.pt_stride = pt_stride;
     a.page_tokens = page_tokens;
+    a.kv_fp8 = kv_fp8;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
     if (page_table && !mfma) return QSA_ERR_UNSUPPORTED;  // the paged gather lives in the MFMA kernels
     clear_launch_err();
     if (mfma)
@@ -510,7 +523,7 @@ static qsa_status_t attn_decode_impl(const void *q, const int32_t *row_pos, int3
                                     int32_t page_tokens, const int32_t *sel_blocks, const int32_t *sel_count,
                                     int32_t top_k, int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
                                     qsa_dtype_t dtype, void *out, float *lse, void *workspace, size_t workspace_bytes,
-                                    void *stream)
+                                    void *stream, bool kv_fp8 = false, float k_scale = 1.0f, float v_scale = 1.0f)
 {
     if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
     if (batch < 0 || q_per_seq < 1) return QSA_ERR_INVALID_ARG;
@@ -519,12 +532,14 @@ static qsa_status_t attn_decode_impl(const void *q, const int32_t *row_pos, int3
         return QSA_ERR_UNSUPPORTED;
     const bool mfma = attn_mfma_supported(Hq, Hkv, q_per_seq, D, dtype == QSA_BF16);
     if (D == kDimWide && !mfma) return QSA_ERR_UNSUPPORTED;  // D = 256 lives in the bf16 MFMA kernels
+    if (kv_fp8 && !mfma) return QSA_ERR_UNSUPPORTED;         // and so do FP8 K/V
+    if (kv_fp8 && !kv_scales_ok(k_scale, v_scale)) return QSA_ERR_INVALID_ARG;
     if (batch == 0) {
         if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || top_k < 1 || top_k > QSA_MAX_TOP_K) return QSA_ERR_INVALID_ARG;
         return QSA_OK;
     }
     qsa_status_t st = check_attn_common(q, k_cache, v_cache, kv_seq_stride, sel_blocks, sel_count, top_k, Hq, Hkv, D,
-                                        softmax_scale, dtype, out);
+                                        softmax_scale, dtype, out, kv_fp8);
     if (st != QSA_OK) return st;
     if (!row_pos) return QSA_ERR_INVALID_ARG;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return QSA_ERR_INVALID_ARG;
@@ -554,6 +569,9 @@ static qsa_status_t attn_decode_impl(const void *q, const int32_t *row_pos, int3
     a.page_table = page_table;
     a.pt_stride = pt_stride;
     a.page_tokens = page_tokens;
+    a.kv_fp8 = kv_fp8;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
     if (page_table && !mfma) return QSA_ERR_UNSUPPORTED;  // the paged gather lives in the MFMA kernels
     clear_launch_err();
     if (mfma) {
@@ -590,6 +608,38 @@ qsa_status_t qsa_sparse_attn_decode_paged(const void *q, const int32_t *row_pos,
     return attn_decode_impl(q, row_pos, batch, q_per_seq, tail_start, k_cache, v_cache, 0, page_table,
                             page_table_stride, page_tokens, sel_blocks, sel_count, top_k, Hq, Hkv, D, softmax_scale,
                             dtype, out, lse, workspace, workspace_bytes, stream);
+}
+
+qsa_status_t qsa_sparse_attn_prefill_fp8kv(const void *q, const int32_t *row_seq, const int32_t *row_pos,
+                                           int32_t rows, const uint8_t *k_codes, const uint8_t *v_codes,
+                                           int64_t kv_seq_stride, const int32_t *page_table,
+                                           int64_t page_table_stride, int32_t page_tokens, float k_scale,
+                                           float v_scale, const int32_t *sel_blocks, const int32_t *sel_count,
+                                           int32_t top_k, int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                                           void *out, float *lse, void *stream)
+{
+    if (page_table && (page_tokens < kBlock || page_tokens % kBlock || page_table_stride < 0))
+        return QSA_ERR_INVALID_ARG;
+    return attn_prefill_impl(q, row_seq, row_pos, rows, k_codes, v_codes, page_table ? 0 : kv_seq_stride,
+                             page_table, page_table_stride, page_tokens, sel_blocks, sel_count, top_k, Hq, Hkv, D,
+                             softmax_scale, QSA_BF16, out, lse, stream, true, k_scale, v_scale);
+}
+
+qsa_status_t qsa_sparse_attn_decode_fp8kv(const void *q, const int32_t *row_pos, int32_t batch, int32_t q_per_seq,
+                                          const int32_t *tail_start, const uint8_t *k_codes, const uint8_t *v_codes,
+                                          int64_t kv_seq_stride, const int32_t *page_table,
+                                          int64_t page_table_stride, int32_t page_tokens, float k_scale,
+                                          float v_scale, const int32_t *sel_blocks, const int32_t *sel_count,
+                                          int32_t top_k, int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                                          void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                          void *stream)
+{
+    if (page_table && (page_tokens < kBlock || page_tokens % kBlock || page_table_stride < 0))
+        return QSA_ERR_INVALID_ARG;
+    return attn_decode_impl(q, row_pos, batch, q_per_seq, tail_start, k_codes, v_codes,
+                            page_table ? 0 : kv_seq_stride, page_table, page_table_stride, page_tokens, sel_blocks,
+                            sel_count, top_k, Hq, Hkv, D, softmax_scale, QSA_BF16, out, lse, workspace,
+                            workspace_bytes, stream, true, k_scale, v_scale);
 }
 
 qsa_status_t qsa_profile_enable(int enable)

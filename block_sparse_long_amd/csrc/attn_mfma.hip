@@ -108,37 +108,96 @@ struct WaveState {
     float m, l;
 };
 
-// A thread's share of one chunk's gather, 64 bytes of K and 64 of V: K row
+// K/V elements: bf16 values, or FP8 E4M3 codes (one byte; their values are
+// a per-tensor k_scale / v_scale times E4M3(code), applied to the logits and
+// the output).  Codes are widened to bf16 on their way into LDS, exactly, so
+// the chunk in LDS and everything after it are the same for both.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// A thread's share of one chunk's gather, 32 elements of K and 32 of V: K row
 // t/kTpp at dims 32*(t%kTpp) .. +31, and V of positions 4q .. 4q+3 at dims
-// 8*(t/(kCh/4)) .. +7, q = t%(kCh/4).
-struct ChunkRegs {
+// 8*(t/(kCh/4)) .. +7, q = t%(kCh/4).  64 + 64 bytes in bf16, 32 + 32 as codes.
+template <typename KV>
+struct ChunkRegs;
+template <>
+struct ChunkRegs<bf16_t> {
     uint4 k[4];
     uint4 v[4];
 };
+template <>
+struct ChunkRegs<uint8_t> {
+    uint4 k[2];
+    uint2 v[4];
+};
+
+// Element-wise vector loads (a struct copy from global memory can be lowered
+// to a copy through scratch).
+__device__ __forceinline__ uint4 load_u4(const void *p)
+{
+    const u32x4_t x = *(const u32x4_t *)p;
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ uint2 load_u2(const void *p)
+{
+    const u32x2_t x = *(const u32x2_t *)p;
+    return make_uint2(x.x, x.y);
+}
+
+// A thread's 32 K elements, and V elements [4 positions x 8 dims] (piece i).
+template <typename KV>
+__device__ __forceinline__ void load_k(ChunkRegs<KV> &cr, const KV *src)
+{
+    constexpr int n = sizeof(KV) == 2 ? 4 : 2;
+#pragma unroll
+    for (int i = 0; i < n; ++i) cr.k[i] = load_u4(src + i * (16 / sizeof(KV)));
+}
+template <typename KV>
+__device__ __forceinline__ void zero_k(ChunkRegs<KV> &cr)
+{
+    constexpr int n = sizeof(KV) == 2 ? 4 : 2;
+#pragma unroll
+    for (int i = 0; i < n; ++i) cr.k[i] = make_uint4(0, 0, 0, 0);
+}
+template <typename KV>
+__device__ __forceinline__ void load_v(ChunkRegs<KV> &cr, int i, const KV *src)
+{
+    if constexpr (sizeof(KV) == 2)
+        cr.v[i] = load_u4(src);
+    else
+        cr.v[i] = load_u2(src);
+}
+template <typename KV>
+__device__ __forceinline__ void zero_v(ChunkRegs<KV> &cr, int i)
+{
+    if constexpr (sizeof(KV) == 2)
+        cr.v[i] = make_uint4(0, 0, 0, 0);
+    else
+        cr.v[i] = make_uint2(0, 0);
+}
 
 // Load the chunk of positions pos(0..n) into registers (zeros beyond n).  The
 // loads are only consumed by chunk_store, so they can stay in flight while
 // the previous chunk is computed.
-template <int DIM, class PosFn>
-__device__ __forceinline__ void chunk_load(ChunkRegs &cr, const bf16_t *__restrict__ kbase,
-                                           const bf16_t *__restrict__ vbase, int64_t row_stride, int n, PosFn pos)
+template <int DIM, typename KV, class PosFn>
+__device__ __forceinline__ void chunk_load(ChunkRegs<KV> &cr, const KV *__restrict__ kbase,
+                                           const KV *__restrict__ vbase, int64_t row_stride, int n, PosFn pos)
 {
     using G = Geo<DIM>;
     const int t = threadIdx.x;
     const int p = t / G::kTpp, dk = (t % G::kTpp) * 32;
-    if (p < n) {
-        const uint4 *src = (const uint4 *)(kbase + (int64_t)pos(p) * row_stride + dk);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cr.k[i] = src[i];
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cr.k[i] = make_uint4(0, 0, 0, 0);
-    }
+    if (p < n)
+        load_k(cr, kbase + (int64_t)pos(p) * row_stride + dk);
+    else
+        zero_k(cr);
     const int p0 = (t % (G::kCh / 4)) * 4, dv = (t / (G::kCh / 4)) * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        cr.v[i] = (p0 + i < n) ? *(const uint4 *)(vbase + (int64_t)pos(p0 + i) * row_stride + dv)
-                               : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+        if (p0 + i < n)
+            load_v(cr, i, vbase + (int64_t)pos(p0 + i) * row_stride + dv);
+        else
+            zero_v(cr, i);
+    }
 }
 
 // Slot of token p of sequence s in the K/V arrays: p itself when the caches
@@ -156,9 +215,9 @@ __device__ __forceinline__ int64_t kv_slot(const AttnArgs &a, int64_t s, int64_t
 // one block id serves each; a thread past the chunk's blocks reads the last
 // one instead (its positions carry no mask bit, so their P is exactly 0).
 // Every load is unconditional.
-template <int DIM>
-__device__ __forceinline__ void chunk_load_blocks(ChunkRegs &cr, const bf16_t *__restrict__ kbase,
-                                                  const bf16_t *__restrict__ vbase, uint32_t row_stride,
+template <int DIM, typename KV>
+__device__ __forceinline__ void chunk_load_blocks(ChunkRegs<KV> &cr, const KV *__restrict__ kbase,
+                                                  const KV *__restrict__ vbase, uint32_t row_stride,
                                                   const int32_t *ublk, int nb, const AttnArgs &a, int64_t seq)
 {
     using G = Geo<DIM>;
@@ -166,21 +225,15 @@ __device__ __forceinline__ void chunk_load_blocks(ChunkRegs &cr, const bf16_t *_
     const int32_t bk = ublk[min(t / (4 * G::kTpp), nb - 1)], bv = ublk[min(t % G::kChB, nb - 1)];
     // first slot of each block: its 4 tokens are consecutive slots
     const uint32_t sk = (uint32_t)kv_slot(a, seq, (int64_t)kBlock * bk), sv = (uint32_t)kv_slot(a, seq, (int64_t)kBlock * bv);
-    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    const u32x4_t *ks = (const u32x4_t *)(kbase + (uint64_t)sk * row_stride +
-                                          ((t / G::kTpp) & 3) * row_stride + (t % G::kTpp) * 32);
-    const bf16_t *vs = vbase + (uint64_t)sv * row_stride + (t / G::kChB) * 8;
+    load_k(cr, kbase + (uint64_t)sk * row_stride + ((t / G::kTpp) & 3) * row_stride + (t % G::kTpp) * 32);
+    const KV *vs = vbase + (uint64_t)sv * row_stride + (t / G::kChB) * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // element-wise vector loads (a block copy would go through memory)
-        const u32x4_t kx = ks[i], vx = *(const u32x4_t *)(vs + i * row_stride);
-        cr.k[i] = make_uint4(kx.x, kx.y, kx.z, kx.w);
-        cr.v[i] = make_uint4(vx.x, vx.y, vx.z, vx.w);
-    }
+    for (int i = 0; i < 4; ++i) load_v(cr, i, vs + i * row_stride);
 }
 
 // Registers -> LDS: K row-major, V transposed.
 template <int DIM>
-__device__ __forceinline__ void chunk_store(ChunkSmem<DIM> &cs, const ChunkRegs &cr)
+__device__ __forceinline__ void chunk_store(ChunkSmem<DIM> &cs, const ChunkRegs<bf16_t> &cr)
 {
     using G = Geo<DIM>;
     const int t = threadIdx.x;
@@ -203,12 +256,26 @@ __device__ __forceinline__ void chunk_store(ChunkSmem<DIM> &cs, const ChunkRegs 
     }
 }
 
-// Gather K and V^T of positions cs.pos[0..n) into LDS (zeros beyond n).
+// FP8 codes: widen to bf16 (exact), then store as above.
 template <int DIM>
-__device__ __forceinline__ void gather_chunk(ChunkSmem<DIM> &cs, const bf16_t *__restrict__ kbase,
-                                             const bf16_t *__restrict__ vbase, int64_t row_stride, int n)
+__device__ __forceinline__ void chunk_store(ChunkSmem<DIM> &cs, const ChunkRegs<uint8_t> &c8)
 {
-    ChunkRegs cr;
+    ChunkRegs<bf16_t> cr;
+    cr.k[0] = fp8x8_to_bf16_words(c8.k[0].x, c8.k[0].y);
+    cr.k[1] = fp8x8_to_bf16_words(c8.k[0].z, c8.k[0].w);
+    cr.k[2] = fp8x8_to_bf16_words(c8.k[1].x, c8.k[1].y);
+    cr.k[3] = fp8x8_to_bf16_words(c8.k[1].z, c8.k[1].w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cr.v[i] = fp8x8_to_bf16_words(c8.v[i].x, c8.v[i].y);
+    chunk_store<DIM>(cs, cr);
+}
+
+// Gather K and V^T of positions cs.pos[0..n) into LDS (zeros beyond n).
+template <int DIM, typename KV>
+__device__ __forceinline__ void gather_chunk(ChunkSmem<DIM> &cs, const KV *__restrict__ kbase,
+                                             const KV *__restrict__ vbase, int64_t row_stride, int n)
+{
+    ChunkRegs<KV> cr;
     chunk_load<DIM>(cr, kbase, vbase, row_stride, n, [&](int i) { return (int64_t)cs.pos[i]; });
     chunk_store<DIM>(cs, cr);
 }
@@ -337,9 +404,10 @@ static_assert(kSplitBlocks * kBlock == kAttnChunk, "a decode split covers one ch
 // ---------------------------------------------------------------------------
 // Prefill: grid (row tiles, Hkv).  rows_per_tile * hg <= 64.
 // ---------------------------------------------------------------------------
-template <int DIM>
+template <int DIM, typename KV>
 __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, int32_t rows_per_tile)
 {
+    constexpr bool kFp8 = sizeof(KV) == 1;
     using G = Geo<DIM>;
     __shared__ ChunkSmem<DIM> cs;
     __shared__ UnionSmem us;
@@ -358,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
     load_query<DIM>((const bf16_t *)a.q + ((row0 + (q_valid ? r_local : 0)) * a.Hq + head) * DIM, q_valid, qb);
     WaveState<DIM> st;
     init_state(st);
-    const float scale2 = a.scale * kLog2e;
+    const float scale2 = kFp8 ? a.scale * a.k_scale * kLog2e : a.scale * kLog2e;
     const int64_t row_stride = (int64_t)a.Hkv * DIM;
     // ---- the tile's rows, read once: position, sequence, kept count, last
     // kept block; and all their kept blocks (at most kMaxUnionBlocks, 16 per
@@ -397,8 +465,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
         todo &= ~active;
         const uint32_t qbit = q_valid ? (active & (1u << r_local)) : 0u;
         const int64_t seq_off = a.page_table ? 0 : (int64_t)seq * a.kv_seq_stride;
-        const bf16_t *kbase = (const bf16_t *)a.k_cache + seq_off + (int64_t)kvh * DIM;
-        const bf16_t *vbase = (const bf16_t *)a.v_cache + seq_off + (int64_t)kvh * DIM;
+        const KV *kbase = (const KV *)a.k_cache + seq_off + (int64_t)kvh * DIM;
+        const KV *vbase = (const KV *)a.v_cache + seq_off + (int64_t)kvh * DIM;
         // block range of the active rows' selections
         int32_t hi_blk = 0;
         for (int r = 0; r < nrows; ++r)
@@ -458,7 +526,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
             // flight while chunk c is computed ----
             constexpr int kChB = G::kChB;
             const int32_t nch = (nu + kChB - 1) / kChB;
-            ChunkRegs cr;
+            ChunkRegs<KV> cr;
             if (nch > 0)
                 chunk_load_blocks<DIM>(cr, kbase, vbase, (uint32_t)row_stride, us.blk, min(kChB, nu), a, seq);
             for (int32_t c = 0; c < nch; ++c) {
@@ -522,7 +590,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
         if (ro >= nrows) continue;
         const int ho = kvh * hg + qo % hg;
         bf16_t *orow = (bf16_t *)a.out + ((row0 + ro) * a.Hq + ho) * DIM;
-        const float inv = lq > 0.0f ? 1.0f / lq : 0.0f;
+        const float inv = lq > 0.0f ? (kFp8 ? a.v_scale : 1.0f) / lq : 0.0f;
 #pragma unroll
         for (int nt = 0; nt < G::kNt; ++nt) orow[16 * nt + m16] = f32_to_bf16(st.o[nt][j] * inv);
     }
@@ -535,9 +603,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
 // Split i < nsplit-1 takes kept blocks [16i, 16i + 16); the last split takes
 // the tails.
 // ---------------------------------------------------------------------------
-template <int DIM>  // D = 256 needs the two-wave register budget to avoid spilling
+template <int DIM, typename KV>  // D = 256 needs the two-wave register budget to avoid spilling
 __global__ __launch_bounds__(256, DIM == 256 ? 2 : 1) void attn_decode_mfma_kernel(AttnArgs a)
 {
+    constexpr bool kFp8 = sizeof(KV) == 1;
     using G = Geo<DIM>;
     __shared__ ChunkSmem<DIM> cs;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -556,12 +625,12 @@ __global__ __launch_bounds__(256, DIM == 256 ? 2 : 1) void attn_decode_mfma_kern
     load_query<DIM>((const bf16_t *)a.q + qrow * DIM, q_valid, qb);
     WaveState<DIM> st;
     init_state(st);
-    const float scale2 = a.scale * kLog2e;
+    const float scale2 = kFp8 ? a.scale * a.k_scale * kLog2e : a.scale * kLog2e;
     const uint32_t qbit = q_valid ? (1u << jrow) : 0u;
     const int64_t row_stride = (int64_t)a.Hkv * DIM;
     const int64_t seq_off = a.page_table ? 0 : s * a.kv_seq_stride;
-    const bf16_t *kbase = (const bf16_t *)a.k_cache + seq_off + (int64_t)kvh * DIM;
-    const bf16_t *vbase = (const bf16_t *)a.v_cache + seq_off + (int64_t)kvh * DIM;
+    const KV *kbase = (const KV *)a.k_cache + seq_off + (int64_t)kvh * DIM;
+    const KV *vbase = (const KV *)a.v_cache + seq_off + (int64_t)kvh * DIM;
     const int32_t count = min(a.sel_count[s], a.top_k);
     const uint32_t all_rows = a.q_per_sel >= 32 ? 0xffffffffu : ((1u << a.q_per_sel) - 1u);
     if (split < a.nsplit - 1) {
@@ -621,8 +690,9 @@ __global__ __launch_bounds__(256, DIM == 256 ? 2 : 1) void attn_decode_mfma_kern
         if (qo >= nq) continue;
         const int jo = qo / hg, ho = kvh * hg + qo % hg;
         float *pp = a.partial + (((s * a.q_per_sel + jo) * a.Hq + ho) * a.nsplit + split) * (DIM + 2);
+        const float vs = kFp8 ? a.v_scale : 1.0f;  // the partial outputs carry the V scale
 #pragma unroll
-        for (int nt = 0; nt < G::kNt; ++nt) pp[16 * nt + m16] = st.o[nt][j];
+        for (int nt = 0; nt < G::kNt; ++nt) pp[16 * nt + m16] = st.o[nt][j] * vs;
     }
     if (q_valid && g == 0) {
         float *pp = a.partial + (qrow * a.nsplit + split) * (DIM + 2);
@@ -653,19 +723,31 @@ void launch_attn_prefill_mfma(const AttnArgs &a, hipStream_t stream)
     const int32_t hg = a.Hq / a.Hkv;
     const int32_t rpt = attn_prefill_rows_per_tile(hg, a.top_k);
     const dim3 grid((unsigned)((a.n_sel + rpt - 1) / rpt), (unsigned)a.Hkv), block(256);
-    if (a.D == 256)
-        QSA_LAUNCH("attn_prefill_mfma_d256", attn_prefill_mfma_kernel<256>, grid, block, 0, stream, a, rpt);
+    if (a.D == 256 && a.kv_fp8)
+        QSA_LAUNCH("attn_prefill_mfma_d256_fp8kv", (attn_prefill_mfma_kernel<256, uint8_t>), grid, block, 0, stream,
+                   a, rpt);
+    else if (a.D == 256)
+        QSA_LAUNCH("attn_prefill_mfma_d256", (attn_prefill_mfma_kernel<256, bf16_t>), grid, block, 0, stream, a,
+                   rpt);
+    else if (a.kv_fp8)
+        QSA_LAUNCH("attn_prefill_mfma_fp8kv", (attn_prefill_mfma_kernel<128, uint8_t>), grid, block, 0, stream, a,
+                   rpt);
     else
-        QSA_LAUNCH("attn_prefill_mfma", attn_prefill_mfma_kernel<128>, grid, block, 0, stream, a, rpt);
+        QSA_LAUNCH("attn_prefill_mfma", (attn_prefill_mfma_kernel<128, bf16_t>), grid, block, 0, stream, a, rpt);
 }
 
 void launch_attn_decode_mfma(const AttnArgs &a, hipStream_t stream)
 {
     const dim3 grid((unsigned)a.nsplit, (unsigned)((int64_t)a.n_sel * a.Hkv)), block(256);
-    if (a.D == 256)
-        QSA_LAUNCH("attn_decode_mfma_d256", attn_decode_mfma_kernel<256>, grid, block, 0, stream, a);
+    if (a.D == 256 && a.kv_fp8)
+        QSA_LAUNCH("attn_decode_mfma_d256_fp8kv", (attn_decode_mfma_kernel<256, uint8_t>), grid, block, 0, stream,
+                   a);
+    else if (a.D == 256)
+        QSA_LAUNCH("attn_decode_mfma_d256", (attn_decode_mfma_kernel<256, bf16_t>), grid, block, 0, stream, a);
+    else if (a.kv_fp8)
+        QSA_LAUNCH("attn_decode_mfma_fp8kv", (attn_decode_mfma_kernel<128, uint8_t>), grid, block, 0, stream, a);
     else
-        QSA_LAUNCH("attn_decode_mfma", attn_decode_mfma_kernel<128>, grid, block, 0, stream, a);
+        QSA_LAUNCH("attn_decode_mfma", (attn_decode_mfma_kernel<128, bf16_t>), grid, block, 0, stream, a);
 }
 
 }  // namespace qsa

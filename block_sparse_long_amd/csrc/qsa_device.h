@@ -26,12 +26,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 // Eight FP8 E4M3 codes (bytes of w0 then w1, lowest first) -> eight bf16, as
 // one MFMA operand.  The conversion is exact: every E4M3 value (at most 4
 // significant bits, 2^-9 .. 448) is a bf16 value.
-__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1)
+__device__ __forceinline__ uint4 fp8x8_to_bf16_words(uint32_t w0, uint32_t w1)
 {
     const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
     const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
-    return as_bf16x8(make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
-                                pack_bf16x2(d[0], d[1])));
+    return make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
+                      pack_bf16x2(d[0], d[1]));
+}
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1)
+{
+    return as_bf16x8(fp8x8_to_bf16_words(w0, w1));
 }
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }

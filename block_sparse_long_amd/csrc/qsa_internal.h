@@ -142,13 +142,17 @@ struct AttnArgs {
     const int32_t *page_table;
     int64_t pt_stride;
     int32_t page_tokens;      // a multiple of 4: a block never straddles pages
+    // FP8 K/V (MFMA path): k_cache / v_cache hold E4M3 codes whose values are
+    // k_scale * E4M3(code) and v_scale * E4M3(code)
+    int32_t kv_fp8;
+    float k_scale, v_scale;
 };
 int32_t attn_decode_splits(int32_t top_k);
 void launch_attn_prefill(const AttnArgs &a, bool bf16, hipStream_t stream);
 void launch_attn_decode(const AttnArgs &a, bool bf16, hipStream_t stream);
 void launch_attn_combine(const AttnArgs &a, bool bf16, hipStream_t stream);
 
-// ---- attn_mfma.hip (bf16, D 128 or 256, Hq/Hkv up to 64) ----------------------
+// ---- attn_mfma.hip (bf16 q, bf16 or FP8 K/V, D 128 or 256, Hq/Hkv up to 64) ---
 bool attn_mfma_supported(int32_t Hq, int32_t Hkv, int32_t q_per_sel, int32_t D, bool bf16);
 int32_t attn_prefill_rows_per_tile(int32_t hg, int32_t top_k);
 void launch_attn_prefill_mfma(const AttnArgs &a, hipStream_t stream);

@@ -27,7 +27,8 @@ INDEX_DIM, INDEX_HEADS, BLOCK_TOKENS, MAX_TOP_K, MAX_QUERY_GROUP = 128, 4, 4, 40
 # every symbol include/qsa.h declares
 EXPORTS = ("qsa_pool_index_keys", "qsa_pool_index_keys_fp8", "qsa_pool_append", "qsa_score_topk_workspace_size",
            "qsa_score_topk", "qsa_score_topk_fp8_workspace_size", "qsa_score_topk_fp8", "qsa_score_topk_paged",
-           "qsa_sparse_attn_prefill_paged", "qsa_sparse_attn_decode_paged",
+           "qsa_sparse_attn_prefill_paged", "qsa_sparse_attn_decode_paged", "qsa_sparse_attn_prefill_fp8kv",
+           "qsa_sparse_attn_decode_fp8kv",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode_workspace_size",
            "qsa_sparse_attn_decode", "qsa_status_string", "qsa_last_device_error", "qsa_profile_enable",
            "qsa_profile_reset", "qsa_profile_kernel_ms")
@@ -80,6 +81,12 @@ def load():
     lib.qsa_sparse_attn_decode_paged.argtypes = [P, P, i32, i32, P, P, P, P, i64, i32, P, P, i32, i32, i32, i32, f32,
                                                  st, P, P, P, sz, P]
     lib.qsa_sparse_attn_decode_paged.restype = st
+    lib.qsa_sparse_attn_prefill_fp8kv.argtypes = [P, P, P, i32, P, P, i64, P, i64, i32, f32, f32, P, P, i32, i32,
+                                                  i32, i32, f32, P, P, P]
+    lib.qsa_sparse_attn_prefill_fp8kv.restype = st
+    lib.qsa_sparse_attn_decode_fp8kv.argtypes = [P, P, i32, i32, P, P, P, i64, P, i64, i32, f32, f32, P, P, i32, i32,
+                                                 i32, i32, f32, P, P, P, sz, P]
+    lib.qsa_sparse_attn_decode_fp8kv.restype = st
     lib.qsa_pool_append.argtypes = [P, P, P, P, P, i32, f64, u32, st, P]
     lib.qsa_pool_append.restype = st
     lib.qsa_score_topk_workspace_size.argtypes = [i32, i32, i32, st, u32]
@@ -374,6 +381,67 @@ def sparse_attn_decode_paged(q, row_pos, k_cache, v_cache, page_table, page_toke
                                              _dtype_code(q), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                              _stream(stream))
     _check("qsa_sparse_attn_decode_paged", rc)
+    return out, lse
+
+
+def _fp8_codes(t):
+    """uint8 codes, or a torch.float8_e4m3fn tensor viewed as its codes."""
+    import torch
+    return t.view(torch.uint8) if t.dtype != torch.uint8 else t
+
+
+def sparse_attn_prefill_fp8kv(q, row_seq, row_pos, k_codes, v_codes, k_scale: float, v_scale: float, sel_blocks,
+                              sel_count, page_table=None, page_tokens: int = 0, softmax_scale: Optional[float] = None,
+                              out=None, lse=None, want_lse=True, stream=None):
+    """a7+a8 on an FP8 K/V cache: E4M3 codes [B][L][Hkv][D] (or [slots][Hkv][D]
+    with a page table), values k_scale * E4M3(code) and v_scale * E4M3(code);
+    q, out bf16."""
+    import torch
+    k_codes, v_codes = _fp8_codes(k_codes), _fp8_codes(v_codes)
+    _need_contig(q, row_seq, row_pos, k_codes, v_codes, page_table, sel_blocks, sel_count)
+    R, Hq, D = q.shape
+    Hkv = k_codes.shape[-2]
+    stride = 0 if page_table is not None else k_codes.shape[1] * Hkv * D
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((R, Hq), dtype=torch.float32, device=q.device)
+    rc = load().qsa_sparse_attn_prefill_fp8kv(
+        _ptr(q), _ptr(row_seq), _ptr(row_pos), R, _ptr(k_codes), _ptr(v_codes), stride, _ptr(page_table),
+        0 if page_table is None else page_table.shape[1], int(page_tokens), float(k_scale), float(v_scale),
+        _ptr(sel_blocks), _ptr(sel_count), sel_blocks.shape[1], Hq, Hkv, D, scale, _ptr(out), _ptr(lse),
+        _stream(stream))
+    _check("qsa_sparse_attn_prefill_fp8kv", rc)
+    return out, lse
+
+
+def sparse_attn_decode_fp8kv(q, row_pos, k_codes, v_codes, k_scale: float, v_scale: float, sel_blocks, sel_count,
+                             tail_start=None, page_table=None, page_tokens: int = 0,
+                             softmax_scale: Optional[float] = None, out=None, lse=None, want_lse=True,
+                             workspace=None, stream=None):
+    """a7+a9 on an FP8 K/V cache (as sparse_attn_prefill_fp8kv)."""
+    import torch
+    k_codes, v_codes = _fp8_codes(k_codes), _fp8_codes(v_codes)
+    _need_contig(q, row_pos, k_codes, v_codes, page_table, sel_blocks, sel_count, tail_start)
+    B, Qn, Hq, D = q.shape
+    Hkv = k_codes.shape[-2]
+    stride = 0 if page_table is not None else k_codes.shape[1] * Hkv * D
+    top_k = sel_blocks.shape[1]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Qn, Hq), dtype=torch.float32, device=q.device)
+    need = sparse_attn_decode_workspace_size(B, Qn, Hq, D, top_k)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+    rc = load().qsa_sparse_attn_decode_fp8kv(
+        _ptr(q), _ptr(row_pos), B, Qn, _ptr(tail_start), _ptr(k_codes), _ptr(v_codes), stride, _ptr(page_table),
+        0 if page_table is None else page_table.shape[1], int(page_tokens), float(k_scale), float(v_scale),
+        _ptr(sel_blocks), _ptr(sel_count), top_k, Hq, Hkv, D, scale, _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel(), _stream(stream))
+    _check("qsa_sparse_attn_decode_fp8kv", rc)
     return out, lse
 
 

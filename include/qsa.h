@@ -207,8 +207,8 @@ qsa_status_t qsa_score_topk_fp8(const void *q_index, const int32_t *row_seq, con
  *   sel_blocks [rows][top_k], sel_count [rows] as written by qsa_score_topk.
  *   out      [rows][Hq][D], dtype.  lse [rows][Hq] fp32 natural-log
  *            log-sum-exp of the scaled logits, or NULL.
- *   D == 128; Hq % Hkv == 0; Hq/Hkv <= QSA_MAX_QUERY_GROUP;
- *   1 <= top_k <= QSA_MAX_TOP_K.
+ *   D == 128, or D == 256 with dtype QSA_BF16; Hq % Hkv == 0;
+ *   Hq/Hkv <= QSA_MAX_QUERY_GROUP; 1 <= top_k <= QSA_MAX_TOP_K.
  */
 qsa_status_t qsa_sparse_attn_prefill(const void *q, const int32_t *row_seq, const int32_t *row_pos,
                                      int32_t rows, const void *k_cache, const void *v_cache,
@@ -242,8 +242,8 @@ qsa_status_t qsa_score_topk_paged(const void *q_index, const int32_t *row_seq, c
                                   uint32_t flags, qsa_dtype_t dtype, int32_t *sel_blocks,
                                   int32_t *sel_count, float *sel_scores, void *workspace,
                                   size_t workspace_bytes, void *stream);
-/* qsa_sparse_attn_prefill on a paged K/V pool (bf16 with Hq/Hkv a power of
- * two up to 64, else QSA_ERR_UNSUPPORTED). */
+/* qsa_sparse_attn_prefill on a paged K/V pool (bf16 only, else
+ * QSA_ERR_UNSUPPORTED). */
 qsa_status_t qsa_sparse_attn_prefill_paged(const void *q, const int32_t *row_seq, const int32_t *row_pos,
                                            int32_t rows, const void *k_cache, const void *v_cache,
                                            const int32_t *page_table, int64_t page_table_stride,
@@ -283,8 +283,8 @@ qsa_status_t qsa_sparse_attn_decode(const void *q, const int32_t *row_pos, int32
                                     qsa_dtype_t dtype, void *out, float *lse, void *workspace,
                                     size_t workspace_bytes, void *stream);
 
-/* qsa_sparse_attn_decode on a paged K/V pool (same restriction as the
- * prefill variant). */
+/* qsa_sparse_attn_decode on a paged K/V pool (bf16 with q_per_seq <= 32,
+ * else QSA_ERR_UNSUPPORTED). */
 qsa_status_t qsa_sparse_attn_decode_paged(const void *q, const int32_t *row_pos, int32_t batch,
                                           int32_t q_per_seq, const int32_t *tail_start,
                                           const void *k_cache, const void *v_cache,
@@ -294,6 +294,40 @@ qsa_status_t qsa_sparse_attn_decode_paged(const void *q, const int32_t *row_pos,
                                           int32_t Hkv, int32_t D, float softmax_scale,
                                           qsa_dtype_t dtype, void *out, float *lse, void *workspace,
                                           size_t workspace_bytes, void *stream);
+
+/*
+ * FP8 K/V cache ("Qwen3.8-Flash-Next, Layer by Layer", section "Serving it":
+ * the KV cache kept in FP8).  k_codes / v_codes hold OCP E4M3 codes (the bit
+ * layout of torch.float8_e4m3fn), one byte per element, laid out as the bf16
+ * caches of qsa_sparse_attn_prefill / _decode (contiguous with kv_seq_stride,
+ * in elements = bytes, a multiple of 16), or paged when page_table is not
+ * NULL (then kv_seq_stride is ignored; see the paged pool above).  An
+ * element's value is k_scale * E4M3(code) for K and v_scale * E4M3(code) for
+ * V: one positive finite FP32 scale per cache tensor.  q, out are bf16;
+ * lse as in the bf16 calls.  Head dim 128 or 256, Hq/Hkv <= 64, decode
+ * q_per_seq <= 32 and q_per_seq * Hq/Hkv <= 64 (else QSA_ERR_UNSUPPORTED);
+ * code arrays 16-byte aligned.  Decode workspace:
+ * qsa_sparse_attn_decode_workspace_size().  Everything else as in the bf16
+ * entry points.
+ */
+qsa_status_t qsa_sparse_attn_prefill_fp8kv(const void *q, const int32_t *row_seq, const int32_t *row_pos,
+                                           int32_t rows, const uint8_t *k_codes, const uint8_t *v_codes,
+                                           int64_t kv_seq_stride, const int32_t *page_table,
+                                           int64_t page_table_stride, int32_t page_tokens, float k_scale,
+                                           float v_scale, const int32_t *sel_blocks,
+                                           const int32_t *sel_count, int32_t top_k, int32_t Hq,
+                                           int32_t Hkv, int32_t D, float softmax_scale, void *out,
+                                           float *lse, void *stream);
+qsa_status_t qsa_sparse_attn_decode_fp8kv(const void *q, const int32_t *row_pos, int32_t batch,
+                                          int32_t q_per_seq, const int32_t *tail_start,
+                                          const uint8_t *k_codes, const uint8_t *v_codes,
+                                          int64_t kv_seq_stride, const int32_t *page_table,
+                                          int64_t page_table_stride, int32_t page_tokens, float k_scale,
+                                          float v_scale, const int32_t *sel_blocks,
+                                          const int32_t *sel_count, int32_t top_k, int32_t Hq,
+                                          int32_t Hkv, int32_t D, float softmax_scale, void *out,
+                                          float *lse, void *workspace, size_t workspace_bytes,
+                                          void *stream);
 
 /* Static description of a status code. */
 const char *qsa_status_string(qsa_status_t status);

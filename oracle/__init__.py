@@ -64,6 +64,8 @@ def _load():
     lib.qsa_oracle_fp8_to_double.restype = f64
     lib.qsa_oracle_fp8_from_double.argtypes = [f64]
     lib.qsa_oracle_fp8_from_double.restype = ctypes.c_uint8
+    lib.qsa_oracle_fp8_encode.argtypes = [P, P, i64]
+    lib.qsa_oracle_fp8_encode.restype = None
     lib.qsa_oracle_pool_fp8.argtypes = [P, i64, P, P, i64, i32, i32, i32, f64, u32, i32]
     lib.qsa_oracle_pool_fp8.restype = ctypes.c_int
     lib.qsa_oracle_score_topk_fp8.argtypes = [P, i32, P, P, i32, P, P, i64, i32, f64, u32, P, P, P, P, i64]
@@ -139,10 +141,10 @@ def fp8_to_float(codes) -> np.ndarray:
 
 def fp8_from_float(x) -> np.ndarray:
     """values -> E4M3 codes (uint8), nearest with ties to the even code."""
-    lib = _load()
-    x = np.asarray(x, dtype=np.float64)
-    out = np.array([lib.qsa_oracle_fp8_from_double(float(v)) for v in x.reshape(-1)], dtype=np.uint8)
-    return out.reshape(x.shape)
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _load().qsa_oracle_fp8_encode(_ptr(x), _ptr(out), x.size)
+    return out
 
 
 def rope(vec, pos: int, theta: float) -> np.ndarray:

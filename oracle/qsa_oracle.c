@@ -144,6 +144,14 @@ uint8_t qsa_oracle_fp8_from_double(double x)
     return sign | (uint8_t)(ef << 3) | (uint8_t)mant;
 }
 
+/* The same rounding over an array (n values). */
+void qsa_oracle_fp8_encode(const double *x, uint8_t *codes, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        codes[i] = qsa_oracle_fp8_from_double(x[i]);
+}
+
 static double load_elem(const void *base, int64_t idx, int dtype)
 {
     if (dtype == OR_BF16)

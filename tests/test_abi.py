@@ -238,3 +238,41 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(qsa, "_lib", None)
     with pytest.raises(qsa.QsaLibraryMissing):
         qsa.load()
+
+
+def test_fp8kv_validation(libqsa):
+    f = libqsa.qsa_sparse_attn_prefill_fp8kv
+    # q, seq, pos, rows, k, v, stride, table, pt_stride, P, ks, vs, sel, cnt, top_k, Hq, Hkv, D, scale, out, lse, st
+    args = [A, B_, C, 4, A, B_, 1024, None, 0, 0, 0.02, 0.03, C, A, 512, 8, 1, 128, 0.1, B_, None, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a3=0) == qsa.OK
+    assert call(a10=0.0) == qsa.ERR_INVALID_ARG                     # scales must be positive and finite
+    assert call(a11=float("nan")) == qsa.ERR_INVALID_ARG
+    assert call(a10=-1.0) == qsa.ERR_INVALID_ARG
+    assert call(a6=1032) == qsa.ERR_INVALID_ARG                     # stride: 16-byte rows of codes
+    assert call(a4=MIS) == qsa.ERR_INVALID_ARG
+    assert call(a17=192) == qsa.ERR_UNSUPPORTED
+    assert call(a15=256, a16=2) == qsa.ERR_UNSUPPORTED              # a group of 128 heads
+    assert call(a7=C, a8=100, a9=6) == qsa.ERR_INVALID_ARG           # pages hold whole blocks
+    d = libqsa.qsa_sparse_attn_decode_fp8kv
+    ws = qsa.sparse_attn_decode_workspace_size(4, 4, 24, 256, 512)
+    dargs = [A, B_, 4, 4, None, A, B_, 1024, None, 0, 0, 0.02, 0.03, C, A, 512, 24, 2, 256, 0.1, B_, None, 0x100000,
+             ws, None]
+
+    def dcall(**kw):
+        a = list(dargs)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return d(*a)
+
+    assert dcall(a2=0) == qsa.OK
+    assert dcall(a23=ws - 1) == qsa.ERR_WORKSPACE
+    assert dcall(a12=0.0) == qsa.ERR_INVALID_ARG
+    assert dcall(a3=6) == qsa.ERR_UNSUPPORTED                       # 6 rows x 12 heads > 64
+    assert dcall(a8=C, a9=100, a10=2) == qsa.ERR_INVALID_ARG

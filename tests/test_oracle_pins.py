@@ -755,3 +755,20 @@ def test_fp8kv_zero_query_averages_the_decoded_values():
             g = h // (q.shape[1] // vint.shape[2])
             np.testing.assert_allclose(out[r, h], vals[0, P, g].mean(0), rtol=1e-6, atol=1e-7)
             assert lse[r, h] == pytest.approx(math.log(len(P)), rel=1e-6)
+
+
+def test_fp8_codes_match_torch_float8_e4m3fn():
+    # the FP8 K/V entry points take torch.float8_e4m3fn tensors as codes: its
+    # conversion (a library routine) and the oracle's rounding give the same
+    # codes on every finite value, the midpoints between them and random values
+    table = oracle.fp8_to_float(np.arange(256, dtype=np.uint8))
+    fin = np.sort(np.unique(table[np.isfinite(table)]))
+    mids = (fin[1:] + fin[:-1]) / 2
+    rng = np.random.default_rng(95)
+    x = np.concatenate([fin, mids, rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 0.01])
+    x32 = x.astype(np.float32)
+    n = len(fin) + len(mids)
+    np.testing.assert_array_equal(x32[:n], x[:n])        # the values and midpoints are exact in fp32
+    mine = oracle.fp8_from_float(x32.astype(np.float64))
+    theirs = torch.from_numpy(x32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(mine, theirs)
