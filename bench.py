@@ -96,6 +96,7 @@ def prefill_work(spec, row_pos):
         "attn_prefill": ("alu", 4.0 * spec.Hq * spec.D * float(npos.sum()), "flop"),
         "attn_prefill_mfma": ("mfma", 4.0 * spec.Hq * spec.D * float(npos.sum()), "flop"),
         "attn_prefill_mfma_d256": ("mfma", 4.0 * spec.Hq * spec.D * float(npos.sum()), "flop"),
+        "attn_prefill_mfma_fp8kv": ("mfma", 4.0 * spec.Hq * spec.D * float(npos.sum()), "flop"),
         "score_filter": ("mfma", 2.0 * 4 * DIM * pairs, "flop"),
         "score_filter_fp8": ("mfma", 2.0 * 4 * DIM * pairs, "flop"),
         "pool_rope_fp8": ("hbm", new_blocks * (4 * DIM * eb + DIM + 4), "B"),
@@ -124,6 +125,7 @@ def decode_work(spec, anchor_pos, attn_pos, tail_start):
         "attn_decode": ("hbm", kv_bytes + q_bytes, "B"),
         "attn_decode_mfma": ("hbm", kv_bytes + q_bytes, "B"),
         "attn_decode_mfma_d256": ("hbm", kv_bytes + q_bytes, "B"),
+        "attn_decode_mfma_fp8kv": ("hbm", kv_bytes / eb + q_bytes, "B"),   # one byte per K/V element
     }, pairs
 
 
@@ -178,6 +180,7 @@ ALL_KERNELS = ["pool_rope", "pool_rope_fp8", "pool_append", "rope_query", "score
                "score_rows_fp8", "score_gemm_bf16", "select_rows", "select_collect", "select_final", "score_sample",
                "score_sample_fp8", "sample_threshold", "score_filter", "score_filter_fp8", "select_merge",
                "attn_prefill_mfma", "attn_decode_mfma", "attn_prefill_mfma_d256", "attn_decode_mfma_d256",
+               "attn_prefill_mfma_fp8kv", "attn_decode_mfma_fp8kv",
                "attn_prefill", "attn_decode", "attn_combine"]
 
 
@@ -185,10 +188,11 @@ ALL_KERNELS = ["pool_rope", "pool_rope_fp8", "pool_append", "rope_query", "score
 # prefill workload
 # ---------------------------------------------------------------------------
 
-def bench_prefill(spec, steps, warmup, cpu_baseline, keys="bf16", w=None):
+def bench_prefill(spec, steps, warmup, cpu_baseline, keys="bf16", w=None, kv="bf16"):
     """keys "fp8": the compressed keys stored as E4M3 codes plus one scale per
-    key (qsa_pool_index_keys_fp8 / qsa_score_topk_fp8); everything else as
-    with bf16 keys."""
+    key (qsa_pool_index_keys_fp8 / qsa_score_topk_fp8); kv "fp8": the K/V
+    cache as E4M3 codes with one scale per tensor (qsa_sparse_attn_*_fp8kv);
+    everything else as with bf16."""
     import torch
     from block_sparse_long_amd import qsa, synth
     if w is None:
@@ -210,6 +214,9 @@ def bench_prefill(spec, steps, warmup, cpu_baseline, keys="bf16", w=None):
             qsa.pool_index_keys(raw, pooled, 0, first_new, spec.theta)
     iq, seq, pos = to_dev(w["idx_q"]), to_dev(w["row_seq"]), to_dev(w["row_pos"])
     q, kc, vc = to_dev(w["q"]), to_dev(w["k_cache"]), to_dev(w["v_cache"])
+    fp8kv = kv == "fp8"
+    if fp8kv:
+        (kc, ks), (vc, vs) = quantize_kv(kc), quantize_kv(vc)
     R = spec.chunk
     max_nb = L // 4
     sel = torch.empty((R, k), dtype=torch.int32, device="cuda")
@@ -228,10 +235,13 @@ def bench_prefill(spec, steps, warmup, cpu_baseline, keys="bf16", w=None):
             qsa.pool_index_keys(raw, pooled, first_new, nb, spec.theta)
             qsa.score_topk(iq, seq, pos, pooled, max_nb, k, spec.theta, sel_blocks=sel, sel_count=cnt,
                            workspace=ws, want_scores=False)
-        qsa.sparse_attn_prefill(q, seq, pos, kc, vc, sel, cnt, out=out, lse=lse)
+        if fp8kv:
+            qsa.sparse_attn_prefill_fp8kv(q, seq, pos, kc, vc, ks, vs, sel, cnt, out=out, lse=lse)
+        else:
+            qsa.sparse_attn_prefill(q, seq, pos, kc, vc, sel, cnt, out=out, lse=lse)
 
     ms = timed(step, steps, warmup)
-    log(f"{spec.name} ({keys} keys): {ms:.3f} ms/step")
+    log(f"{spec.name} ({keys} keys, {kv} K/V): {ms:.3f} ms/step")
     kt = kernel_times(step, max(3, min(steps, 10)), ALL_KERNELS)
     work, pairs, npos = prefill_work(spec, w["row_pos"])
     kernels = {n: {"launches_per_step": c / max(3, min(steps, 10)), "avg_us": round(a * 1e3, 2)}
@@ -285,8 +295,8 @@ def cpu_prefill(spec, w, target_s=12.0):
 # decode workload
 # ---------------------------------------------------------------------------
 
-def bench_decode(spec, steps, warmup, cpu_baseline, copies=3, keys="bf16", w=None):
-    """keys "fp8": E4M3 codes plus one scale per key, as in bench_prefill."""
+def bench_decode(spec, steps, warmup, cpu_baseline, copies=3, keys="bf16", w=None, kv="bf16"):
+    """keys / kv "fp8": as in bench_prefill."""
     import torch
     from block_sparse_long_amd import qsa, synth
     if w is None:
@@ -309,6 +319,9 @@ def bench_decode(spec, steps, warmup, cpu_baseline, copies=3, keys="bf16", w=Non
             pooled_h = pooled0[:1].cpu()
     del raw
     kc0, vc0 = to_dev(w["k_cache"]), to_dev(w["v_cache"])
+    fp8kv = kv == "fp8"
+    if fp8kv:
+        (kc0, ks), (vc0, vs) = quantize_kv(kc0), quantize_kv(vc0)
     if fp8:
         kcodes = [codes0] + [codes0.clone() for _ in range(copies - 1)]
         kscales = [scales0] + [scales0.clone() for _ in range(copies - 1)]
@@ -338,10 +351,14 @@ def bench_decode(spec, steps, warmup, cpu_baseline, copies=3, keys="bf16", w=Non
         else:
             qsa.score_topk(iq, seq, apos, pooled[c], max_nb, k, spec.theta, sel_blocks=sel, sel_count=cnt,
                            workspace=ws, want_scores=False)
-        qsa.sparse_attn_decode(q, rpos, kcs[c], vcs[c], sel, cnt, ts, out=out, lse=lse, workspace=wsa)
+        if fp8kv:
+            qsa.sparse_attn_decode_fp8kv(q, rpos, kcs[c], vcs[c], ks, vs, sel, cnt, ts, out=out, lse=lse,
+                                         workspace=wsa)
+        else:
+            qsa.sparse_attn_decode(q, rpos, kcs[c], vcs[c], sel, cnt, ts, out=out, lse=lse, workspace=wsa)
 
     ms = timed(step, steps, warmup)
-    log(f"{spec.name} ({keys} keys): {ms:.3f} ms/step")
+    log(f"{spec.name} ({keys} keys, {kv} K/V): {ms:.3f} ms/step")
     nprof = max(3, min(steps, 30))
     kt = kernel_times(step, nprof, ALL_KERNELS)
     work, pairs = decode_work(spec, w["row_pos"], w["attn_pos"], w["tail_start"])
@@ -352,15 +369,29 @@ def bench_decode(spec, steps, warmup, cpu_baseline, copies=3, keys="bf16", w=Non
     res = {"workload": spec.name, "value": rows / (ms * 1e-3), "unit": "query rows/s", "ms_per_step": ms,
            "kernels": kernels, "roofline": roofline_for(dom, work[dom], kt[dom][1], tr),
            "rooflines": {n: roofline_for(n, work[n], kt[n][1], tr) for n in kt if n in work}}
-    if not fp8:
+    if not fp8 and not fp8kv:
         res["pool_append"] = bench_pool_append(spec)
-    if not fp8 and spec.draft:
+    if not fp8 and not fp8kv and spec.draft:
         res["draft_loop"] = bench_draft_loop(spec, iq, seq, apos, pooled, kcs, vcs, q, ts, max_nb, ws,
                                              max(steps, 10), warmup)
-    if cpu_baseline and not fp8:
+    if cpu_baseline and not fp8 and not fp8kv:
         res["cpu_baseline"] = cpu_decode(spec, w, pooled_h)
     res["_inputs"] = w
     return res
+
+
+def quantize_kv(x):
+    """bf16 cache on the device -> (E4M3 codes as uint8, per-tensor scale
+    amax / 448), converted by torch's float8_e4m3fn (OCP E4M3, nearest-even)."""
+    import torch
+    amax = float(x.abs().max().float().item())
+    scale = amax / 448.0
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    flat_x, flat_c = x.view(-1), codes.view(-1)
+    step = 1 << 28                                  # bounded fp32 temporaries
+    for i in range(0, flat_x.numel(), step):
+        flat_c[i:i + step] = (flat_x[i:i + step].float() / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
 
 
 def serving_shape_inputs(spec, w, Hq=24, Hkv=2, D=256, seed=2024):
@@ -490,7 +521,8 @@ KERNEL_SOURCE = {"pool_rope": "pool.hip", "pool_append": "pool.hip", "rope_query
                  "sample_threshold": "score_fused.hip", "score_filter": "score_fused.hip",
                  "select_merge": "score_fused.hip", "attn_prefill_mfma": "attn_mfma.hip",
                  "attn_decode_mfma": "attn_mfma.hip", "attn_prefill_mfma_d256": "attn_mfma.hip",
-                 "attn_decode_mfma_d256": "attn_mfma.hip", "attn_prefill": "attn.hip", "attn_decode": "attn.hip",
+                 "attn_decode_mfma_d256": "attn_mfma.hip", "attn_prefill_mfma_fp8kv": "attn_mfma.hip",
+                 "attn_decode_mfma_fp8kv": "attn_mfma.hip", "attn_prefill": "attn.hip", "attn_decode": "attn.hip",
                  "attn_combine": "attn.hip", "pool_rope_fp8": "pool.hip", "score_rows_fp8": "score.hip",
                  "score_sample_fp8": "score_fused.hip", "score_filter_fp8": "score_fused.hip"}
 COPY_BYTES = 1 << 30
@@ -519,8 +551,8 @@ def short_kernel_name(full):
         return "attn_combine"
     if base in ("score_sample_kernel", "score_filter_kernel") and tmpl.startswith("<true"):
         return base[:-7] + "_fp8"   # the FP8-key instance
-    if base in ("attn_prefill_mfma_kernel", "attn_decode_mfma_kernel") and tmpl.startswith("<256"):
-        return base[:-7] + "_d256"  # the head-dim-256 instance
+    if base in ("attn_prefill_mfma_kernel", "attn_decode_mfma_kernel"):  # <head dim, K/V element>
+        return base[:-7] + ("_d256" if tmpl.startswith("<256") else "") + ("_fp8kv" if "char" in tmpl else "")
     return base[:-7] if base.endswith("_kernel") else base
 
 
@@ -673,11 +705,16 @@ def main():
         else:
             serve_res[spec.name] = bench_decode(s2, args.steps * 10, args.warmup, False, w=w2)
         del w2
+    fp8kv_res = {}
     if args.fp8 and spec.dtype == "bf16":
         if spec.kind == "prefill":
             fp8_res[spec.name] = bench_prefill(spec, args.steps, args.warmup, False, keys="fp8", w=pre["_inputs"])
+            fp8kv_res[spec.name] = bench_prefill(spec, args.steps, args.warmup, False, keys="fp8", kv="fp8",
+                                                 w=pre["_inputs"])
         else:
             fp8_res[spec.name] = bench_decode(spec, args.steps * 10, args.warmup, False, keys="fp8", w=pre["_inputs"])
+            fp8kv_res[spec.name] = bench_decode(spec, args.steps * 10, args.warmup, False, keys="fp8", kv="fp8",
+                                                w=pre["_inputs"])
     pre.pop("_inputs", None)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1, "steps": args.steps,
@@ -697,6 +734,8 @@ def main():
         if args.fp8 and dspec.dtype == "bf16":
             fp8_res[dspec.name] = bench_decode(dspec, args.steps * 10, args.warmup, False, keys="fp8",
                                                w=dec["_inputs"])
+            fp8kv_res[dspec.name] = bench_decode(dspec, args.steps * 10, args.warmup, False, keys="fp8", kv="fp8",
+                                                 w=dec["_inputs"])
         if args.serving and dspec.dtype == "bf16":
             s2, w2 = serving_shape_inputs(dspec, dec["_inputs"])
             serve_res[dspec.name] = bench_decode(s2, args.steps * 10, args.warmup, False, w=w2)
@@ -716,6 +755,16 @@ def main():
                                       "unit": "tokens/s" if "workload" not in r else r["unit"],
                                       "ms_per_step": round(r["ms_per_step"], 4), "kernels": r["kernels"],
                                       "roofline": r["roofline"]}
+    if fp8kv_res:
+        # FP8 index keys and an FP8 K/V cache (E4M3, one scale per tensor)
+        line["fp8_keys_kv"] = {}
+        for name, r in fp8kv_res.items():
+            r.pop("_inputs", None)
+            line["fp8_keys_kv"][name] = {"value": round(r["value"], 1),
+                                         "unit": "tokens/s" if "workload" not in r else r["unit"],
+                                         "ms_per_step": round(r["ms_per_step"], 4), "kernels": r["kernels"],
+                                         "rooflines": {n: v for n, v in r["rooflines"].items()
+                                                       if n.startswith("attn")}}
     if serve_res:
         # the same workloads with attention at the serving head layout (24
         # query heads, 2 KV heads, head dim 256); index side unchanged
