@@ -121,25 +121,28 @@ void launch_select_rows(const float *scores, int64_t sc_stride, const int32_t *r
 // Few rows, many blocks: the selection split over many workgroups.
 //   - the scorer has filled the row's 12-bit key histogram;
 //   - collect (grid: chunks of 4096 blocks x rows): every workgroup finds the
-//     bin b* holding the k-th best key, then appends the blocks of its chunk
-//     above b* to the row's "sure" list and those inside b* to its candidate
-//     list;
+//     bin b* holding the k-th best key, gathers the blocks of its chunk above
+//     b* ("sure") and inside b* (candidates) in LDS, then reserves room in
+//     the row's two global lists with one atomic each and copies them out;
 //   - final (one workgroup per row, a second launch): picks the missing
 //     `need` entries among the candidates with a radix select on the unique
 //     composite (low 20 key bits, ~block) -- a higher score first, then the
 //     lower block -- and writes the kept set sorted by block id.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void wave_append(bool pred, uint2 item, uint32_t *counter, uint2 *list)
+// Append the wave's `pred` items to an LDS list (slot `base + i`, or
+// `base - i` when `down`): one LDS atomic per wave.
+__device__ __forceinline__ void wave_append_lds(bool pred, uint2 item, uint32_t *counter, uint2 *list, uint32_t base,
+                                                bool down)
 {
     const uint64_t mask = __ballot(pred);
     if (!mask) return;
     const int lane = threadIdx.x & 63;
     const uint32_t n = (uint32_t)__popcll(mask);
     const int leader = __ffsll((unsigned long long)mask) - 1;
-    uint32_t base = 0;
-    if (lane == leader) base = atomicAdd(counter, n);
-    base = __shfl(base, leader);
-    if (pred) list[base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull))] = item;
+    uint32_t off = 0;
+    if (lane == leader) off = atomicAdd(counter, n);
+    off = __shfl(off, leader) + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+    if (pred) list[down ? base - off : base + off] = item;
 }
 
 __device__ __forceinline__ uint64_t composite20(uint2 e)
@@ -186,6 +189,10 @@ __global__ __launch_bounds__(kSplitThreads) void select_collect_kernel(
 {
     __shared__ uint32_t wtot[kSplitThreads / kWave];
     __shared__ uint32_t s_bin, s_above;
+    // the chunk's sure entries grow from the front, its candidates from the
+    // back: together at most one per block of the chunk
+    __shared__ uint2 st[kCollectChunk];
+    __shared__ uint32_t s_n[2], s_base[2];
     const int t = threadIdx.x;
     const int64_t r = blockIdx.y;
     const int32_t nc = (int32_t)min(visible_blocks(row_pos[r]), (int64_t)max_nb);
@@ -208,6 +215,7 @@ __global__ __launch_bounds__(kSplitThreads) void select_collect_kernel(
         return;
     }
     if (b_begin >= nc) return;
+    if (t < 2) s_n[t] = 0u;
     // ---- collect ----
     // the whole chunk in flight at once, issued before the histogram search:
     // thread t holds blocks b_begin + 1024*j + 4*t + i (rows are padded to 64
@@ -231,10 +239,17 @@ __global__ __launch_bounds__(kSplitThreads) void select_collect_kernel(
             const uint32_t key = valid ? score_key(e[i]) : 0u;
             const uint32_t bin = key >> kHistShift;
             const uint2 item = make_uint2(key, (uint32_t)b);
-            wave_append(valid && bin > beta, item, &cnt[0], sure);
-            wave_append(valid && bin == beta, item, &cnt[1], cand);
+            wave_append_lds(valid && bin > beta, item, &s_n[0], st, 0u, false);
+            wave_append_lds(valid && bin == beta, item, &s_n[1], st, kCollectChunk - 1u, true);
         }
     }
+    __syncthreads();
+    const uint32_t n_sure = s_n[0], n_cand = s_n[1];
+    if (t == 0) s_base[0] = n_sure ? atomicAdd(&cnt[0], n_sure) : 0u;
+    if (t == kWave) s_base[1] = n_cand ? atomicAdd(&cnt[1], n_cand) : 0u;
+    __syncthreads();
+    for (uint32_t i = t; i < n_sure; i += kSplitThreads) sure[s_base[0] + i] = st[i];
+    for (uint32_t i = t; i < n_cand; i += kSplitThreads) cand[s_base[1] + i] = st[kCollectChunk - 1u - i];
 }
 
 // One workgroup per row: picks the missing `need` entries among the row's
