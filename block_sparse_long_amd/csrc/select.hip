@@ -324,14 +324,26 @@ __global__ __launch_bounds__(kSplitThreads) void select_final_kernel(
     // ---- kept set: the sure entries and the picked candidates ----
     if (t == 0) s_fill = 0;
     __syncthreads();
+    // one LDS atomic per wave and pass (the ballot gives each lane its slot)
+    auto keep = [&](bool pred, uint2 e) {
+        const uint64_t mask = __ballot(pred);
+        if (!mask) return;
+        const int lane = t & (kWave - 1);
+        const int leader = __ffsll((unsigned long long)mask) - 1;
+        uint32_t off = 0;
+        if (lane == leader) off = atomicAdd(&s_fill, (uint32_t)__popcll(mask));
+        off = __shfl(off, leader) + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+        if (pred) buf[off] = ((uint64_t)e.y << 32) | e.x;
+    };
 #pragma unroll
     for (int j = 0; j < kSurePer; ++j) {
         const uint32_t i = (uint32_t)(t + j * kSplitThreads);
-        if (i < n_sure) buf[atomicAdd(&s_fill, 1u)] = ((uint64_t)sure_r[j].y << 32) | sure_r[j].x;
+        keep(i < n_sure, sure_r[j]);
     }
-    for (uint32_t i = t; i < n_cand; i += kSplitThreads) {
-        const uint2 e = cl[i];
-        if ((composite20(e) & pmask) >= prefix) buf[atomicAdd(&s_fill, 1u)] = ((uint64_t)e.y << 32) | e.x;
+    for (uint32_t i0 = 0; i0 < n_cand; i0 += kSplitThreads) {
+        const uint32_t i = i0 + t;
+        const uint2 e = i < n_cand ? cl[i] : make_uint2(0u, 0u);
+        keep(i < n_cand && (composite20(e) & pmask) >= prefix, e);
     }
     __syncthreads();
     const uint32_t n = min(s_fill, (uint32_t)kk);
@@ -350,15 +362,24 @@ __global__ __launch_bounds__(kSplitThreads) void select_final_kernel(
             if (b >= 0 && b < 32 * (int64_t)nwords) atomicOr(&bm[emit_slot((int)(b >> 5))], 1u << (b & 31));
         }
         __syncthreads();
+        // the thread's run of words, read once into registers (all reads in
+        // flight together), counted, then emitted from the registers
+        constexpr int kPerMax = kEmitWords / kSplitThreads;
         const int per = (nwords + kSplitThreads - 1) / kSplitThreads;
         const int i0 = min(nwords, t * per), i1 = min(nwords, i0 + per);
+        uint32_t words[kPerMax];
+#pragma unroll
+        for (int j = 0; j < kPerMax; ++j) words[j] = i0 + j < i1 ? bm[emit_slot(i0 + j)] : 0u;
         uint32_t c = 0;
-        for (int i = i0; i < i1; ++i) c += (uint32_t)__popc(bm[emit_slot(i)]);
+#pragma unroll
+        for (int j = 0; j < kPerMax; ++j) c += (uint32_t)__popc(words[j]);
         const uint32_t incl = wg_inclusive_scan<kSplitThreads>(c, wtot);
         if (t == kSplitThreads - 1) s_total = incl;
         uint32_t pos = out_base + incl - c;
-        for (int i = i0; i < i1; ++i) {
-            uint32_t word = bm[emit_slot(i)];
+#pragma unroll
+        for (int j = 0; j < kPerMax; ++j) {
+            const int i = i0 + j;
+            uint32_t word = words[j];
             while (word) {
                 const int bit = __ffs(word) - 1;
                 word &= word - 1u;
