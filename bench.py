@@ -458,6 +458,99 @@ def bench_draft_loop(spec, iq, seq, apos, pooled, kcs, vcs, q, ts, max_nb, ws, s
             "kernels": {n: {"launches_per_loop": c / 5, "avg_us": round(a * 1e3, 2)} for n, (c, a, _) in kt.items()}}
 
 
+def paged_layout(spec, page_tokens, seed=77):
+    """A shuffled page table for the workload's sequences (synth.page_table)
+    and, on the device, the slot of every token and the key slot of every
+    block: token p of sequence s -> table[s][p / P] * P + p % P; block b ->
+    slot(4b) / 4."""
+    import torch
+    from block_sparse_long_amd import synth
+    rng = np.random.default_rng(seed)
+    table_h = synth.page_table(rng, spec.batch, spec.kv_len, page_tokens=page_tokens, spare_pages=spec.batch)
+    table = torch.from_numpy(table_h).cuda()
+    P, bpp = page_tokens, page_tokens // 4
+    n_pages = int(table_h.max()) + 1
+    p = torch.arange(spec.kv_len, device="cuda")
+    tok_slot = table[:, p // P].long() * P + p % P                          # [B][kv_len]
+    b = torch.arange(spec.n_blocks, device="cuda")
+    key_slot = table[:, b // bpp].long() * bpp + b % bpp                   # [B][n_blocks]
+    return table, n_pages, tok_slot, key_slot
+
+
+def scatter_rows(x, slots, n_slots):
+    """[B][n][...] -> [n_slots][...] with row (s, i) at slots[s][i]."""
+    import torch
+    out = torch.zeros((n_slots,) + tuple(x.shape[2:]), dtype=x.dtype, device=x.device)
+    out.index_copy_(0, slots.reshape(-1), x.reshape((-1,) + tuple(x.shape[2:])))
+    return out
+
+
+def bench_paged(spec, w, steps, warmup, page_tokens=16):
+    """The workload with the compressed keys and the K/V in a paged pool of
+    page_tokens-token pages (qsa_*_paged): prefill pools the chunk's blocks
+    straight into the pool, then scores and attends through the table; decode
+    scores and attends through it.  Same inputs as the contiguous run."""
+    import torch
+    from block_sparse_long_amd import qsa
+    table, n_pages, tok_slot, key_slot = paged_layout(spec, page_tokens)
+    P, k = page_tokens, spec.top_k
+    raw = to_dev(w["raw_keys"])
+    B, nb = spec.batch, spec.n_blocks
+    kp = scatter_rows(to_dev(w["k_cache"]), tok_slot, n_pages * P)
+    vp = scatter_rows(to_dev(w["v_cache"]), tok_slot, n_pages * P)
+    keys = torch.zeros((n_pages * P // 4, DIM), dtype=raw.dtype, device="cuda")
+    iq, seq, pos = to_dev(w["idx_q"]), to_dev(w["row_seq"]), to_dev(w["row_pos"])
+    q = to_dev(w["q"])
+    dcode = qsa.BF16 if spec.dtype == "bf16" else qsa.F32
+    R = iq.shape[0]
+    max_nb = int(visible(w["row_pos"]).max())
+    sel = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((R,), dtype=torch.int32, device="cuda")
+    ws = torch.empty((max(qsa.score_topk_workspace_size(R, max_nb, k, dcode), 256),), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(q)
+    if spec.kind == "prefill":
+        first_new = (spec.ctx - spec.chunk) // 4
+        if first_new > 0:  # the context before the chunk, pooled before timing
+            qsa.pool_index_keys_paged(raw, table, P, 0, first_new, spec.theta, pooled=keys)
+        lse = torch.empty((R, spec.Hq), dtype=torch.float32, device="cuda")
+
+        def step(_i):
+            qsa.pool_index_keys_paged(raw, table, P, first_new, nb, spec.theta, pooled=keys)
+            qsa.score_topk_paged(iq, seq, pos, table, P, max_nb, k, spec.theta, pooled=keys, sel_blocks=sel,
+                                 sel_count=cnt, workspace=ws, want_scores=False)
+            qsa.sparse_attn_prefill_paged(q, seq, pos, kp, vp, table, P, sel, cnt, out=out, lse=lse)
+        rows = R
+    else:
+        qsa.pool_index_keys_paged(raw, table, P, 0, nb, spec.theta, pooled=keys)
+        # three copies of the pools, used in turn (as in bench_decode): the
+        # 268 MB of compressed keys would otherwise partly stay in the 256 MB
+        # Infinity Cache between steps
+        keys_c = [keys] + [keys.clone() for _ in range(2)]
+        kp_c = [kp] + [kp.clone() for _ in range(2)]
+        vp_c = [vp] + [vp.clone() for _ in range(2)]
+        rpos = to_dev(w["attn_pos"])
+        ts = None if w["tail_start"] is None else to_dev(w["tail_start"])
+        lse = torch.empty((B, spec.q_per_seq, spec.Hq), dtype=torch.float32, device="cuda")
+        wsa = torch.empty((max(qsa.sparse_attn_decode_workspace_size(B, spec.q_per_seq, spec.Hq, spec.D, k), 256),),
+                          dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            c = i % 3
+            qsa.score_topk_paged(iq, seq, pos, table, P, max_nb, k, spec.theta, pooled=keys_c[c], sel_blocks=sel,
+                                 sel_count=cnt, workspace=ws, want_scores=False)
+            qsa.sparse_attn_decode_paged(q, rpos, kp_c[c], vp_c[c], table, P, sel, cnt, ts, out=out, lse=lse,
+                                         workspace=wsa)
+        rows = B * spec.q_per_seq
+    ms = timed(step, steps, warmup)
+    log(f"{spec.name} (paged pool, {P}-token pages): {ms:.3f} ms/step")
+    nprof = max(3, min(steps, 10))
+    kt = kernel_times(step, nprof, ALL_KERNELS)
+    return {"page_tokens": P, "value": round(rows / (ms * 1e-3), 1),
+            "unit": "tokens/s" if spec.kind == "prefill" else "query rows/s", "ms_per_step": round(ms, 4),
+            "kernels": {n: {"launches_per_step": c / nprof, "avg_us": round(a * 1e3, 2)} for n, (c, a, _) in kt.items()}}
+
+
 def bench_pool_append(spec, launches=50):
     """Incremental decode pooling for the workload's batch: every launch
     completes a block for every request (the costlier case), with the
@@ -664,6 +757,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", dest="fp8", action="store_false",
                     help="skip the extra runs with FP8 index keys")
+    ap.add_argument("--no-paged", dest="paged", action="store_false",
+                    help="skip the extra runs on a paged pool")
     ap.add_argument("--no-serving-shape", dest="serving", action="store_false",
                     help="skip the extra runs with attention at 24 q / 2 KV heads, head dim 256")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -697,7 +792,10 @@ def main():
         pre = bench_decode(spec, args.steps * 10, args.warmup, cpu)
         value, unit, ms = pre["value"], pre["unit"], pre["ms_per_step"]
         main_res = pre
-    fp8_res, serve_res = {}, {}
+    fp8_res, serve_res, paged_res = {}, {}, {}
+    if args.paged:
+        paged_res[spec.name] = bench_paged(spec, pre["_inputs"], args.steps if spec.kind == "prefill" else
+                                           args.steps * 10, args.warmup)
     if args.serving and spec.dtype == "bf16":
         s2, w2 = serving_shape_inputs(spec, pre["_inputs"])
         if spec.kind == "prefill":
@@ -736,6 +834,8 @@ def main():
                                                w=dec["_inputs"])
             fp8kv_res[dspec.name] = bench_decode(dspec, args.steps * 10, args.warmup, False, keys="fp8", kv="fp8",
                                                  w=dec["_inputs"])
+        if args.paged:
+            paged_res[dspec.name] = bench_paged(dspec, dec["_inputs"], args.steps * 10, args.warmup)
         if args.serving and dspec.dtype == "bf16":
             s2, w2 = serving_shape_inputs(dspec, dec["_inputs"])
             serve_res[dspec.name] = bench_decode(s2, args.steps * 10, args.warmup, False, w=w2)
@@ -765,6 +865,9 @@ def main():
                                          "ms_per_step": round(r["ms_per_step"], 4), "kernels": r["kernels"],
                                          "rooflines": {n: v for n, v in r["rooflines"].items()
                                                        if n.startswith("attn")}}
+    if paged_res:
+        # the same workloads on a paged pool (compressed keys and K/V)
+        line["paged_pool"] = paged_res
     if serve_res:
         # the same workloads with attention at the serving head layout (24
         # query heads, 2 KV heads, head dim 256); index side unchanged

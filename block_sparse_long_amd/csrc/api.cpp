@@ -207,8 +207,8 @@ qsa_status_t qsa_pool_index_keys(const void *raw_keys, int64_t raw_seq_stride, v
     if (batch > 1 && (raw_seq_stride < (int64_t)kBlock * block_end * kDim || pooled_seq_stride < (int64_t)block_end * kDim))
         return QSA_ERR_INVALID_ARG;
     clear_launch_err();
-    launch_pool(raw_keys, raw_seq_stride, pooled, pooled_seq_stride, batch, block_begin, block_end, rope_theta, flags,
-                dtype == QSA_BF16, (hipStream_t)stream);
+    launch_pool(raw_keys, raw_seq_stride, pooled, pooled_seq_stride, KeyPages{nullptr, 0, 0}, batch, block_begin,
+                block_end, rope_theta, flags, dtype == QSA_BF16, (hipStream_t)stream);
     return launch_status();
 }
 
@@ -227,8 +227,38 @@ qsa_status_t qsa_pool_index_keys_fp8(const void *raw_keys, int64_t raw_seq_strid
     if (batch > 1 && (raw_seq_stride < (int64_t)kBlock * block_end * kDim || pooled_seq_stride < (int64_t)block_end))
         return QSA_ERR_INVALID_ARG;
     clear_launch_err();
-    launch_pool_fp8(raw_keys, raw_seq_stride, codes, scales, pooled_seq_stride, batch, block_begin, block_end,
-                    rope_theta, flags, raw_dtype == QSA_BF16, (hipStream_t)stream);
+    launch_pool_fp8(raw_keys, raw_seq_stride, codes, scales, pooled_seq_stride, KeyPages{nullptr, 0, 0}, batch,
+                    block_begin, block_end, rope_theta, flags, raw_dtype == QSA_BF16, (hipStream_t)stream);
+    return launch_status();
+}
+
+qsa_status_t qsa_pool_index_keys_paged(const void *raw_keys, int64_t raw_seq_stride, void *pooled, uint8_t *codes,
+                                       float *scales, const int32_t *page_table, int64_t page_table_stride,
+                                       int32_t page_tokens, int32_t batch, int32_t block_begin, int32_t block_end,
+                                       double rope_theta, uint32_t flags, qsa_dtype_t raw_dtype, void *stream)
+{
+    const bool fp8 = codes != nullptr;
+    if (!dtype_ok(raw_dtype)) return QSA_ERR_UNSUPPORTED;
+    if (batch < 0 || block_begin < 0 || block_end < block_begin) return QSA_ERR_INVALID_ARG;
+    if (flags & ~(uint32_t)(QSA_FLAG_NO_ROPE | QSA_FLAG_POOL_RMSNORM)) return QSA_ERR_INVALID_ARG;
+    if (!(flags & QSA_FLAG_NO_ROPE) && !(rope_theta > 1.0 && std::isfinite(rope_theta))) return QSA_ERR_INVALID_ARG;
+    if (page_tokens < kBlock || page_tokens % kBlock || page_table_stride < 0) return QSA_ERR_INVALID_ARG;
+    if (batch == 0 || block_end == block_begin) return QSA_OK;
+    if (!aligned16(raw_keys) || raw_seq_stride % 8 || !page_table) return QSA_ERR_INVALID_ARG;
+    if (fp8 ? (!aligned16(codes) || !scales || (reinterpret_cast<uintptr_t>(scales) & 3u) || pooled)
+            : (!aligned16(pooled) || scales))
+        return QSA_ERR_INVALID_ARG;
+    if (batch > 1 && raw_seq_stride < (int64_t)kBlock * block_end * kDim) return QSA_ERR_INVALID_ARG;
+    const int32_t bpp = page_tokens / kBlock;
+    if ((int64_t)block_end > page_table_stride * bpp) return QSA_ERR_INVALID_ARG;  // the table covers the blocks
+    const KeyPages kp{page_table, page_table_stride, bpp};
+    clear_launch_err();
+    if (fp8)
+        launch_pool_fp8(raw_keys, raw_seq_stride, codes, scales, 0, kp, batch, block_begin, block_end, rope_theta,
+                        flags, raw_dtype == QSA_BF16, (hipStream_t)stream);
+    else
+        launch_pool(raw_keys, raw_seq_stride, pooled, 0, kp, batch, block_begin, block_end, rope_theta, flags,
+                    raw_dtype == QSA_BF16, (hipStream_t)stream);
     return launch_status();
 }
 

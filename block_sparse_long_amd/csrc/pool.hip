@@ -31,10 +31,11 @@ static RopeFreq rope_freq(double theta)
 
 // One wave per pooled block: lane j owns the rotary pair (j, j + 64).  The
 // wave reads the block's 4 tokens x 128 dims (contiguous in memory) with 8
-// coalesced loads.
+// coalesced loads.  The key goes to block b of its sequence, contiguous or
+// through the page table of a paged compressed-key pool.
 template <typename T>
 __global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ raw, int64_t raw_stride,
-                                                        T *__restrict__ pooled, int64_t pooled_stride,
+                                                        T *__restrict__ pooled, int64_t pooled_stride, KeyPages kp,
                                                         int64_t total, int32_t nblk, int32_t block_begin,
                                                         RopeFreq rf, uint32_t flags)
 {
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ ra
         dy *= inv;
     }
     if (!(flags & kFlagNoRope)) rope_pair(dx, dy, kBlock * b, rf.f[lane]);
-    T *dst = pooled + s * pooled_stride + b * kDim;
+    T *dst = pooled + key_offset(kp, pooled_stride, s, b);
     store_f64(dst + lane, dx);
     store_f64(dst + kHalf + lane, dy);
 }
@@ -75,8 +76,9 @@ __global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ ra
 template <typename T>
 __global__ __launch_bounds__(256) void pool_rope_fp8_kernel(const T *__restrict__ raw, int64_t raw_stride,
                                                             uint8_t *__restrict__ codes, float *__restrict__ scales,
-                                                            int64_t pooled_stride, int64_t total, int32_t nblk,
-                                                            int32_t block_begin, RopeFreq rf, uint32_t flags)
+                                                            int64_t pooled_stride, KeyPages kp, int64_t total,
+                                                            int32_t nblk, int32_t block_begin, RopeFreq rf,
+                                                            uint32_t flags)
 {
     const int lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void pool_rope_fp8_kernel(const T *__restrict_
     const float amax = wave_max(fmaxf(fabsf(fx), fabsf(fy)));
     const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
     const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fx * inv, fy * inv, 0, false);
-    const int64_t slot = s * pooled_stride + b;
+    const int64_t slot = key_index(kp, pooled_stride, s, b);
     codes[slot * kDim + lane] = (uint8_t)(pk & 0xffu);
     codes[slot * kDim + kHalf + lane] = (uint8_t)((pk >> 8) & 0xffu);
     if (lane == 0) scales[slot] = amax / 448.0f;
@@ -214,8 +216,8 @@ void launch_pool_append(const void *new_keys, const int32_t *positions, const in
                    positions, full_slots, (float *)ring, (float *)compressed, batch, rf, flags);
 }
 
-void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pooled_stride, int32_t batch,
-                 int32_t block_begin, int32_t block_end, double theta, uint32_t flags, bool bf16,
+void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pooled_stride, const KeyPages &kp,
+                 int32_t batch, int32_t block_begin, int32_t block_end, double theta, uint32_t flags, bool bf16,
                  hipStream_t stream)
 {
     const int32_t nblk = block_end - block_begin;
@@ -224,15 +226,15 @@ void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pool
     const RopeFreq rf = rope_freq(theta);
     if (bf16)
         QSA_LAUNCH("pool_rope", (pool_rope_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)raw,
-                   raw_stride, (bf16_t *)pooled, pooled_stride, total, nblk, block_begin, rf, flags);
+                   raw_stride, (bf16_t *)pooled, pooled_stride, kp, total, nblk, block_begin, rf, flags);
     else
         QSA_LAUNCH("pool_rope", (pool_rope_kernel<float>), grid, block, 0, stream, (const float *)raw, raw_stride,
-                   (float *)pooled, pooled_stride, total, nblk, block_begin, rf, flags);
+                   (float *)pooled, pooled_stride, kp, total, nblk, block_begin, rf, flags);
 }
 
 void launch_pool_fp8(const void *raw, int64_t raw_stride, uint8_t *codes, float *scales, int64_t pooled_stride,
-                     int32_t batch, int32_t block_begin, int32_t block_end, double theta, uint32_t flags,
-                     bool bf16_raw, hipStream_t stream)
+                     const KeyPages &kp, int32_t batch, int32_t block_begin, int32_t block_end, double theta,
+                     uint32_t flags, bool bf16_raw, hipStream_t stream)
 {
     const int32_t nblk = block_end - block_begin;
     const int64_t total = (int64_t)batch * nblk;
@@ -240,10 +242,10 @@ void launch_pool_fp8(const void *raw, int64_t raw_stride, uint8_t *codes, float 
     const RopeFreq rf = rope_freq(theta);
     if (bf16_raw)
         QSA_LAUNCH("pool_rope_fp8", (pool_rope_fp8_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)raw,
-                   raw_stride, codes, scales, pooled_stride, total, nblk, block_begin, rf, flags);
+                   raw_stride, codes, scales, pooled_stride, kp, total, nblk, block_begin, rf, flags);
     else
         QSA_LAUNCH("pool_rope_fp8", (pool_rope_fp8_kernel<float>), grid, block, 0, stream, (const float *)raw,
-                   raw_stride, codes, scales, pooled_stride, total, nblk, block_begin, rf, flags);
+                   raw_stride, codes, scales, pooled_stride, kp, total, nblk, block_begin, rf, flags);
 }
 
 void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,

@@ -24,22 +24,7 @@ void prof_begin(const char *name, hipStream_t stream);
 void prof_end(hipStream_t stream);
 void note_launch(hipError_t err);
 
-// ---- pool.hip ---------------------------------------------------------------
-void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pooled_stride, int32_t batch,
-                 int32_t block_begin, int32_t block_end, double theta, uint32_t flags, bool bf16,
-                 hipStream_t stream);
-void launch_pool_fp8(const void *raw, int64_t raw_stride, uint8_t *codes, float *scales, int64_t pooled_stride,
-                     int32_t batch, int32_t block_begin, int32_t block_end, double theta, uint32_t flags,
-                     bool bf16_raw, hipStream_t stream);
-void launch_pool_append(const void *new_keys, const int32_t *positions, const int64_t *full_slots, void *ring,
-                        void *compressed, int32_t batch, double theta, uint32_t flags, bool bf16, hipStream_t stream);
-void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,
-                       uint32_t flags, bool bf16, uint32_t *zero, int64_t zero_per_row, hipStream_t stream);
-
-// ---- score.hip --------------------------------------------------------------
-// Select histogram: 4096 bins of the top 12 bits of a score's order key.
-constexpr int kHistBins = 4096;
-constexpr int kHistShift = 20;
+// ---- paged compressed keys (pool.hip, score.hip, score_fused.hip) -----------
 // Paged compressed keys (table null: contiguous per sequence).  The KV pool
 // keeps one compressed key per 4 token slots, at full_slot / 4; with pages of
 // page_tokens slots (a multiple of 4), block b of sequence s is key
@@ -49,6 +34,23 @@ struct KeyPages {
     int64_t stride;
     int32_t bpp;
 };
+
+// ---- pool.hip ---------------------------------------------------------------
+void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pooled_stride, const KeyPages &kp,
+                 int32_t batch, int32_t block_begin, int32_t block_end, double theta, uint32_t flags, bool bf16,
+                 hipStream_t stream);
+void launch_pool_fp8(const void *raw, int64_t raw_stride, uint8_t *codes, float *scales, int64_t pooled_stride,
+                     const KeyPages &kp, int32_t batch, int32_t block_begin, int32_t block_end, double theta,
+                     uint32_t flags, bool bf16_raw, hipStream_t stream);
+void launch_pool_append(const void *new_keys, const int32_t *positions, const int64_t *full_slots, void *ring,
+                        void *compressed, int32_t batch, double theta, uint32_t flags, bool bf16, hipStream_t stream);
+void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,
+                       uint32_t flags, bool bf16, uint32_t *zero, int64_t zero_per_row, hipStream_t stream);
+
+// ---- score.hip --------------------------------------------------------------
+// Select histogram: 4096 bins of the top 12 bits of a score's order key.
+constexpr int kHistBins = 4096;
+constexpr int kHistShift = 20;
 void launch_score_rows(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
                        const void *pooled, int64_t pooled_stride, const KeyPages &kp, int32_t max_nb, float *scores,
                        int64_t sc_stride, uint32_t *hist, bool bf16, hipStream_t stream);

@@ -27,6 +27,30 @@ __device__ __forceinline__ float relu_sum4(f32x4_t a)
 
 // Per-row histogram of the score keys' top 12 bits: counted in LDS, then
 // added to the row's global histogram (only the non-empty bins).
+// Paged pools: the table entries of a lane's 4 keys of a step (block
+// min(base + 4m + nt, b_end - 1)), read one step ahead of the keys, so a key
+// load never waits for its table entry.  Contiguous keys read no table.
+struct PageAhead {
+    int32_t pg[4];
+};
+__device__ __forceinline__ void page_ahead(const KeyPages &kp, int64_t seq, int64_t base, int m, int64_t b_end,
+                                           PageAhead &p)
+{
+    if (!kp.table) return;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const uint32_t b = (uint32_t)min(base + 4 * m + nt, b_end - 1);
+        p.pg[nt] = kp.table[seq * kp.stride + b / (uint32_t)kp.bpp];
+    }
+}
+// Key number of block b given its table entry (as key_index).
+__device__ __forceinline__ int64_t key_at(const KeyPages &kp, int64_t keys_per_seq, int64_t seq, int64_t b,
+                                          int32_t pg)
+{
+    if (!kp.table) return seq * keys_per_seq + b;
+    return (int64_t)pg * kp.bpp + (int64_t)((uint32_t)b % (uint32_t)kp.bpp);
+}
+
 __device__ __forceinline__ void hist_clear(uint32_t *lhist)
 {
     for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lhist[i] = 0u;
@@ -69,18 +93,23 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
     // step's MFMAs.  Every load is issued unconditionally (addresses are
     // clamped to the last visible block), so the wait before each MFMA counts
     // only the loads it needs and never drains the prefetch.
-    auto load = [&](int64_t base, uint4 (&v)[4][4]) {
+    auto load = [&](int64_t base, const PageAhead &p, uint4 (&v)[4][4]) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const int64_t b = min(base + 4 * m + nt, b_end - 1);  // clamp: stays inside the visible range
-            const uint4 *src = (const uint4 *)(pooled + key_offset(kp, pooled_stride, seq, b) + 32 * g);
+            const int64_t off = kp.table ? key_at(kp, 0, seq, b, p.pg[nt]) * kDim : seq * pooled_stride + b * kDim;
+            const uint4 *src = (const uint4 *)(pooled + off + 32 * g);
 #pragma unroll
             for (int s = 0; s < 4; ++s) v[nt][s] = src[s];
         }
     };
     uint4 v0[4][4], v1[4][4];
+    PageAhead p0{}, p1{};  // table entries of the next v0 / v1 loads
     int64_t base = b_begin + wave * 64;
-    load(base, v0);
+    page_ahead(kp, seq, base, m, b_end, p0);
+    load(base, p0, v0);
+    page_ahead(kp, seq, base + 256, m, b_end, p1);
+    page_ahead(kp, seq, base + 512, m, b_end, p0);
     if (hist) hist_clear(lhist);
     bf16x8_t a[4];
 #pragma unroll
@@ -116,10 +145,12 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
     // block; a second step past the end only re-reads the clamped last block
     // and stores nothing.
     for (; base < b_end; base += 512) {
-        load(base + 256, v1);
+        load(base + 256, p1, v1);
+        page_ahead(kp, seq, base + 768, m, b_end, p1);
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the MFMAs
         score(base, v0);
-        load(base + 512, v0);
+        load(base + 512, p0, v0);
+        page_ahead(kp, seq, base + 1024, m, b_end, p0);
         __builtin_amdgcn_sched_barrier(0);
         score(base + 256, v1);
     }
@@ -156,10 +187,10 @@ __global__ __launch_bounds__(256) void score_rows_fp8_kernel(
         uint4 c[4][2];
         float sc[4];
     };
-    auto load = [&](int64_t base, Step &v) {
+    auto load = [&](int64_t base, const PageAhead &p, Step &v) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            const int64_t key = key_index(kp, pooled_stride, seq, min(base + 4 * m + nt, b_end - 1));
+            const int64_t key = key_at(kp, pooled_stride, seq, min(base + 4 * m + nt, b_end - 1), p.pg[nt]);
             const uint4 *src = (const uint4 *)(codes + key * kDim + 32 * g);
             v.c[nt][0] = src[0];
             v.c[nt][1] = src[1];
@@ -167,8 +198,12 @@ __global__ __launch_bounds__(256) void score_rows_fp8_kernel(
         }
     };
     Step v0, v1;
+    PageAhead p0{}, p1{};  // table entries of the next v0 / v1 loads
     int64_t base = b_begin + wave * 64;
-    load(base, v0);
+    page_ahead(kp, seq, base, m, b_end, p0);
+    load(base, p0, v0);
+    page_ahead(kp, seq, base + 256, m, b_end, p1);
+    page_ahead(kp, seq, base + 512, m, b_end, p0);
     if (hist) hist_clear(lhist);
     bf16x8_t a[4];
 #pragma unroll
@@ -204,10 +239,12 @@ __global__ __launch_bounds__(256) void score_rows_fp8_kernel(
         }
     };
     for (; base < b_end; base += 512) {
-        load(base + 256, v1);
+        load(base + 256, p1, v1);
+        page_ahead(kp, seq, base + 768, m, b_end, p1);
         __builtin_amdgcn_sched_barrier(0);
         score(base, v0);
-        load(base + 512, v0);
+        load(base + 512, p0, v0);
+        page_ahead(kp, seq, base + 1024, m, b_end, p0);
         __builtin_amdgcn_sched_barrier(0);
         score(base + 256, v1);
     }

@@ -27,7 +27,8 @@ INDEX_DIM, INDEX_HEADS, BLOCK_TOKENS, MAX_TOP_K, MAX_QUERY_GROUP = 128, 4, 4, 40
 # every symbol include/qsa.h declares
 EXPORTS = ("qsa_pool_index_keys", "qsa_pool_index_keys_fp8", "qsa_pool_append", "qsa_score_topk_workspace_size",
            "qsa_score_topk", "qsa_score_topk_fp8_workspace_size", "qsa_score_topk_fp8", "qsa_score_topk_paged",
-           "qsa_sparse_attn_prefill_paged", "qsa_sparse_attn_decode_paged", "qsa_sparse_attn_prefill_fp8kv",
+           "qsa_pool_index_keys_paged", "qsa_sparse_attn_prefill_paged", "qsa_sparse_attn_decode_paged",
+           "qsa_sparse_attn_prefill_fp8kv",
            "qsa_sparse_attn_decode_fp8kv",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode_workspace_size",
            "qsa_sparse_attn_decode", "qsa_status_string", "qsa_last_device_error", "qsa_profile_enable",
@@ -81,6 +82,8 @@ def load():
     lib.qsa_sparse_attn_decode_paged.argtypes = [P, P, i32, i32, P, P, P, P, i64, i32, P, P, i32, i32, i32, i32, f32,
                                                  st, P, P, P, sz, P]
     lib.qsa_sparse_attn_decode_paged.restype = st
+    lib.qsa_pool_index_keys_paged.argtypes = [P, i64, P, P, P, P, i64, i32, i32, i32, i32, f64, u32, st, P]
+    lib.qsa_pool_index_keys_paged.restype = st
     lib.qsa_sparse_attn_prefill_fp8kv.argtypes = [P, P, P, i32, P, P, i64, P, i64, i32, f32, f32, P, P, i32, i32,
                                                   i32, i32, f32, P, P, P]
     lib.qsa_sparse_attn_prefill_fp8kv.restype = st
@@ -382,6 +385,20 @@ def sparse_attn_decode_paged(q, row_pos, k_cache, v_cache, page_table, page_toke
                                              _stream(stream))
     _check("qsa_sparse_attn_decode_paged", rc)
     return out, lse
+
+
+def pool_index_keys_paged(raw_keys, page_table, page_tokens: int, block_begin: int, block_end: int,
+                          rope_theta: float, pooled=None, codes=None, scales=None, flags: int = 0, stream=None):
+    """a1-a3 into a paged compressed-key pool: raw_keys [B][L][128]; `pooled`
+    [slots/4][128] (raw dtype), or FP8 `codes` [slots/4][128] uint8 + `scales`
+    [slots/4]; block b of sequence s goes to key slot(4b) / 4."""
+    _need_contig(raw_keys, page_table, pooled, codes, scales)
+    B, L, _ = raw_keys.shape
+    rc = load().qsa_pool_index_keys_paged(_ptr(raw_keys), L * INDEX_DIM, _ptr(pooled), _ptr(codes), _ptr(scales),
+                                          _ptr(page_table), page_table.shape[1], int(page_tokens), B,
+                                          int(block_begin), int(block_end), float(rope_theta), int(flags),
+                                          _dtype_code(raw_keys), _stream(stream))
+    _check("qsa_pool_index_keys_paged", rc)
 
 
 def _fp8_codes(t):

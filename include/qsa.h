@@ -231,6 +231,17 @@ qsa_status_t qsa_sparse_attn_prefill(const void *q, const int32_t *row_seq, cons
  * every position the call reads.  Everything else is as in the contiguous
  * entry points.
  */
+/* qsa_pool_index_keys into a paged compressed-key pool: block b of sequence s
+ * (raw keys contiguous as in qsa_pool_index_keys) is stored at key
+ * slot(4b) / 4 -- into `pooled` (dtype = raw_dtype) or, for FP8 keys, into
+ * `codes` + `scales` (as qsa_pool_index_keys_fp8; pass pooled = NULL).  The
+ * table must cover block_end blocks (page_table_stride * page_tokens / 4 >=
+ * block_end). */
+qsa_status_t qsa_pool_index_keys_paged(const void *raw_keys, int64_t raw_seq_stride, void *pooled,
+                                       uint8_t *codes, float *scales, const int32_t *page_table,
+                                       int64_t page_table_stride, int32_t page_tokens, int32_t batch,
+                                       int32_t block_begin, int32_t block_end, double rope_theta,
+                                       uint32_t flags, qsa_dtype_t raw_dtype, void *stream);
 /* qsa_score_topk on paged compressed keys: `pooled` (dtype) or, for FP8 keys,
  * `codes` + `scales` (with dtype QSA_BF16 for the index queries; pass
  * pooled = NULL).  Workspace: qsa_score_topk_workspace_size(..., dtype, flags). */

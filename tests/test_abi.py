@@ -177,6 +177,28 @@ def test_paged_validation(libqsa):
     assert d(*bad) == qsa.ERR_INVALID_ARG
 
 
+def test_pool_paged_validation(libqsa):
+    f = libqsa.qsa_pool_index_keys_paged
+    # raw, raw_stride, pooled, codes, scales, table, pt_stride, P, batch, b0, b1, theta, flags, dtype, stream
+    args = [A, 1024, B_, None, None, C, 10, 16, 2, 0, 40, 1e7, 0, qsa.BF16, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a8=0) == qsa.OK
+    assert call(a10=0) == qsa.OK                                    # empty block range
+    assert call(a7=6) == qsa.ERR_INVALID_ARG                        # pages hold whole blocks
+    assert call(a5=None) == qsa.ERR_INVALID_ARG
+    assert call(a10=41) == qsa.ERR_INVALID_ARG                      # 10 pages x 4 blocks cover 40
+    assert call(a3=B_, a4=C) == qsa.ERR_INVALID_ARG                 # both key formats
+    assert call(a2=MIS) == qsa.ERR_INVALID_ARG
+    assert call(a13=9) == qsa.ERR_UNSUPPORTED
+    assert call(a11=0.5) == qsa.ERR_INVALID_ARG
+
+
 def test_attn_validation(libqsa):
     fp = libqsa.qsa_sparse_attn_prefill
     # rows == 0 -> OK without touching anything

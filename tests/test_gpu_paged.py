@@ -45,6 +45,51 @@ def _layout(rng, B, L, P, spare=7):
     return table, table.shape[1] * B + spare
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "f32", "fp8"])
+@pytest.mark.parametrize("P", [4, 64])
+def test_pool_paged_equals_contiguous(gpu, fmt, P):
+    # a chunk's blocks pooled straight into the paged pool: exactly the
+    # contiguous pooling, scattered by the table; pages outside the range keep
+    # their contents
+    import torch
+    rng = np.random.default_rng(91 + P)
+    B, NB, b0 = 2, 1500, 300
+    raw = rng.standard_normal((B, 4 * NB + 3, DIM)).astype(np.float32)
+    dt = "f32" if fmt == "f32" else "bf16"
+    raw = synth.bf16_bits(raw) if dt == "bf16" else raw
+    table, n_pages = _layout(rng, B, 4 * NB + 3, P)
+    nkeys = n_pages * P // 4
+    if fmt == "fp8":
+        codes = torch.zeros((B, NB, DIM), dtype=torch.uint8, device="cuda")
+        scales = torch.zeros((B, NB), dtype=torch.float32, device="cuda")
+        qsa.pool_index_keys_fp8(dev(raw, dt), codes, scales, b0, NB, THETA)
+        pc = torch.full((nkeys, DIM), 7, dtype=torch.uint8, device="cuda")
+        ps = torch.full((nkeys,), -1.0, dtype=torch.float32, device="cuda")
+        qsa.pool_index_keys_paged(dev(raw, dt), dev(table, "i"), P, b0, NB, THETA, codes=pc, scales=ps)
+        want_c = _scatter_keys(host(codes), table, P, n_pages)
+        want_s = _scatter_keys(host(scales), table, P, n_pages)
+        got_c, got_s = host(pc), host(ps)
+    else:
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        pooled = torch.zeros((B, NB, DIM), dtype=tdt, device="cuda")
+        qsa.pool_index_keys(dev(raw, dt), pooled, b0, NB, THETA)
+        pp = torch.full((nkeys, DIM), 3.0, dtype=tdt, device="cuda")
+        qsa.pool_index_keys_paged(dev(raw, dt), dev(table, "i"), P, b0, NB, THETA, pooled=pp)
+        want_c = _scatter_keys(host(pooled), table, P, n_pages)
+        got_c = host(pp)
+    # keys of blocks [b0, NB) of every sequence
+    slots = np.concatenate([table[s, (4 * np.arange(b0, NB)) // P].astype(np.int64) * (P // 4) +
+                            np.arange(b0, NB) % (P // 4) for s in range(B)])
+    np.testing.assert_array_equal(got_c[slots], want_c[slots])
+    if fmt == "fp8":
+        np.testing.assert_array_equal(got_s[slots], want_s[slots])
+    untouched = np.setdiff1d(np.arange(nkeys), slots)
+    fill = {"fp8": 7, "bf16": synth.bf16_bits(np.float32(3.0)), "f32": 3.0}[fmt]
+    assert np.all(got_c[untouched] == fill)
+    if fmt == "fp8":
+        assert np.all(got_s[untouched] == -1.0)
+
+
 @pytest.mark.parametrize("P", [16, 256])
 @pytest.mark.parametrize("path,R", [("rows", 40), ("gemm", 130)])
 def test_score_topk_paged_equals_contiguous(gpu, P, path, R):
