@@ -111,6 +111,19 @@ __device__ __forceinline__ int64_t key_index(const KeyPages &kp, int64_t keys_pe
     if (!kp.table) return seq * keys_per_seq + b;
     return (int64_t)kp.table[seq * kp.stride + b / kp.bpp] * kp.bpp + b % kp.bpp;
 }
+// The table entry of block b's page (paged pools; 0 when contiguous), and
+// the key number of block b given that entry, as key_index.  Reading the
+// entry a step ahead of the key lets a key load skip the wait for the table.
+__device__ __forceinline__ int32_t page_entry(const KeyPages &kp, int64_t seq, int64_t b)
+{
+    return kp.table ? kp.table[seq * kp.stride + (uint32_t)b / (uint32_t)kp.bpp] : 0;
+}
+__device__ __forceinline__ int64_t key_at(const KeyPages &kp, int64_t keys_per_seq, int64_t seq, int64_t b,
+                                          int32_t pg)
+{
+    if (!kp.table) return seq * keys_per_seq + b;
+    return (int64_t)pg * kp.bpp + (int64_t)((uint32_t)b % (uint32_t)kp.bpp);
+}
 // Element offset of that key's 128 values in a bf16 / fp32 key array whose
 // sequences are `seq_stride` elements apart when contiguous.
 __device__ __forceinline__ int64_t key_offset(const KeyPages &kp, int64_t seq_stride, int64_t seq, int64_t b)

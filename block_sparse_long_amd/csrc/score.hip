@@ -38,17 +38,7 @@ __device__ __forceinline__ void page_ahead(const KeyPages &kp, int64_t seq, int6
 {
     if (!kp.table) return;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const uint32_t b = (uint32_t)min(base + 4 * m + nt, b_end - 1);
-        p.pg[nt] = kp.table[seq * kp.stride + b / (uint32_t)kp.bpp];
-    }
-}
-// Key number of block b given its table entry (as key_index).
-__device__ __forceinline__ int64_t key_at(const KeyPages &kp, int64_t keys_per_seq, int64_t seq, int64_t b,
-                                          int32_t pg)
-{
-    if (!kp.table) return seq * keys_per_seq + b;
-    return (int64_t)pg * kp.bpp + (int64_t)((uint32_t)b % (uint32_t)kp.bpp);
+    for (int nt = 0; nt < 4; ++nt) p.pg[nt] = page_entry(kp, seq, min(base + 4 * m + nt, b_end - 1));
 }
 
 __device__ __forceinline__ void hist_clear(uint32_t *lhist)

@@ -137,10 +137,12 @@ template <> struct TileShare<false> {
     uint4 p0, p1, p2, p3;
     // element-wise vector loads: a plain 64-byte copy into the struct would be
     // turned into a block copy and kept in scratch memory
-    __device__ __forceinline__ void load(const FusedScoreArgs &a, int32_t seq, int64_t b, int ldim)
+    // pg: the table entry of b's page (paged pools)
+    __device__ __forceinline__ void load(const FusedScoreArgs &a, int32_t seq, int64_t b, int ldim, int32_t pg)
     {
         typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-        const u32x4_t *src = (const u32x4_t *)((const bf16_t *)a.pooled + key_offset(a.kp, a.pooled_stride, seq, b) + ldim);
+        const int64_t off = a.kp.table ? key_at(a.kp, 0, seq, b, pg) * kDim : seq * a.pooled_stride + b * kDim;
+        const u32x4_t *src = (const u32x4_t *)((const bf16_t *)a.pooled + off + ldim);
         const u32x4_t x0 = src[0], x1 = src[1], x2 = src[2], x3 = src[3];
         p0 = make_uint4(x0.x, x0.y, x0.z, x0.w);
         p1 = make_uint4(x1.x, x1.y, x1.z, x1.w);
@@ -159,9 +161,9 @@ template <> struct TileShare<false> {
 template <> struct TileShare<true> {
     uint4 c[2];  // indexed with constants only
     float s;
-    __device__ __forceinline__ void load(const FusedScoreArgs &a, int32_t seq, int64_t b, int ldim)
+    __device__ __forceinline__ void load(const FusedScoreArgs &a, int32_t seq, int64_t b, int ldim, int32_t pg)
     {
-        const int64_t key = key_index(a.kp, a.pooled_stride, seq, b);
+        const int64_t key = key_at(a.kp, a.pooled_stride, seq, b, pg);
         const uint4 *src = (const uint4 *)(a.codes + key * kDim + ldim);
         c[0] = src[0];
         c[1] = src[1];
@@ -234,7 +236,10 @@ __global__ __launch_bounds__(256, 2) void score_sample_kernel(FusedScoreArgs a)
         const int64_t hi = min(s_hi, (nb_hi + kSampleStride - 1) / kSampleStride);  // samples that can be visible
         const int lrow = t >> 2, ldim = (t & 3) * 32;
         TileShare<FP8> ts;
-        auto fetch = [&](int64_t i0) { ts.load(a, seq, min(sample_block(min(i0 + lrow, hi - 1)), nb_hi - 1), ldim); };
+        auto fetch = [&](int64_t i0) {
+            const int64_t b = min(sample_block(min(i0 + lrow, hi - 1)), nb_hi - 1);
+            ts.load(a, seq, b, ldim, page_entry(a.kp, seq, b));
+        };
         if (s_lo < hi) fetch(s_lo);
         for (int64_t i0 = s_lo; i0 < hi; i0 += kFStep) {
             ts.store(&keys[lrow][ldim], &tile_scale[lrow], (t & 3) == 0);
@@ -402,13 +407,22 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
         if (lo >= hi) continue;
         const int lrow = t >> 2, ldim = (t & 3) * 32;
         TileShare<FP8> ts;  // the next tile's share of this thread
-        ts.load(a, seq, min(lo + lrow, hi - 1), ldim);
+        {
+            const int64_t b = min(lo + lrow, hi - 1);
+            ts.load(a, seq, b, ldim, page_entry(a.kp, seq, b));
+        }
+        // paged pools: the table entry of this thread's row of the next tile,
+        // read a step ahead of its key
+        int32_t pg_next = page_entry(a.kp, seq, min(lo + kFStep + lrow, hi - 1));
         ts.store(&keys[0][lrow][ldim], &tile_scale[0][lrow], (t & 3) == 0);
         __syncthreads();
         int cur = 0;
         for (int64_t base = lo; base < hi; base += kFStep) {
             const bool more = base + kFStep < hi;
-            if (more) ts.load(a, seq, min(base + kFStep + lrow, hi - 1), ldim);
+            if (more) {
+                ts.load(a, seq, min(base + kFStep + lrow, hi - 1), ldim, pg_next);
+                pg_next = page_entry(a.kp, seq, min(base + 2 * kFStep + lrow, hi - 1));
+            }
             float sc[4][4];
             tile_scores(keys[cur], qa, sc);
             apply_scales<FP8>(tile_scale[cur], sc);
