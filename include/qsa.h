@@ -13,7 +13,10 @@
  *          the model", item 2 (RoPE after key pooling; 512 blocks = 2,048
  *          tokens plus the incomplete tail block).
  *   [LBL]  "Qwen3.8-Flash-Next, Layer by Layer", section "Token mixing" (4 query
- *          heads and 1 key head of 128 dims, mean of every 4 keys, best 512).
+ *          heads and 1 key head of 128 dims, mean of every 4 keys, best 512;
+ *          the full-attention layers' 24 query heads over 2 KV heads of 256
+ *          dims) and section "Serving it" (indexer keys and the KV cache in
+ *          FP8).
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a device pointer (hipMalloc'd or equivalent).
@@ -33,7 +36,9 @@
  *     present for every visible block, kept block ids below the row's visible
  *     count) are the caller's; they are not checked.
  *   - Index-key dim 128, 4 indexer heads, 4 tokens per block ([SGL], [LBL]);
- *     the attention head dim must be 128.
+ *     the attention head dim is 128, or 256 on the bf16 path ([LBL]).
+ *   - FP8 arrays (E4M3 codes) are bytes: their strides count bytes, and code
+ *     rows must be 16-byte aligned like the other tensors.
  *   - A block b is visible to a query at position t when it is complete:
  *     4b + 3 <= t, i.e. b < nc(t) = floor((t+1)/4) ([SGL]: the visible
  *     compressed blocks plus the zero-to-three tail tokens).
