@@ -7,7 +7,10 @@
 // attention reads the original K/V at those positions.  Section "IndexShare
 // MTP": draft rows share one selection plus the positions drafted since.
 // Readings: query head h uses KV head floor(h / (Hq/Hkv)); logits are
-// softmax_scale * <q, k>; P is rounded to bf16 as an MFMA operand.
+// softmax_scale * <q, k>; P is rounded to bf16 as an MFMA operand.  K/V are
+// bf16, or FP8 E4M3 codes with one scale per cache tensor ("Qwen3.8-Flash-
+// Next, Layer by Layer", section "Serving it"), widened to bf16 on their way
+// into LDS; the caches are contiguous per sequence or a paged pool.
 //
 // Layout of the work.  A workgroup owns up to 64 queries that share one KV
 // head: (rows of the tile) x (Hq/Hkv heads), as 4 MFMA tiles of 16 queries,
