@@ -286,7 +286,6 @@ __global__ __launch_bounds__(256, 2) void score_sample_kernel(FusedScoreArgs a)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedScoreArgs a)
 {
-    __shared__ uint32_t hb[4][256];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t r = (int64_t)blockIdx.x * 4 + w;
     if (r >= a.rows) return;
@@ -294,62 +293,27 @@ __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedScoreArgs a)
     const int n = a.ssplit * 64;
     const uint32_t *crow = a.cand + r * n;
     uint32_t v[kMaxPer];
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) v[q] = q * 64 + lane < n ? crow[q * 64 + lane] : 0u;
     uint32_t valid = 0;
 #pragma unroll
-    for (int q = 0; q < kMaxPer; ++q) {
-        v[q] = q * 64 + lane < n ? crow[q * 64 + lane] : 0u;
-        valid += v[q] != 0u ? 1u : 0u;
-    }
-    for (int o = 32; o > 0; o >>= 1) valid += __shfl_xor(valid, o);
+    for (int q = 0; q < kMaxPer; ++q) valid += (uint32_t)__popcll(__ballot(v[q] != 0u));
     const uint32_t j = (uint32_t)sample_j(a.top_k);
     if (valid < j) {
         if (lane == 0) a.tau[r] = 0u;
         return;
     }
-    uint32_t *h = hb[w];
-    uint32_t need = j, prefix = 0;
-    int sh = 32;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int nsh = sh - 8;
+    // the j-th largest key T is the largest t with #{keys >= t} >= j: fixed
+    // bit by bit from the top, each count from ballots of the 64 lanes
+    uint32_t tkey = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = tkey | (1u << bit);
+        uint32_t cnt = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) h[4 * lane + q] = 0u;
-        wave_fence();
-#pragma unroll
-        for (int q = 0; q < kMaxPer; ++q)
-            if (v[q] != 0u && (sh == 32 || (v[q] >> sh) == prefix)) atomicAdd(&h[(v[q] >> nsh) & 0xffu], 1u);
-        wave_fence();
-        uint32_t hv[4], sum = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            hv[q] = h[255 - 4 * lane - q];
-            sum += hv[q];
-        }
-        uint32_t incl = sum;
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
-        const int ls = __ffsll((unsigned long long)__ballot(incl >= need)) - 1;
-        uint32_t digit = 0, above = 0;
-        if (lane == ls) {
-            uint32_t acc = incl - sum;
-            for (int q = 0; q < 4; ++q) {
-                if (acc + hv[q] >= need) {
-                    digit = 255u - 4u * (uint32_t)lane - (uint32_t)q;
-                    above = acc;
-                    break;
-                }
-                acc += hv[q];
-            }
-        }
-        digit = __shfl(digit, ls);
-        above = __shfl(above, ls);
-        need -= above;
-        prefix = (sh == 32 ? 0u : (prefix << 8)) | digit;
-        sh = nsh;
-        wave_fence();
+        for (int q = 0; q < kMaxPer; ++q) cnt += (uint32_t)__popcll(__ballot(v[q] >= c));
+        if (cnt >= j) tkey = c;
     }
-    if (lane == 0) a.tau[r] = prefix;  // all 32 bits resolved: the j-th best key
+    if (lane == 0) a.tau[r] = tkey;
 }
 
 // ---------------------------------------------------------------------------
