@@ -103,6 +103,30 @@ constexpr float kNoMax = -1.0e30f;  // reference max before a query's first logi
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// Reductions over the 4 lane groups of a query: v_permlane16_swap /
+// v_permlane32_swap of a register with itself give every lane its own value
+// and that of lane l ^ 16 (l ^ 32), without a trip through LDS.
+__device__ __forceinline__ float max_xor16(float x)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // Per-wave attention state: 16 queries, lane l <-> query l%16 for m / l,
 // O[q = 4*(l/16) + j][dim 16*nt + l%16] in o[nt][j].
 template <int DIM>
@@ -323,8 +347,7 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem<DIM> &cs, const bf16x
     for (int sub = 0; sub < G::kSub; ++sub)
 #pragma unroll
         for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, s[sub][j]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    cmax = max_xor32(max_xor16(cmax));
     const bool raise = cmax > st.m + kLazy;  // also the first logit of a query (st.m = kNoMax)
     const float m_ref = raise ? cmax : st.m;
     if (__ballot(raise && st.m != kNoMax)) {  // some query's O and l change scale
@@ -394,10 +417,7 @@ __device__ __forceinline__ void init_state(WaveState<DIM> &st)
 template <int DIM>
 __device__ __forceinline__ float total_l(const WaveState<DIM> &st)
 {
-    float l = st.l;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    return l;
+    return sum_xor32(sum_xor16(st.l));
 }
 
 }  // namespace
