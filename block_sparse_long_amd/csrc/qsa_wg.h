@@ -35,12 +35,7 @@ __device__ __forceinline__ uint32_t wg_inclusive_scan(uint32_t v, uint32_t *wtot
 {
     constexpr int kSelWaves = NT / kWave;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_incl_scan(v);  // DPP row shifts and broadcasts: no LDS round trips
     if (lane == 63) wtot[wave] = x;
     __syncthreads();
     uint32_t before = 0;
