@@ -202,15 +202,21 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v)
     return lane_value(wave_incl_scan_op(v, [](uint32_t x, uint32_t y) { return x | y; }), 63);
 }
 
+// Max and sum of a float over the wave's lanes (every lane gets the result):
+// the DPP scan on the value's bits, then lane 63's total.
 __device__ __forceinline__ float wave_max(float v)
 {
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    const uint32_t s = wave_incl_scan_op(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+        return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y)));
+    });
+    return __uint_as_float(lane_value(s, 63));
 }
 __device__ __forceinline__ float wave_sum(float v)
 {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    const uint32_t s = wave_incl_scan_op(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+        return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
+    });
+    return __uint_as_float(lane_value(s, 63));
 }
 __device__ __forceinline__ double wave_sum_f64(double v)
 {
