@@ -187,3 +187,21 @@ def test_wide_heads_whole_path_sampled(gpu, name, overrides):
                                                    w["tail_start"])
         assert_close_out(host(out), want, "bf16")
         np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("Qn,Hq,Hkv", [(32, 2, 1), (40, 1, 1)])
+def test_attn_decode_row_mask_limits(gpu, Qn, Hq, Hkv):
+    # 32 rows sharing a selection fill the MFMA path's 32-bit row masks (all
+    # bits set for the kept blocks); 40 rows go to the VALU path
+    rng = np.random.default_rng(340 + Qn)
+    B, ctx, k, D = 2, 4 * 600 + 2, 64, 128
+    L = ctx + Qn
+    rp = (ctx + np.tile(np.arange(Qn), (B, 1))).astype(np.int32)
+    ts = np.full(B, 4 * (ctx // 4), np.int32)
+    sel, cnt = _random_selection(rng, np.full(B, ctx - 1), k)
+    q, kc, vc = _bf16(rng, (B, Qn, Hq, D)), _bf16(rng, (B, L, Hkv, D)), _bf16(rng, (B, L, Hkv, D))
+    want, want_lse = oracle.sparse_attn_decode(q, rp, kc, vc, sel, cnt, ts)
+    out, lse = qsa.sparse_attn_decode(dev(q, "bf16"), dev(rp, "i"), dev(kc, "bf16"), dev(vc, "bf16"),
+                                      dev(sel, "i"), dev(cnt, "i"), dev(ts, "i"))
+    assert_close_out(host(out), want, "bf16")
+    np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
