@@ -584,22 +584,36 @@ def bench_pool_append(spec, launches=50):
             "bound": "latency"}
 
 
-def cpu_decode(spec, w, pooled_h):
+def cpu_decode(spec, w, pooled_h, target_s=10.0, max_passes=64):
+    """The oracle's decode step (score/top-k of a sequence's anchor, then the
+    attention of its rows), over the workload's sequences in turn until about
+    target_s seconds have passed.  pooled_h holds the first sequence's pooled
+    keys; the others are pooled by the oracle before timing."""
     import torch
     import oracle
     k = spec.top_k
     p = pooled_h
-    pooled = (p.view(torch.int16).numpy().view(np.uint16) if p.dtype == torch.bfloat16 else p.numpy())
+    first = (p.view(torch.int16).numpy().view(np.uint16) if p.dtype == torch.bfloat16 else p.numpy())
+    B = spec.batch
+    pooled = [first] + [oracle.pool(w["raw_keys"][s:s + 1], 0, spec.n_blocks, spec.theta) for s in range(1, B)]
+    rows, passes = 0, 0
     t0 = time.perf_counter()
-    s, c, _, _ = oracle.score_topk(w["idx_q"][:1], w["row_seq"][:1], w["row_pos"][:1], pooled, k, spec.theta)
-    ts = None if w["tail_start"] is None else w["tail_start"][:1]
-    oracle.sparse_attn_decode(w["q"][:1], w["attn_pos"][:1], w["k_cache"][:1], w["v_cache"][:1], s, c, ts)
+    while passes < max_passes:
+        s = passes % B
+        sl = slice(s, s + 1)
+        sel, cnt, _, _ = oracle.score_topk(w["idx_q"][sl], np.zeros(1, np.int32), w["row_pos"][sl], pooled[s], k,
+                                           spec.theta)
+        ts = None if w["tail_start"] is None else w["tail_start"][sl]
+        oracle.sparse_attn_decode(w["q"][sl], w["attn_pos"][sl], w["k_cache"][sl], w["v_cache"][sl], sel, cnt, ts)
+        rows += spec.q_per_seq
+        passes += 1
+        if time.perf_counter() - t0 >= target_s and passes >= B:
+            break
     t = time.perf_counter() - t0
-    return {"value": spec.q_per_seq / t, "unit": "query rows/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"one of {spec.batch} sequences: score/top-{k} of its anchor over "
-                      f"{int(visible(w['row_pos'][0]))} blocks and attention of its {spec.q_per_seq} rows "
-                      f"({t:.1f}s)"}
-
+    return {"value": rows / t, "unit": "query rows/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{passes} sequence steps over the {B} sequences (each: score/top-{k} of the anchor over "
+                      f"{int(visible(w['row_pos'][0]))} blocks, then attention of its {spec.q_per_seq} rows) "
+                      f"in {t:.1f}s"}
 
 
 # ---------------------------------------------------------------------------
