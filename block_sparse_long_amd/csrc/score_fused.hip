@@ -634,18 +634,23 @@ __device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n,
             atomicOr(&bm[k ? bm_slot(b >> 5) : (uint32_t)lane], k ? 1u << (b & 31u) : 0u);
         }
         wave_fence();
-        // exclusive prefix count of each word, in word order
+        // the lane's words, read once (all reads in flight together), and the
+        // exclusive prefix count of its run in word order
         constexpr int kPer = kWinWords / kWave;
-        uint32_t c = 0;
+        uint32_t words[kPer], c = 0;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) c += (uint32_t)__popc(bm[bm_slot((uint32_t)(lane * kPer + j))]);
+        for (int j = 0; j < kPer; ++j) words[j] = bm[bm_slot((uint32_t)(lane * kPer + j))];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) c += (uint32_t)__popc(words[j]);
         const uint32_t incl = wave_incl_scan(c);
+        // each kept pair finds its slot from its word's prefix count and the
+        // bits below it (kept blocks cluster, so walking each lane's set bits
+        // would serialise on the lanes that hold the clusters)
         uint32_t run = incl - c;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const uint32_t wi = (uint32_t)(lane * kPer + j);
-            pre[pre_slot(wi)] = (uint16_t)run;
-            run += (uint32_t)__popc(bm[bm_slot(wi)]);
+            pre[pre_slot((uint32_t)(lane * kPer + j))] = (uint16_t)run;
+            run += (uint32_t)__popc(words[j]);
         }
         wave_fence();
 #pragma unroll
