@@ -30,6 +30,9 @@ constexpr int kEmitWords = 8192;     // bitmap window of the final pass: 262,144
 // wave walking their own runs of 32 words hit distinct LDS banks.
 constexpr int kEmitSlots = kEmitWords + kEmitWords / 32;
 __device__ __forceinline__ int emit_slot(int w) { return w + (w >> 5); }
+// u16 count of word w: 2 slots of padding per 32 words, so the threads writing
+// their runs of 32 hit distinct banks
+__device__ __forceinline__ int emit_pre_slot(int w) { return w + 2 * (w >> 5); }
 
 // Reported score s = raw / sqrt(128) (the score equation's scale), divided in
 // double and rounded once to float.
@@ -349,9 +352,14 @@ __global__ __launch_bounds__(kSplitThreads) void select_final_kernel(
     const uint32_t n = min(s_fill, (uint32_t)kk);
     if (t == 0) sel_count[r] = (int32_t)n;
     // ---- emit in block order: mark the kept blocks in an LDS bitmap (one
-    // window of the visible range at a time), then each thread writes the set
-    // bits of its run of words at its prefix-sum offset ----
-    const float *srow = scores + r * sc_stride;
+    // window of the visible range at a time); each thread reads its run of
+    // words once, the runs' prefix counts give every word its exclusive
+    // count, and each kept entry then finds its slot from its word's count
+    // and the bits below it.  (Kept blocks cluster, so walking each thread's
+    // set bits would serialise on the threads that hold the clusters.)  The
+    // candidate stage is free by now and holds the word counts. ----
+    static_assert(kEmitWords + 2 * (kEmitWords / 32) <= 4 * kCandStage, "word counts fit the candidate stage");
+    uint16_t *pre = (uint16_t *)cst;
     uint32_t out_base = 0;
     for (int64_t w0 = 0; w0 < nc; w0 += 32 * kEmitWords) {
         const int nwords = (int)min((int64_t)kEmitWords, (nc - w0 + 31) / 32);
@@ -363,7 +371,7 @@ __global__ __launch_bounds__(kSplitThreads) void select_final_kernel(
         }
         __syncthreads();
         // the thread's run of words, read once into registers (all reads in
-        // flight together), counted, then emitted from the registers
+        // flight together)
         constexpr int kPerMax = kEmitWords / kSplitThreads;
         const int per = (nwords + kSplitThreads - 1) / kSplitThreads;
         const int i0 = min(nwords, t * per), i1 = min(nwords, i0 + per);
@@ -375,20 +383,23 @@ __global__ __launch_bounds__(kSplitThreads) void select_final_kernel(
         for (int j = 0; j < kPerMax; ++j) c += (uint32_t)__popc(words[j]);
         const uint32_t incl = wg_inclusive_scan<kSplitThreads>(c, wtot);
         if (t == kSplitThreads - 1) s_total = incl;
-        uint32_t pos = out_base + incl - c;
+        uint32_t run = incl - c;
 #pragma unroll
         for (int j = 0; j < kPerMax; ++j) {
-            const int i = i0 + j;
-            uint32_t word = words[j];
-            while (word) {
-                const int bit = __ffs(word) - 1;
-                word &= word - 1u;
-                const int64_t b = w0 + 32 * (int64_t)i + bit;
-                if (pos < (uint32_t)kk) {
-                    out[pos] = (int32_t)b;
-                    if (osc) osc[pos] = scaled_score(srow[b]);
-                }
-                ++pos;
+            if (i0 + j < i1) pre[emit_pre_slot(i0 + j)] = (uint16_t)run;
+            run += (uint32_t)__popc(words[j]);
+        }
+        __syncthreads();
+        for (uint32_t i = t; i < n; i += kSplitThreads) {
+            const uint64_t e = buf[i];
+            const int64_t blk = (int64_t)(e >> 32), b = blk - w0;
+            if (b < 0 || b >= 32 * (int64_t)nwords) continue;
+            const int wd = (int)(b >> 5);
+            const uint32_t pos = out_base + (uint32_t)pre[emit_pre_slot(wd)] +
+                                 (uint32_t)__popc(bm[emit_slot(wd)] & ((1u << (b & 31)) - 1u));
+            if (pos < (uint32_t)kk) {
+                out[pos] = (int32_t)blk;
+                if (osc) osc[pos] = scaled_score(key_score((uint32_t)e));  // the entry's key is its score's
             }
         }
         __syncthreads();
