@@ -284,12 +284,12 @@ __global__ __launch_bounds__(256, 2) void score_sample_kernel(FusedScoreArgs a)
 //    row's candidates (at most the j-th best sampled score), or 0 (no
 //    threshold) when fewer than j candidates exist.
 // ---------------------------------------------------------------------------
+template <int kMaxPer>  // ssplit <= kMaxPer: at most kMaxPer candidates per lane
 __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedScoreArgs a)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t r = (int64_t)blockIdx.x * 4 + w;
     if (r >= a.rows) return;
-    constexpr int kMaxPer = 8;  // ssplit <= 8: at most 8 candidates per lane
     const int n = a.ssplit * 64;
     const uint32_t *crow = a.cand + r * n;
     uint32_t v[kMaxPer];
@@ -1043,8 +1043,12 @@ void launch_score_fused(const FusedScoreArgs &a, int32_t *sel_blocks, int32_t *s
         else
             QSA_LAUNCH("score_sample", score_sample_kernel<false>, dim3(tiles, (unsigned)a.ssplit), dim3(256), 0,
                        stream, a);
-        QSA_LAUNCH("sample_threshold", sample_threshold_kernel, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0,
-                   stream, a);
+        if (a.ssplit <= 4)
+            QSA_LAUNCH("sample_threshold", sample_threshold_kernel<4>, dim3((unsigned)((a.rows + 3) / 4)), dim3(256),
+                       0, stream, a);
+        else
+            QSA_LAUNCH("sample_threshold", sample_threshold_kernel<8>, dim3((unsigned)((a.rows + 3) / 4)), dim3(256),
+                       0, stream, a);
         if (fp8)
             QSA_LAUNCH("score_filter_fp8", score_filter_kernel<true>, dim3(tiles, (unsigned)a.nsplit), dim3(256), 0,
                        stream, a);

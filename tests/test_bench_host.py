@@ -76,6 +76,7 @@ def test_roofline_fraction(bench):
     ("void qsa::score_filter_kernel<false>(qsa::FusedScoreArgs)", "score_filter"),
     ("void qsa::score_filter_kernel<true>(qsa::FusedScoreArgs)", "score_filter_fp8"),
     ("void qsa::score_sample_kernel<true>(qsa::FusedScoreArgs)", "score_sample_fp8"),
+    ("void qsa::sample_threshold_kernel<4>(qsa::FusedScoreArgs)", "sample_threshold"),
     ("qsa::score_rows_bf16_kernel(unsigned short const*, int const*)", "score_rows_bf16"),
     ("void qsa::attn_prefill_mfma_kernel<128, unsigned short>(qsa::AttnArgs, int)", "attn_prefill_mfma"),
     ("void qsa::attn_prefill_mfma_kernel<256, unsigned short>(qsa::AttnArgs, int)", "attn_prefill_mfma_d256"),
