@@ -136,9 +136,11 @@ def test_score_topk_matches_oracle(gpu, dtype, path, R, NB, k):
         assert np.all(g_sc[r, n:] == 0)
 
 
+# (8 rows, 40,000 blocks: ~5,700 blocks share each score value, more tied
+# candidates than the split selection stages in LDS)
 @pytest.mark.parametrize("dtype,path,R,NB", [("bf16", "rows", 80, 1500), ("bf16", "gemm", 80, 1500),
                                              ("f32", "rows", 80, 1500), ("bf16", "rows", 30, 9001),
-                                             ("f32", "rows", 30, 9001)])
+                                             ("f32", "rows", 30, 9001), ("bf16", "rows", 8, 40000)])
 def test_score_topk_integer_inputs_bit_exact(gpu, dtype, path, R, NB):
     B, k = 2, 64
     pooled, iq, seq, pos = _score_case(5, dtype, B, NB, R, k, integer=True)
