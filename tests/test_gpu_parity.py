@@ -136,6 +136,23 @@ def test_score_topk_matches_oracle(gpu, dtype, path, R, NB, k):
         assert np.all(g_sc[r, n:] == 0)
 
 
+def test_score_topk_fused_crowded_bin_bit_exact(gpu):
+    # integer inputs, 40,000 blocks, k = 512 on the fused scorer: ~5,700 blocks
+    # tie at the top score, so no pair list overflows but the k-th key's bin
+    # holds more pairs than the merge stages, and the merge walks the lists
+    B, R, NB, k = 1, 8, 40000, 512
+    pooled, iq, seq, pos = _score_case(9, "bf16", B, NB, R, k, integer=True)
+    o_sel, o_cnt, _, o_raw = oracle.score_topk(iq, seq, pos, pooled, k, THETA, qsa.FLAG_NO_ROPE, want_raw=True)
+    sel, cnt, sc = qsa.score_topk(dev(iq, "bf16"), dev(seq, "i"), dev(pos, "i"), dev(pooled, "bf16"), NB, k,
+                                  THETA, flags=qsa.FLAG_NO_ROPE | qsa.FLAG_SCORE_GEMM)
+    np.testing.assert_array_equal(host(cnt), o_cnt)
+    np.testing.assert_array_equal(host(sel), o_sel)       # ties resolved to the lower block, exactly
+    g_sel, g_cnt, g_sc = host(sel), host(cnt), host(sc)
+    for r in range(R):
+        n = g_cnt[r]
+        np.testing.assert_allclose(g_sc[r, :n], o_raw[r, g_sel[r, :n]] / math.sqrt(128), rtol=1e-6, atol=1e-6)
+
+
 # (8 rows, 40,000 blocks: ~5,700 blocks share each score value, more tied
 # candidates than the split selection stages in LDS)
 @pytest.mark.parametrize("dtype,path,R,NB", [("bf16", "rows", 80, 1500), ("bf16", "gemm", 80, 1500),
