@@ -359,34 +359,38 @@ __global__ __launch_bounds__(kSplitThreads) void select_final_kernel(
     // set bits would serialise on the threads that hold the clusters.)  The
     // candidate stage is free by now and holds the word counts. ----
     static_assert(kEmitWords + 2 * (kEmitWords / 32) <= 4 * kCandStage, "word counts fit the candidate stage");
+    static_assert(kEmitWords % (32 * kSplitThreads) == 0, "whole 32-word runs per thread");
     uint16_t *pre = (uint16_t *)cst;
     uint32_t out_base = 0;
     for (int64_t w0 = 0; w0 < nc; w0 += 32 * kEmitWords) {
         const int nwords = (int)min((int64_t)kEmitWords, (nc - w0 + 31) / 32);
-        for (int i = t; i < emit_slot(nwords); i += kSplitThreads) bm[i] = 0u;
+        // the whole bitmap is cleared, so words past the window read as 0
+        static_assert(kEmitSlots % kSplitThreads == 0, "the bitmap clears in whole rounds");
+#pragma unroll
+        for (int q = 0; q < kEmitSlots / kSplitThreads; ++q) bm[q * kSplitThreads + t] = 0u;
         __syncthreads();
         for (uint32_t i = t; i < n; i += kSplitThreads) {
             const int64_t b = (int64_t)(buf[i] >> 32) - w0;
             if (b >= 0 && b < 32 * (int64_t)nwords) atomicOr(&bm[emit_slot((int)(b >> 5))], 1u << (b & 31));
         }
         __syncthreads();
-        // the thread's run of words, read once into registers (all reads in
-        // flight together)
-        constexpr int kPerMax = kEmitWords / kSplitThreads;
-        const int per = (nwords + kSplitThreads - 1) / kSplitThreads;
-        const int i0 = min(nwords, t * per), i1 = min(nwords, i0 + per);
-        uint32_t words[kPerMax];
+        // the thread's run of kPer words, read once into registers (all
+        // reads in flight together; no guards, so the reads are not split
+        // into separate branches)
+        constexpr int kPer = kEmitWords / kSplitThreads;
+        const int i0 = t * kPer;
+        uint32_t words[kPer];
 #pragma unroll
-        for (int j = 0; j < kPerMax; ++j) words[j] = i0 + j < i1 ? bm[emit_slot(i0 + j)] : 0u;
+        for (int j = 0; j < kPer; ++j) words[j] = bm[emit_slot(i0 + j)];
         uint32_t c = 0;
 #pragma unroll
-        for (int j = 0; j < kPerMax; ++j) c += (uint32_t)__popc(words[j]);
+        for (int j = 0; j < kPer; ++j) c += (uint32_t)__popc(words[j]);
         const uint32_t incl = wg_inclusive_scan<kSplitThreads>(c, wtot);
         if (t == kSplitThreads - 1) s_total = incl;
         uint32_t run = incl - c;
 #pragma unroll
-        for (int j = 0; j < kPerMax; ++j) {
-            if (i0 + j < i1) pre[emit_pre_slot(i0 + j)] = (uint16_t)run;
+        for (int j = 0; j < kPer; ++j) {
+            pre[emit_pre_slot(i0 + j)] = (uint16_t)run;
             run += (uint32_t)__popc(words[j]);
         }
         __syncthreads();
