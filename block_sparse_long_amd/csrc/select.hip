@@ -224,11 +224,15 @@ __global__ __launch_bounds__(kSplitThreads) void select_collect_kernel(
     // thread t holds blocks b_begin + 1024*j + 4*t + i (rows are padded to 64
     // floats, so a 4-block group that starts inside the row ends inside it)
     const int64_t b_end = min((int64_t)nc, b_begin + kCollectChunk);
+    // a group past the chunk's end reads the last group inside it instead
+    // (every load stays in the row, none needs a guard, so all are issued
+    // together); its entries are masked below
+    const int64_t b_last4 = (b_end - 1) & ~(int64_t)3;
     float4 v[kCollectChunk / (4 * kSplitThreads)];
 #pragma unroll
     for (int j = 0; j < kCollectChunk / (4 * kSplitThreads); ++j) {
         const int64_t b4 = b_begin + (int64_t)j * 4 * kSplitThreads + 4 * t;
-        v[j] = b4 < b_end ? *(const float4 *)(srow + b4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        v[j] = *(const float4 *)(srow + min(b4, b_last4));
     }
     find_bin_global(hist, (uint32_t)kk, wtot, &s_bin, &s_above);
     const uint32_t beta = s_bin;
