@@ -228,12 +228,27 @@ __global__ __launch_bounds__(DIM) void attn_combine_kernel(const float *__restri
     const int64_t qrow = blockIdx.x;
     const int d = threadIdx.x;
     const float *pp = partial + qrow * nsplit * (DIM + 2);
+    // the first kPre splits' values, read up front (clamped, so every read is
+    // in the row and none needs a guard) while wave 0 forms the weights: the
+    // reads do not depend on them
+    constexpr int kPre = 48;
+    float pv[kPre];
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) pv[j] = pp[min(j, nsplit - 1) * (DIM + 2) + d];
     if (d < kWave) {
-        float m = -INFINITY;
-        for (int s = d; s < nsplit; s += kWave) m = fmaxf(m, pp[s * (DIM + 2) + DIM]);
+        // each lane's first split's (m, l) is read once and kept for both passes
+        const float m0 = d < nsplit ? pp[d * (DIM + 2) + DIM] : -INFINITY;
+        const float l0 = d < nsplit ? pp[d * (DIM + 2) + DIM + 1] : 0.0f;
+        float m = m0;
+        for (int s = d + kWave; s < nsplit; s += kWave) m = fmaxf(m, pp[s * (DIM + 2) + DIM]);
         m = wave_max(m);
         float l = 0.0f;
-        for (int s = d; s < nsplit; s += kWave) {
+        if (d < nsplit) {
+            const float e = m0 == -INFINITY ? 0.0f : __expf(m0 - m);
+            wsplit[d] = e;
+            l = l0 * e;
+        }
+        for (int s = d + kWave; s < nsplit; s += kWave) {
             const float ms = pp[s * (DIM + 2) + DIM];
             const float e = ms == -INFINITY ? 0.0f : __expf(ms - m);
             wsplit[s] = e;
@@ -249,7 +264,9 @@ __global__ __launch_bounds__(DIM) void attn_combine_kernel(const float *__restri
     const float M = s_m, L = s_l;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (L > 0.0f) {
-        int s = 0;
+#pragma unroll
+        for (int j = 0; j < kPre; ++j) acc[j & 3] += (j < nsplit ? wsplit[j] : 0.0f) * pv[j];
+        int s = kPre;
         for (; s + 4 <= nsplit; s += 4) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[j] += wsplit[s + j] * pp[(s + j) * (DIM + 2) + d];
