@@ -685,10 +685,13 @@ __device__ __forceinline__ void for_each_listed(const uint2 *__restrict__ lists,
         uint32_t cmax = c;
         for (int o = 1; o < 64; o <<= 1) cmax = max(cmax, (uint32_t)__shfl_xor((int)cmax, o));
         const uint4 *src = (const uint4 *)(lists + (int64_t)min(li, nlists - 1) * subcap);
+        // a load past the list's last 16-byte pair of pairs re-reads that one (every load
+        // stays in the list, none needs a guard, so all 8 are issued together)
+        const uint32_t qlast = c > 0u ? (c - 1u) >> 1 : 0u;
         for (uint32_t j = 0; j < cmax; j += 16) {
             uint4 e[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) e[q] = j + 2 * q < c ? src[(j >> 1) + q] : make_uint4(0u, 0u, 0u, 0u);
+            for (int q = 0; q < 8; ++q) e[q] = src[min((j >> 1) + (uint32_t)q, qlast)];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 fn(make_uint2(e[q].x, e[q].y), j + 2 * q < c);
