@@ -90,7 +90,6 @@ def prefill_work(spec, row_pos):
     new_blocks = spec.chunk // 4
     return {
         "pool_rope": ("hbm", new_blocks * (4 + 1) * DIM * eb, "B"),
-        "score_gemm_bf16": ("mfma", 2.0 * 4 * DIM * pairs, "flop"),
         "score_rows_bf16": ("hbm", float(pairs) * DIM * eb, "B"),
         "select_rows": ("hbm", 4.0 * pairs, "B"),   # scans the fp32 scores once
         "attn_prefill": ("alu", 4.0 * spec.Hq * spec.D * float(npos.sum()), "flop"),
@@ -177,7 +176,7 @@ def timed(run_step, steps, warmup):
 
 
 ALL_KERNELS = ["pool_rope", "pool_rope_fp8", "pool_append", "rope_query", "score_rows_bf16", "score_rows_f32",
-               "score_rows_fp8", "score_gemm_bf16", "select_rows", "select_collect", "select_final", "score_sample",
+               "score_rows_fp8", "select_rows", "select_collect", "select_final", "score_sample",
                "score_sample_fp8", "sample_threshold", "score_filter", "score_filter_fp8", "select_merge",
                "attn_prefill_mfma", "attn_decode_mfma", "attn_prefill_mfma_d256", "attn_decode_mfma_d256",
                "attn_prefill_mfma_fp8kv", "attn_decode_mfma_fp8kv",
@@ -623,7 +622,7 @@ def cpu_decode(spec, w, pooled_h, target_s=10.0, max_passes=64):
 CSRC = os.path.join(ROOT, "block_sparse_long_amd", "csrc")
 HEADERS = ["qsa_internal.h", "qsa_device.h", "qsa_wg.h"]
 KERNEL_SOURCE = {"pool_rope": "pool.hip", "pool_append": "pool.hip", "rope_query": "pool.hip", "score_rows_bf16": "score.hip",
-                 "score_rows_f32": "score.hip", "score_gemm_bf16": "score.hip", "select_rows": "select.hip",
+                 "score_rows_f32": "score.hip", "select_rows": "select.hip",
                  "select_collect": "select.hip", "select_final": "select.hip", "score_sample": "score_fused.hip",
                  "sample_threshold": "score_fused.hip", "score_filter": "score_fused.hip",
                  "select_merge": "score_fused.hip", "attn_prefill_mfma": "attn_mfma.hip",

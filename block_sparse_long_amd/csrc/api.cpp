@@ -3,8 +3,10 @@
 // status strings and optional per-kernel timing.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -33,29 +35,37 @@ static void clear_launch_err()
 }
 static qsa_status_t launch_status() { return g_launch_err == hipSuccess ? QSA_OK : QSA_ERR_DEVICE; }
 
+// Timing records.  The enable flag is atomic; a launch's pending start event
+// and name belong to the launching thread; the finished records and the pool
+// of free events are shared and guarded by one mutex.  Timing is meant for
+// benchmarks: records from several threads land in one list.
 struct ProfRecord {
     std::string name;
     hipEvent_t start, stop;
 };
-static bool g_prof = false;
-static std::vector<ProfRecord> g_records;
-static std::vector<hipEvent_t> g_free_events;
-static std::string g_pending_name;
-static hipEvent_t g_pending_start = nullptr;
+static std::atomic<bool> g_prof{false};
+static std::mutex g_prof_mutex;
+static std::vector<ProfRecord> g_records;        // guarded by g_prof_mutex
+static std::vector<hipEvent_t> g_free_events;    // guarded by g_prof_mutex
+static thread_local std::string g_pending_name;
+static thread_local hipEvent_t g_pending_start = nullptr;
 
 static hipEvent_t take_event()
 {
-    if (!g_free_events.empty()) {
-        hipEvent_t e = g_free_events.back();
-        g_free_events.pop_back();
-        return e;
+    {
+        std::lock_guard<std::mutex> lock(g_prof_mutex);
+        if (!g_free_events.empty()) {
+            hipEvent_t e = g_free_events.back();
+            g_free_events.pop_back();
+            return e;
+        }
     }
     hipEvent_t e = nullptr;
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
     return e;
 }
 
-bool profiling_enabled() { return g_prof; }
+bool profiling_enabled() { return g_prof.load(std::memory_order_relaxed); }
 
 void prof_begin(const char *name, hipStream_t stream)
 {
@@ -69,6 +79,7 @@ void prof_end(hipStream_t stream)
     hipEvent_t stop = take_event();
     if (!g_pending_start || !stop) return;
     (void)hipEventRecord(stop, stream);
+    std::lock_guard<std::mutex> lock(g_prof_mutex);
     g_records.push_back({g_pending_name, g_pending_start, stop});
     g_pending_start = nullptr;
 }
@@ -112,7 +123,7 @@ struct ScoreLayout {
     int64_t sc_stride;
     size_t qrot_off, scores_off, scratch_off, sure_off, cand_off;
     int32_t nsplit, split_len, subcap, nsample, ssplit;
-    size_t buf_off, cnt_off, scand_off, tau_off;
+    size_t buf_off, cnt_off, scand_off, tau_off, mode_off;
     size_t total;
 };
 
@@ -133,7 +144,8 @@ static ScoreLayout score_layout(int32_t rows, int32_t max_nb, int32_t top_k, qsa
         L.cnt_off = L.buf_off + align256((size_t)rows * L.nsplit * 16 * (size_t)L.subcap * sizeof(uint2));
         L.scand_off = L.cnt_off + align256((size_t)rows * L.nsplit * 16 * sizeof(uint32_t));
         L.tau_off = L.scand_off + align256((size_t)rows * L.ssplit * 64 * sizeof(uint32_t));
-        L.total = L.tau_off + align256((size_t)rows * sizeof(uint32_t));
+        L.mode_off = L.tau_off + align256((size_t)rows * sizeof(uint32_t));
+        L.total = L.mode_off + align256((size_t)rows * sizeof(int32_t));
         return L;
     }
     L.scores_off = off;
@@ -287,6 +299,14 @@ size_t qsa_score_topk_workspace_size(int32_t rows, int32_t max_visible_blocks, i
     return score_layout(rows, max_visible_blocks, top_k, dtype, flags).total;
 }
 
+size_t qsa_score_topk_merge_modes_offset(int32_t rows, int32_t max_visible_blocks, int32_t top_k, qsa_dtype_t dtype,
+                                         uint32_t flags)
+{
+    if (qsa_score_topk_workspace_size(rows, max_visible_blocks, top_k, dtype, flags) == 0) return (size_t)-1;
+    const ScoreLayout L = score_layout(rows, max_visible_blocks, top_k, dtype, flags);
+    return L.plan.fused ? L.mode_off : (size_t)-1;
+}
+
 size_t qsa_score_topk_fp8_workspace_size(int32_t rows, int32_t max_visible_blocks, int32_t top_k, uint32_t flags)
 {
     return qsa_score_topk_workspace_size(rows, max_visible_blocks, top_k, QSA_BF16, flags);
@@ -410,6 +430,7 @@ static qsa_status_t score_topk_run(const void *q_index, const int32_t *row_seq, 
         fa.ssplit = L.ssplit;
         fa.cand = (uint32_t *)(ws + L.scand_off);
         fa.tau = (uint32_t *)(ws + L.tau_off);
+        fa.mode = (int32_t *)(ws + L.mode_off);
         launch_score_fused(fa, sel_blocks, sel_count, sel_scores, st);
         return launch_status();
     }
@@ -674,12 +695,13 @@ qsa_status_t qsa_sparse_attn_decode_fp8kv(const void *q, const int32_t *row_pos,
 
 qsa_status_t qsa_profile_enable(int enable)
 {
-    g_prof = enable != 0;
+    g_prof.store(enable != 0, std::memory_order_relaxed);
     return QSA_OK;
 }
 
 qsa_status_t qsa_profile_reset(void)
 {
+    std::lock_guard<std::mutex> lock(g_prof_mutex);
     for (auto &r : g_records) {
         g_free_events.push_back(r.start);
         g_free_events.push_back(r.stop);
@@ -693,8 +715,13 @@ int32_t qsa_profile_kernel_ms(const char *name, double *total_ms)
     double total = 0.0;
     int32_t n = 0;
     if (name) {
-        for (auto &r : g_records) {
-            if (r.name != name) continue;
+        std::vector<ProfRecord> mine;
+        {
+            std::lock_guard<std::mutex> lock(g_prof_mutex);
+            for (auto &r : g_records)
+                if (r.name == name) mine.push_back(r);
+        }
+        for (auto &r : mine) {  // waits outside the lock
             if (hipEventSynchronize(r.stop) != hipSuccess) continue;
             float ms = 0.0f;
             if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) continue;

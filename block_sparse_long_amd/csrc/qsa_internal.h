@@ -57,9 +57,6 @@ void launch_score_rows(const void *qrot, const int32_t *row_seq, const int32_t *
 void launch_score_rows_fp8(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
                            const uint8_t *codes, const float *scales, int64_t pooled_stride, const KeyPages &kp,
                            int32_t max_nb, float *scores, int64_t sc_stride, uint32_t *hist, hipStream_t stream);
-void launch_score_gemm(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
-                       const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores,
-                       int64_t sc_stride, hipStream_t stream);
 
 // ---- score_fused.hip (many rows, bf16) ----------------------------------------
 struct FusedScoreArgs {
@@ -83,6 +80,15 @@ struct FusedScoreArgs {
     int32_t ssplit;           // sample-range splits
     uint32_t *cand;           // [rows][ssplit][16][4] best sampled keys of each lane (0: none)
     uint32_t *tau;            // [rows] threshold key (0: no threshold)
+    int32_t *mode;            // [rows] how the merge ranked the row (kMergeMode*)
+};
+// Merge modes of a row, recorded for diagnostics.
+enum : int32_t {
+    kMergeNone = 0,         // no visible block
+    kMergeStaged = 1,       // every pair staged in LDS and ranked there
+    kMergePrefilter = 2,    // more pairs than the stage: a histogram picks those that can be kept
+    kMergeListWalk = 3,     // the k-th key's bin too crowded to stage: radix passes over the lists
+    kMergeRecompute = 4     // count short or a list overflowed (or too many exact ties): scores recomputed
 };
 int32_t fused_score_splits(int32_t rows, int32_t max_nb);
 int32_t fused_score_split_len(int32_t max_nb, int32_t nsplit);

@@ -282,88 +282,6 @@ __global__ __launch_bounds__(256) void score_rows_f32_kernel(
     if (hist) hist_flush(lhist, hist + (int64_t)r * kRowScratch);
 }
 
-// ---------------------------------------------------------------------------
-// Many rows (prefill), bf16: a GEMM of the rotated queries (rows x 4 heads)
-// against the pooled keys.  One wave owns 16 query rows = 4 MFMA row tiles of
-// (4 rows x 4 heads): MFMA row m of tile mt is query row 4*mt + m/4, head m%4,
-// so the 4 accumulators a lane receives are the 4 heads of one (row, block)
-// pair and the ReLU-sum stays inside the lane.  The 16 x 4 x 128 query tile
-// stays in registers while the wave streams 64 blocks per step; grid.y splits
-// the block range so that the chip has enough waves.  Rows of one wave that
-// belong to different sequences are handled one sequence at a time.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void score_gemm_bf16_kernel(
-    const bf16_t *__restrict__ qrot, const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_pos,
-    int32_t rows, const bf16_t *__restrict__ pooled, int64_t pooled_stride, int32_t max_nb, float *__restrict__ scores,
-    int64_t sc_stride)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int m = lane & 15, g = lane >> 4;
-    const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * 16;
-    if (row0 >= rows) return;
-    bf16x8_t a[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int64_t qr = row0 + 4 * mt + (m >> 2);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            a[mt][s] = qr < rows ? as_bf16x8(*(const uint4 *)(qrot + (qr * kIdxHeads + (m & 3)) * kDim + 32 * g + 8 * s))
-                                 : zero_bf16x8();
-    }
-    // the output rows this lane writes: row0 + 4*mt + g
-    int64_t my_nc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int64_t qr = row0 + 4 * mt + g;
-        my_nc[mt] = qr < rows ? min(visible_blocks(row_pos[qr]), (int64_t)max_nb) : 0;
-    }
-    const int64_t split_len = ((int64_t)max_nb + gridDim.y - 1) / gridDim.y;
-    const int64_t split_lo = (int64_t)blockIdx.y * split_len;
-    const int64_t split_hi = min((int64_t)max_nb, split_lo + split_len);
-    uint32_t todo = 0;  // bit i: row row0 + i still to do
-    for (int i = 0; i < 16; ++i)
-        if (row0 + i < rows) todo |= 1u << i;
-    while (todo) {  // wave-uniform: one sequence of this wave's rows at a time
-        const int first = __builtin_ctz(todo);
-        const int seq = row_seq[row0 + first];
-        int64_t nb_hi = 0;
-        uint32_t mine = 0;
-        for (int i = 0; i < 16; ++i) {
-            if (((todo >> i) & 1u) && row_seq[row0 + i] == seq) {
-                mine |= 1u << i;
-                nb_hi = max(nb_hi, visible_blocks(row_pos[row0 + i]));
-            }
-        }
-        todo &= ~mine;
-        const int64_t lo = split_lo, hi = min(split_hi, nb_hi);
-        const bf16_t *kb = pooled + (int64_t)seq * pooled_stride;
-        for (int64_t base = lo; base < hi; base += 64) {
-            uint4 v[4][4];
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int64_t b = min(base + nt * 16 + m, hi - 1);
-                const uint4 *src = (const uint4 *)(kb + b * kDim + 32 * g);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) v[nt][s] = src[s];
-            }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][s], as_bf16x8(v[nt][s]), acc, 0, 0, 0);
-                    const int64_t b = base + nt * 16 + m;
-                    const int ri = 4 * mt + g;
-                    if (((mine >> ri) & 1u) && b < my_nc[mt] && b < hi)
-                        scores[(row0 + ri) * sc_stride + b] = relu_sum4(acc);
-                }
-            }
-        }
-    }
-}
-
 int64_t score_chunks(int32_t max_nb) { return ((int64_t)max_nb + kChunk - 1) / kChunk; }
 
 void launch_score_rows(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
@@ -386,19 +304,6 @@ void launch_score_rows_fp8(const void *qrot, const int32_t *row_seq, const int32
     const dim3 grid((unsigned)score_chunks(max_nb), (unsigned)rows), block(256);
     QSA_LAUNCH("score_rows_fp8", score_rows_fp8_kernel, grid, block, 0, stream, (const bf16_t *)qrot, row_seq,
                row_pos, codes, scales, pooled_stride, kp, max_nb, scores, sc_stride, hist);
-}
-
-void launch_score_gemm(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
-                       const void *pooled, int64_t pooled_stride, int32_t max_nb, float *scores, int64_t sc_stride,
-                       hipStream_t stream)
-{
-    const int64_t waves = ((int64_t)rows + 15) / 16;
-    const int64_t wgs = (waves + 3) / 4;
-    int64_t split = (2048 + waves - 1) / waves;  // aim at >= 2048 waves on the chip
-    split = max((int64_t)1, min(split, ((int64_t)max_nb + 1023) / 1024));
-    const dim3 grid((unsigned)wgs, (unsigned)split), block(256);
-    QSA_LAUNCH("score_gemm_bf16", score_gemm_bf16_kernel, grid, block, 0, stream, (const bf16_t *)qrot, row_seq,
-               row_pos, rows, (const bf16_t *)pooled, pooled_stride, max_nb, scores, sc_stride);
 }
 
 }  // namespace qsa

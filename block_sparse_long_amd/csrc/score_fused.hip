@@ -724,7 +724,10 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
     const int32_t kk = max(0, min(a.top_k, nc));
     int32_t *out = sel_blocks + r * a.top_k;
     float *osc = sel_scores ? sel_scores + r * a.top_k : nullptr;
-    if (lane == 0) sel_count[r] = kk;
+    if (lane == 0) {
+        sel_count[r] = kk;
+        a.mode[r] = kMergeNone;
+    }
     for (int32_t i = kk + lane; i < a.top_k; i += kWave) {
         out[i] = -1;
         if (osc) osc[i] = 0.0f;
@@ -747,6 +750,7 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
     // kept set too large to sort in LDS is ranked and emitted in block order
     // from recomputed scores
     int mode = (overflow || total < (uint32_t)kk || kk > kStage) ? 2 : (total <= (uint32_t)kStage ? 0 : 1);
+    if (lane == 0) a.mode[r] = mode == 0 ? kMergeStaged : mode == 1 ? kMergeListWalk : kMergeRecompute;
     const uint2 *lists = a.buf + (int64_t)r * nlists * a.subcap;
     uint32_t n = 0;
     if (mode == 0) {  // stage the pairs in LDS: 64 lists at a time, lane i copies list i
@@ -822,6 +826,7 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
                 nst += (uint32_t)__popcll(tb);
             });
             wave_fence();
+            if (lane == 0) a.mode[r] = kMergePrefilter;
             merge_staged(st, h, nst, nc, kk, out, osc);
             return;
         }
@@ -922,6 +927,7 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
         visit([&](uint2 e, bool v) { g += (uint32_t)__popcll(__ballot(v && (above_t(e.x) || at_t(e.x)))); });
         if (g > (uint32_t)kStage) {  // too many exact ties to sort: rank recomputed scores instead
             mode = 2;
+            if (lane == 0) a.mode[r] = kMergeRecompute;
             n = (uint32_t)nc;
             select_t();
         }

@@ -26,7 +26,8 @@ INDEX_DIM, INDEX_HEADS, BLOCK_TOKENS, MAX_TOP_K, MAX_QUERY_GROUP = 128, 4, 4, 40
 
 # every symbol include/qsa.h declares
 EXPORTS = ("qsa_pool_index_keys", "qsa_pool_index_keys_fp8", "qsa_pool_append", "qsa_score_topk_workspace_size",
-           "qsa_score_topk", "qsa_score_topk_fp8_workspace_size", "qsa_score_topk_fp8", "qsa_score_topk_paged",
+           "qsa_score_topk", "qsa_score_topk_merge_modes_offset", "qsa_score_topk_fp8_workspace_size",
+           "qsa_score_topk_fp8", "qsa_score_topk_paged",
            "qsa_pool_index_keys_paged", "qsa_sparse_attn_prefill_paged", "qsa_sparse_attn_decode_paged",
            "qsa_sparse_attn_prefill_fp8kv",
            "qsa_sparse_attn_decode_fp8kv",
@@ -94,6 +95,8 @@ def load():
     lib.qsa_pool_append.restype = st
     lib.qsa_score_topk_workspace_size.argtypes = [i32, i32, i32, st, u32]
     lib.qsa_score_topk_workspace_size.restype = sz
+    lib.qsa_score_topk_merge_modes_offset.argtypes = [i32, i32, i32, st, u32]
+    lib.qsa_score_topk_merge_modes_offset.restype = sz
     lib.qsa_score_topk.argtypes = [P, P, P, i32, P, i64, i32, i32, f64, u32, st, P, P, P, P, sz, P]
     lib.qsa_score_topk.restype = st
     lib.qsa_sparse_attn_prefill.argtypes = [P, P, P, i32, P, P, i64, P, P, i32, i32, i32, i32, f32, st,
@@ -199,6 +202,18 @@ def score_topk_workspace_size(rows: int, max_visible_blocks: int, top_k: int, dt
                               flags: int = 0) -> int:
     return int(load().qsa_score_topk_workspace_size(int(rows), int(max_visible_blocks), int(top_k),
                                                     int(dtype_code), int(flags)))
+
+
+MERGE_MODES = {0: "none", 1: "staged", 2: "prefiltered", 3: "list_walk", 4: "recomputed"}
+
+
+def score_topk_merge_modes_offset(rows: int, max_visible_blocks: int, top_k: int, dtype_code: int,
+                                  flags: int = 0) -> Optional[int]:
+    """Byte offset of the fused scorer's per-row merge modes in a score_topk
+    workspace (int32 [rows], see MERGE_MODES), or None for the per-row path."""
+    off = int(load().qsa_score_topk_merge_modes_offset(int(rows), int(max_visible_blocks), int(top_k),
+                                                       int(dtype_code), int(flags)))
+    return None if off == ctypes.c_size_t(-1).value else off
 
 
 def score_topk(q_index, row_seq, row_pos, pooled, max_visible_blocks: int, top_k: int,

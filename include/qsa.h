@@ -186,6 +186,21 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
                             size_t workspace_bytes, void *stream);
 
 /*
+ * Diagnostics of the many-rows scorer.  When qsa_score_topk (or its FP8 and
+ * paged forms) runs the fused MFMA scorer for these arguments, the call
+ * leaves in its workspace, at this byte offset, int32 [rows]: how the merge
+ * ranked each row -- 0 no visible block; 1 all of the row's candidate pairs
+ * ranked in LDS; 2 a histogram first narrowed the candidates to those that
+ * can be kept; 3 radix passes over the candidate lists (the k-th score's bin
+ * too crowded to stage); 4 the row's scores recomputed and ranked (too few
+ * candidates, a full candidate list, or too many exact ties).  The selection
+ * is the same whatever the mode.  Returns (size_t)-1 when the arguments are
+ * invalid or the call would use the per-row scorer (no such record).
+ */
+size_t qsa_score_topk_merge_modes_offset(int32_t rows, int32_t max_visible_blocks, int32_t top_k,
+                                         qsa_dtype_t dtype, uint32_t flags);
+
+/*
  * qsa_score_topk on FP8 keys (as written by qsa_pool_index_keys_fp8).  The
  * index queries are bf16 and rotated as in qsa_score_topk; the key of block b
  * is code_b * scale_b, so raw(t,b) = scale_b * sum_h max(0, <q~_h, code_b>)
@@ -362,7 +377,10 @@ const char *qsa_last_device_error(void);
  * launches of kernel `name` were recorded and their total duration in
  * milliseconds (*total_ms).  qsa_profile_reset() drops the records.  A kernel
  * name not launched returns 0.  Timing is off by default and costs nothing
- * then.  Not thread-safe: enable it from one host thread at a time.
+ * then.  Thread-safe: the flag is atomic and the records are kept under a
+ * lock, so calls from several threads are all recorded in one list; a
+ * qsa_profile_reset() while another thread is launching may drop that
+ * launch's record.  The per-kernel sums read the records of every thread.
  */
 qsa_status_t qsa_profile_enable(int enable);
 qsa_status_t qsa_profile_reset(void);

@@ -112,6 +112,19 @@ def test_score_topk_validation(libqsa):
     assert call(theta=float("nan")) == qsa.ERR_INVALID_ARG
 
 
+def test_merge_modes_offset(libqsa):
+    # the fused scorer's per-row merge record sits inside its workspace; the
+    # per-row scorer keeps none
+    for rows, nb, k, flags in ((8192, 65536, 512, 0), (100, 5000, 37, qsa.FLAG_SCORE_GEMM)):
+        ws = qsa.score_topk_workspace_size(rows, nb, k, qsa.BF16, flags)
+        off = qsa.score_topk_merge_modes_offset(rows, nb, k, qsa.BF16, flags)
+        assert off is not None and off % 256 == 0 and off + 4 * rows <= ws
+    assert qsa.score_topk_merge_modes_offset(4, 100, 16, qsa.BF16) is None          # few rows: per-row path
+    assert qsa.score_topk_merge_modes_offset(8192, 65536, 512, qsa.BF16, qsa.FLAG_SCORE_ROWS) is None
+    assert qsa.score_topk_merge_modes_offset(0, 100, 16, qsa.BF16) is None
+    assert qsa.score_topk_merge_modes_offset(100, 100, 0, qsa.BF16) is None
+
+
 def test_fp8_validation(libqsa):
     f = libqsa.qsa_pool_index_keys_fp8
     assert f(A, 1024, B_, C, 8, 0, 0, 2, 1e7, 0, qsa.BF16, None) == qsa.OK          # empty batch

@@ -1,9 +1,11 @@
 """Parity at the five workloads' full sizes, in the launch configuration the
 benchmark times (default score path, caller-provided workspaces, the chunk's
-new blocks pooled on top of a pooled context).  The GPU runs every row; the
-oracle checks a sample of rows it can compute one by one: selections under the
-near-tie rule, then attention on the GPU's own selection (the same tolerances
-as the small-size parity tests).
+new blocks pooled on top of a pooled context).  The GPU runs every row.  The
+oracle checks the selection of every row under the near-tie rule (prefill
+rows in batches, so the oracle's raw scores stay in memory), and attention on
+the GPU's own selection on a sample of rows (decode: every row), with the
+tolerances of the small-size parity tests.  Prefill prints how many rows each
+of the fused scorer's merge modes ranked.
 """
 import numpy as np
 import pytest
@@ -42,15 +44,29 @@ def _prefill(spec):
                                  workspace=ws, want_scores=False)
     out, lse = qsa.sparse_attn_prefill(dev(w["q"], dt), seq, pos, dev(w["k_cache"], dt),
                                        dev(w["v_cache"], dt), sel, cnt)
+    moff = qsa.score_topk_merge_modes_offset(R, max_nb, k, qsa.BF16)
+    assert moff is not None   # many rows: the fused scorer
+    modes = host(ws[moff:moff + 4 * R]).view(np.int32)
+    counts = {qsa.MERGE_MODES[m]: int((modes == m).sum()) for m in sorted(qsa.MERGE_MODES)}
+    print(f"[full-size] {spec.name}: rows per merge mode {counts}", flush=True)
+    assert set(np.unique(modes).tolist()) <= set(qsa.MERGE_MODES)
     pooled = host(pooled_d)
     o_pooled = oracle.pool(w["raw_keys"], 0, nb, spec.theta)
     assert np.abs(pooled.astype(np.int32) - o_pooled.astype(np.int32)).max() <= 1
+    g_sel_all, g_cnt_all = host(sel), host(cnt)
+    batch = max(64, int(2.5e8 // (8 * nb)))   # rows per oracle call: its raw scores stay near 256 MB
+    swaps = 0
+    for r0 in range(0, R, batch):
+        rr = np.arange(r0, min(R, r0 + batch))
+        o_sel, o_cnt, _, o_raw = oracle.score_topk(w["idx_q"][rr], w["row_seq"][rr], w["row_pos"][rr], pooled,
+                                                   k, spec.theta, want_raw=True)
+        swaps += check_selection(g_sel_all[rr], g_cnt_all[rr], o_sel, o_cnt, o_raw, exact=False)
+        del o_raw
+        print(f"[full-size] {spec.name}: selections of rows {rr[0]}..{rr[-1]} match ({swaps} near-tie swaps)",
+              flush=True)
     rows = _sample_rows(R)
-    print(f"[full-size] {spec.name}: checking rows {rows.tolist()}", flush=True)
-    g_sel, g_cnt = host(sel)[rows], host(cnt)[rows]
-    o_sel, o_cnt, _, o_raw = oracle.score_topk(w["idx_q"][rows], w["row_seq"][rows], w["row_pos"][rows], pooled,
-                                               k, spec.theta, want_raw=True)
-    check_selection(g_sel, g_cnt, o_sel, o_cnt, o_raw, exact=False)
+    print(f"[full-size] {spec.name}: attention on rows {rows.tolist()}", flush=True)
+    g_sel, g_cnt = g_sel_all[rows], g_cnt_all[rows]
     want, want_lse = oracle.sparse_attn_prefill(w["q"][rows], w["row_seq"][rows], w["row_pos"][rows],
                                                 w["k_cache"], w["v_cache"], g_sel, g_cnt)
     assert_close_out(host(out)[rows], want, dt)
@@ -100,8 +116,9 @@ def _decode(spec):
     np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", synth.CONFIG_ORDER)
-def test_full_size_sampled(gpu, name):
+def test_full_size(gpu, name):
     spec = synth.SPECS[name]
     if spec.kind == "prefill":
         _prefill(spec)

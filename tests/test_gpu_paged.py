@@ -1,11 +1,13 @@
 """Paged KV pool on the GPU ([SGL] "Qwen Sparse Attention": the compressed
 keys and K/V live in a paged pool; one compressed key per four token slots at
-full_slot / 4).  Paging only moves data: every paged call must give exactly
-the result of the contiguous call on the same logical data (bit for bit),
-and the contiguous calls are checked against the oracle elsewhere.  One case
-per entry point is also checked against the oracle directly, and a decode
-loop writes its compressed keys with qsa_pool_append straight into the paged
-pool that the paged scorer reads.
+full_slot / 4).  Every paged path is checked against the oracle on the
+logical (unpaged) data, with the tolerances of the contiguous parity tests:
+pooled keys within 1 bf16 ulp (codes within one E4M3 step), selections
+identical except near-ties within 1e-3 relative of the k-th score, attention
+within 2e-2 abs + 1e-2 rel.  Paging only moves data, so each paged call is
+also required to equal the contiguous call on the same logical data bit for
+bit.  A decode loop writes its compressed keys with qsa_pool_append straight
+into the paged pool that the paged scorer reads.
 """
 import numpy as np
 import pytest
@@ -83,6 +85,23 @@ def test_pool_paged_equals_contiguous(gpu, fmt, P):
     np.testing.assert_array_equal(got_c[slots], want_c[slots])
     if fmt == "fp8":
         np.testing.assert_array_equal(got_s[slots], want_s[slots])
+    # the oracle on the logical keys: the paged pool gathered back to [B][NB]
+    logical = got_c[slots].reshape(B, NB - b0, DIM)
+    if fmt == "fp8":
+        o_codes, o_scales = oracle.pool_fp8(raw, b0, NB, THETA)
+        np.testing.assert_allclose(got_s[slots].reshape(B, NB - b0), o_scales[:, b0:], rtol=4e-7, atol=0)
+        gv, ov = oracle.fp8_to_float(logical), oracle.fp8_to_float(o_codes[:, b0:])
+        step = np.where(np.abs(ov) < 2.0 ** -6, 2.0 ** -9,
+                        2.0 ** (np.floor(np.log2(np.maximum(np.abs(ov), 2.0 ** -6))) - 3))
+        assert np.all(np.abs(gv - ov) <= step * (1 + 1e-9)), "a code is more than one step from the oracle's"
+        assert np.mean(logical == o_codes[:, b0:]) > 0.999
+    else:
+        o_pooled = oracle.pool(raw, b0, NB, THETA)[:, b0:]
+        if fmt == "bf16":
+            diff = np.abs(logical.astype(np.int32) - o_pooled.astype(np.int32))
+            assert diff.max() <= 1 and (diff == 0).mean() > 0.999
+        else:
+            np.testing.assert_allclose(logical, o_pooled, rtol=2e-6, atol=1e-6)
     untouched = np.setdiff1d(np.arange(nkeys), slots)
     fill = {"fp8": 7, "bf16": synth.bf16_bits(np.float32(3.0)), "f32": 3.0}[fmt]
     assert np.all(got_c[untouched] == fill)
@@ -111,9 +130,32 @@ def test_score_topk_paged_equals_contiguous(gpu, P, path, R):
                                                flags=flags)]
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
-    if path == "rows" and P == 16:   # and once against the oracle on the logical keys
-        o_sel, o_cnt, _, o_raw = oracle.score_topk(iq, seq, pos, pooled, k, THETA, want_raw=True)
-        check_selection(b[0], b[1], o_sel, o_cnt, o_raw, exact=False)
+    o_sel, o_cnt, o_sc, o_raw = oracle.score_topk(iq, seq, pos, pooled, k, THETA, want_raw=True)
+    check_selection(b[0], b[1], o_sel, o_cnt, o_raw, exact=False)
+    same = np.array([np.array_equal(b[0][r], o_sel[r]) for r in range(R)])
+    np.testing.assert_allclose(b[2][same], o_sc[same], rtol=2e-5, atol=1e-5)   # scaled scores of kept blocks
+
+
+@pytest.mark.parametrize("path,R", [("rows", 12), ("gemm", 100)])
+def test_score_topk_paged_integer_inputs_exact(gpu, path, R):
+    # integer keys and queries with RoPE off: every score is exact on both
+    # sides, so the paged selection equals the oracle's with no exception
+    rng = np.random.default_rng(83)
+    B, NB, k, P = 2, 2600, 256, 16
+    L = 4 * NB
+    pooled = synth.bf16_bits(rng.integers(-3, 4, size=(B, NB, DIM)).astype(np.float32))
+    iq = synth.bf16_bits(rng.integers(-2, 3, size=(R, 4, DIM)).astype(np.float32))
+    seq = rng.integers(0, B, R).astype(np.int32)
+    pos = rng.integers(0, L, R).astype(np.int32)
+    pos[:2] = [L - 1, 4 * k + 1]
+    table, n_pages = _layout(rng, B, L, P)
+    paged = _scatter_keys(pooled, table, P, n_pages)
+    flags = (qsa.FLAG_SCORE_ROWS if path == "rows" else qsa.FLAG_SCORE_GEMM) | qsa.FLAG_NO_ROPE
+    got = [host(x) for x in qsa.score_topk_paged(dev(iq, "bf16"), dev(seq, "i"), dev(pos, "i"), dev(table, "i"),
+                                                 P, NB, k, THETA, pooled=dev(paged, "bf16"), flags=flags)]
+    o_sel, o_cnt, _, o_raw = oracle.score_topk(iq, seq, pos, pooled, k, THETA, flags=oracle.FLAG_NO_ROPE,
+                                               want_raw=True)
+    check_selection(got[0], got[1], o_sel, o_cnt, o_raw, exact=True)
 
 
 @pytest.mark.parametrize("path,R", [("rows", 8), ("gemm", 100)])
@@ -140,6 +182,10 @@ def test_score_topk_paged_fp8_equals_contiguous(gpu, path, R):
                                                flags=flags)]
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+    # the oracle scores the logical FP8 keys (the GPU's codes and scales)
+    o_sel, o_cnt, _, o_raw = oracle.score_topk_fp8(iq, seq, pos, host(codes), host(scales), k, THETA,
+                                                   want_raw=True)
+    check_selection(b[0], b[1], o_sel, o_cnt, o_raw, exact=False)
 
 
 @pytest.mark.parametrize("P", [4, 64])
@@ -169,9 +215,9 @@ def test_attn_prefill_paged_equals_contiguous(gpu, P, Hq, Hkv):
                                            dev(sel, "i"), dev(cnt, "i"))
     np.testing.assert_array_equal(host(o1), host(o2))
     np.testing.assert_array_equal(host(l1), host(l2))
-    if P == 4 and Hq == 8:
-        want, want_lse = oracle.sparse_attn_prefill(q, seq, pos, kc, vc, sel, cnt)
-        assert_close_out(host(o2), want, "bf16")
+    want, want_lse = oracle.sparse_attn_prefill(q, seq, pos, kc, vc, sel, cnt)
+    assert_close_out(host(o2), want, "bf16")
+    np.testing.assert_allclose(host(l2), want_lse, rtol=1e-5, atol=1e-4)
 
 
 @pytest.mark.parametrize("P", [8, 128])
@@ -229,3 +275,14 @@ def test_decode_loop_pool_append_into_paged_pool(gpu):
             want = [host(x) for x in qsa.score_topk(dev(iq, "bf16"), seqs, dev(pos, "i"), pooled, nb, k, THETA)]
             for x, y in zip(got, want):
                 np.testing.assert_array_equal(x, y)
+            # the oracle: the appended keys, gathered to logical order, are the
+            # oracle's pooled keys, and the selection is the oracle's on them
+            comp_h = host(comp)
+            blocks = np.arange(nb)
+            logical = np.stack([comp_h[slots[s, 4 * blocks] // 4] for s in range(B)])
+            o_pooled = oracle.pool(raw, 0, nb, THETA)
+            diff = np.abs(logical.astype(np.int32) - o_pooled.astype(np.int32))
+            assert diff.max() <= 1 and (diff == 0).mean() > 0.999
+            o_sel, o_cnt, _, o_raw = oracle.score_topk(iq, np.arange(B, dtype=np.int32), pos, logical, k, THETA,
+                                                       want_raw=True)
+            check_selection(got[0], got[1], o_sel, o_cnt, o_raw, exact=False)

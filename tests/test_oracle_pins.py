@@ -523,6 +523,41 @@ def test_position_budget_from_the_pages():
     assert sel_tok + GOLD["tail_tokens_max"]["value"] == mx
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_index_cache_cut_from_the_pages(dtype):
+    # "Day-0 Support in SGLang", section "Qwen Sparse Attention": one compressed
+    # index key per four tokens plus a four-slot per-request ring of raw keys,
+    # instead of retaining the raw index keys of the whole context, cuts the
+    # index cache by 80%.  Reading: the cache it replaces held every token's
+    # raw key next to the compressed keys (raw + raw/4 per token); the cut of
+    # keeping only compressed keys and the ring is then 1 - (L/4 + 4)/(5L/4),
+    # which tends to 80% from below.  The per-token bytes come from running
+    # the incremental pooling over a stream: it writes one compressed key per
+    # four token slots and touches only the ring besides.
+    rng = np.random.default_rng(12)
+    B, L = 2, 64
+    keys = rng.standard_normal((B, L, DIM)).astype(np.float32)
+    keys = synth.bf16_bits(keys) if dtype == "bf16" else keys
+    esz = keys.dtype.itemsize
+    ring = np.zeros((B, 4, DIM), keys.dtype)
+    comp = np.zeros((B * L // 4, DIM), keys.dtype)
+    sentinel = comp.copy()
+    for t in range(L):
+        slots = np.arange(B, dtype=np.int64) * L + t   # contiguous pages: full_slot = s*L + t
+        oracle.pool_append(keys[:, t].copy(), np.full(B, t, np.int32), slots, ring, comp, 1.0e7)
+    written = np.any(comp != sentinel, axis=1).sum()
+    assert written == B * L // 4                           # one compressed key per 4 tokens
+    comp_bytes_per_token = written * DIM * esz / (B * L)
+    raw_bytes_per_token = DIM * esz
+    ring_bytes_per_request = ring[0].nbytes
+    want = GOLD["index_cache_cut_percent"]["value"] / 100.0
+    for ctx in (262_144, 1_048_576):
+        before = ctx * (raw_bytes_per_token + comp_bytes_per_token)
+        after = ctx * comp_bytes_per_token + ring_bytes_per_request
+        cut = 1.0 - after / before
+        assert cut <= want and want - cut < 2e-5, (ctx, cut)
+
+
 def test_decode_shared_selection_with_drafted_positions():
     # IndexShare: rows after the anchor reuse its selection and add [tail_start, t]
     rng = np.random.default_rng(40)
