@@ -86,6 +86,16 @@ def _load():
     lib.qsa_oracle_sparse_attn_decode_fp8kv.argtypes = [P, P, i32, i32, P, P, P, i64, f64, f64, P, P, i32,
                                                         i32, i32, i32, f64, i32, P, P]
     lib.qsa_oracle_sparse_attn_decode_fp8kv.restype = ctypes.c_int
+    lib.qsa_oracle_rope_freq.argtypes = [P, i64, P]
+    lib.qsa_oracle_rope_freq.restype = None
+    lib.qsa_oracle_rope_plain_freq.argtypes = [f64, P]
+    lib.qsa_oracle_rope_plain_freq.restype = None
+    lib.qsa_oracle_yarn_freq.argtypes = [f64, f64, f64, f64, f64, P]
+    lib.qsa_oracle_yarn_freq.restype = ctypes.c_int
+    lib.qsa_oracle_pool_ex.argtypes = [P, i64, P, i64, i32, i32, i32, P, P, u32, i32]
+    lib.qsa_oracle_pool_ex.restype = ctypes.c_int
+    lib.qsa_oracle_score_topk_ex.argtypes = [P, P, P, i32, P, i64, i32, P, u32, i32, P, P, P, P, i64]
+    lib.qsa_oracle_score_topk_ex.restype = ctypes.c_int
     lib.qsa_oracle_threads.argtypes = []
     lib.qsa_oracle_threads.restype = ctypes.c_int
     _lib = lib
@@ -152,6 +162,55 @@ def rope(vec, pos: int, theta: float) -> np.ndarray:
     v = np.array(vec, dtype=np.float64, copy=True).reshape(DIM)
     _load().qsa_oracle_rope(_ptr(v), int(pos), float(theta))
     return v
+
+
+def rope_freq(vec, pos: int, inv_freq) -> np.ndarray:
+    """Rotate one 128-d vector at `pos` with the 64 pair frequencies given."""
+    v = np.array(vec, dtype=np.float64, copy=True).reshape(DIM)
+    f = _c(inv_freq, np.float64)
+    assert f.shape == (DIM // 2,)
+    _load().qsa_oracle_rope_freq(_ptr(v), int(pos), _ptr(f))
+    return v
+
+
+def plain_freq(theta: float) -> np.ndarray:
+    """Plain RoPE's pair frequencies theta^(-j/64)."""
+    f = np.empty(DIM // 2, np.float64)
+    _load().qsa_oracle_rope_plain_freq(float(theta), _ptr(f))
+    return f
+
+
+# YaRN for the 1M-token extension of the 262,144-token native context (see
+# qsa_oracle_yarn_freq): scale 4, original context 262,144, ramp 1..32.
+YARN_1M = dict(s=4.0, L=262144.0, alpha=1.0, beta=32.0)
+
+
+def yarn_freq(base: float, s: float, L: float, alpha: float = 1.0, beta: float = 32.0) -> np.ndarray:
+    """YaRN's interpolated pair frequencies h(theta_d) (qsa_oracle_yarn_freq)."""
+    f = np.empty(DIM // 2, np.float64)
+    _check(_load().qsa_oracle_yarn_freq(float(base), float(s), float(L), float(alpha), float(beta), _ptr(f)),
+           "yarn_freq")
+    return f
+
+
+def pool_ex(raw, block_begin: int, block_end: int, inv_freq, norm_weight=None, flags: int = 0,
+            pooled=None) -> np.ndarray:
+    """pool() with the rotation's pair frequencies given and an optional
+    learned per-dim weight of the RMS norm (needs FLAG_POOL_RMSNORM)."""
+    raw = _c(raw)
+    dt = _dtype_code(raw)
+    B, L, d = raw.shape
+    assert d == DIM and 4 * block_end <= L
+    if pooled is None:
+        pooled = np.zeros((B, block_end, DIM), dtype=raw.dtype)
+    assert pooled.dtype == raw.dtype and pooled.flags.c_contiguous
+    f = _c(inv_freq, np.float64)
+    w = None if norm_weight is None else _c(norm_weight, np.float32)
+    assert f.shape == (DIM // 2,) and (w is None or w.shape == (DIM,))
+    rc = _load().qsa_oracle_pool_ex(_ptr(raw), L * DIM, _ptr(pooled), pooled.shape[1] * DIM, B, int(block_begin),
+                                    int(block_end), _ptr(f), _ptr(w), int(flags), dt)
+    _check(rc, "pool_ex")
+    return pooled
 
 
 def pool(raw, block_begin: int, block_end: int, theta: float, flags: int = 0,
@@ -233,6 +292,34 @@ def score_topk(q_index, row_seq, row_pos, pooled, top_k: int, theta: float, flag
                                        NB * DIM, int(top_k), float(theta), int(flags), dt,
                                        _ptr(sel), _ptr(cnt), _ptr(sc), _ptr(raw), NB)
     _check(rc, "score_topk")
+    return sel, cnt, sc, raw
+
+
+def score_topk_ex(q_index, row_seq, row_pos, pooled, top_k: int, inv_freq, flags: int = 0,
+                  want_raw: bool = False):
+    """score_topk() with the index queries rotated by the given pair
+    frequencies (the keys pooled with the same ones)."""
+    q_index = _c(q_index)
+    pooled = _c(pooled)
+    dt = _dtype_code(q_index)
+    assert _dtype_code(pooled) == dt
+    row_seq = _c(row_seq, np.int32)
+    row_pos = _c(row_pos, np.int32)
+    R = q_index.shape[0]
+    NB = pooled.shape[1]
+    assert q_index.shape[1:] == (IDX_HEADS, DIM)
+    for r in range(R):
+        assert (int(row_pos[r]) + 1) // BLOCK <= NB
+    f = _c(inv_freq, np.float64)
+    assert f.shape == (DIM // 2,)
+    sel = np.empty((R, top_k), np.int32)
+    cnt = np.empty((R,), np.int32)
+    sc = np.empty((R, top_k), np.float32)
+    raw = np.full((R, NB), np.nan, np.float64) if want_raw else None
+    rc = _load().qsa_oracle_score_topk_ex(_ptr(q_index), _ptr(row_seq), _ptr(row_pos), R, _ptr(pooled),
+                                          NB * DIM, int(top_k), _ptr(f), int(flags), dt,
+                                          _ptr(sel), _ptr(cnt), _ptr(sc), _ptr(raw), NB)
+    _check(rc, "score_topk_ex")
     return sel, cnt, sc, raw
 
 

@@ -200,6 +200,75 @@ void qsa_oracle_rope(double *v, int64_t pos, double theta)
     }
 }
 
+/*
+ * The same rotation with the 64 pair frequencies given (inv_freq[j] for the
+ * pair (j, j + 64)): the angle of pair j at `pos` is pos * inv_freq[j].
+ */
+void qsa_oracle_rope_freq(double *v, int64_t pos, const double *inv_freq)
+{
+    for (int j = 0; j < OR_HALF; ++j) {
+        double ang = (double)pos * inv_freq[j];
+        double c = cos(ang), s = sin(ang);
+        double x = v[j], y = v[j + OR_HALF];
+        v[j] = x * c - y * s;
+        v[j + OR_HALF] = x * s + y * c;
+    }
+}
+
+/* Plain RoPE's frequencies theta^(-j/64), as qsa_oracle_rope forms them. */
+void qsa_oracle_rope_plain_freq(double theta, double *inv_freq)
+{
+    for (int j = 0; j < OR_HALF; ++j)
+        inv_freq[j] = pow(theta, -(double)j / (double)OR_HALF);
+}
+
+/*
+ * YaRN-scaled frequencies for long contexts.  The pages say only that the
+ * 262,144-token native context extends to one million tokens with YaRN
+ * (flozi.net guide, "What the published evidence does and does not show";
+ * aicontrolled journal, "Remembering does not require looking at everything
+ * at once"); they give no parameters.  Reading: the published YaRN method
+ * (Peng, Quesnelle, Fan and Shippole, "YaRN: Efficient Context Window
+ * Extension of Large Language Models", 2023), its frequency interpolation
+ * "by parts", in its notation:
+ *   theta_d = base^(-2d/|D|) is pair d's frequency and lambda_d = 2 pi / theta_d
+ *     its wavelength (|D| = 128 rotary dims, so theta_d = base^(-d/64));
+ *   r(d) = L / lambda_d is how many turns pair d makes over the original
+ *     context L;
+ *   the ramp gamma(r) is 0 for r < alpha, 1 for r > beta and
+ *     (r - alpha) / (beta - alpha) between;
+ *   h(theta_d) = (1 - gamma(r(d))) * theta_d / s + gamma(r(d)) * theta_d,
+ *     with s the context scale factor.
+ * Pairs that turn many times over L keep their frequency, pairs that turn
+ * less than once are interpolated by 1/s, and the ramp blends in between.
+ * For the indexer, s = 1,048,576 / 262,144 = 4, L = 262,144 and the paper's
+ * alpha = 1, beta = 32.  YaRN's attention temperature scales logits by a
+ * positive constant; the indexer's ranking of ReLU sums cannot see it, so it
+ * is not applied here (for the final attention it is part of the softmax
+ * scale the caller passes).  s == 1 gives plain RoPE's frequencies up to
+ * rounding.
+ */
+int qsa_oracle_yarn_freq(double base, double s, double L, double alpha, double beta, double *inv_freq)
+{
+    if (!(base > 1.0) || !(s >= 1.0) || !(L > 0.0) || !(beta > alpha) || !inv_freq)
+        return OR_ERR_ARG;
+    const double two_pi = 2.0 * acos(-1.0);
+    for (int d = 0; d < OR_HALF; ++d) {
+        const double theta_d = pow(base, -2.0 * d / (double)OR_DIM);
+        const double lambda_d = two_pi / theta_d;
+        const double r = L / lambda_d;
+        double gamma;
+        if (r < alpha)
+            gamma = 0.0;
+        else if (r > beta)
+            gamma = 1.0;
+        else
+            gamma = (r - alpha) / (beta - alpha);
+        inv_freq[d] = (1.0 - gamma) * theta_d / s + gamma * theta_d;
+    }
+    return OR_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* a1-a3: block pooling, then RoPE at the block's first position             */
 /* ------------------------------------------------------------------------ */
@@ -221,9 +290,9 @@ void qsa_oracle_rope(double *v, int64_t pos, double theta)
  *         raw + s*raw_seq_stride + i*128.
  * pooled: [batch][pooled_seq_stride], block b at pooled + s*stride + b*128.
  */
-int qsa_oracle_pool(const void *raw, int64_t raw_seq_stride, void *pooled,
-                    int64_t pooled_seq_stride, int32_t batch, int32_t block_begin,
-                    int32_t block_end, double theta, uint32_t flags, int32_t dtype)
+static int pool_core(const void *raw, int64_t raw_seq_stride, void *pooled, int64_t pooled_seq_stride,
+                     int32_t batch, int32_t block_begin, int32_t block_end, const double *inv_freq,
+                     const float *norm_weight, uint32_t flags, int32_t dtype)
 {
     if (!raw || !pooled || batch < 0 || block_begin < 0 || block_end < block_begin)
         return OR_ERR_ARG;
@@ -249,13 +318,45 @@ int qsa_oracle_pool(const void *raw, int64_t raw_seq_stride, void *pooled,
             double inv = 1.0 / sqrt(ss / OR_DIM + 1e-6);
             for (int d = 0; d < OR_DIM; ++d)
                 m[d] *= inv;
+            if (norm_weight)
+                for (int d = 0; d < OR_DIM; ++d)
+                    m[d] *= (double)norm_weight[d];
         }
         if (!(flags & OR_FLAG_NO_ROPE))
-            qsa_oracle_rope(m, OR_BLOCK * b, theta);
+            qsa_oracle_rope_freq(m, OR_BLOCK * b, inv_freq);
         for (int d = 0; d < OR_DIM; ++d)
             store_elem(pooled, s * pooled_seq_stride + b * OR_DIM + d, dtype, m[d]);
     }
     return OR_OK;
+}
+
+int qsa_oracle_pool(const void *raw, int64_t raw_seq_stride, void *pooled,
+                    int64_t pooled_seq_stride, int32_t batch, int32_t block_begin,
+                    int32_t block_end, double theta, uint32_t flags, int32_t dtype)
+{
+    double inv_freq[OR_HALF];
+    qsa_oracle_rope_plain_freq(theta, inv_freq);
+    return pool_core(raw, raw_seq_stride, pooled, pooled_seq_stride, batch, block_begin, block_end, inv_freq,
+                     NULL, flags, dtype);
+}
+
+/*
+ * qsa_oracle_pool with the rotation's pair frequencies given (plain RoPE's, or
+ * YaRN's from qsa_oracle_yarn_freq) and a learned per-dimension weight for the
+ * normalization.  [SGL] says the averaged keys are "normalized" before the
+ * rotation and gives neither the norm nor a weight; reading, for a learned
+ * weight w: with OR_FLAG_POOL_RMSNORM, m <- (m / sqrt(mean(m^2) + 1e-6)) * w
+ * element by element (RMS norm with a weight, as in the rest of the model);
+ * norm_weight NULL is unit weight.  A weight without the flag is an error.
+ */
+int qsa_oracle_pool_ex(const void *raw, int64_t raw_seq_stride, void *pooled, int64_t pooled_seq_stride,
+                       int32_t batch, int32_t block_begin, int32_t block_end, const double *inv_freq,
+                       const float *norm_weight, uint32_t flags, int32_t dtype)
+{
+    if (!inv_freq || (norm_weight && !(flags & OR_FLAG_POOL_RMSNORM)))
+        return OR_ERR_ARG;
+    return pool_core(raw, raw_seq_stride, pooled, pooled_seq_stride, batch, block_begin, block_end, inv_freq,
+                     norm_weight, flags, dtype);
 }
 
 /*
@@ -459,9 +560,9 @@ static double block_raw(const double q[OR_IDX_HEADS][OR_DIM], const key_source *
  * raw_out[r*raw_stride + b].
  */
 static int score_topk_core(const void *q_index, int q_dtype, const int32_t *row_seq, const int32_t *row_pos,
-                           int32_t rows, const key_source *ks, int64_t stride, int32_t top_k, double theta,
-                           uint32_t flags, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
-                           double *raw_out, int64_t raw_stride)
+                           int32_t rows, const key_source *ks, int64_t stride, int32_t top_k,
+                           const double *inv_freq, uint32_t flags, int32_t *sel_blocks, int32_t *sel_count,
+                           float *sel_scores, double *raw_out, int64_t raw_stride)
 {
     int failed = 0;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -474,7 +575,7 @@ static int score_topk_core(const void *q_index, int q_dtype, const int32_t *row_
             for (int d = 0; d < OR_DIM; ++d)
                 q[h][d] = load_elem(q_index, ((int64_t)r * OR_IDX_HEADS + h) * OR_DIM + d, q_dtype);
             if (!(flags & OR_FLAG_NO_ROPE))
-                qsa_oracle_rope(q[h], t, theta);
+                qsa_oracle_rope_freq(q[h], t, inv_freq);
             for (int d = 0; d < OR_DIM; ++d)
                 q[h][d] = round_to_dtype(q[h][d], q_dtype);
         }
@@ -526,8 +627,27 @@ int qsa_oracle_score_topk(const void *q_index, const int32_t *row_seq, const int
         !sel_count || pooled_seq_stride % OR_DIM)
         return OR_ERR_ARG;
     const key_source ks = {pooled, dtype, NULL, NULL};
-    return score_topk_core(q_index, dtype, row_seq, row_pos, rows, &ks, pooled_seq_stride / OR_DIM, top_k, theta,
-                           flags, sel_blocks, sel_count, sel_scores, raw_out, raw_stride);
+    double inv_freq[OR_HALF];
+    qsa_oracle_rope_plain_freq(theta, inv_freq);
+    return score_topk_core(q_index, dtype, row_seq, row_pos, rows, &ks, pooled_seq_stride / OR_DIM, top_k,
+                           inv_freq, flags, sel_blocks, sel_count, sel_scores, raw_out, raw_stride);
+}
+
+/* qsa_oracle_score_topk with the index queries rotated by the given pair
+ * frequencies (plain RoPE's, or YaRN's from qsa_oracle_yarn_freq): the keys
+ * must have been pooled with the same ones. */
+int qsa_oracle_score_topk_ex(const void *q_index, const int32_t *row_seq, const int32_t *row_pos,
+                             int32_t rows, const void *pooled, int64_t pooled_seq_stride,
+                             int32_t top_k, const double *inv_freq, uint32_t flags, int32_t dtype,
+                             int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
+                             double *raw_out, int64_t raw_stride)
+{
+    if (rows < 0 || top_k < 1 || !q_index || !row_seq || !row_pos || !pooled || !sel_blocks ||
+        !sel_count || !inv_freq || pooled_seq_stride % OR_DIM)
+        return OR_ERR_ARG;
+    const key_source ks = {pooled, dtype, NULL, NULL};
+    return score_topk_core(q_index, dtype, row_seq, row_pos, rows, &ks, pooled_seq_stride / OR_DIM, top_k,
+                           inv_freq, flags, sel_blocks, sel_count, sel_scores, raw_out, raw_stride);
 }
 
 /* The same with FP8 keys (see qsa_oracle_pool_fp8); pooled_seq_stride counts
@@ -543,8 +663,10 @@ int qsa_oracle_score_topk_fp8(const void *q_index, int32_t q_dtype, const int32_
         !sel_count)
         return OR_ERR_ARG;
     const key_source ks = {NULL, 0, codes, scales};
-    return score_topk_core(q_index, q_dtype, row_seq, row_pos, rows, &ks, pooled_seq_stride, top_k, theta, flags,
-                           sel_blocks, sel_count, sel_scores, raw_out, raw_stride);
+    double inv_freq[OR_HALF];
+    qsa_oracle_rope_plain_freq(theta, inv_freq);
+    return score_topk_core(q_index, q_dtype, row_seq, row_pos, rows, &ks, pooled_seq_stride, top_k, inv_freq,
+                           flags, sel_blocks, sel_count, sel_scores, raw_out, raw_stride);
 }
 
 /* ------------------------------------------------------------------------ */

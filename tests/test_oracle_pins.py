@@ -807,3 +807,128 @@ def test_fp8_codes_match_torch_float8_e4m3fn():
     mine = oracle.fp8_from_float(x32.astype(np.float64))
     theirs = torch.from_numpy(x32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     np.testing.assert_array_equal(mine, theirs)
+
+
+# --------------------------------------------------------------------------
+# Learned-weight normalization of the pooled key, and YaRN-scaled RoPE
+# ("normalized" in the SGLang post's QSA section; YaRN to 1M tokens in the
+# flozi.net guide and the aicontrolled journal)
+# --------------------------------------------------------------------------
+
+def test_yarn_worked_example_by_regime():
+    # base 2^64 makes pair d's frequency 2^-d, and L = 2*pi*2^10 makes it
+    # turn r(d) = 2^(10-d) times over the original context: d = 5 sits on
+    # the ramp's top (r = 32 -> unchanged), d = 10 on its foot (r = 1 -> 1/s),
+    # d = 6 in between (r = 16: gamma = 15/31, h = (16/31)/4 + 15/31 = 19/31
+    # of the frequency, at s = 4), d = 2 above it and d = 20 below it.
+    L = 2 * math.pi * 2 ** 10
+    f = oracle.yarn_freq(2.0 ** 64, s=4.0, L=L, alpha=1.0, beta=32.0)
+    for d, factor in ((2, 1.0), (5, 1.0), (6, 19 / 31), (8, (1 - 3 / 31) / 4 + 3 / 31), (10, 0.25),
+                      (20, 0.25)):
+        assert math.isclose(f[d], factor * 2.0 ** -d, rel_tol=1e-12), (d, f[d] / 2.0 ** -d)
+    # frequencies fall with d and stay within [theta/s, theta]
+    plain = oracle.plain_freq(2.0 ** 64)
+    assert np.all(np.diff(f) < 0)
+    assert np.all(f <= plain * (1 + 1e-15)) and np.all(f >= plain / 4 * (1 - 1e-15))
+    with pytest.raises(RuntimeError):
+        oracle.yarn_freq(1e7, s=0.5, L=L)
+    with pytest.raises(RuntimeError):
+        oracle.yarn_freq(1e7, s=4.0, L=L, alpha=32.0, beta=1.0)
+
+
+def test_yarn_keeps_fast_pairs_and_interpolates_slow_ones():
+    # At the 1M setting, a pair that turns more than beta times over the
+    # native context rotates exactly as plain RoPE; a pair that turns less
+    # than alpha times rotates at position p as plain RoPE does at p/4
+    # (position interpolation); scale 1 is plain RoPE.
+    th = 1e7
+    f = oracle.yarn_freq(th, **oracle.YARN_1M)
+    plain = oracle.plain_freq(th)
+    turns = 262144 * plain / (2 * math.pi)
+    fast, slow = np.where(turns > 32)[0], np.where(turns < 1)[0]
+    assert len(fast) > 20 and len(slow) > 15 and len(fast) + len(slow) < 64   # all three regimes at 1e7
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal(DIM)
+    for p in (4, 1000, 262_144, 1_048_572):
+        y, yp, yq = oracle.rope_freq(x, p, f), oracle.rope(x, p, th), oracle.rope(x, p // 4, th)
+        np.testing.assert_allclose(y[fast], yp[fast], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(y[fast + 64], yp[fast + 64], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(y[slow], yq[slow], rtol=0, atol=1e-9)
+        np.testing.assert_allclose(y[slow + 64], yq[slow + 64], rtol=0, atol=1e-9)
+    one = oracle.yarn_freq(th, s=1.0, L=262144.0)
+    np.testing.assert_allclose(one, plain, rtol=1e-15)
+    np.testing.assert_allclose(oracle.rope_freq(x, 123457, one), oracle.rope(x, 123457, th), atol=1e-9)
+
+
+def test_pool_ex_yarn_is_rotation_after_pooling():
+    # a constant block pools to its key rotated at 4b with YaRN's frequencies
+    rng = np.random.default_rng(32)
+    k = rng.standard_normal(DIM).astype(np.float32)
+    raw = _raw(4 * 300)
+    raw[0, 4 * 257:4 * 258] = k
+    f = oracle.yarn_freq(1e7, **oracle.YARN_1M)
+    out = oracle.pool_ex(raw, 257, 258, f)[0, 257]
+    np.testing.assert_allclose(out, oracle.rope_freq(k.astype(np.float64), 4 * 257, f), rtol=1e-6, atol=1e-6)
+    # with plain frequencies it is qsa pooling itself
+    np.testing.assert_array_equal(oracle.pool_ex(raw, 0, 300, oracle.plain_freq(1e7)), oracle.pool(raw, 0, 300, 1e7))
+
+
+def test_pool_ex_norm_weight():
+    rng = np.random.default_rng(33)
+    raw = rng.standard_normal((2, 4 * 50, DIM)).astype(np.float32)
+    f = oracle.plain_freq(1e7)
+    nf = oracle.FLAG_POOL_RMSNORM
+    # unit weight is the unweighted norm
+    np.testing.assert_array_equal(oracle.pool_ex(raw, 0, 50, f, np.ones(DIM, np.float32), nf),
+                                  oracle.pool(raw, 0, 50, 1e7, nf))
+    # one-hot weight c*e_j (no rotation): only dim j survives, as c * m_j / rms(m)
+    j, c = 37, 1.5
+    w = np.zeros(DIM, np.float32)
+    w[j] = c
+    out = oracle.pool_ex(raw, 0, 50, f, w, nf | oracle.FLAG_NO_ROPE)
+    m = raw.reshape(2, 50, 4, DIM).astype(np.float32)
+    m = ((((m[:, :, 0] + m[:, :, 1]) + m[:, :, 2]) + m[:, :, 3]) * np.float32(0.25)).astype(np.float64)
+    rms = np.sqrt((m * m).mean(-1) + 1e-6)
+    want = np.zeros_like(out)
+    want[:, :, j] = (c * m[:, :, j] / rms).astype(np.float32)
+    np.testing.assert_allclose(out, want, rtol=1e-7, atol=0)
+    # the weight scales each dim: doubling it doubles the (fp32) key exactly
+    w = rng.uniform(0.5, 1.5, DIM).astype(np.float32)
+    a = oracle.pool_ex(raw, 0, 50, f, w, nf | oracle.FLAG_NO_ROPE)
+    b = oracle.pool_ex(raw, 0, 50, f, 2 * w, nf | oracle.FLAG_NO_ROPE)
+    np.testing.assert_array_equal(b, 2 * a)
+    # with rotation, the norm of the rotated key is that of the weighted normalized mean
+    r = oracle.pool_ex(raw, 0, 50, oracle.yarn_freq(1e7, **oracle.YARN_1M), w, nf).astype(np.float64)
+    np.testing.assert_allclose(np.linalg.norm(r, axis=-1), np.linalg.norm(w * m / rms[..., None], axis=-1),
+                               rtol=1e-6)
+    with pytest.raises(RuntimeError):   # a weight without the norm
+        oracle.pool_ex(raw, 0, 50, f, w, 0)
+
+
+def test_score_topk_ex_yarn_brute_force_and_relative_shift():
+    rng = np.random.default_rng(34)
+    f = oracle.yarn_freq(1e7, **oracle.YARN_1M)
+    NB, R, k = 300, 6, 20
+    raw = rng.standard_normal((1, 4 * NB, DIM)).astype(np.float32)
+    pooled = oracle.pool_ex(raw, 0, NB, f)
+    iq = rng.standard_normal((R, 4, DIM)).astype(np.float32)
+    pos = rng.integers(4 * k, 4 * NB, R).astype(np.int32)
+    seq = np.zeros(R, np.int32)
+    sel, cnt, _, raw_s = oracle.score_topk_ex(iq, seq, pos, pooled, k, f, want_raw=True)
+    for r in range(R):    # numpy fp64 brute force on the same rotations
+        qr = np.stack([oracle.rope_freq(iq[r, h], int(pos[r]), f) for h in range(4)]).astype(np.float32)
+        nc = (int(pos[r]) + 1) // 4
+        dots = np.einsum("hd,bd->hb", qr.astype(np.float64), pooled[0, :nc].astype(np.float64))
+        np.testing.assert_allclose(raw_s[r, :nc], np.maximum(dots, 0).sum(0), rtol=1e-12, atol=1e-12)
+        order = np.lexsort((np.arange(nc), -raw_s[r, :nc]))[:k]
+        np.testing.assert_array_equal(sel[r, :cnt[r]], np.sort(order))
+    # scores depend only on query position minus key position: moving the
+    # queries and the keys by 4*D tokens leaves them unchanged
+    D = 1000
+    raw2 = np.zeros((1, 4 * (NB + D), DIM), np.float32)
+    raw2[0, 4 * D:] = raw[0]
+    pooled2 = oracle.pool_ex(raw2, 0, NB + D, f)
+    _, _, _, raw_t = oracle.score_topk_ex(iq, seq, pos + 4 * D, pooled2, k, f, want_raw=True)
+    for r in range(R):
+        nc = (int(pos[r]) + 1) // 4
+        np.testing.assert_allclose(raw_t[r, D:D + nc], raw_s[r, :nc], rtol=2e-5, atol=2e-5)
