@@ -128,39 +128,85 @@ def decode_work(spec, anchor_pos, attn_pos, tail_start):
     }, pairs
 
 
-def roofline_for(name, work, avg_ms, traffic=None):
+def _rate(work, ms):
     bound, amount, unit = work
     if unit == "flop":
-        achieved = amount / (avg_ms * 1e-3) / 1e12
-        peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_F32_VALU_TFLOPS
-        u = "TFLOP/s"
-    else:
-        achieved = amount / (avg_ms * 1e-3) / 1e9
-        peak = PEAK_HBM_GBS
-        u = "GB/s"
-    return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": u,
-            "frac": round(achieved / peak, 4), "per_launch": amount, "avg_us": round(avg_ms * 1e3, 2),
-            "traffic": (traffic or {}).get(name)}
+        return amount / (ms * 1e-3) / 1e12, (PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_F32_VALU_TFLOPS), "TFLOP/s"
+    return amount / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+
+
+def roofline_for(name, work, kt_entry, traffic=None, trace=None):
+    """kt_entry: kernel_times()'s record of the kernel.  `achieved` uses the
+    mean launch time; the median / p10 / p90 launch times are reported with
+    it, and the committed rocprofv3 trace's mean when one matches the
+    kernel's current source (trace_avg_us, trace_frac)."""
+    bound, amount, unit = work
+    avg_ms, per_step = kt_entry[1], kt_entry[3]
+    achieved, peak, u = _rate(work, avg_ms)
+    r = {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": u,
+         "frac": round(achieved / peak, 4), "per_launch": amount, "avg_us": round(avg_ms * 1e3, 2),
+         "median_us": round(pct(per_step, 50) * 1e3, 2), "p10_us": round(pct(per_step, 10) * 1e3, 2),
+         "p90_us": round(pct(per_step, 90) * 1e3, 2), "traffic": (traffic or {}).get(name)}
+    if trace and name in trace:
+        t_avg = trace[name]
+        r["trace_avg_us"] = round(t_avg, 2)
+        r["trace_frac"] = round(_rate(work, t_avg * 1e-3)[0] / peak, 4)
+    return r
+
+
+def pct(v, q):
+    return float(np.percentile(np.asarray(v, np.float64), q))
 
 
 def kernel_times(run_step, nsteps, names):
-    """Average per-launch ms of each kernel over `nsteps` steps (hipEvents)."""
+    """Per-kernel launch times over `nsteps` steps, from the hipEvents the
+    library records around each launch on its launch stream.  Returns
+    {kernel: (launches, mean ms per launch, ms per step, [per-step mean ms
+    per launch])}; the list gives the median / p10 / p90."""
     import torch
     from block_sparse_long_amd import qsa
     torch.cuda.synchronize()
-    qsa.profile_reset()
-    qsa.profile_enable(True)
+    per = {}
     for i in range(nsteps):
+        qsa.profile_reset()
+        qsa.profile_enable(True)
         run_step(i)
-    torch.cuda.synchronize()
-    qsa.profile_enable(False)
-    out = {}
-    for n in names:
-        cnt, tot = qsa.profile_kernel_ms(n)
-        if cnt:
-            out[n] = (cnt, tot / cnt, tot / nsteps)
+        torch.cuda.synchronize()
+        qsa.profile_enable(False)
+        for n in names:
+            cnt, tot = qsa.profile_kernel_ms(n)
+            if cnt:
+                per.setdefault(n, []).append((cnt, tot))
     qsa.profile_reset()
+    out = {}
+    for n, v in per.items():
+        c = sum(x[0] for x in v)
+        t = sum(x[1] for x in v)
+        out[n] = (c, t / c, t / nsteps, [x[1] / x[0] for x in v])
     return out
+
+
+def kernel_table(kt, nsteps):
+    return {n: {"launches_per_step": c / nsteps, "avg_us": round(a * 1e3, 2),
+                "median_us": round(pct(v, 50) * 1e3, 2), "p10_us": round(pct(v, 10) * 1e3, 2),
+                "p90_us": round(pct(v, 90) * 1e3, 2)}
+            for n, (c, a, _, v) in kt.items()}
+
+
+def step_times(run_step, n, offset=0):
+    """Per-step durations (ms) of `n` steps, each bracketed by events on the
+    current stream (the one the library launches on): median, p10, p90."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[i][0].record()
+        run_step(offset + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    d = [a.elapsed_time(b) for a, b in ev]
+    return {"n": n, "median_ms": round(pct(d, 50), 4), "p10_ms": round(pct(d, 10), 4),
+            "p90_ms": round(pct(d, 90), 4), "mean_ms": round(float(np.mean(d)), 4)}
 
 
 def timed(run_step, steps, warmup):
@@ -187,7 +233,7 @@ ALL_KERNELS = ["pool_rope", "pool_rope_fp8", "pool_append", "rope_query", "score
 # prefill workload
 # ---------------------------------------------------------------------------
 
-def bench_prefill(spec, steps, warmup, cpu_baseline, keys="bf16", w=None, kv="bf16"):
+def bench_prefill(spec, steps, warmup, cpu_baseline, keys="bf16", w=None, kv="bf16", cpu_target_s=12.0):
     """keys "fp8": the compressed keys stored as E4M3 codes plus one scale per
     key (qsa_pool_index_keys_fp8 / qsa_score_topk_fp8); kv "fp8": the K/V
     cache as E4M3 codes with one scale per tensor (qsa_sparse_attn_*_fp8kv);
@@ -241,18 +287,19 @@ def bench_prefill(spec, steps, warmup, cpu_baseline, keys="bf16", w=None, kv="bf
 
     ms = timed(step, steps, warmup)
     log(f"{spec.name} ({keys} keys, {kv} K/V): {ms:.3f} ms/step")
-    kt = kernel_times(step, max(3, min(steps, 10)), ALL_KERNELS)
+    st = step_times(step, max(30, steps))
+    nprof = max(10, min(steps, 30))
+    kt = kernel_times(step, nprof, ALL_KERNELS)
     work, pairs, npos = prefill_work(spec, w["row_pos"])
-    kernels = {n: {"launches_per_step": c / max(3, min(steps, 10)), "avg_us": round(a * 1e3, 2)}
-               for n, (c, a, _) in kt.items()}
+    kernels = kernel_table(kt, nprof)
     dom = max((n for n in kt if n in work), key=lambda n: kt[n][2])
-    tr = load_traffic(spec.name)
-    res = {"ms_per_step": ms, "value": R / (ms * 1e-3), "kernels": kernels,
-           "roofline": roofline_for(dom, work[dom], kt[dom][1], tr),
-           "rooflines": {n: roofline_for(n, work[n], kt[n][1], tr) for n in kt if n in work},
+    tr, trc = load_traffic(spec.name), load_trace(spec.name)
+    res = {"ms_per_step": ms, "value": R / (ms * 1e-3), "step_ms": st, "kernels": kernels,
+           "roofline": roofline_for(dom, work[dom], kt[dom], tr, trc),
+           "rooflines": {n: roofline_for(n, work[n], kt[n], tr, trc) for n in kt if n in work},
            "pairs": pairs, "positions": npos}
     if cpu_baseline:
-        res["cpu_baseline"] = cpu_prefill(spec, w)
+        res["cpu_baseline"] = cpu_prefill(spec, w, cpu_target_s)
     res["_inputs"] = w
     return res
 
@@ -294,7 +341,7 @@ def cpu_prefill(spec, w, target_s=12.0):
 # decode workload
 # ---------------------------------------------------------------------------
 
-def bench_decode(spec, steps, warmup, cpu_baseline, copies=3, keys="bf16", w=None, kv="bf16"):
+def bench_decode(spec, steps, warmup, cpu_baseline, copies=3, keys="bf16", w=None, kv="bf16", cpu_target_s=10.0):
     """keys / kv "fp8": as in bench_prefill."""
     import torch
     from block_sparse_long_amd import qsa, synth
@@ -358,23 +405,24 @@ def bench_decode(spec, steps, warmup, cpu_baseline, copies=3, keys="bf16", w=Non
 
     ms = timed(step, steps, warmup)
     log(f"{spec.name} ({keys} keys, {kv} K/V): {ms:.3f} ms/step")
-    nprof = max(3, min(steps, 30))
+    st = step_times(step, max(30, min(steps, 100)))
+    nprof = max(10, min(steps, 30))
     kt = kernel_times(step, nprof, ALL_KERNELS)
     work, pairs = decode_work(spec, w["row_pos"], w["attn_pos"], w["tail_start"])
-    kernels = {n: {"launches_per_step": c / nprof, "avg_us": round(a * 1e3, 2)} for n, (c, a, _) in kt.items()}
+    kernels = kernel_table(kt, nprof)
     dom = max((n for n in kt if n in work), key=lambda n: kt[n][2])
     rows = spec.batch * spec.q_per_seq
-    tr = load_traffic(spec.name)
+    tr, trc = load_traffic(spec.name), load_trace(spec.name)
     res = {"workload": spec.name, "value": rows / (ms * 1e-3), "unit": "query rows/s", "ms_per_step": ms,
-           "kernels": kernels, "roofline": roofline_for(dom, work[dom], kt[dom][1], tr),
-           "rooflines": {n: roofline_for(n, work[n], kt[n][1], tr) for n in kt if n in work}}
+           "step_ms": st, "kernels": kernels, "roofline": roofline_for(dom, work[dom], kt[dom], tr, trc),
+           "rooflines": {n: roofline_for(n, work[n], kt[n], tr, trc) for n in kt if n in work}}
     if not fp8 and not fp8kv:
         res["pool_append"] = bench_pool_append(spec)
     if not fp8 and not fp8kv and spec.draft:
         res["draft_loop"] = bench_draft_loop(spec, iq, seq, apos, pooled, kcs, vcs, q, ts, max_nb, ws,
                                              max(steps, 10), warmup)
     if cpu_baseline and not fp8 and not fp8kv:
-        res["cpu_baseline"] = cpu_decode(spec, w, pooled_h)
+        res["cpu_baseline"] = cpu_decode(spec, w, pooled_h, cpu_target_s)
     res["_inputs"] = w
     return res
 
@@ -454,7 +502,7 @@ def bench_draft_loop(spec, iq, seq, apos, pooled, kcs, vcs, q, ts, max_nb, ws, s
     log(f"{spec.name} draft loop ({N} steps): {ms:.3f} ms/loop")
     return {"draft_steps": N, "ms_per_loop": round(ms, 4), "value": round(B * N / (ms * 1e-3), 1),
             "unit": "draft rows/s",
-            "kernels": {n: {"launches_per_loop": c / 5, "avg_us": round(a * 1e3, 2)} for n, (c, a, _) in kt.items()}}
+            "kernels": {n: {"launches_per_loop": c / 5, "avg_us": round(a * 1e3, 2)} for n, (c, a, _, _) in kt.items()}}
 
 
 def paged_layout(spec, page_tokens, seed=77):
@@ -547,7 +595,7 @@ def bench_paged(spec, w, steps, warmup, page_tokens=16):
     kt = kernel_times(step, nprof, ALL_KERNELS)
     return {"page_tokens": P, "value": round(rows / (ms * 1e-3), 1),
             "unit": "tokens/s" if spec.kind == "prefill" else "query rows/s", "ms_per_step": round(ms, 4),
-            "kernels": {n: {"launches_per_step": c / nprof, "avg_us": round(a * 1e3, 2)} for n, (c, a, _) in kt.items()}}
+            "kernels": kernel_table(kt, nprof)}
 
 
 def bench_pool_append(spec, launches=50):
@@ -679,7 +727,8 @@ def _csvs(d, suffix):
 
 
 def kernel_trace_stats(d):
-    """{kernel: (launches, avg_us, min_us, max_us)} from a --kernel-trace run."""
+    """{kernel: (launches, avg_us, median_us, p10_us, p90_us, min_us, max_us)}
+    from a --kernel-trace run."""
     per = {}
     for f in _csvs(d, "kernel_trace.csv"):
         for r in csv.DictReader(open(f)):
@@ -687,7 +736,8 @@ def kernel_trace_stats(d):
             if n is None:
                 continue
             per.setdefault(n, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    return {n: (len(v), sum(v) / len(v), min(v), max(v)) for n, v in per.items()}
+    return {n: (len(v), sum(v) / len(v), pct(v, 50), pct(v, 10), pct(v, 90), min(v), max(v))
+            for n, v in per.items()}
 
 
 def counter_means(d):
@@ -712,9 +762,11 @@ def rocprof_summary(dirs):
         print(f"# rocprofv3 output: {d}")
         st = kernel_trace_stats(d)
         if st:
-            print(f"{'kernel':<20} {'launches':>9} {'avg_us':>10} {'min_us':>10} {'max_us':>10}")
-            for n, (c, a, lo, hi) in sorted(st.items(), key=lambda x: -x[1][0] * x[1][1]):
-                print(f"{n:<20} {c:>9} {a:>10.2f} {lo:>10.2f} {hi:>10.2f}")
+            print("# kernel  name  source_digest  launches  avg_us  median_us  p10_us  p90_us  min_us  max_us")
+            for n, (c, a, med, p10, p90, lo, hi) in sorted(st.items(), key=lambda x: -x[1][0] * x[1][1]):
+                dg = source_digest(n) if n in KERNEL_SOURCE else "-"
+                print(f"kernel {n:<24} {dg} {c:>6} {a:>10.2f} {med:>10.2f} {p10:>10.2f} {p90:>10.2f} {lo:>10.2f} "
+                      f"{hi:>10.2f}")
         for f in _csvs(d, "kernel_stats.csv"):  # rocprofv3's own --stats table
             print(f"# {os.path.basename(f)}: kernel, calls, average ns, min ns, max ns")
             for r in csv.DictReader(open(f)):
@@ -742,6 +794,21 @@ def traffic_summary(fetch_dir, write_dir, workload):
         fb = fm[n]["FETCH_SIZE"] * 1024.0 * ff
         wb = wm[n]["WRITE_SIZE"] * 1024.0 * fw
         print(f"kernel {n} {source_digest(n)} {fb:.0f} {wb:.0f} {fb + wb:.0f}")
+
+
+def load_trace(workload):
+    """{kernel: mean launch time in us} from profiles/kernel_trace_<workload>.txt
+    (a rocprofv3 --kernel-trace run of this bench on that workload alone),
+    for kernels whose source still matches the digest recorded there."""
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.txt")
+    out = {}
+    if not os.path.exists(path):
+        return out
+    for line in open(path):
+        p = line.split()
+        if len(p) == 10 and p[0] == "kernel" and p[1] in KERNEL_SOURCE and p[2] == source_digest(p[1]):
+            out[p[1]] = float(p[4])
+    return out
 
 
 def load_traffic(workload):
@@ -774,6 +841,9 @@ def main():
                     help="skip the extra runs on a paged pool")
     ap.add_argument("--no-serving-shape", dest="serving", action="store_false",
                     help="skip the extra runs with attention at 24 q / 2 KV heads, head dim 256")
+    ap.add_argument("--no-other-workloads", dest="others", action="store_false",
+                    help="skip the side entries for the other three workloads (decode-8k-f32, prefill-32k, "
+                         "decode-128k)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a copy of known size first (for scaling memory counters)")
     ap.add_argument("--rocprof-summary", nargs="+", metavar="DIR")
@@ -834,6 +904,7 @@ def main():
         "config": {"workload": spec.name, "context": spec.ctx, "rows": spec.attn_rows, "batch": spec.batch,
                    "Hq": spec.Hq, "Hkv": spec.Hkv, "head_dim": spec.D, "index_heads": 4, "index_dim": 128,
                    "block": 4, "top_k": spec.top_k, "rope_theta": spec.theta},
+        "step_ms": main_res["step_ms"],
         "roofline": main_res["roofline"],
         "cpu_baseline": main_res.get("cpu_baseline"),
         "kernels": main_res["kernels"],
@@ -858,6 +929,29 @@ def main():
         line["decode"]["config"] = {"context": dspec.ctx, "batch": dspec.batch, "q_per_seq": dspec.q_per_seq,
                                     "Hq": dspec.Hq, "Hkv": dspec.Hkv, "top_k": dspec.top_k,
                                     "steps": args.steps * 10}
+    if args.others:
+        # the other workloads, each timed as its own step with its own roofline
+        # (not the headline): value, per-step median / p10 / p90, the
+        # dominant kernel against its peak, and the oracle on a short sample
+        line["other_workloads"] = {}
+        for name in synth.CONFIG_ORDER:
+            if name in (spec.name, args.decode_workload):
+                continue
+            o = synth.SPECS[name]
+            if o.kind == "prefill":
+                r = bench_prefill(o, args.steps, args.warmup, cpu, cpu_target_s=5.0)
+                unit_o = "tokens/s"
+            else:
+                r = bench_decode(o, args.steps * 10, args.warmup, cpu, cpu_target_s=3.0)
+                unit_o = r["unit"]
+            r.pop("_inputs", None)
+            line["other_workloads"][name] = {
+                "value": round(r["value"], 1), "unit": unit_o, "ms_per_step": round(r["ms_per_step"], 4),
+                "step_ms": r["step_ms"], "dtype": o.dtype,
+                "config": {"context": o.ctx, "rows": o.attn_rows, "batch": o.batch, "Hq": o.Hq, "Hkv": o.Hkv,
+                           "head_dim": o.D, "top_k": o.top_k},
+                "roofline": r["roofline"], "cpu_baseline": r.get("cpu_baseline"), "kernels": r["kernels"]}
+            del r
     if fp8_res:
         # the same workloads with the compressed index keys in FP8 E4M3 (one
         # FP32 scale per key); not the headline: the headline keeps bf16 keys

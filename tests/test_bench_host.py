@@ -64,10 +64,12 @@ def test_decode_work_bytes(bench):
 
 
 def test_roofline_fraction(bench):
-    r = bench.roofline_for("score_filter", ("mfma", 1.25e12, "flop"), 1.0, {"score_filter": 123.0})
+    r = bench.roofline_for("score_filter", ("mfma", 1.25e12, "flop"), (3, 1.0, 1.0, [0.9, 1.0, 1.1]),
+                           {"score_filter": 123.0})
     assert r["achieved"] == pytest.approx(1250.0) and r["unit"] == "TFLOP/s"
     assert r["frac"] == pytest.approx(0.5) and r["traffic"] == 123.0
-    r = bench.roofline_for("score_rows_bf16", ("hbm", 4e6, "B"), 0.001, None)
+    assert r["median_us"] == 1000.0 and r["p10_us"] == 920.0 and r["p90_us"] == 1080.0
+    r = bench.roofline_for("score_rows_bf16", ("hbm", 4e6, "B"), (1, 0.001, 0.001, [0.001]), None)
     assert r["achieved"] == pytest.approx(4000.0) and r["unit"] == "GB/s"
     assert r["frac"] == pytest.approx(0.5) and r["traffic"] is None
 
@@ -107,7 +109,7 @@ def test_kernel_trace_and_counter_summaries(bench, tmp_path):
                 {"Kernel_Name": k, "Start_Timestamp": 9000, "End_Timestamp": 11000},
                 {"Kernel_Name": "other", "Start_Timestamp": 0, "End_Timestamp": 7}])
     st = bench.kernel_trace_stats(str(tmp_path / "t"))
-    assert st == {"score_filter": (2, 3.0, 2.0, 4.0)}
+    assert st == {"score_filter": (2, 3.0, 3.0, 2.2, 3.8, 2.0, 4.0)}   # launches, mean, median, p10, p90, min, max
     # counters are summed over a dispatch's rows (one per XCD or instance), then averaged over dispatches
     _write_csv(str(tmp_path / "c" / "run_counter_collection.csv"),
                ["Kernel_Name", "Counter_Name", "Dispatch_Id", "Counter_Value"],
@@ -128,3 +130,26 @@ def test_traffic_is_used_only_while_the_source_matches(bench, tmp_path, monkeypa
         f.write("kernel not_a_kernel abc 1 1 2\n")
     assert bench.load_traffic("w") == {"score_filter": 3.0}
     assert bench.load_traffic("missing") == {}
+
+
+def test_trace_is_used_only_while_the_source_matches(bench, tmp_path, monkeypatch, capsys):
+    # a summary written by --rocprof-summary is read back by load_trace
+    k = "void qsa::score_filter_kernel<false>(qsa::FusedScoreArgs)"
+    m = "void qsa::select_merge_kernel<false>(qsa::FusedScoreArgs, int*, int*, float*)"
+    _write_csv(str(tmp_path / "t" / "run_kernel_trace.csv"), ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+               [{"Kernel_Name": k, "Start_Timestamp": 0, "End_Timestamp": 500_000},
+                {"Kernel_Name": k, "Start_Timestamp": 0, "End_Timestamp": 520_000},
+                {"Kernel_Name": m, "Start_Timestamp": 0, "End_Timestamp": 80_000}])
+    bench.rocprof_summary([str(tmp_path / "t")])
+    lines = capsys.readouterr().out.splitlines()   # select_merge's line as if its source had changed since
+    text = "\n".join(ln.replace(bench.source_digest("select_merge"), "0000000000000000")
+                     if ln.startswith("kernel select_merge") else ln for ln in lines) + "\n"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    with open(tmp_path / "profiles" / "kernel_trace_w.txt", "w") as f:
+        f.write(text)
+    assert bench.load_trace("w") == {"score_filter": 510.0}      # select_merge's digest no longer matches
+    assert bench.load_trace("missing") == {}
+    r = bench.roofline_for("score_filter", ("mfma", 5.0e11, "flop"), (1, 0.5, 0.5, [0.5]), None,
+                           bench.load_trace("w"))
+    assert r["frac"] == 0.4 and r["trace_avg_us"] == 510.0 and r["trace_frac"] == round(5.0e11 / 510e-6 / 2.5e15, 4)
