@@ -181,7 +181,7 @@ struct KeySource {
 };
 static qsa_status_t score_topk_run(const void *q_index, const int32_t *row_seq, const int32_t *row_pos,
                                    int32_t rows, const KeySource &keys, int64_t pooled_seq_stride,
-                                   int32_t max_visible_blocks, int32_t top_k, double rope_theta, uint32_t flags,
+                                   int32_t max_visible_blocks, int32_t top_k, const RopeFreq &rf, uint32_t flags,
                                    qsa_dtype_t dtype, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
@@ -220,7 +220,7 @@ qsa_status_t qsa_pool_index_keys(const void *raw_keys, int64_t raw_seq_stride, v
         return QSA_ERR_INVALID_ARG;
     clear_launch_err();
     launch_pool(raw_keys, raw_seq_stride, pooled, pooled_seq_stride, KeyPages{nullptr, 0, 0}, batch, block_begin,
-                block_end, rope_theta, flags, dtype == QSA_BF16, (hipStream_t)stream);
+                block_end, rope_freq_plain(rope_theta), flags, dtype == QSA_BF16, (hipStream_t)stream);
     return launch_status();
 }
 
@@ -240,7 +240,8 @@ qsa_status_t qsa_pool_index_keys_fp8(const void *raw_keys, int64_t raw_seq_strid
         return QSA_ERR_INVALID_ARG;
     clear_launch_err();
     launch_pool_fp8(raw_keys, raw_seq_stride, codes, scales, pooled_seq_stride, KeyPages{nullptr, 0, 0}, batch,
-                    block_begin, block_end, rope_theta, flags, raw_dtype == QSA_BF16, (hipStream_t)stream);
+                    block_begin, block_end, rope_freq_plain(rope_theta), flags, raw_dtype == QSA_BF16,
+                    (hipStream_t)stream);
     return launch_status();
 }
 
@@ -266,11 +267,11 @@ qsa_status_t qsa_pool_index_keys_paged(const void *raw_keys, int64_t raw_seq_str
     const KeyPages kp{page_table, page_table_stride, bpp};
     clear_launch_err();
     if (fp8)
-        launch_pool_fp8(raw_keys, raw_seq_stride, codes, scales, 0, kp, batch, block_begin, block_end, rope_theta,
-                        flags, raw_dtype == QSA_BF16, (hipStream_t)stream);
+        launch_pool_fp8(raw_keys, raw_seq_stride, codes, scales, 0, kp, batch, block_begin, block_end,
+                        rope_freq_plain(rope_theta), flags, raw_dtype == QSA_BF16, (hipStream_t)stream);
     else
-        launch_pool(raw_keys, raw_seq_stride, pooled, 0, kp, batch, block_begin, block_end, rope_theta, flags,
-                    raw_dtype == QSA_BF16, (hipStream_t)stream);
+        launch_pool(raw_keys, raw_seq_stride, pooled, 0, kp, batch, block_begin, block_end,
+                    rope_freq_plain(rope_theta), flags, raw_dtype == QSA_BF16, (hipStream_t)stream);
     return launch_status();
 }
 
@@ -286,8 +287,47 @@ qsa_status_t qsa_pool_append(const void *new_keys, const int32_t *positions, con
     if (!aligned16(new_keys) || !aligned16(ring) || !aligned16(compressed) || !positions || !full_slots)
         return QSA_ERR_INVALID_ARG;
     clear_launch_err();
-    launch_pool_append(new_keys, positions, full_slots, ring, compressed, batch, rope_theta, flags, dtype == QSA_BF16,
-                       (hipStream_t)stream);
+    launch_pool_append(new_keys, positions, full_slots, ring, compressed, batch, rope_freq_plain(rope_theta), flags,
+                       dtype == QSA_BF16, (hipStream_t)stream);
+    return launch_status();
+}
+
+// qsa_rope_t: a valid rotation (unused with QSA_FLAG_NO_ROPE, where it may be NULL).
+static bool rope_ok(const qsa_rope_t *r, uint32_t flags)
+{
+    if (flags & QSA_FLAG_NO_ROPE) return true;
+    if (!r || !(r->theta > 1.0 && std::isfinite(r->theta))) return false;
+    if (!(r->yarn_factor >= 1.0 && std::isfinite(r->yarn_factor))) return false;
+    if (r->yarn_factor == 1.0) return true;
+    return r->yarn_original_context > 0.0 && std::isfinite(r->yarn_original_context) && r->yarn_alpha >= 0.0 &&
+           std::isfinite(r->yarn_beta) && r->yarn_beta > r->yarn_alpha;
+}
+
+static RopeFreq rope_freq_of(const qsa_rope_t *r, uint32_t flags)
+{
+    if ((flags & QSA_FLAG_NO_ROPE) || !r) return RopeFreq{};  // not read by the kernels
+    return rope_freq_yarn(r->theta, r->yarn_factor, r->yarn_original_context, r->yarn_alpha, r->yarn_beta);
+}
+
+qsa_status_t qsa_pool_index_keys_ex(const void *raw_keys, int64_t raw_seq_stride, void *pooled,
+                                    int64_t pooled_seq_stride, int32_t batch, int32_t block_begin, int32_t block_end,
+                                    const qsa_rope_t *rope, const float *norm_weight, uint32_t flags,
+                                    qsa_dtype_t dtype, void *stream)
+{
+    if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
+    if (batch < 0 || block_begin < 0 || block_end < block_begin) return QSA_ERR_INVALID_ARG;
+    if (flags & ~(uint32_t)(QSA_FLAG_NO_ROPE | QSA_FLAG_POOL_RMSNORM)) return QSA_ERR_INVALID_ARG;
+    if (!rope_ok(rope, flags)) return QSA_ERR_INVALID_ARG;
+    if (norm_weight && (!(flags & QSA_FLAG_POOL_RMSNORM) || (reinterpret_cast<uintptr_t>(norm_weight) & 3u)))
+        return QSA_ERR_INVALID_ARG;
+    if (batch == 0 || block_end == block_begin) return QSA_OK;
+    if (!aligned16(raw_keys) || !aligned16(pooled)) return QSA_ERR_INVALID_ARG;
+    if (raw_seq_stride % 8 || pooled_seq_stride % 8) return QSA_ERR_INVALID_ARG;
+    if (batch > 1 && (raw_seq_stride < (int64_t)kBlock * block_end * kDim || pooled_seq_stride < (int64_t)block_end * kDim))
+        return QSA_ERR_INVALID_ARG;
+    clear_launch_err();
+    launch_pool(raw_keys, raw_seq_stride, pooled, pooled_seq_stride, KeyPages{nullptr, 0, 0}, batch, block_begin,
+                block_end, rope_freq_of(rope, flags), flags, dtype == QSA_BF16, (hipStream_t)stream, norm_weight);
     return launch_status();
 }
 
@@ -329,8 +369,29 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
     if (pooled_seq_stride % 8 || pooled_seq_stride < 0) return QSA_ERR_INVALID_ARG;
     const KeySource keys{pooled, nullptr, nullptr, KeyPages{nullptr, 0, 1}};
     return score_topk_run(q_index, row_seq, row_pos, rows, keys, pooled_seq_stride, max_visible_blocks, top_k,
-                          rope_theta, flags, dtype, sel_blocks, sel_count, sel_scores, workspace, workspace_bytes,
-                          stream);
+                          rope_freq_plain(rope_theta), flags, dtype, sel_blocks, sel_count, sel_scores, workspace,
+                          workspace_bytes, stream);
+}
+
+qsa_status_t qsa_score_topk_ex(const void *q_index, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
+                               const void *pooled, int64_t pooled_seq_stride, int32_t max_visible_blocks,
+                               int32_t top_k, const qsa_rope_t *rope, uint32_t flags, qsa_dtype_t dtype,
+                               int32_t *sel_blocks, int32_t *sel_count, float *sel_scores, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
+    if (rows < 0 || max_visible_blocks < 0 || top_k < 1 || top_k > QSA_MAX_TOP_K) return QSA_ERR_INVALID_ARG;
+    if (!score_flags_ok(flags, dtype)) return QSA_ERR_INVALID_ARG;
+    if ((flags & QSA_FLAG_SCORE_GEMM) && dtype != QSA_BF16) return QSA_ERR_UNSUPPORTED;
+    if (!rope_ok(rope, flags)) return QSA_ERR_INVALID_ARG;
+    if (rows == 0) return QSA_OK;
+    if (!aligned16(q_index) || !aligned16(pooled) || !row_seq || !row_pos || !sel_blocks || !sel_count)
+        return QSA_ERR_INVALID_ARG;
+    if (pooled_seq_stride % 8 || pooled_seq_stride < 0) return QSA_ERR_INVALID_ARG;
+    const KeySource keys{pooled, nullptr, nullptr, KeyPages{nullptr, 0, 1}};
+    return score_topk_run(q_index, row_seq, row_pos, rows, keys, pooled_seq_stride, max_visible_blocks, top_k,
+                          rope_freq_of(rope, flags), flags, dtype, sel_blocks, sel_count, sel_scores, workspace,
+                          workspace_bytes, stream);
 }
 
 qsa_status_t qsa_score_topk_fp8(const void *q_index, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
@@ -349,8 +410,8 @@ qsa_status_t qsa_score_topk_fp8(const void *q_index, const int32_t *row_seq, con
     if (pooled_seq_stride < 0) return QSA_ERR_INVALID_ARG;
     const KeySource keys{nullptr, codes, scales, KeyPages{nullptr, 0, 1}};
     return score_topk_run(q_index, row_seq, row_pos, rows, keys, pooled_seq_stride, max_visible_blocks, top_k,
-                          rope_theta, flags, QSA_BF16, sel_blocks, sel_count, sel_scores, workspace, workspace_bytes,
-                          stream);
+                          rope_freq_plain(rope_theta), flags, QSA_BF16, sel_blocks, sel_count, sel_scores, workspace,
+                          workspace_bytes, stream);
 }
 
 qsa_status_t qsa_score_topk_paged(const void *q_index, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
@@ -376,8 +437,9 @@ qsa_status_t qsa_score_topk_paged(const void *q_index, const int32_t *row_seq, c
         return QSA_ERR_INVALID_ARG;
     if ((int64_t)max_visible_blocks * kBlock > page_table_stride * (int64_t)page_tokens) return QSA_ERR_INVALID_ARG;
     const KeySource keys{fp8 ? nullptr : pooled, codes, scales, KeyPages{page_table, page_table_stride, page_tokens / kBlock}};
-    return score_topk_run(q_index, row_seq, row_pos, rows, keys, 0, max_visible_blocks, top_k, rope_theta, flags, dtype,
-                          sel_blocks, sel_count, sel_scores, workspace, workspace_bytes, stream);
+    return score_topk_run(q_index, row_seq, row_pos, rows, keys, 0, max_visible_blocks, top_k,
+                          rope_freq_plain(rope_theta), flags, dtype, sel_blocks, sel_count, sel_scores, workspace,
+                          workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -387,7 +449,7 @@ qsa_status_t qsa_score_topk_paged(const void *q_index, const int32_t *row_seq, c
 // codes converted to bf16 on the way to the MFMA).
 static qsa_status_t score_topk_run(const void *q_index, const int32_t *row_seq, const int32_t *row_pos,
                                    int32_t rows, const KeySource &keys, int64_t pooled_seq_stride,
-                                   int32_t max_visible_blocks, int32_t top_k, double rope_theta, uint32_t flags,
+                                   int32_t max_visible_blocks, int32_t top_k, const RopeFreq &rf, uint32_t flags,
                                    qsa_dtype_t dtype, int32_t *sel_blocks, int32_t *sel_count, float *sel_scores,
                                    void *workspace, size_t workspace_bytes, void *stream)
 {
@@ -406,7 +468,7 @@ static qsa_status_t score_topk_run(const void *q_index, const int32_t *row_seq, 
         ss.cand_stride = L.sc_stride;
     }
     clear_launch_err();
-    launch_rope_query(q_index, row_pos, rows, qrot, rope_theta, flags & QSA_FLAG_NO_ROPE, bf16,
+    launch_rope_query(q_index, row_pos, rows, qrot, rf, flags & QSA_FLAG_NO_ROPE, bf16,
                       L.plan.split ? ss.scratch : nullptr, kRowScratch, st);
     if (L.plan.fused) {
         FusedScoreArgs fa{};
@@ -593,9 +655,9 @@ static qsa_status_t attn_decode_impl(const void *q, const int32_t *row_pos, int3
                                         softmax_scale, dtype, out, kv_fp8);
     if (st != QSA_OK) return st;
     if (!row_pos) return QSA_ERR_INVALID_ARG;
+    const size_t need = qsa_sparse_attn_decode_workspace_size(batch, q_per_seq, Hq, D, top_k);
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return QSA_ERR_INVALID_ARG;
-    if (workspace_bytes < qsa_sparse_attn_decode_workspace_size(batch, q_per_seq, Hq, D, top_k))
-        return QSA_ERR_WORKSPACE;
+    if (workspace_bytes < need) return QSA_ERR_WORKSPACE;
     AttnArgs a{};
     a.q = q;
     a.row_seq = nullptr;

@@ -16,16 +16,35 @@
 
 namespace qsa {
 
-// RoPE frequencies theta^(-j/64) of the 64 rotary pairs, formed once on the
-// host in double precision and passed by value.
-struct RopeFreq {
-    double f[kHalf];
-};
-
-static RopeFreq rope_freq(double theta)
+// RoPE frequencies theta^(-j/64) of the 64 rotary pairs.
+RopeFreq rope_freq_plain(double theta)
 {
     RopeFreq r;
     for (int j = 0; j < kHalf; ++j) r.f[j] = std::pow(theta, -(double)j / (double)kHalf);
+    return r;
+}
+
+// YaRN for long contexts (the pages: the 262,144-token native context extends
+// to one million tokens with YaRN; the method is Peng, Quesnelle, Fan and
+// Shippole, "YaRN: Efficient Context Window Extension of Large Language
+// Models", 2023, its interpolation by parts).  Pair j turns
+// r = L * theta_j / (2 pi) times over the original context of L tokens; a
+// pair with r > beta keeps theta_j, a pair with r < alpha gets theta_j / s,
+// and between them the weight gamma = (r - alpha) / (beta - alpha) blends the
+// two: (1 - gamma) * theta_j / s + gamma * theta_j.  The method's attention
+// temperature scales scores by a positive constant, which the indexer's
+// ranking cannot see; it is not applied here.
+RopeFreq rope_freq_yarn(double theta, double s, double L, double alpha, double beta)
+{
+    RopeFreq r = rope_freq_plain(theta);
+    if (s == 1.0) return r;
+    const double two_pi = 6.283185307179586476925;
+    for (int j = 0; j < kHalf; ++j) {
+        const double th = r.f[j];
+        const double turns = L * th / two_pi;
+        const double gamma = turns < alpha ? 0.0 : turns > beta ? 1.0 : (turns - alpha) / (beta - alpha);
+        r.f[j] = (1.0 - gamma) * th / s + gamma * th;
+    }
     return r;
 }
 
@@ -37,7 +56,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ raw, int64_t raw_stride,
                                                         T *__restrict__ pooled, int64_t pooled_stride, KeyPages kp,
                                                         int64_t total, int32_t nblk, int32_t block_begin,
-                                                        RopeFreq rf, uint32_t flags)
+                                                        RopeFreq rf, uint32_t flags,
+                                                        const float *__restrict__ norm_w)
 {
     const int lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -59,6 +79,10 @@ __global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ ra
         const double inv = 1.0 / sqrt(ss / (double)kDim + 1e-6);
         dx *= inv;
         dy *= inv;
+        if (norm_w) {  // learned per-dim weight of the norm
+            dx *= (double)norm_w[lane];
+            dy *= (double)norm_w[kHalf + lane];
+        }
     }
     if (!(flags & kFlagNoRope)) rope_pair(dx, dy, kBlock * b, rf.f[lane]);
     T *dst = pooled + key_offset(kp, pooled_stride, s, b);
@@ -204,10 +228,10 @@ __global__ __launch_bounds__(256) void pool_append_kernel(const T *__restrict__ 
 }
 
 void launch_pool_append(const void *new_keys, const int32_t *positions, const int64_t *full_slots, void *ring,
-                        void *compressed, int32_t batch, double theta, uint32_t flags, bool bf16, hipStream_t stream)
+                        void *compressed, int32_t batch, const RopeFreq &rf, uint32_t flags, bool bf16,
+                        hipStream_t stream)
 {
     const dim3 grid((unsigned)((batch + 3) / 4)), block(256);
-    const RopeFreq rf = rope_freq(theta);
     if (bf16)
         QSA_LAUNCH("pool_append", (pool_append_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)new_keys,
                    positions, full_slots, (bf16_t *)ring, (bf16_t *)compressed, batch, rf, flags);
@@ -217,29 +241,28 @@ void launch_pool_append(const void *new_keys, const int32_t *positions, const in
 }
 
 void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pooled_stride, const KeyPages &kp,
-                 int32_t batch, int32_t block_begin, int32_t block_end, double theta, uint32_t flags, bool bf16,
-                 hipStream_t stream)
+                 int32_t batch, int32_t block_begin, int32_t block_end, const RopeFreq &rf, uint32_t flags,
+                 bool bf16, hipStream_t stream, const float *norm_weight)
 {
     const int32_t nblk = block_end - block_begin;
     const int64_t total = (int64_t)batch * nblk;
     const dim3 grid((unsigned)((total + 3) / 4)), block(256);
-    const RopeFreq rf = rope_freq(theta);
     if (bf16)
         QSA_LAUNCH("pool_rope", (pool_rope_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)raw,
-                   raw_stride, (bf16_t *)pooled, pooled_stride, kp, total, nblk, block_begin, rf, flags);
+                   raw_stride, (bf16_t *)pooled, pooled_stride, kp, total, nblk, block_begin, rf, flags,
+                   norm_weight);
     else
         QSA_LAUNCH("pool_rope", (pool_rope_kernel<float>), grid, block, 0, stream, (const float *)raw, raw_stride,
-                   (float *)pooled, pooled_stride, kp, total, nblk, block_begin, rf, flags);
+                   (float *)pooled, pooled_stride, kp, total, nblk, block_begin, rf, flags, norm_weight);
 }
 
 void launch_pool_fp8(const void *raw, int64_t raw_stride, uint8_t *codes, float *scales, int64_t pooled_stride,
-                     const KeyPages &kp, int32_t batch, int32_t block_begin, int32_t block_end, double theta,
+                     const KeyPages &kp, int32_t batch, int32_t block_begin, int32_t block_end, const RopeFreq &rf,
                      uint32_t flags, bool bf16_raw, hipStream_t stream)
 {
     const int32_t nblk = block_end - block_begin;
     const int64_t total = (int64_t)batch * nblk;
     const dim3 grid((unsigned)((total + 3) / 4)), block(256);
-    const RopeFreq rf = rope_freq(theta);
     if (bf16_raw)
         QSA_LAUNCH("pool_rope_fp8", (pool_rope_fp8_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)raw,
                    raw_stride, codes, scales, pooled_stride, kp, total, nblk, block_begin, rf, flags);
@@ -248,11 +271,10 @@ void launch_pool_fp8(const void *raw, int64_t raw_stride, uint8_t *codes, float 
                    raw_stride, codes, scales, pooled_stride, kp, total, nblk, block_begin, rf, flags);
 }
 
-void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,
+void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, const RopeFreq &rf,
                        uint32_t flags, bool bf16, uint32_t *zero, int64_t zero_per_row, hipStream_t stream)
 {
     const dim3 grid((unsigned)(((int64_t)rows + 3) / 4)), block(256);
-    const RopeFreq rf = rope_freq(theta);
     if (bf16)
         QSA_LAUNCH("rope_query", (rope_query_kernel<bf16_t>), grid, block, 0, stream, (const bf16_t *)q, row_pos,
                    rows, (bf16_t *)qrot, rf, flags, zero, zero_per_row);

@@ -36,15 +36,25 @@ struct KeyPages {
 };
 
 // ---- pool.hip ---------------------------------------------------------------
+// Frequencies of the 64 rotary pairs (inv_freq of pair (j, j + 64)), formed on
+// the host in double precision and passed to the kernels by value.
+struct RopeFreq {
+    double f[kHalf];
+};
+RopeFreq rope_freq_plain(double theta);  // theta^(-j/64)
+// YaRN's interpolated frequencies (scale s >= 1 over an original context of
+// L tokens, ramp alpha..beta in turns over L); s == 1 gives rope_freq_plain.
+RopeFreq rope_freq_yarn(double theta, double s, double L, double alpha, double beta);
 void launch_pool(const void *raw, int64_t raw_stride, void *pooled, int64_t pooled_stride, const KeyPages &kp,
-                 int32_t batch, int32_t block_begin, int32_t block_end, double theta, uint32_t flags, bool bf16,
-                 hipStream_t stream);
+                 int32_t batch, int32_t block_begin, int32_t block_end, const RopeFreq &rf, uint32_t flags,
+                 bool bf16, hipStream_t stream, const float *norm_weight = nullptr);
 void launch_pool_fp8(const void *raw, int64_t raw_stride, uint8_t *codes, float *scales, int64_t pooled_stride,
-                     const KeyPages &kp, int32_t batch, int32_t block_begin, int32_t block_end, double theta,
+                     const KeyPages &kp, int32_t batch, int32_t block_begin, int32_t block_end, const RopeFreq &rf,
                      uint32_t flags, bool bf16_raw, hipStream_t stream);
 void launch_pool_append(const void *new_keys, const int32_t *positions, const int64_t *full_slots, void *ring,
-                        void *compressed, int32_t batch, double theta, uint32_t flags, bool bf16, hipStream_t stream);
-void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, double theta,
+                        void *compressed, int32_t batch, const RopeFreq &rf, uint32_t flags, bool bf16,
+                        hipStream_t stream);
+void launch_rope_query(const void *q, const int32_t *row_pos, int32_t rows, void *qrot, const RopeFreq &rf,
                        uint32_t flags, bool bf16, uint32_t *zero, int64_t zero_per_row, hipStream_t stream);
 
 // ---- score.hip --------------------------------------------------------------

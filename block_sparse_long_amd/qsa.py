@@ -25,14 +25,15 @@ FLAG_SCORE_GEMM = 1 << 9
 INDEX_DIM, INDEX_HEADS, BLOCK_TOKENS, MAX_TOP_K, MAX_QUERY_GROUP = 128, 4, 4, 4096, 64
 
 # every symbol include/qsa.h declares
-EXPORTS = ("qsa_pool_index_keys", "qsa_pool_index_keys_fp8", "qsa_pool_append", "qsa_score_topk_workspace_size",
+EXPORTS = ("qsa_pool_index_keys", "qsa_pool_index_keys_ex", "qsa_score_topk_ex", "qsa_pool_index_keys_fp8", "qsa_pool_append", "qsa_score_topk_workspace_size",
            "qsa_score_topk", "qsa_score_topk_merge_modes_offset", "qsa_score_topk_fp8_workspace_size",
            "qsa_score_topk_fp8", "qsa_score_topk_paged",
            "qsa_pool_index_keys_paged", "qsa_sparse_attn_prefill_paged", "qsa_sparse_attn_decode_paged",
            "qsa_sparse_attn_prefill_fp8kv",
            "qsa_sparse_attn_decode_fp8kv",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode_workspace_size",
-           "qsa_sparse_attn_decode", "qsa_status_string", "qsa_last_device_error", "qsa_profile_enable",
+           "qsa_sparse_attn_decode", "qsa_status_string",
+           "qsa_last_device_error", "qsa_profile_enable",
            "qsa_profile_reset", "qsa_profile_kernel_ms")
 
 
@@ -68,6 +69,10 @@ def load():
     st = ctypes.c_int
     lib.qsa_pool_index_keys.argtypes = [P, i64, P, i64, i32, i32, i32, f64, u32, st, P]
     lib.qsa_pool_index_keys.restype = st
+    lib.qsa_pool_index_keys_ex.argtypes = [P, i64, P, i64, i32, i32, i32, P, P, u32, st, P]
+    lib.qsa_pool_index_keys_ex.restype = st
+    lib.qsa_score_topk_ex.argtypes = [P, P, P, i32, P, i64, i32, i32, P, u32, st, P, P, P, P, sz, P]
+    lib.qsa_score_topk_ex.restype = st
     lib.qsa_pool_index_keys_fp8.argtypes = [P, i64, P, P, i64, i32, i32, i32, f64, u32, st, P]
     lib.qsa_pool_index_keys_fp8.restype = st
     lib.qsa_score_topk_fp8_workspace_size.argtypes = [i32, i32, i32, u32]
@@ -158,9 +163,34 @@ def _need_contig(*ts):
             raise ValueError("libqsa takes contiguous tensors")
 
 
+class Rope(ctypes.Structure):
+    """qsa_rope_t: RoPE base and YaRN scaling (yarn_factor 1 = plain RoPE)."""
+    _fields_ = [("theta", ctypes.c_double), ("yarn_factor", ctypes.c_double),
+                ("yarn_original_context", ctypes.c_double), ("yarn_alpha", ctypes.c_double),
+                ("yarn_beta", ctypes.c_double)]
+
+
+def rope(theta: float, yarn_factor: float = 1.0, yarn_original_context: float = 0.0, yarn_alpha: float = 1.0,
+         yarn_beta: float = 32.0) -> Rope:
+    return Rope(float(theta), float(yarn_factor), float(yarn_original_context), float(yarn_alpha),
+                float(yarn_beta))
+
+
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
+
+def pool_index_keys_ex(raw_keys, pooled, block_begin: int, block_end: int, rope_params: Optional[Rope],
+                       norm_weight=None, flags: int = 0, stream=None):
+    """pool_index_keys with a Rope (YaRN scaling) and an optional learned
+    norm weight (fp32 [128] on the device; needs FLAG_POOL_RMSNORM)."""
+    _need_contig(raw_keys, pooled, norm_weight)
+    B, L, _ = raw_keys.shape
+    rp = ctypes.byref(rope_params) if rope_params is not None else None
+    rc = load().qsa_pool_index_keys_ex(_ptr(raw_keys), L * INDEX_DIM, _ptr(pooled), pooled.shape[1] * INDEX_DIM, B,
+                                       int(block_begin), int(block_end), rp, _ptr(norm_weight), int(flags),
+                                       _dtype_code(raw_keys), _stream(stream))
+    _check("qsa_pool_index_keys_ex", rc)
 
 def pool_index_keys(raw_keys, pooled, block_begin: int, block_end: int, rope_theta: float,
                     flags: int = 0, stream=None):
@@ -241,6 +271,33 @@ def score_topk(q_index, row_seq, row_pos, pooled, max_visible_blocks: int, top_k
                                float(rope_theta), int(flags), dt, _ptr(sel_blocks), _ptr(sel_count),
                                _ptr(sel_scores), _ptr(workspace), workspace.numel(), _stream(stream))
     _check("qsa_score_topk", rc)
+    return sel_blocks, sel_count, sel_scores
+
+
+def score_topk_ex(q_index, row_seq, row_pos, pooled, max_visible_blocks: int, top_k: int,
+                  rope_params: Optional[Rope], flags: int = 0, sel_blocks=None, sel_count=None, sel_scores=None,
+                  workspace=None, want_scores: bool = True, stream=None):
+    """score_topk with a Rope (the keys pooled with the same rotation)."""
+    import torch
+    _need_contig(q_index, row_seq, row_pos, pooled)
+    R = q_index.shape[0]
+    dev = q_index.device
+    dt = _dtype_code(q_index)
+    if sel_blocks is None:
+        sel_blocks = torch.empty((R, top_k), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty((R,), dtype=torch.int32, device=dev)
+    if sel_scores is None and want_scores:
+        sel_scores = torch.empty((R, top_k), dtype=torch.float32, device=dev)
+    need = score_topk_workspace_size(R, max_visible_blocks, top_k, dt, flags)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    rp = ctypes.byref(rope_params) if rope_params is not None else None
+    rc = load().qsa_score_topk_ex(_ptr(q_index), _ptr(row_seq), _ptr(row_pos), R, _ptr(pooled),
+                                  pooled.shape[1] * INDEX_DIM, int(max_visible_blocks), int(top_k), rp,
+                                  int(flags), dt, _ptr(sel_blocks), _ptr(sel_count), _ptr(sel_scores),
+                                  _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("qsa_score_topk_ex", rc)
     return sel_blocks, sel_count, sel_scores
 
 

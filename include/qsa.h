@@ -104,6 +104,50 @@ qsa_status_t qsa_pool_index_keys(const void *raw_keys, int64_t raw_seq_stride, v
                                  qsa_dtype_t dtype, void *stream);
 
 /*
+ * Rotation of the _ex entry points: RoPE with base `theta` (> 1) on the pairs
+ * (j, j+64), optionally with YaRN's frequency scaling for contexts beyond the
+ * native one (flozi.net guide, "What the published evidence does and does
+ * not show", and the aicontrolled journal: the 262,144-token native context
+ * extends to one million tokens with YaRN; the pages give no parameters).
+ * YaRN is the published method of Peng, Quesnelle, Fan and Shippole (2023),
+ * its interpolation by parts: pair j, of frequency th_j = theta^(-j/64),
+ * turns r_j = L * th_j / (2 pi) times over the original context of
+ * L = yarn_original_context tokens; with g_j = 0 for r_j < alpha, 1 for
+ * r_j > beta and (r_j - alpha) / (beta - alpha) between, the pair rotates at
+ * (1 - g_j) * th_j / s + g_j * th_j, s = yarn_factor.  yarn_factor == 1 is
+ * plain RoPE (the other YaRN fields are then ignored).  For 1M tokens from
+ * the native 262,144: s = 4, L = 262144, alpha = 1, beta = 32 (the paper's
+ * ramp).  YaRN's attention temperature multiplies scores by a positive
+ * constant, which cannot change the indexer's ranking; it is not applied
+ * (for the final attention it belongs in the caller's softmax_scale).
+ */
+typedef struct {
+    double theta;
+    double yarn_factor;
+    double yarn_original_context;
+    double yarn_alpha;
+    double yarn_beta;
+} qsa_rope_t;
+
+/*
+ * qsa_pool_index_keys with the rotation given as a qsa_rope_t, which may be NULL
+ * with QSA_FLAG_NO_ROPE, and an optional learned weight for the pooled-key
+ * normalization ([SGL]: the averaged keys are "normalized" before the
+ * rotation; the pages give no norm or weight).  Reading: with
+ * QSA_FLAG_POOL_RMSNORM the mean m becomes (m / sqrt(mean(m^2) + 1e-6)) * w
+ * element by element, w = norm_weight (fp32 [128], device memory, 4-byte
+ * aligned), or unit weight when norm_weight is NULL.  A weight without
+ * QSA_FLAG_POOL_RMSNORM is QSA_ERR_INVALID_ARG.  With a NULL weight and
+ * yarn_factor 1 this is exactly qsa_pool_index_keys; the weight costs one
+ * multiply per element, the YaRN table nothing (it is formed on the host).
+ */
+qsa_status_t qsa_pool_index_keys_ex(const void *raw_keys, int64_t raw_seq_stride, void *pooled,
+                                    int64_t pooled_seq_stride, int32_t batch, int32_t block_begin,
+                                    int32_t block_end, const qsa_rope_t *rope,
+                                    const float *norm_weight, uint32_t flags, qsa_dtype_t dtype,
+                                    void *stream);
+
+/*
  * Steps a1-a3 with the compressed keys stored in FP8 ([LBL] section "Serving
  * it": the deployment keeps the indexer's keys in FP8).  Each block is pooled
  * and rotated exactly as by qsa_pool_index_keys, then rounded to FP32; with
@@ -184,6 +228,19 @@ qsa_status_t qsa_score_topk(const void *q_index, const int32_t *row_seq, const i
                             uint32_t flags, qsa_dtype_t dtype, int32_t *sel_blocks,
                             int32_t *sel_count, float *sel_scores, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/*
+ * qsa_score_topk with the index queries rotated by a qsa_rope_t, which may be NULL
+ * with QSA_FLAG_NO_ROPE; the keys must have been pooled with the same
+ * rotation (qsa_pool_index_keys_ex).  Workspace:
+ * qsa_score_topk_workspace_size().  Everything else as qsa_score_topk.
+ */
+qsa_status_t qsa_score_topk_ex(const void *q_index, const int32_t *row_seq, const int32_t *row_pos,
+                               int32_t rows, const void *pooled, int64_t pooled_seq_stride,
+                               int32_t max_visible_blocks, int32_t top_k, const qsa_rope_t *rope,
+                               uint32_t flags, qsa_dtype_t dtype, int32_t *sel_blocks,
+                               int32_t *sel_count, float *sel_scores, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /*
  * Diagnostics of the many-rows scorer.  When qsa_score_topk (or its FP8 and

@@ -112,6 +112,43 @@ def test_score_topk_validation(libqsa):
     assert call(theta=float("nan")) == qsa.ERR_INVALID_ARG
 
 
+def test_ex_validation(libqsa):
+    # qsa_pool_index_keys_ex / qsa_score_topk_ex: the rotation and the norm
+    # weight are checked before any HIP call
+    import ctypes as ct
+    f = libqsa.qsa_pool_index_keys_ex
+    good = qsa.rope(1e7, 4.0, 262144.0, 1.0, 32.0)
+    nf = qsa.FLAG_POOL_RMSNORM
+
+    def pool(rope=good, w=None, flags=0, batch=1, dt=qsa.BF16):
+        rp = ct.byref(rope) if rope is not None else None
+        return f(A, 4 * 128 * 100, B_, 128 * 100, batch, 0, 100, rp, w, flags, dt, None)
+
+    assert pool(batch=0) == qsa.OK
+    assert pool(rope=None) == qsa.ERR_INVALID_ARG                   # rotation without parameters
+    assert pool(w=C) == qsa.ERR_INVALID_ARG                         # a weight without the norm
+    assert pool(w=C + 2, flags=nf) == qsa.ERR_INVALID_ARG           # misaligned weight
+    assert pool(rope=qsa.rope(1.0)) == qsa.ERR_INVALID_ARG          # base must exceed 1
+    assert pool(rope=qsa.rope(1e7, 0.5, 262144.0)) == qsa.ERR_INVALID_ARG
+    assert pool(rope=qsa.rope(1e7, 4.0, 0.0)) == qsa.ERR_INVALID_ARG
+    assert pool(rope=qsa.rope(1e7, 4.0, 262144.0, 32.0, 1.0)) == qsa.ERR_INVALID_ARG
+    assert pool(rope=qsa.rope(1e7, float("inf"), 262144.0)) == qsa.ERR_INVALID_ARG
+    assert pool(flags=1 << 5) == qsa.ERR_INVALID_ARG
+    assert pool(dt=7) == qsa.ERR_UNSUPPORTED
+    g = libqsa.qsa_score_topk_ex
+    ws = qsa.score_topk_workspace_size(4, 100, 16, qsa.BF16)
+
+    def score(rope=good, flags=0, rows=4, k=16):
+        rp = ct.byref(rope) if rope is not None else None
+        return g(A, B_, C, rows, A, 128 * 100, 100, k, rp, flags, qsa.BF16, B_, C, None, 0x100000, ws, None)
+
+    assert score(rows=0) == qsa.OK
+    assert score(rope=None) == qsa.ERR_INVALID_ARG
+    assert score(rope=qsa.rope(1e7, 2.0, -5.0)) == qsa.ERR_INVALID_ARG
+    assert score(k=0) == qsa.ERR_INVALID_ARG
+    assert score(flags=qsa.FLAG_POOL_RMSNORM) == qsa.ERR_INVALID_ARG
+
+
 def test_merge_modes_offset(libqsa):
     # the fused scorer's per-row merge record sits inside its workspace; the
     # per-row scorer keeps none
@@ -259,6 +296,7 @@ def test_attn_validation(libqsa):
     assert fd(*d256[:19], ws256 - 1, *d256[20:]) == qsa.ERR_WORKSPACE
     assert dcall(18, 0x100004) == qsa.ERR_INVALID_ARG
     assert dcall(1, None) == qsa.ERR_INVALID_ARG
+
 
 
 def test_profile_api_without_launches(libqsa):
