@@ -514,6 +514,43 @@ static qsa_status_t score_topk_run(const void *q_index, const int32_t *row_seq, 
     return launch_status();
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free decode (qsa_sparse_attn_decode_noalloc): the split partials
+// live in this file-scope device array instead of a caller's workspace.  Every
+// GPU the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, so its device address is taken
+// once per device with hipGetSymbolAddress (with that device current) and
+// only that address is ever handed to a kernel.  Calls that overlap on one
+// GPU share the array and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[QSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once known
+std::mutex g_scratch_mutex;
+}  // namespace
+
+// The current device's copy of `scratch` (null if it cannot be resolved).
+static void *noalloc_scratch()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+    void *addr = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !addr) {
+        g_launch_err = g_last_failure = err != hipSuccess ? err : hipErrorInvalidSymbol;
+        return nullptr;
+    }
+    g_scratch_ptr[dev].store(addr, std::memory_order_release);
+    return addr;
+}
+
 extern "C" {
 
 static qsa_status_t check_attn_common(const void *q, const void *k_cache, const void *v_cache, int64_t kv_seq_stride,
@@ -636,7 +673,8 @@ static qsa_status_t attn_decode_impl(const void *q, const int32_t *row_pos, int3
                                     int32_t page_tokens, const int32_t *sel_blocks, const int32_t *sel_count,
                                     int32_t top_k, int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
                                     qsa_dtype_t dtype, void *out, float *lse, void *workspace, size_t workspace_bytes,
-                                    void *stream, bool kv_fp8 = false, float k_scale = 1.0f, float v_scale = 1.0f)
+                                    void *stream, bool kv_fp8 = false, float k_scale = 1.0f, float v_scale = 1.0f,
+                                    bool static_scratch = false)
 {
     if (!dtype_ok(dtype)) return QSA_ERR_UNSUPPORTED;
     if (batch < 0 || q_per_seq < 1) return QSA_ERR_INVALID_ARG;
@@ -656,6 +694,12 @@ static qsa_status_t attn_decode_impl(const void *q, const int32_t *row_pos, int3
     if (st != QSA_OK) return st;
     if (!row_pos) return QSA_ERR_INVALID_ARG;
     const size_t need = qsa_sparse_attn_decode_workspace_size(batch, q_per_seq, Hq, D, top_k);
+    if (static_scratch) {  // the library's own scratch array; the first HIP call of this path
+        if (need > (size_t)QSA_NOALLOC_SCRATCH_BYTES) return QSA_ERR_WORKSPACE;
+        workspace = noalloc_scratch();
+        if (!workspace) return QSA_ERR_DEVICE;
+        workspace_bytes = QSA_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return QSA_ERR_INVALID_ARG;
     if (workspace_bytes < need) return QSA_ERR_WORKSPACE;
     AttnArgs a{};
@@ -706,6 +750,17 @@ qsa_status_t qsa_sparse_attn_decode(const void *q, const int32_t *row_pos, int32
     return attn_decode_impl(q, row_pos, batch, q_per_seq, tail_start, k_cache, v_cache, kv_seq_stride, nullptr, 0, 0,
                             sel_blocks, sel_count, top_k, Hq, Hkv, D, softmax_scale, dtype, out, lse, workspace,
                             workspace_bytes, stream);
+}
+
+qsa_status_t qsa_sparse_attn_decode_noalloc(const void *q, const int32_t *row_pos, int32_t batch, int32_t q_per_seq,
+                                            const int32_t *tail_start, const void *k_cache, const void *v_cache,
+                                            int64_t kv_seq_stride, const int32_t *sel_blocks, const int32_t *sel_count,
+                                            int32_t top_k, int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                                            qsa_dtype_t dtype, void *out, float *lse, void *stream)
+{
+    return attn_decode_impl(q, row_pos, batch, q_per_seq, tail_start, k_cache, v_cache, kv_seq_stride, nullptr, 0, 0,
+                            sel_blocks, sel_count, top_k, Hq, Hkv, D, softmax_scale, dtype, out, lse, nullptr, 0,
+                            stream, false, 1.0f, 1.0f, true);
 }
 
 qsa_status_t qsa_sparse_attn_decode_paged(const void *q, const int32_t *row_pos, int32_t batch, int32_t q_per_seq,

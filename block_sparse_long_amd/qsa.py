@@ -32,7 +32,7 @@ EXPORTS = ("qsa_pool_index_keys", "qsa_pool_index_keys_ex", "qsa_score_topk_ex",
            "qsa_sparse_attn_prefill_fp8kv",
            "qsa_sparse_attn_decode_fp8kv",
            "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode_workspace_size",
-           "qsa_sparse_attn_decode", "qsa_status_string",
+           "qsa_sparse_attn_decode", "qsa_sparse_attn_decode_noalloc", "qsa_status_string",
            "qsa_last_device_error", "qsa_profile_enable",
            "qsa_profile_reset", "qsa_profile_kernel_ms")
 
@@ -112,6 +112,9 @@ def load():
     lib.qsa_sparse_attn_decode.argtypes = [P, P, i32, i32, P, P, P, i64, P, P, i32, i32, i32, i32, f32,
                                            st, P, P, P, sz, P]
     lib.qsa_sparse_attn_decode.restype = st
+    lib.qsa_sparse_attn_decode_noalloc.argtypes = [P, P, i32, i32, P, P, P, i64, P, P, i32, i32, i32, i32, f32,
+                                                   st, P, P, P]
+    lib.qsa_sparse_attn_decode_noalloc.restype = st
     lib.qsa_status_string.argtypes = [st]
     lib.qsa_status_string.restype = ctypes.c_char_p
     lib.qsa_last_device_error.argtypes = []
@@ -379,6 +382,34 @@ def sparse_attn_decode(q, row_pos, k_cache, v_cache, sel_blocks, sel_count, tail
                                        Hq, Hkv, D, scale, _dtype_code(q), _ptr(out), _ptr(lse),
                                        _ptr(workspace), workspace.numel(), _stream(stream))
     _check("qsa_sparse_attn_decode", rc)
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def sparse_attn_decode_noalloc(q, row_pos, k_cache, v_cache, sel_blocks, sel_count, tail_start=None,
+                               softmax_scale: Optional[float] = None, out=None, lse=None, want_lse=True,
+                               stream=None):
+    """sparse_attn_decode through the allocation-free entry point: the split
+    partials live in the library's static per-device scratch, so no workspace
+    is passed (the call itself allocates nothing; pass `out` / `lse` to keep
+    this wrapper from allocating them).  Returns (out, lse)."""
+    import torch
+    _need_contig(q, row_pos, k_cache, v_cache, sel_blocks, sel_count, tail_start)
+    B, Qn, Hq, D = q.shape
+    _, L, Hkv, _ = k_cache.shape
+    top_k = sel_blocks.shape[1]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Qn, Hq), dtype=torch.float32, device=q.device)
+    rc = load().qsa_sparse_attn_decode_noalloc(_ptr(q), _ptr(row_pos), B, Qn, _ptr(tail_start), _ptr(k_cache),
+                                               _ptr(v_cache), L * Hkv * D, _ptr(sel_blocks), _ptr(sel_count),
+                                               top_k, Hq, Hkv, D, scale, _dtype_code(q), _ptr(out), _ptr(lse),
+                                               _stream(stream))
+    _check("qsa_sparse_attn_decode_noalloc", rc)
     return out, lse
 
 

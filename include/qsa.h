@@ -371,6 +371,31 @@ qsa_status_t qsa_sparse_attn_decode(const void *q, const int32_t *row_pos, int32
                                     qsa_dtype_t dtype, void *out, float *lse, void *workspace,
                                     size_t workspace_bytes, void *stream);
 
+/*
+ * qsa_sparse_attn_decode without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops
+ * or harnesses that forbid hipMalloc.  The split partials go to a static
+ * device array of QSA_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends (the copy of the calling thread's
+ * current device is used; `stream` must belong to that device).  The call
+ * allocates nothing (with kernel timing enabled, timing events are created
+ * as for every entry point).  Arguments, results and errors are those of
+ * qsa_sparse_attn_decode; a call whose workspace
+ * (qsa_sparse_attn_decode_workspace_size) would exceed the array returns
+ * QSA_ERR_WORKSPACE before any HIP call.  Every call on one GPU shares that
+ * GPU's array, and nothing in it needs to start at zero: calls that overlap
+ * on one GPU (concurrent streams or threads) race and are the caller's to
+ * order.
+ */
+#define QSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+qsa_status_t qsa_sparse_attn_decode_noalloc(const void *q, const int32_t *row_pos, int32_t batch,
+                                            int32_t q_per_seq, const int32_t *tail_start,
+                                            const void *k_cache, const void *v_cache,
+                                            int64_t kv_seq_stride, const int32_t *sel_blocks,
+                                            const int32_t *sel_count, int32_t top_k, int32_t Hq,
+                                            int32_t Hkv, int32_t D, float softmax_scale,
+                                            qsa_dtype_t dtype, void *out, float *lse, void *stream);
+
 /* qsa_sparse_attn_decode on a paged K/V pool (bf16 with q_per_seq <= 32,
  * else QSA_ERR_UNSUPPORTED). */
 qsa_status_t qsa_sparse_attn_decode_paged(const void *q, const int32_t *row_pos, int32_t batch,

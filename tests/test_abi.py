@@ -298,6 +298,33 @@ def test_attn_validation(libqsa):
     assert dcall(1, None) == qsa.ERR_INVALID_ARG
 
 
+def test_attn_decode_noalloc_validation(libqsa):
+    # the allocation-free decode: qsa_sparse_attn_decode's checks, then the
+    # static scratch's limit, all before any HIP call
+    fn = libqsa.qsa_sparse_attn_decode_noalloc
+    d = [A, B_, 4, 4, None, A, B_, 1024, C, A, 512, 8, 1, 128, 0.1, qsa.BF16, B_, None, None]
+
+    def call(i, v):
+        a = list(d)
+        a[i] = v
+        return fn(*a)
+
+    assert call(2, 0) == qsa.OK                                        # nothing to do
+    assert call(3, 9) == qsa.ERR_UNSUPPORTED                           # 9 rows x 8 heads > 64
+    assert call(0, MIS) == qsa.ERR_INVALID_ARG
+    assert call(1, None) == qsa.ERR_INVALID_ARG
+    assert call(10, 0) == qsa.ERR_INVALID_ARG
+    assert call(13, 64) == qsa.ERR_UNSUPPORTED
+    # a call whose partials would not fit the static scratch is refused
+    big = 200
+    assert qsa.sparse_attn_decode_workspace_size(big, 1, 8, 128, 512) > qsa.NOALLOC_SCRATCH_BYTES
+    assert qsa.sparse_attn_decode_workspace_size(100, 1, 8, 128, 512) <= qsa.NOALLOC_SCRATCH_BYTES
+    a = list(d)
+    a[2], a[3] = big, 1
+    assert fn(*a) == qsa.ERR_WORKSPACE
+    hdr = open(HDR).read()
+    assert f"#define QSA_NOALLOC_SCRATCH_BYTES (16u << 20)" in hdr and qsa.NOALLOC_SCRATCH_BYTES == 16 << 20
+
 
 def test_profile_api_without_launches(libqsa):
     qsa.profile_enable(True)
