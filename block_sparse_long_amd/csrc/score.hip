@@ -10,15 +10,16 @@
 // supplies A[m = l%16][8 k-slots] and B[8 k-slots][n = l%16] and receives
 // C[4*(l/16) + j][l%16], j = 0..3.  A and B take the same 8 k-slots for one
 // lane group l/16, so any one-to-one assignment of head dims to (group, slot)
-// pairs gives the same dot product: lane group g supplies the dims
-// 32g + 8s .. 32g + 8s + 7 at MFMA step s (s = 0..3), i.e. 64 contiguous bytes
-// of a key per lane.
+// pairs gives the same dot product: in the bf16 decode scorer lane group g
+// supplies the dims 8g + 32s .. +7 at MFMA step s (s = 0..3), so the four
+// groups of a key column read one contiguous 64-byte run per step.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
 namespace qsa {
 
 constexpr int kChunk = 2048;  // blocks per workgroup in the row-split kernels
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float relu_sum4(f32x4_t a)
 {
@@ -88,9 +89,15 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
         for (int nt = 0; nt < 4; ++nt) {
             const int64_t b = min(base + 4 * m + nt, b_end - 1);  // clamp: stays inside the visible range
             const int64_t off = kp.table ? key_at(kp, 0, seq, b, p.pg[nt]) * kDim : seq * pooled_stride + b * kDim;
-            const uint4 *src = (const uint4 *)(pooled + off + 32 * g);
+            // lane group g takes head dims 8g + 32s .. +7 at step s: the four
+            // groups read one 64-byte run of the key per step; the keys are read
+            // once per call, so the loads are non-temporal
+            const uint4 *src = (const uint4 *)(pooled + off + 8 * g);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) v[nt][s] = src[s];
+            for (int s = 0; s < 4; ++s) {
+                const u32x4_t x = __builtin_nontemporal_load((const u32x4_t *)(src + 4 * s));
+                v[nt][s] = make_uint4(x.x, x.y, x.z, x.w);
+            }
         }
     };
     uint4 v0[4][4], v1[4][4];
@@ -105,7 +112,7 @@ __global__ __launch_bounds__(256) void score_rows_bf16_kernel(
 #pragma unroll
     for (int s = 0; s < 4; ++s)
         a[s] = m < kIdxHeads
-                   ? as_bf16x8(*(const uint4 *)(qrot + ((int64_t)r * kIdxHeads + m) * kDim + 32 * g + 8 * s))
+                   ? as_bf16x8(*(const uint4 *)(qrot + ((int64_t)r * kIdxHeads + m) * kDim + 8 * g + 32 * s))
                    : zero_bf16x8();
     auto score = [&](int64_t base, const uint4 (&v)[4][4]) {
         float sc[4];

@@ -12,9 +12,9 @@
 //   1. sample: every row is scored against one block in 32 (a fixed
 //      pseudo-random pick inside each group of 32), about 3% of the GEMM;
 //      each lane keeps its 4 best sampled scores per row;
-//   2. threshold: tau = the j-th best of those candidates, j = ceil(3k/32),
-//      which is at most the row's j-th best sampled score (so about 3k of the
-//      row's blocks are expected to score >= tau);
+//   2. threshold: tau = the j-th best of those candidates, j = ceil(2.5k/32),
+//      which is at most the row's j-th best sampled score (so about 2.5k of
+//      the row's blocks are expected to score >= tau);
 //   3. filter: the full GEMM writes out only the (key, block) pairs with
 //      score >= tau, each lane into its own list (no atomics, no cross-lane
 //      work in the MFMA loop);
@@ -45,7 +45,16 @@ constexpr int kSampleStride = 32;     // one sampled block per 32
 constexpr int kMergeWaves = 4;        // merge: rows per workgroup, one wave each
 constexpr int kStage = 2048;          // merge: pairs a wave stages in LDS
 
-__device__ __forceinline__ int32_t sample_j(int32_t top_k) { return (3 * top_k + kSampleStride - 1) / kSampleStride; }
+// tau is the j-th best sampled score of a row, j = ceil(2.5 k / 32): about
+// 2.5 k of the row's blocks reach it.  The row's k-th best block is below tau
+// only if at least j of its k best blocks were sampled; for k = 512 that
+// takes 40 of an expected 16 (binomial tail 1.8e-7 per row when the best
+// blocks fall at random, less when they cluster).  Such a row is still
+// exact: the merge recomputes it.
+__host__ __device__ __forceinline__ int32_t sample_j(int32_t top_k)
+{
+    return (5 * top_k + 2 * kSampleStride - 1) / (2 * kSampleStride);
+}
 
 // Block of sample i: group i of 32 blocks, a fixed pseudo-random offset in it.
 __device__ __forceinline__ int64_t sample_block(int64_t i)
@@ -1021,7 +1030,7 @@ int32_t fused_score_split_len(int32_t max_nb, int32_t nsplit)
 // i.e. fewer than about 32*j visible blocks).
 int32_t fused_score_subcap(int32_t top_k, int32_t nsplit)
 {
-    const int32_t j = (3 * top_k + kSampleStride - 1) / kSampleStride;
+    const int32_t j = sample_j(top_k);
     const int32_t no_tau = (j + 1) * kSampleStride / 16 + 8;
     const int32_t share = (int32_t)(((int64_t)6 * top_k + 16 * nsplit - 1) / (16 * nsplit));
     return (max(no_tau, share) + 7) / 8 * 8;
