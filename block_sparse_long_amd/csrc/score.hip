@@ -249,9 +249,12 @@ __global__ __launch_bounds__(256) void score_rows_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// fp32, any number of rows: one thread per block, q~ of the row in LDS.
+// fp32, any number of rows: grid (chunks of 256 blocks, rows), one thread per
+// block, q~ of the row in LDS (read by broadcast).  A thread's 512-byte key
+// is read with all of its 16-byte loads in flight: two batches of 16.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void score_rows_f32_kernel(
+constexpr int kChunkF32 = 256;
+__global__ __launch_bounds__(kChunkF32) void score_rows_f32_kernel(
     const float *__restrict__ qrot, const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_pos,
     const float *__restrict__ pooled, int64_t pooled_stride, KeyPages kp, int32_t max_nb, float *__restrict__ scores,
     int64_t sc_stride, uint32_t *__restrict__ hist)
@@ -260,28 +263,41 @@ __global__ __launch_bounds__(256) void score_rows_f32_kernel(
     __shared__ uint32_t lhist[kHistBins];
     const int r = blockIdx.y;
     const int64_t nc = min(visible_blocks(row_pos[r]), (int64_t)max_nb);
-    const int64_t b_begin = (int64_t)blockIdx.x * kChunk;
+    const int64_t b_begin = (int64_t)blockIdx.x * kChunkF32;
     if (b_begin >= nc) return;
-    const int64_t b_end = min(nc, b_begin + (int64_t)kChunk);
+    const int64_t b = b_begin + threadIdx.x;
+    const bool valid = b < nc;
+    const int64_t seq = row_seq[r];
+    // the key is requested before the query and histogram are set up
+    const float4 *kr = (const float4 *)(pooled + key_offset(kp, pooled_stride, seq, valid ? b : nc - 1));
+    constexpr int kHalf4 = kDim / 8;  // float4s per batch
+    float4 kv[kHalf4];
+#pragma unroll
+    for (int i = 0; i < kHalf4; ++i) kv[i] = kr[i];
     if (hist) hist_clear(lhist);
     for (int i = threadIdx.x; i < kIdxHeads * kDim / 4; i += blockDim.x)
         qs[i] = ((const float4 *)(qrot + (int64_t)r * kIdxHeads * kDim))[i];
     __syncthreads();
-    const int64_t seq = row_seq[r];
-    for (int64_t b = b_begin + threadIdx.x; b < b_end; b += blockDim.x) {
-        const float4 *kr = (const float4 *)(pooled + key_offset(kp, pooled_stride, seq, b));
-        float d[kIdxHeads] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int i = 0; i < kDim / 4; ++i) {
-            const float4 kv = kr[i];
+    float d[kIdxHeads] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        if (half == 1) {
+#pragma unroll
+            for (int i = 0; i < kHalf4; ++i) kv[i] = kr[kHalf4 + i];
+        }
+#pragma unroll
+        for (int i = 0; i < kHalf4; ++i) {
 #pragma unroll
             for (int h = 0; h < kIdxHeads; ++h) {
-                const float4 qv = qs[h * (kDim / 4) + i];
-                d[h] = fmaf(qv.x, kv.x, d[h]);
-                d[h] = fmaf(qv.y, kv.y, d[h]);
-                d[h] = fmaf(qv.z, kv.z, d[h]);
-                d[h] = fmaf(qv.w, kv.w, d[h]);
+                const float4 qv = qs[h * (kDim / 4) + half * kHalf4 + i];
+                d[h] = fmaf(qv.x, kv[i].x, d[h]);
+                d[h] = fmaf(qv.y, kv[i].y, d[h]);
+                d[h] = fmaf(qv.z, kv[i].z, d[h]);
+                d[h] = fmaf(qv.w, kv[i].w, d[h]);
             }
         }
+    }
+    if (valid) {
         const float sc = ((fmaxf(d[0], 0.0f) + fmaxf(d[1], 0.0f)) + fmaxf(d[2], 0.0f)) + fmaxf(d[3], 0.0f);
         scores[(int64_t)r * sc_stride + b] = sc;
         if (hist) atomicAdd(&lhist[score_key(sc) >> kHistShift], 1u);
@@ -295,13 +311,15 @@ void launch_score_rows(const void *qrot, const int32_t *row_seq, const int32_t *
                        const void *pooled, int64_t pooled_stride, const KeyPages &kp, int32_t max_nb, float *scores,
                        int64_t sc_stride, uint32_t *hist, bool bf16, hipStream_t stream)
 {
-    const dim3 grid((unsigned)score_chunks(max_nb), (unsigned)rows), block(256);
-    if (bf16)
+    if (bf16) {
+        const dim3 grid((unsigned)score_chunks(max_nb), (unsigned)rows), block(256);
         QSA_LAUNCH("score_rows_bf16", score_rows_bf16_kernel, grid, block, 0, stream, (const bf16_t *)qrot, row_seq,
                    row_pos, (const bf16_t *)pooled, pooled_stride, kp, max_nb, scores, sc_stride, hist);
-    else
+    } else {
+        const dim3 grid((unsigned)(((int64_t)max_nb + kChunkF32 - 1) / kChunkF32), (unsigned)rows), block(kChunkF32);
         QSA_LAUNCH("score_rows_f32", score_rows_f32_kernel, grid, block, 0, stream, (const float *)qrot, row_seq,
                    row_pos, (const float *)pooled, pooled_stride, kp, max_nb, scores, sc_stride, hist);
+    }
 }
 
 void launch_score_rows_fp8(const void *qrot, const int32_t *row_seq, const int32_t *row_pos, int32_t rows,
