@@ -304,6 +304,17 @@ def bench_prefill(spec, steps, warmup, cpu_baseline, keys="bf16", w=None, kv="bf
     return res
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_prefill(spec, w, target_s=12.0):
     import oracle
     L, nb, k = spec.ctx, spec.n_blocks, spec.top_k
@@ -331,7 +342,7 @@ def cpu_prefill(spec, w, target_s=12.0):
     rows = np.unique(np.linspace(0, R - 1, n).astype(np.int64))
     t = rows_time(rows)
     per_step = t_pool + t * R / len(rows)
-    return {"value": R / per_step, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+    return {"value": R / per_step, "unit": "tokens/s", "cores": oracle.threads(), "cpu": cpu_model(), "kind": "oracle",
             "sample": f"pool of the chunk's {spec.chunk // 4} new blocks, then score/top-{k} and attention for "
                       f"{len(rows)} of {R} rows spread over the chunk ({t_pool + t:.1f}s); per-step time "
                       f"extrapolated to all rows"}
@@ -657,7 +668,7 @@ def cpu_decode(spec, w, pooled_h, target_s=10.0, max_passes=64):
         if time.perf_counter() - t0 >= target_s and passes >= B:
             break
     t = time.perf_counter() - t0
-    return {"value": rows / t, "unit": "query rows/s", "cores": oracle.threads(), "kind": "oracle",
+    return {"value": rows / t, "unit": "query rows/s", "cores": oracle.threads(), "cpu": cpu_model(), "kind": "oracle",
             "sample": f"{passes} sequence steps over the {B} sequences (each: score/top-{k} of the anchor over "
                       f"{int(visible(w['row_pos'][0]))} blocks, then attention of its {spec.q_per_seq} rows) "
                       f"in {t:.1f}s"}
@@ -680,6 +691,7 @@ KERNEL_SOURCE = {"pool_rope": "pool.hip", "pool_append": "pool.hip", "rope_query
                  "attn_combine": "attn.hip", "pool_rope_fp8": "pool.hip", "score_rows_fp8": "score.hip",
                  "score_sample_fp8": "score_fused.hip", "score_filter_fp8": "score_fused.hip"}
 COPY_BYTES = 1 << 30
+XCDS, SIMDS = 8, 256 * 4   # MI355X: 8 XCDs, 256 CUs of 4 SIMDs
 
 
 def source_digest(kernel):
@@ -773,8 +785,23 @@ def rocprof_summary(dirs):
                 n = short_kernel_name(r["Name"]) or r["Name"][:40]
                 print(f"  {n:<20} {r['Calls']:>6} {float(r['AverageNs']):>12.0f} {r['MinNs']:>10} {r['MaxNs']:>10}")
         cm = counter_means(d)
+        if cm:
+            print("# counters  name  source_digest  counter=mean per dispatch ...  [derived]")
+            print(f"# derived: mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} XCDs * {SIMDS} SIMDs); "
+                  "coexec = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES; "
+                  "valu_per_mfma = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA")
         for n in sorted(cm):
-            print(f"{n:<20} " + "  ".join(f"{c}={v:.6g}" for c, v in sorted(cm[n].items())))
+            c = cm[n]
+            dg = source_digest(n) if n in KERNEL_SOURCE else "-"
+            der = []
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c and c.get("GRBM_GUI_ACTIVE"):
+                der.append(f"mfma_busy={c['SQ_VALU_MFMA_BUSY_CYCLES'] / (c['GRBM_GUI_ACTIVE'] / XCDS * SIMDS):.4f}")
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in c and c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+                der.append(f"coexec={c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.4f}")
+            if "SQ_INSTS_VALU" in c and c.get("SQ_INSTS_MFMA"):
+                der.append(f"valu_per_mfma={(c['SQ_INSTS_VALU'] - c['SQ_INSTS_MFMA']) / c['SQ_INSTS_MFMA']:.3f}")
+            print(f"counters {n:<20} {dg} " + "  ".join(f"{k}={v:.6g}" for k, v in sorted(c.items())) +
+                  ("  [" + " ".join(der) + "]" if der else ""))
 
 
 def traffic_summary(fetch_dir, write_dir, workload):

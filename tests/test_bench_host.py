@@ -153,3 +153,19 @@ def test_trace_is_used_only_while_the_source_matches(bench, tmp_path, monkeypatc
     r = bench.roofline_for("score_filter", ("mfma", 5.0e11, "flop"), (1, 0.5, 0.5, [0.5]), None,
                            bench.load_trace("w"))
     assert r["frac"] == 0.4 and r["trace_avg_us"] == 510.0 and r["trace_frac"] == round(5.0e11 / 510e-6 / 2.5e15, 4)
+
+
+def test_counter_summary_is_digest_stamped_with_derived_rates(bench, tmp_path, capsys):
+    k = "void qsa::score_filter_kernel<false>(qsa::FusedScoreArgs)"
+    rows = []
+    for name, val in [("SQ_VALU_MFMA_BUSY_CYCLES", 4.0e8), ("GRBM_GUI_ACTIVE", 8.0e6), ("SQ_INSTS_VALU", 5.0e6),
+                      ("SQ_INSTS_MFMA", 1.0e6), ("SQ_VALU_MFMA_COEXEC_CYCLES", 1.0e8)]:
+        rows.append({"Kernel_Name": k, "Counter_Name": name, "Dispatch_Id": 1, "Counter_Value": val})
+    _write_csv(str(tmp_path / "c" / "run_counter_collection.csv"),
+               ["Kernel_Name", "Counter_Name", "Dispatch_Id", "Counter_Value"], rows)
+    bench.rocprof_summary([str(tmp_path / "c")])
+    line = [ln for ln in capsys.readouterr().out.splitlines() if ln.startswith("counters score_filter")][0]
+    assert bench.source_digest("score_filter") in line
+    # busy cycles over (GUI cycles per XCD x SIMDs): 4e8 / (8e6 / 8 * 1024)
+    assert f"mfma_busy={4.0e8 / (8.0e6 / 8 * 1024):.4f}" in line
+    assert "coexec=0.2500" in line and "valu_per_mfma=4.000" in line
