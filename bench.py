@@ -770,6 +770,10 @@ def counter_means(d):
 
 
 def rocprof_summary(dirs):
+    merged = {}  # counters of every directory (one --pmc pass each), per kernel
+    for d in dirs:
+        for n, c in counter_means(d).items():
+            merged.setdefault(n, {}).update(c)
     for d in dirs:
         print(f"# rocprofv3 output: {d}")
         st = kernel_trace_stats(d)
@@ -784,24 +788,24 @@ def rocprof_summary(dirs):
             for r in csv.DictReader(open(f)):
                 n = short_kernel_name(r["Name"]) or r["Name"][:40]
                 print(f"  {n:<20} {r['Calls']:>6} {float(r['AverageNs']):>12.0f} {r['MinNs']:>10} {r['MaxNs']:>10}")
-        cm = counter_means(d)
-        if cm:
-            print("# counters  name  source_digest  counter=mean per dispatch ...  [derived]")
-            print(f"# derived: mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} XCDs * {SIMDS} SIMDs); "
-                  "coexec = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES; "
-                  "valu_per_mfma = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA")
-        for n in sorted(cm):
-            c = cm[n]
-            dg = source_digest(n) if n in KERNEL_SOURCE else "-"
-            der = []
-            if "SQ_VALU_MFMA_BUSY_CYCLES" in c and c.get("GRBM_GUI_ACTIVE"):
-                der.append(f"mfma_busy={c['SQ_VALU_MFMA_BUSY_CYCLES'] / (c['GRBM_GUI_ACTIVE'] / XCDS * SIMDS):.4f}")
-            if "SQ_VALU_MFMA_COEXEC_CYCLES" in c and c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
-                der.append(f"coexec={c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.4f}")
-            if "SQ_INSTS_VALU" in c and c.get("SQ_INSTS_MFMA"):
-                der.append(f"valu_per_mfma={(c['SQ_INSTS_VALU'] - c['SQ_INSTS_MFMA']) / c['SQ_INSTS_MFMA']:.3f}")
-            print(f"counters {n:<20} {dg} " + "  ".join(f"{k}={v:.6g}" for k, v in sorted(c.items())) +
-                  ("  [" + " ".join(der) + "]" if der else ""))
+    cm = merged
+    if cm:
+        print("# counters  name  source_digest  counter=mean per dispatch ...  [derived]")
+        print(f"# derived: mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} XCDs * {SIMDS} SIMDs); "
+              "coexec = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES; "
+              "valu_per_mfma = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA")
+    for n in sorted(cm):
+        c = cm[n]
+        dg = source_digest(n) if n in KERNEL_SOURCE else "-"
+        der = []
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and c.get("GRBM_GUI_ACTIVE"):
+            der.append(f"mfma_busy={c['SQ_VALU_MFMA_BUSY_CYCLES'] / (c['GRBM_GUI_ACTIVE'] / XCDS * SIMDS):.4f}")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in c and c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            der.append(f"coexec={c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.4f}")
+        if "SQ_INSTS_VALU" in c and c.get("SQ_INSTS_MFMA"):
+            der.append(f"valu_per_mfma={(c['SQ_INSTS_VALU'] - c['SQ_INSTS_MFMA']) / c['SQ_INSTS_MFMA']:.3f}")
+        print(f"counters {n:<20} {dg} " + "  ".join(f"{k}={v:.6g}" for k, v in sorted(c.items())) +
+              ("  [" + " ".join(der) + "]" if der else ""))
 
 
 def traffic_summary(fetch_dir, write_dir, workload):
