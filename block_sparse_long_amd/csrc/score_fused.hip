@@ -505,13 +505,15 @@ __device__ __forceinline__ float scaled(float raw) { return (float)((double)raw 
 // in the stage's LDS), whose per-word prefix counts give each one its slot.
 constexpr int kRegPairs = kStage / kWave;
 constexpr int kWinWords = 2048;  // bitmap window: 65,536 blocks
-// Lane l owns bitmap words [32l, 32l + 32).  Word w is stored at w + w/32 and
-// its u16 prefix count at w + 2(w/32), so the 64 lanes walking their own
-// words hit distinct LDS banks.
-__device__ __forceinline__ uint32_t bm_slot(uint32_t w) { return w + (w >> 5); }
-__device__ __forceinline__ uint32_t pre_slot(uint32_t w) { return w + 2u * (w >> 5); }
-constexpr int kBmSlots = kWinWords + kWinWords / 32;
-constexpr int kPreSlots = kWinWords + 2 * (kWinWords / 32);
+// Lane l owns bitmap words [32l, 32l + 32).  Word w is stored at w + 4(w/32)
+// and its u16 prefix count at w + 8(w/32): a lane's run is 16-byte aligned,
+// so it is cleared, read and its counts written 16 bytes at a time, and the
+// runs' strides (144 and 80 bytes) put the 16 lanes of an access on distinct
+// LDS bank groups.
+__device__ __forceinline__ uint32_t bm_slot(uint32_t w) { return w + 4u * (w >> 5); }
+__device__ __forceinline__ uint32_t pre_slot(uint32_t w) { return w + 8u * (w >> 5); }
+constexpr int kBmSlots = kWinWords + 4 * (kWinWords / 32);
+constexpr int kPreSlots = kWinWords + 8 * (kWinWords / 32);
 static_assert(kBmSlots * 4 + kPreSlots * 2 <= kStage * 8, "bitmap + prefix fit the stage");
 
 // The pick step of one radix pass (of `width` <= 8 bits) of a descending
@@ -634,7 +636,10 @@ __device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n,
     for (int32_t w0 = 0; w0 < nc; w0 += 32 * kWinWords) {
         const int nwords = min(kWinWords, (nc - w0 + 31) / 32);
         const uint32_t wbits = 32u * (uint32_t)nwords;
-        for (int i = lane; i < kBmSlots; i += kWave) bm[i] = 0u;
+        // the lane's run of 32 words (the padding words are never read)
+#pragma unroll
+        for (int j = 0; j < kWinWords / kWave / 4; ++j)
+            ((uint4 *)(bm + bm_slot((uint32_t)lane * (kWinWords / kWave))))[j] = make_uint4(0u, 0u, 0u, 0u);
         wave_fence();
 #pragma unroll
         for (int i = 0; i < kRegPairs; ++i) {  // a pair not kept ORs 0 into its lane's word
@@ -648,7 +653,13 @@ __device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n,
         constexpr int kPer = kWinWords / kWave;
         uint32_t words[kPer], c = 0;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) words[j] = bm[bm_slot((uint32_t)(lane * kPer + j))];
+        for (int j = 0; j < kPer / 4; ++j) {
+            const uint4 x = ((const uint4 *)(bm + bm_slot((uint32_t)(lane * kPer))))[j];
+            words[4 * j] = x.x;
+            words[4 * j + 1] = x.y;
+            words[4 * j + 2] = x.z;
+            words[4 * j + 3] = x.w;
+        }
 #pragma unroll
         for (int j = 0; j < kPer; ++j) c += (uint32_t)__popc(words[j]);
         const uint32_t incl = wave_incl_scan(c);
@@ -657,9 +668,16 @@ __device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n,
         // would serialise on the lanes that hold the clusters)
         uint32_t run = incl - c;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            pre[pre_slot((uint32_t)(lane * kPer + j))] = (uint16_t)run;
-            run += (uint32_t)__popc(words[j]);
+        for (int j = 0; j < kPer / 8; ++j) {  // 8 counts per 16-byte write
+            uint32_t h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = run;
+                run += (uint32_t)__popc(words[8 * j + 2 * e]);
+                h[e] = lo | (run << 16);
+                run += (uint32_t)__popc(words[8 * j + 2 * e + 1]);
+            }
+            ((uint4 *)(pre + pre_slot((uint32_t)(lane * kPer))))[j] = make_uint4(h[0], h[1], h[2], h[3]);
         }
         wave_fence();
 #pragma unroll
@@ -723,7 +741,7 @@ template <bool FP8>
 __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, int32_t *__restrict__ sel_blocks,
                                                          int32_t *__restrict__ sel_count, float *__restrict__ sel_scores)
 {
-    __shared__ uint2 stage[kMergeWaves][kStage];
+    __shared__ __align__(16) uint2 stage[kMergeWaves][kStage];
     __shared__ uint32_t hb[kMergeWaves][256 + kWave];  // 256 bins + a spare slot per lane
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t r = (int64_t)blockIdx.x * kMergeWaves + w;
