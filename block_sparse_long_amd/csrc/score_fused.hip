@@ -243,6 +243,13 @@ __global__ __launch_bounds__(256, 2) void score_sample_kernel(FusedScoreArgs a)
         int64_t nb_hi;
         const int32_t seq = next_seq_group(a, row0, nrows, todo, nb_hi);
         const int64_t hi = min(s_hi, (nb_hi + kSampleStride - 1) / kSampleStride);  // samples that can be visible
+        // smallest visible bound over the wave's rows of this group
+        int64_t lim_min = INT64_MAX;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            if (my_seq[mt] == seq) lim_min = min(lim_min, my_nc[mt]);
+        lim_min = min(lim_min, (int64_t)__shfl_xor((long long)lim_min, 16));
+        lim_min = min(lim_min, (int64_t)__shfl_xor((long long)lim_min, 32));
         const int lrow = t >> 2, ldim = (t & 3) * 32;
         TileShare<FP8> ts;
         auto fetch = [&](int64_t i0) {
@@ -257,19 +264,24 @@ __global__ __launch_bounds__(256, 2) void score_sample_kernel(FusedScoreArgs a)
             float sc[4][4];
             tile_scores(keys, qa, sc);
             apply_scales<FP8>(tile_scale, sc);
+            // every sample of the step visible to every row of the wave: no
+            // per-sample test (sample i's block is below 32 i + 32)
+            const bool all_vis = i0 + kFStep <= hi && (i0 + kFStep) * kSampleStride <= lim_min;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 if (my_seq[mt] != seq) continue;
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
                     const int64_t i = i0 + nt * 16 + m;
-                    float v = (i < hi && sample_block(i) < my_nc[mt]) ? sc[mt][nt] : -1.0f;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {  // insert into the descending top-4
-                        const float hi_v = fmaxf(top[mt][q], v);
-                        v = fminf(top[mt][q], v);
-                        top[mt][q] = hi_v;
-                    }
+                    const float v = (all_vis || (i < hi && sample_block(i) < my_nc[mt])) ? sc[mt][nt] : -1.0f;
+                    // insert into the descending top-4: the new q-th best of
+                    // {top[0..q], v} is the median of top[q-1], top[q] and v
+                    float *tp = top[mt];
+                    const float t0 = tp[0], t1 = tp[1], t2 = tp[2];
+                    tp[0] = fmaxf(t0, v);
+                    tp[1] = __builtin_amdgcn_fmed3f(t0, t1, v);
+                    tp[2] = __builtin_amdgcn_fmed3f(t1, t2, v);
+                    tp[3] = __builtin_amdgcn_fmed3f(t2, tp[3], v);
                 }
             }
             __syncthreads();
