@@ -569,13 +569,14 @@ __device__ __forceinline__ uint32_t radix_pass_pick(uint32_t *h, uint32_t &need,
     return cntd;
 }
 
-__device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n, int32_t nc, int32_t kk,
-                                             int32_t *__restrict__ out, float *__restrict__ osc)
+template <int P>  // pair slots per lane: n <= 64 P
+__device__ __forceinline__ void merge_staged_p(uint2 *st, uint32_t *h, uint32_t n, int32_t nc, int32_t kk,
+                                               int32_t *__restrict__ out, float *__restrict__ osc)
 {
     const int lane = threadIdx.x & 63;
-    uint32_t key[kRegPairs], nblk[kRegPairs];  // key and ~block; an empty slot is (0, 0)
+    uint32_t key[P], nblk[P];  // key and ~block; an empty slot is (0, 0)
 #pragma unroll
-    for (int i = 0; i < kRegPairs; ++i) {
+    for (int i = 0; i < P; ++i) {
         const uint32_t idx = (uint32_t)(i * kWave + lane);
         const uint2 e = idx < n ? st[idx] : make_uint2(0u, 0xffffffffu);
         key[i] = e.x;
@@ -592,7 +593,7 @@ __device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n,
         const uint32_t k0 = lane_value(key[0], 0);  // the first staged pair
         uint32_t x = 0;
 #pragma unroll
-        for (int i = 0; i < kRegPairs; ++i) x |= key[i] != 0u ? key[i] ^ k0 : 0u;
+        for (int i = 0; i < P; ++i) x |= key[i] != 0u ? key[i] ^ k0 : 0u;
         x = wave_or(x);
         sh = x ? 32 - __clz(x) : 0;  // pair keys share bit 31, so sh <= 31
         tp = k0 >> sh;
@@ -604,7 +605,7 @@ __device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n,
             for (int q = 0; q < 4; ++q) h[4 * lane + q] = 0u;
             wave_fence();
 #pragma unroll
-            for (int i = 0; i < kRegPairs; ++i) {
+            for (int i = 0; i < P; ++i) {
                 const bool m = (key[i] & himask) == hv;
                 atomicAdd(&h[m ? (key[i] >> nsh) & ((1u << width) - 1u) : 256u + (uint32_t)lane], 1u);
             }
@@ -626,7 +627,7 @@ __device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n,
             for (int q = 0; q < 4; ++q) h[4 * lane + q] = 0u;
             wave_fence();
 #pragma unroll
-            for (int i = 0; i < kRegPairs; ++i) {
+            for (int i = 0; i < P; ++i) {
                 const bool m = (key[i] == tp) & ((nblk[i] & himask) == hv);
                 atomicAdd(&h[m ? (nblk[i] >> nsh) & 0xffu : 256u + (uint32_t)lane], 1u);
             }
@@ -654,7 +655,7 @@ __device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n,
             ((uint4 *)(bm + bm_slot((uint32_t)lane * (kWinWords / kWave))))[j] = make_uint4(0u, 0u, 0u, 0u);
         wave_fence();
 #pragma unroll
-        for (int i = 0; i < kRegPairs; ++i) {  // a pair not kept ORs 0 into its lane's word
+        for (int i = 0; i < P; ++i) {  // a pair not kept ORs 0 into its lane's word
             const uint32_t b = ~nblk[i] - (uint32_t)w0;
             const bool k = ((((uint64_t)key[i] << 32) | nblk[i]) >= C) & (b < wbits);
             atomicOr(&bm[k ? bm_slot(b >> 5) : (uint32_t)lane], k ? 1u << (b & 31u) : 0u);
@@ -693,7 +694,7 @@ __device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n,
         }
         wave_fence();
 #pragma unroll
-        for (int i = 0; i < kRegPairs; ++i) {
+        for (int i = 0; i < P; ++i) {
             const uint32_t b = ~nblk[i] - (uint32_t)w0;
             const bool k = ((((uint64_t)key[i] << 32) | nblk[i]) >= C) & (b < wbits);
             const uint32_t wd = k ? b >> 5 : 0u;
@@ -707,6 +708,18 @@ __device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n,
         base += lane_value(incl, kWave - 1);
         if (w0 + 32 * kWinWords < nc) wave_fence();  // the next window reuses the bitmap
     }
+}
+
+// Rows whose pairs fit 24 slots per lane (most rows at a threshold of the
+// ~40th sampled score) run the passes over 24 slots instead of 32.
+constexpr int kRegPairsShort = 24;
+__device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n, int32_t nc, int32_t kk,
+                                             int32_t *__restrict__ out, float *__restrict__ osc)
+{
+    if (n <= (uint32_t)(kRegPairsShort * kWave))
+        merge_staged_p<kRegPairsShort>(st, h, n, nc, kk, out, osc);
+    else
+        merge_staged_p<kRegPairs>(st, h, n, nc, kk, out, osc);
 }
 
 // Every pair of a row's lists, read lane-parallel: lane i walks list i of
