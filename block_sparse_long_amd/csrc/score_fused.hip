@@ -710,14 +710,18 @@ __device__ __forceinline__ void merge_staged_p(uint2 *st, uint32_t *h, uint32_t 
     }
 }
 
-// Rows whose pairs fit 24 slots per lane (most rows at a threshold of the
-// ~40th sampled score) run the passes over 24 slots instead of 32.
-constexpr int kRegPairsShort = 24;
+// The passes run over as few register slots per lane as the row's pairs
+// need: 8, 16, 24 or 32 (at a threshold of the ~40th sampled score most rows
+// of a long context fit 24; rows with few visible blocks fit fewer).
 __device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n, int32_t nc, int32_t kk,
                                              int32_t *__restrict__ out, float *__restrict__ osc)
 {
-    if (n <= (uint32_t)(kRegPairsShort * kWave))
-        merge_staged_p<kRegPairsShort>(st, h, n, nc, kk, out, osc);
+    if (n <= 8u * kWave)
+        merge_staged_p<8>(st, h, n, nc, kk, out, osc);
+    else if (n <= 16u * kWave)
+        merge_staged_p<16>(st, h, n, nc, kk, out, osc);
+    else if (n <= 24u * kWave)
+        merge_staged_p<24>(st, h, n, nc, kk, out, osc);
     else
         merge_staged_p<kRegPairs>(st, h, n, nc, kk, out, osc);
 }
@@ -877,10 +881,9 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
                 if (take) st[nst + (uint32_t)__popcll(tb & lt)] = e;
                 nst += (uint32_t)__popcll(tb);
             });
-            wave_fence();
             if (lane == 0) a.mode[r] = kMergePrefilter;
-            merge_staged(st, h, nst, nc, kk, out, osc);
-            return;
+            mode = 0;  // ranked from the stage like a staged row
+            n = nst;
         }
     } else {
         n = (uint32_t)nc;
