@@ -60,7 +60,7 @@ struct Geo {
 constexpr int kSplitBlocks = 16;    // kept blocks of one decode split (64 positions)
 constexpr int kWin = 1 << 16;       // union bitmap window, in blocks
 constexpr int kWinWords = kWin / 32;
-constexpr int kMaxUnionBlocks = 4096;  // rows per tile x top_k is kept at or below this
+constexpr int kMaxUnionBlocks = 8192;  // rows per tile x top_k is kept at or below this
 constexpr int kMaxTileRows = 16;       // row masks are 16 bits, two per LDS word
 
 // Column of chunk position p in a V^T row.  The P V MFMA of 32-position step
@@ -81,10 +81,16 @@ struct alignas(16) ChunkSmem {
     uint32_t pmask[Geo<DIM>::kCh];
 };
 
-struct alignas(16) UnionSmem {
+// The union of a tile's kept blocks in one window of kWin blocks.  The bitmap
+// and its word prefix counts are needed only while the union is built, so
+// they share LDS with the chunk buffer; the union's block list (offsets from
+// the window's first block) and row masks stay for the window's chunks.
+struct alignas(16) UnionBuild {
     uint32_t bitmap[kWinWords];
-    uint16_t wprefix[kWinWords];         // < kMaxUnionBlocks
-    int32_t blk[kMaxUnionBlocks];
+    uint16_t wprefix[kWinWords];          // < kMaxUnionBlocks
+};
+struct alignas(16) UnionSmem {
+    uint16_t blk[kMaxUnionBlocks];        // union block i is block w0 + blk[i]
     uint32_t mask2[kMaxUnionBlocks / 2];  // union block i: bits 16(i%2) + r of word i/2, r = tile row keeping it
     uint32_t count;
 };
@@ -236,8 +242,8 @@ __device__ __forceinline__ int64_t kv_slot(const AttnArgs &a, int64_t s, int64_t
     return (int64_t)a.page_table[s * a.pt_stride + p / a.page_tokens] * a.page_tokens + p % a.page_tokens;
 }
 
-// The same share of a chunk of whole blocks: ublk[0..nb) are the chunk's
-// blocks (kChB at most, nb >= 1).  Thread t's K position is token (t/kTpp)%4
+// The same share of a chunk of whole blocks: w0 + ublk[0..nb) are the
+// chunk's blocks (kChB at most, nb >= 1).  Thread t's K position is token (t/kTpp)%4
 // of block t/(4 kTpp) and its V positions are tokens 0..3 of block t%kChB, so
 // one block id serves each; a thread past the chunk's blocks reads the last
 // one instead (its positions carry no mask bit, so their P is exactly 0).
@@ -245,11 +251,12 @@ __device__ __forceinline__ int64_t kv_slot(const AttnArgs &a, int64_t s, int64_t
 template <int DIM, typename KV>
 __device__ __forceinline__ void chunk_load_blocks(ChunkRegs<KV> &cr, const KV *__restrict__ kbase,
                                                   const KV *__restrict__ vbase, uint32_t row_stride,
-                                                  const int32_t *ublk, int nb, const AttnArgs &a, int64_t seq)
+                                                  const uint16_t *ublk, int32_t w0, int nb, const AttnArgs &a,
+                                                  int64_t seq)
 {
     using G = Geo<DIM>;
     const int t = threadIdx.x;
-    const int32_t bk = ublk[min(t / (4 * G::kTpp), nb - 1)], bv = ublk[min(t % G::kChB, nb - 1)];
+    const int32_t bk = w0 + ublk[min(t / (4 * G::kTpp), nb - 1)], bv = w0 + ublk[min(t % G::kChB, nb - 1)];
     // first slot of each block: its 4 tokens are consecutive slots
     const uint32_t sk = (uint32_t)kv_slot(a, seq, (int64_t)kBlock * bk), sv = (uint32_t)kv_slot(a, seq, (int64_t)kBlock * bv);
     load_k(cr, kbase + (uint64_t)sk * row_stride + ((t / G::kTpp) & 3) * row_stride + (t % G::kTpp) * 32);
@@ -307,24 +314,37 @@ __device__ __forceinline__ void gather_chunk(ChunkSmem<DIM> &cs, const KV *__res
     chunk_store<DIM>(cs, cr);
 }
 
-// One chunk for one wave: S^T, online softmax, O += P V.  `qbit` is the mask
-// bit of this lane's query row (0 when the query slot is unused); positions
-// past the chunk's end carry no mask bit.  `scale2` = softmax_scale * log2(e).
-template <int DIM>
-__device__ __forceinline__ void wave_chunk(const ChunkSmem<DIM> &cs, const bf16x8_t (&qb)[Geo<DIM>::kKs],
-                                           uint32_t qbit, float scale2, WaveState<DIM> &st)
+// One chunk for one wave and its QG groups of 16 queries: S^T, online
+// softmax, O += P V.  Every K and V^T operand read from LDS feeds the MFMAs
+// of all QG groups.  `qbit[q]` is the mask bit of this lane's query row in
+// group q (0 when the query slot is unused); positions past the chunk's end
+// carry no mask bit.  `scale2` = softmax_scale * log2(e).
+template <int DIM, int QG>
+__device__ __forceinline__ void wave_chunk(const ChunkSmem<DIM> &cs, const bf16x8_t (&qb)[QG][Geo<DIM>::kKs],
+                                           const uint32_t (&qbit)[QG], float scale2, WaveState<DIM> (&st)[QG])
 {
     using G = Geo<DIM>;
     const int lane = threadIdx.x & 63;
     const int m16 = lane & 15, g = lane >> 4;
-    float s[G::kSub][4];
+    float s[QG][G::kSub][4];
     bool any[G::kSub];
 #pragma unroll
     for (int sub = 0; sub < G::kSub; ++sub) {
         const uint4 pm = *(const uint4 *)&cs.pmask[sub * 16 + 4 * g];  // positions 4g .. 4g+3 of the sub-tile
-        const bool ok[4] = {(pm.x & qbit) != 0u, (pm.y & qbit) != 0u, (pm.z & qbit) != 0u, (pm.w & qbit) != 0u};
-        any[sub] = __ballot(ok[0] | ok[1] | ok[2] | ok[3]) != 0ull;
-        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        bool ok[QG][4];
+        bool some = false;
+#pragma unroll
+        for (int q = 0; q < QG; ++q) {
+            ok[q][0] = (pm.x & qbit[q]) != 0u;
+            ok[q][1] = (pm.y & qbit[q]) != 0u;
+            ok[q][2] = (pm.z & qbit[q]) != 0u;
+            ok[q][3] = (pm.w & qbit[q]) != 0u;
+            some |= ok[q][0] | ok[q][1] | ok[q][2] | ok[q][3];
+        }
+        any[sub] = __ballot(some) != 0ull;
+        f32x4_t acc[QG];
+#pragma unroll
+        for (int q = 0; q < QG; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         if (any[sub]) {  // the sub-tile's K operands are read 4 at a time, then their MFMAs issue
 #pragma unroll
             for (int k0 = 0; k0 < G::kKs; k0 += 4) {
@@ -335,53 +355,63 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem<DIM> &cs, const bf16x
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks]), qb[k0 + ks], acc, 0, 0, 0);
+#pragma unroll
+                    for (int q = 0; q < QG; ++q)
+                        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks]), qb[q][k0 + ks], acc[q], 0,
+                                                                         0, 0);
             }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s[sub][j] = ok[j] ? acc[j] * scale2 : -INFINITY;
+        for (int q = 0; q < QG; ++q)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[q][sub][j] = ok[q][j] ? acc[q][j] * scale2 : -INFINITY;
     }
-    // online softmax per query (lane l%16; the 4 lane groups hold its positions)
-    float cmax = -INFINITY;
+    // online softmax per query (lane l%16 of group q; the 4 lane groups hold its positions)
+    uint4 pa[QG][G::kSub / 2];
 #pragma unroll
-    for (int sub = 0; sub < G::kSub; ++sub)
+    for (int q = 0; q < QG; ++q) {
+        float cmax = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, s[sub][j]);
-    cmax = max_xor32(max_xor16(cmax));
-    const bool raise = cmax > st.m + kLazy;  // also the first logit of a query (st.m = kNoMax)
-    const float m_ref = raise ? cmax : st.m;
-    if (__ballot(raise && st.m != kNoMax)) {  // some query's O and l change scale
-        const float alpha = raise ? __builtin_amdgcn_exp2f(st.m - m_ref) : 1.0f;
-        st.l *= alpha;
-        float a4[4];
+        for (int sub = 0; sub < G::kSub; ++sub)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a4[j] = __shfl(alpha, 4 * g + j);
+            for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, s[q][sub][j]);
+        cmax = max_xor32(max_xor16(cmax));
+        const bool raise = cmax > st[q].m + kLazy;  // also the first logit of a query (st.m = kNoMax)
+        const float m_ref = raise ? cmax : st[q].m;
+        if (__ballot(raise && st[q].m != kNoMax)) {  // some query's O and l change scale
+            const float alpha = raise ? __builtin_amdgcn_exp2f(st[q].m - m_ref) : 1.0f;
+            st[q].l *= alpha;
+            float a4[4];
 #pragma unroll
-        for (int nt = 0; nt < G::kNt; ++nt)
+            for (int j = 0; j < 4; ++j) a4[j] = __shfl(alpha, 4 * g + j);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) st.o[nt][j] *= a4[j];
-    }
-    st.m = m_ref;
-    float p[G::kSub][4];
-    float psum = 0.0f;
+            for (int nt = 0; nt < G::kNt; ++nt)
 #pragma unroll
-    for (int sub = 0; sub < G::kSub; ++sub)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {  // a masked logit (-inf) gives 0; m_ref is finite
-            p[sub][j] = __builtin_amdgcn_exp2f(s[sub][j] - m_ref);
-            psum += p[sub][j];
+                for (int j = 0; j < 4; ++j) st[q].o[nt][j] *= a4[j];
         }
-    st.l += psum;  // per-lane partial; the 4 groups are summed at the end
+        st[q].m = m_ref;
+        float p[G::kSub][4];
+        float psum = 0.0f;
+#pragma unroll
+        for (int sub = 0; sub < G::kSub; ++sub)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {  // a masked logit (-inf) gives 0; m_ref is finite
+                p[sub][j] = __builtin_amdgcn_exp2f(s[q][sub][j] - m_ref);
+                psum += p[sub][j];
+            }
+        st[q].l += psum;  // per-lane partial; the 4 groups are summed at the end
+#pragma unroll
+        for (int i = 0; i < G::kSub / 2; ++i)
+            pa[q][i] = make_uint4(pack_bf16x2(p[2 * i][0], p[2 * i][1]), pack_bf16x2(p[2 * i][2], p[2 * i][3]),
+                                  pack_bf16x2(p[2 * i + 1][0], p[2 * i + 1][1]),
+                                  pack_bf16x2(p[2 * i + 1][2], p[2 * i + 1][3]));
+    }
     // O += P V over the chunk's 32-position steps
 #pragma unroll
     for (int i = 0; i < G::kSub / 2; ++i) {
         if (!(any[2 * i] || any[2 * i + 1])) continue;
-        const uint4 pa = make_uint4(pack_bf16x2(p[2 * i][0], p[2 * i][1]), pack_bf16x2(p[2 * i][2], p[2 * i][3]),
-                                    pack_bf16x2(p[2 * i + 1][0], p[2 * i + 1][1]),
-                                    pack_bf16x2(p[2 * i + 1][2], p[2 * i + 1][3]));
-        const bf16x8_t A = as_bf16x8(pa);
 #pragma unroll
-        for (int h = 0; h < G::kNt / 4; ++h) {  // V^T operands 4 at a time: one LDS wait per 4 MFMAs
+        for (int h = 0; h < G::kNt / 4; ++h) {  // V^T operands 4 at a time: one LDS wait per 4 x QG MFMAs
             bf16x8_t Bv[4];
 #pragma unroll
             for (int n = 0; n < 4; ++n)
@@ -389,7 +419,10 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem<DIM> &cs, const bf16x
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int n = 0; n < 4; ++n)
-                st.o[4 * h + n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv[n], st.o[4 * h + n], 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < QG; ++q)
+                    st[q].o[4 * h + n] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa[q][i]), Bv[n], st[q].o[4 * h + n], 0, 0, 0);
         }
     }
 }
@@ -425,14 +458,21 @@ __device__ __forceinline__ float total_l(const WaveState<DIM> &st)
 static_assert(kSplitBlocks * kBlock == kAttnChunk, "a decode split covers one chunk of attn_decode_splits()");
 
 // ---------------------------------------------------------------------------
-// Prefill: grid (row tiles, Hkv).  rows_per_tile * hg <= 64.
+// Prefill: grid (row tiles, Hkv).  rows_per_tile * hg <= 64 QG: each wave
+// holds QG groups of 16 queries.
 // ---------------------------------------------------------------------------
-template <int DIM, typename KV>
+template <int DIM, typename KV, int QG>
 __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, int32_t rows_per_tile)
 {
     constexpr bool kFp8 = sizeof(KV) == 1;
     using G = Geo<DIM>;
-    __shared__ ChunkSmem<DIM> cs;
+    static_assert(sizeof(UnionBuild) <= sizeof(ChunkSmem<DIM>), "the union build fits the chunk buffer");
+    __shared__ union {
+        ChunkSmem<DIM> cs;
+        UnionBuild ub;
+    } sm;
+    ChunkSmem<DIM> &cs = sm.cs;
+    UnionBuild &ub = sm.ub;
     __shared__ UnionSmem us;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int m16 = lane & 15, g = lane >> 4;
@@ -440,20 +480,25 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
     const int kvh = blockIdx.y;
     const int64_t row0 = (int64_t)blockIdx.x * rows_per_tile;
     const int nrows = (int)min((int64_t)rows_per_tile, (int64_t)a.n_sel - row0);
-    // this lane's query (as an S^T column): tile query qi = 16*wave + m16
-    const int qi = 16 * wave + m16;
-    const int r_local = qi / hg;
-    const bool q_valid = r_local < nrows;
-    const int head = kvh * hg + qi % hg;
-    bf16x8_t qb[G::kKs];
-    load_query<DIM>((const bf16_t *)a.q + ((row0 + (q_valid ? r_local : 0)) * a.Hq + head) * DIM, q_valid, qb);
-    WaveState<DIM> st;
-    init_state(st);
+    // this lane's query in group q (an S^T column): tile query 16 (QG wave + q) + m16
+    int r_local[QG], head[QG];
+    bool q_valid[QG];
+    bf16x8_t qb[QG][G::kKs];
+    WaveState<DIM> st[QG];
+#pragma unroll
+    for (int q = 0; q < QG; ++q) {
+        const int qi = 16 * (QG * wave + q) + m16;
+        r_local[q] = qi / hg;
+        q_valid[q] = r_local[q] < nrows;
+        head[q] = kvh * hg + qi % hg;
+        load_query<DIM>((const bf16_t *)a.q + ((row0 + (q_valid[q] ? r_local[q] : 0)) * a.Hq + head[q]) * DIM,
+                        q_valid[q], qb[q]);
+        init_state(st[q]);
+    }
     const float scale2 = kFp8 ? a.scale * a.k_scale * kLog2e : a.scale * kLog2e;
     const int64_t row_stride = (int64_t)a.Hkv * DIM;
     // ---- the tile's rows, read once: position, sequence, kept count, last
-    // kept block; and all their kept blocks (at most kMaxUnionBlocks, 16 per
-    // thread), loaded together and kept in registers for the union passes ----
+    // kept block ----
     __shared__ int32_t s_pos[kMaxTileRows], s_seq[kMaxTileRows], s_cnt[kMaxTileRows], s_last[kMaxTileRows];
     if (t < nrows) {
         const int64_t r = row0 + t;
@@ -464,20 +509,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
         s_last[t] = c > 0 ? a.sel_blocks[r * a.top_k + c - 1] : -1;
     }
     __syncthreads();
-    constexpr int kSelPerThread = kMaxUnionBlocks / 256;
-    int32_t eblk[kSelPerThread];           // kept block, or -1
-    uint32_t erow4[kSelPerThread / 8];     // its tile row, 4 bits per entry
-#pragma unroll
-    for (int j = 0; j < kSelPerThread / 8; ++j) erow4[j] = 0u;
-#pragma unroll
-    for (int j = 0; j < kSelPerThread; ++j) {
-        const int32_t idx = t + 256 * j;
-        const int32_t r = idx / a.top_k, i = idx - r * a.top_k;
-        const bool ok = r < nrows && i < s_cnt[min(r, nrows - 1)];
-        erow4[j / 8] |= (uint32_t)(ok ? r : 0) << (4 * (j % 8));
-        eblk[j] = ok ? a.sel_blocks[(row0 + r) * a.top_k + i] : -1;
-    }
-    auto erow = [&](int j) { return (int)((erow4[j / 8] >> (4 * (j % 8))) & 15u); };
+    constexpr int kBatch = 8;  // selection entries a thread reads together
     uint32_t todo = nrows >= 32 ? 0xffffffffu : ((1u << nrows) - 1u);
     while (todo) {  // rows of one sequence at a time (uniform across the workgroup)
         const int first = __builtin_ctz(todo);
@@ -486,7 +518,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
         for (int r = first; r < nrows; ++r)
             if (((todo >> r) & 1u) && s_seq[r] == seq) active |= 1u << r;
         todo &= ~active;
-        const uint32_t qbit = q_valid ? (active & (1u << r_local)) : 0u;
+        uint32_t qbit[QG];
+#pragma unroll
+        for (int q = 0; q < QG; ++q) qbit[q] = q_valid[q] ? (active & (1u << r_local[q])) : 0u;
         const int64_t seq_off = a.page_table ? 0 : (int64_t)seq * a.kv_seq_stride;
         const KV *kbase = (const KV *)a.k_cache + seq_off + (int64_t)kvh * DIM;
         const KV *vbase = (const KV *)a.v_cache + seq_off + (int64_t)kvh * DIM;
@@ -495,21 +529,35 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
         for (int r = 0; r < nrows; ++r)
             if ((active >> r) & 1u) hi_blk = max(hi_blk, s_last[r] + 1);
         for (int32_t w0 = 0; w0 < hi_blk; w0 += kWin) {
-            // ---- union of the active rows' kept blocks in [w0, w0 + kWin) ----
-            for (int i = t; i < kWinWords; i += blockDim.x) us.bitmap[i] = 0u;
-            __syncthreads();
+            // ---- union of the active rows' kept blocks in [w0, w0 + kWin).
+            // The tile's selections (row-major, top_k per row) are read in
+            // batches of kBatch entries per thread, twice: to set the bitmap,
+            // then to set each union block's row bits ----
+            const int32_t nent = nrows * a.top_k;
+            auto entries = [&](auto &&fn) {
+                for (int32_t base = 0; base < nent; base += 256 * kBatch) {
+                    int32_t eb[kBatch], er[kBatch];
 #pragma unroll
-            for (int j = 0; j < kSelPerThread; ++j) {
-                const int32_t b = eblk[j] - w0;
-                if (eblk[j] >= 0 && ((active >> erow(j)) & 1u) && b >= 0 && b < kWin)
-                    atomicOr(&us.bitmap[b >> 5], 1u << (b & 31));
-            }
+                    for (int u = 0; u < kBatch; ++u) {
+                        const int32_t idx = min(base + t + 256 * u, nent - 1);
+                        const int32_t r = idx / a.top_k, i = idx - r * a.top_k;
+                        er[u] = base + t + 256 * u < nent && ((active >> r) & 1u) && i < s_cnt[r] ? r : -1;
+                        eb[u] = a.sel_blocks[(row0 + r) * a.top_k + i] - w0;
+                    }
+#pragma unroll
+                    for (int u = 0; u < kBatch; ++u)
+                        if (er[u] >= 0 && eb[u] >= 0 && eb[u] < kWin) fn(eb[u], er[u]);
+                }
+            };
+            for (int i = t; i < kWinWords; i += blockDim.x) ub.bitmap[i] = 0u;
+            __syncthreads();
+            entries([&](int32_t b, int32_t) { atomicOr(&ub.bitmap[b >> 5], 1u << (b & 31)); });
             __syncthreads();
             {   // exclusive prefix of popcounts over the words (8 words per thread)
                 constexpr int per = kWinWords / 256;
                 uint32_t cnt = 0;
 #pragma unroll
-                for (int i = 0; i < per; ++i) cnt += __popc(us.bitmap[t * per + i]);
+                for (int i = 0; i < per; ++i) cnt += __popc(ub.bitmap[t * per + i]);
                 const uint32_t x = wave_incl_scan(cnt);
                 __shared__ uint32_t wsum[4];
                 if (lane == 63) wsum[wave] = x;
@@ -520,13 +568,13 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
                 uint32_t run = before + x - cnt;
 #pragma unroll
                 for (int i = 0; i < per; ++i) {
-                    const uint32_t word = us.bitmap[t * per + i];
-                    us.wprefix[t * per + i] = (uint16_t)run;
+                    const uint32_t word = ub.bitmap[t * per + i];
+                    ub.wprefix[t * per + i] = (uint16_t)run;
                     uint32_t bits = word, k = run;
                     while (bits) {
                         const int b = __builtin_ctz(bits);
                         bits &= bits - 1u;
-                        us.blk[k] = w0 + (t * per + i) * 32 + b;
+                        us.blk[k] = (uint16_t)((t * per + i) * 32 + b);
                         if (!(k & 1u)) us.mask2[k >> 1] = 0u;  // word k/2 has one even index, owned here
                         ++k;
                     }
@@ -534,15 +582,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
                 }
             }
             __syncthreads();
-#pragma unroll
-            for (int j = 0; j < kSelPerThread; ++j) {
-                const int32_t b = eblk[j] - w0;
-                if (eblk[j] >= 0 && ((active >> erow(j)) & 1u) && b >= 0 && b < kWin) {
-                    const uint32_t word = us.bitmap[b >> 5];
-                    const uint32_t idx = us.wprefix[b >> 5] + __popc(word & ((1u << (b & 31)) - 1u));
-                    atomicOr(&us.mask2[idx >> 1], 1u << (erow(j) + 16 * (idx & 1u)));
-                }
-            }
+            entries([&](int32_t b, int32_t r) {
+                const uint32_t word = ub.bitmap[b >> 5];
+                const uint32_t idx = ub.wprefix[b >> 5] + __popc(word & ((1u << (b & 31)) - 1u));
+                atomicOr(&us.mask2[idx >> 1], 1u << (r + 16 * (idx & 1u)));
+            });
             __syncthreads();
             const int32_t nu = (int32_t)us.count;
             // ---- the union's blocks, kChB per chunk; chunk c+1's gather is in
@@ -551,7 +595,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
             const int32_t nch = (nu + kChB - 1) / kChB;
             ChunkRegs<KV> cr;
             if (nch > 0)
-                chunk_load_blocks<DIM>(cr, kbase, vbase, (uint32_t)row_stride, us.blk, min(kChB, nu), a, seq);
+                chunk_load_blocks<DIM>(cr, kbase, vbase, (uint32_t)row_stride, us.blk, w0, min(kChB, nu), a, seq);
             for (int32_t c = 0; c < nch; ++c) {
                 const int32_t c0 = c * kChB;
                 const int nb = min(kChB, nu - c0);
@@ -560,10 +604,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
                 __syncthreads();
                 if (c + 1 < nch) {
                     const int32_t c1 = c0 + kChB;
-                    chunk_load_blocks<DIM>(cr, kbase, vbase, (uint32_t)row_stride, us.blk + c1, min(kChB, nu - c1),
-                                           a, seq);
+                    chunk_load_blocks<DIM>(cr, kbase, vbase, (uint32_t)row_stride, us.blk + c1, w0,
+                                           min(kChB, nu - c1), a, seq);
                 }
-                wave_chunk<DIM>(cs, qb, qbit, scale2, st);
+                wave_chunk<DIM, QG>(cs, qb, qbit, scale2, st);
                 __syncthreads();
             }
         }
@@ -599,26 +643,29 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
             // positions beyond the tails carry no mask bit, so they stay out
             gather_chunk<DIM>(cs, kbase, vbase, row_stride, min(G::kCh, ntail - tc));
             __syncthreads();
-            wave_chunk<DIM>(cs, qb, qbit, scale2, st);
+            wave_chunk<DIM, QG>(cs, qb, qbit, scale2, st);
             __syncthreads();
         }
     }
     // ---- output ----
-    const float ltot = total_l(st);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int qo = 16 * wave + 4 * g + j;   // query of o[.][j]
-        const int ro = qo / hg;
-        const float lq = __shfl(ltot, 4 * g + j);
-        if (ro >= nrows) continue;
-        const int ho = kvh * hg + qo % hg;
-        bf16_t *orow = (bf16_t *)a.out + ((row0 + ro) * a.Hq + ho) * DIM;
-        const float inv = lq > 0.0f ? (kFp8 ? a.v_scale : 1.0f) / lq : 0.0f;
+    for (int q = 0; q < QG; ++q) {
+        const float ltot = total_l(st[q]);
 #pragma unroll
-        for (int nt = 0; nt < G::kNt; ++nt) orow[16 * nt + m16] = f32_to_bf16(st.o[nt][j] * inv);
+        for (int j = 0; j < 4; ++j) {
+            const int qo = 16 * (QG * wave + q) + 4 * g + j;  // query of o[.][j]
+            const int ro = qo / hg;
+            const float lq = __shfl(ltot, 4 * g + j);
+            if (ro >= nrows) continue;
+            const int ho = kvh * hg + qo % hg;
+            bf16_t *orow = (bf16_t *)a.out + ((row0 + ro) * a.Hq + ho) * DIM;
+            const float inv = lq > 0.0f ? (kFp8 ? a.v_scale : 1.0f) / lq : 0.0f;
+#pragma unroll
+            for (int nt = 0; nt < G::kNt; ++nt) orow[16 * nt + m16] = f32_to_bf16(st[q].o[nt][j] * inv);
+        }
+        if (a.lse && g == 0 && q_valid[q])
+            a.lse[(row0 + r_local[q]) * a.Hq + head[q]] = ltot > 0.0f ? (st[q].m + __log2f(ltot)) * kLn2 : -INFINITY;
     }
-    if (a.lse && g == 0 && q_valid)
-        a.lse[(row0 + r_local) * a.Hq + head] = ltot > 0.0f ? (st.m + __log2f(ltot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -644,12 +691,12 @@ __global__ __launch_bounds__(256, DIM == 256 ? 2 : 1) void attn_decode_mfma_kern
     const bool q_valid = qi < nq;
     const int head = kvh * hg + qi % hg;
     const int64_t qrow = (s * a.q_per_sel + (q_valid ? jrow : 0)) * a.Hq + head;
-    bf16x8_t qb[G::kKs];
-    load_query<DIM>((const bf16_t *)a.q + qrow * DIM, q_valid, qb);
-    WaveState<DIM> st;
-    init_state(st);
+    bf16x8_t qb[1][G::kKs];
+    load_query<DIM>((const bf16_t *)a.q + qrow * DIM, q_valid, qb[0]);
+    WaveState<DIM> st[1];
+    init_state(st[0]);
     const float scale2 = kFp8 ? a.scale * a.k_scale * kLog2e : a.scale * kLog2e;
-    const uint32_t qbit = q_valid ? (1u << jrow) : 0u;
+    const uint32_t qbit[1] = {q_valid ? (1u << jrow) : 0u};
     const int64_t row_stride = (int64_t)a.Hkv * DIM;
     const int64_t seq_off = a.page_table ? 0 : s * a.kv_seq_stride;
     const KV *kbase = (const KV *)a.k_cache + seq_off + (int64_t)kvh * DIM;
@@ -671,7 +718,7 @@ __global__ __launch_bounds__(256, DIM == 256 ? 2 : 1) void attn_decode_mfma_kern
             __syncthreads();
             gather_chunk<DIM>(cs, kbase, vbase, row_stride, cb * kBlock);
             __syncthreads();
-            wave_chunk<DIM>(cs, qb, qbit, scale2, st);
+            wave_chunk<DIM, 1>(cs, qb, qbit, scale2, st);
             __syncthreads();
         }
     } else {
@@ -701,12 +748,12 @@ __global__ __launch_bounds__(256, DIM == 256 ? 2 : 1) void attn_decode_mfma_kern
             __syncthreads();
             gather_chunk<DIM>(cs, kbase, vbase, row_stride, n);
             __syncthreads();
-            wave_chunk<DIM>(cs, qb, qbit, scale2, st);
+            wave_chunk<DIM, 1>(cs, qb, qbit, scale2, st);
             __syncthreads();
         }
     }
     // ---- partial softmax state of this split ----
-    const float ltot = total_l(st);
+    const float ltot = total_l(st[0]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int qo = 16 * wave + 4 * g + j;
@@ -715,21 +762,29 @@ __global__ __launch_bounds__(256, DIM == 256 ? 2 : 1) void attn_decode_mfma_kern
         float *pp = a.partial + (((s * a.q_per_sel + jo) * a.Hq + ho) * a.nsplit + split) * (DIM + 2);
         const float vs = kFp8 ? a.v_scale : 1.0f;  // the partial outputs carry the V scale
 #pragma unroll
-        for (int nt = 0; nt < G::kNt; ++nt) pp[16 * nt + m16] = st.o[nt][j] * vs;
+        for (int nt = 0; nt < G::kNt; ++nt) pp[16 * nt + m16] = st[0].o[nt][j] * vs;
     }
     if (q_valid && g == 0) {
         float *pp = a.partial + (qrow * a.nsplit + split) * (DIM + 2);
-        pp[DIM] = st.m * kLn2;  // natural-log units for the combine
+        pp[DIM] = st[0].m * kLn2;  // natural-log units for the combine
         pp[DIM + 1] = ltot;
     }
 }
 
-int32_t attn_prefill_rows_per_tile(int32_t hg, int32_t top_k)
+// Rows of a prefill tile whose waves hold qg groups of 16 queries each.
+static int32_t prefill_rows(int32_t hg, int32_t top_k, int32_t qg)
 {
-    int32_t r = max(1, 64 / hg);
+    int32_t r = max(1, 64 * qg / hg);
     r = min(r, kMaxTileRows);                  // row masks are 16 bits
     r = min(r, kMaxUnionBlocks / top_k);       // the union of the rows' selections fits LDS
     return max(r, 1);
+}
+
+// Two query groups per wave at head dim 128 when the tile then holds more
+// than 64 queries (so no wave's second group is always empty).
+static int32_t prefill_groups(int32_t hg, int32_t top_k, int32_t D)
+{
+    return D == 128 && (int64_t)prefill_rows(hg, top_k, 2) * hg > 64 ? 2 : 1;
 }
 
 bool attn_mfma_supported(int32_t Hq, int32_t Hkv, int32_t q_per_sel, int32_t D, bool bf16)
@@ -744,19 +799,25 @@ bool attn_mfma_supported(int32_t Hq, int32_t Hkv, int32_t q_per_sel, int32_t D, 
 void launch_attn_prefill_mfma(const AttnArgs &a, hipStream_t stream)
 {
     const int32_t hg = a.Hq / a.Hkv;
-    const int32_t rpt = attn_prefill_rows_per_tile(hg, a.top_k);
+    const int32_t qg = prefill_groups(hg, a.top_k, a.D);
+    const int32_t rpt = prefill_rows(hg, a.top_k, qg);
     const dim3 grid((unsigned)((a.n_sel + rpt - 1) / rpt), (unsigned)a.Hkv), block(256);
     if (a.D == 256 && a.kv_fp8)
-        QSA_LAUNCH("attn_prefill_mfma_d256_fp8kv", (attn_prefill_mfma_kernel<256, uint8_t>), grid, block, 0, stream,
-                   a, rpt);
+        QSA_LAUNCH("attn_prefill_mfma_d256_fp8kv", (attn_prefill_mfma_kernel<256, uint8_t, 1>), grid, block, 0,
+                   stream, a, rpt);
     else if (a.D == 256)
-        QSA_LAUNCH("attn_prefill_mfma_d256", (attn_prefill_mfma_kernel<256, bf16_t>), grid, block, 0, stream, a,
+        QSA_LAUNCH("attn_prefill_mfma_d256", (attn_prefill_mfma_kernel<256, bf16_t, 1>), grid, block, 0, stream, a,
                    rpt);
+    else if (a.kv_fp8 && qg == 2)
+        QSA_LAUNCH("attn_prefill_mfma_fp8kv", (attn_prefill_mfma_kernel<128, uint8_t, 2>), grid, block, 0, stream,
+                   a, rpt);
     else if (a.kv_fp8)
-        QSA_LAUNCH("attn_prefill_mfma_fp8kv", (attn_prefill_mfma_kernel<128, uint8_t>), grid, block, 0, stream, a,
-                   rpt);
+        QSA_LAUNCH("attn_prefill_mfma_fp8kv", (attn_prefill_mfma_kernel<128, uint8_t, 1>), grid, block, 0, stream,
+                   a, rpt);
+    else if (qg == 2)
+        QSA_LAUNCH("attn_prefill_mfma", (attn_prefill_mfma_kernel<128, bf16_t, 2>), grid, block, 0, stream, a, rpt);
     else
-        QSA_LAUNCH("attn_prefill_mfma", (attn_prefill_mfma_kernel<128, bf16_t>), grid, block, 0, stream, a, rpt);
+        QSA_LAUNCH("attn_prefill_mfma", (attn_prefill_mfma_kernel<128, bf16_t, 1>), grid, block, 0, stream, a, rpt);
 }
 
 void launch_attn_decode_mfma(const AttnArgs &a, hipStream_t stream)

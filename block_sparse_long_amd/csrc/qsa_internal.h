@@ -172,7 +172,6 @@ void launch_attn_combine(const AttnArgs &a, bool bf16, hipStream_t stream);
 
 // ---- attn_mfma.hip (bf16 q, bf16 or FP8 K/V, D 128 or 256, Hq/Hkv up to 64) ---
 bool attn_mfma_supported(int32_t Hq, int32_t Hkv, int32_t q_per_sel, int32_t D, bool bf16);
-int32_t attn_prefill_rows_per_tile(int32_t hg, int32_t top_k);
 void launch_attn_prefill_mfma(const AttnArgs &a, hipStream_t stream);
 void launch_attn_decode_mfma(const AttnArgs &a, hipStream_t stream);
 

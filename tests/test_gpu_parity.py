@@ -290,6 +290,40 @@ def test_attn_prefill_overlapping_and_mixed_sequences(gpu):
     np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
 
 
+def test_attn_prefill_union_across_windows(gpu):
+    # the prefill kernel builds a tile's union of kept blocks one window of
+    # 65,536 blocks at a time: kept blocks on both sides of each window edge,
+    # a ragged third window, rows keeping fewer blocks, and tiles of 16 rows
+    # (8 query heads per KV head) with a ragged last tile
+    rng = np.random.default_rng(35)
+    W = 65536
+    NB = 2 * W + 5001
+    L, R, k, Hq, Hkv = 4 * NB + 2, 40, 128, 8, 1
+    pos = np.sort(rng.integers(4 * (W + 16), L, R)).astype(np.int32)
+    pos[-1] = L - 1
+    edges = np.array([0, 1, W - 2, W - 1, W, W + 1, 2 * W - 1, 2 * W, 2 * W + 1, NB - 1], np.int64)
+    sel = np.full((R, k), -1, np.int32)
+    cnt = np.zeros(R, np.int32)
+    for r, t in enumerate(pos):
+        nc = (int(t) + 1) // 4
+        base = edges[edges < nc]
+        n = k if r % 7 else k // 3
+        extra = rng.choice(nc, size=3 * k, replace=False)
+        extra = extra[~np.isin(extra, base)][: n - len(base)]
+        sel[r, :n] = np.sort(np.concatenate([base, extra]))
+        cnt[r] = n
+    print(f"[windows] attention prefill L={L} rows={R} k={k}", flush=True)
+    q = synth.bf16_bits(rng.standard_normal((R, Hq, DIM)).astype(np.float32))
+    kc = synth.bf16_bits(rng.standard_normal((1, L, Hkv, DIM)).astype(np.float32))
+    vc = synth.bf16_bits(rng.standard_normal((1, L, Hkv, DIM)).astype(np.float32))
+    seq = np.zeros(R, np.int32)
+    want, want_lse = oracle.sparse_attn_prefill(q, seq, pos, kc, vc, sel, cnt)
+    out, lse = qsa.sparse_attn_prefill(dev(q, "bf16"), dev(seq, "i"), dev(pos, "i"), dev(kc, "bf16"),
+                                       dev(vc, "bf16"), dev(sel, "i"), dev(cnt, "i"))
+    assert_close_out(host(out), want, "bf16")
+    np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("Qn,Hq,Hkv,draft", [(1, 8, 1, False), (4, 8, 1, True), (2, 16, 2, True),
                                              (3, 4, 2, False), (2, 6, 2, True), (8, 8, 1, True)])
