@@ -314,33 +314,38 @@ __device__ __forceinline__ void gather_chunk(ChunkSmem<DIM> &cs, const KV *__res
     chunk_store<DIM>(cs, cr);
 }
 
+// A raw logit where the query attends the position (bit r of its mask word
+// set), -inf where it does not: one bit-field extract and one bit-field insert.
+__device__ __forceinline__ float masked_logit(float x, uint32_t pmask_word, uint32_t r)
+{
+    const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int32_t)pmask_word, r, 1u);  // all ones or zero
+    return __uint_as_float((__float_as_uint(x) & m) | (0xff800000u & ~m));
+}
+
 // One chunk for one wave and its QG groups of 16 queries: S^T, online
 // softmax, O += P V.  Every K and V^T operand read from LDS feeds the MFMAs
-// of all QG groups.  `qbit[q]` is the mask bit of this lane's query row in
-// group q (0 when the query slot is unused); positions past the chunk's end
-// carry no mask bit.  `scale2` = softmax_scale * log2(e).
+// of all QG groups.  `rbit[q]` is the mask bit of this lane's query row in
+// group q (31, a bit no position carries, when the query slot is unused);
+// positions past the chunk's end carry no mask bit.  `scale2` =
+// |softmax_scale| * log2(e) > 0: a negative scale is carried by the sign of
+// the queries, so the logits' reference max can be taken on raw <q, k> and
+// the scale folded into the exponent's FMA.
 template <int DIM, int QG>
 __device__ __forceinline__ void wave_chunk(const ChunkSmem<DIM> &cs, const bf16x8_t (&qb)[QG][Geo<DIM>::kKs],
-                                           const uint32_t (&qbit)[QG], float scale2, WaveState<DIM> (&st)[QG])
+                                           const uint32_t (&rbit)[QG], float scale2, WaveState<DIM> (&st)[QG])
 {
     using G = Geo<DIM>;
     const int lane = threadIdx.x & 63;
     const int m16 = lane & 15, g = lane >> 4;
-    float s[QG][G::kSub][4];
+    float x[QG][G::kSub][4];  // raw logits, -inf where the query does not attend
     bool any[G::kSub];
 #pragma unroll
     for (int sub = 0; sub < G::kSub; ++sub) {
         const uint4 pm = *(const uint4 *)&cs.pmask[sub * 16 + 4 * g];  // positions 4g .. 4g+3 of the sub-tile
-        bool ok[QG][4];
+        const uint32_t pall = pm.x | pm.y | pm.z | pm.w;
         bool some = false;
 #pragma unroll
-        for (int q = 0; q < QG; ++q) {
-            ok[q][0] = (pm.x & qbit[q]) != 0u;
-            ok[q][1] = (pm.y & qbit[q]) != 0u;
-            ok[q][2] = (pm.z & qbit[q]) != 0u;
-            ok[q][3] = (pm.w & qbit[q]) != 0u;
-            some |= ok[q][0] | ok[q][1] | ok[q][2] | ok[q][3];
-        }
+        for (int q = 0; q < QG; ++q) some |= ((pall >> rbit[q]) & 1u) != 0u;
         any[sub] = __ballot(some) != 0ull;
         f32x4_t acc[QG];
 #pragma unroll
@@ -362,20 +367,23 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem<DIM> &cs, const bf16x
             }
         }
 #pragma unroll
-        for (int q = 0; q < QG; ++q)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s[q][sub][j] = ok[q][j] ? acc[q][j] * scale2 : -INFINITY;
+        for (int q = 0; q < QG; ++q) {
+            x[q][sub][0] = masked_logit(acc[q][0], pm.x, rbit[q]);
+            x[q][sub][1] = masked_logit(acc[q][1], pm.y, rbit[q]);
+            x[q][sub][2] = masked_logit(acc[q][2], pm.z, rbit[q]);
+            x[q][sub][3] = masked_logit(acc[q][3], pm.w, rbit[q]);
+        }
     }
     // online softmax per query (lane l%16 of group q; the 4 lane groups hold its positions)
     uint4 pa[QG][G::kSub / 2];
 #pragma unroll
     for (int q = 0; q < QG; ++q) {
-        float cmax = -INFINITY;
+        float xmax = -INFINITY;
 #pragma unroll
         for (int sub = 0; sub < G::kSub; ++sub)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, s[q][sub][j]);
-        cmax = max_xor32(max_xor16(cmax));
+            for (int j = 0; j < 4; ++j) xmax = fmaxf(xmax, x[q][sub][j]);
+        const float cmax = max_xor32(max_xor16(xmax)) * scale2;  // scale2 > 0: the max of the scaled logits
         const bool raise = cmax > st[q].m + kLazy;  // also the first logit of a query (st.m = kNoMax)
         const float m_ref = raise ? cmax : st[q].m;
         if (__ballot(raise && st[q].m != kNoMax)) {  // some query's O and l change scale
@@ -396,7 +404,7 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem<DIM> &cs, const bf16x
         for (int sub = 0; sub < G::kSub; ++sub)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {  // a masked logit (-inf) gives 0; m_ref is finite
-                p[sub][j] = __builtin_amdgcn_exp2f(s[q][sub][j] - m_ref);
+                p[sub][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[q][sub][j], scale2, -m_ref));
                 psum += p[sub][j];
             }
         st[q].l += psum;  // per-lane partial; the 4 groups are summed at the end
@@ -427,14 +435,33 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem<DIM> &cs, const bf16x
     }
 }
 
+// A lane's query operands, negated when `neg` (exact in bf16).
 template <int DIM>
-__device__ __forceinline__ void load_query(const bf16_t *__restrict__ qrow, bool valid,
+__device__ __forceinline__ void load_query(const bf16_t *__restrict__ qrow, bool valid, bool neg,
                                            bf16x8_t (&qb)[Geo<DIM>::kKs])
 {
     const int g = (threadIdx.x & 63) >> 4;
+    const uint32_t flip = neg ? 0x80008000u : 0u;
 #pragma unroll
-    for (int ks = 0; ks < Geo<DIM>::kKs; ++ks)
-        qb[ks] = valid ? as_bf16x8(*(const uint4 *)(qrow + (DIM / 4) * g + 8 * ks)) : zero_bf16x8();
+    for (int ks = 0; ks < Geo<DIM>::kKs; ++ks) {
+        uint4 w = valid ? *(const uint4 *)(qrow + (DIM / 4) * g + 8 * ks) : make_uint4(0, 0, 0, 0);
+        w.x ^= flip;
+        w.y ^= flip;
+        w.z ^= flip;
+        w.w ^= flip;
+        qb[ks] = as_bf16x8(w);
+    }
+}
+
+// The exponent scale of the logits, |softmax_scale| * log2(e) (times the
+// K scale for FP8 keys), kept positive: a negative scale is carried by the
+// sign of the queries, and a zero one becomes the smallest normal float
+// (every logit then rounds to 0 in the exponent, as with a zero scale).
+__device__ __forceinline__ float logit_scale2(const AttnArgs &a, bool fp8, bool &neg)
+{
+    const float s2 = (fp8 ? a.scale * a.k_scale : a.scale) * kLog2e;
+    neg = s2 < 0.0f;
+    return fmaxf(fabsf(s2), __FLT_MIN__);
 }
 
 template <int DIM>
@@ -481,21 +508,21 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
     const int64_t row0 = (int64_t)blockIdx.x * rows_per_tile;
     const int nrows = (int)min((int64_t)rows_per_tile, (int64_t)a.n_sel - row0);
     // this lane's query in group q (an S^T column): tile query 16 (QG wave + q) + m16
-    int r_local[QG], head[QG];
-    bool q_valid[QG];
+    bool qneg;
+    const float scale2 = logit_scale2(a, kFp8, qneg);
+    uint32_t rbit[QG];
     bf16x8_t qb[QG][G::kKs];
     WaveState<DIM> st[QG];
 #pragma unroll
     for (int q = 0; q < QG; ++q) {
         const int qi = 16 * (QG * wave + q) + m16;
-        r_local[q] = qi / hg;
-        q_valid[q] = r_local[q] < nrows;
-        head[q] = kvh * hg + qi % hg;
-        load_query<DIM>((const bf16_t *)a.q + ((row0 + (q_valid[q] ? r_local[q] : 0)) * a.Hq + head[q]) * DIM,
-                        q_valid[q], qb[q]);
+        const int r_local = qi / hg, head = kvh * hg + qi % hg;
+        const bool q_valid = r_local < nrows;
+        rbit[q] = q_valid ? (uint32_t)r_local : 31u;  // rows of other sequences carry no bit either
+        load_query<DIM>((const bf16_t *)a.q + ((row0 + (q_valid ? r_local : 0)) * a.Hq + head) * DIM, q_valid,
+                        qneg, qb[q]);
         init_state(st[q]);
     }
-    const float scale2 = kFp8 ? a.scale * a.k_scale * kLog2e : a.scale * kLog2e;
     const int64_t row_stride = (int64_t)a.Hkv * DIM;
     // ---- the tile's rows, read once: position, sequence, kept count, last
     // kept block ----
@@ -518,9 +545,6 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
         for (int r = first; r < nrows; ++r)
             if (((todo >> r) & 1u) && s_seq[r] == seq) active |= 1u << r;
         todo &= ~active;
-        uint32_t qbit[QG];
-#pragma unroll
-        for (int q = 0; q < QG; ++q) qbit[q] = q_valid[q] ? (active & (1u << r_local[q])) : 0u;
         const int64_t seq_off = a.page_table ? 0 : (int64_t)seq * a.kv_seq_stride;
         const KV *kbase = (const KV *)a.k_cache + seq_off + (int64_t)kvh * DIM;
         const KV *vbase = (const KV *)a.v_cache + seq_off + (int64_t)kvh * DIM;
@@ -607,7 +631,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
                     chunk_load_blocks<DIM>(cr, kbase, vbase, (uint32_t)row_stride, us.blk + c1, w0,
                                            min(kChB, nu - c1), a, seq);
                 }
-                wave_chunk<DIM, QG>(cs, qb, qbit, scale2, st);
+                wave_chunk<DIM, QG>(cs, qb, rbit, scale2, st);
                 __syncthreads();
             }
         }
@@ -643,7 +667,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
             // positions beyond the tails carry no mask bit, so they stay out
             gather_chunk<DIM>(cs, kbase, vbase, row_stride, min(G::kCh, ntail - tc));
             __syncthreads();
-            wave_chunk<DIM, QG>(cs, qb, qbit, scale2, st);
+            wave_chunk<DIM, QG>(cs, qb, rbit, scale2, st);
             __syncthreads();
         }
     }
@@ -663,8 +687,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
 #pragma unroll
             for (int nt = 0; nt < G::kNt; ++nt) orow[16 * nt + m16] = f32_to_bf16(st[q].o[nt][j] * inv);
         }
-        if (a.lse && g == 0 && q_valid[q])
-            a.lse[(row0 + r_local[q]) * a.Hq + head[q]] = ltot > 0.0f ? (st[q].m + __log2f(ltot)) * kLn2 : -INFINITY;
+        const int qi = 16 * (QG * wave + q) + m16;
+        if (a.lse && g == 0 && qi / hg < nrows)
+            a.lse[(row0 + qi / hg) * a.Hq + kvh * hg + qi % hg] =
+                ltot > 0.0f ? (st[q].m + __log2f(ltot)) * kLn2 : -INFINITY;
     }
 }
 
@@ -691,12 +717,13 @@ __global__ __launch_bounds__(256, DIM == 256 ? 2 : 1) void attn_decode_mfma_kern
     const bool q_valid = qi < nq;
     const int head = kvh * hg + qi % hg;
     const int64_t qrow = (s * a.q_per_sel + (q_valid ? jrow : 0)) * a.Hq + head;
+    bool qneg;
+    const float scale2 = logit_scale2(a, kFp8, qneg);
     bf16x8_t qb[1][G::kKs];
-    load_query<DIM>((const bf16_t *)a.q + qrow * DIM, q_valid, qb[0]);
+    load_query<DIM>((const bf16_t *)a.q + qrow * DIM, q_valid, qneg, qb[0]);
     WaveState<DIM> st[1];
     init_state(st[0]);
-    const float scale2 = kFp8 ? a.scale * a.k_scale * kLog2e : a.scale * kLog2e;
-    const uint32_t qbit[1] = {q_valid ? (1u << jrow) : 0u};
+    const uint32_t rbit[1] = {q_valid ? (uint32_t)jrow : 31u};
     const int64_t row_stride = (int64_t)a.Hkv * DIM;
     const int64_t seq_off = a.page_table ? 0 : s * a.kv_seq_stride;
     const KV *kbase = (const KV *)a.k_cache + seq_off + (int64_t)kvh * DIM;
@@ -718,7 +745,7 @@ __global__ __launch_bounds__(256, DIM == 256 ? 2 : 1) void attn_decode_mfma_kern
             __syncthreads();
             gather_chunk<DIM>(cs, kbase, vbase, row_stride, cb * kBlock);
             __syncthreads();
-            wave_chunk<DIM, 1>(cs, qb, qbit, scale2, st);
+            wave_chunk<DIM, 1>(cs, qb, rbit, scale2, st);
             __syncthreads();
         }
     } else {
@@ -748,7 +775,7 @@ __global__ __launch_bounds__(256, DIM == 256 ? 2 : 1) void attn_decode_mfma_kern
             __syncthreads();
             gather_chunk<DIM>(cs, kbase, vbase, row_stride, n);
             __syncthreads();
-            wave_chunk<DIM, 1>(cs, qb, qbit, scale2, st);
+            wave_chunk<DIM, 1>(cs, qb, rbit, scale2, st);
             __syncthreads();
         }
     }

@@ -290,6 +290,40 @@ def test_attn_prefill_overlapping_and_mixed_sequences(gpu):
     np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5, 1e-3])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (4, 4)])
+def test_attn_softmax_scale_sign_and_zero(gpu, scale, Hq, Hkv):
+    # the kernels keep the exponent scale positive: a negative softmax_scale
+    # is carried by the queries' sign, a zero one gives every attended
+    # position the same weight
+    rng = np.random.default_rng(36)
+    L, R, k = 4 * 300 + 1, 37, 32
+    pos = np.sort(rng.choice(L, R, replace=False)).astype(np.int32)
+    pos[:3] = [0, 5, 6]
+    seq = np.zeros(R, np.int32)
+    sel, cnt = _random_selection(rng, pos, k)
+    q = synth.bf16_bits(rng.standard_normal((R, Hq, DIM)).astype(np.float32))
+    kc = synth.bf16_bits(rng.standard_normal((1, L, Hkv, DIM)).astype(np.float32))
+    vc = synth.bf16_bits(rng.standard_normal((1, L, Hkv, DIM)).astype(np.float32))
+    want, want_lse = oracle.sparse_attn_prefill(q, seq, pos, kc, vc, sel, cnt, softmax_scale=scale)
+    out, lse = qsa.sparse_attn_prefill(dev(q, "bf16"), dev(seq, "i"), dev(pos, "i"), dev(kc, "bf16"),
+                                       dev(vc, "bf16"), dev(sel, "i"), dev(cnt, "i"), softmax_scale=scale)
+    assert_close_out(host(out), want, "bf16")
+    np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
+    # decode: the last row of each of two sequences, sharing the prefill's cache
+    B = 2
+    qd = synth.bf16_bits(rng.standard_normal((B, 1, Hq, DIM)).astype(np.float32))
+    kd = np.concatenate([kc, kc[:, ::-1]], axis=0)
+    vd = np.concatenate([vc, vc[:, ::-1]], axis=0)
+    pd = np.array([[L - 1], [L - 3]], np.int32)
+    seld, cntd = _random_selection(rng, pd[:, 0], k)
+    want, want_lse = oracle.sparse_attn_decode(qd, pd, kd, vd, seld, cntd, softmax_scale=scale)
+    out, lse = qsa.sparse_attn_decode(dev(qd, "bf16"), dev(pd, "i"), dev(kd, "bf16"), dev(vd, "bf16"),
+                                      dev(seld, "i"), dev(cntd, "i"), softmax_scale=scale)
+    assert_close_out(host(out), want, "bf16")
+    np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
+
+
 def test_attn_prefill_union_across_windows(gpu):
     # the prefill kernel builds a tile's union of kept blocks one window of
     # 65,536 blocks at a time: kept blocks on both sides of each window edge,
