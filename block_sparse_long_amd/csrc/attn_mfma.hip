@@ -536,7 +536,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
         s_last[t] = c > 0 ? a.sel_blocks[r * a.top_k + c - 1] : -1;
     }
     __syncthreads();
-    constexpr int kBatch = 8;  // selection entries a thread reads together
+    constexpr int kSelPerThread = kMaxUnionBlocks / 256;
     uint32_t todo = nrows >= 32 ? 0xffffffffu : ((1u << nrows) - 1u);
     while (todo) {  // rows of one sequence at a time (uniform across the workgroup)
         const int first = __builtin_ctz(todo);
@@ -554,28 +554,37 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
             if ((active >> r) & 1u) hi_blk = max(hi_blk, s_last[r] + 1);
         for (int32_t w0 = 0; w0 < hi_blk; w0 += kWin) {
             // ---- union of the active rows' kept blocks in [w0, w0 + kWin).
-            // The tile's selections (row-major, top_k per row) are read in
-            // batches of kBatch entries per thread, twice: to set the bitmap,
-            // then to set each union block's row bits ----
+            // Entry idx = r top_k + i of the tile's selections (row r, rank
+            // i) sits at sel_blocks[row0 top_k + idx].  Each of the two
+            // passes below reads a thread's entries t + 256 j together; an
+            // entry's row is floor((idx + 0.5) / top_k) in float, exact for
+            // idx, top_k <= 8,192 (the quotient's rounding error is below
+            // 2^-10 / top_k, its distance to an integer at least 0.5 / top_k) ----
             const int32_t nent = nrows * a.top_k;
-            auto entries = [&](auto &&fn) {
-                for (int32_t base = 0; base < nent; base += 256 * kBatch) {
-                    int32_t eb[kBatch], er[kBatch];
+            const float inv_k = 1.0f / (float)a.top_k;
+            const int32_t *sel = a.sel_blocks + row0 * a.top_k;
+            // calls fn(block - w0, row) for the thread's entries kept by an
+            // active row inside the window
+            auto for_entries = [&](auto &&fn) {
+                // the entries' addresses and rows are computed here, per
+                // pass, not hoisted to the kernel's start and held across it
+                int32_t tt = t;
+                asm volatile("" : "+v"(tt));
+                int32_t eb[kSelPerThread];
 #pragma unroll
-                    for (int u = 0; u < kBatch; ++u) {
-                        const int32_t idx = min(base + t + 256 * u, nent - 1);
-                        const int32_t r = idx / a.top_k, i = idx - r * a.top_k;
-                        er[u] = base + t + 256 * u < nent && ((active >> r) & 1u) && i < s_cnt[r] ? r : -1;
-                        eb[u] = a.sel_blocks[(row0 + r) * a.top_k + i] - w0;
-                    }
+                for (int j = 0; j < kSelPerThread; ++j) eb[j] = sel[min(tt + 256 * j, nent - 1)] - w0;
 #pragma unroll
-                    for (int u = 0; u < kBatch; ++u)
-                        if (er[u] >= 0 && eb[u] >= 0 && eb[u] < kWin) fn(eb[u], er[u]);
+                for (int j = 0; j < kSelPerThread; ++j) {
+                    const int32_t idx = tt + 256 * j;
+                    const int32_t r = min((int32_t)(((float)idx + 0.5f) * inv_k), kMaxTileRows - 1);
+                    if (idx < nent && ((active >> r) & 1u) && idx - r * a.top_k < s_cnt[r] && eb[j] >= 0 &&
+                        eb[j] < kWin)
+                        fn(eb[j], r);
                 }
             };
             for (int i = t; i < kWinWords; i += blockDim.x) ub.bitmap[i] = 0u;
             __syncthreads();
-            entries([&](int32_t b, int32_t) { atomicOr(&ub.bitmap[b >> 5], 1u << (b & 31)); });
+            for_entries([&](int32_t b, int32_t) { atomicOr(&ub.bitmap[b >> 5], 1u << (b & 31)); });
             __syncthreads();
             {   // exclusive prefix of popcounts over the words (8 words per thread)
                 constexpr int per = kWinWords / 256;
@@ -606,7 +615,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
                 }
             }
             __syncthreads();
-            entries([&](int32_t b, int32_t r) {
+            for_entries([&](int32_t b, int32_t r) {
                 const uint32_t word = ub.bitmap[b >> 5];
                 const uint32_t idx = ub.wprefix[b >> 5] + __popc(word & ((1u << (b & 31)) - 1u));
                 atomicOr(&us.mask2[idx >> 1], 1u << (r + 16 * (idx & 1u)));
