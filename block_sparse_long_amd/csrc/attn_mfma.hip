@@ -595,29 +595,27 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
                 __shared__ uint32_t wsum[4];
                 if (lane == 63) wsum[wave] = x;
                 __syncthreads();
-                uint32_t before = 0;
-                for (int w = 0; w < wave; ++w) before += wsum[w];
-                if (t == 255) us.count = before + x;
+                uint32_t before = 0, total = 0;
+                for (int w = 0; w < 4; ++w) {
+                    before += w < wave ? wsum[w] : 0u;
+                    total += wsum[w];
+                }
+                if (t == 0) us.count = total;
                 uint32_t run = before + x - cnt;
 #pragma unroll
                 for (int i = 0; i < per; ++i) {
-                    const uint32_t word = ub.bitmap[t * per + i];
                     ub.wprefix[t * per + i] = (uint16_t)run;
-                    uint32_t bits = word, k = run;
-                    while (bits) {
-                        const int b = __builtin_ctz(bits);
-                        bits &= bits - 1u;
-                        us.blk[k] = (uint16_t)((t * per + i) * 32 + b);
-                        if (!(k & 1u)) us.mask2[k >> 1] = 0u;  // word k/2 has one even index, owned here
-                        ++k;
-                    }
-                    run += __popc(word);
+                    run += __popc(ub.bitmap[t * per + i]);
                 }
+                for (uint32_t k = t; k < (total + 1) / 2; k += blockDim.x) us.mask2[k] = 0u;
             }
             __syncthreads();
+            // each entry's union index: its word's prefix plus the set bits below it;
+            // entries of several rows with one block store the same list value
             for_entries([&](int32_t b, int32_t r) {
                 const uint32_t word = ub.bitmap[b >> 5];
                 const uint32_t idx = ub.wprefix[b >> 5] + __popc(word & ((1u << (b & 31)) - 1u));
+                us.blk[idx] = (uint16_t)b;
                 atomicOr(&us.mask2[idx >> 1], 1u << (r + 16 * (idx & 1u)));
             });
             __syncthreads();
