@@ -338,40 +338,60 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem<DIM> &cs, const bf16x
     const int lane = threadIdx.x & 63;
     const int m16 = lane & 15, g = lane >> 4;
     float x[QG][G::kSub][4];  // raw logits, -inf where the query does not attend
-    bool any[G::kSub];
+    uint4 pm[G::kSub];        // mask words of the lane's positions 4g .. 4g+3 of each sub-tile
+    bool any[G::kSub];        // some query of the wave attends the sub-tile
 #pragma unroll
     for (int sub = 0; sub < G::kSub; ++sub) {
-        const uint4 pm = *(const uint4 *)&cs.pmask[sub * 16 + 4 * g];  // positions 4g .. 4g+3 of the sub-tile
-        const uint32_t pall = pm.x | pm.y | pm.z | pm.w;
+        pm[sub] = *(const uint4 *)&cs.pmask[sub * 16 + 4 * g];
+        const uint32_t pall = pm[sub].x | pm[sub].y | pm[sub].z | pm[sub].w;
         bool some = false;
 #pragma unroll
         for (int q = 0; q < QG; ++q) some |= ((pall >> rbit[q]) & 1u) != 0u;
         any[sub] = __ballot(some) != 0ull;
+    }
+    // S^T of one sub-tile: its K operands are read 4 at a time, then their MFMAs issue
+    auto sub_tile = [&](int sub) {
         f32x4_t acc[QG];
 #pragma unroll
         for (int q = 0; q < QG; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        if (any[sub]) {  // the sub-tile's K operands are read 4 at a time, then their MFMAs issue
 #pragma unroll
-            for (int k0 = 0; k0 < G::kKs; k0 += 4) {
-                uint4 kv[4];
+        for (int k0 = 0; k0 < G::kKs; k0 += 4) {
+            uint4 kv[4];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    kv[ks] = *(const uint4 *)&cs.k[sub * 16 + m16][(DIM / 4) * g + 8 * (k0 + ks)];
-                __builtin_amdgcn_sched_barrier(0);
+            for (int ks = 0; ks < 4; ++ks)
+                kv[ks] = *(const uint4 *)&cs.k[sub * 16 + m16][(DIM / 4) * g + 8 * (k0 + ks)];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
+            for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                    for (int q = 0; q < QG; ++q)
-                        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks]), qb[q][k0 + ks], acc[q], 0,
-                                                                         0, 0);
-            }
+                for (int q = 0; q < QG; ++q)
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks]), qb[q][k0 + ks], acc[q], 0, 0, 0);
         }
 #pragma unroll
         for (int q = 0; q < QG; ++q) {
-            x[q][sub][0] = masked_logit(acc[q][0], pm.x, rbit[q]);
-            x[q][sub][1] = masked_logit(acc[q][1], pm.y, rbit[q]);
-            x[q][sub][2] = masked_logit(acc[q][2], pm.z, rbit[q]);
-            x[q][sub][3] = masked_logit(acc[q][3], pm.w, rbit[q]);
+            x[q][sub][0] = masked_logit(acc[q][0], pm[sub].x, rbit[q]);
+            x[q][sub][1] = masked_logit(acc[q][1], pm[sub].y, rbit[q]);
+            x[q][sub][2] = masked_logit(acc[q][2], pm[sub].z, rbit[q]);
+            x[q][sub][3] = masked_logit(acc[q][3], pm[sub].w, rbit[q]);
+        }
+    };
+    bool all_any = true;
+#pragma unroll
+    for (int sub = 0; sub < G::kSub; ++sub) all_any = all_any && any[sub];
+    if (all_any) {  // every sub-tile has work for the wave (neighbouring rows sharing their blocks)
+#pragma unroll
+        for (int sub = 0; sub < G::kSub; ++sub) sub_tile(sub);
+    } else {
+#pragma unroll
+        for (int sub = 0; sub < G::kSub; ++sub) {
+            if (any[sub]) {
+                sub_tile(sub);
+            } else {
+#pragma unroll
+                for (int q = 0; q < QG; ++q)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) x[q][sub][j] = -INFINITY;
+            }
         }
     }
     // online softmax per query (lane l%16 of group q; the 4 lane groups hold its positions)
