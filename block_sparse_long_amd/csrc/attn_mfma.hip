@@ -37,6 +37,8 @@
 // sub-tiles 2i and 2i+1; group g's slots 0-3 are positions 4g..4g+3 of
 // sub-tile 2i and slots 4-7 those of sub-tile 2i+1 -- exactly the S^T values
 // the lane already holds, so P needs no shuffle.
+#include <type_traits>
+
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -350,7 +352,7 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem<DIM> &cs, const bf16x
         any[sub] = __ballot(some) != 0ull;
     }
     // S^T of one sub-tile: its K operands are read 4 at a time, then their MFMAs issue
-    auto sub_tile = [&](int sub) {
+    auto sub_tile = [&](int sub, auto masked) {
         f32x4_t acc[QG];
 #pragma unroll
         for (int q = 0; q < QG; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -369,23 +371,38 @@ __device__ __forceinline__ void wave_chunk(const ChunkSmem<DIM> &cs, const bf16x
         }
 #pragma unroll
         for (int q = 0; q < QG; ++q) {
-            x[q][sub][0] = masked_logit(acc[q][0], pm[sub].x, rbit[q]);
-            x[q][sub][1] = masked_logit(acc[q][1], pm[sub].y, rbit[q]);
-            x[q][sub][2] = masked_logit(acc[q][2], pm[sub].z, rbit[q]);
-            x[q][sub][3] = masked_logit(acc[q][3], pm[sub].w, rbit[q]);
+            if (decltype(masked)::value) {
+                x[q][sub][0] = masked_logit(acc[q][0], pm[sub].x, rbit[q]);
+                x[q][sub][1] = masked_logit(acc[q][1], pm[sub].y, rbit[q]);
+                x[q][sub][2] = masked_logit(acc[q][2], pm[sub].z, rbit[q]);
+                x[q][sub][3] = masked_logit(acc[q][3], pm[sub].w, rbit[q]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[q][sub][j] = acc[q][j];
+            }
         }
     };
     bool all_any = true;
+    uint32_t pand = ~0u;  // the mask bits every position of the lane's four per sub-tile carries
 #pragma unroll
-    for (int sub = 0; sub < G::kSub; ++sub) all_any = all_any && any[sub];
-    if (all_any) {  // every sub-tile has work for the wave (neighbouring rows sharing their blocks)
+    for (int sub = 0; sub < G::kSub; ++sub) {
+        all_any = all_any && any[sub];
+        pand &= pm[sub].x & pm[sub].y & pm[sub].z & pm[sub].w;
+    }
+    bool lane_full = true;
 #pragma unroll
-        for (int sub = 0; sub < G::kSub; ++sub) sub_tile(sub);
+    for (int q = 0; q < QG; ++q) lane_full = lane_full && ((pand >> rbit[q]) & 1u);
+    if (__ballot(lane_full) == ~0ull) {  // every query of the wave attends every position: no masks
+#pragma unroll
+        for (int sub = 0; sub < G::kSub; ++sub) sub_tile(sub, std::false_type{});
+    } else if (all_any) {  // every sub-tile has work for the wave (neighbouring rows sharing their blocks)
+#pragma unroll
+        for (int sub = 0; sub < G::kSub; ++sub) sub_tile(sub, std::true_type{});
     } else {
 #pragma unroll
         for (int sub = 0; sub < G::kSub; ++sub) {
             if (any[sub]) {
-                sub_tile(sub);
+                sub_tile(sub, std::true_type{});
             } else {
 #pragma unroll
                 for (int q = 0; q < QG; ++q)
