@@ -862,7 +862,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="chunk-256k")
     ap.add_argument("--decode-workload", default="decode-1m-draft")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -903,19 +903,19 @@ def main():
         value, unit, ms = pre["value"], "tokens/s", pre["ms_per_step"]
         main_res = pre
     else:
-        pre = bench_decode(spec, args.steps * 10, args.warmup, cpu)
+        pre = bench_decode(spec, args.steps * 10, args.warmup * 10, cpu)
         value, unit, ms = pre["value"], pre["unit"], pre["ms_per_step"]
         main_res = pre
     fp8_res, serve_res, paged_res = {}, {}, {}
     if args.paged:
         paged_res[spec.name] = bench_paged(spec, pre["_inputs"], args.steps if spec.kind == "prefill" else
-                                           args.steps * 10, args.warmup)
+                                           args.steps * 10, args.warmup * 10)
     if args.serving and spec.dtype == "bf16":
         s2, w2 = serving_shape_inputs(spec, pre["_inputs"])
         if spec.kind == "prefill":
             serve_res[spec.name] = bench_prefill(s2, args.steps, args.warmup, False, w=w2)
         else:
-            serve_res[spec.name] = bench_decode(s2, args.steps * 10, args.warmup, False, w=w2)
+            serve_res[spec.name] = bench_decode(s2, args.steps * 10, args.warmup * 10, False, w=w2)
         del w2
     fp8kv_res = {}
     if args.fp8 and spec.dtype == "bf16":
@@ -924,8 +924,8 @@ def main():
             fp8kv_res[spec.name] = bench_prefill(spec, args.steps, args.warmup, False, keys="fp8", kv="fp8",
                                                  w=pre["_inputs"])
         else:
-            fp8_res[spec.name] = bench_decode(spec, args.steps * 10, args.warmup, False, keys="fp8", w=pre["_inputs"])
-            fp8kv_res[spec.name] = bench_decode(spec, args.steps * 10, args.warmup, False, keys="fp8", kv="fp8",
+            fp8_res[spec.name] = bench_decode(spec, args.steps * 10, args.warmup * 10, False, keys="fp8", w=pre["_inputs"])
+            fp8kv_res[spec.name] = bench_decode(spec, args.steps * 10, args.warmup * 10, False, keys="fp8", kv="fp8",
                                                 w=pre["_inputs"])
     pre.pop("_inputs", None)
     line = {
@@ -943,17 +943,17 @@ def main():
     }
     if args.decode_workload != "none" and spec.kind == "prefill":
         dspec = synth.SPECS[args.decode_workload]
-        dec = bench_decode(dspec, args.steps * 10, args.warmup, cpu)
+        dec = bench_decode(dspec, args.steps * 10, args.warmup * 10, cpu)
         if args.fp8 and dspec.dtype == "bf16":
-            fp8_res[dspec.name] = bench_decode(dspec, args.steps * 10, args.warmup, False, keys="fp8",
+            fp8_res[dspec.name] = bench_decode(dspec, args.steps * 10, args.warmup * 10, False, keys="fp8",
                                                w=dec["_inputs"])
-            fp8kv_res[dspec.name] = bench_decode(dspec, args.steps * 10, args.warmup, False, keys="fp8", kv="fp8",
+            fp8kv_res[dspec.name] = bench_decode(dspec, args.steps * 10, args.warmup * 10, False, keys="fp8", kv="fp8",
                                                  w=dec["_inputs"])
         if args.paged:
-            paged_res[dspec.name] = bench_paged(dspec, dec["_inputs"], args.steps * 10, args.warmup)
+            paged_res[dspec.name] = bench_paged(dspec, dec["_inputs"], args.steps * 10, args.warmup * 10)
         if args.serving and dspec.dtype == "bf16":
             s2, w2 = serving_shape_inputs(dspec, dec["_inputs"])
-            serve_res[dspec.name] = bench_decode(s2, args.steps * 10, args.warmup, False, w=w2)
+            serve_res[dspec.name] = bench_decode(s2, args.steps * 10, args.warmup * 10, False, w=w2)
             del w2
         dec.pop("_inputs", None)
         line["decode"] = {k: v for k, v in dec.items()}
@@ -973,7 +973,7 @@ def main():
                 r = bench_prefill(o, args.steps, args.warmup, cpu, cpu_target_s=5.0)
                 unit_o = "tokens/s"
             else:
-                r = bench_decode(o, args.steps * 10, args.warmup, cpu, cpu_target_s=3.0)
+                r = bench_decode(o, args.steps * 10, args.warmup * 10, cpu, cpu_target_s=3.0)
                 unit_o = r["unit"]
             r.pop("_inputs", None)
             line["other_workloads"][name] = {
