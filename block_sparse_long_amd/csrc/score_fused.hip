@@ -120,20 +120,37 @@ __device__ __forceinline__ void tile_scores(const bf16_t (*keys)[kFKRow], const 
     for (int mt = 0; mt < 4; ++mt) sc[mt][3] = relu_sum4f(acc[1][mt]);
 }
 
-// Rows of one sequence at a time: the next group of the workgroup's rows
-// (uniform across the workgroup).  Returns the sequence and the largest
-// visible-block count of the group; clears the group's bits from `todo`.
-__device__ __forceinline__ int32_t next_seq_group(const FusedScoreArgs &a, int64_t row0, int nrows, uint64_t &todo,
-                                                  int64_t &nb_hi)
+// Row r of a 64-row tile as lane r of every wave holds it: its sequence (-1
+// past the tile's rows) and its visible-block count, read once, in parallel.
+struct TileRows {
+    int32_t seq;
+    int32_t nb;
+};
+__device__ __forceinline__ TileRows tile_rows(const FusedScoreArgs &a, int64_t row0, int nrows)
 {
+    static_assert(kFRows == kWave, "one tile row per lane");
+    const int lane = threadIdx.x & 63;
+    const bool ok = lane < nrows;
+    TileRows tr;
+    tr.seq = ok ? a.row_seq[row0 + lane] : -1;
+    tr.nb = ok ? (int32_t)min(visible_blocks(a.row_pos[row0 + lane]), (int64_t)a.max_nb) : 0;
+    return tr;
+}
+
+// Rows of one sequence at a time: the next group of the workgroup's rows
+// (uniform across the workgroup), found with one ballot.  Returns the
+// sequence and the largest visible-block count of the group; clears the
+// group's bits from `todo`.
+__device__ __forceinline__ int32_t next_seq_group(const TileRows &tr, uint64_t &todo, int64_t &nb_hi)
+{
+    const int lane = threadIdx.x & 63;
     const int first = __builtin_ctzll(todo);
-    const int32_t seq = a.row_seq[row0 + first];
-    nb_hi = 0;
-    for (int r = first; r < nrows; ++r)
-        if (((todo >> r) & 1ull) && a.row_seq[row0 + r] == seq) {
-            todo &= ~(1ull << r);
-            nb_hi = max(nb_hi, min(visible_blocks(a.row_pos[row0 + r]), (int64_t)a.max_nb));
-        }
+    const int32_t seq = (int32_t)lane_value((uint32_t)tr.seq, first);
+    const bool in = ((todo >> lane) & 1ull) && tr.seq == seq;
+    todo &= ~__ballot(in);
+    const uint32_t nbmax =
+        wave_incl_scan_op((uint32_t)(in ? tr.nb : 0), [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+    nb_hi = (int64_t)lane_value(nbmax, 63);
     return seq;
 }
 
@@ -238,10 +255,11 @@ __global__ __launch_bounds__(256, 2) void score_sample_kernel(FusedScoreArgs a)
 #pragma unroll
         for (int q = 0; q < 4; ++q) top[mt][q] = -1.0f;
     }
+    const TileRows trow = tile_rows(a, row0, nrows);
     uint64_t todo = nrows >= 64 ? ~0ull : ((1ull << nrows) - 1ull);
     while (todo) {
         int64_t nb_hi;
-        const int32_t seq = next_seq_group(a, row0, nrows, todo, nb_hi);
+        const int32_t seq = next_seq_group(trow, todo, nb_hi);
         const int64_t hi = min(s_hi, (nb_hi + kSampleStride - 1) / kSampleStride);  // samples that can be visible
         // smallest visible bound over the wave's rows of this group
         int64_t lim_min = INT64_MAX;
@@ -372,10 +390,11 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
         tauf[mt] = ok ? tau_float(a.tau[row0 + rw]) : INFINITY;
     }
     const uint32_t cap_last = (uint32_t)a.subcap - 1u;
+    const TileRows trow = tile_rows(a, row0, nrows);
     uint64_t todo = nrows >= 64 ? ~0ull : ((1ull << nrows) - 1ull);
     while (todo) {
         int64_t nb_hi;
-        const int32_t seq = next_seq_group(a, row0, nrows, todo, nb_hi);
+        const int32_t seq = next_seq_group(trow, todo, nb_hi);
         int64_t lim[4];  // visible bound of the lane's rows in this group (0: not in it)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) lim[mt] = my_seq[mt] == seq ? my_nc[mt] : 0;
