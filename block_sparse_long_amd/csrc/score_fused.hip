@@ -75,7 +75,7 @@ __device__ __forceinline__ float tau_float(uint32_t key) { return key == 0u ? -I
 
 __device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
-// The 16 x 4 x 128 query tile of a wave as MFMA A operands (zeros past nrows).
+// The 16 x 4 x 128 query tile of a wave as MFMA A operands.
 __device__ __forceinline__ void load_query_tile(const bf16_t *__restrict__ qrot, int64_t row0, int nrows, int wave,
                                                 bf16x8_t (&qa)[4][4])
 {
@@ -83,11 +83,13 @@ __device__ __forceinline__ void load_query_tile(const bf16_t *__restrict__ qrot,
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const int rw = 16 * wave + 4 * mt + (m >> 2);
-        const bool ok = rw < nrows;
+        // a row slot past the tile's rows takes the last row's query (clamped, so every load
+        // is issued together with no branch): its scores are finite and never used, since the
+        // slot belongs to no sequence and has tau = +inf
+        const int rc = min(rw, nrows - 1);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            qa[mt][s] = ok ? as_bf16x8(*(const uint4 *)(qrot + ((row0 + rw) * kIdxHeads + (m & 3)) * kDim + 32 * g + 8 * s))
-                           : zero_bf16x8();
+            qa[mt][s] = as_bf16x8(*(const uint4 *)(qrot + ((row0 + rc) * kIdxHeads + (m & 3)) * kDim + 32 * g + 8 * s));
     }
 }
 
@@ -130,10 +132,12 @@ __device__ __forceinline__ TileRows tile_rows(const FusedScoreArgs &a, int64_t r
 {
     static_assert(kFRows == kWave, "one tile row per lane");
     const int lane = threadIdx.x & 63;
-    const bool ok = lane < nrows;
+    const int32_t okm = lane < nrows ? -1 : 0;
+    const int rc = min(lane, nrows - 1);  // loads issued unconditionally (clamped), then masked
+    const int32_t sq = a.row_seq[row0 + rc], p = a.row_pos[row0 + rc];
     TileRows tr;
-    tr.seq = ok ? a.row_seq[row0 + lane] : -1;
-    tr.nb = ok ? (int32_t)min(visible_blocks(a.row_pos[row0 + lane]), (int64_t)a.max_nb) : 0;
+    tr.seq = sq | ~okm;
+    tr.nb = (int32_t)min(visible_blocks(p), (int64_t)a.max_nb) & okm;
     return tr;
 }
 
@@ -244,18 +248,18 @@ __global__ __launch_bounds__(256, 2) void score_sample_kernel(FusedScoreArgs a)
     const int64_t s_lo = split * slen, s_hi = min((int64_t)a.nsample, s_lo + slen);
     bf16x8_t qa[4][4];
     load_query_tile(qrot, row0, nrows, wave, qa);
+    const TileRows trow = tile_rows(a, row0, nrows);
     int64_t my_nc[4];
     int32_t my_seq[4];
     float top[4][4];  // per row: the lane's 4 best sampled scores, descending (-1: none)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        const int rw = 16 * wave + 4 * mt + g;
-        my_nc[mt] = rw < nrows ? min(visible_blocks(a.row_pos[row0 + rw]), (int64_t)a.max_nb) : 0;
-        my_seq[mt] = rw < nrows ? a.row_seq[row0 + rw] : -1;
+        const int rw = 16 * wave + 4 * mt + g;  // its sequence and bound: lane rw of the tile's rows
+        my_nc[mt] = __shfl(trow.nb, rw);
+        my_seq[mt] = __shfl(trow.seq, rw);
 #pragma unroll
         for (int q = 0; q < 4; ++q) top[mt][q] = -1.0f;
     }
-    const TileRows trow = tile_rows(a, row0, nrows);
     uint64_t todo = nrows >= 64 ? ~0ull : ((1ull << nrows) - 1ull);
     while (todo) {
         int64_t nb_hi;
@@ -379,18 +383,21 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
     uint2 *my_list[4];
     uint32_t my_cnt[4];
     float tauf[4];
+    const TileRows trow = tile_rows(a, row0, nrows);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        const int rw = 16 * wave + 4 * mt + g;
-        const bool ok = rw < nrows;
-        my_nc[mt] = ok ? min(visible_blocks(a.row_pos[row0 + rw]), (int64_t)a.max_nb) : 0;
-        my_seq[mt] = ok ? a.row_seq[row0 + rw] : -1;
-        my_list[mt] = a.buf + (((row0 + (ok ? rw : 0)) * a.nsplit + split) * 16 + m) * (int64_t)a.subcap;
+        const int rw = 16 * wave + 4 * mt + g;  // its sequence and bound: lane rw of the tile's rows
+        const uint32_t okm = rw < nrows ? ~0u : 0u;
+        const int rc = min(rw, nrows - 1);
+        const uint32_t tk = a.tau[row0 + rc];  // issued unconditionally (clamped), then masked
+        my_nc[mt] = __shfl(trow.nb, rw);
+        my_seq[mt] = __shfl(trow.seq, rw);
+        my_list[mt] = a.buf + (((row0 + rc) * a.nsplit + split) * 16 + m) * (int64_t)a.subcap;
         my_cnt[mt] = 0;
-        tauf[mt] = ok ? tau_float(a.tau[row0 + rw]) : INFINITY;
+        // an empty row slot gets tau = +inf, so it never appends
+        tauf[mt] = __uint_as_float((__float_as_uint(tau_float(tk)) & okm) | (0x7f800000u & ~okm));
     }
     const uint32_t cap_last = (uint32_t)a.subcap - 1u;
-    const TileRows trow = tile_rows(a, row0, nrows);
     uint64_t todo = nrows >= 64 ? ~0ull : ((1ull << nrows) - 1ull);
     while (todo) {
         int64_t nb_hi;
