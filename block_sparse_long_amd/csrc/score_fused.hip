@@ -289,22 +289,32 @@ __global__ __launch_bounds__(256, 2) void score_sample_kernel(FusedScoreArgs a)
             // every sample of the step visible to every row of the wave: no
             // per-sample test (sample i's block is below 32 i + 32)
             const bool all_vis = i0 + kFStep <= hi && (i0 + kFStep) * kSampleStride <= lim_min;
+            // insert v into the lane's descending top-4 of row tile mt: the new q-th best of
+            // {top[0..q], v} is the median of top[q-1], top[q] and v.  The lists start at -1
+            // and scores are >= 0, so inserting -1 (a row of another sequence, a sample past
+            // the row's visible blocks) changes nothing: the insertions stay straight-line code.
+            auto insert = [&](int mt, float v) {
+                float *tp = top[mt];
+                const float t0 = tp[0], t1 = tp[1], t2 = tp[2];
+                tp[0] = fmaxf(t0, v);
+                tp[1] = __builtin_amdgcn_fmed3f(t0, t1, v);
+                tp[2] = __builtin_amdgcn_fmed3f(t1, t2, v);
+                tp[3] = __builtin_amdgcn_fmed3f(t2, tp[3], v);
+            };
+            if (all_vis) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                if (my_seq[mt] != seq) continue;
+                for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    const int64_t i = i0 + nt * 16 + m;
-                    const float v = (all_vis || (i < hi && sample_block(i) < my_nc[mt])) ? sc[mt][nt] : -1.0f;
-                    // insert into the descending top-4: the new q-th best of
-                    // {top[0..q], v} is the median of top[q-1], top[q] and v
-                    float *tp = top[mt];
-                    const float t0 = tp[0], t1 = tp[1], t2 = tp[2];
-                    tp[0] = fmaxf(t0, v);
-                    tp[1] = __builtin_amdgcn_fmed3f(t0, t1, v);
-                    tp[2] = __builtin_amdgcn_fmed3f(t1, t2, v);
-                    tp[3] = __builtin_amdgcn_fmed3f(t2, tp[3], v);
-                }
+                    for (int nt = 0; nt < 4; ++nt) insert(mt, my_seq[mt] == seq ? sc[mt][nt] : -1.0f);
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) {
+                        const int64_t i = i0 + nt * 16 + m;
+                        const bool vis = my_seq[mt] == seq && i < hi && sample_block(i) < my_nc[mt];
+                        insert(mt, vis ? sc[mt][nt] : -1.0f);
+                    }
             }
             __syncthreads();
         }
