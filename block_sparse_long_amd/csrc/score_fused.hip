@@ -75,6 +75,14 @@ __device__ __forceinline__ float tau_float(uint32_t key) { return key == 0u ? -I
 
 __device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
+// A row's pair lists: 16 per split, the 16 of a split interleaved slot by slot
+// (pair j of list m at 16 j + m), so that a 128-byte line holds slot j of all
+// 16 and the lines a row keeps open while its lists grow are few enough for L2.
+__device__ __forceinline__ int64_t list_slot(int li, uint32_t j, int32_t subcap)
+{
+    return (int64_t)(li >> 4) * 16 * subcap + (int64_t)j * 16 + (li & 15);
+}
+
 // The 16 x 4 x 128 query tile of a wave as MFMA A operands.
 __device__ __forceinline__ void load_query_tile(const bf16_t *__restrict__ qrot, int64_t row0, int nrows, int wave,
                                                 bf16x8_t (&qa)[4][4])
@@ -402,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
         const uint32_t tk = a.tau[row0 + rc];  // issued unconditionally (clamped), then masked
         my_nc[mt] = __shfl(trow.nb, rw);
         my_seq[mt] = __shfl(trow.seq, rw);
-        my_list[mt] = a.buf + (((row0 + rc) * a.nsplit + split) * 16 + m) * (int64_t)a.subcap;
+        my_list[mt] = a.buf + ((row0 + rc) * a.nsplit + split) * 16 * (int64_t)a.subcap + m;  // slot j at [16 j]
         my_cnt[mt] = 0;
         // an empty row slot gets tau = +inf, so it never appends
         tauf[mt] = __uint_as_float((__float_as_uint(tau_float(tk)) & okm) | (0x7f800000u & ~okm));
@@ -457,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
                         if (sc[mt][nt] >= tauf[mt]) {
-                            my_list[mt][min(my_cnt[mt], cap_last)] =
+                            my_list[mt][16 * min(my_cnt[mt], cap_last)] =
                                 make_uint2(pos_key(sc[mt][nt]), (uint32_t)(base + nt * 16 + m));
                             ++my_cnt[mt];
                         }
@@ -469,7 +477,7 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
                         if (sc[mt][nt] >= tauf[mt] && 16 * nt < lr) {
-                            my_list[mt][min(my_cnt[mt], cap_last)] =
+                            my_list[mt][16 * min(my_cnt[mt], cap_last)] =
                                 make_uint2(pos_key(sc[mt][nt]), (uint32_t)(base + nt * 16 + m));
                             ++my_cnt[mt];
                         }
@@ -776,19 +784,16 @@ __device__ __forceinline__ void for_each_listed(const uint2 *__restrict__ lists,
         const uint32_t c = li < nlists ? cnt[li] : 0u;
         uint32_t cmax = c;
         for (int o = 1; o < 64; o <<= 1) cmax = max(cmax, (uint32_t)__shfl_xor((int)cmax, o));
-        const uint4 *src = (const uint4 *)(lists + (int64_t)min(li, nlists - 1) * subcap);
-        // a load past the list's last 16-byte pair of pairs re-reads that one (every load
-        // stays in the list, none needs a guard, so all 8 are issued together)
-        const uint32_t qlast = c > 0u ? (c - 1u) >> 1 : 0u;
+        const uint2 *src = lists + list_slot(min(li, nlists - 1), 0u, subcap);  // slot j at [16 j]
+        // a load past the list's last pair re-reads that one (every load stays in
+        // the list, none needs a guard, so all 16 are issued together)
+        const uint32_t last = c > 0u ? c - 1u : 0u;
         for (uint32_t j = 0; j < cmax; j += 16) {
-            uint4 e[8];
+            uint2 e[16];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) e[q] = src[min((j >> 1) + (uint32_t)q, qlast)];
+            for (int q = 0; q < 16; ++q) e[q] = src[16 * min(j + (uint32_t)q, last)];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                fn(make_uint2(e[q].x, e[q].y), j + 2 * q < c);
-                fn(make_uint2(e[q].z, e[q].w), j + 2 * q + 1 < c);
-            }
+            for (int q = 0; q < 16; ++q) fn(e[q], j + q < c);
         }
     }
 }
@@ -857,19 +862,18 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
             }
             const uint32_t chunk = __shfl(off, 63);
             off = n + off - c;
-            const uint2 *src = lists + (int64_t)min(li, nlists - 1) * a.subcap;
-            // 16-byte loads, two pairs each, 8 in flight per lane (a list's
-            // capacity is a multiple of 8 pairs, so a load never leaves it)
+            const uint2 *src = lists + list_slot(min(li, nlists - 1), 0u, a.subcap);  // slot j at [16 j]
+            // 16 pairs in flight per lane; the lanes of a split read the same
+            // slot of their 16 lists, one 128-byte line; a load past the
+            // list's last pair re-reads that one
+            const uint32_t last = c > 0u ? c - 1u : 0u;
             for (uint32_t j = 0; j < cmax; j += 16) {
-                uint4 e[8];
+                uint2 e[16];
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    e[q] = j + 2 * q < c ? ((const uint4 *)src)[(j >> 1) + q] : make_uint4(0u, 0u, 0u, 0u);
+                for (int q = 0; q < 16; ++q) e[q] = src[16 * min(j + (uint32_t)q, last)];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    if (j + 2 * q < c) st[off + j + 2 * q] = make_uint2(e[q].x, e[q].y);
-                    if (j + 2 * q + 1 < c) st[off + j + 2 * q + 1] = make_uint2(e[q].z, e[q].w);
-                }
+                for (int q = 0; q < 16; ++q)
+                    if (j + q < c) st[off + j + q] = e[q];
             }
             n += chunk;
         }
@@ -944,7 +948,7 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
                 const uint32_t c = a.cnt[r * nlists + li];
                 for (uint32_t i0 = 0; i0 < c; i0 += kWave) {
                     const uint32_t i = i0 + lane;
-                    fn(i < c ? lists[(int64_t)li * a.subcap + i] : make_uint2(0u, 0u), i < c);
+                    fn(i < c ? lists[list_slot(li, i, a.subcap)] : make_uint2(0u, 0u), i < c);
                 }
             }
         } else {
