@@ -84,7 +84,8 @@ struct FusedScoreArgs {
     int32_t nsplit;           // block-range splits of the main pass
     int32_t split_len;        // blocks per split (multiple of 64)
     int32_t subcap;           // capacity of one lane's pair list (16 lists per row and split)
-    uint2 *buf;               // [rows][nsplit][16][subcap] (key, block)
+    uint2 *buf;               // [rows][nsplit] blocks of 16 lists x subcap (key, block) pairs; the 16
+                              // lists of a block interleaved slot by slot when nsplit >= 2
     uint32_t *cnt;            // [rows][nsplit][16] pairs per list (may exceed subcap: overflow)
     int32_t nsample;          // sampled blocks per row (one per 32)
     int32_t ssplit;           // sample-range splits

@@ -75,12 +75,16 @@ __device__ __forceinline__ float tau_float(uint32_t key) { return key == 0u ? -I
 
 __device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
-// A row's pair lists: 16 per split, the 16 of a split interleaved slot by slot
-// (pair j of list m at 16 j + m), so that a 128-byte line holds slot j of all
-// 16 and the lines a row keeps open while its lists grow are few enough for L2.
-__device__ __forceinline__ int64_t list_slot(int li, uint32_t j, int32_t subcap)
+// A row's pair lists: 16 per split.  With the block range split (short lists,
+// many rows' lists growing at once) the 16 lists of a split are interleaved slot
+// by slot (pair j of list m at 16 j + m): an append instruction's lanes of one
+// row at the same slot share a line, and the merge reads a row's lists in whole
+// lines.  With one split (long lists that fill out of step) each list is
+// contiguous (pair j of list m at subcap m + j) and fills its own lines.
+__host__ __device__ __forceinline__ bool lists_interleaved(int32_t nsplit) { return nsplit >= 2; }
+__device__ __forceinline__ int64_t list_slot(int li, uint32_t j, int32_t subcap, bool inter)
 {
-    return (int64_t)(li >> 4) * 16 * subcap + (int64_t)j * 16 + (li & 15);
+    return inter ? (int64_t)(li >> 4) * 16 * subcap + (int64_t)j * 16 + (li & 15) : (int64_t)li * subcap + j;
 }
 
 // The 16 x 4 x 128 query tile of a wave as MFMA A operands.
@@ -381,7 +385,7 @@ __global__ __launch_bounds__(256) void sample_threshold_kernel(FusedScoreArgs a)
 // 3. filter: grid (row tiles, splits).  Lane (mt, g, m) owns list m of row
 //    16*wave + 4*mt + g in this split and appends its pairs >= tau there.
 // ---------------------------------------------------------------------------
-template <bool FP8>
+template <bool FP8, bool INTER>  // INTER: lists_interleaved(a.nsplit)
 __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
 {
     __shared__ bf16_t keys[2][kFStep][kFKRow];
@@ -410,7 +414,8 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
         const uint32_t tk = a.tau[row0 + rc];  // issued unconditionally (clamped), then masked
         my_nc[mt] = __shfl(trow.nb, rw);
         my_seq[mt] = __shfl(trow.seq, rw);
-        my_list[mt] = a.buf + ((row0 + rc) * a.nsplit + split) * 16 * (int64_t)a.subcap + m;  // slot j at [16 j]
+        my_list[mt] = a.buf + ((row0 + rc) * a.nsplit + split) * 16 * (int64_t)a.subcap +
+                      (INTER ? m : m * (int64_t)a.subcap);  // pair j at [16 j] or [j]
         my_cnt[mt] = 0;
         // an empty row slot gets tau = +inf, so it never appends
         tauf[mt] = __uint_as_float((__float_as_uint(tau_float(tk)) & okm) | (0x7f800000u & ~okm));
@@ -465,7 +470,7 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
                         if (sc[mt][nt] >= tauf[mt]) {
-                            my_list[mt][16 * min(my_cnt[mt], cap_last)] =
+                            my_list[mt][(INTER ? 16 : 1) * min(my_cnt[mt], cap_last)] =
                                 make_uint2(pos_key(sc[mt][nt]), (uint32_t)(base + nt * 16 + m));
                             ++my_cnt[mt];
                         }
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
                         if (sc[mt][nt] >= tauf[mt] && 16 * nt < lr) {
-                            my_list[mt][16 * min(my_cnt[mt], cap_last)] =
+                            my_list[mt][(INTER ? 16 : 1) * min(my_cnt[mt], cap_last)] =
                                 make_uint2(pos_key(sc[mt][nt]), (uint32_t)(base + nt * 16 + m));
                             ++my_cnt[mt];
                         }
@@ -776,7 +781,7 @@ __device__ __forceinline__ void merge_staged(uint2 *st, uint32_t *h, uint32_t n,
 // order on every lane, so it may use wave-wide ballots.
 template <typename F>
 __device__ __forceinline__ void for_each_listed(const uint2 *__restrict__ lists, const uint32_t *__restrict__ cnt,
-                                                int nlists, int32_t subcap, F &&fn)
+                                                int nlists, int32_t subcap, bool inter, F &&fn)
 {
     const int lane = threadIdx.x & 63;
     for (int i0 = 0; i0 < nlists; i0 += kWave) {
@@ -784,16 +789,30 @@ __device__ __forceinline__ void for_each_listed(const uint2 *__restrict__ lists,
         const uint32_t c = li < nlists ? cnt[li] : 0u;
         uint32_t cmax = c;
         for (int o = 1; o < 64; o <<= 1) cmax = max(cmax, (uint32_t)__shfl_xor((int)cmax, o));
-        const uint2 *src = lists + list_slot(min(li, nlists - 1), 0u, subcap);  // slot j at [16 j]
+        const uint2 *src = lists + list_slot(min(li, nlists - 1), 0u, subcap, inter);
         // a load past the list's last pair re-reads that one (every load stays in
-        // the list, none needs a guard, so all 16 are issued together)
-        const uint32_t last = c > 0u ? c - 1u : 0u;
-        for (uint32_t j = 0; j < cmax; j += 16) {
-            uint2 e[16];
+        // the list, none needs a guard, so all of a round are issued together)
+        if (inter) {  // pair j at [16 j]
+            const uint32_t last = c > 0u ? c - 1u : 0u;
+            for (uint32_t j = 0; j < cmax; j += 16) {
+                uint2 e[16];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) e[q] = src[16 * min(j + (uint32_t)q, last)];
+                for (int q = 0; q < 16; ++q) e[q] = src[16 * min(j + (uint32_t)q, last)];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) fn(e[q], j + q < c);
+                for (int q = 0; q < 16; ++q) fn(e[q], j + q < c);
+            }
+        } else {  // pair j at [j]: 16-byte loads of two pairs
+            const uint32_t qlast = c > 0u ? (c - 1u) >> 1 : 0u;
+            for (uint32_t j = 0; j < cmax; j += 16) {
+                uint4 e[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) e[q] = ((const uint4 *)src)[min((j >> 1) + (uint32_t)q, qlast)];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    fn(make_uint2(e[q].x, e[q].y), j + 2 * q < c);
+                    fn(make_uint2(e[q].z, e[q].w), j + 2 * q + 1 < c);
+                }
+            }
         }
     }
 }
@@ -849,6 +868,7 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
     int mode = (overflow || total < (uint32_t)kk || kk > kStage) ? 2 : (total <= (uint32_t)kStage ? 0 : 1);
     if (lane == 0) a.mode[r] = mode == 0 ? kMergeStaged : mode == 1 ? kMergeListWalk : kMergeRecompute;
     const uint2 *lists = a.buf + (int64_t)r * nlists * a.subcap;
+    const bool inter = lists_interleaved(a.nsplit);
     uint32_t n = 0;
     if (mode == 0) {  // stage the pairs in LDS: 64 lists at a time, lane i copies list i
         for (int i0 = 0; i0 < nlists; i0 += kWave) {
@@ -862,18 +882,34 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
             }
             const uint32_t chunk = __shfl(off, 63);
             off = n + off - c;
-            const uint2 *src = lists + list_slot(min(li, nlists - 1), 0u, a.subcap);  // slot j at [16 j]
-            // 16 pairs in flight per lane; the lanes of a split read the same
-            // slot of their 16 lists, one 128-byte line; a load past the
-            // list's last pair re-reads that one
-            const uint32_t last = c > 0u ? c - 1u : 0u;
-            for (uint32_t j = 0; j < cmax; j += 16) {
-                uint2 e[16];
+            const uint2 *src = lists + list_slot(min(li, nlists - 1), 0u, a.subcap, inter);
+            if (inter) {
+                // pair j at [16 j]: 16 pairs in flight per lane; the lanes of a split read
+                // the same slot of their 16 lists, one 128-byte line; a load past the
+                // list's last pair re-reads that one
+                const uint32_t last = c > 0u ? c - 1u : 0u;
+                for (uint32_t j = 0; j < cmax; j += 16) {
+                    uint2 e[16];
 #pragma unroll
-                for (int q = 0; q < 16; ++q) e[q] = src[16 * min(j + (uint32_t)q, last)];
+                    for (int q = 0; q < 16; ++q) e[q] = src[16 * min(j + (uint32_t)q, last)];
 #pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    if (j + q < c) st[off + j + q] = e[q];
+                    for (int q = 0; q < 16; ++q)
+                        if (j + q < c) st[off + j + q] = e[q];
+                }
+            } else {
+                // pair j at [j]: 16-byte loads, two pairs each, 8 in flight per lane
+                // (a list's capacity is a multiple of 8 pairs, so a load never leaves it)
+                for (uint32_t j = 0; j < cmax; j += 16) {
+                    uint4 e[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        e[q] = j + 2 * q < c ? ((const uint4 *)src)[(j >> 1) + q] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        if (j + 2 * q < c) st[off + j + 2 * q] = make_uint2(e[q].x, e[q].y);
+                        if (j + 2 * q + 1 < c) st[off + j + 2 * q + 1] = make_uint2(e[q].z, e[q].w);
+                    }
+                }
             }
             n += chunk;
         }
@@ -888,7 +924,7 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
         for (uint32_t i = (uint32_t)lane; i < kPreBins; i += kWave) hist[i] = 0u;
         wave_fence();
         const uint32_t *lcnt = a.cnt + r * nlists;
-        for_each_listed(lists, lcnt, nlists, a.subcap, [&](uint2 e, bool v) {
+        for_each_listed(lists, lcnt, nlists, a.subcap, inter, [&](uint2 e, bool v) {
             if (v) atomicAdd(&hist[(e.x >> kPreShift) & (kPreBins - 1u)], 1u);
         });
         wave_fence();
@@ -915,7 +951,7 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
         if (staged <= (uint32_t)kStage) {
             const uint32_t kmin = 0x80000000u | (bin << kPreShift);
             uint32_t nst = 0;
-            for_each_listed(lists, lcnt, nlists, a.subcap, [&](uint2 e, bool v) {
+            for_each_listed(lists, lcnt, nlists, a.subcap, inter, [&](uint2 e, bool v) {
                 const bool take = v && e.x >= kmin;
                 const uint64_t tb = __ballot(take);
                 if (take) st[nst + (uint32_t)__popcll(tb & lt)] = e;
@@ -948,7 +984,7 @@ __global__ __launch_bounds__(256, 2) void select_merge_kernel(FusedScoreArgs a, 
                 const uint32_t c = a.cnt[r * nlists + li];
                 for (uint32_t i0 = 0; i0 < c; i0 += kWave) {
                     const uint32_t i = i0 + lane;
-                    fn(i < c ? lists[list_slot(li, i, a.subcap)] : make_uint2(0u, 0u), i < c);
+                    fn(i < c ? lists[list_slot(li, i, a.subcap, inter)] : make_uint2(0u, 0u), i < c);
                 }
             }
         } else {
@@ -1153,12 +1189,19 @@ void launch_score_fused(const FusedScoreArgs &a, int32_t *sel_blocks, int32_t *s
         else
             QSA_LAUNCH("sample_threshold", sample_threshold_kernel<8>, dim3((unsigned)((a.rows + 3) / 4)), dim3(256),
                        0, stream, a);
-        if (fp8)
-            QSA_LAUNCH("score_filter_fp8", score_filter_kernel<true>, dim3(tiles, (unsigned)a.nsplit), dim3(256), 0,
-                       stream, a);
+        const bool inter = lists_interleaved(a.nsplit);
+        if (fp8 && inter)
+            QSA_LAUNCH("score_filter_fp8", (score_filter_kernel<true, true>), dim3(tiles, (unsigned)a.nsplit),
+                       dim3(256), 0, stream, a);
+        else if (fp8)
+            QSA_LAUNCH("score_filter_fp8", (score_filter_kernel<true, false>), dim3(tiles, (unsigned)a.nsplit),
+                       dim3(256), 0, stream, a);
+        else if (inter)
+            QSA_LAUNCH("score_filter", (score_filter_kernel<false, true>), dim3(tiles, (unsigned)a.nsplit),
+                       dim3(256), 0, stream, a);
         else
-            QSA_LAUNCH("score_filter", score_filter_kernel<false>, dim3(tiles, (unsigned)a.nsplit), dim3(256), 0,
-                       stream, a);
+            QSA_LAUNCH("score_filter", (score_filter_kernel<false, false>), dim3(tiles, (unsigned)a.nsplit),
+                       dim3(256), 0, stream, a);
     }
     const dim3 mgrid((unsigned)((a.rows + kMergeWaves - 1) / kMergeWaves)), mblock(kMergeWaves * kWave);
     if (fp8)
