@@ -403,6 +403,12 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
     int64_t my_nc[4];
     int32_t my_seq[4];
     uint2 *my_list[4];
+    // the next slot of each list (kept while the lists have room), a global
+    // address so its stores stay global stores (a flat store would also count
+    // against the LDS waits)
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(1))) u32x2_t global_pair;
+    global_pair *my_ptr[4];
     uint32_t my_cnt[4];
     float tauf[4];
     const TileRows trow = tile_rows(a, row0, nrows);
@@ -416,6 +422,7 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
         my_seq[mt] = __shfl(trow.seq, rw);
         my_list[mt] = a.buf + ((row0 + rc) * a.nsplit + split) * 16 * (int64_t)a.subcap +
                       (INTER ? m : m * (int64_t)a.subcap);  // pair j at [16 j] or [j]
+        my_ptr[mt] = (global_pair *)my_list[mt];
         my_cnt[mt] = 0;
         // an empty row slot gets tau = +inf, so it never appends
         tauf[mt] = __uint_as_float((__float_as_uint(tau_float(tk)) & okm) | (0x7f800000u & ~okm));
@@ -464,14 +471,19 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
             // a pair >= tau goes to the lane's list; past the list's capacity
             // the last slot is overwritten but the count goes on, so the
             // merge sees the overflow (and recomputes the row)
-            if (base + kFStep <= lim_min) {  // every block of the step is visible to every row of the wave
+            // A lane appends at most 4 pairs per list in a step: while every list
+            // of the wave has room for 4 more, the appends go to a running slot
+            // pointer with no capacity clamp.
+            const uint32_t cnt_hi = max(max(my_cnt[0], my_cnt[1]), max(my_cnt[2], my_cnt[3]));
+            const bool roomy = __ballot(cnt_hi + 4u > (uint32_t)a.subcap) == 0ull;
+            if (roomy && base + kFStep <= lim_min) {  // and every block of the step is visible to every row
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
                         if (sc[mt][nt] >= tauf[mt]) {
-                            my_list[mt][(INTER ? 16 : 1) * min(my_cnt[mt], cap_last)] =
-                                make_uint2(pos_key(sc[mt][nt]), (uint32_t)(base + nt * 16 + m));
+                            *my_ptr[mt] = u32x2_t{pos_key(sc[mt][nt]), (uint32_t)(base + nt * 16 + m)};
+                            my_ptr[mt] += INTER ? 16 : 1;
                             ++my_cnt[mt];
                         }
             } else {
@@ -486,6 +498,7 @@ __global__ __launch_bounds__(256, 2) void score_filter_kernel(FusedScoreArgs a)
                                 make_uint2(pos_key(sc[mt][nt]), (uint32_t)(base + nt * 16 + m));
                             ++my_cnt[mt];
                         }
+                    my_ptr[mt] = (global_pair *)(my_list[mt] + (INTER ? 16 : 1) * min(my_cnt[mt], cap_last));
                 }
             }
             __syncthreads();
