@@ -358,6 +358,46 @@ def test_attn_prefill_union_across_windows(gpu):
     np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (4, 4)])
+def test_attn_prefill_tails_share_blocks_and_skip_unwritten(gpu, Hq, Hkv):
+    # runs of consecutive rows (a row's tail block is a kept, fully visible
+    # block of the rows 4 positions later), rows at the first positions (a
+    # tail and nothing else), two sequences; every cache position past a
+    # sequence's last row holds NaN, as memory never written may: no row
+    # attends those tokens, and none of them may reach the result
+    rng = np.random.default_rng(37)
+    B, L, k = 2, 4 * 600 + 3, 64
+    runs = [(0, np.arange(0, 7)), (0, np.arange(1500, 1540)), (1, np.arange(900, 925)),
+            (1, np.arange(2, 4)), (0, np.array([2001]))]
+    seq = np.concatenate([np.full(len(p_), s_, np.int32) for s_, p_ in runs])
+    pos = np.concatenate([p_ for _, p_ in runs]).astype(np.int32)
+    R = len(pos)
+    sel = np.full((R, k), -1, np.int32)
+    cnt = np.zeros(R, np.int32)
+    for r, t in enumerate(pos):
+        nc = (int(t) + 1) // 4
+        n = min(k, nc)
+        if n:
+            recent = np.arange(max(0, nc - 6), nc)          # the blocks holding earlier rows' tails
+            rest = rng.permutation(np.setdiff1d(np.arange(nc), recent))[: max(0, n - len(recent))]
+            sel[r, :n] = np.sort(np.concatenate([recent, rest]))[:n]
+        cnt[r] = n
+    q = synth.bf16_bits(rng.standard_normal((R, Hq, DIM)).astype(np.float32))
+    kf = rng.standard_normal((B, L, Hkv, DIM)).astype(np.float32)
+    vf = rng.standard_normal((B, L, Hkv, DIM)).astype(np.float32)
+    for b in range(B):
+        last = pos[seq == b].max()
+        kf[b, last + 1:] = np.nan
+        vf[b, last + 1:] = np.nan
+    kc, vc = synth.bf16_bits(kf), synth.bf16_bits(vf)
+    want, want_lse = oracle.sparse_attn_prefill(q, seq, pos, kc, vc, sel, cnt)
+    assert np.isfinite(synth.bf16_to_f32(want)).all()
+    out, lse = qsa.sparse_attn_prefill(dev(q, "bf16"), dev(seq, "i"), dev(pos, "i"), dev(kc, "bf16"),
+                                       dev(vc, "bf16"), dev(sel, "i"), dev(cnt, "i"))
+    assert_close_out(host(out), want, "bf16")
+    np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("Qn,Hq,Hkv,draft", [(1, 8, 1, False), (4, 8, 1, True), (2, 16, 2, True),
                                              (3, 4, 2, False), (2, 6, 2, True), (8, 8, 1, True)])
