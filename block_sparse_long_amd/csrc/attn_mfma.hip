@@ -92,8 +92,10 @@ struct alignas(16) UnionBuild {
     uint16_t wprefix[kWinWords];          // < kMaxUnionBlocks
 };
 struct alignas(16) UnionSmem {
-    uint16_t blk[kMaxUnionBlocks];        // union block i is block w0 + blk[i]
-    uint32_t mask2[kMaxUnionBlocks / 2];  // union block i: bits 16(i%2) + r of word i/2, r = tile row keeping it
+    // union block i is block w0 + blk[i]; slot kMaxUnionBlocks takes the
+    // stores of entries that are not kept
+    uint16_t blk[kMaxUnionBlocks + 8];
+    uint32_t mask2[kMaxUnionBlocks / 2 + 4];  // union block i: bits 16(i%2) + r of word i/2, r = tile row keeping it
     uint32_t count;
 };
 
@@ -573,7 +575,13 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
         s_last[t] = c > 0 ? a.sel_blocks[r * a.top_k + c - 1] : -1;
     }
     __syncthreads();
-    constexpr int kSelPerThread = kMaxUnionBlocks / 256;
+    // the union build's view of the selections: thread t reads row er = t / 16
+    // of the tile (ranks below ecnt are kept, 0 for a row not being built)
+    static_assert(256 / 16 == kMaxTileRows, "16 threads per tile row");
+    constexpr int kEntBatch = 32;  // entries a thread reads per batch (512 ranks per row)
+    const int er = t >> 4, ei = t & 15;
+    const __amdgpu_buffer_rsrc_t sel_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.sel_blocks + row0 * a.top_k), 0, nrows * a.top_k * 4, 0x00020000);
     uint32_t todo = nrows >= 32 ? 0xffffffffu : ((1u << nrows) - 1u);
     while (todo) {  // rows of one sequence at a time (uniform across the workgroup)
         const int first = __builtin_ctz(todo);
@@ -582,6 +590,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
         for (int r = first; r < nrows; ++r)
             if (((todo >> r) & 1u) && s_seq[r] == seq) active |= 1u << r;
         todo &= ~active;
+        const uint32_t ecnt = er < nrows && ((active >> er) & 1u) ? (uint32_t)s_cnt[er] : 0u;
         const int64_t seq_off = a.page_table ? 0 : (int64_t)seq * a.kv_seq_stride;
         const KV *kbase = (const KV *)a.k_cache + seq_off + (int64_t)kvh * DIM;
         const KV *vbase = (const KV *)a.v_cache + seq_off + (int64_t)kvh * DIM;
@@ -591,37 +600,37 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
             if ((active >> r) & 1u) hi_blk = max(hi_blk, s_last[r] + 1);
         for (int32_t w0 = 0; w0 < hi_blk; w0 += kWin) {
             // ---- union of the active rows' kept blocks in [w0, w0 + kWin).
-            // Entry idx = r top_k + i of the tile's selections (row r, rank
-            // i) sits at sel_blocks[row0 top_k + idx].  Each of the two
-            // passes below reads a thread's entries t + 256 j together; an
-            // entry's row is floor((idx + 0.5) / top_k) in float, exact for
-            // idx, top_k <= 8,192 (the quotient's rounding error is below
-            // 2^-10 / top_k, its distance to an integer at least 0.5 / top_k) ----
-            const int32_t nent = nrows * a.top_k;
-            const float inv_k = 1.0f / (float)a.top_k;
-            const int32_t *sel = a.sel_blocks + row0 * a.top_k;
-            // calls fn(block - w0, row) for the thread's entries kept by an
-            // active row inside the window
-            auto for_entries = [&](auto &&fn) {
-                // the entries' addresses and rows are computed here, per
-                // pass, not hoisted to the kernel's start and held across it
-                int32_t tt = t;
-                asm volatile("" : "+v"(tt));
-                int32_t eb[kSelPerThread];
+            // Thread t takes row er = t / 16 of the tile and its ranks
+            // i0 + t % 16 + 16 j (j < 32) of each batch of 512 ranks, so all
+            // of a thread's entries share one row and one count.  A batch's
+            // 32 entries are buffer loads in flight together (past the
+            // tile's entries they read 0; a rank at or past the row's count
+            // is not kept), and an entry that is not kept updates nothing
+            // (an OR of 0, a store to a spare slot): no pass branches. ----
+            // pk[j] = (block - w0) | kept << 16
+            auto load_batch = [&](int32_t i0, uint32_t(&pk)[kEntBatch]) {
+                // computed here, per pass, not hoisted to the kernel's start and held across it
+                int32_t vo = (er * a.top_k + i0 + ei) * 4;
+                asm volatile("" : "+v"(vo));
+                int32_t eb[kEntBatch];
 #pragma unroll
-                for (int j = 0; j < kSelPerThread; ++j) eb[j] = sel[min(tt + 256 * j, nent - 1)] - w0;
+                for (int j = 0; j < kEntBatch; ++j)
+                    eb[j] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(sel_rsrc, vo + 64 * j, 0, 0) - w0;
 #pragma unroll
-                for (int j = 0; j < kSelPerThread; ++j) {
-                    const int32_t idx = tt + 256 * j;
-                    const int32_t r = min((int32_t)(((float)idx + 0.5f) * inv_k), kMaxTileRows - 1);
-                    if (idx < nent && ((active >> r) & 1u) && idx - r * a.top_k < s_cnt[r] && eb[j] >= 0 &&
-                        eb[j] < kWin)
-                        fn(eb[j], r);
+                for (int j = 0; j < kEntBatch; ++j) {
+                    const bool ok = (uint32_t)(i0 + ei + 16 * j) < ecnt && (uint32_t)eb[j] < (uint32_t)kWin;
+                    pk[j] = ((uint32_t)eb[j] & 0xffffu) | ((uint32_t)ok << 16);
                 }
             };
             for (int i = t; i < kWinWords; i += blockDim.x) ub.bitmap[i] = 0u;
             __syncthreads();
-            for_entries([&](int32_t b, int32_t) { atomicOr(&ub.bitmap[b >> 5], 1u << (b & 31)); });
+            for (int32_t i0 = 0; i0 < a.top_k; i0 += 16 * kEntBatch) {
+                uint32_t pk[kEntBatch];
+                load_batch(i0, pk);
+#pragma unroll
+                for (int j = 0; j < kEntBatch; ++j)
+                    atomicOr(&ub.bitmap[(pk[j] & 0xffffu) >> 5], ((pk[j] >> 16) & 1u) << (pk[j] & 31u));
+            }
             __syncthreads();
             {   // exclusive prefix of popcounts over the words (8 words per thread)
                 constexpr int per = kWinWords / 256;
@@ -649,12 +658,28 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
             __syncthreads();
             // each entry's union index: its word's prefix plus the set bits below it;
             // entries of several rows with one block store the same list value
-            for_entries([&](int32_t b, int32_t r) {
-                const uint32_t word = ub.bitmap[b >> 5];
-                const uint32_t idx = ub.wprefix[b >> 5] + __popc(word & ((1u << (b & 31)) - 1u));
-                us.blk[idx] = (uint16_t)b;
-                atomicOr(&us.mask2[idx >> 1], 1u << (r + 16 * (idx & 1u)));
-            });
+            for (int32_t i0 = 0; i0 < a.top_k; i0 += 16 * kEntBatch) {
+                uint32_t pk[kEntBatch];
+                load_batch(i0, pk);
+                constexpr int kHalf = kEntBatch / 2;  // half the entries' LDS reads in flight at a time
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t wd[kHalf], pf[kHalf];
+#pragma unroll
+                    for (int j = 0; j < kHalf; ++j) {
+                        const uint32_t w = (pk[h * kHalf + j] & 0xffffu) >> 5;
+                        wd[j] = ub.bitmap[w];
+                        pf[j] = ub.wprefix[w];
+                    }
+#pragma unroll
+                    for (int j = 0; j < kHalf; ++j) {
+                        const uint32_t e = pk[h * kHalf + j], b = e & 0xffffu, ok = (e >> 16) & 1u;
+                        const uint32_t idx = ok ? pf[j] + __popc(wd[j] & ((1u << (b & 31u)) - 1u)) : kMaxUnionBlocks;
+                        us.blk[idx] = (uint16_t)b;
+                        atomicOr(&us.mask2[idx >> 1], ok << (er + 16 * (idx & 1u)));
+                    }
+                }
+            }
             __syncthreads();
             const int32_t nu = (int32_t)us.count;
             // ---- the union's blocks, kChB per chunk; chunk c+1's gather is in
