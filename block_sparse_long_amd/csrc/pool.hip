@@ -64,12 +64,21 @@ __global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ ra
     if (w >= total) return;
     const int64_t s = w / nblk;
     const int64_t b = block_begin + w % nblk;
+    const double freq = rf.f[lane];  // loaded ahead of the keys: the angle is formed while they are in flight
     const T *src = raw + s * raw_stride + b * (kBlock * kDim);
+    float vx[kBlock], vy[kBlock];
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) {
+        vx[i] = load_f32(src + i * kDim + lane);
+        vy[i] = load_f32(src + i * kDim + kHalf + lane);
+    }
+    double c, sn;
+    rope_angle(kBlock * b, freq, c, sn);
     float x = 0.0f, y = 0.0f;
 #pragma unroll
     for (int i = 0; i < kBlock; ++i) {  // FP32 sum in token order, then times 1/4
-        x += load_f32(src + i * kDim + lane);
-        y += load_f32(src + i * kDim + kHalf + lane);
+        x += vx[i];
+        y += vy[i];
     }
     x *= 0.25f;
     y *= 0.25f;
@@ -84,7 +93,7 @@ __global__ __launch_bounds__(256) void pool_rope_kernel(const T *__restrict__ ra
             dy *= (double)norm_w[kHalf + lane];
         }
     }
-    if (!(flags & kFlagNoRope)) rope_pair(dx, dy, kBlock * b, rf.f[lane]);
+    if (!(flags & kFlagNoRope)) rope_apply(dx, dy, c, sn);
     T *dst = pooled + key_offset(kp, pooled_stride, s, b);
     store_f64(dst + lane, dx);
     store_f64(dst + kHalf + lane, dy);
@@ -109,12 +118,21 @@ __global__ __launch_bounds__(256) void pool_rope_fp8_kernel(const T *__restrict_
     if (w >= total) return;
     const int64_t s = w / nblk;
     const int64_t b = block_begin + w % nblk;
+    const double freq = rf.f[lane];  // loaded ahead of the keys: the angle is formed while they are in flight
     const T *src = raw + s * raw_stride + b * (kBlock * kDim);
+    float vx[kBlock], vy[kBlock];
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) {
+        vx[i] = load_f32(src + i * kDim + lane);
+        vy[i] = load_f32(src + i * kDim + kHalf + lane);
+    }
+    double c, sn;
+    rope_angle(kBlock * b, freq, c, sn);
     float x = 0.0f, y = 0.0f;
 #pragma unroll
     for (int i = 0; i < kBlock; ++i) {  // FP32 sum in token order, then times 1/4
-        x += load_f32(src + i * kDim + lane);
-        y += load_f32(src + i * kDim + kHalf + lane);
+        x += vx[i];
+        y += vy[i];
     }
     x *= 0.25f;
     y *= 0.25f;
@@ -125,7 +143,7 @@ __global__ __launch_bounds__(256) void pool_rope_fp8_kernel(const T *__restrict_
         dx *= inv;
         dy *= inv;
     }
-    if (!(flags & kFlagNoRope)) rope_pair(dx, dy, kBlock * b, rf.f[lane]);
+    if (!(flags & kFlagNoRope)) rope_apply(dx, dy, c, sn);
     const float fx = (float)dx, fy = (float)dy;
     const float amax = wave_max(fmaxf(fabsf(fx), fabsf(fy)));
     const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
@@ -157,16 +175,26 @@ __global__ __launch_bounds__(256) void rope_query_kernel(const T *__restrict__ q
             for (int64_t i = lane; i < zero_per_row; i += kWave) z[i] = 0u;
         }
     }
+    // the position and the frequency are loaded first, so the angle's sine
+    // and cosine are formed while the query's 8 loads are in flight
+    const int64_t pos = row_pos[r];
+    const double freq = rf.f[lane];
     const T *src = q + r * kIdxHeads * kDim;
+    float fx[kIdxHeads], fy[kIdxHeads];
+#pragma unroll
+    for (int h = 0; h < kIdxHeads; ++h) {
+        fx[h] = load_f32(src + h * kDim + lane);
+        fy[h] = load_f32(src + h * kDim + kHalf + lane);
+    }
     double dx[kIdxHeads], dy[kIdxHeads];
 #pragma unroll
     for (int h = 0; h < kIdxHeads; ++h) {
-        dx[h] = load_f32(src + h * kDim + lane);
-        dy[h] = load_f32(src + h * kDim + kHalf + lane);
+        dx[h] = fx[h];
+        dy[h] = fy[h];
     }
+    double c, s;
+    rope_angle(pos, freq, c, s);  // formed on every path, so its loads stay ahead of the query's
     if (!(flags & kFlagNoRope)) {
-        double c, s;
-        rope_angle(row_pos[r], rf.f[lane], c, s);
 #pragma unroll
         for (int h = 0; h < kIdxHeads; ++h) rope_apply(dx[h], dy[h], c, s);
     }
