@@ -77,9 +77,14 @@ void prof_begin(const char *name, hipStream_t stream)
 void prof_end(hipStream_t stream)
 {
     hipEvent_t stop = take_event();
-    if (!g_pending_start || !stop) return;
-    (void)hipEventRecord(stop, stream);
     std::lock_guard<std::mutex> lock(g_prof_mutex);
+    if (!g_pending_start || !stop) {  // no record: an event that was taken goes back to the pool
+        if (g_pending_start) g_free_events.push_back(g_pending_start);
+        if (stop) g_free_events.push_back(stop);
+        g_pending_start = nullptr;
+        return;
+    }
+    (void)hipEventRecord(stop, stream);
     g_records.push_back({g_pending_name, g_pending_start, stop});
     g_pending_start = nullptr;
 }
