@@ -24,10 +24,12 @@
 namespace qsa {
 
 constexpr int kAC = kAttnChunk;   // positions per chunk
-constexpr int kKPad = kDim + 1;   // LDS row stride of K (bank-conflict free column reads)
+// LDS row stride of K: 16-byte rows, and 4 banks of skew per row, so the 16
+// lanes of a quarter-wave reading 16 bytes each of 16 rows hit all 64 banks once
+constexpr int kKPad = kDim + 4;
 
 template <typename T, int MAXQ>
-struct AttnSmem {
+struct alignas(16) AttnSmem {
     float q[MAXQ][kDim];
     float k[kAC][kKPad];
     float v[kAC][kDim];
@@ -45,42 +47,51 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<T, MAXQ> &sm, const T *__res
                                            int nq, float scale, float (&o)[MAXQ / 2])
 {
     const int t = threadIdx.x;
-    // gather K/V rows: thread t -> row t/4, dims [32*(t%4), +32)
+    // gather K/V rows: thread t -> row t/4, dims [32*(t%4), +32); every load of
+    // the thread is issued before its LDS stores, which are 16 bytes each
     {
         const int p = t >> 2, d0 = (t & 3) * 32;
         if (p < n) {
             const T *ks = kbase + sm.pos[p] * row_stride + d0;
             const T *vs = vbase + sm.pos[p] * row_stride + d0;
+            float kf[32], vf[32];
 #pragma unroll
             for (int i = 0; i < 32; i += 8) {
-                float kf[8], vf[8];
-                load8(ks + i, kf);
-                load8(vs + i, vf);
+                load8(ks + i, kf + i);
+                load8(vs + i, vf + i);
+            }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    sm.k[p][d0 + i + e] = kf[e];
-                    sm.v[p][d0 + i + e] = vf[e];
-                }
+            for (int i = 0; i < 32; i += 4) {
+                *(float4 *)&sm.k[p][d0 + i] = make_float4(kf[i], kf[i + 1], kf[i + 2], kf[i + 3]);
+                *(float4 *)&sm.v[p][d0 + i] = make_float4(vf[i], vf[i + 1], vf[i + 2], vf[i + 3]);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                sm.k[p][d0 + i] = 0.0f;
-                sm.v[p][d0 + i] = 0.0f;
+            for (int i = 0; i < 32; i += 4) {
+                *(float4 *)&sm.k[p][d0 + i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                *(float4 *)&sm.v[p][d0 + i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
         }
     }
     __syncthreads();
-    // logits: lane -> position p, wave w -> queries w, w+4, ...
+    // logits: lane -> position p, wave w -> queries w, w+4, ...; four dims per
+    // LDS read, summed in dim order
     {
         const int p = t & 63, w = t >> 6;
         float acc[MAXQ / 4];
 #pragma unroll
         for (int i = 0; i < MAXQ / 4; ++i) acc[i] = 0.0f;
-        for (int d = 0; d < kDim; ++d) {
-            const float kv = sm.k[p][d];
+#pragma unroll 4
+        for (int d = 0; d < kDim; d += 4) {
+            const float4 kv = *(const float4 *)&sm.k[p][d];
 #pragma unroll
-            for (int i = 0; i < MAXQ / 4; ++i) acc[i] = fmaf(kv, sm.q[w + 4 * i][d], acc[i]);
+            for (int i = 0; i < MAXQ / 4; ++i) {
+                const float4 qv = *(const float4 *)&sm.q[w + 4 * i][d];
+                acc[i] = fmaf(kv.x, qv.x, acc[i]);
+                acc[i] = fmaf(kv.y, qv.y, acc[i]);
+                acc[i] = fmaf(kv.z, qv.z, acc[i]);
+                acc[i] = fmaf(kv.w, qv.w, acc[i]);
+            }
         }
         const int64_t pp = sm.pos[p < n ? p : 0];
 #pragma unroll
@@ -110,7 +121,9 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<T, MAXQ> &sm, const T *__res
         }
     }
     __syncthreads();
-    // P.V: thread -> dim d, half h2 -> queries h2, h2+2, ...
+    // P.V: thread -> dim d, half h2 -> queries h2, h2+2, ...; the weights of
+    // four positions per LDS read (past position n both the weights and V are
+    // 0, so the last group of four adds exact zeros)
     {
         const int d = t & 127, h2 = t >> 7;
 #pragma unroll
@@ -118,10 +131,17 @@ __device__ __forceinline__ void attn_chunk(AttnSmem<T, MAXQ> &sm, const T *__res
             const int qi = h2 + 2 * i;
             if (qi < nq) o[i] *= sm.alpha[qi];
         }
-        for (int p = 0; p < n; ++p) {
-            const float vv = sm.v[p][d];
+#pragma unroll 2
+        for (int p = 0; p < n; p += 4) {
+            const float v0 = sm.v[p][d], v1 = sm.v[p + 1][d], v2 = sm.v[p + 2][d], v3 = sm.v[p + 3][d];
 #pragma unroll
-            for (int i = 0; i < MAXQ / 2; ++i) o[i] = fmaf(sm.w[h2 + 2 * i][p], vv, o[i]);
+            for (int i = 0; i < MAXQ / 2; ++i) {
+                const float4 wv = *(const float4 *)&sm.w[h2 + 2 * i][p];
+                o[i] = fmaf(wv.x, v0, o[i]);
+                o[i] = fmaf(wv.y, v1, o[i]);
+                o[i] = fmaf(wv.z, v2, o[i]);
+                o[i] = fmaf(wv.w, v3, o[i]);
+            }
         }
     }
     __syncthreads();
@@ -284,7 +304,10 @@ void launch_attn_prefill(const AttnArgs &a, bool bf16, hipStream_t stream)
 {
     const dim3 grid(1, (unsigned)((int64_t)a.n_sel * a.Hkv)), block(256);
     const int nq = a.q_per_sel * (a.Hq / a.Hkv);
-    if (nq <= 16) {
+    if (nq <= 8) {
+        if (bf16) QSA_LAUNCH("attn_prefill", (attn_kernel<bf16_t, 8, false>), grid, block, 0, stream, a);
+        else QSA_LAUNCH("attn_prefill", (attn_kernel<float, 8, false>), grid, block, 0, stream, a);
+    } else if (nq <= 16) {
         if (bf16) QSA_LAUNCH("attn_prefill", (attn_kernel<bf16_t, 16, false>), grid, block, 0, stream, a);
         else QSA_LAUNCH("attn_prefill", (attn_kernel<float, 16, false>), grid, block, 0, stream, a);
     } else {
@@ -297,7 +320,10 @@ void launch_attn_decode(const AttnArgs &a, bool bf16, hipStream_t stream)
 {
     const dim3 grid((unsigned)a.nsplit, (unsigned)((int64_t)a.n_sel * a.Hkv)), block(256);
     const int nq = a.q_per_sel * (a.Hq / a.Hkv);
-    if (nq <= 16) {
+    if (nq <= 8) {
+        if (bf16) QSA_LAUNCH("attn_decode", (attn_kernel<bf16_t, 8, true>), grid, block, 0, stream, a);
+        else QSA_LAUNCH("attn_decode", (attn_kernel<float, 8, true>), grid, block, 0, stream, a);
+    } else if (nq <= 16) {
         if (bf16) QSA_LAUNCH("attn_decode", (attn_kernel<bf16_t, 16, true>), grid, block, 0, stream, a);
         else QSA_LAUNCH("attn_decode", (attn_kernel<float, 16, true>), grid, block, 0, stream, a);
     } else {
