@@ -7,7 +7,9 @@ At 4096 the fused scorer's sampled threshold rests on more candidates than
 its lanes keep, so every visible block is listed and the rows overflow the
 merge's stage; the prefill attention fits only two rows' selections per tile,
 and decode runs 257 splits.  Rows whose visible blocks number fewer than
-top_k keep them all.  Tolerances are those of the other parity tests.
+top_k keep them all.  Also the largest query group (QSA_MAX_QUERY_GROUP = 64
+queries on one KV head and one selection) in prefill and decode, at head dims
+128 and 256.  Tolerances are those of the other parity tests.
 """
 import numpy as np
 import pytest
@@ -120,6 +122,62 @@ def test_attn_decode_extreme_k(gpu, k, dtype, Qn, draft):
     q = _store(rng.standard_normal((B, Qn, Hq, DIM)), dtype)
     kc = _store(rng.standard_normal((B, L, Hkv, DIM)), dtype)
     vc = _store(rng.standard_normal((B, L, Hkv, DIM)), dtype)
+    want, want_lse = oracle.sparse_attn_decode(q, rp, kc, vc, sel, cnt, ts)
+    out, lse = qsa.sparse_attn_decode(dev(q, dtype), dev(rp, "i"), dev(kc, dtype), dev(vc, dtype), dev(sel, "i"),
+                                      dev(cnt, "i"), None if ts is None else dev(ts, "i"))
+    assert_close_out(host(out), want, dtype)
+    np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
+
+
+# ---------------------------------------------------------------------------
+# the largest query group the C-ABI accepts: QSA_MAX_QUERY_GROUP = 64 queries
+# share one KV head and one selection (64 query heads per KV head, or decode
+# rows x heads = 64)
+# ---------------------------------------------------------------------------
+
+MAX_GROUP = 64
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,dtype", [(128, 64, 1, "bf16"), (128, 128, 2, "bf16"), (128, 64, 1, "f32"),
+                                            (256, 64, 1, "bf16")])
+def test_attn_prefill_max_query_group(gpu, D, Hq, Hkv, dtype):
+    assert Hq // Hkv == MAX_GROUP
+    rng = np.random.default_rng(80 + D + Hq)
+    L, R, k = 4 * 500 + 3, 19, 48
+    pos = np.sort(rng.choice(L, R, replace=False)).astype(np.int32)
+    pos[:3] = [1, 4 * k - 1, L - 1]
+    pos = np.sort(pos)
+    seq = np.zeros(R, np.int32)
+    sel, cnt = _selection(rng, pos, k)
+    q = _store(rng.standard_normal((R, Hq, D)), dtype)
+    kc = _store(rng.standard_normal((1, L, Hkv, D)), dtype)
+    vc = _store(rng.standard_normal((1, L, Hkv, D)), dtype)
+    want, want_lse = oracle.sparse_attn_prefill(q, seq, pos, kc, vc, sel, cnt)
+    out, lse = qsa.sparse_attn_prefill(dev(q, dtype), dev(seq, "i"), dev(pos, "i"), dev(kc, dtype), dev(vc, dtype),
+                                       dev(sel, "i"), dev(cnt, "i"))
+    assert_close_out(host(out), want, dtype)
+    np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("D,Qn,Hq,Hkv,dtype,draft", [(128, 1, 64, 1, "bf16", False), (128, 4, 16, 1, "bf16", True),
+                                                     (128, 1, 128, 2, "f32", False), (256, 2, 32, 1, "bf16", True)])
+def test_attn_decode_max_query_group(gpu, D, Qn, Hq, Hkv, dtype, draft):
+    assert Qn * (Hq // Hkv) == MAX_GROUP
+    rng = np.random.default_rng(90 + D + Qn * Hq)
+    B, ctx, k = 3, 4 * 700 + 2, 96
+    L = ctx + (Qn if draft else 0)
+    if draft:
+        rp = (ctx + np.tile(np.arange(Qn), (B, 1))).astype(np.int32)
+        ts = np.full(B, 4 * (ctx // 4), np.int32)
+        anchor = np.full(B, ctx - 1, np.int32)
+    else:
+        rp = rng.integers(4 * k, ctx, size=(B, Qn)).astype(np.int32)
+        ts = None
+        anchor = rp.min(1)
+    sel, cnt = _selection(rng, anchor, k)
+    q = _store(rng.standard_normal((B, Qn, Hq, D)), dtype)
+    kc = _store(rng.standard_normal((B, L, Hkv, D)), dtype)
+    vc = _store(rng.standard_normal((B, L, Hkv, D)), dtype)
     want, want_lse = oracle.sparse_attn_decode(q, rp, kc, vc, sel, cnt, ts)
     out, lse = qsa.sparse_attn_decode(dev(q, dtype), dev(rp, "i"), dev(kc, dtype), dev(vc, dtype), dev(sel, "i"),
                                       dev(cnt, "i"), None if ts is None else dev(ts, "i"))
