@@ -672,6 +672,26 @@ size_t qsa_sparse_attn_decode_workspace_size(int32_t batch, int32_t q_per_seq, i
     return align256((size_t)batch * q_per_seq * Hq * nsplit * (D + 2) * sizeof(float));
 }
 
+// Splits of the MFMA decode attention.  One split of 16 kept blocks per
+// workgroup while the launch fits one round of resident workgroups (two per CU
+// at this kernel's register use, 256 CUs).  A launch of two to four rounds
+// whose splits, merged `rounds` at a time, fit one round gives each workgroup
+// that many 16-block groups instead (a workgroup's chunks then run back to
+// back, and the last rounds' start-up waits are gone); larger launches keep
+// one group per workgroup.  The kernel derives a split's length from the
+// count; the workspace of qsa_sparse_attn_decode_workspace_size (one split per
+// 16 blocks) covers any of these.
+constexpr int64_t kDecodeResident = 2 * 256;
+static int32_t attn_decode_mfma_splits(int32_t top_k, int32_t batch, int32_t Hkv)
+{
+    const int64_t n16 = attn_decode_splits(top_k) - 1;  // 16-block groups of the selection
+    const int64_t rows = (int64_t)batch * Hkv;
+    const int64_t rounds = ((n16 + 1) * rows + kDecodeResident - 1) / kDecodeResident;
+    if (rounds <= 1 || rounds > 4) return (int32_t)(n16 + 1);
+    const int64_t merged = (n16 + rounds - 1) / rounds + 1;
+    return merged * rows <= kDecodeResident ? (int32_t)merged : (int32_t)(n16 + 1);
+}
+
 static qsa_status_t attn_decode_impl(const void *q, const int32_t *row_pos, int32_t batch, int32_t q_per_seq,
                                     const int32_t *tail_start, const void *k_cache, const void *v_cache,
                                     int64_t kv_seq_stride, const int32_t *page_table, int64_t pt_stride,
@@ -727,7 +747,7 @@ static qsa_status_t attn_decode_impl(const void *q, const int32_t *row_pos, int3
     a.out = out;
     a.lse = lse;
     a.partial = (float *)workspace;
-    a.nsplit = attn_decode_splits(top_k);
+    a.nsplit = mfma ? attn_decode_mfma_splits(top_k, batch, Hkv) : attn_decode_splits(top_k);
     a.page_table = page_table;
     a.pt_stride = pt_stride;
     a.page_tokens = page_tokens;

@@ -800,8 +800,12 @@ __global__ __launch_bounds__(256, DIM == 256 ? 2 : 1) void attn_decode_mfma_kern
     const int32_t count = min(a.sel_count[s], a.top_k);
     const uint32_t all_rows = a.q_per_sel >= 32 ? 0xffffffffu : ((1u << a.q_per_sel) - 1u);
     if (split < a.nsplit - 1) {
-        const int32_t b0 = split * kSplitBlocks;
-        const int nb = max(0, min(kSplitBlocks, count - b0));
+        // the kept blocks in nsplit - 1 runs of whole 16-block groups: one group
+        // per split, or several when the caller gave fewer splits
+        const int32_t n16 = (a.top_k + kSplitBlocks - 1) / kSplitBlocks;
+        const int32_t sb = kSplitBlocks * ((n16 + a.nsplit - 2) / (a.nsplit - 1));
+        const int32_t b0 = split * sb;
+        const int nb = max(0, min(sb, count - b0));
         for (int c0 = 0; c0 < nb; c0 += G::kChB) {
             const int cb = min(G::kChB, nb - c0);
             if (t < G::kCh) {

@@ -183,3 +183,36 @@ def test_attn_decode_max_query_group(gpu, D, Qn, Hq, Hkv, dtype, draft):
                                       dev(cnt, "i"), None if ts is None else dev(ts, "i"))
     assert_close_out(host(out), want, dtype)
     np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
+
+
+# ---------------------------------------------------------------------------
+# decode launches of two to four rounds of workgroups: each workgroup takes
+# several 16-block groups of the selection (here 3: 48-block splits)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,Qn,Hq,Hkv,D,draft", [(40, 1, 8, 1, 128, False), (16, 2, 24, 2, 256, True),
+                                                 (24, 4, 8, 1, 128, True)])
+def test_attn_decode_merged_splits(gpu, B, Qn, Hq, Hkv, D, draft):
+    rng = np.random.default_rng(100 + B + D)
+    ctx, k = 4 * 700 + 1, 512
+    L = ctx + (Qn if draft else 0)
+    if draft:
+        rp = (ctx + np.tile(np.arange(Qn), (B, 1))).astype(np.int32)
+        ts = np.full(B, 4 * (ctx // 4), np.int32)
+        anchor = np.full(B, ctx - 1, np.int32)
+    else:
+        rp = rng.integers(4 * k, ctx, size=(B, Qn)).astype(np.int32)
+        ts = None
+        anchor = rp.min(1)
+    sel, cnt = _selection(rng, anchor, k)
+    for s_, c in zip(range(1, 8), [5, 47, 48, 49, 96, 145, 511]):  # selections ending inside and on split edges
+        cnt[s_] = c
+        sel[s_, c:] = -1
+    q = _store(rng.standard_normal((B, Qn, Hq, D)), "bf16")
+    kc = _store(rng.standard_normal((B, L, Hkv, D)), "bf16")
+    vc = _store(rng.standard_normal((B, L, Hkv, D)), "bf16")
+    want, want_lse = oracle.sparse_attn_decode(q, rp, kc, vc, sel, cnt, ts)
+    out, lse = qsa.sparse_attn_decode(dev(q, "bf16"), dev(rp, "i"), dev(kc, "bf16"), dev(vc, "bf16"), dev(sel, "i"),
+                                      dev(cnt, "i"), None if ts is None else dev(ts, "i"))
+    assert_close_out(host(out), want, "bf16")
+    np.testing.assert_allclose(host(lse), want_lse, rtol=1e-5, atol=1e-4)
