@@ -25,8 +25,9 @@
 //     list is the union of their kept blocks (built in LDS with a bitmap per
 //     window of 65,536 blocks) followed by each row's tail tokens;
 //   - decode: the rows of one sequence share its selection; a workgroup takes
-//     16 kept blocks (a split, one or two chunks) or the tail, and a combine
-//     kernel merges the splits' partial softmaxes.
+//     a split of 16 kept blocks (one or two chunks; several 16-block groups
+//     when the caller merges splits) or the tail, and a combine kernel merges
+//     the splits' partial softmaxes.
 // A wave skips the MFMAs of a 16-position sub-tile that none of its rows
 // attends, so disjoint selections cost gathers but not matrix work.
 //
@@ -59,7 +60,7 @@ struct Geo {
     static constexpr int kTpp = 256 / kCh;    // gather threads per K row, 32 dims each
     static constexpr int kChB = kCh / kBlock; // whole blocks per chunk
 };
-constexpr int kSplitBlocks = 16;    // kept blocks of one decode split (64 positions)
+constexpr int kSplitBlocks = 16;    // kept blocks of one decode split group (64 positions)
 constexpr int kWin = 1 << 16;       // union bitmap window, in blocks
 constexpr int kWinWords = kWin / 32;
 constexpr int kMaxUnionBlocks = 8192;  // rows per tile x top_k is kept at or below this
@@ -765,8 +766,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(AttnArgs a, i
 
 // ---------------------------------------------------------------------------
 // Decode: grid (splits, batch * Hkv).  q_per_sel * hg <= 64, q_per_sel <= 32.
-// Split i < nsplit-1 takes kept blocks [16i, 16i + 16); the last split takes
-// the tails.
+// Split i < nsplit-1 takes kept blocks [S i, S i + S), S = 16 ceil(n / (nsplit
+// - 1)) for the n 16-block groups of top_k (S = 16 with one split per group);
+// the last split takes the tails.
 // ---------------------------------------------------------------------------
 template <int DIM, typename KV>  // D = 256 needs the two-wave register budget to avoid spilling
 __global__ __launch_bounds__(256, DIM == 256 ? 2 : 1) void attn_decode_mfma_kernel(AttnArgs a)
