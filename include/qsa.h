@@ -342,7 +342,9 @@ qsa_status_t qsa_sparse_attn_prefill_paged(const void *q, const int32_t *row_seq
 
 /*
  * Bytes of device workspace qsa_sparse_attn_decode needs (fp32 partial
- * softmax states, one per row, head and split of the positions).
+ * softmax states, one per row, head and split of the positions; sized for one
+ * split per 16 kept blocks, which bounds every launch: large bf16 launches
+ * merge splits and use less).
  */
 size_t qsa_sparse_attn_decode_workspace_size(int32_t batch, int32_t q_per_seq, int32_t Hq,
                                              int32_t D, int32_t top_k);
